@@ -1,0 +1,98 @@
+"""Planted mistakes in the oracle (CPU only) must each fail at least one pin.
+
+Every mutation below is a plausible slip in writing the recurrence (a dropped
+term, a wrong sign, a wrong index, a transposed operand); the test patches
+it into oracle.recurrence for the duration of one check and runs the pins of
+test_oracle_pins against it.
+"""
+import numpy as np
+import pytest
+
+from oracle import recurrence as R
+from tests import test_oracle_pins as P
+
+
+def _step_sign(S, g_t, beta_t, v_t, k_t):
+    Sd = S * np.exp(g_t)[..., None, None]
+    pred = np.einsum("...vk,...k->...v", Sd, k_t)
+    delta = beta_t[..., None] * (v_t + pred)
+    return Sd, delta, Sd + delta[..., :, None] * k_t[..., None, :]
+
+
+def _step_undecayed_pred(S, g_t, beta_t, v_t, k_t):
+    Sd = S * np.exp(g_t)[..., None, None]
+    pred = np.einsum("...vk,...k->...v", S, k_t)
+    delta = beta_t[..., None] * (v_t - pred)
+    return Sd, delta, Sd + delta[..., :, None] * k_t[..., None, :]
+
+
+def _step_decay_after_write(S, g_t, beta_t, v_t, k_t):
+    pred = np.einsum("...vk,...k->...v", S, k_t)
+    delta = beta_t[..., None] * (v_t - pred)
+    S_new = (S + delta[..., :, None] * k_t[..., None, :]) * np.exp(g_t)[..., None, None]
+    return S * np.exp(g_t)[..., None, None], delta, S_new
+
+
+def _step_no_beta_on_pred(S, g_t, beta_t, v_t, k_t):
+    Sd = S * np.exp(g_t)[..., None, None]
+    pred = np.einsum("...vk,...k->...v", Sd, k_t)
+    delta = beta_t[..., None] * v_t - pred
+    return Sd, delta, Sd + delta[..., :, None] * k_t[..., None, :]
+
+
+def _step_transposed_state(S, g_t, beta_t, v_t, k_t):
+    Sd = S * np.exp(g_t)[..., None, None]
+    pred = np.einsum("...kv,...k->...v", Sd, k_t) if Sd.shape[-1] == Sd.shape[-2] else \
+        np.einsum("...vk,...k->...v", Sd, k_t)
+    delta = beta_t[..., None] * (v_t - pred)
+    return Sd, delta, Sd + delta[..., :, None] * k_t[..., None, :]
+
+
+def _l2norm_no_eps(x):
+    x = np.asarray(x, np.float64)
+    n = np.sqrt((x * x).sum(-1, keepdims=True))
+    return x / np.where(n == 0, 1, n)
+
+
+def _head_map_modulo(H, HV):
+    return np.arange(HV) % H
+
+
+MUTATIONS = {
+    "delta sign": ("_step", _step_sign),
+    "prediction from the undecayed state": ("_step", _step_undecayed_pred),
+    "decay after the write": ("_step", _step_decay_after_write),
+    "beta dropped on the prediction": ("_step", _step_no_beta_on_pred),
+    "transposed state in the prediction": ("_step", _step_transposed_state),
+    "eps dropped from the norm": ("l2norm", _l2norm_no_eps),
+    "value head -> key head by modulo": ("_head_map", _head_map_modulo),
+}
+
+PINS = [
+    lambda c: P.test_chunk_form_equals_recurrence(4),
+    lambda c: P.test_orthogonal_keys_reduce_to_causal_linear_attention(),
+    lambda c: P.test_brute_force_matrix_form_exact(),
+    lambda c: P.test_beta_zero_is_pure_decay(),
+    lambda c: P.test_scalar_case_is_an_exponential_moving_average(),
+    lambda c: P.test_forget_all_decay(),
+    lambda c: P.test_grouped_heads_equal_repeated_key_heads(),
+    lambda c: P.test_decode_is_one_recurrence_step_with_the_fused_gates(),
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_a_planted_mistake_fails_a_pin(name, monkeypatch, contract):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(R, attr, fn)
+    failed = 0
+    for pin in PINS:
+        try:
+            pin(contract)
+        except (AssertionError, ValueError, IndexError):
+            failed += 1
+    assert failed >= 1, f"no pin caught the mutation: {name}"
+
+
+def test_the_pins_pass_without_a_mutation(contract):
+    for pin in PINS:
+        pin(contract)

@@ -1,0 +1,357 @@
+"""Pins of the CPU oracle against facts it does not compute itself.
+
+Each test ties oracle.recurrence to something independent of it: the chunk
+(WY / transition) formulation, closed forms, a textbook reduction, a library
+filter, exact brute force, finite differences and the pages' invariants.
+"""
+from decimal import Decimal, getcontext
+
+import numpy as np
+import pytest
+from scipy.signal import lfilter
+
+from oracle import chunked, recurrence as R
+
+
+def rand_inputs(rng, lens, H, HV, K, V, h0=True, g_scale=1.0):
+    T = sum(lens)
+    q = rng.standard_normal((T, H, K))
+    k = rng.standard_normal((T, H, K))
+    v = rng.standard_normal((T, HV, V))
+    g = -g_scale * np.exp(rng.uniform(0, np.log(16), HV))[None] * np.log1p(
+        np.exp(rng.standard_normal((T, HV))))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((T, HV))))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    S0 = 0.1 * rng.standard_normal((len(lens), HV, V, K)) if h0 else None
+    return q, k, v, g, beta, cu, S0
+
+
+def rel_err(a, b):
+    return np.abs(a - b).max() / max(np.abs(b).max(), 1e-300)
+
+
+# ---------------------------------------------------------------- chunk form
+@pytest.mark.parametrize("chunk", [1, 2, 3, 4, 64])
+def test_chunk_form_equals_recurrence(chunk):
+    rng = np.random.default_rng(1 + chunk)
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, [5, 70, 1, 131], H=2, HV=4, K=8, V=6, g_scale=0.2)
+    o, hT = R.forward(q, k, v, g, beta, cu, S0)
+    oc, hc = chunked.chunked_forward(q, k, v, g, beta, cu, S0, chunk=chunk)
+    assert rel_err(oc, o) < 1e-12 and rel_err(hc, hT) < 1e-12
+
+
+def test_chunk_form_full_head_dim():
+    rng = np.random.default_rng(7)
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, [130, 64], H=1, HV=2, K=128, V=128)
+    o, hT = R.forward(q, k, v, g, beta, cu, S0)
+    oc, hc = chunked.chunked_forward(q, k, v, g, beta, cu, S0, chunk=64)
+    assert rel_err(oc, o) < 1e-12 and rel_err(hc, hT) < 1e-12
+
+
+def test_transition_product_form_equals_recurrence():
+    rng = np.random.default_rng(3)
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, [150, 37], H=1, HV=2, K=16, V=8, g_scale=0.1)
+    o, hT = R.forward(q, k, v, g, beta, cu, S0)
+    oc, hc = chunked.chunked_forward(q, k, v, g, beta, cu, S0, chunk=64, use_transition=True)
+    assert rel_err(oc, o) < 1e-11 and rel_err(hc, hT) < 1e-11
+
+
+# ---------------------------------------------------------------- closed forms
+def test_beta_zero_is_pure_decay():
+    """beta = 0: nothing is written; o_t = exp(sum_{s<=t} g_s) S0 q~_t and hT = exp(sum g) S0."""
+    rng = np.random.default_rng(11)
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, [40], H=1, HV=1, K=8, V=5)
+    beta[:] = 0.0
+    o, hT = R.forward(q, k, v, g, beta, cu, S0)
+    G = np.cumsum(g[:, 0])
+    qn = q[:, 0] / np.sqrt((q[:, 0] ** 2).sum(-1, keepdims=True) + 1e-6) * 8 ** -0.5
+    expect = np.exp(G)[:, None] * (qn @ S0[0, 0].T)
+    assert rel_err(o[:, 0], expect) < 1e-13
+    assert rel_err(hT[0, 0], np.exp(G[-1]) * S0[0, 0]) < 1e-13
+
+
+def test_orthogonal_keys_reduce_to_causal_linear_attention():
+    """g = 0, zero state and orthonormal keys: S_{t-1} k_t = 0, so delta_t = beta_t v_t and
+    o = tril(Q~ K^T) diag(beta) V, a masked matrix product (causal linear attention)."""
+    rng = np.random.default_rng(5)
+    T, K, V = 48, 64, 32
+    Qm, _ = np.linalg.qr(rng.standard_normal((K, K)))
+    k = Qm[:T][:, None, :]                     # orthonormal rows
+    q = rng.standard_normal((T, 1, K))
+    v = rng.standard_normal((T, 1, V))
+    beta = rng.uniform(0.1, 0.9, (T, 1))
+    g = np.zeros((T, 1))
+    o, _ = R.forward(q, k, v, g, beta, [0, T])
+    kn = k[:, 0] / np.sqrt(1 + 1e-6)
+    qn = q[:, 0] / np.sqrt((q[:, 0] ** 2).sum(-1, keepdims=True) + 1e-6) * K ** -0.5
+    expect = np.tril(qn @ kn.T) @ (beta * v[:, 0])
+    assert rel_err(o[:, 0], expect) < 1e-12
+
+
+def test_scalar_case_is_an_exponential_moving_average():
+    """K = V = 1, g = 0, q = k = 1, constant beta: with c = 1/sqrt(1 + 1e-6),
+    S_t = (1 - beta c^2) S_{t-1} + beta c v_t, a first-order IIR filter (scipy lfilter)."""
+    rng = np.random.default_rng(9)
+    T, b = 200, 0.3
+    v = rng.standard_normal((T, 1, 1))
+    ones = np.ones((T, 1, 1))
+    o, hT = R.forward(ones, ones, v, np.zeros((T, 1)), np.full((T, 1), b), [0, T])
+    c = 1 / np.sqrt(1 + 1e-6)
+    S = lfilter([b * c], [1.0, -(1 - b * c * c)], v[:, 0, 0])
+    assert rel_err(o[:, 0, 0], S * c) < 1e-12        # o = S q~, q~ = c (scale = 1)
+    assert abs(hT[0, 0, 0, 0] - S[-1]) < 1e-12
+
+
+def test_forget_all_decay():
+    """g = -60: the carried state is wiped each step, o_t = beta_t (k^_t . q~_t) v_t, no NaN."""
+    rng = np.random.default_rng(2)
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, [64, 3], H=1, HV=1, K=16, V=8)
+    g[:] = -60.0
+    o, hT = R.forward(q, k, v, g, beta, cu, S0)
+    kn = R.l2norm(k[:, 0])
+    qn = R.l2norm(q[:, 0]) * 16 ** -0.5
+    expect = (beta[:, 0] * (kn * qn).sum(-1))[:, None] * v[:, 0]
+    assert np.isfinite(o).all() and np.isfinite(hT).all()
+    assert rel_err(o[:, 0], expect) < 1e-13
+    oc, hc = chunked.chunked_forward(q, k, v, g, beta, cu, S0, chunk=64)
+    assert np.isfinite(oc).all() and rel_err(oc, o) < 1e-12
+
+
+def test_brute_force_matrix_form_exact():
+    """T = 4, K = V = 2: the state recurrence evaluated literally as
+    S_t = a S_{t-1} (I - beta k k^T) + beta v k^T with full 2x2 matrix products in
+    50-digit decimal arithmetic."""
+    getcontext().prec = 50
+    rng = np.random.default_rng(4)
+    T, K, V = 4, 2, 2
+    q = np.round(rng.standard_normal((T, 1, K)), 3)
+    k = np.round(rng.standard_normal((T, 1, K)), 3)
+    v = np.round(rng.standard_normal((T, 1, V)), 3)
+    g = np.round(-rng.uniform(0, 1, (T, 1)), 3)
+    beta = np.round(rng.uniform(0, 1, (T, 1)), 3)
+    S0 = np.round(rng.standard_normal((1, 1, V, K)), 3)
+    o, hT = R.forward(q, k, v, g, beta, [0, T], S0)
+
+    D = lambda x: Decimal(repr(float(x)))  # noqa: E731
+    eps = Decimal("0.000001")
+    S = [[D(S0[0, 0, i, j]) for j in range(K)] for i in range(V)]
+    scale = Decimal(1) / Decimal(K).sqrt()
+    for t in range(T):
+        kk = [D(x) for x in k[t, 0]]
+        nk = (sum(x * x for x in kk) + eps).sqrt()
+        kk = [x / nk for x in kk]
+        qq = [D(x) for x in q[t, 0]]
+        nq = (sum(x * x for x in qq) + eps).sqrt()
+        qq = [scale * x / nq for x in qq]
+        a = D(g[t, 0]).exp()
+        b = D(beta[t, 0])
+        M = [[(Decimal(1) if i == j else Decimal(0)) - b * kk[i] * kk[j] for j in range(K)]
+             for i in range(K)]
+        S = [[a * sum(S[r][m] * M[m][c] for m in range(K)) + b * D(v[t, 0, r]) * kk[c]
+              for c in range(K)] for r in range(V)]
+        ot = [sum(S[r][c] * qq[c] for c in range(K)) for r in range(V)]
+        for r in range(V):
+            assert abs(float(ot[r]) - o[t, 0, r]) < 1e-14
+    for r in range(V):
+        for c in range(K):
+            assert abs(float(S[r][c]) - hT[0, 0, r, c]) < 1e-14
+
+
+# ---------------------------------------------------------------- invariants
+def test_state_carry_at_the_pages_split_points(contract):
+    """One call equals two calls with hT -> h0, at the boundary sweep's prefixes and
+    continuations (torchtitan PR #4389)."""
+    rng = np.random.default_rng(21)
+    pre = contract["continuity_prefixes"]["value"]
+    cont = contract["continuity_continuations"]["value"]
+    T = max(pre) + max(cont)
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, [T], H=1, HV=2, K=8, V=4, g_scale=0.05)
+    for p in pre:
+        for c in cont:
+            n = p + c
+            o, hT = R.forward(q[:n], k[:n], v[:n], g[:n], beta[:n], [0, n], S0)
+            o1, h1 = R.forward(q[:p], k[:p], v[:p], g[:p], beta[:p], [0, p], S0)
+            o2, h2 = R.forward(q[p:n], k[p:n], v[p:n], g[p:n], beta[p:n], [0, c], h1)
+            assert rel_err(np.concatenate([o1, o2]), o) < 1e-12
+            assert rel_err(h2, hT) < 1e-12
+
+
+def test_a_sequence_alone_equals_it_inside_a_pack():
+    rng = np.random.default_rng(8)
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, [17, 64, 90], H=2, HV=4, K=8, V=8)
+    o, hT = R.forward(q, k, v, g, beta, cu, S0)
+    s0, s1 = cu[1], cu[2]
+    o1, h1 = R.forward(q[s0:s1], k[s0:s1], v[s0:s1], g[s0:s1], beta[s0:s1], [0, s1 - s0],
+                       S0[1:2])
+    assert np.array_equal(o1, o[s0:s1]) and np.array_equal(h1[0], hT[1])
+
+
+def test_linearity_in_state_and_values():
+    rng = np.random.default_rng(12)
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, [33, 20], H=1, HV=2, K=8, V=8)
+    o, hT = R.forward(q, k, v, g, beta, cu, S0)
+    o2, h2 = R.forward(q, k, 2 * v, g, beta, cu, 2 * S0)
+    assert np.array_equal(o2, 2 * o) and np.array_equal(h2, 2 * hT)
+
+
+def test_grouped_heads_equal_repeated_key_heads():
+    """Value head hv reads key head hv // (HV/H): the same as repeating q/k per value head
+    (FLA's repeat_interleave), and q/k gradients sum over the value heads of a key head."""
+    rng = np.random.default_rng(13)
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, [20, 9], H=2, HV=4, K=8, V=8)
+    qr, kr = np.repeat(q, 2, axis=1), np.repeat(k, 2, axis=1)
+    o, hT = R.forward(q, k, v, g, beta, cu, S0)
+    o2, h2 = R.forward(qr, kr, v, g, beta, cu, S0)
+    assert np.array_equal(o, o2) and np.array_equal(hT, h2)
+    do = rng.standard_normal(o.shape)
+    gr = R.backward(q, k, v, g, beta, cu, do, S0)
+    gr2 = R.backward(qr, kr, v, g, beta, cu, do, S0)
+    assert rel_err(gr["dq"], gr2["dq"].reshape(-1, 2, 2, 8).sum(2)) < 1e-13
+    assert rel_err(gr["dk"], gr2["dk"].reshape(-1, 2, 2, 8).sum(2)) < 1e-13
+
+
+# ---------------------------------------------------------------- gradients
+def test_adjoint_matches_central_finite_differences():
+    rng = np.random.default_rng(31)
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, [3, 5], H=1, HV=2, K=3, V=3, g_scale=0.3)
+    wo = rng.standard_normal((8, 2, 3))
+    wh = rng.standard_normal((2, 2, 3, 3))
+
+    def loss(q, k, v, g, beta, S0):
+        o, hT = R.forward(q, k, v, g, beta, cu, S0)
+        return (o * wo).sum() + (hT * wh).sum()
+
+    grads = R.backward(q, k, v, g, beta, cu, wo, S0, dhT=wh, ckpt=2)
+    args = dict(q=q, k=k, v=v, g=g, beta=beta, S0=S0)
+    names = dict(q="dq", k="dk", v="dv", g="dg", beta="dbeta", S0="dh0")
+    h = 1e-6
+    for name, gname in names.items():
+        x = args[name]
+        num = np.zeros_like(x)
+        for i in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[i] += h
+            xm[i] -= h
+            num[i] = (loss(**{**args, name: xp}) - loss(**{**args, name: xm})) / (2 * h)
+        assert rel_err(grads[gname], num) < 1e-6, name
+
+
+def test_dh0_matches_the_reverse_chunk_state_recurrence():
+    rng = np.random.default_rng(41)
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, [100, 64, 7], H=1, HV=2, K=16, V=8, g_scale=0.1)
+    do = rng.standard_normal((171, 2, 8))
+    dhT = rng.standard_normal((3, 2, 8, 16))
+    gr = R.backward(q, k, v, g, beta, cu, do, S0, dhT=dhT)
+    dh0 = chunked.chunked_dh0(q, k, v, g, beta, cu, do, dhT=dhT, chunk=64)
+    assert rel_err(gr["dh0"], dh0) < 1e-11
+
+
+def test_l2norm_backward_matches_finite_differences():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((4, 7))
+    w = rng.standard_normal((4, 7))
+    num = np.zeros_like(x)
+    for i in np.ndindex(x.shape):
+        xp, xm = x.copy(), x.copy()
+        xp[i] += 1e-6
+        xm[i] -= 1e-6
+        num[i] = ((R.l2norm(xp) * w).sum() - (R.l2norm(xm) * w).sum()) / 2e-6
+    assert rel_err(R.l2norm_backward(x, w), num) < 1e-8
+
+
+def test_l2norm_values(contract):
+    eps = contract["l2norm_eps"]["value"]
+    out = R.l2norm(np.array([[3.0, 4.0]]))
+    assert np.allclose(out, np.array([[3.0, 4.0]]) / np.sqrt(25 + eps), rtol=0, atol=1e-16)
+    assert np.array_equal(R.l2norm(np.zeros((1, 4))), np.zeros((1, 4)))
+
+
+# ---------------------------------------------------------------- decode
+def test_softplus_threshold_branches(contract):
+    th = contract["softplus_threshold"]["value"]
+    x = np.array([-30.0, -1.0, 0.0, 19.5, th, th + 1e-3, 50.0])
+    sp = R.softplus_thresholded(x)
+    assert sp[0] == np.log1p(np.exp(-30.0)) and sp[2] == np.log(2.0)
+    assert sp[4] == np.log1p(np.exp(th))          # at the threshold: the log branch
+    assert sp[5] == th + 1e-3 and sp[6] == 50.0   # above: identity
+    assert abs(np.log1p(np.exp(th)) - th) < 2.1e-9
+
+
+def test_decode_gating_closed_forms():
+    g, beta = R.decode_gating(np.zeros((1, 2)), np.zeros((1, 2)), np.array([0.0, np.log(4.0)]),
+                              np.zeros(2))
+    assert beta[0, 0] == 0.5 and abs(g[0, 0] + np.log(2.0)) < 1e-16
+    assert abs(g[0, 1] + 4 * np.log(2.0)) < 1e-15
+
+
+def _decode_case(rng, N=6, H=2, HV=4, K=8, V=8, slots=10):
+    q = rng.standard_normal((N, H, K))
+    k = rng.standard_normal((N, H, K))
+    v = rng.standard_normal((N, HV, V))
+    a = rng.standard_normal((N, HV))
+    b = rng.standard_normal((N, HV))
+    A_log = rng.uniform(0, np.log(16), HV)
+    dt_bias = rng.standard_normal(HV) * 0.1
+    pool = 0.1 * rng.standard_normal((slots, HV, V, K))
+    return q, k, v, a, b, A_log, dt_bias, pool
+
+
+def test_decode_skips_null_and_negative_rows():
+    rng = np.random.default_rng(51)
+    q, k, v, a, b, A_log, dt_bias, pool = _decode_case(rng)
+    idx = np.array([3, 0, 7, -2, 1, 9])
+    o, new = R.decode_step(q, k, v, a, b, A_log, dt_bias, pool, idx)
+    assert np.array_equal(o[1], np.zeros_like(o[1])) and np.array_equal(o[3], np.zeros_like(o[3]))
+    untouched = [s for s in range(10) if s not in (3, 7, 1, 9)]
+    assert np.array_equal(new[untouched], pool[untouched])
+    assert np.array_equal(new[0], pool[0])
+
+
+def test_decode_rejects_bad_active_indices():
+    rng = np.random.default_rng(52)
+    q, k, v, a, b, A_log, dt_bias, pool = _decode_case(rng)
+    with pytest.raises(ValueError):
+        R.decode_step(q, k, v, a, b, A_log, dt_bias, pool, np.array([3, 0, 7, 3, 1, 9]))
+    with pytest.raises(ValueError):
+        R.decode_step(q, k, v, a, b, A_log, dt_bias, pool, np.array([3, 0, 7, 10, 1, 9]))
+    # repeated null rows are fine
+    R.decode_step(q, k, v, a, b, A_log, dt_bias, pool, np.array([0, 0, -1, -1, 1, 9]))
+
+
+def test_decode_is_one_recurrence_step_with_the_fused_gates():
+    rng = np.random.default_rng(53)
+    q, k, v, a, b, A_log, dt_bias, pool = _decode_case(rng)
+    idx = np.array([3, 0, 7, 2, 1, 9])
+    o, new = R.decode_step(q, k, v, a, b, A_log, dt_bias, pool, idx)
+    x = a + dt_bias
+    g = -np.exp(A_log) * np.where(x > 20, x, np.log1p(np.exp(x)))
+    beta = 1 / (1 + np.exp(-b))
+    for n in [0, 2, 3, 4, 5]:
+        S = pool[idx[n]]
+        for hv in range(4):
+            kk = k[n, hv // 2] / np.sqrt((k[n, hv // 2] ** 2).sum() + 1e-6)
+            qq = q[n, hv // 2] / np.sqrt((q[n, hv // 2] ** 2).sum() + 1e-6) * 8 ** -0.5
+            M = np.eye(8) - beta[n, hv] * np.outer(kk, kk)
+            Sn = np.exp(g[n, hv]) * S[hv] @ M + beta[n, hv] * np.outer(v[n, hv], kk)
+            assert rel_err(new[idx[n], hv], Sn) < 1e-13
+            assert rel_err(o[n, hv], Sn @ qq) < 1e-12
+
+
+def test_decode_steps_equal_the_chunk_forward():
+    """T decode steps on one slot reproduce the forward over the same T tokens
+    (the pages compare the two paths: RL-Kernel PR #469, 'Decode versus chunked prefill')."""
+    rng = np.random.default_rng(54)
+    T, H, HV, K, V = 9, 1, 2, 8, 8
+    q, k, v = (rng.standard_normal((T, H, K)), rng.standard_normal((T, H, K)),
+               rng.standard_normal((T, HV, V)))
+    a, b = rng.standard_normal((T, HV)), rng.standard_normal((T, HV))
+    A_log, dt_bias = rng.uniform(0, 2, HV), np.zeros(HV)
+    pool = 0.1 * rng.standard_normal((3, HV, V, K))
+    g, beta = R.decode_gating(a, b, A_log, dt_bias)
+    o_ref, hT = R.forward(q, k, v, g, beta, [0, T], pool[2:3])
+    cur = pool
+    for t in range(T):
+        o_t, cur = R.decode_step(q[t:t + 1], k[t:t + 1], v[t:t + 1], a[t:t + 1], b[t:t + 1],
+                                 A_log, dt_bias, cur, np.array([2]))
+        assert rel_err(o_t[0], o_ref[t]) < 1e-12
+    assert rel_err(cur[2], hT[0]) < 1e-12
