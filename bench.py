@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Throughput of the chunked gated delta rule on one MI355X.
+
+One step = one chunk forward (saving what the backward needs) plus one chunk
+backward, over the 2 x 8192-token pack with 16 key / 32 value heads
+(K = V = 128, chunk 64): every kernel of the chunk path, from the chunk table
+to dq/dk/dv/dg/dbeta/dh0. Inputs are seeded synthetic tensors already resident
+in HBM when timing starts. Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+
+Per-kernel durations come from HIP events that the library records around
+each kernel it launches, on the stream it launches on. The roofline object is
+for the kernel with the largest average duration. The CPU baseline times the
+fp64 oracle on a bounded sample of the same workload.
+"""
+import argparse
+import ctypes
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD = "fwdbwd_2x8192_h16_hv32"
+METRIC = "GDN chunk fwd+bwd tokens/sec (H=16, HV=32, K=V=128); % bf16 MFMA peak"
+PEAK_BF16 = 2.5e15       # MI355X dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12        # MI355X HBM3E, B/s
+
+# Algorithmic work per chunk of 64 tokens and value head (K = V = 128). The
+# masked triangles of the 64 x 64 products are not counted.
+C, D = 64, 128
+F_KKT = C * (C - 1) // 2 * 2 * D            # strictly lower K K^T
+F_TSOLVE = C ** 3 // 3                      # (I + A)^-1
+F_TRI = C * (C + 1) // 2 * 2 * D            # one lower-triangular 64x64 by 64x128 product
+F_STATE = 2 * C * D * D                     # one 64x128 by 128x128 product
+F_FWD = F_KKT + F_TSOLVE + 4 * F_TRI + 3 * F_STATE     # 9,024,853
+F_FWDBWD = 3 * F_FWD
+# per-kernel shares of the model (forward: WY pass vs scan; backward: its two kernels
+# split the 2 * F_FWD gradient work as the gradient contractions are assigned to them)
+KERNEL_FLOPS = {
+    "chunk_prep": F_KKT + F_TSOLVE + 3 * F_TRI,                 # K K^T, T, W, U, Q K^T
+    "fwd_scan": F_TRI + 3 * F_STATE,                            # attn D, W h, Q h, K^T D
+    "chunk_prep_bwd": F_KKT + F_TSOLVE + 2 * F_TRI,             # K K^T, T, W, Q K^T
+    "bwd_dh_scan": F_TRI + 3 * F_STATE,                         # P^T dO, K dh, Q^T dO, W^T dD
+    "bwd_chunk": 2 * F_FWD - (F_TRI + 3 * F_STATE),             # the remaining gradient work
+}
+
+
+def hip():
+    lib = ctypes.CDLL("libamdhip64.so")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def make_events(h, n):
+    arr = (ctypes.c_void_p * n)()
+    for i in range(n):
+        ev = ctypes.c_void_p()
+        if h.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        arr[i] = ev
+    return arr
+
+
+def elapsed_ms(h, a, b):
+    ms = ctypes.c_float()
+    if h.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+        raise RuntimeError("hipEventElapsedTime failed")
+    return ms.value
+
+
+def cpu_baseline(inp, sample_tokens):
+    """fp64 oracle forward + backward on the first `sample_tokens` tokens of the
+    first sequence, all heads; tokens per second on this host."""
+    import numpy as np
+    import torch
+    from oracle import recurrence as R
+
+    def f64(t):
+        return t.to(torch.float64).numpy()
+
+    n = sample_tokens
+    sl = slice(0, n)
+    args = [f64(inp[k][sl]) for k in ("q", "k", "v", "g", "beta")]
+    h0 = f64(inp["h0"][0:1])
+    do = f64(inp["do"][sl])
+    t0 = time.perf_counter()
+    R.forward(*args, [0, n], h0)
+    R.backward(*args, [0, n], do, h0)
+    dt = time.perf_counter() - t0
+    return dict(value=n / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample=(f"fp64 oracle forward + backward over the first {n} tokens of sequence 0 "
+                        f"of {WORKLOAD} (all 16 key / 32 value heads), {dt:.1f} s on "
+                        f"{platform.processor() or platform.machine()} ({os.cpu_count()} host cores "
+                        f"visible; numpy einsum runs on 1)"))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=192)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from chunked_gated_delta_04_amd import gdn, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = synth.workload_inputs(WORKLOAD)
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    T, H, _ = inp["q"].shape
+    HV = inp["v"].shape[1]
+    N = inp["cu_seqlens"].numel() - 1
+    host = inp["cu_seqlens"].to(torch.int32)
+    p = gdn.make_problem(N, T, H, HV, d["cu_seqlens"], host)
+    NC = gdn.gdn_num_chunks(p)
+
+    o = torch.empty(T, HV, 128, dtype=torch.bfloat16, device=dev)
+    hT = torch.empty(N, HV, 128, 128, dtype=torch.float32, device=dev)
+    saved = torch.empty(gdn.gdn_chunk_saved_size(p), dtype=torch.uint8, device=dev)
+    wsf = torch.empty(gdn.gdn_chunk_fwd_workspace_size(p), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(gdn.gdn_chunk_bwd_workspace_size(p), dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+    dg = torch.empty(T, HV, dtype=torch.float32, device=dev)
+    dbeta = torch.empty_like(dg)
+    dh0 = torch.empty(N, HV, 128, 128, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev_f=None, ev_b=None):
+        if ev_f is None:
+            gdn.gdn_chunk_fwd(p, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], o, hT, saved,
+                              wsf, stream)
+            gdn.gdn_chunk_bwd(p, d["q"], d["k"], d["v"], d["g"], d["beta"], saved, d["do"], None,
+                              dq, dk, dv, dg, dbeta, dh0, wsb, stream)
+            return None
+        nf = gdn.gdn_chunk_fwd_timed(p, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], o, hT,
+                                     saved, wsf, ev_f, stream)
+        nb = gdn.gdn_chunk_bwd_timed(p, d["q"], d["k"], d["v"], d["g"], d["beta"], saved, d["do"],
+                                     None, dq, dk, dv, dg, dbeta, dh0, wsb, ev_b, stream)
+        return nf, nb
+
+    h = hip()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    S = gdn.GDN_MAX_STAGES
+    evf = [make_events(h, 2 * S) for _ in range(args.steps)]
+    evb = [make_events(h, 2 * S) for _ in range(args.steps)]
+    outer = make_events(h, 2)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    h.hipEventRecord(outer[0], ctypes.c_void_p(stream.cuda_stream))
+    counts = None
+    for i in range(args.steps):
+        counts = step(evf[i], evb[i])
+    h.hipEventRecord(outer[1], ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    h.hipEventSynchronize(outer[1])
+    total_ms = elapsed_ms(h, outer[0], outer[1])
+    ms_per_step = total_ms / args.steps
+
+    stages = {}
+    nf, nb = counts
+    for i in range(args.steps):
+        for j in range(nf):
+            name = gdn.gdn_stage_name(0, j)
+            stages.setdefault(name, []).append(elapsed_ms(h, evf[i][2 * j], evf[i][2 * j + 1]))
+        for j in range(nb):
+            name = gdn.gdn_stage_name(1, j)
+            if name == "chunk_table":
+                name = "chunk_table_bwd"
+            stages.setdefault(name, []).append(elapsed_ms(h, evb[i][2 * j], evb[i][2 * j + 1]))
+    stage_ms = {k: sum(v) / len(v) for k, v in stages.items()}
+    dom = max(stage_ms, key=stage_ms.get)
+
+    units = NC * HV                                   # (chunk, value head) pairs per launch
+    step_flops = F_FWDBWD * units
+    tokens_per_s = T / (ms_per_step * 1e-3)
+    mfma_frac = step_flops / (ms_per_step * 1e-3) / PEAK_BF16
+    dom_flops = KERNEL_FLOPS.get(dom, 0) * units
+    dom_achieved = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(dom_achieved, 3), "peak": PEAK_BF16 / 1e12,
+                "unit": "TFLOP/s", "frac": round(dom_achieved * 1e12 / PEAK_BF16, 5),
+                "traffic": None, "kernel": dom, "kernel_ms": round(stage_ms[dom], 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, args.cpu_sample_tokens)
+        cpu["value"] = round(cpu["value"], 3)
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "global_batch": N, "seq_len": T // N,
+                   "tokens_per_step": T, "H": H, "HV": HV, "K": 128, "V": 128, "chunk": 64,
+                   "parallelism": "single-gpu"},
+        "mfma_frac_of_bf16_peak": round(mfma_frac, 5),
+        "algorithmic_tflops": round(step_flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

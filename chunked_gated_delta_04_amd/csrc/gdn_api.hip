@@ -1,0 +1,339 @@
+// C ABI of the gated delta rule library: argument checks, workspace layout,
+// launch sequencing. Every argument error returns before anything is
+// enqueued (the Cake page "[Cake 1/13] gdn", "Review items": extents are
+// checked before any launch; RL-Kernel PR #469, "What": an active decode
+// index out of range or repeated is an error).
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+#define GDN_API extern "C" __attribute__((visibility("default")))
+
+using namespace gdn;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kBlk64x128 = 64 * 128;  // bf16 elements of one (value head, chunk) tile
+constexpr size_t kBlk64x64 = 64 * 64;
+constexpr size_t kState = (size_t)kHead * kHead;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Layout {
+  size_t table, seq_first, W, U, Qg, P, Kb, gL, dh, dD, dDT, total;
+};
+
+// Chunk slots: exact with a host copy of the boundaries, else T/64 + N.
+int64_t chunk_slots(const gdn_problem* p) {
+  if (p->cu_seqlens_host) {
+    int64_t nc = 0;
+    for (int n = 0; n < p->N; ++n) {
+      const int64_t L = (int64_t)p->cu_seqlens_host[n + 1] - p->cu_seqlens_host[n];
+      nc += (L + kChunk - 1) / kChunk;
+    }
+    return nc;
+  }
+  return (int64_t)p->T / kChunk + p->N;
+}
+
+gdn_status check_problem(const gdn_problem* p, int64_t* nc) {
+  if (!p) return GDN_ERR_NULL;
+  if (p->N < 0 || p->T < 0 || p->H <= 0 || p->HV <= 0 || p->K <= 0 || p->V <= 0 ||
+      p->chunk <= 0)
+    return GDN_ERR_SHAPE;
+  if (p->K != kHead || p->V != kHead || p->chunk != kChunk || p->HV % p->H != 0)
+    return GDN_ERR_UNSUPPORTED;
+  if (p->H > 65535) return GDN_ERR_SHAPE;  // grid.y of the per-chunk kernels
+  if (p->N == 0 && p->T != 0) return GDN_ERR_SHAPE;
+  if (p->T > 0 && !p->cu_seqlens) return GDN_ERR_NULL;
+  if (p->cu_seqlens_host) {
+    const int32_t* cu = p->cu_seqlens_host;
+    if (cu[0] != 0 || cu[p->N] != p->T) return GDN_ERR_SEQLENS;
+    for (int n = 0; n < p->N; ++n)
+      if (cu[n + 1] < cu[n]) return GDN_ERR_SEQLENS;
+  }
+  const int64_t c = chunk_slots(p);
+  if (c > (int64_t)INT32_MAX / 2 || (int64_t)p->N * p->HV > (int64_t)INT32_MAX / 64)
+    return GDN_ERR_SHAPE;
+  *nc = c;
+  return GDN_OK;
+}
+
+Layout make_layout(const gdn_problem* p, int64_t NC, bool bwd) {
+  Layout L;
+  const size_t blocks = (size_t)p->HV * (size_t)NC;
+  size_t off = 0;
+  L.table = off;     off = align_up(off + sizeof(ChunkInfo) * (size_t)NC);
+  L.seq_first = off; off = align_up(off + sizeof(int32_t) * (size_t)(p->N + 1));
+  L.W = off;         off = align_up(off + 2 * kBlk64x128 * blocks);
+  L.U = off;         off = bwd ? off : align_up(off + 2 * kBlk64x128 * blocks);
+  L.Qg = off;        off = align_up(off + 2 * kBlk64x128 * blocks);
+  L.P = off;         off = align_up(off + 2 * kBlk64x64 * blocks);
+  L.Kb = off;        off = align_up(off + 2 * kBlk64x128 * blocks);
+  L.gL = off;        off = align_up(off + sizeof(float) * blocks);
+  L.dh = off;        off = bwd ? align_up(off + 2 * kState * blocks) : off;
+  L.dD = off;        off = bwd ? align_up(off + 2 * kBlk64x128 * blocks) : off;
+  L.dDT = off;       off = bwd ? align_up(off + 2 * kBlk64x128 * blocks) : off;
+  L.total = off;
+  return L;
+}
+
+PrepOut prep_views(char* ws, const Layout& L, bool bwd) {
+  PrepOut o;
+  o.W = reinterpret_cast<uint16_t*>(ws + L.W);
+  o.U = bwd ? nullptr : reinterpret_cast<uint16_t*>(ws + L.U);
+  o.Qg = reinterpret_cast<uint16_t*>(ws + L.Qg);
+  o.P = reinterpret_cast<uint16_t*>(ws + L.P);
+  o.Kb = reinterpret_cast<uint16_t*>(ws + L.Kb);
+  o.gL = reinterpret_cast<float*>(ws + L.gL);
+  return o;
+}
+
+float effective_scale(const gdn_problem* p) {
+  return p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->K);
+}
+
+#define GDN_TRY(expr)                              \
+  do {                                             \
+    if ((expr) != hipSuccess) return GDN_ERR_HIP;  \
+  } while (0)
+
+}  // namespace
+
+GDN_API const char* gdn_status_string(int status) {
+  switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL: return "a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "a negative or inconsistent extent";
+    case GDN_ERR_UNSUPPORTED: return "unsupported configuration (K = V = 128, chunk = 64, HV % H == 0)";
+    case GDN_ERR_SEQLENS: return "cu_seqlens must start at 0, be non-decreasing and end at T";
+    case GDN_ERR_INDEX: return "an active state index is out of range or repeated";
+    case GDN_ERR_WORKSPACE: return "workspace missing or smaller than the size query";
+    case GDN_ERR_HIP: return "a HIP launch failed";
+    case GDN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+GDN_API int64_t gdn_num_chunks(const gdn_problem* p) {
+  int64_t nc = 0;
+  return check_problem(p, &nc) == GDN_OK ? nc : 0;
+}
+
+GDN_API size_t gdn_chunk_saved_size(const gdn_problem* p) {
+  int64_t nc = 0;
+  if (check_problem(p, &nc) != GDN_OK) return 0;
+  return sizeof(uint16_t) * (size_t)kSavedBlock * (size_t)p->HV * (size_t)nc;
+}
+
+GDN_API size_t gdn_chunk_fwd_workspace_size(const gdn_problem* p) {
+  int64_t nc = 0;
+  if (check_problem(p, &nc) != GDN_OK) return 0;
+  return make_layout(p, nc, false).total;
+}
+
+GDN_API size_t gdn_chunk_bwd_workspace_size(const gdn_problem* p) {
+  int64_t nc = 0;
+  if (check_problem(p, &nc) != GDN_OK) return 0;
+  return make_layout(p, nc, true).total;
+}
+
+// Records events[2 i] / events[2 i + 1] around stage i when events are given.
+struct StageClock {
+  void* const* ev;
+  int n;
+  hipStream_t s;
+  template <typename F>
+  hipError_t run(F&& launch) {
+    if (ev && hipEventRecord(reinterpret_cast<hipEvent_t>(ev[2 * n]), s) != hipSuccess)
+      return hipErrorUnknown;
+    hipError_t e = launch();
+    if (e != hipSuccess) return e;
+    if (ev && hipEventRecord(reinterpret_cast<hipEvent_t>(ev[2 * n + 1]), s) != hipSuccess)
+      return hipErrorUnknown;
+    ++n;
+    return hipSuccess;
+  }
+};
+
+static int chunk_fwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_t* k,
+                          const uint16_t* v, const float* g, const float* beta, const float* h0,
+                          uint16_t* o, float* hT, uint16_t* saved, void* workspace,
+                          size_t workspace_bytes, void* stream, void* const* events,
+                          int* n_stages) {
+  if (n_stages) *n_stages = 0;
+  int64_t NC = 0;
+  gdn_status st = check_problem(p, &NC);
+  if (st != GDN_OK) return st;
+  if (p->T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(h0) ||
+      !aligned16(hT) || !aligned16(saved) || !aligned16(workspace))
+    return GDN_ERR_ALIGN;
+  const Layout L = make_layout(p, NC, false);
+  if (!workspace || workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  StageClock clk{events, 0, s};
+  if (p->T == 0) {  // no tokens: the state passes through
+    if (hT)
+      GDN_TRY(clk.run([&] { return launch_state_copy(h0, hT, (size_t)p->N * p->HV * kState, s); }));
+    if (n_stages) *n_stages = clk.n;
+    return GDN_OK;
+  }
+  char* ws = static_cast<char*>(workspace);
+  ChunkInfo* table = reinterpret_cast<ChunkInfo*>(ws + L.table);
+  int32_t* seq_first = reinterpret_cast<int32_t*>(ws + L.seq_first);
+  const PrepOut prep = prep_views(ws, L, false);
+  GDN_TRY(clk.run([&] {
+    return launch_chunk_table(p->cu_seqlens, p->N, p->T, (int)NC, table, seq_first, s);
+  }));
+  GDN_TRY(clk.run([&] {
+    return launch_chunk_prep(false, table, (int)NC, p->H, p->HV, effective_scale(p), q, k, v, g,
+                             beta, prep, s);
+  }));
+  GDN_TRY(clk.run([&] {
+    return launch_fwd_scan(seq_first, p->N, p->HV, (int)NC, table, prep, h0, o, hT, saved, s);
+  }));
+  if (n_stages) *n_stages = clk.n;
+  return GDN_OK;
+}
+
+GDN_API int gdn_chunk_fwd(const gdn_problem* p, const uint16_t* q, const uint16_t* k,
+                          const uint16_t* v, const float* g, const float* beta, const float* h0,
+                          uint16_t* o, float* hT, uint16_t* saved, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return chunk_fwd_impl(p, q, k, v, g, beta, h0, o, hT, saved, workspace, workspace_bytes, stream,
+                        nullptr, nullptr);
+}
+
+GDN_API int gdn_chunk_fwd_timed(const gdn_problem* p, const uint16_t* q, const uint16_t* k,
+                                const uint16_t* v, const float* g, const float* beta,
+                                const float* h0, uint16_t* o, float* hT, uint16_t* saved,
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                void* const* events, int* n_stages) {
+  if (!events || !n_stages) return GDN_ERR_NULL;
+  return chunk_fwd_impl(p, q, k, v, g, beta, h0, o, hT, saved, workspace, workspace_bytes, stream,
+                        events, n_stages);
+}
+
+static int chunk_bwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_t* k,
+                          const uint16_t* v, const float* g, const float* beta,
+                          const uint16_t* saved, const uint16_t* dO, const float* dhT,
+                          uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dg, float* dbeta,
+                          float* dh0, void* workspace, size_t workspace_bytes, void* stream,
+                          void* const* events, int* n_stages) {
+  if (n_stages) *n_stages = 0;
+  int64_t NC = 0;
+  gdn_status st = check_problem(p, &NC);
+  if (st != GDN_OK) return st;
+  if (p->T > 0 && (!q || !k || !v || !g || !beta || !saved || !dO || !dq || !dk || !dv ||
+                   !dg || !dbeta))
+    return GDN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(saved) ||
+      !aligned16(dO) || !aligned16(dhT) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      !aligned16(dh0) || !aligned16(workspace))
+    return GDN_ERR_ALIGN;
+  const Layout L = make_layout(p, NC, true);
+  if (!workspace || workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  StageClock clk{events, 0, s};
+  if (p->T == 0) {  // no tokens: the state cotangent passes through
+    if (dh0)
+      GDN_TRY(clk.run([&] { return launch_state_copy(dhT, dh0, (size_t)p->N * p->HV * kState, s); }));
+    if (n_stages) *n_stages = clk.n;
+    return GDN_OK;
+  }
+  char* ws = static_cast<char*>(workspace);
+  ChunkInfo* table = reinterpret_cast<ChunkInfo*>(ws + L.table);
+  int32_t* seq_first = reinterpret_cast<int32_t*>(ws + L.seq_first);
+  const PrepOut prep = prep_views(ws, L, true);
+  BwdBufs bufs;
+  bufs.dh = reinterpret_cast<uint16_t*>(ws + L.dh);
+  bufs.dD = reinterpret_cast<uint16_t*>(ws + L.dD);
+  bufs.dDT = reinterpret_cast<uint16_t*>(ws + L.dDT);
+  const float scale = effective_scale(p);
+  GDN_TRY(clk.run([&] {
+    return launch_chunk_table(p->cu_seqlens, p->N, p->T, (int)NC, table, seq_first, s);
+  }));
+  GDN_TRY(clk.run([&] {
+    return launch_chunk_prep(true, table, (int)NC, p->H, p->HV, scale, q, k, v, g, beta, prep, s);
+  }));
+  GDN_TRY(clk.run([&] {
+    return launch_bwd_dh_scan(seq_first, p->N, p->HV, (int)NC, table, prep, dO, dhT, dh0, bufs, s);
+  }));
+  GDN_TRY(clk.run([&] {
+    return launch_bwd_chunk(table, (int)NC, p->H, p->HV, scale, q, k, v, g, beta, saved, bufs, dO,
+                            dq, dk, dv, dg, dbeta, s);
+  }));
+  if (n_stages) *n_stages = clk.n;
+  return GDN_OK;
+}
+
+GDN_API int gdn_chunk_bwd(const gdn_problem* p, const uint16_t* q, const uint16_t* k,
+                          const uint16_t* v, const float* g, const float* beta,
+                          const uint16_t* saved, const uint16_t* dO, const float* dhT,
+                          uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dg, float* dbeta,
+                          float* dh0, void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_bwd_impl(p, q, k, v, g, beta, saved, dO, dhT, dq, dk, dv, dg, dbeta, dh0, workspace,
+                        workspace_bytes, stream, nullptr, nullptr);
+}
+
+GDN_API int gdn_chunk_bwd_timed(const gdn_problem* p, const uint16_t* q, const uint16_t* k,
+                                const uint16_t* v, const float* g, const float* beta,
+                                const uint16_t* saved, const uint16_t* dO, const float* dhT,
+                                uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dg,
+                                float* dbeta, float* dh0, void* workspace,
+                                size_t workspace_bytes, void* stream, void* const* events,
+                                int* n_stages) {
+  if (!events || !n_stages) return GDN_ERR_NULL;
+  return chunk_bwd_impl(p, q, k, v, g, beta, saved, dO, dhT, dq, dk, dv, dg, dbeta, dh0, workspace,
+                        workspace_bytes, stream, events, n_stages);
+}
+
+GDN_API const char* gdn_stage_name(int op, int stage) {
+  static const char* fwd[] = {"chunk_table", "chunk_prep", "fwd_scan"};
+  static const char* bwd[] = {"chunk_table", "chunk_prep_bwd", "bwd_dh_scan", "bwd_chunk"};
+  if (op == 0 && stage >= 0 && stage < 3) return fwd[stage];
+  if (op == 1 && stage >= 0 && stage < 4) return bwd[stage];
+  return "";
+}
+
+GDN_API int gdn_recurrent_step(int32_t N, int32_t H, int32_t HV, int32_t K, int32_t V, float scale,
+                               const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               const uint16_t* a, const uint16_t* b, const float* A_log,
+                               const float* dt_bias, float* state_pool, int32_t slots,
+                               const int32_t* ssm_state_indices, const int32_t* indices_host,
+                               uint16_t* o, void* stream) {
+  if (N < 0 || H <= 0 || HV <= 0 || K <= 0 || V <= 0 || slots < 0) return GDN_ERR_SHAPE;
+  if (K != kHead || V != kHead || HV % H != 0) return GDN_ERR_UNSUPPORTED;
+  if ((int64_t)N * HV > (int64_t)INT32_MAX) return GDN_ERR_SHAPE;
+  if (N == 0) return GDN_OK;
+  if (!q || !k || !v || !a || !b || !A_log || !state_pool || !ssm_state_indices || !o)
+    return GDN_ERR_NULL;
+  if (!aligned16(state_pool) || !aligned16(o) || ((uintptr_t)q & 3u) || ((uintptr_t)k & 3u))
+    return GDN_ERR_ALIGN;
+  if (indices_host) {
+    std::vector<int32_t> act;
+    act.reserve(N);
+    for (int n = 0; n < N; ++n) {
+      const int32_t x = indices_host[n];
+      if (x <= 0) continue;  // null block or negative: skipped, never an error
+      if (x >= slots) return GDN_ERR_INDEX;
+      act.push_back(x);
+    }
+    std::sort(act.begin(), act.end());
+    if (std::adjacent_find(act.begin(), act.end()) != act.end()) return GDN_ERR_INDEX;
+  }
+  const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)K);
+  if (launch_decode_step(N, H, HV, sc, q, k, v, a, b, A_log, dt_bias, state_pool, slots,
+                         ssm_state_indices, o, reinterpret_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return GDN_ERR_HIP;
+  return GDN_OK;
+}

@@ -1,0 +1,212 @@
+// Forward state scan with the fused output of the chunked gated delta rule.
+//
+// Per chunk, with h = S^T the K x V start state (fp32, kept in registers):
+//   D  = U - W h                     corrected values of the chunk
+//   O  = Q_g h + P D                 inter-chunk plus intra-chunk output
+//   h <- e^gamma_L h + K_bwd^T D     state at the next chunk's start
+// (the chunk form of the recurrence; the scan and the output are the
+// forward stages named on the cake_gdn page, miles PR #3597, "What the
+// commits add"; the start state of every chunk is stored in bf16 for the
+// backward while the running state stays fp32, as its "Summary" requires).
+// For the backward each chunk also saves D, so that the gradient kernel
+// never has to rebuild it from the other layout of the state.
+//
+// The columns of the state (value dims) evolve independently, so one chain
+// (sequence, value head) is split into 128/VB value blocks, each its own
+// workgroup: with VB = 32 a 4 x 4096 pack at 32 value heads launches 512
+// workgroups. Block b runs on XCD b % 8; the value blocks of one chain get
+// the same b % 8 so they share that XCD's L2 for the chunk operands they all
+// read. All operands come straight from global memory in MFMA fragment
+// layout (16 bytes per lane per operand); only S (bf16) and D pass through
+// LDS, where every wave needs all of them.
+#include "gdn_common.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+template <int VB>
+__global__ __launch_bounds__(256) void fwd_scan_kernel(
+    const int32_t* __restrict__ seq_first, int N, int HV, int NC,
+    const ChunkInfo* __restrict__ table, PrepOut prep, const float* __restrict__ h0,
+    uint16_t* __restrict__ o, float* __restrict__ hT, uint16_t* __restrict__ saved) {
+  constexpr int NVB = kHead / VB;  // value blocks per head
+  constexpr int VT = VB / 16;      // 16-wide value tiles per block
+  constexpr int SP = 136;          // LDS pitch of S rows (bf16)
+  constexpr int DP = 72;           // LDS pitch of D^T rows (bf16)
+
+  const int b = blockIdx.x;
+  const int xcd = b & 7, slot = b >> 3;
+  const int vb = slot % NVB;
+  const int chain = (slot / NVB) * 8 + xcd;
+  if (chain >= N * HV) return;
+  const int seq = chain / HV, hv = chain - seq * HV;
+  const int v0 = vb * VB;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, kq = lane >> 4;
+
+  __shared__ __align__(16) uint16_t Ss[VB * SP];  // S[v][k] of the chunk start (bf16)
+  __shared__ __align__(16) uint16_t Ds[VB * DP];  // D^T[v][tok] (bf16)
+
+  // h[dt][vt][r] = h[k = 16 (2 wave + dt) + 4 kq + r][v = v0 + 16 vt + li]
+  f32x4 h[2][VT];
+  const size_t state_base = ((size_t)seq * HV + hv) * kHead * kHead;
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt) {
+      const int kk = 16 * (2 * wave + dt) + 4 * kq;
+      const int vv = v0 + 16 * vt + li;
+      if (h0) {
+        const float4 x = *reinterpret_cast<const float4*>(h0 + state_base + (size_t)vv * kHead + kk);
+        h[dt][vt] = f32x4{x.x, x.y, x.z, x.w};
+      } else {
+        h[dt][vt] = zero4();
+      }
+    }
+
+  const int c_begin = seq_first[seq], c_end = seq_first[seq + 1];
+  for (int c = c_begin; c < c_end; ++c) {
+    const ChunkInfo ci = table[c];
+    const size_t blk = (size_t)hv * NC + c;
+
+    // 1. chunk-start state -> LDS (bf16)
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) {
+        const int kk = 16 * (2 * wave + dt) + 4 * kq;
+        const int vl = 16 * vt + li;
+        *reinterpret_cast<uint2*>(&Ss[vl * SP + kk]) =
+            pack4_bf16(h[dt][vt][0], h[dt][vt][1], h[dt][vt][2], h[dt][vt][3]);
+      }
+    __syncthreads();
+    // saved for the backward: h = S^T as [k][v] rows (16-byte column gathers of Ss)
+    uint16_t* sv = saved ? saved + blk_saved(c, hv, HV) : nullptr;
+    if (sv) {
+      for (int e = tid; e < kHead * (VB / 8); e += 256) {
+        const int kk = e / (VB / 8), vg = e - kk * (VB / 8);
+        *reinterpret_cast<uint4*>(sv + kk * kHead + v0 + 8 * vg) = gather8(&Ss[(8 * vg) * SP + kk], SP);
+      }
+    }
+
+    // 2. D = U - W h; wave w owns tokens 16 w .. 16 w + 15
+    {
+      const uint16_t* Wb = prep.W + blk * 8192;
+      const uint16_t* Ub = prep.U + blk * 8192;
+      bf16x8 wa[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) wa[s] = ld8(Wb + (16 * wave + li) * kHead + 32 * s + 8 * kq);
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          acc = mfma(wa[s], ld8(&Ss[(16 * vt + li) * SP + 32 * s + 8 * kq]), acc);
+        // acc[r] = (W h)[t = 16 w + 4 kq + r][v = 16 vt + li]
+        const uint2 u = *reinterpret_cast<const uint2*>(Ub + (size_t)(v0 + 16 * vt + li) * 64 +
+                                                        16 * wave + 4 * kq);
+        *reinterpret_cast<uint2*>(&Ds[(16 * vt + li) * DP + 16 * wave + 4 * kq]) =
+            pack4_bf16(bf2f(u.x & 0xffffu) - acc[0], bf2f(u.x >> 16) - acc[1],
+                       bf2f(u.y & 0xffffu) - acc[2], bf2f(u.y >> 16) - acc[3]);
+      }
+    }
+    __syncthreads();
+    // saved for the backward: D as [tok][v] rows
+    if (sv) {
+      for (int e = tid; e < kChunk * (VB / 8); e += 256) {
+        const int t = e / (VB / 8), vg = e - t * (VB / 8);
+        *reinterpret_cast<uint4*>(sv + kSavedH + t * kHead + v0 + 8 * vg) =
+            gather8(&Ds[(8 * vg) * DP + t], DP);
+      }
+    }
+
+    // 3. O^T = S Q_g^T + D^T P^T; wave w owns tokens 16 w .. 16 w + 15
+    {
+      const uint16_t* Qb = prep.Qg + blk * 8192;
+      const uint16_t* Pb = prep.P + blk * 4096;
+      bf16x8 qa[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qa[s] = ld8(Qb + (16 * wave + li) * kHead + 32 * s + 8 * kq);
+      bf16x8 pa[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) pa[s] = ld8(Pb + (16 * wave + li) * 64 + 32 * s + 8 * kq);
+      const int tl = 16 * wave + li;
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          acc = mfma(ld8(&Ss[(16 * vt + li) * SP + 32 * s + 8 * kq]), qa[s], acc);
+        // P is lower triangular: tokens j > 16 w + 15 contribute nothing
+        acc = mfma(ld8(&Ds[(16 * vt + li) * DP + 8 * kq]), pa[0], acc);
+        if (wave >= 2) acc = mfma(ld8(&Ds[(16 * vt + li) * DP + 32 + 8 * kq]), pa[1], acc);
+        // acc[r] = O[t = t0 + 16 w + li][v = v0 + 16 vt + 4 kq + r]
+        if (tl < ci.len)
+          *reinterpret_cast<uint2*>(o + ((size_t)(ci.t0 + tl) * HV + hv) * kHead + v0 + 16 * vt +
+                                    4 * kq) = pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
+      }
+    }
+
+    // 4. h <- e^gamma_L h + K_bwd^T D; wave w owns key rows 32 w .. 32 w + 31
+    {
+      const uint16_t* Kb = prep.Kb + blk * 8192;
+      const float gl = prep.gL[blk];
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        bf16x8 ka[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          ka[s] = ld8(Kb + (16 * (2 * wave + dt) + li) * 64 + 32 * s + 8 * kq);
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt) {
+          f32x4 acc = h[dt][vt] * gl;
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            acc = mfma(ka[s], ld8(&Ds[(16 * vt + li) * DP + 32 * s + 8 * kq]), acc);
+          h[dt][vt] = acc;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (hT) {
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) {
+        const int kk = 16 * (2 * wave + dt) + 4 * kq;
+        const int vv = v0 + 16 * vt + li;
+        *reinterpret_cast<float4*>(hT + state_base + (size_t)vv * kHead + kk) =
+            make_float4(h[dt][vt][0], h[dt][vt][1], h[dt][vt][2], h[dt][vt][3]);
+      }
+  }
+}
+
+__global__ __launch_bounds__(256) void state_copy_kernel(const float* __restrict__ src,
+                                                         float* __restrict__ dst, size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
+constexpr int kFwdVB = 32;
+
+hipError_t launch_fwd_scan(const int32_t* seq_first, int N, int HV, int NC,
+                           const ChunkInfo* table, const PrepOut& prep, const float* h0,
+                           uint16_t* o, float* hT, uint16_t* saved, hipStream_t stream) {
+  const long chains = (long)N * HV;
+  const long groups = (chains + 7) / 8;
+  const long blocks = groups * 8 * (kHead / kFwdVB);
+  hipLaunchKernelGGL(fwd_scan_kernel<kFwdVB>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     seq_first, N, HV, NC, table, prep, h0, o, hT, saved);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_copy(const float* src, float* dst, size_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     src, dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,453 @@
+// Chunk table and the per-chunk WY pass of the chunked gated delta rule.
+//
+// Chunk form (one sequence, one value head, chunk of L <= 64 tokens, start
+// state h = S^T of size K x V):
+//   gamma   = within-chunk inclusive cumsum of g                (fp32)
+//   A_ij    = beta_i e^(gamma_i - gamma_j) k^_i . k^_j, i > j
+//   T       = (I + A)^-1                                        (fp32)
+//   W       = T diag(beta e^gamma) K^,   U = T diag(beta) V
+//   P_ij    = e^(gamma_i - gamma_j) q~_i . k^_j, i >= j
+//   Q_g     = diag(e^gamma) Q~,   K_bwd = diag(e^(gamma_L - gamma)) K^
+// The state-dependent part (D = U - W h, O = Q_g h + P D,
+// h' = e^gamma_L h + K_bwd^T D) runs in the scan kernels. This is the
+// WY / UT-transform pass that the cake_gdn page (miles PR #3597, "What the
+// commits add") lists before its forward state scan, and the chunk
+// transition h' = (e^gamma_L I - K_bwd^T W) h + K_bwd^T U written on the
+// maxtext page ("Qwen3.5-397B RL trainer on 128 v7x", the gdn_cp_m_scan
+// commit). Chunks restart at each sequence start; the last chunk of a
+// sequence may be short and is zero-padded, which leaves every product exact.
+//
+// One workgroup (4 waves) handles one chunk of one key head: q and k are
+// normalised once and K^K^T / Q~K^T are formed once on MFMA, then each value
+// head of the key head gets its gates, A, T and the products above. Only
+// e^x of x <= 0 (i >= j) is formed, so strong decays underflow to 0.
+//
+// Outputs per (value head, chunk) block, bf16 unless noted, in the layouts
+// the scans read with one 16-byte load per MFMA operand:
+//            forward scan (kBwd = false)     dh scan (kBwd = true)
+//   W        [64 tok][128 k]                 W^T   [128 k][64 tok]
+//   U        U^T [128 v][64 tok]             (not written)
+//   Q_g      [64 tok][128 k]                 Q_g^T [128 k][64 tok]
+//   P        [64 i][64 j]                    P^T   [64 j][64 i]
+//   K_bwd    K_bwd^T [128 k][64 tok]         K_bwd [64 tok][128 k]
+//   gL       e^gamma_L (fp32)                same
+#include "gdn_common.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+__global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t* __restrict__ cu, int N,
+                                                          int T, int NC,
+                                                          ChunkInfo* __restrict__ table,
+                                                          int32_t* __restrict__ seq_first) {
+  __shared__ int s_scan[256];
+  __shared__ int s_carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  for (int base = 0; base < N; base += 256) {
+    const int n = base + tid;
+    int cnt = 0, bos = 0, eos = 0;
+    if (n < N) {  // clamp so that device boundaries can never address outside [0, T)
+      bos = min(max(cu[n], 0), T);
+      eos = min(max(cu[n + 1], bos), T);
+      cnt = (eos - bos + kChunk - 1) / kChunk;
+    }
+    s_scan[tid] = cnt;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int add = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += add;
+      __syncthreads();
+    }
+    const int excl = s_carry + s_scan[tid] - cnt;
+    if (n < N) {
+      seq_first[n] = min(excl, NC);
+      for (int j = 0; j < cnt && excl + j < NC; ++j) {
+        ChunkInfo ci;
+        ci.seq = n;
+        ci.t0 = bos + kChunk * j;
+        ci.len = min(kChunk, eos - ci.t0);
+        ci.pos = j;
+        table[excl + j] = ci;
+      }
+    }
+    __syncthreads();
+    if (tid == 255) s_carry += s_scan[255];
+    __syncthreads();
+  }
+  const int total = min(s_carry, NC);
+  if (tid == 0) seq_first[N] = total;
+  for (int c = total + tid; c < NC; c += 256) {
+    ChunkInfo ci;
+    ci.seq = -1; ci.t0 = 0; ci.len = 0; ci.pos = 0;
+    table[c] = ci;
+  }
+}
+
+namespace {
+constexpr int KP = 136;  // LDS row pitch (bf16) of [64][128] tiles
+constexpr int TP = 72;   // LDS row pitch (bf16) of [128][64] tiles
+constexpr int FP = 68;   // LDS row pitch (fp32) of [64][64] tiles
+
+// lower-including 16x16 tile t (0..9) of a 64x64 matrix -> (row block, col block)
+__device__ __forceinline__ void lower_tile(int t, int& ib, int& jb) {
+  ib = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+  jb = t - (ib * (ib + 1)) / 2;
+}
+}  // namespace
+
+template <bool kBwd>
+__global__ __launch_bounds__(256) void chunk_prep_kernel(
+    const ChunkInfo* __restrict__ table, int NC, int H, int HV, float scale,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ g,
+    const float* __restrict__ beta, PrepOut out) {
+  const int c = blockIdx.x, h = blockIdx.y;
+  const ChunkInfo ci = table[c];
+  if (ci.seq < 0) return;
+  const int t0 = ci.t0, L = ci.len;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, kq = lane >> 4;
+
+  __shared__ __align__(16) uint16_t Ks[64 * KP];   // k^ rows (bf16)
+  __shared__ __align__(16) uint16_t Qs[64 * KP];   // q~ rows (bf16)
+  __shared__ __align__(16) float As[64 * FP];      // A (strictly lower)
+  __shared__ __align__(16) float Ts[64 * FP];      // T = (I + A)^-1
+  __shared__ __align__(16) uint16_t Xt[128 * TP];  // (beta e^gamma K^)^T, then (beta V)^T
+  __shared__ float gam[64], bet[64], eg[64], ebw[64];
+  __shared__ float Xs[3 * 256];
+
+  // ---- 1. load and L2-normalise q, k rows (thread: row tid/4, 32 columns)
+  {
+    const int r = tid >> 2, sg0 = (tid & 3) * 4;
+    uint4 kr[4], qr[4];
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (r < L) {
+        const size_t off = ((size_t)(t0 + r) * H + h) * kHead + (sg0 + j) * 8;
+        kr[j] = *reinterpret_cast<const uint4*>(k + off);
+        qr[j] = *reinterpret_cast<const uint4*>(q + off);
+      } else {
+        kr[j] = make_uint4(0, 0, 0, 0);
+        qr[j] = make_uint4(0, 0, 0, 0);
+      }
+      const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[j]);
+      const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qr[j]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a0 = bf2f(kw[e] & 0xffffu), a1 = bf2f(kw[e] >> 16);
+        const float b0 = bf2f(qw[e] & 0xffffu), b1 = bf2f(qw[e] >> 16);
+        sk += a0 * a0 + a1 * a1;
+        sq += b0 * b0 + b1 * b1;
+      }
+    }
+    sk = group_sum<4>(sk);
+    sq = group_sum<4>(sq);
+    const float nk = sqrtf(sk + kNormEps), nq = sqrtf(sq + kNormEps);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[j]);
+      const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qr[j]);
+      uint4 ko, qo;
+      uint32_t* kow = reinterpret_cast<uint32_t*>(&ko);
+      uint32_t* qow = reinterpret_cast<uint32_t*>(&qo);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kow[e] = (uint32_t)f2bf(bf2f(kw[e] & 0xffffu) / nk) |
+                 ((uint32_t)f2bf(bf2f(kw[e] >> 16) / nk) << 16);
+        qow[e] = (uint32_t)f2bf((bf2f(qw[e] & 0xffffu) / nq) * scale) |
+                 ((uint32_t)f2bf((bf2f(qw[e] >> 16) / nq) * scale) << 16);
+      }
+      *reinterpret_cast<uint4*>(&Ks[r * KP + (sg0 + j) * 8]) = ko;
+      *reinterpret_cast<uint4*>(&Qs[r * KP + (sg0 + j) * 8]) = qo;
+    }
+  }
+  __syncthreads();
+
+  const int G = HV / H;
+  for (int jg = 0; jg < G; ++jg) {
+    const int hv = h * G + jg;
+    const size_t blk = (size_t)hv * NC + c;
+
+    // ---- 2. gates: gamma = inclusive cumsum of g inside the chunk
+    if (wave == 0) {
+      float gv = lane < L ? g[(size_t)(t0 + lane) * HV + hv] : 0.f;
+      const float bv = lane < L ? beta[(size_t)(t0 + lane) * HV + hv] : 0.f;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(gv, off, 64);
+        if (lane >= off) gv += y;
+      }
+      gam[lane] = gv;
+      bet[lane] = bv;
+      const float gl = __shfl(gv, L - 1, 64);
+      eg[lane] = expf(gv);
+      ebw[lane] = lane < L ? expf(gl - gv) : 0.f;
+      if (lane == 0) out.gL[blk] = expf(gl);
+    }
+    __syncthreads();
+
+    // ---- 3. A (fp32, LDS) and P (bf16, global): 10 lower tiles of A, 16 tiles of P
+    uint16_t* Pb = out.P + blk * (64 * 64);
+    for (int job = wave; job < 26; job += 4) {
+      if (job < 10) {
+        int ib, jb;
+        lower_tile(job, ib, jb);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          acc = mfma(ld8(&Ks[(16 * ib + li) * KP + 32 * s + 8 * kq]),
+                     ld8(&Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), acc);
+        const int j = 16 * jb + li;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * ib + 4 * kq + r;
+          As[i * FP + j] = i > j ? bet[i] * expf(gam[i] - gam[j]) * acc[r] : 0.f;
+        }
+      } else {
+        const int pt = job - 10, ib = pt >> 2, jb = pt & 3;  // P tile (row block ib, col block jb)
+        if (!kBwd) {
+          // C = K^ Q~^T tile: C[4kq+r][li] = P-row i = 16 ib + li, cols j = 16 jb + 4kq + r
+          f32x4 acc = zero4();
+          if (jb <= ib) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              acc = mfma(ld8(&Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]),
+                         ld8(&Qs[(16 * ib + li) * KP + 32 * s + 8 * kq]), acc);
+          }
+          const int i = 16 * ib + li;
+          float pv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = 16 * jb + 4 * kq + r;
+            pv[r] = i >= j ? expf(gam[i] - gam[j]) * acc[r] : 0.f;
+          }
+          *reinterpret_cast<uint2*>(Pb + i * 64 + 16 * jb + 4 * kq) =
+              pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
+        } else {
+          // C = Q~ K^T tile: C[4kq+r][li] = P[i = 16 ib + 4kq + r][j = 16 jb + li] -> P^T[j][i..i+3]
+          f32x4 acc = zero4();
+          if (jb <= ib) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              acc = mfma(ld8(&Qs[(16 * ib + li) * KP + 32 * s + 8 * kq]),
+                         ld8(&Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), acc);
+          }
+          const int j = 16 * jb + li;
+          float pv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * ib + 4 * kq + r;
+            pv[r] = i >= j ? expf(gam[i] - gam[j]) * acc[r] : 0.f;
+          }
+          *reinterpret_cast<uint2*>(Pb + j * 64 + 16 * ib + 4 * kq) =
+              pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
+        }
+      }
+    }
+    // zero the strictly upper blocks of T
+    for (int e = tid; e < 64 * 64; e += 256) {
+      const int i = e >> 6, j = e & 63;
+      if ((j >> 4) > (i >> 4)) Ts[i * FP + j] = 0.f;
+    }
+    __syncthreads();
+
+    // ---- 4. T = (I + A)^-1: diagonal 16x16 blocks by forward substitution ...
+    if (tid < 64) {
+      const int o16 = 16 * (tid >> 4), jc = tid & 15;
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float acc = i == jc ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < i; ++m) acc -= As[(o16 + i) * FP + o16 + m] * x[m];
+        x[i] = acc;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Ts[(o16 + i) * FP + o16 + jc] = x[i];
+    }
+    __syncthreads();
+    // ... then block rows: T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj
+    {
+      const int r = tid >> 4, cc = tid & 15;
+      for (int ib = 1; ib < 4; ++ib) {
+        for (int jb = 0; jb < ib; ++jb) {
+          float acc = 0.f;
+          for (int m = 16 * jb; m < 16 * ib; ++m)
+            acc += As[(16 * ib + r) * FP + m] * Ts[m * FP + 16 * jb + cc];
+          Xs[jb * 256 + r * 16 + cc] = acc;
+        }
+        __syncthreads();
+        for (int jb = 0; jb < ib; ++jb) {
+          float acc = 0.f;
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            acc += Ts[(16 * ib + r) * FP + 16 * ib + u] * Xs[jb * 256 + u * 16 + cc];
+          Ts[(16 * ib + r) * FP + 16 * jb + cc] = -acc;
+        }
+        __syncthreads();
+      }
+    }
+
+    // ---- 5. Xt = (beta e^gamma K^)^T  [k][tok]; Q_g and K_bwd to global
+    for (int e = tid; e < 128 * 8; e += 256) {
+      const int d = e >> 3, tg = e & 7;
+      uint4 o4;
+      uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int ta = 8 * tg + 2 * u, tb = ta + 1;
+        ow[u] = (uint32_t)f2bf(bet[ta] * eg[ta] * bf2f(Ks[ta * KP + d])) |
+                ((uint32_t)f2bf(bet[tb] * eg[tb] * bf2f(Ks[tb * KP + d])) << 16);
+      }
+      *reinterpret_cast<uint4*>(&Xt[d * TP + 8 * tg]) = o4;
+    }
+    {
+      uint16_t* Qgb = out.Qg + blk * 8192;
+      uint16_t* Kbb = out.Kb + blk * 8192;
+      if (!kBwd) {
+        // Q_g [tok][k] (row segments) and K_bwd^T [k][tok] (column gathers)
+        for (int e = tid; e < 64 * 16; e += 256) {
+          const int t = e >> 4, sg = e & 15;
+          const uint4 x = *reinterpret_cast<const uint4*>(&Qs[t * KP + sg * 8]);
+          const uint32_t* xw = reinterpret_cast<const uint32_t*>(&x);
+          uint4 o4;
+          uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            ow[u] = (uint32_t)f2bf(eg[t] * bf2f(xw[u] & 0xffffu)) |
+                    ((uint32_t)f2bf(eg[t] * bf2f(xw[u] >> 16)) << 16);
+          *reinterpret_cast<uint4*>(Qgb + t * 128 + sg * 8) = o4;
+        }
+        for (int e = tid; e < 128 * 8; e += 256) {
+          const int d = e >> 3, tg = e & 7;
+          uint4 o4;
+          uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int ta = 8 * tg + 2 * u, tb = ta + 1;
+            ow[u] = (uint32_t)f2bf(ebw[ta] * bf2f(Ks[ta * KP + d])) |
+                    ((uint32_t)f2bf(ebw[tb] * bf2f(Ks[tb * KP + d])) << 16);
+          }
+          *reinterpret_cast<uint4*>(Kbb + d * 64 + 8 * tg) = o4;
+        }
+      } else {
+        // Q_g^T [k][tok] (column gathers) and K_bwd [tok][k] (row segments)
+        for (int e = tid; e < 128 * 8; e += 256) {
+          const int d = e >> 3, tg = e & 7;
+          uint4 o4;
+          uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int ta = 8 * tg + 2 * u, tb = ta + 1;
+            ow[u] = (uint32_t)f2bf(eg[ta] * bf2f(Qs[ta * KP + d])) |
+                    ((uint32_t)f2bf(eg[tb] * bf2f(Qs[tb * KP + d])) << 16);
+          }
+          *reinterpret_cast<uint4*>(Qgb + d * 64 + 8 * tg) = o4;
+        }
+        for (int e = tid; e < 64 * 16; e += 256) {
+          const int t = e >> 4, sg = e & 15;
+          const uint4 x = *reinterpret_cast<const uint4*>(&Ks[t * KP + sg * 8]);
+          const uint32_t* xw = reinterpret_cast<const uint32_t*>(&x);
+          uint4 o4;
+          uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            ow[u] = (uint32_t)f2bf(ebw[t] * bf2f(xw[u] & 0xffffu)) |
+                    ((uint32_t)f2bf(ebw[t] * bf2f(xw[u] >> 16)) << 16);
+          *reinterpret_cast<uint4*>(Kbb + t * 128 + sg * 8) = o4;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- 6. W: 32 tiles of 16x16 over 4 waves, contraction over the chunk (2 steps)
+    {
+      uint16_t* Wb = out.W + blk * 8192;
+      for (int tt = wave; tt < 32; tt += 4) {
+        if (!kBwd) {
+          // C = Xt T^T: C[4kq+r][li] = W[t = 16 tb + li][k = 16 db + 4kq + r]
+          const int db = tt >> 2, tb = tt & 3;
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            acc = mfma(ld8(&Xt[(16 * db + li) * TP + 32 * s + 8 * kq]),
+                       cvt8(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq]), acc);
+          *reinterpret_cast<uint2*>(Wb + (16 * tb + li) * 128 + 16 * db + 4 * kq) =
+              pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
+        } else {
+          // C = T Xt^T: C[4kq+r][li] = W[t = 16 tb + 4kq + r][k = 16 db + li] -> W^T[k][t..t+3]
+          const int tb = tt >> 3, db = tt & 7;
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            acc = mfma(cvt8(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq]),
+                       ld8(&Xt[(16 * db + li) * TP + 32 * s + 8 * kq]), acc);
+          *reinterpret_cast<uint2*>(Wb + (16 * db + li) * 64 + 16 * tb + 4 * kq) =
+              pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
+        }
+      }
+    }
+
+    if (!kBwd) {
+      // ---- 7. U = T diag(beta) V, written as U^T [v][tok]
+      __syncthreads();  // Xt is rewritten
+      {
+        const int r = tid >> 2, sg0 = (tid & 3) * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint4 x = make_uint4(0, 0, 0, 0);
+          if (r < L) x = *reinterpret_cast<const uint4*>(v + ((size_t)(t0 + r) * HV + hv) * kHead +
+                                                           (sg0 + j) * 8);
+          const uint32_t* xw = reinterpret_cast<const uint32_t*>(&x);
+          const float br = bet[r];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int d = (sg0 + j) * 8 + 2 * e;
+            Xt[d * TP + r] = f2bf(br * bf2f(xw[e] & 0xffffu));
+            Xt[(d + 1) * TP + r] = f2bf(br * bf2f(xw[e] >> 16));
+          }
+        }
+      }
+      __syncthreads();
+      uint16_t* Ub = out.U + blk * 8192;
+      for (int tt = wave; tt < 32; tt += 4) {
+        // C = T Xt^T: C[4kq+r][li] = U[t = 16 tb + 4kq + r][v = 16 vb + li] -> U^T[v][t..t+3]
+        const int tb = tt >> 3, vb = tt & 7;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          acc = mfma(cvt8(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq]),
+                     ld8(&Xt[(16 * vb + li) * TP + 32 * s + 8 * kq]), acc);
+        *reinterpret_cast<uint2*>(Ub + (16 * vb + li) * 64 + 16 * tb + 4 * kq) =
+            pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
+      }
+    }
+    __syncthreads();  // gates, A, T and Xt are rewritten for the next value head
+  }
+}
+
+hipError_t launch_chunk_table(const int32_t* cu, int N, int T, int NC, ChunkInfo* table,
+                              int32_t* seq_first, hipStream_t stream) {
+  hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, stream, cu, N, T, NC, table,
+                     seq_first);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_prep(bool bwd_layout, const ChunkInfo* table, int NC, int H, int HV,
+                             float scale, const uint16_t* q, const uint16_t* k,
+                             const uint16_t* v, const float* g, const float* beta,
+                             const PrepOut& out, hipStream_t stream) {
+  if (bwd_layout)
+    hipLaunchKernelGGL(chunk_prep_kernel<true>, dim3(NC, H), dim3(256), 0, stream, table, NC, H,
+                       HV, scale, q, k, v, g, beta, out);
+  else
+    hipLaunchKernelGGL(chunk_prep_kernel<false>, dim3(NC, H), dim3(256), 0, stream, table, NC, H,
+                       HV, scale, q, k, v, g, beta, out);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,111 @@
+// Device helpers shared by the gfx950 kernels of the gated delta rule.
+//
+// MFMA fragment layout used throughout (v_mfma_f32_16x16x32_bf16, wave64):
+// lane l = 16*kq + i (i = l & 15, kq = l >> 4) supplies
+//   A[i][kb + 8*kq .. kb + 8*kq + 7]      (8 bf16, one 16-byte read)
+//   B[kb + 8*kq .. kb + 8*kq + 7][i]
+// and receives C[4*kq + r][i], r = 0..3. Every operand is therefore read as
+// 8 consecutive bf16 along the contraction axis, and the kernels keep each
+// operand in the memory layout that makes that read contiguous.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHead = 128;   // K = V
+constexpr int kChunk = 64;   // tokens per chunk
+constexpr float kNormEps = 1e-6f;
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest even.
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
+  uint2 r;
+  r.x = (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+  r.y = (uint32_t)f2bf(c) | ((uint32_t)f2bf(d) << 16);
+  return r;
+}
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// 8 fp32 from LDS/global -> bf16x8 (round to nearest even)
+__device__ __forceinline__ bf16x8 cvt8(const float* p) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  float4 b = *reinterpret_cast<const float4*>(p + 4);
+  bf16x8 r;
+  r[0] = (__bf16)a.x; r[1] = (__bf16)a.y; r[2] = (__bf16)a.z; r[3] = (__bf16)a.w;
+  r[4] = (__bf16)b.x; r[5] = (__bf16)b.y; r[6] = (__bf16)b.z; r[7] = (__bf16)b.w;
+  return r;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// 8 bf16 spaced `pitch` elements apart (a column of a row-major tile), packed
+// into 16 bytes.
+__device__ __forceinline__ uint4 gather8(const uint16_t* p, int pitch) {
+  uint4 r;
+  r.x = (uint32_t)p[0] | ((uint32_t)p[pitch] << 16);
+  r.y = (uint32_t)p[2 * pitch] | ((uint32_t)p[3 * pitch] << 16);
+  r.z = (uint32_t)p[4 * pitch] | ((uint32_t)p[5 * pitch] << 16);
+  r.w = (uint32_t)p[6 * pitch] | ((uint32_t)p[7 * pitch] << 16);
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 gather8_bf16(const uint16_t* p, int pitch) {
+  const uint4 r = gather8(p, pitch);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// 8 fp32 spaced `pitch` apart -> bf16x8
+__device__ __forceinline__ bf16x8 gather8_f32(const float* p, int pitch) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)p[e * pitch];
+  return r;
+}
+
+// Saved-for-backward block of one (chunk, value head): the chunk-start state
+// h = S^T as [k][v] bf16, then the chunk's D as [tok][v] bf16.
+constexpr int kSavedH = kHead * kHead;
+constexpr int kSavedBlock = kSavedH + kChunk * kHead;
+__device__ __host__ __forceinline__ size_t blk_saved(int c, int hv, int HV) {
+  return ((size_t)c * HV + hv) * kSavedBlock;
+}
+
+// Sum over the 64 lanes of a wave; every lane gets the total. Fixed order.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+// Sum over groups of `W` consecutive lanes (W a power of two <= 64).
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int m = W / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+// One chunk of the packed token axis: sequence, first token, length, and
+// the chunk's position inside its sequence. seq < 0 marks an unused slot.
+struct ChunkInfo {
+  int seq, t0, len, pos;
+};
+
+}  // namespace gdn

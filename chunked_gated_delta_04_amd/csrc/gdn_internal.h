@@ -1,0 +1,60 @@
+// Host-side declarations shared by the launchers and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_common.h"
+
+namespace gdn {
+
+// Per (value head, chunk) blocks written by the WY pass; block index
+// blk = hv * NC + c, so the chunks of one chain are contiguous.
+struct PrepOut {
+  uint16_t* W;   // 64 x 128 per block
+  uint16_t* U;   // 128 x 64 per block (forward layout only)
+  uint16_t* Qg;  // 64 x 128
+  uint16_t* P;   // 64 x 64
+  uint16_t* Kb;  // 128 x 64
+  float* gL;     // 1 per block
+};
+
+// Backward scratch per (value head, chunk) block, blk = hv * NC + c.
+struct BwdBufs {
+  uint16_t* dh;   // gradient of the chunk's end state, [k][v] (128 x 128)
+  uint16_t* dD;   // dD as [tok][v] (64 x 128)
+  uint16_t* dDT;  // dD as [v][tok] (128 x 64)
+};
+
+hipError_t launch_chunk_table(const int32_t* cu, int N, int T, int NC, ChunkInfo* table,
+                              int32_t* seq_first, hipStream_t stream);
+
+hipError_t launch_chunk_prep(bool bwd_layout, const ChunkInfo* table, int NC, int H, int HV,
+                             float scale, const uint16_t* q, const uint16_t* k,
+                             const uint16_t* v, const float* g, const float* beta,
+                             const PrepOut& out, hipStream_t stream);
+
+hipError_t launch_fwd_scan(const int32_t* seq_first, int N, int HV, int NC,
+                           const ChunkInfo* table, const PrepOut& prep, const float* h0,
+                           uint16_t* o, float* hT, uint16_t* saved, hipStream_t stream);
+
+hipError_t launch_bwd_dh_scan(const int32_t* seq_first, int N, int HV, int NC,
+                              const ChunkInfo* table, const PrepOut& prep, const uint16_t* dO,
+                              const float* dhT, float* dh0, const BwdBufs& bufs,
+                              hipStream_t stream);
+
+hipError_t launch_bwd_chunk(const ChunkInfo* table, int NC, int H, int HV, float scale,
+                            const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const float* g, const float* beta, const uint16_t* saved,
+                            const BwdBufs& bufs, const uint16_t* dO, uint16_t* dq, uint16_t* dk,
+                            uint16_t* dv, float* dg, float* dbeta, hipStream_t stream);
+
+hipError_t launch_state_copy(const float* src, float* dst, size_t n, hipStream_t stream);
+
+hipError_t launch_decode_step(int N, int H, int HV, float scale, const uint16_t* q,
+                              const uint16_t* k, const uint16_t* v, const uint16_t* a,
+                              const uint16_t* b, const float* A_log, const float* dt_bias,
+                              float* pool, int slots, const int32_t* idx, uint16_t* o,
+                              hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,273 @@
+"""Thin Python binding of libgdn.so (the C ABI declared in include/gdn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library. Functions named gdn_* mirror the C entry points one
+for one and take torch tensors (or None for a NULL pointer); the lower-case
+helpers at the end allocate outputs and workspaces with torch and call them.
+
+The library is loaded from this package directory. If it is missing, importing
+this module raises ImportError: there is no fallback of any kind.
+"""
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"{_LIB_PATH} is not built; run `python -m chunked_gated_delta_04_amd.build` "
+        "(hipcc, gfx950) first")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+GDN_OK = 0
+STATUS_NAMES = {
+    0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
+    4: "GDN_ERR_SEQLENS", 5: "GDN_ERR_INDEX", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP",
+    8: "GDN_ERR_ALIGN",
+}
+EXPORTED = (
+    "gdn_status_string", "gdn_num_chunks", "gdn_chunk_saved_size",
+    "gdn_chunk_fwd_workspace_size", "gdn_chunk_bwd_workspace_size",
+    "gdn_chunk_fwd", "gdn_chunk_bwd", "gdn_recurrent_step",
+    "gdn_chunk_fwd_timed", "gdn_chunk_bwd_timed", "gdn_stage_name",
+)
+GDN_MAX_STAGES = 8
+
+
+class GdnProblem(ctypes.Structure):
+    _fields_ = [
+        ("N", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("HV", ctypes.c_int32), ("K", ctypes.c_int32), ("V", ctypes.c_int32),
+        ("chunk", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p),
+    ]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} "
+                         f"({gdn_status_string(status)})")
+
+
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_i32 = ctypes.c_int32
+_P = ctypes.POINTER(GdnProblem)
+
+_lib.gdn_status_string.restype = ctypes.c_char_p
+_lib.gdn_status_string.argtypes = [ctypes.c_int]
+_lib.gdn_num_chunks.restype = ctypes.c_int64
+_lib.gdn_num_chunks.argtypes = [_P]
+for _n in ("gdn_chunk_saved_size", "gdn_chunk_fwd_workspace_size", "gdn_chunk_bwd_workspace_size"):
+    getattr(_lib, _n).restype = _sz
+    getattr(_lib, _n).argtypes = [_P]
+_lib.gdn_chunk_fwd.restype = ctypes.c_int
+_lib.gdn_chunk_fwd.argtypes = [_P] + [_vp] * 10 + [_sz, _vp]
+_lib.gdn_chunk_bwd.restype = ctypes.c_int
+_lib.gdn_chunk_bwd.argtypes = [_P] + [_vp] * 15 + [_sz, _vp]
+_lib.gdn_chunk_fwd_timed.restype = ctypes.c_int
+_lib.gdn_chunk_fwd_timed.argtypes = ([_P] + [_vp] * 10 + [_sz, _vp] +
+                                     [ctypes.POINTER(_vp), ctypes.POINTER(ctypes.c_int)])
+_lib.gdn_chunk_bwd_timed.restype = ctypes.c_int
+_lib.gdn_chunk_bwd_timed.argtypes = ([_P] + [_vp] * 15 + [_sz, _vp] +
+                                     [ctypes.POINTER(_vp), ctypes.POINTER(ctypes.c_int)])
+_lib.gdn_stage_name.restype = ctypes.c_char_p
+_lib.gdn_stage_name.argtypes = [ctypes.c_int, ctypes.c_int]
+_lib.gdn_recurrent_step.restype = ctypes.c_int
+_lib.gdn_recurrent_step.argtypes = ([_i32] * 5 + [ctypes.c_float] + [_vp] * 8 + [_i32] +
+                                    [_vp] * 4)
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    """Device pointer of a contiguous tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor or None")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return stream
+
+
+def make_problem(N, T, H, HV, cu_seqlens, cu_seqlens_host=None, scale=0.0, K=128, V=128,
+                 chunk=64):
+    """Build the gdn_problem descriptor. cu_seqlens: int32 device tensor [N+1];
+    cu_seqlens_host: optional int32 CPU tensor [N+1] (kept alive by the caller)."""
+    p = GdnProblem()
+    p.N, p.T, p.H, p.HV, p.K, p.V, p.chunk = N, T, H, HV, K, V, chunk
+    p.scale = float(scale)
+    p.cu_seqlens = _ptr(cu_seqlens, torch.int32, "cu_seqlens")
+    if cu_seqlens_host is not None:
+        if cu_seqlens_host.device.type != "cpu":
+            raise ValueError("cu_seqlens_host must be a CPU tensor")
+        p.cu_seqlens_host = _ptr(cu_seqlens_host, torch.int32, "cu_seqlens_host")
+    return p
+
+
+def gdn_status_string(status):
+    return _lib.gdn_status_string(int(status)).decode()
+
+
+def gdn_num_chunks(problem):
+    return int(_lib.gdn_num_chunks(ctypes.byref(problem)))
+
+
+def gdn_chunk_saved_size(problem):
+    return int(_lib.gdn_chunk_saved_size(ctypes.byref(problem)))
+
+
+def gdn_chunk_fwd_workspace_size(problem):
+    return int(_lib.gdn_chunk_fwd_workspace_size(ctypes.byref(problem)))
+
+
+def gdn_chunk_bwd_workspace_size(problem):
+    return int(_lib.gdn_chunk_bwd_workspace_size(ctypes.byref(problem)))
+
+
+def _check(status, where):
+    if status != GDN_OK:
+        raise GdnError(status, where)
+
+
+def gdn_chunk_fwd(problem, q, k, v, g, beta, h0, o, hT, saved, workspace, stream=None):
+    bf, f32 = torch.bfloat16, torch.float32
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.gdn_chunk_fwd(
+        ctypes.byref(problem), _ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"),
+        _ptr(g, f32, "g"), _ptr(beta, f32, "beta"), _ptr(h0, f32, "h0"), _ptr(o, bf, "o"),
+        _ptr(hT, f32, "hT"), _ptr(saved, None, "saved"), _ptr(workspace, None, "workspace"),
+        ws_bytes, _stream(stream))
+    _check(st, "gdn_chunk_fwd")
+
+
+def gdn_stage_name(op, stage):
+    return _lib.gdn_stage_name(int(op), int(stage)).decode()
+
+
+def gdn_chunk_fwd_timed(problem, q, k, v, g, beta, h0, o, hT, saved, workspace, events,
+                        stream=None):
+    """gdn_chunk_fwd recording events (a ctypes array of 2*GDN_MAX_STAGES hipEvent_t)
+    around each stage. Returns the number of stages launched."""
+    bf, f32 = torch.bfloat16, torch.float32
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    n = ctypes.c_int(0)
+    st = _lib.gdn_chunk_fwd_timed(
+        ctypes.byref(problem), _ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"),
+        _ptr(g, f32, "g"), _ptr(beta, f32, "beta"), _ptr(h0, f32, "h0"), _ptr(o, bf, "o"),
+        _ptr(hT, f32, "hT"), _ptr(saved, None, "saved"), _ptr(workspace, None, "workspace"),
+        ws_bytes, _stream(stream), events, ctypes.byref(n))
+    _check(st, "gdn_chunk_fwd_timed")
+    return n.value
+
+
+def gdn_chunk_bwd_timed(problem, q, k, v, g, beta, saved, dO, dhT, dq, dk, dv, dg, dbeta, dh0,
+                        workspace, events, stream=None):
+    bf, f32 = torch.bfloat16, torch.float32
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    n = ctypes.c_int(0)
+    st = _lib.gdn_chunk_bwd_timed(
+        ctypes.byref(problem), _ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"),
+        _ptr(g, f32, "g"), _ptr(beta, f32, "beta"), _ptr(saved, None, "saved"),
+        _ptr(dO, bf, "dO"), _ptr(dhT, f32, "dhT"), _ptr(dq, bf, "dq"), _ptr(dk, bf, "dk"),
+        _ptr(dv, bf, "dv"), _ptr(dg, f32, "dg"), _ptr(dbeta, f32, "dbeta"),
+        _ptr(dh0, f32, "dh0"), _ptr(workspace, None, "workspace"), ws_bytes, _stream(stream),
+        events, ctypes.byref(n))
+    _check(st, "gdn_chunk_bwd_timed")
+    return n.value
+
+
+def gdn_chunk_bwd(problem, q, k, v, g, beta, saved, dO, dhT, dq, dk, dv, dg, dbeta, dh0,
+                  workspace, stream=None):
+    bf, f32 = torch.bfloat16, torch.float32
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.gdn_chunk_bwd(
+        ctypes.byref(problem), _ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"),
+        _ptr(g, f32, "g"), _ptr(beta, f32, "beta"), _ptr(saved, None, "saved"),
+        _ptr(dO, bf, "dO"), _ptr(dhT, f32, "dhT"), _ptr(dq, bf, "dq"), _ptr(dk, bf, "dk"),
+        _ptr(dv, bf, "dv"), _ptr(dg, f32, "dg"), _ptr(dbeta, f32, "dbeta"),
+        _ptr(dh0, f32, "dh0"), _ptr(workspace, None, "workspace"), ws_bytes, _stream(stream))
+    _check(st, "gdn_chunk_bwd")
+
+
+def gdn_recurrent_step(N, H, HV, K, V, scale, q, k, v, a, b, A_log, dt_bias, state_pool, slots,
+                       ssm_state_indices, indices_host, o, stream=None):
+    bf, f32 = torch.bfloat16, torch.float32
+    st = _lib.gdn_recurrent_step(
+        N, H, HV, K, V, float(scale), _ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"),
+        _ptr(a, bf, "a"), _ptr(b, bf, "b"), _ptr(A_log, f32, "A_log"),
+        _ptr(dt_bias, f32, "dt_bias"), _ptr(state_pool, f32, "state_pool"), slots,
+        _ptr(ssm_state_indices, torch.int32, "ssm_state_indices"),
+        _ptr(indices_host, torch.int32, "indices_host"), _ptr(o, bf, "o"), _stream(stream))
+    _check(st, "gdn_recurrent_step")
+
+
+# ---------------------------------------------------------------- allocating helpers
+def _ws(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, scale=0.0, cu_seqlens_host=None,
+              save_for_backward=False, output_final_state=True, stream=None):
+    """Allocate outputs and workspace and run gdn_chunk_fwd.
+
+    q, k [T, H, 128] bf16; v [T, HV, 128] bf16; g, beta [T, HV] fp32 (device);
+    cu_seqlens [N+1] int32 (device). Returns (o, hT or None, saved or None).
+    """
+    T, H, _ = q.shape
+    HV = v.shape[1]
+    N = cu_seqlens.numel() - 1
+    p = make_problem(N, T, H, HV, cu_seqlens, cu_seqlens_host, scale)
+    dev = q.device
+    o = torch.empty(T, HV, 128, dtype=torch.bfloat16, device=dev)
+    hT = torch.empty(N, HV, 128, 128, dtype=torch.float32, device=dev) if output_final_state else None
+    saved = _ws(gdn_chunk_saved_size(p), dev) if save_for_backward else None
+    ws = _ws(gdn_chunk_fwd_workspace_size(p), dev)
+    gdn_chunk_fwd(p, q, k, v, g, beta, h0, o, hT, saved, ws, stream)
+    return o, hT, saved
+
+
+def chunk_bwd(q, k, v, g, beta, cu_seqlens, saved, dO, dhT=None, scale=0.0,
+              cu_seqlens_host=None, want_dh0=True, stream=None):
+    """Allocate gradients and workspace and run gdn_chunk_bwd.
+
+    Returns dict dq, dk, dv, dg, dbeta, dh0 (dh0 None unless want_dh0).
+    """
+    T, H, _ = q.shape
+    HV = v.shape[1]
+    N = cu_seqlens.numel() - 1
+    p = make_problem(N, T, H, HV, cu_seqlens, cu_seqlens_host, scale)
+    dev = q.device
+    out = dict(
+        dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+        dg=torch.empty(T, HV, dtype=torch.float32, device=dev),
+        dbeta=torch.empty(T, HV, dtype=torch.float32, device=dev),
+        dh0=torch.empty(N, HV, 128, 128, dtype=torch.float32, device=dev) if want_dh0 else None,
+    )
+    ws = _ws(gdn_chunk_bwd_workspace_size(p), dev)
+    gdn_chunk_bwd(p, q, k, v, g, beta, saved, dO, dhT, out["dq"], out["dk"], out["dv"],
+                  out["dg"], out["dbeta"], out["dh0"], ws, stream)
+    return out
+
+
+def recurrent_step(q, k, v, a, b, A_log, dt_bias, state_pool, ssm_state_indices,
+                   indices_host=None, scale=0.0, stream=None):
+    """Allocate o and run gdn_recurrent_step (the pool is updated in place)."""
+    N, H, K = q.shape
+    HV, V = v.shape[1], v.shape[2]
+    o = torch.empty(N, HV, V, dtype=torch.bfloat16, device=q.device)
+    gdn_recurrent_step(N, H, HV, K, V, scale, q, k, v, a, b, A_log, dt_bias, state_pool,
+                       state_pool.shape[0], ssm_state_indices, indices_host, o, stream)
+    return o

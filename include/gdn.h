@@ -1,0 +1,212 @@
+/*
+ * gdn.h - C ABI of the gated delta rule library for MI355X (gfx950).
+ *
+ * The library computes the chunked gated delta rule, forward and backward,
+ * and its one-token recurrent decode step, on one GPU, with hand-written HIP
+ * kernels. Per sequence and value head the state S is a V x K fp32 matrix:
+ *
+ *   S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *   o_t = S_t q_t,
+ *
+ * where q and k are first divided by sqrt(sum(x*x) + 1e-6) in fp32, q is then
+ * multiplied by `scale` (K^-1/2 by default) and k is never scaled, and value
+ * head hv reads key head hv / (HV / H). Sources:
+ *   - the recurrence, the norm, the scale, the head grouping and the decode
+ *     gating: RL-Kernel PR #469 "[WS1][CUDA][Qwen3-Next] C6: GDN decode-step
+ *     goldens and recurrent/conv state contract", "What" section and the
+ *     agent note on where the kernel and the HF model disagree;
+ *   - the chunk contract (chunk 64, K = V = 128, bf16 q/k/v, fp32 g/beta,
+ *     varlen packing by cu_seqlens, in-kernel L2 norm, a call without tokens
+ *     passes the state through, extents checked before any launch):
+ *     "[Cake 1/13] gdn" (miles-ext-kernels PR #1), "API and flags" and
+ *     "Review items";
+ *   - the precision and determinism contract (fp32 running state across
+ *     chunks, per-chunk state stored bf16, no device atomics, repeated runs
+ *     bit-identical): "cake_gdn: deterministic chunked GDN training kernels"
+ *     (miles PR #3597), "Summary".
+ *
+ * Conventions for every entry point
+ *   - bf16 tensors are passed as uint16_t pointers holding bf16 bit patterns;
+ *     fp32 as float; indices as int32_t. All tensors are dense, row-major,
+ *     in the layouts stated per argument. Pointers are device pointers unless
+ *     the name ends in _host.
+ *   - `stream` is a hipStream_t (NULL: the null stream). Work is enqueued on
+ *     it and the call returns without synchronising.
+ *   - The caller owns every buffer. The library allocates nothing, frees
+ *     nothing and keeps no state between calls; calls on different streams
+ *     with disjoint buffers may run concurrently.
+ *   - Every argument error is returned before anything is enqueued. A launch
+ *     failure returns GDN_ERR_HIP; the outputs are then undefined.
+ *   - Tensor and workspace pointers must be 16-byte aligned (the decode q and
+ *     k rows 4-byte aligned), else GDN_ERR_ALIGN. Token tensors may be NULL
+ *     when T = 0.
+ *   - No kernel uses atomics: identical inputs, shapes and device give
+ *     bit-identical outputs.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  GDN_ERR_SHAPE = 2,       /* a negative or inconsistent extent                  */
+  GDN_ERR_UNSUPPORTED = 3, /* K or V != 128, chunk != 64, HV % H != 0            */
+  GDN_ERR_SEQLENS = 4,     /* cu_seqlens_host not 0 .. T and non-decreasing      */
+  GDN_ERR_INDEX = 5,       /* an active decode index >= slots, or repeated       */
+  GDN_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the size query      */
+  GDN_ERR_HIP = 7,         /* a HIP launch failed                                */
+  GDN_ERR_ALIGN = 8        /* a tensor or workspace pointer not 16-byte aligned  */
+} gdn_status;
+
+/* Human-readable text of a status code; never NULL. */
+const char* gdn_status_string(int status);
+
+/* Problem description of one chunk call (forward or backward).
+ *   N      number of sequences packed along the token axis (N >= 0)
+ *   T      total tokens (T >= 0)
+ *   H      key heads of q and k; HV value heads of v, o, g, beta (HV % H == 0)
+ *   K, V   head dims, both 128
+ *   chunk  64
+ *   scale  multiplier of q after its norm; <= 0 selects K^-1/2
+ *   cu_seqlens       device int32 [N+1]: sequence n owns tokens
+ *                    [cu[n], cu[n+1]). Read by the kernels, never copied to
+ *                    the host (no device-to-host synchronisation).
+ *   cu_seqlens_host  optional host copy of the same boundaries. When given,
+ *                    it is validated (0 = cu[0] <= ... <= cu[N] = T) and the
+ *                    grids are sized exactly; when NULL the grids are sized
+ *                    for the bound T/64 + N chunks and chunks that do not
+ *                    exist exit at once. Device boundaries that are not
+ *                    monotone or leave [0, T] are clamped, never
+ *                    dereferenced out of range.
+ * Chunks restart at every sequence start; the last chunk of a sequence may be
+ * shorter than 64. Chunks are numbered sequence by sequence in token order;
+ * chunk c of the pack is the slot index used by the saved buffer. */
+typedef struct {
+  int32_t N, T, H, HV, K, V, chunk;
+  float scale;
+  const int32_t* cu_seqlens;
+  const int32_t* cu_seqlens_host;
+} gdn_problem;
+
+/* Number of chunk slots the chunk calls index: exact sum of ceil(L_n / 64)
+ * when cu_seqlens_host is given, else the bound T/64 + N. 0 on a bad problem. */
+int64_t gdn_num_chunks(const gdn_problem* p);
+
+/* Bytes of the `saved` buffer that gdn_chunk_fwd fills for gdn_chunk_bwd
+ * (0 on a bad problem). */
+size_t gdn_chunk_saved_size(const gdn_problem* p);
+
+/* Workspace bytes needed by gdn_chunk_fwd / gdn_chunk_bwd for this problem
+ * (0 on a bad problem). The workspace is caller-allocated device memory,
+ * 256-byte aligned, used only during the call, and need not be zeroed. */
+size_t gdn_chunk_fwd_workspace_size(const gdn_problem* p);
+size_t gdn_chunk_bwd_workspace_size(const gdn_problem* p);
+
+/* Chunked forward.
+ *   q, k      bf16 [T, H, K]
+ *   v         bf16 [T, HV, V]
+ *   g         fp32 [T, HV]  log-decay (exp(g) multiplies the state)
+ *   beta      fp32 [T, HV]  write strength (already passed through a sigmoid)
+ *   h0        fp32 [N, HV, V, K] initial states, or NULL for zero states
+ *   o         bf16 [T, HV, V] output (written)
+ *   hT        fp32 [N, HV, V, K] final states, or NULL to skip
+ *   saved     gdn_chunk_saved_size(p) bytes kept for gdn_chunk_bwd, or NULL
+ *             when no backward follows. For chunk slot c and value head hv
+ *             the block at element offset (c * HV + hv) * (K*V + 64*V) holds
+ *             the chunk's start state, the fp32 running state rounded to
+ *             nearest-even bf16 and stored transposed (element (k, v) at
+ *             k * V + v is S[v][k]), then the chunk's 64 x V corrected values
+ *             D = U - W h (bf16, rows past the chunk's end are zero).
+ * A sequence of length 0 gets hT = h0 (or 0). T = 0 is valid: nothing is
+ * read from the token tensors and hT = h0 (or 0).
+ * Errors: GDN_ERR_NULL (p, q, k, v, g, beta, o, cu_seqlens when T > 0, or
+ * workspace), GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_SEQLENS,
+ * GDN_ERR_WORKSPACE, GDN_ERR_HIP. */
+int gdn_chunk_fwd(const gdn_problem* p,
+                  const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                  const float* g, const float* beta, const float* h0,
+                  uint16_t* o, float* hT, uint16_t* saved,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Chunked backward of gdn_chunk_fwd (same p, q, k, v, g, beta).
+ *   saved     as written by gdn_chunk_fwd for the same problem and inputs
+ *   dO        bf16 [T, HV, V] cotangent of o
+ *   dhT       fp32 [N, HV, V, K] cotangent of hT, or NULL for zero
+ *   dq, dk    bf16 [T, H, K]; dv bf16 [T, HV, V]; dg, dbeta fp32 [T, HV]
+ *   dh0       fp32 [N, HV, V, K] cotangent of h0, or NULL to skip
+ * The value heads of one key head are summed into dq, dk in a fixed order.
+ * No atomics: repeated calls on identical inputs give identical bits. */
+int gdn_chunk_bwd(const gdn_problem* p,
+                  const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                  const float* g, const float* beta,
+                  const uint16_t* saved, const uint16_t* dO, const float* dhT,
+                  uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                  float* dg, float* dbeta, float* dh0,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Per-kernel timing, for measurement tools. Same as gdn_chunk_fwd /
+ * gdn_chunk_bwd, plus `events`: 2 * GDN_MAX_STAGES hipEvent_t handles created
+ * by the caller (hipEventCreate). The library records events[2 i] before and
+ * events[2 i + 1] after launching stage i on `stream` and stores the number of
+ * stages it launched in *n_stages; gdn_stage_name(op, i) names stage i
+ * (op 0: forward, 1: backward; "" past the last stage). Results are the same
+ * bits as the untimed calls. GDN_ERR_NULL if events or n_stages is NULL. */
+#define GDN_MAX_STAGES 8
+int gdn_chunk_fwd_timed(const gdn_problem* p,
+                        const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const float* g, const float* beta, const float* h0,
+                        uint16_t* o, float* hT, uint16_t* saved,
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        void* const* events, int* n_stages);
+int gdn_chunk_bwd_timed(const gdn_problem* p,
+                        const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const float* g, const float* beta,
+                        const uint16_t* saved, const uint16_t* dO, const float* dhT,
+                        uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                        float* dg, float* dbeta, float* dh0,
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        void* const* events, int* n_stages);
+const char* gdn_stage_name(int op, int stage);
+
+/* One recurrent decode step, in place on a state pool.
+ *   N rows (requests), one token each; H, HV, K = V = 128 as above.
+ *   q, k      bf16 [N, H, K];  v bf16 [N, HV, V]
+ *   a, b      bf16 [N, HV]: beta = sigmoid(b) and
+ *             g = -exp(A_log) * softplus(a + dt_bias), in fp32, with
+ *             softplus(x) = x for x > 20 and log(1 + e^x) otherwise
+ *   A_log     fp32 [HV];  dt_bias fp32 [HV] or NULL for zero
+ *   state_pool fp32 [slots, HV, V, K], updated in place
+ *   ssm_state_indices int32 [N] (device): row n updates block
+ *             ssm_state_indices[n]. An index <= 0 (0 is the null block) skips
+ *             the row: its o row is written as zeros and no state block is
+ *             read or written. The kernel also skips an index >= slots
+ *             instead of dereferencing it.
+ *   indices_host optional host copy of the indices: when given, an active
+ *             index >= slots or an active index used by two rows returns
+ *             GDN_ERR_INDEX before any launch. Without it the caller
+ *             guarantees that active indices are distinct.
+ *   o         bf16 [N, HV, V] (written)
+ * Each (row, value head) is computed alone, so a row's output and state do
+ * not depend on the other rows of the batch.
+ * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_INDEX,
+ * GDN_ERR_HIP. N = 0 is valid and enqueues nothing. */
+int gdn_recurrent_step(int32_t N, int32_t H, int32_t HV, int32_t K, int32_t V, float scale,
+                       const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       const uint16_t* a, const uint16_t* b,
+                       const float* A_log, const float* dt_bias,
+                       float* state_pool, int32_t slots,
+                       const int32_t* ssm_state_indices, const int32_t* indices_host,
+                       uint16_t* o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

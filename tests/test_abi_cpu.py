@@ -1,0 +1,170 @@
+"""The C ABI on the CPU: the library loads, exports what include/gdn.h declares,
+and rejects every bad argument before anything is enqueued.
+
+No test here reaches a kernel launch: each call fails validation first, so the
+fake device addresses below are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "chunked_gated_delta_04_amd", "libgdn.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libgdn.so not built")
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced
+FAKE_MISALIGNED = 0x10008
+
+
+@pytest.fixture(scope="module")
+def G():
+    from chunked_gated_delta_04_amd import gdn
+    return gdn
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_\w+)\s*\(", src)))
+
+
+def test_every_declared_function_is_exported(G):
+    names = declared_functions()
+    assert set(names) == set(G.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (gdn_\w+)", out))
+    assert set(names) <= exported
+    # nothing but the declared API is exported under the gdn_ prefix
+    assert exported == set(names)
+
+
+def test_status_strings(G):
+    for s in range(9):
+        assert G.gdn_status_string(s) and G.gdn_status_string(s) != "unknown status"
+    assert G.gdn_status_string(99) == "unknown status"
+
+
+def problem(G, N=2, T=130, H=2, HV=4, K=128, V=128, chunk=64, cu_host=(0, 70, 130), dev=FAKE):
+    p = G.GdnProblem()
+    p.N, p.T, p.H, p.HV, p.K, p.V, p.chunk = N, T, H, HV, K, V, chunk
+    p.scale = 0.0
+    p.cu_seqlens = dev
+    keep = None
+    if cu_host is not None:
+        keep = (ctypes.c_int32 * len(cu_host))(*cu_host)
+        p.cu_seqlens_host = ctypes.cast(keep, ctypes.c_void_p)
+    p._keep = keep
+    return p
+
+
+def fwd(G, p, ws_bytes=1 << 40, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, o=FAKE, hT=None,
+                saved=None, ws=FAKE)
+    args.update(over)
+    return G._lib.gdn_chunk_fwd(ctypes.byref(p), args["q"], args["k"], args["v"], args["g"],
+                                args["beta"], args["h0"], args["o"], args["hT"], args["saved"],
+                                args["ws"], ws_bytes, None)
+
+
+def bwd(G, p, ws_bytes=1 << 40, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, saved=FAKE, dO=FAKE, dhT=None,
+                dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, dbeta=FAKE, dh0=None, ws=FAKE)
+    args.update(over)
+    return G._lib.gdn_chunk_bwd(ctypes.byref(p), *[args[n] for n in (
+        "q", "k", "v", "g", "beta", "saved", "dO", "dhT", "dq", "dk", "dv", "dg", "dbeta",
+        "dh0", "ws")], ws_bytes, None)
+
+
+def test_chunk_counts_and_sizes(G):
+    p = problem(G)
+    assert G.gdn_num_chunks(p) == 2 + 1       # ceil(70/64) + ceil(60/64)
+    p2 = problem(G, cu_host=None)
+    assert G.gdn_num_chunks(p2) == 130 // 64 + 2
+    s = G.gdn_chunk_saved_size(p)
+    assert s == 2 * (128 * 128 + 64 * 128) * 4 * 3
+    assert G.gdn_chunk_fwd_workspace_size(p) > 0
+    assert G.gdn_chunk_bwd_workspace_size(p) > G.gdn_chunk_fwd_workspace_size(p) // 2
+    assert G.gdn_chunk_fwd_workspace_size(p) == G.gdn_chunk_fwd_workspace_size(p)
+    bad = problem(G, K=64)
+    assert G.gdn_num_chunks(bad) == 0 and G.gdn_chunk_fwd_workspace_size(bad) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=64), 3), (dict(V=256), 3), (dict(chunk=32), 3), (dict(H=3, HV=4), 3),
+    (dict(N=-1), 2), (dict(T=-5), 2), (dict(H=0), 2),
+    (dict(cu_host=(0, 70, 131)), 4), (dict(cu_host=(1, 70, 130)), 4),
+    (dict(cu_host=(0, 80, 70, 130)[:3]), 4),
+])
+def test_forward_rejects_bad_problems(G, kw, status):
+    p = problem(G, **kw)
+    assert fwd(G, p) == status
+    assert bwd(G, p) == status
+
+
+def test_non_monotone_host_boundaries(G):
+    p = problem(G, N=3, T=130, cu_host=(0, 90, 60, 130))
+    assert fwd(G, p) == 4
+
+
+def test_null_pointers(G):
+    p = problem(G)
+    assert G._lib.gdn_chunk_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE,
+                                1 << 40, None) == 1
+    for name in ("q", "k", "v", "g", "beta", "o"):
+        assert fwd(G, p, **{name: None}) == 1, name
+    for name in ("q", "k", "v", "g", "beta", "saved", "dO", "dq", "dk", "dv", "dg", "dbeta"):
+        assert bwd(G, p, **{name: None}) == 1, name
+    p.cu_seqlens = None
+    assert fwd(G, p) == 1
+
+
+def test_workspace_checks(G):
+    p = problem(G)
+    need = G.gdn_chunk_fwd_workspace_size(p)
+    assert fwd(G, p, ws_bytes=need - 1) == 6
+    assert fwd(G, p, ws=None) == 6
+    needb = G.gdn_chunk_bwd_workspace_size(p)
+    assert bwd(G, p, ws_bytes=needb - 1) == 6
+
+
+def test_alignment_checks(G):
+    p = problem(G)
+    assert fwd(G, p, q=FAKE_MISALIGNED) == 8
+    assert fwd(G, p, hT=FAKE_MISALIGNED) == 8
+    assert bwd(G, p, dv=FAKE_MISALIGNED) == 8
+
+
+def decode(G, N=4, H=2, HV=4, K=128, V=128, slots=8, host=None, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, A_log=FAKE, dt_bias=None, pool=FAKE,
+                idx=FAKE, o=FAKE)
+    args.update(over)
+    keep = None
+    hp = None
+    if host is not None:
+        keep = (ctypes.c_int32 * len(host))(*host)
+        hp = ctypes.cast(keep, ctypes.c_void_p)
+    return G._lib.gdn_recurrent_step(N, H, HV, K, V, 0.0, args["q"], args["k"], args["v"],
+                                     args["a"], args["b"], args["A_log"], args["dt_bias"],
+                                     args["pool"], slots, args["idx"], hp, args["o"], None)
+
+
+def test_decode_rejects_bad_arguments(G):
+    assert decode(G, K=64) == 3
+    assert decode(G, H=3, HV=4) == 3
+    assert decode(G, N=-1) == 2
+    assert decode(G, slots=-1) == 2
+    assert decode(G, N=0) == 0          # nothing to do, nothing enqueued
+    for name in ("q", "k", "v", "a", "b", "A_log", "pool", "idx", "o"):
+        assert decode(G, **{name: None}) == 1, name
+    assert decode(G, pool=FAKE_MISALIGNED) == 8
+
+
+def test_decode_index_rules_on_the_host_copy(G):
+    # out of range, repeated: errors before any launch
+    assert decode(G, host=[1, 8, 2, 3]) == 5
+    assert decode(G, host=[1, 2, 2, 3]) == 5
+    assert decode(G, host=[1, 2, 7, 7]) == 5

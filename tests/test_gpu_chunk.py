@@ -1,0 +1,239 @@
+"""GPU parity of the chunk forward/backward (HIP path through the C ABI) with the
+fp64 oracle, plus the bitwise invariants the method implies."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from chunked_gated_delta_04_amd import synth
+from tests.gpu_helpers import (assert_bar, f64, head_slice, oracle_backward, oracle_forward,
+                               to_dev)
+from oracle import recurrence as R
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from chunked_gated_delta_04_amd import gdn
+else:
+    gdn = None
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def run_fwd(inp, save=False, host_cu=True, stream=None):
+    d = to_dev(inp)
+    host = inp["cu_seqlens"].to(torch.int32) if host_cu else None
+    return gdn.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], h0=d["h0"],
+                         cu_seqlens_host=host, save_for_backward=save, stream=stream)
+
+
+def run_fwd_bwd(inp, dhT=None, stream=None):
+    d = to_dev(inp)
+    host = inp["cu_seqlens"].to(torch.int32)
+    o, hT, saved = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                                 h0=d["h0"], cu_seqlens_host=host, save_for_backward=True,
+                                 stream=stream)
+    grads = gdn.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], saved,
+                          d["do"], dhT=None if dhT is None else dhT.cuda(), cu_seqlens_host=host,
+                          want_dh0=True, stream=stream)
+    return o, hT, grads
+
+
+SMALL_LENS = [1, 63, 64, 65, 200, 130]
+
+
+def small_inputs(lens=SMALL_LENS, H=2, HV=4, seed=7, h0=True, with_do=False):
+    return synth.chunk_inputs(lens, H, HV, seed, h0_std=0.1 if h0 else None, with_do=with_do)
+
+
+# ------------------------------------------------------------------ forward parity
+@pytest.mark.parametrize("h0", [True, False])
+def test_forward_matches_oracle_small_varlen(h0):
+    _say(f"fwd small varlen h0={h0}")
+    inp = small_inputs(h0=h0)
+    o, hT, _ = run_fwd(inp)
+    o_ref, hT_ref = oracle_forward(inp)
+    assert_bar("o", f64(o), o_ref)
+    assert_bar("hT", f64(hT), hT_ref)
+
+
+def test_forward_matches_oracle_single_head_workload():
+    _say("fwd 1x256 h1")
+    inp = synth.workload_inputs("fwd_1x256_h1")
+    o, hT, _ = run_fwd(inp)
+    o_ref, hT_ref = oracle_forward(inp)
+    assert_bar("o", f64(o), o_ref)
+    assert_bar("hT", f64(hT), hT_ref)
+
+
+@pytest.mark.parametrize("name", ["fwd_4x4096_h16_hv32", "fwd_varlen12_32768_h16_hv32"])
+def test_forward_full_size_sampled_heads(name):
+    _say(f"fwd full {name}")
+    inp = synth.workload_inputs(name)
+    H, HV = inp["q"].shape[1], inp["v"].shape[1]
+    o, hT, _ = run_fwd(inp)
+    o, hT = o.cpu(), hT.cpu()
+    N = inp["cu_seqlens"].numel() - 1
+    rng = np.random.default_rng(0)
+    picks = [(0, 0), (N - 1, HV - 1)] + [(int(rng.integers(N)), int(rng.integers(HV)))
+                                         for _ in range(2)]
+    for seq, hv in picks:
+        s, (t0, t1), h, hvs = head_slice(inp, seq, hv, H, HV)
+        o_ref, hT_ref = R.forward(s["q"], s["k"], s["v"], s["g"], s["beta"], s["cu"], s["h0"])
+        j = hvs.index(hv)
+        assert_bar(f"o[{seq},{hv}]", f64(o[t0:t1, hv]), o_ref[:, j])
+        assert_bar(f"hT[{seq},{hv}]", f64(hT[seq, hv]), hT_ref[0, j])
+
+
+def test_forward_device_only_boundaries_match_host_route_bitwise():
+    inp = small_inputs()
+    o1, h1, _ = run_fwd(inp, host_cu=True)
+    o2, h2, _ = run_fwd(inp, host_cu=False)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+def test_forward_strong_decay_is_finite():
+    inp = small_inputs()
+    inp["g"] = torch.full_like(inp["g"], -60.0)
+    o, hT, _ = run_fwd(inp)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(hT).all()
+    o_ref, hT_ref = oracle_forward(inp)
+    assert_bar("o", f64(o), o_ref)
+
+
+# ------------------------------------------------------------------ edge cases
+def test_no_tokens_passes_the_state_through():
+    H, HV, N = 2, 4, 3
+    h0 = 0.1 * torch.randn(N, HV, 128, 128, device="cuda")
+    cu = torch.zeros(N + 1, dtype=torch.int32, device="cuda")
+    e = torch.empty(0, H, 128, dtype=torch.bfloat16, device="cuda")
+    ev = torch.empty(0, HV, 128, dtype=torch.bfloat16, device="cuda")
+    eg = torch.empty(0, HV, dtype=torch.float32, device="cuda")
+    o, hT, _ = gdn.chunk_fwd(e, e, ev, eg, eg, cu, h0=h0, cu_seqlens_host=cu.cpu())
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.equal(hT, h0)
+    o, hT, _ = gdn.chunk_fwd(e, e, ev, eg, eg, cu, h0=None, cu_seqlens_host=cu.cpu())
+    assert torch.equal(hT, torch.zeros_like(hT))
+
+
+def test_zero_length_sequence_inside_a_pack():
+    inp = small_inputs(lens=[70, 0, 33])
+    o, hT, _ = run_fwd(inp)
+    assert torch.equal(hT[1].cpu(), inp["h0"][1])
+    o_ref, hT_ref = oracle_forward(inp)
+    assert_bar("o", f64(o), o_ref)
+    assert_bar("hT", f64(hT), hT_ref)
+
+
+# ------------------------------------------------------------------ invariants (bitwise)
+def test_a_sequence_alone_equals_it_inside_a_pack_bitwise():
+    inp = small_inputs(lens=[100, 150, 77])
+    o, hT, _ = run_fwd(inp)
+    cu = inp["cu_seqlens"].tolist()
+    s0, s1 = cu[1], cu[2]
+    alone = dict(q=inp["q"][s0:s1], k=inp["k"][s0:s1], v=inp["v"][s0:s1], g=inp["g"][s0:s1],
+                 beta=inp["beta"][s0:s1], cu_seqlens=torch.tensor([0, s1 - s0], dtype=torch.int32),
+                 h0=inp["h0"][1:2].contiguous())
+    o1, h1, _ = run_fwd(alone)
+    assert torch.equal(o1, o[s0:s1]) and torch.equal(h1[0], hT[1])
+
+
+def test_linearity_in_state_and_values_bitwise():
+    inp = small_inputs()
+    o, hT, _ = run_fwd(inp)
+    inp2 = dict(inp, v=(2 * inp["v"].float()).to(torch.bfloat16), h0=2 * inp["h0"])
+    o2, h2, _ = run_fwd(inp2)
+    assert torch.equal(o2.float(), 2 * o.float()) and torch.equal(h2, 2 * hT)
+
+
+def test_value_heads_of_one_key_head_with_equal_inputs_agree_bitwise():
+    inp = small_inputs(H=1, HV=2)
+    for key in ("v", "g", "beta"):
+        inp[key][:, 1] = inp[key][:, 0]
+    inp["h0"][:, 1] = inp["h0"][:, 0]
+    o, hT, _ = run_fwd(inp)
+    assert torch.equal(o[:, 0], o[:, 1]) and torch.equal(hT[:, 0], hT[:, 1])
+
+
+def test_state_carry_across_two_calls():
+    lens = [600]
+    inp = small_inputs(lens=lens, H=1, HV=2)
+    o, hT, _ = run_fwd(inp)
+    for p in (1, 63, 64, 65, 527):
+        a = dict(q=inp["q"][:p], k=inp["k"][:p], v=inp["v"][:p], g=inp["g"][:p],
+                 beta=inp["beta"][:p], cu_seqlens=torch.tensor([0, p], dtype=torch.int32),
+                 h0=inp["h0"])
+        oa, ha, _ = run_fwd(a)
+        b = dict(q=inp["q"][p:], k=inp["k"][p:], v=inp["v"][p:], g=inp["g"][p:],
+                 beta=inp["beta"][p:], cu_seqlens=torch.tensor([0, 600 - p], dtype=torch.int32),
+                 h0=ha.cpu())
+        ob, hb, _ = run_fwd(b)
+        assert_bar(f"o split {p}", f64(torch.cat([oa, ob])), f64(o))
+        assert_bar(f"hT split {p}", f64(hb), f64(hT))
+
+
+# ------------------------------------------------------------------ backward parity
+def _check_grads(grads, ref, tag):
+    for name in ("dq", "dk", "dv", "dbeta", "dh0"):
+        assert_bar(f"{tag} {name}", f64(grads[name]), ref[name])
+    dg_ref = ref["dg"]
+    assert_bar(f"{tag} dg", f64(grads["dg"]), dg_ref, atol=1e-2 * float(np.abs(dg_ref).max()))
+
+
+@pytest.mark.parametrize("with_dhT", [False, True])
+def test_backward_matches_oracle_small_varlen(with_dhT):
+    _say(f"bwd small varlen dhT={with_dhT}")
+    inp = small_inputs(with_do=True)
+    dhT = 0.1 * torch.randn(len(SMALL_LENS), 4, 128, 128, generator=torch.Generator().manual_seed(3)) \
+        if with_dhT else None
+    o, hT, grads = run_fwd_bwd(inp, dhT=dhT)
+    ref = oracle_backward(inp, dhT=dhT)
+    o_ref, _ = oracle_forward(inp)
+    assert_bar("o", f64(o), o_ref)
+    _check_grads(grads, ref, "small")
+
+
+def test_backward_full_size_sampled_heads_and_determinism():
+    _say("bwd full 2x8192")
+    inp = synth.workload_inputs("fwdbwd_2x8192_h16_hv32")
+    H, HV = 16, 32
+    o, hT, grads = run_fwd_bwd(inp)
+    # bitwise repeat
+    o2, hT2, grads2 = run_fwd_bwd(inp)
+    assert torch.equal(o, o2) and torch.equal(hT, hT2)
+    for kname in grads:
+        assert torch.equal(grads[kname], grads2[kname]), kname
+    grads = {kk: vv.cpu() for kk, vv in grads.items()}
+    for seq, hv in [(0, 0), (1, 31), (1, 10)]:
+        s, (t0, t1), h, hvs = head_slice(inp, seq, hv, H, HV)
+        ref = R.backward(s["q"], s["k"], s["v"], s["g"], s["beta"], s["cu"], s["do"], s["h0"])
+        tag = f"[{seq},{h}]"
+        assert_bar(f"dq{tag}", f64(grads["dq"][t0:t1, h]), ref["dq"][:, 0])
+        assert_bar(f"dk{tag}", f64(grads["dk"][t0:t1, h]), ref["dk"][:, 0])
+        for j, hh in enumerate(hvs):
+            assert_bar(f"dv{tag}", f64(grads["dv"][t0:t1, hh]), ref["dv"][:, j])
+            assert_bar(f"dbeta{tag}", f64(grads["dbeta"][t0:t1, hh]), ref["dbeta"][:, j])
+            assert_bar(f"dh0{tag}", f64(grads["dh0"][seq, hh]), ref["dh0"][0, j])
+            dg_ref = ref["dg"][:, j]
+            assert_bar(f"dg{tag}", f64(grads["dg"][t0:t1, hh]), dg_ref,
+                       atol=1e-2 * float(np.abs(dg_ref).max()))
+
+
+def test_backward_repeats_bitwise_many_times_and_on_a_side_stream():
+    inp = small_inputs(with_do=True)
+    o, hT, g0 = run_fwd_bwd(inp)
+    side = torch.cuda.Stream()
+    for i in range(20):
+        if i % 2:
+            with torch.cuda.stream(side):
+                o2, hT2, g2 = run_fwd_bwd(inp)
+        else:
+            o2, hT2, g2 = run_fwd_bwd(inp)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o2) and torch.equal(hT, hT2)
+        for kname in g0:
+            assert torch.equal(g0[kname], g2[kname]), (i, kname)
