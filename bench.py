@@ -78,25 +78,29 @@ def elapsed_ms(h, a, b):
     return ms.value
 
 
-def cpu_baseline(inp, sample_tokens):
-    """fp64 oracle forward + backward on the first `sample_tokens` tokens of the
-    first sequence, all heads; tokens per second on this host."""
-    import numpy as np
+def cpu_baseline(inp, target_s):
+    """fp64 oracle forward + backward on the first tokens of the first sequence,
+    all heads; tokens per second on this host. A 32-token probe sizes the
+    sample to about `target_s` seconds of oracle work."""
     import torch
     from oracle import recurrence as R
 
     def f64(t):
         return t.to(torch.float64).numpy()
 
-    n = sample_tokens
-    sl = slice(0, n)
-    args = [f64(inp[k][sl]) for k in ("q", "k", "v", "g", "beta")]
-    h0 = f64(inp["h0"][0:1])
-    do = f64(inp["do"][sl])
-    t0 = time.perf_counter()
-    R.forward(*args, [0, n], h0)
-    R.backward(*args, [0, n], do, h0)
-    dt = time.perf_counter() - t0
+    def run(n):
+        sl = slice(0, n)
+        args = [f64(inp[k][sl]) for k in ("q", "k", "v", "g", "beta")]
+        h0 = f64(inp["h0"][0:1])
+        do = f64(inp["do"][sl])
+        t0 = time.perf_counter()
+        R.forward(*args, [0, n], h0)
+        R.backward(*args, [0, n], do, h0)
+        return time.perf_counter() - t0
+
+    probe = run(32)
+    n = int(max(32, min(8192, 32 * target_s / max(probe, 1e-3))))
+    dt = run(n)
     return dict(value=n / dt, unit="tokens/s", cores=1, kind="oracle",
                 sample=(f"fp64 oracle forward + backward over the first {n} tokens of sequence 0 "
                         f"of {WORKLOAD} (all 16 key / 32 value heads), {dt:.1f} s on "
@@ -110,7 +114,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=192)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
@@ -203,7 +207,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args.cpu_sample_tokens)
+        cpu = cpu_baseline(inp, args.cpu_seconds)
         cpu["value"] = round(cpu["value"], 3)
 
     out = {

@@ -27,7 +27,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
-  size_t table, seq_first, W, U, Qg, P, Kb, gL, dh, dD, dDT, total;
+  size_t table, seq_first, W, U, Qg, P, Kb, gL, T, dh, dD, dDT, total;
 };
 
 // Chunk slots: exact with a host copy of the boundaries, else T/64 + N.
@@ -78,6 +78,7 @@ Layout make_layout(const gdn_problem* p, int64_t NC, bool bwd) {
   L.P = off;         off = align_up(off + 2 * kBlk64x64 * blocks);
   L.Kb = off;        off = align_up(off + 2 * kBlk64x128 * blocks);
   L.gL = off;        off = align_up(off + sizeof(float) * blocks);
+  L.T = off;         off = bwd ? align_up(off + 2 * 2 * kBlk64x64 * blocks) : off;
   L.dh = off;        off = bwd ? align_up(off + 2 * kState * blocks) : off;
   L.dD = off;        off = bwd ? align_up(off + 2 * kBlk64x128 * blocks) : off;
   L.dDT = off;       off = bwd ? align_up(off + 2 * kBlk64x128 * blocks) : off;
@@ -93,6 +94,7 @@ PrepOut prep_views(char* ws, const Layout& L, bool bwd) {
   o.P = reinterpret_cast<uint16_t*>(ws + L.P);
   o.Kb = reinterpret_cast<uint16_t*>(ws + L.Kb);
   o.gL = reinterpret_cast<float*>(ws + L.gL);
+  o.T = bwd ? reinterpret_cast<uint16_t*>(ws + L.T) : nullptr;
   return o;
 }
 
@@ -268,8 +270,8 @@ static int chunk_bwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_
     return launch_bwd_dh_scan(seq_first, p->N, p->HV, (int)NC, table, prep, dO, dhT, dh0, bufs, s);
   }));
   GDN_TRY(clk.run([&] {
-    return launch_bwd_chunk(table, (int)NC, p->H, p->HV, scale, q, k, v, g, beta, saved, bufs, dO,
-                            dq, dk, dv, dg, dbeta, s);
+    return launch_bwd_chunk(table, (int)NC, p->H, p->HV, scale, q, k, v, g, beta, saved, prep.T,
+                            bufs, dO, dq, dk, dv, dg, dbeta, s);
   }));
   if (n_stages) *n_stages = clk.n;
   return GDN_OK;

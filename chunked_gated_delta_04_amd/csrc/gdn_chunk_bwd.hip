@@ -89,9 +89,47 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
       }
     }
 
+  static_assert(kChunk * (VB / 8) == 256, "one dO segment per thread");
+  struct Ops {
+    bf16x8 pa[2], ka[4], qa[2][2], wa[2][2];
+    uint4 dO;
+    float gl;
+    ChunkInfo ci;
+  };
+  const int ot = tid / (VB / 8), osg = tid - ot * (VB / 8);  // dO segment of this thread
+  auto load_ops = [&](int c, Ops& x) {
+    const size_t blk = (size_t)hv * NC + c;
+    const uint16_t* PTb = prep.P + blk * 4096;   // P^T: row i holds P[j][i], j >= i
+    const uint16_t* Kbb = prep.Kb + blk * 8192;  // K_bwd [tok][k]
+    const uint16_t* QgT = prep.Qg + blk * 8192;  // Q_g^T [k][tok]
+    const uint16_t* WT = prep.W + blk * 8192;    // W^T [k][tok]
+#pragma unroll
+    for (int s = 0; s < 2; ++s) x.pa[s] = ld8(PTb + (16 * wave + li) * 64 + 32 * s + 8 * kq);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) x.ka[s] = ld8(Kbb + (16 * wave + li) * kHead + 32 * s + 8 * kq);
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      const int kr = 16 * (2 * wave + dt) + li;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        x.qa[dt][s] = ld8(QgT + kr * 64 + 32 * s + 8 * kq);
+        x.wa[dt][s] = ld8(WT + kr * 64 + 32 * s + 8 * kq);
+      }
+    }
+    x.gl = prep.gL[blk];
+    x.ci = table[c];
+    x.dO = make_uint4(0, 0, 0, 0);
+    if (ot < x.ci.len)
+      x.dO = *reinterpret_cast<const uint4*>(dO + ((size_t)(x.ci.t0 + ot) * HV + hv) * kHead + v0 +
+                                             8 * osg);
+  };
+
   const int c_begin = seq_first[seq], c_end = seq_first[seq + 1];
+  Ops nxt;
+  if (c_begin < c_end) load_ops(c_end - 1, nxt);
   for (int c = c_end - 1; c >= c_begin; --c) {
-    const ChunkInfo ci = table[c];
+    const Ops cur = nxt;
+    if (c - 1 >= c_begin) load_ops(c - 1, nxt);
     const size_t blk = (size_t)hv * NC + c;
 
     // 1. dh -> LDS; stage dO^T for this value block
@@ -103,14 +141,10 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
         *reinterpret_cast<uint2*>(&Hs[(16 * vt + li) * SP + kk]) =
             pack4_bf16(dh[dt][vt][0], dh[dt][vt][1], dh[dt][vt][2], dh[dt][vt][3]);
       }
-    for (int e = tid; e < kChunk * (VB / 8); e += 256) {
-      const int t = e / (VB / 8), sg = e - t * (VB / 8);
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (t < ci.len)
-        x = *reinterpret_cast<const uint4*>(dO + ((size_t)(ci.t0 + t) * HV + hv) * kHead + v0 + 8 * sg);
-      const uint16_t* xs = reinterpret_cast<const uint16_t*>(&x);
+    {
+      const uint16_t* xs = reinterpret_cast<const uint16_t*>(&cur.dO);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) Os[(8 * sg + u) * DP + t] = xs[u];
+      for (int u = 0; u < 8; ++u) Os[(8 * osg + u) * DP + ot] = xs[u];
     }
     __syncthreads();
     // dh' (gradient of this chunk's end state) as [k][v]
@@ -123,26 +157,17 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
     }
 
     // 2. dD = P^T dO + K_bwd dh; wave w owns tokens 16 w .. 16 w + 15
-    {
-      const uint16_t* PTb = prep.P + blk * 4096;  // P^T: row i holds P[j][i], j >= i
-      const uint16_t* Kbb = prep.Kb + blk * 8192; // K_bwd [tok][k]
-      bf16x8 pa[2], ka[4];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) pa[s] = ld8(PTb + (16 * wave + li) * 64 + 32 * s + 8 * kq);
+    for (int vt = 0; vt < VT; ++vt) {
+      f32x4 acc = zero4();
+      if (wave < 2) acc = mfma(cur.pa[0], ld8(&Os[(16 * vt + li) * DP + 8 * kq]), acc);
+      acc = mfma(cur.pa[1], ld8(&Os[(16 * vt + li) * DP + 32 + 8 * kq]), acc);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) ka[s] = ld8(Kbb + (16 * wave + li) * kHead + 32 * s + 8 * kq);
-#pragma unroll
-      for (int vt = 0; vt < VT; ++vt) {
-        f32x4 acc = zero4();
-        if (wave < 2) acc = mfma(pa[0], ld8(&Os[(16 * vt + li) * DP + 8 * kq]), acc);
-        acc = mfma(pa[1], ld8(&Os[(16 * vt + li) * DP + 32 + 8 * kq]), acc);
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          acc = mfma(ka[s], ld8(&Hs[(16 * vt + li) * SP + 32 * s + 8 * kq]), acc);
-        // acc[r] = dD[t = 16 w + 4 kq + r][v = 16 vt + li]
-        *reinterpret_cast<uint2*>(&Es[(16 * vt + li) * DP + 16 * wave + 4 * kq]) =
-            pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
-      }
+      for (int s = 0; s < 4; ++s)
+        acc = mfma(cur.ka[s], ld8(&Hs[(16 * vt + li) * SP + 32 * s + 8 * kq]), acc);
+      // acc[r] = dD[t = 16 w + 4 kq + r][v = 16 vt + li]
+      *reinterpret_cast<uint2*>(&Es[(16 * vt + li) * DP + 16 * wave + 4 * kq]) =
+          pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
     }
     __syncthreads();
     // dD to global as [v][tok] (row copies) and [tok][v] (column gathers)
@@ -161,32 +186,19 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
     }
 
     // 3. dh <- e^gamma_L dh + Q_g^T dO - W^T dD; wave w owns key rows 32 w .. 32 w + 31
-    {
-      const uint16_t* QgT = prep.Qg + blk * 8192;  // Q_g^T [k][tok]
-      const uint16_t* WT = prep.W + blk * 8192;    // W^T [k][tok]
-      const float gl = prep.gL[blk];
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const int kr = 16 * (2 * wave + dt) + li;
-        bf16x8 qa[2], wa[2];
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) {
+        f32x4 acc = dh[dt][vt] * cur.gl;
+        f32x4 acw = zero4();
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          qa[s] = ld8(QgT + kr * 64 + 32 * s + 8 * kq);
-          wa[s] = ld8(WT + kr * 64 + 32 * s + 8 * kq);
+          acc = mfma(cur.qa[dt][s], ld8(&Os[(16 * vt + li) * DP + 32 * s + 8 * kq]), acc);
+          acw = mfma(cur.wa[dt][s], ld8(&Es[(16 * vt + li) * DP + 32 * s + 8 * kq]), acw);
         }
-#pragma unroll
-        for (int vt = 0; vt < VT; ++vt) {
-          f32x4 acc = dh[dt][vt] * gl;
-          f32x4 acw = zero4();
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            acc = mfma(qa[s], ld8(&Os[(16 * vt + li) * DP + 32 * s + 8 * kq]), acc);
-            acw = mfma(wa[s], ld8(&Es[(16 * vt + li) * DP + 32 * s + 8 * kq]), acw);
-          }
-          dh[dt][vt] = acc - acw;
-        }
+        dh[dt][vt] = acc - acw;
       }
-    }
     __syncthreads();
   }
 
@@ -204,49 +216,88 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Per-chunk gradients: one workgroup per (chunk, key head), value heads of the
-// key head in order. Wave w owns tokens 16 w .. 16 w + 15 of every
-// token-indexed result, so per-token sums stay inside one wave.
-__global__ __launch_bounds__(256) void bwd_chunk_kernel(
+// Per-chunk gradients: one 512-thread workgroup per (chunk, key head); the
+// value heads of the key head run in order. Wave w owns token tile tw = w & 3
+// (tokens 16 tw .. 16 tw + 15) and column half kh = w >> 2 (key or value
+// columns 64 kh .. 64 kh + 63) of every token-indexed result. Every matrix
+// that is contracted over the chunk's tokens is kept in LDS transposed as well
+// (bf16), so every MFMA operand is one 16-byte read. Per-token and per-column
+// partial sums go to LDS slots owned by one wave each and are added once per
+// value head in a fixed order.
+namespace {
+constexpr int BP = 72;  // LDS pitch (bf16) of [64][64] tiles
+
+struct BwdLds {
+  uint16_t Ks[64 * KP], Qs[64 * KP];        // k^, q~ rows
+  uint16_t KsT[128 * TP], QsT[128 * TP];    // k^, q~ transposed [k][tok]
+  uint16_t Tb[64 * BP], TbT[64 * BP];       // T, T^T
+  uint16_t Pm[64 * BP], PmT[64 * BP];       // dP o Gamma and transpose; later M, M^T
+  union {                                   // time-shared regions
+    uint16_t Z[64 * KP];                    //   Z = T^T dD [tok][v]
+    uint16_t dT[64 * BP];                   //   dT [i][m]
+  } rz;
+  union {
+    uint16_t dW[64 * KP];                   //   dW [tok][k]
+    uint16_t Y1T[64 * BP];                  //   (dT T^T)^T
+  } rw;
+  float gam[64], bet[64], eg[64], ebw[64];
+  float nrm_k[64], nrm_q[64];
+  float rowF[2][64], colF[8][64];           // F = dP o P
+  float rowG[2][64], rowB2[2][64];          // row terms of the key-column loop
+  float rowB[2][64];                        // dbeta of U
+  float rowE[2][64], colE[8][64], rowB3[2][64];  // E = dA o A, dbeta of A
+  float gl_part[8], hd_part[8];
+  float dot_q[2][64], dot_k[2][64];
+};
+
+__device__ __forceinline__ bf16x8 zero8() {
+  return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+}
+__device__ __forceinline__ float4 ld4_bf16(const uint16_t* p) {  // 4 bf16 -> fp32
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(bf2f(u.x & 0xffffu), bf2f(u.x >> 16), bf2f(u.y & 0xffffu), bf2f(u.y >> 16));
+}
+__device__ __forceinline__ float dot8(const bf16x8& a, const bf16x8& b) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s += (float)a[e] * (float)b[e];
+  return s;
+}
+}  // namespace
+
+__global__ __launch_bounds__(512) void bwd_chunk_kernel(
     const ChunkInfo* __restrict__ table, int NC, int H, int HV, float scale,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ g,
-    const float* __restrict__ beta, const uint16_t* __restrict__ saved, BwdBufs bufs,
-    const uint16_t* __restrict__ dO, uint16_t* __restrict__ dq, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta) {
+    const float* __restrict__ beta, const uint16_t* __restrict__ saved,
+    const uint16_t* __restrict__ Tmat, BwdBufs bufs, const uint16_t* __restrict__ dO,
+    uint16_t* __restrict__ dq, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+    float* __restrict__ dg, float* __restrict__ dbeta) {
   const int c = blockIdx.x, h = blockIdx.y;
   const ChunkInfo ci = table[c];
   if (ci.seq < 0) return;
   const int t0 = ci.t0, L = ci.len;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, kq = lane >> 4;
+  const int tw = wave & 3, kh = wave >> 2;
+  const int trow = 16 * tw + li;  // token row this lane supplies as an A operand
+  const bool trow_ok = trow < L;
 
-  __shared__ __align__(16) uint16_t Ks[64 * KP];   // k^ rows (bf16); dk staging at the end
-  __shared__ __align__(16) uint16_t Qs[64 * KP];   // q~ rows (bf16); dq staging at the end
-  __shared__ __align__(16) float Ts[64 * FP];      // T
-  __shared__ __align__(16) float As[64 * FP];      // A -> F -> dT -> M
-  __shared__ __align__(16) float PS[64 * FP];      // P -> E
-  __shared__ __align__(16) float G1[64 * FP];      // dP o Gamma -> Y1
-  __shared__ __align__(16) uint16_t dWs[128 * TP]; // dW as [k][tok]
-  __shared__ float gam[64], bet[64], eg[64], ebw[64], dgam[64], dbet[64];
-  __shared__ float nrm_k[64], nrm_q[64];
-  __shared__ float Xs[3 * 256];
-  __shared__ float red[8];
+  __shared__ __align__(16) BwdLds S;
 
-  // ---- load and normalise q, k (as the forward does), keep the norms
+  // ---- q, k rows: L2 norm, bf16 copies in both layouts (8 threads per row)
   {
-    const int r = tid >> 2, sg0 = (tid & 3) * 4;
-    uint4 kr[4], qr[4];
+    const int r = tid >> 3, sg0 = (tid & 7) * 2;
+    uint4 kr[2], qr[2];
     float sk = 0.f, sq = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
+      kr[j] = make_uint4(0, 0, 0, 0);
+      qr[j] = make_uint4(0, 0, 0, 0);
       if (r < L) {
         const size_t off = ((size_t)(t0 + r) * H + h) * kHead + (sg0 + j) * 8;
         kr[j] = *reinterpret_cast<const uint4*>(k + off);
         qr[j] = *reinterpret_cast<const uint4*>(q + off);
-      } else {
-        kr[j] = make_uint4(0, 0, 0, 0);
-        qr[j] = make_uint4(0, 0, 0, 0);
       }
       const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[j]);
       const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qr[j]);
@@ -258,15 +309,15 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
         sq += b0 * b0 + b1 * b1;
       }
     }
-    sk = group_sum<4>(sk);
-    sq = group_sum<4>(sq);
+    sk = group_sum<8>(sk);
+    sq = group_sum<8>(sq);
     const float nk = sqrtf(sk + kNormEps), nq = sqrtf(sq + kNormEps);
-    if ((tid & 3) == 0) {
-      nrm_k[r] = nk;
-      nrm_q[r] = nq;
+    if ((tid & 7) == 0) {
+      S.nrm_k[r] = nk;
+      S.nrm_q[r] = nq;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[j]);
       const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qr[j]);
       uint4 ko, qo;
@@ -274,29 +325,42 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
       uint32_t* qow = reinterpret_cast<uint32_t*>(&qo);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        kow[e] = (uint32_t)f2bf(bf2f(kw[e] & 0xffffu) / nk) |
-                 ((uint32_t)f2bf(bf2f(kw[e] >> 16) / nk) << 16);
-        qow[e] = (uint32_t)f2bf((bf2f(qw[e] & 0xffffu) / nq) * scale) |
-                 ((uint32_t)f2bf((bf2f(qw[e] >> 16) / nq) * scale) << 16);
+        const uint16_t k0 = f2bf(bf2f(kw[e] & 0xffffu) / nk), k1 = f2bf(bf2f(kw[e] >> 16) / nk);
+        const uint16_t q0 = f2bf((bf2f(qw[e] & 0xffffu) / nq) * scale);
+        const uint16_t q1 = f2bf((bf2f(qw[e] >> 16) / nq) * scale);
+        kow[e] = (uint32_t)k0 | ((uint32_t)k1 << 16);
+        qow[e] = (uint32_t)q0 | ((uint32_t)q1 << 16);
+        const int d = (sg0 + j) * 8 + 2 * e;
+        S.KsT[d * TP + r] = k0;
+        S.KsT[(d + 1) * TP + r] = k1;
+        S.QsT[d * TP + r] = q0;
+        S.QsT[(d + 1) * TP + r] = q1;
       }
-      *reinterpret_cast<uint4*>(&Ks[r * KP + (sg0 + j) * 8]) = ko;
-      *reinterpret_cast<uint4*>(&Qs[r * KP + (sg0 + j) * 8]) = qo;
+      *reinterpret_cast<uint4*>(&S.Ks[r * KP + (sg0 + j) * 8]) = ko;
+      *reinterpret_cast<uint4*>(&S.Qs[r * KP + (sg0 + j) * 8]) = qo;
     }
   }
-  __syncthreads();
 
-  // dq~, dk^ accumulated over the value heads: [kt][r] = d[16 w + 4 kq + r][16 kt + li]
-  f32x4 adq[8], adk[8];
+  // dq~, dk^ over the value heads: [j][r] = d[16 tw + 4 kq + r][16 (4 kh + j) + li]
+  f32x4 adq[4], adk[4];
 #pragma unroll
-  for (int kt = 0; kt < 8; ++kt) {
-    adq[kt] = zero4();
-    adk[kt] = zero4();
+  for (int j = 0; j < 4; ++j) {
+    adq[j] = zero4();
+    adk[j] = zero4();
   }
-  const int trow = 16 * wave + li;          // token row this lane supplies as an A operand
-  const bool trow_ok = trow < L;
 
   const int G = HV / H;
+  const size_t rs = (size_t)HV * kHead;  // token stride of dO, v, dv
   for (int jg = 0; jg < G; ++jg) {
+    // Re-derive the thread coordinates each iteration from an opaque copy, so
+    // the many LDS addresses built from them are not hoisted out of the loop
+    // (they would not fit in the register budget of two waves per SIMD).
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int li = lane & 15, kq = lane >> 4;
+    const int trow = 16 * tw + li;
+    const bool trow_ok = trow < L;
     const int hv = h * G + jg;
     const size_t blk = (size_t)hv * NC + c;
     const uint16_t* hb = saved + blk_saved(c, hv, HV);  // h [k][v]
@@ -304,11 +368,10 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
     const uint16_t* dhb = bufs.dh + blk * (kHead * kHead);
     const uint16_t* dDb = bufs.dD + blk * 8192;          // dD [tok][v]
     const uint16_t* dDTb = bufs.dDT + blk * 8192;        // dD^T [v][tok]
-    const size_t rs = (size_t)HV * kHead;                // token stride of dO, v, dv
     const uint16_t* dOb = dO + ((size_t)t0 * HV + hv) * kHead;
     const uint16_t* vb = v + ((size_t)t0 * HV + hv) * kHead;
 
-    // ---- gates
+    // ---- gates; T and T^T (from the WY pass of the backward) into LDS
     if (wave == 0) {
       float gv = lane < L ? g[(size_t)(t0 + lane) * HV + hv] : 0.f;
       const float bv = lane < L ? beta[(size_t)(t0 + lane) * HV + hv] : 0.f;
@@ -317,452 +380,447 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
         const float y = __shfl_up(gv, off, 64);
         if (lane >= off) gv += y;
       }
-      gam[lane] = gv;
-      bet[lane] = bv;
+      S.gam[lane] = gv;
+      S.bet[lane] = bv;
       const float gl = __shfl(gv, L - 1, 64);
-      eg[lane] = expf(gv);
-      ebw[lane] = lane < L ? expf(gl - gv) : 0.f;
-      dgam[lane] = 0.f;
-      dbet[lane] = 0.f;
+      S.eg[lane] = expf(gv);
+      S.ebw[lane] = lane < L ? expf(gl - gv) : 0.f;
     }
-    __syncthreads();
-
-    // ---- A (lower tiles) and P (all tiles), fp32 in LDS
-    for (int job = wave; job < 26; job += 4) {
-      if (job < 10) {
-        int ib, jb;
-        lower_tile(job, ib, jb);
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          acc = mfma(ld8(&Ks[(16 * ib + li) * KP + 32 * s + 8 * kq]),
-                     ld8(&Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), acc);
-        const int j = 16 * jb + li;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * ib + 4 * kq + r;
-          As[i * FP + j] = i > j ? bet[i] * expf(gam[i] - gam[j]) * acc[r] : 0.f;
-        }
-      } else {
-        const int pt = job - 10, ib = pt >> 2, jb = pt & 3;
-        f32x4 acc = zero4();
-        if (jb <= ib) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            acc = mfma(ld8(&Qs[(16 * ib + li) * KP + 32 * s + 8 * kq]),
-                       ld8(&Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), acc);
-        }
-        const int j = 16 * jb + li;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * ib + 4 * kq + r;
-          PS[i * FP + j] = i >= j ? expf(gam[i] - gam[j]) * acc[r] : 0.f;
-        }
-      }
-    }
-    for (int e = tid; e < 64 * 64; e += 256) {
-      const int i = e >> 6, j = e & 63;
-      if ((j >> 4) > (i >> 4)) Ts[i * FP + j] = 0.f;
-    }
-    __syncthreads();
-
-    // ---- T = (I + A)^-1
-    if (tid < 64) {
-      const int o16 = 16 * (tid >> 4), jc = tid & 15;
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float acc = i == jc ? 1.f : 0.f;
-#pragma unroll
-        for (int m = 0; m < i; ++m) acc -= As[(o16 + i) * FP + o16 + m] * x[m];
-        x[i] = acc;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) Ts[(o16 + i) * FP + o16 + jc] = x[i];
-    }
-    __syncthreads();
     {
-      const int r = tid >> 4, cc = tid & 15;
-      for (int ib = 1; ib < 4; ++ib) {
-        for (int jb = 0; jb < ib; ++jb) {
-          float acc = 0.f;
-          for (int m = 16 * jb; m < 16 * ib; ++m)
-            acc += As[(16 * ib + r) * FP + m] * Ts[m * FP + 16 * jb + cc];
-          Xs[jb * 256 + r * 16 + cc] = acc;
-        }
-        __syncthreads();
-        for (int jb = 0; jb < ib; ++jb) {
-          float acc = 0.f;
-#pragma unroll
-          for (int u = 0; u < 16; ++u)
-            acc += Ts[(16 * ib + r) * FP + 16 * ib + u] * Xs[jb * 256 + u * 16 + cc];
-          Ts[(16 * ib + r) * FP + 16 * jb + cc] = -acc;
-        }
-        __syncthreads();
-      }
+      const uint16_t* Tg = Tmat + blk * 8192;
+      const int i = (tid >> 3) & 63, j0 = (tid & 7) * 8;
+      *reinterpret_cast<uint4*>(&S.Tb[i * BP + j0]) =
+          *reinterpret_cast<const uint4*>(Tg + i * 64 + j0);
+      *reinterpret_cast<uint4*>(&S.TbT[i * BP + j0]) =
+          *reinterpret_cast<const uint4*>(Tg + 4096 + i * 64 + j0);
     }
-
-    // ---- dP = dO D^T (i >= j): G1 <- dP o Gamma, As <- F = dP o P
-    {
-      bf16x8 oa[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) oa[s] = ld8_or0(dOb + (size_t)trow * rs + 32 * s + 8 * kq, trow_ok);
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        f32x4 acc = zero4();
-        if (jb <= wave) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            acc = mfma(oa[s], ld8(Db + (16 * jb + li) * kHead + 32 * s + 8 * kq), acc);
-        }
-        // acc[r] = dP[i = 16 w + 4 kq + r][j = 16 jb + li]
-        const int j = 16 * jb + li;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * wave + 4 * kq + r;
-          const bool on = i >= j;
-          G1[i * FP + j] = on ? acc[r] * expf(gam[i] - gam[j]) : 0.f;
-          As[i * FP + j] = on ? acc[r] * PS[i * FP + j] : 0.f;
-        }
-      }
+    // clear the per-wave partial slots of this value head
+    for (int e = tid; e < 8 * 64; e += 512) {
+      (&S.colF[0][0])[e] = 0.f;
+      (&S.colE[0][0])[e] = 0.f;
     }
     __syncthreads();
-    // dgamma_i += sum_j F_ij - sum_j F_ji
-    if (tid < 64) {
-      float rsum = 0.f, csum = 0.f;
-      for (int j = 0; j < 64; ++j) {
-        rsum += As[tid * FP + j];
-        csum += As[j * FP + tid];
-      }
-      dgam[tid] += rsum - csum;
+
+    // own token rows of dO, D and dD (A operands of several products)
+    bf16x8 oa[4], da[4], ea[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      oa[s] = trow_ok ? ld8(dOb + (size_t)trow * rs + 32 * s + 8 * kq) : zero8();
+      da[s] = ld8(Db + trow * kHead + 32 * s + 8 * kq);
+      ea[s] = ld8(dDb + trow * kHead + 32 * s + 8 * kq);
     }
 
-    // ---- token-row products of this wave (contractions over v from global)
-    {
-      float dg_row[4] = {0.f, 0.f, 0.f, 0.f};   // per r: this lane's partial of row 16w+4kq+r
-      float dgl_part = 0.f;                     // partial of the dgamma_L term from K_bwd
-      bf16x8 oa[4], da[4], ea[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        oa[s] = ld8_or0(dOb + (size_t)trow * rs + 32 * s + 8 * kq, trow_ok);
-        da[s] = ld8(Db + trow * kHead + 32 * s + 8 * kq);
-        ea[s] = ld8(dDb + trow * kHead + 32 * s + 8 * kq);
-      }
-#pragma unroll
-      for (int kt = 0; kt < 8; ++kt) {
-        const int kr = 16 * kt + li;  // key column supplied by this lane as B operand
-        f32x4 x1 = zero4(), x2 = zero4(), x3 = zero4();
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 hf = ld8(hb + kr * kHead + 32 * s + 8 * kq);
-          x1 = mfma(oa[s], hf, x1);                                        // dO h^T
-          x3 = mfma(ea[s], hf, x3);                                        // dD h^T
-          x2 = mfma(da[s], ld8(dhb + kr * kHead + 32 * s + 8 * kq), x2);  // D dh'^T
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * wave + 4 * kq + r;
-          const float qk = bf2f(Qs[t * KP + kr]);
-          const float kk = bf2f(Ks[t * KP + kr]);
-          adq[kt][r] += eg[t] * x1[r];
-          dg_row[r] += eg[t] * qk * x1[r];          // inter-chunk output decay
-          adk[kt][r] += ebw[t] * x2[r];
-          const float dc = kk * x2[r];
-          dg_row[r] -= ebw[t] * dc;                 // K_bwd decay, token side
-          dgl_part += ebw[t] * dc;                  // K_bwd decay, gamma_L side
-        }
-        // dW = -dD h^T stored as [k][tok]
-        *reinterpret_cast<uint2*>(&dWs[kr * TP + 16 * wave + 4 * kq]) =
-            pack4_bf16(-x3[0], -x3[1], -x3[2], -x3[3]);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dg_row[r] = sum16(dg_row[r]);
-      dgl_part = wave_sum(dgl_part);
-      __syncthreads();  // dgam row/col pass above is done before these writes
-      if (li == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dgam[16 * wave + 4 * kq + r] += dg_row[r];
-      }
-      if (lane == 0) red[wave] = dgl_part;
-    }
-
-    // ---- dq~ += (dP o Gamma) K^ ; dk^ += (dP o Gamma)^T Q~
-#pragma unroll
-    for (int kt = 0; kt < 8; ++kt) {
-      f32x4 acq = adq[kt], ack = adk[kt];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8 kcol = gather8_bf16(&Ks[(32 * s + 8 * kq) * KP + 16 * kt + li], KP);
-        const bf16x8 qcol = gather8_bf16(&Qs[(32 * s + 8 * kq) * KP + 16 * kt + li], KP);
-        if (32 * s <= 16 * wave + 15)  // j <= i
-          acq = mfma(cvt8(&G1[trow * FP + 32 * s + 8 * kq]), kcol, acq);
-        if (32 * s + 31 >= 16 * wave)  // i >= j
-          ack = mfma(gather8_f32(&G1[(32 * s + 8 * kq) * FP + trow], FP), qcol, ack);
-      }
-      adq[kt] = acq;
-      adk[kt] = ack;
-    }
-    __syncthreads();  // dWs complete; G1 free
-
-    // ---- T^T dW: dk^ += diag(beta e^gamma) T^T dW; dbeta, dgamma of the W factor
+    // ---- dP = dO D^T (i >= j) and P from Q~K^T: Pm = dP o Gamma (+ transpose);
+    //      F = dP o P row / column partial sums. Wave: row tile tw, col tiles kh, kh + 2.
     {
       float rowp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kt = 0; kt < 8; ++kt) {
-        f32x4 z = zero4();
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const int jb = kh + 2 * q2;
+        const int j = 16 * jb + li;
+        float pv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (jb <= tw) {
+          f32x4 dp = zero4(), qk = zero4();
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          if (32 * s + 31 >= 16 * wave)  // T[m][t] needs m >= t
-            z = mfma(gather8_f32(&Ts[(32 * s + 8 * kq) * FP + trow], FP),
-                     ld8(&dWs[(16 * kt + li) * TP + 32 * s + 8 * kq]), z);
+          for (int s = 0; s < 4; ++s) {
+            dp = mfma(oa[s], ld8(Db + (16 * jb + li) * kHead + 32 * s + 8 * kq), dp);
+            qk = mfma(ld8(&S.Qs[trow * KP + 32 * s + 8 * kq]),
+                      ld8(&S.Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), qk);
+          }
+          float colp = 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * tw + 4 * kq + r;
+            if (i >= j) {
+              const float dpm = dp[r] * expf(S.gam[i] - S.gam[j]);
+              const float f = dpm * qk[r];
+              pv[r] = dpm;
+              rowp[r] += f;
+              colp += f;
+            }
+          }
+          colp += __shfl_xor(colp, 16, 64);
+          colp += __shfl_xor(colp, 32, 64);
+          if (kq == 0) S.colF[wave][j] = colp;
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * wave + 4 * kq + r;
-          adk[kt][r] += bet[t] * eg[t] * z[r];
-          rowp[r] += bf2f(Ks[t * KP + 16 * kt + li]) * z[r];
-        }
+        for (int r = 0; r < 4; ++r) S.Pm[(16 * tw + 4 * kq + r) * BP + j] = f2bf(pv[r]);
+        *reinterpret_cast<uint2*>(&S.PmT[j * BP + 16 * tw + 4 * kq]) =
+            pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) rowp[r] = sum16(rowp[r]);
       if (li == 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * wave + 4 * kq + r;
-          dbet[t] += eg[t] * rowp[r];
-          dgam[t] += bet[t] * eg[t] * rowp[r];
-        }
+        for (int r = 0; r < 4; ++r) S.rowF[kh][16 * tw + 4 * kq + r] = rowp[r];
       }
     }
 
-    // ---- dV = diag(beta) T^T dD (written as dv[t][v..v+3]); dbeta of the U factor
+    // ---- Z = T^T dD (written [tok][v]); dV = diag(beta) Z; dbeta of U.
+    //      Wave: token columns of tile tw, value tiles 4 kh .. 4 kh + 3.
     {
       float bp = 0.f;
+      bf16x8 tt[2];
 #pragma unroll
-      for (int vt = 0; vt < 8; ++vt) {
+      for (int s = 0; s < 2; ++s) tt[s] = ld8(&S.TbT[trow * BP + 32 * s + 8 * kq]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int vt = 4 * kh + j;
         f32x4 z = zero4();
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          if (32 * s + 31 >= 16 * wave)
-            z = mfma(ld8(dDTb + (16 * vt + li) * 64 + 32 * s + 8 * kq),
-                     gather8_f32(&Ts[(32 * s + 8 * kq) * FP + trow], FP), z);
-        }
-        // z[r] = (T^T dD)[t = trow][v = 16 vt + 4 kq + r]
+        for (int s = 0; s < 2; ++s)
+          if (32 * s + 31 >= 16 * tw)  // T[m][t] needs m >= t
+            z = mfma(ld8(dDTb + (16 * vt + li) * 64 + 32 * s + 8 * kq), tt[s], z);
+        // z[r] = Z[t = trow][v = 16 vt + 4 kq + r]
+        const int vv = 16 * vt + 4 * kq;
+        *reinterpret_cast<uint2*>(&S.rz.Z[trow * KP + vv]) = pack4_bf16(z[0], z[1], z[2], z[3]);
         if (trow_ok) {
-          const int vv = 16 * vt + 4 * kq;
           const uint2 vr = *reinterpret_cast<const uint2*>(vb + (size_t)trow * rs + vv);
           bp += bf2f(vr.x & 0xffffu) * z[0] + bf2f(vr.x >> 16) * z[1] +
                 bf2f(vr.y & 0xffffu) * z[2] + bf2f(vr.y >> 16) * z[3];
-          const float bt = bet[trow];
+          const float bt = S.bet[trow];
           *reinterpret_cast<uint2*>(dv + ((size_t)(t0 + trow) * HV + hv) * kHead + vv) =
               pack4_bf16(bt * z[0], bt * z[1], bt * z[2], bt * z[3]);
         }
       }
       bp += __shfl_xor(bp, 16, 64);
       bp += __shfl_xor(bp, 32, 64);
-      __syncthreads();  // the dbet writes of the previous block are done
-      if (kq == 0) dbet[trow] += bp;
-    }
-
-    // ---- dT = dD (beta V)^T + dW (beta e^gamma K^)^T, strictly lower -> As
-    {
-      bf16x8 ea[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) ea[s] = ld8(dDb + trow * kHead + 32 * s + 8 * kq);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        f32x4 a1 = zero4(), a2 = zero4();
-        if (mb <= wave) {
-          const int mrow = 16 * mb + li;
-          const bool mok = mrow < L;
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            a1 = mfma(ea[s], ld8_or0(vb + (size_t)mrow * rs + 32 * s + 8 * kq, mok), a1);
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            a2 = mfma(gather8_bf16(&dWs[(32 * s + 8 * kq) * TP + trow], TP),
-                      ld8(&Ks[mrow * KP + 32 * s + 8 * kq]), a2);
-        }
-        const int m = 16 * mb + li;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * wave + 4 * kq + r;
-          As[i * FP + m] = i > m ? bet[m] * (a1[r] + eg[m] * a2[r]) : 0.f;
-        }
-      }
+      if (kq == 0) S.rowB[kh][trow] = bp;
     }
     __syncthreads();
 
-    // ---- Y1 = dT T^T (lower) -> G1
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      f32x4 acc = zero4();
-      if (jb <= wave) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          acc = mfma(cvt8(&As[trow * FP + 32 * s + 8 * kq]),
-                     cvt8(&Ts[(16 * jb + li) * FP + 32 * s + 8 * kq]), acc);
-      }
-      const int j = 16 * jb + li;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * wave + 4 * kq + r;
-        G1[i * FP + j] = i > j ? acc[r] : 0.f;
-      }
-    }
-    __syncthreads();
-
-    // ---- dA = -T^T Y1 (i > j); M = dA o beta_i e^(gamma_i - gamma_j) -> As;
-    //      E = dA o A -> PS; dbeta and row part of dgamma of the A factor
+    // ---- key-column loops (columns 16 kt + li, kt = 4 kh .. 4 kh + 3), in two
+    //      passes to bound the live operands:
+    //      pass 1: x1 = dO h^T, x3 = dD h^T (= -dW), x4 = Z h^T (= -T^T dW),
+    //              y1 = (dP o Gamma) K^, y2 = (dP o Gamma)^T Q~
+    //      pass 2: x2 = D dh'^T, and <h, dh'> for the state-decay gradient
     {
-      float rb[4] = {0.f, 0.f, 0.f, 0.f}, re[4] = {0.f, 0.f, 0.f, 0.f};
+      float gr[4] = {0.f, 0.f, 0.f, 0.f}, br[4] = {0.f, 0.f, 0.f, 0.f};
+      float glp = 0.f, hd = 0.f;
+      {
+        bf16x8 za[4], pa[2], pta[2];
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        f32x4 acc = zero4(), kk = zero4();
-        if (jb <= wave) {
+        for (int s = 0; s < 4; ++s) za[s] = ld8(&S.rz.Z[trow * KP + 32 * s + 8 * kq]);
 #pragma unroll
-          for (int s = 0; s < 2; ++s)
-            if (32 * s + 31 >= 16 * wave)
-              acc = mfma(gather8_f32(&Ts[(32 * s + 8 * kq) * FP + trow], FP),
-                         gather8_f32(&G1[(32 * s + 8 * kq) * FP + 16 * jb + li], FP), acc);
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            kk = mfma(ld8(&Ks[trow * KP + 32 * s + 8 * kq]),
-                      ld8(&Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), kk);
+        for (int s = 0; s < 2; ++s) {
+          pa[s] = ld8(&S.Pm[trow * BP + 32 * s + 8 * kq]);
+          pta[s] = ld8(&S.PmT[trow * BP + 32 * s + 8 * kq]);
         }
-        const int j = 16 * jb + li;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * wave + 4 * kq + r;
-          float mval = 0.f, eval = 0.f;
-          if (i > j) {
-            const float da = -acc[r];
-            const float dec = expf(gam[i] - gam[j]);
-            mval = da * bet[i] * dec;
-            eval = mval * kk[r];
-            rb[r] += da * dec * kk[r];
-            re[r] += eval;
+        for (int j = 0; j < 4; ++j) {
+          const int kr = 16 * (4 * kh + j) + li;
+          bf16x8 hf[4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) hf[s] = ld8(hb + kr * kHead + 32 * s + 8 * kq);
+          f32x4 x1 = zero4(), x3 = zero4(), x4 = zero4(), y1 = zero4(), y2 = zero4();
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            x1 = mfma(oa[s], hf[s], x1);
+            x3 = mfma(ea[s], hf[s], x3);
+            x4 = mfma(za[s], hf[s], x4);
           }
-          As[i * FP + j] = mval;
-          PS[i * FP + j] = eval;
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            if (32 * s <= 16 * tw + 15)  // (dP o Gamma)[t][j] needs j <= t
+              y1 = mfma(pa[s], ld8(&S.KsT[kr * TP + 32 * s + 8 * kq]), y1);
+            if (32 * s + 31 >= 16 * tw)  // (dP o Gamma)[i][t] needs i >= t
+              y2 = mfma(pta[s], ld8(&S.QsT[kr * TP + 32 * s + 8 * kq]), y2);
+          }
+          const int tr = 16 * tw + 4 * kq;
+          const float4 qv = ld4_bf16(&S.QsT[kr * TP + tr]);
+          const float4 kv = ld4_bf16(&S.KsT[kr * TP + tr]);
+          const float qa_[4] = {qv.x, qv.y, qv.z, qv.w};
+          const float ka_[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = tr + r;
+            const float e = S.eg[t], bt = S.bet[t];
+            adq[j][r] += e * x1[r] + y1[r];
+            gr[r] += e * qa_[r] * x1[r];               // inter-chunk output decay
+            adk[j][r] += y2[r] - bt * e * x4[r];
+            const float zk = -ka_[r] * x4[r];          // k^ . (T^T dW)
+            br[r] += e * zk;
+            gr[r] += bt * e * zk;
+            S.rw.dW[t * KP + kr] = f2bf(-x3[r]);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kr = 16 * (4 * kh + j) + li;
+        bf16x8 df[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) df[s] = ld8(dhb + kr * kHead + 32 * s + 8 * kq);
+        f32x4 x2 = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) x2 = mfma(da[s], df[s], x2);
+        if (tw == 0) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) hd += dot8(ld8(hb + kr * kHead + 32 * s + 8 * kq), df[s]);
+        }
+        const int tr = 16 * tw + 4 * kq;
+        const float4 kv = ld4_bf16(&S.KsT[kr * TP + tr]);
+        const float ka_[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = tr + r;
+          const float bw = S.ebw[t];
+          adk[j][r] += bw * x2[r];
+          const float dc = ka_[r] * x2[r];
+          gr[r] -= bw * dc;                            // K_bwd decay, token side
+          glp += bw * dc;                              // K_bwd decay, gamma_L side
         }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        rb[r] = sum16(rb[r]);
-        re[r] = sum16(re[r]);
+        gr[r] = sum16(gr[r]);
+        br[r] = sum16(br[r]);
       }
       if (li == 0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int i = 16 * wave + 4 * kq + r;
-          dbet[i] += rb[r];
-          dgam[i] += re[r];
+          S.rowG[kh][16 * tw + 4 * kq + r] = gr[r];
+          S.rowB2[kh][16 * tw + 4 * kq + r] = br[r];
+        }
+      }
+      glp = wave_sum(glp);
+      hd = wave_sum(hd);
+      if (lane == 0) {
+        S.gl_part[wave] = glp;
+        S.hd_part[wave] = hd;
+      }
+    }
+    __syncthreads();
+
+    // ---- dT = dD (beta V)^T + dW (beta e^gamma K^)^T, strictly lower
+    //      (wave: row tile tw, col tiles kh, kh + 2)
+    {
+      bf16x8 wa[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) wa[s] = ld8(&S.rw.dW[trow * KP + 32 * s + 8 * kq]);
+      f32x4 acc[2];
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const int mb = kh + 2 * q2;
+        f32x4 a1 = zero4(), a2 = zero4();
+        if (mb <= tw) {
+          const int mrow = 16 * mb + li;
+          const bool mok = mrow < L;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            a1 = mfma(ea[s], mok ? ld8(vb + (size_t)mrow * rs + 32 * s + 8 * kq) : zero8(), a1);
+            a2 = mfma(wa[s], ld8(&S.Ks[mrow * KP + 32 * s + 8 * kq]), a2);
+          }
+        }
+        const int m = 16 * mb + li;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * tw + 4 * kq + r;
+          acc[q2][r] = i > m ? S.bet[m] * (a1[r] + S.eg[m] * a2[r]) : 0.f;
+        }
+      }
+      __syncthreads();  // every wave has read dW before dT overwrites the region
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const int m = 16 * (kh + 2 * q2) + li;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S.rz.dT[(16 * tw + 4 * kq + r) * BP + m] = f2bf(acc[q2][r]);
+      }
+    }
+    __syncthreads();
+
+    // ---- Y1 = dT T^T (i > j), stored transposed
+    {
+      bf16x8 ta[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) ta[s] = ld8(&S.rz.dT[trow * BP + 32 * s + 8 * kq]);
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const int jb = kh + 2 * q2;
+        f32x4 acc = zero4();
+        if (jb <= tw) {
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            acc = mfma(ta[s], ld8(&S.Tb[(16 * jb + li) * BP + 32 * s + 8 * kq]), acc);
+        }
+        const int j = 16 * jb + li;
+        float y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = (16 * tw + 4 * kq + r) > j ? acc[r] : 0.f;
+        *reinterpret_cast<uint2*>(&S.rw.Y1T[j * BP + 16 * tw + 4 * kq]) =
+            pack4_bf16(y[0], y[1], y[2], y[3]);
+      }
+    }
+    __syncthreads();
+
+    // ---- dA = -T^T Y1 (i > j); M = dA o beta_i Gamma -> Pm, PmT; E = dA o A sums; dbeta of A
+    {
+      bf16x8 ta[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) ta[s] = ld8(&S.TbT[trow * BP + 32 * s + 8 * kq]);
+      float re[4] = {0.f, 0.f, 0.f, 0.f}, rb[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const int jb = kh + 2 * q2;
+        const int j = 16 * jb + li;
+        float mv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (jb <= tw) {
+          f32x4 acc = zero4(), kk = zero4();
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            if (32 * s + 31 >= 16 * tw)
+              acc = mfma(ta[s], ld8(&S.rw.Y1T[(16 * jb + li) * BP + 32 * s + 8 * kq]), acc);
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            kk = mfma(ld8(&S.Ks[trow * KP + 32 * s + 8 * kq]),
+                      ld8(&S.Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), kk);
+          float colp = 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * tw + 4 * kq + r;
+            if (i > j) {
+              const float da_ = -acc[r];
+              const float dec = expf(S.gam[i] - S.gam[j]);
+              const float m_ = da_ * S.bet[i] * dec;
+              const float e_ = m_ * kk[r];
+              mv[r] = m_;
+              rb[r] += da_ * dec * kk[r];
+              re[r] += e_;
+              colp += e_;
+            }
+          }
+          colp += __shfl_xor(colp, 16, 64);
+          colp += __shfl_xor(colp, 32, 64);
+          if (kq == 0) S.colE[wave][j] = colp;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S.Pm[(16 * tw + 4 * kq + r) * BP + j] = f2bf(mv[r]);
+        *reinterpret_cast<uint2*>(&S.PmT[j * BP + 16 * tw + 4 * kq]) =
+            pack4_bf16(mv[0], mv[1], mv[2], mv[3]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        re[r] = sum16(re[r]);
+        rb[r] = sum16(rb[r]);
+      }
+      if (li == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          S.rowE[kh][16 * tw + 4 * kq + r] = re[r];
+          S.rowB3[kh][16 * tw + 4 * kq + r] = rb[r];
         }
       }
     }
     __syncthreads();
-    // column part of dgamma of the A factor; gamma_L terms; then dg, dbeta out
-    if (tid < 64) {
-      float csum = 0.f;
-      for (int i = 0; i < 64; ++i) csum += PS[i * FP + tid];
-      dgam[tid] -= csum;
-    }
-    {
-      // e^gamma_L <h, dh'> over the whole 128 x 128 state
-      float p = 0.f;
-      for (int e = tid; e < kHead * kHead / 8; e += 256) {
-        const uint4 a = *reinterpret_cast<const uint4*>(hb + 8 * e);
-        const uint4 d = *reinterpret_cast<const uint4*>(dhb + 8 * e);
-        const uint32_t* aw = reinterpret_cast<const uint32_t*>(&a);
-        const uint32_t* dw = reinterpret_cast<const uint32_t*>(&d);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          p += bf2f(aw[u] & 0xffffu) * bf2f(dw[u] & 0xffffu) + bf2f(aw[u] >> 16) * bf2f(dw[u] >> 16);
-      }
-      p = wave_sum(p);
-      if (lane == 0) red[4 + wave] = p;
-    }
-    __syncthreads();
+
+    // ---- gate gradients of this value head: fixed-order sums of the partial slots,
+    //      then dg = reverse cumsum of dgamma inside the chunk
     if (wave == 0) {
-      float x = lane < L ? dgam[lane] : 0.f;
-      if (lane == L - 1) {
-        const float hh = red[4] + red[5] + red[6] + red[7];
-        x += (red[0] + red[1] + red[2] + red[3]) + expf(gam[L - 1]) * hh;
+      const int t = lane;
+      float dgm = (S.rowF[0][t] + S.rowF[1][t]) + (S.rowG[0][t] + S.rowG[1][t]) +
+                  (S.rowE[0][t] + S.rowE[1][t]);
+#pragma unroll
+      for (int w = 0; w < 8; ++w) dgm -= S.colF[w][t] + S.colE[w][t];
+      const float dbt = (S.rowB[0][t] + S.rowB[1][t]) + (S.rowB2[0][t] + S.rowB2[1][t]) +
+                        (S.rowB3[0][t] + S.rowB3[1][t]);
+      float x = t < L ? dgm : 0.f;
+      if (t == L - 1) {
+        float glsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) glsum += S.gl_part[w];
+        const float hdsum = (S.hd_part[0] + S.hd_part[1]) + (S.hd_part[4] + S.hd_part[5]) +
+                            (S.hd_part[2] + S.hd_part[3]) + (S.hd_part[6] + S.hd_part[7]);
+        x += glsum + expf(S.gam[L - 1]) * hdsum;
       }
-      // reverse inclusive cumsum inside the chunk
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_down(x, off, 64);
         if (lane + off < 64) x += y;
       }
-      if (lane < L) {
-        dg[(size_t)(t0 + lane) * HV + hv] = x;
-        dbeta[(size_t)(t0 + lane) * HV + hv] = dbet[lane];
+      if (t < L) {
+        dg[(size_t)(t0 + t) * HV + hv] = x;
+        dbeta[(size_t)(t0 + t) * HV + hv] = dbt;
       }
     }
 
     // ---- dk^ += M K^ + M^T K^
-#pragma unroll
-    for (int kt = 0; kt < 8; ++kt) {
-      f32x4 ack = adk[kt];
+    {
+      bf16x8 ma[2], mta[2];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const bf16x8 kcol = gather8_bf16(&Ks[(32 * s + 8 * kq) * KP + 16 * kt + li], KP);
-        if (32 * s <= 16 * wave + 15)
-          ack = mfma(cvt8(&As[trow * FP + 32 * s + 8 * kq]), kcol, ack);
-        if (32 * s + 31 >= 16 * wave)
-          ack = mfma(gather8_f32(&As[(32 * s + 8 * kq) * FP + trow], FP), kcol, ack);
+        ma[s] = ld8(&S.Pm[trow * BP + 32 * s + 8 * kq]);
+        mta[s] = ld8(&S.PmT[trow * BP + 32 * s + 8 * kq]);
       }
-      adk[kt] = ack;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kr = 16 * (4 * kh + j) + li;
+        f32x4 acc = adk[j];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8 kc = ld8(&S.KsT[kr * TP + 32 * s + 8 * kq]);
+          if (32 * s <= 16 * tw + 15) acc = mfma(ma[s], kc, acc);
+          if (32 * s + 31 >= 16 * tw) acc = mfma(mta[s], kc, acc);
+        }
+        adk[j] = acc;
+      }
     }
     __syncthreads();  // everything is rewritten by the next value head
   }
 
-  // ---- L2-norm backward and scale; stage rows in LDS, then coalesced stores
+  // ---- L2-norm backward and scale: x^ . dx^ over all 128 columns (two halves)
+  float xq[4][4], xk[4][4];
   {
-    float dotq[4] = {0.f, 0.f, 0.f, 0.f}, dotk[4] = {0.f, 0.f, 0.f, 0.f};
-    float xq[8][4], xk[8][4];
+    float dq_[4] = {0.f, 0.f, 0.f, 0.f}, dk_[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kt = 0; kt < 8; ++kt)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * wave + 4 * kq + r;
-        const int kc = 16 * kt + li;
+        const int t = 16 * tw + 4 * kq + r;
+        const int kc = 16 * (4 * kh + j) + li;
         float qv = 0.f, kv = 0.f;
         if (t < L) {
           const size_t off = ((size_t)(t0 + t) * H + h) * kHead + kc;
-          qv = bf2f(q[off]) / nrm_q[t];
-          kv = bf2f(k[off]) / nrm_k[t];
+          qv = bf2f(q[off]) / S.nrm_q[t];
+          kv = bf2f(k[off]) / S.nrm_k[t];
         }
-        xq[kt][r] = qv;
-        xk[kt][r] = kv;
-        dotq[r] += qv * scale * adq[kt][r];
-        dotk[r] += kv * adk[kt][r];
+        xq[j][r] = qv;
+        xk[j][r] = kv;
+        dq_[r] += qv * scale * adq[j][r];
+        dk_[r] += kv * adk[j][r];
       }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      dotq[r] = sum16(dotq[r]);
-      dotk[r] = sum16(dotk[r]);
+      dq_[r] = sum16(dq_[r]);
+      dk_[r] = sum16(dk_[r]);
     }
-#pragma unroll
-    for (int kt = 0; kt < 8; ++kt)
+    if (li == 0) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * wave + 4 * kq + r;
-        const int kc = 16 * kt + li;
-        const float dqh = scale * adq[kt][r];
-        Qs[t * KP + kc] = f2bf((dqh - xq[kt][r] * dotq[r]) / nrm_q[t]);
-        Ks[t * KP + kc] = f2bf((adk[kt][r] - xk[kt][r] * dotk[r]) / nrm_k[t]);
+        S.dot_q[kh][16 * tw + 4 * kq + r] = dq_[r];
+        S.dot_k[kh][16 * tw + 4 * kq + r] = dk_[r];
       }
+    }
   }
   __syncthreads();
-  for (int e = tid; e < 64 * 16; e += 256) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * tw + 4 * kq + r;
+      const int kc = 16 * (4 * kh + j) + li;
+      const float dotq = S.dot_q[0][t] + S.dot_q[1][t];
+      const float dotk = S.dot_k[0][t] + S.dot_k[1][t];
+      const float dqh = scale * adq[j][r];
+      S.Qs[t * KP + kc] = f2bf((dqh - xq[j][r] * dotq) / S.nrm_q[t]);
+      S.Ks[t * KP + kc] = f2bf((adk[j][r] - xk[j][r] * dotk) / S.nrm_k[t]);
+    }
+  __syncthreads();
+  for (int e = tid; e < 64 * 16; e += 512) {
     const int t = e >> 4, sg = e & 15;
     if (t < L) {
       const size_t off = ((size_t)(t0 + t) * H + h) * kHead + sg * 8;
-      *reinterpret_cast<uint4*>(dq + off) = *reinterpret_cast<const uint4*>(&Qs[t * KP + sg * 8]);
-      *reinterpret_cast<uint4*>(dk + off) = *reinterpret_cast<const uint4*>(&Ks[t * KP + sg * 8]);
+      *reinterpret_cast<uint4*>(dq + off) = *reinterpret_cast<const uint4*>(&S.Qs[t * KP + sg * 8]);
+      *reinterpret_cast<uint4*>(dk + off) = *reinterpret_cast<const uint4*>(&S.Ks[t * KP + sg * 8]);
     }
   }
 }
@@ -784,10 +842,11 @@ hipError_t launch_bwd_dh_scan(const int32_t* seq_first, int N, int HV, int NC,
 hipError_t launch_bwd_chunk(const ChunkInfo* table, int NC, int H, int HV, float scale,
                             const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const float* g, const float* beta, const uint16_t* saved,
-                            const BwdBufs& bufs, const uint16_t* dO, uint16_t* dq, uint16_t* dk,
-                            uint16_t* dv, float* dg, float* dbeta, hipStream_t stream) {
-  hipLaunchKernelGGL(bwd_chunk_kernel, dim3(NC, H), dim3(256), 0, stream, table, NC, H, HV, scale,
-                     q, k, v, g, beta, saved, bufs, dO, dq, dk, dv, dg, dbeta);
+                            const uint16_t* Tmat, const BwdBufs& bufs, const uint16_t* dO,
+                            uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dg, float* dbeta,
+                            hipStream_t stream) {
+  hipLaunchKernelGGL(bwd_chunk_kernel, dim3(NC, H), dim3(512), 0, stream, table, NC, H, HV, scale,
+                     q, k, v, g, beta, saved, Tmat, bufs, dO, dq, dk, dv, dg, dbeta);
   return hipGetLastError();
 }
 

@@ -64,10 +64,48 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
       }
     }
 
-  const int c_begin = seq_first[seq], c_end = seq_first[seq + 1];
-  for (int c = c_begin; c < c_end; ++c) {
-    const ChunkInfo ci = table[c];
+  // Operands of one chunk in MFMA fragment layout; the next chunk's are loaded
+  // while the current one computes, so the chain never waits on memory.
+  struct Ops {
+    bf16x8 wa[4], qa[4], pa[2], ka[2][2];
+    uint2 u[VT];
+    float gl;
+    ChunkInfo ci;
+  };
+  auto load_ops = [&](int c, Ops& x) {
     const size_t blk = (size_t)hv * NC + c;
+    const uint16_t* Wb = prep.W + blk * 8192;
+    const uint16_t* Ub = prep.U + blk * 8192;
+    const uint16_t* Qb = prep.Qg + blk * 8192;
+    const uint16_t* Pb = prep.P + blk * 4096;
+    const uint16_t* Kb = prep.Kb + blk * 8192;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      x.wa[s] = ld8(Wb + (16 * wave + li) * kHead + 32 * s + 8 * kq);
+      x.qa[s] = ld8(Qb + (16 * wave + li) * kHead + 32 * s + 8 * kq);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) x.pa[s] = ld8(Pb + (16 * wave + li) * 64 + 32 * s + 8 * kq);
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        x.ka[dt][s] = ld8(Kb + (16 * (2 * wave + dt) + li) * 64 + 32 * s + 8 * kq);
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt)
+      x.u[vt] = *reinterpret_cast<const uint2*>(Ub + (size_t)(v0 + 16 * vt + li) * 64 +
+                                                16 * wave + 4 * kq);
+    x.gl = prep.gL[blk];
+    x.ci = table[c];
+  };
+
+  const int c_begin = seq_first[seq], c_end = seq_first[seq + 1];
+  Ops nxt;
+  if (c_begin < c_end) load_ops(c_begin, nxt);
+  for (int c = c_begin; c < c_end; ++c) {
+    const Ops cur = nxt;
+    if (c + 1 < c_end) load_ops(c + 1, nxt);
+    const ChunkInfo ci = cur.ci;
 
     // 1. chunk-start state -> LDS (bf16)
 #pragma unroll
@@ -90,25 +128,17 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     }
 
     // 2. D = U - W h; wave w owns tokens 16 w .. 16 w + 15
-    {
-      const uint16_t* Wb = prep.W + blk * 8192;
-      const uint16_t* Ub = prep.U + blk * 8192;
-      bf16x8 wa[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) wa[s] = ld8(Wb + (16 * wave + li) * kHead + 32 * s + 8 * kq);
+    for (int vt = 0; vt < VT; ++vt) {
+      f32x4 acc = zero4();
 #pragma unroll
-      for (int vt = 0; vt < VT; ++vt) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          acc = mfma(wa[s], ld8(&Ss[(16 * vt + li) * SP + 32 * s + 8 * kq]), acc);
-        // acc[r] = (W h)[t = 16 w + 4 kq + r][v = 16 vt + li]
-        const uint2 u = *reinterpret_cast<const uint2*>(Ub + (size_t)(v0 + 16 * vt + li) * 64 +
-                                                        16 * wave + 4 * kq);
-        *reinterpret_cast<uint2*>(&Ds[(16 * vt + li) * DP + 16 * wave + 4 * kq]) =
-            pack4_bf16(bf2f(u.x & 0xffffu) - acc[0], bf2f(u.x >> 16) - acc[1],
-                       bf2f(u.y & 0xffffu) - acc[2], bf2f(u.y >> 16) - acc[3]);
-      }
+      for (int s = 0; s < 4; ++s)
+        acc = mfma(cur.wa[s], ld8(&Ss[(16 * vt + li) * SP + 32 * s + 8 * kq]), acc);
+      // acc[r] = (W h)[t = 16 w + 4 kq + r][v = 16 vt + li]
+      const uint2 u = cur.u[vt];
+      *reinterpret_cast<uint2*>(&Ds[(16 * vt + li) * DP + 16 * wave + 4 * kq]) =
+          pack4_bf16(bf2f(u.x & 0xffffu) - acc[0], bf2f(u.x >> 16) - acc[1],
+                     bf2f(u.y & 0xffffu) - acc[2], bf2f(u.y >> 16) - acc[3]);
     }
     __syncthreads();
     // saved for the backward: D as [tok][v] rows
@@ -122,24 +152,16 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
 
     // 3. O^T = S Q_g^T + D^T P^T; wave w owns tokens 16 w .. 16 w + 15
     {
-      const uint16_t* Qb = prep.Qg + blk * 8192;
-      const uint16_t* Pb = prep.P + blk * 4096;
-      bf16x8 qa[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) qa[s] = ld8(Qb + (16 * wave + li) * kHead + 32 * s + 8 * kq);
-      bf16x8 pa[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) pa[s] = ld8(Pb + (16 * wave + li) * 64 + 32 * s + 8 * kq);
       const int tl = 16 * wave + li;
 #pragma unroll
       for (int vt = 0; vt < VT; ++vt) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          acc = mfma(ld8(&Ss[(16 * vt + li) * SP + 32 * s + 8 * kq]), qa[s], acc);
+          acc = mfma(ld8(&Ss[(16 * vt + li) * SP + 32 * s + 8 * kq]), cur.qa[s], acc);
         // P is lower triangular: tokens j > 16 w + 15 contribute nothing
-        acc = mfma(ld8(&Ds[(16 * vt + li) * DP + 8 * kq]), pa[0], acc);
-        if (wave >= 2) acc = mfma(ld8(&Ds[(16 * vt + li) * DP + 32 + 8 * kq]), pa[1], acc);
+        acc = mfma(ld8(&Ds[(16 * vt + li) * DP + 8 * kq]), cur.pa[0], acc);
+        if (wave >= 2) acc = mfma(ld8(&Ds[(16 * vt + li) * DP + 32 + 8 * kq]), cur.pa[1], acc);
         // acc[r] = O[t = t0 + 16 w + li][v = v0 + 16 vt + 4 kq + r]
         if (tl < ci.len)
           *reinterpret_cast<uint2*>(o + ((size_t)(ci.t0 + tl) * HV + hv) * kHead + v0 + 16 * vt +
@@ -148,25 +170,16 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     }
 
     // 4. h <- e^gamma_L h + K_bwd^T D; wave w owns key rows 32 w .. 32 w + 31
-    {
-      const uint16_t* Kb = prep.Kb + blk * 8192;
-      const float gl = prep.gL[blk];
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        bf16x8 ka[2];
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) {
+        f32x4 acc = h[dt][vt] * cur.gl;
 #pragma unroll
         for (int s = 0; s < 2; ++s)
-          ka[s] = ld8(Kb + (16 * (2 * wave + dt) + li) * 64 + 32 * s + 8 * kq);
-#pragma unroll
-        for (int vt = 0; vt < VT; ++vt) {
-          f32x4 acc = h[dt][vt] * gl;
-#pragma unroll
-          for (int s = 0; s < 2; ++s)
-            acc = mfma(ka[s], ld8(&Ds[(16 * vt + li) * DP + 32 * s + 8 * kq]), acc);
-          h[dt][vt] = acc;
-        }
+          acc = mfma(cur.ka[dt][s], ld8(&Ds[(16 * vt + li) * DP + 32 * s + 8 * kq]), acc);
+        h[dt][vt] = acc;
       }
-    }
     __syncthreads();
   }
 

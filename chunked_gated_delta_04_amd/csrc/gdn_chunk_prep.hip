@@ -113,11 +113,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 
   __shared__ __align__(16) uint16_t Ks[64 * KP];   // k^ rows (bf16)
   __shared__ __align__(16) uint16_t Qs[64 * KP];   // q~ rows (bf16)
-  __shared__ __align__(16) float As[64 * FP];      // A (strictly lower)
-  __shared__ __align__(16) float Ts[64 * FP];      // T = (I + A)^-1
+  __shared__ __align__(16) float Ts[64 * FP];      // A (strictly lower), inverted in place into T
   __shared__ __align__(16) uint16_t Xt[128 * TP];  // (beta e^gamma K^)^T, then (beta V)^T
   __shared__ float gam[64], bet[64], eg[64], ebw[64];
-  __shared__ float Xs[3 * 256];
+  __shared__ float Xs[3 * 256];  // solve scratch
 
   // ---- 1. load and L2-normalise q, k rows (thread: row tid/4, 32 columns)
   {
@@ -205,7 +204,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 16 * ib + 4 * kq + r;
-          As[i * FP + j] = i > j ? bet[i] * expf(gam[i] - gam[j]) * acc[r] : 0.f;
+          Ts[i * FP + j] = i > j ? bet[i] * expf(gam[i] - gam[j]) * acc[r] : 0.f;
         }
       } else {
         const int pt = job - 10, ib = pt >> 2, jb = pt & 3;  // P tile (row block ib, col block jb)
@@ -255,42 +254,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     }
     __syncthreads();
 
-    // ---- 4. T = (I + A)^-1: diagonal 16x16 blocks by forward substitution ...
-    if (tid < 64) {
-      const int o16 = 16 * (tid >> 4), jc = tid & 15;
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float acc = i == jc ? 1.f : 0.f;
-#pragma unroll
-        for (int m = 0; m < i; ++m) acc -= As[(o16 + i) * FP + o16 + m] * x[m];
-        x[i] = acc;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) Ts[(o16 + i) * FP + o16 + jc] = x[i];
-    }
-    __syncthreads();
-    // ... then block rows: T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj
-    {
-      const int r = tid >> 4, cc = tid & 15;
-      for (int ib = 1; ib < 4; ++ib) {
-        for (int jb = 0; jb < ib; ++jb) {
-          float acc = 0.f;
-          for (int m = 16 * jb; m < 16 * ib; ++m)
-            acc += As[(16 * ib + r) * FP + m] * Ts[m * FP + 16 * jb + cc];
-          Xs[jb * 256 + r * 16 + cc] = acc;
-        }
-        __syncthreads();
-        for (int jb = 0; jb < ib; ++jb) {
-          float acc = 0.f;
-#pragma unroll
-          for (int u = 0; u < 16; ++u)
-            acc += Ts[(16 * ib + r) * FP + 16 * ib + u] * Xs[jb * 256 + u * 16 + cc];
-          Ts[(16 * ib + r) * FP + 16 * jb + cc] = -acc;
-        }
-        __syncthreads();
-      }
-    }
+    // ---- 4. T = (I + A)^-1 in place
+    invert_unit_lower_64(Ts, Xs, tid, 256);
 
     // ---- 5. Xt = (beta e^gamma K^)^T  [k][tok]; Q_g and K_bwd to global
     for (int e = tid; e < 128 * 8; e += 256) {
@@ -363,6 +328,28 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
       }
     }
     __syncthreads();
+
+    // T and T^T in bf16 for the backward's gradient pass
+    if (kBwd) {
+      uint16_t* Tg = out.T + blk * 8192;
+      const int i = tid >> 2, j0 = (tid & 3) * 16;
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        uint4 o4, t4;
+        uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
+        uint32_t* tw4 = reinterpret_cast<uint32_t*>(&t4);
+        const int jj = j0 + 8 * hlf;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          ow[u] = (uint32_t)f2bf(Ts[i * FP + jj + 2 * u]) |
+                  ((uint32_t)f2bf(Ts[i * FP + jj + 2 * u + 1]) << 16);
+          tw4[u] = (uint32_t)f2bf(Ts[(jj + 2 * u) * FP + i]) |
+                   ((uint32_t)f2bf(Ts[(jj + 2 * u + 1) * FP + i]) << 16);
+        }
+        *reinterpret_cast<uint4*>(Tg + i * 64 + jj) = o4;
+        *reinterpret_cast<uint4*>(Tg + 4096 + i * 64 + jj) = t4;
+      }
+    }
 
     // ---- 6. W: 32 tiles of 16x16 over 4 waves, contraction over the chunk (2 steps)
     {

@@ -79,6 +79,62 @@ __device__ __forceinline__ bf16x8 gather8_f32(const float* p, int pitch) {
   return r;
 }
 
+// In-place inverse of I + A for a strictly lower-triangular 64 x 64 fp32 matrix A
+// in LDS (row pitch 68): on return T = (I + A)^-1, unit lower triangular, with
+// zeros above the diagonal blocks as on entry. Blocked in 16 x 16: each
+// diagonal block by forward substitution (one column per thread), then block
+// rows i = 1..3 from T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj. scratch: 768
+// floats. Must be called by every thread of the workgroup (it synchronises);
+// threads with tid >= 256 only take part in the barriers. Fixed summation order.
+__device__ __forceinline__ void invert_unit_lower_64(float* M, float* scratch, int tid,
+                                                     int nthreads) {
+  constexpr int P = 68;
+  float x[16];
+  if (tid < 64) {
+    const int o16 = 16 * (tid >> 4), jc = tid & 15;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float acc = i == jc ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) acc -= M[(o16 + i) * P + o16 + m] * x[m];
+      x[i] = acc;
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int o16 = 16 * (tid >> 4), jc = tid & 15;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) M[(o16 + i) * P + o16 + jc] = x[i];
+  }
+  __syncthreads();
+  const int r = (tid >> 4) & 15, cc = tid & 15;
+  for (int ib = 1; ib < 4; ++ib) {
+    if (tid < 256) {
+      for (int jb = 0; jb < ib; ++jb) {
+        float a4[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int mb = jb; mb < ib; ++mb) {
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            a4[u & 3] += M[(16 * ib + r) * P + 16 * mb + u] * M[(16 * mb + u) * P + 16 * jb + cc];
+        }
+        scratch[jb * 256 + r * 16 + cc] = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+      }
+    }
+    __syncthreads();
+    if (tid < 256) {
+      for (int jb = 0; jb < ib; ++jb) {
+        float a4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          a4[u & 3] += M[(16 * ib + r) * P + 16 * ib + u] * scratch[jb * 256 + u * 16 + cc];
+        M[(16 * ib + r) * P + 16 * jb + cc] = -((a4[0] + a4[1]) + (a4[2] + a4[3]));
+      }
+    }
+    __syncthreads();
+  }
+  (void)nthreads;
+}
+
 // Saved-for-backward block of one (chunk, value head): the chunk-start state
 // h = S^T as [k][v] bf16, then the chunk's D as [tok][v] bf16.
 constexpr int kSavedH = kHead * kHead;

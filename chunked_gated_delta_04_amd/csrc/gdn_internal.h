@@ -17,6 +17,7 @@ struct PrepOut {
   uint16_t* P;   // 64 x 64
   uint16_t* Kb;  // 128 x 64
   float* gL;     // 1 per block
+  uint16_t* T;   // T then T^T, 2 x 64 x 64 per block (backward layout only)
 };
 
 // Backward scratch per (value head, chunk) block, blk = hv * NC + c.
@@ -46,7 +47,8 @@ hipError_t launch_bwd_dh_scan(const int32_t* seq_first, int N, int HV, int NC,
 hipError_t launch_bwd_chunk(const ChunkInfo* table, int NC, int H, int HV, float scale,
                             const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const float* g, const float* beta, const uint16_t* saved,
-                            const BwdBufs& bufs, const uint16_t* dO, uint16_t* dq, uint16_t* dk,
+                            const uint16_t* Tmat, const BwdBufs& bufs, const uint16_t* dO,
+                            uint16_t* dq, uint16_t* dk,
                             uint16_t* dv, float* dg, float* dbeta, hipStream_t stream);
 
 hipError_t launch_state_copy(const float* src, float* dst, size_t n, hipStream_t stream);
