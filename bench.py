@@ -108,18 +108,98 @@ def cpu_baseline(inp, target_s):
                         f"visible; numpy einsum runs on 1)"))
 
 
+def copy_probe(mib):
+    """A plain device-to-device copy of known size, for scaling the HBM byte
+    counters (FETCH_SIZE / WRITE_SIZE) of a profiler run."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_per_dispatch": n * 4, "dispatches": 3}), flush=True)
+
+
+def time_call(h, stream, fn, steps, warmup):
+    """Average ms of fn() over `steps` calls, HIP events on `stream`."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = make_events(h, 2)
+    h.hipEventRecord(ev[0], ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(steps):
+        fn()
+    h.hipEventRecord(ev[1], ctypes.c_void_p(stream.cuda_stream))
+    h.hipEventSynchronize(ev[1])
+    return elapsed_ms(h, ev[0], ev[1]) / steps
+
+
+def secondary(h, stream, steps, warmup):
+    """Forward-only throughput on the 4 x 4096 and the 12-sequence varlen packs, and
+    the decode step against the HBM roofline."""
+    import torch
+    from chunked_gated_delta_04_amd import gdn, synth
+    out = {}
+    for name in ("fwd_4x4096_h16_hv32", "fwd_varlen12_32768_h16_hv32"):
+        inp = synth.workload_inputs(name)
+        d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        T, H, _ = inp["q"].shape
+        HV = inp["v"].shape[1]
+        N = inp["cu_seqlens"].numel() - 1
+        p = gdn.make_problem(N, T, H, HV, d["cu_seqlens"], inp["cu_seqlens"])
+        o = torch.empty(T, HV, 128, dtype=torch.bfloat16, device="cuda")
+        hT = torch.empty(N, HV, 128, 128, dtype=torch.float32, device="cuda")
+        ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(p), dtype=torch.uint8, device="cuda")
+        ms = time_call(h, stream, lambda: gdn.gdn_chunk_fwd(
+            p, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], o, hT, None, ws, stream),
+            steps, warmup)
+        out[name] = {"ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1)}
+        del d, o, hT, ws
+    name = "decode_256_pool512_h16_hv32"
+    inp = synth.workload_inputs(name)
+    d = {k: v.cuda() for k, v in inp.items()}
+    N, H, _ = inp["q"].shape
+    HV = inp["v"].shape[1]
+    o = torch.empty(N, HV, 128, dtype=torch.bfloat16, device="cuda")
+    slots = d["state_pool"].shape[0]
+    ms = time_call(h, stream, lambda: gdn.gdn_recurrent_step(
+        N, H, HV, 128, 128, 0.0, d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"],
+        d["dt_bias"], d["state_pool"], slots, d["ssm_state_indices"], None, o, stream),
+        steps, warmup)
+    active = int((inp["ssm_state_indices"] > 0).sum())
+    # algorithmic bytes: the active rows' fp32 state read and written once, their q, k, v,
+    # a, b read once, every o row written, the index vector and the per-head A_log/dt_bias
+    state = active * HV * 128 * 128 * 4 * 2
+    io = active * (2 * H * 128 * 2 + HV * 128 * 2 + 2 * HV * 2) + N * HV * 128 * 2 + N * 4 + HV * 8
+    bytes_ = state + io
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    out[name] = {"ms": round(ms, 4), "rows_per_s": round(N / (ms * 1e-3), 1),
+                 "algorithmic_bytes": bytes_, "achieved_GBps": round(gbs, 1),
+                 "hbm_frac": round(gbs * 1e9 / PEAK_HBM, 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the forward-only and decode timings")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
 
     import torch
     from chunked_gated_delta_04_amd import gdn, synth
@@ -205,6 +285,11 @@ def main():
                 "unit": "TFLOP/s", "frac": round(dom_achieved * 1e12 / PEAK_BF16, 5),
                 "traffic": None, "kernel": dom, "kernel_ms": round(stage_ms[dom], 4)}
 
+    extra = None
+    if not args.no_secondary:
+        del d, saved, wsf, wsb
+        extra = secondary(h, stream, args.steps, args.warmup)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, args.cpu_seconds)
@@ -224,6 +309,7 @@ def main():
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "secondary": extra,
     }
     print(json.dumps(out), flush=True)
 

@@ -89,7 +89,8 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
       }
     }
 
-  static_assert(kChunk * (VB / 8) == 256, "one dO segment per thread");
+  static_assert(kChunk * (VB / 8) <= 256, "at most one dO segment per thread");
+  const bool o_ok = tid < kChunk * (VB / 8);
   struct Ops {
     bf16x8 pa[2], ka[4], qa[2][2], wa[2][2];
     uint4 dO;
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
     x.gl = prep.gL[blk];
     x.ci = table[c];
     x.dO = make_uint4(0, 0, 0, 0);
-    if (ot < x.ci.len)
+    if (o_ok && ot < x.ci.len)
       x.dO = *reinterpret_cast<const uint4*>(dO + ((size_t)(x.ci.t0 + ot) * HV + hv) * kHead + v0 +
                                              8 * osg);
   };
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
         *reinterpret_cast<uint2*>(&Hs[(16 * vt + li) * SP + kk]) =
             pack4_bf16(dh[dt][vt][0], dh[dt][vt][1], dh[dt][vt][2], dh[dt][vt][3]);
       }
-    {
+    if (o_ok) {
       const uint16_t* xs = reinterpret_cast<const uint16_t*>(&cur.dO);
 #pragma unroll
       for (int u = 0; u < 8; ++u) Os[(8 * osg + u) * DP + ot] = xs[u];
@@ -159,12 +160,19 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
     // 2. dD = P^T dO + K_bwd dh; wave w owns tokens 16 w .. 16 w + 15
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt) {
-      f32x4 acc = zero4();
-      if (wave < 2) acc = mfma(cur.pa[0], ld8(&Os[(16 * vt + li) * DP + 8 * kq]), acc);
-      acc = mfma(cur.pa[1], ld8(&Os[(16 * vt + li) * DP + 32 + 8 * kq]), acc);
+      bf16x8 ob[2], hb4[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        acc = mfma(cur.ka[s], ld8(&Hs[(16 * vt + li) * SP + 32 * s + 8 * kq]), acc);
+      for (int s = 0; s < 2; ++s) ob[s] = ld8(&Os[(16 * vt + li) * DP + 32 * s + 8 * kq]);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) hb4[s] = ld8(&Hs[(16 * vt + li) * SP + 32 * s + 8 * kq]);
+      // two independent partial sums, so the MFMAs do not wait on each other
+      f32x4 a0 = mfma(cur.ka[0], hb4[0], zero4());
+      f32x4 a1 = mfma(cur.ka[1], hb4[1], zero4());
+      a0 = mfma(cur.ka[2], hb4[2], a0);
+      a1 = mfma(cur.ka[3], hb4[3], a1);
+      a1 = mfma(cur.pa[1], ob[1], a1);
+      if (wave < 2) a0 = mfma(cur.pa[0], ob[0], a0);
+      const f32x4 acc = a0 + a1;
       // acc[r] = dD[t = 16 w + 4 kq + r][v = 16 vt + li]
       *reinterpret_cast<uint2*>(&Es[(16 * vt + li) * DP + 16 * wave + 4 * kq]) =
           pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
@@ -401,18 +409,13 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     }
     __syncthreads();
 
-    // own token rows of dO, D and dD (A operands of several products)
-    bf16x8 oa[4], da[4], ea[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      oa[s] = trow_ok ? ld8(dOb + (size_t)trow * rs + 32 * s + 8 * kq) : zero8();
-      da[s] = ld8(Db + trow * kHead + 32 * s + 8 * kq);
-      ea[s] = ld8(dDb + trow * kHead + 32 * s + 8 * kq);
-    }
-
     // ---- dP = dO D^T (i >= j) and P from Q~K^T: Pm = dP o Gamma (+ transpose);
     //      F = dP o P row / column partial sums. Wave: row tile tw, col tiles kh, kh + 2.
     {
+      bf16x8 oa[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        oa[s] = trow_ok ? ld8(dOb + (size_t)trow * rs + 32 * s + 8 * kq) : zero8();
       float rowp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
@@ -491,14 +494,18 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 
     // ---- key-column loops (columns 16 kt + li, kt = 4 kh .. 4 kh + 3), in two
     //      passes to bound the live operands:
-    //      pass 1: x1 = dO h^T, x3 = dD h^T (= -dW), x4 = Z h^T (= -T^T dW),
+    //      pass 1: x1 = dO h^T, x4 = Z h^T (= -T^T dW),
     //              y1 = (dP o Gamma) K^, y2 = (dP o Gamma)^T Q~
-    //      pass 2: x2 = D dh'^T, and <h, dh'> for the state-decay gradient
+    //      pass 2: x3 = dD h^T (= -dW), stored for dT
+    //      pass 3: x2 = D dh'^T, and <h, dh'> for the state-decay gradient
     {
       float gr[4] = {0.f, 0.f, 0.f, 0.f}, br[4] = {0.f, 0.f, 0.f, 0.f};
       float glp = 0.f, hd = 0.f;
       {
-        bf16x8 za[4], pa[2], pta[2];
+        bf16x8 oa[4], za[4], pa[2], pta[2];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          oa[s] = trow_ok ? ld8(dOb + (size_t)trow * rs + 32 * s + 8 * kq) : zero8();
 #pragma unroll
         for (int s = 0; s < 4; ++s) za[s] = ld8(&S.rz.Z[trow * KP + 32 * s + 8 * kq]);
 #pragma unroll
@@ -512,11 +519,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
           bf16x8 hf[4];
 #pragma unroll
           for (int s = 0; s < 4; ++s) hf[s] = ld8(hb + kr * kHead + 32 * s + 8 * kq);
-          f32x4 x1 = zero4(), x3 = zero4(), x4 = zero4(), y1 = zero4(), y2 = zero4();
+          f32x4 x1 = zero4(), x4 = zero4(), y1 = zero4(), y2 = zero4();
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             x1 = mfma(oa[s], hf[s], x1);
-            x3 = mfma(ea[s], hf[s], x3);
             x4 = mfma(za[s], hf[s], x4);
           }
 #pragma unroll
@@ -541,10 +547,27 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
             const float zk = -ka_[r] * x4[r];          // k^ . (T^T dW)
             br[r] += e * zk;
             gr[r] += bt * e * zk;
-            S.rw.dW[t * KP + kr] = f2bf(-x3[r]);
           }
         }
       }
+      {
+        bf16x8 ea[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) ea[s] = ld8(dDb + trow * kHead + 32 * s + 8 * kq);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kr = 16 * (4 * kh + j) + li;
+          f32x4 x3 = zero4();
+#pragma unroll
+          for (int s = 0; s < 4; ++s) x3 = mfma(ea[s], ld8(hb + kr * kHead + 32 * s + 8 * kq), x3);
+          const int tr = 16 * tw + 4 * kq;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S.rw.dW[(tr + r) * KP + kr] = f2bf(-x3[r]);
+        }
+      }
+      bf16x8 da[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) da[s] = ld8(Db + trow * kHead + 32 * s + 8 * kq);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int kr = 16 * (4 * kh + j) + li;
@@ -595,9 +618,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     // ---- dT = dD (beta V)^T + dW (beta e^gamma K^)^T, strictly lower
     //      (wave: row tile tw, col tiles kh, kh + 2)
     {
-      bf16x8 wa[4];
+      bf16x8 wa[4], ea[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) wa[s] = ld8(&S.rw.dW[trow * KP + 32 * s + 8 * kq]);
+      for (int s = 0; s < 4; ++s) {
+        wa[s] = ld8(&S.rw.dW[trow * KP + 32 * s + 8 * kq]);
+        ea[s] = ld8(dDb + trow * kHead + 32 * s + 8 * kq);
+      }
       f32x4 acc[2];
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
@@ -825,7 +851,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
   }
 }
 
-constexpr int kBwdVB = 32;
+int scan_value_block(long chains);  // shared with the forward scan
 
 hipError_t launch_bwd_dh_scan(const int32_t* seq_first, int N, int HV, int NC,
                               const ChunkInfo* table, const PrepOut& prep, const uint16_t* dO,
@@ -833,9 +859,14 @@ hipError_t launch_bwd_dh_scan(const int32_t* seq_first, int N, int HV, int NC,
                               hipStream_t stream) {
   const long chains = (long)N * HV;
   const long groups = (chains + 7) / 8;
-  const long blocks = groups * 8 * (kHead / kBwdVB);
-  hipLaunchKernelGGL(bwd_dh_scan_kernel<kBwdVB>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     seq_first, N, HV, NC, table, prep, dO, dhT, dh0, bufs);
+  const int vb = scan_value_block(chains);
+  const long blocks = groups * 8 * (kHead / vb);
+  if (vb == 16)
+    hipLaunchKernelGGL(bwd_dh_scan_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       seq_first, N, HV, NC, table, prep, dO, dhT, dh0, bufs);
+  else
+    hipLaunchKernelGGL(bwd_dh_scan_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       seq_first, N, HV, NC, table, prep, dO, dhT, dh0, bufs);
   return hipGetLastError();
 }
 

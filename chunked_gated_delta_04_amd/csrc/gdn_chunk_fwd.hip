@@ -130,10 +130,15 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     // 2. D = U - W h; wave w owns tokens 16 w .. 16 w + 15
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt) {
-      f32x4 acc = zero4();
+      bf16x8 sb[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        acc = mfma(cur.wa[s], ld8(&Ss[(16 * vt + li) * SP + 32 * s + 8 * kq]), acc);
+      for (int s = 0; s < 4; ++s) sb[s] = ld8(&Ss[(16 * vt + li) * SP + 32 * s + 8 * kq]);
+      // two independent partial sums, so the MFMAs do not wait on each other
+      f32x4 a0 = mfma(cur.wa[0], sb[0], zero4());
+      f32x4 a1 = mfma(cur.wa[1], sb[1], zero4());
+      a0 = mfma(cur.wa[2], sb[2], a0);
+      a1 = mfma(cur.wa[3], sb[3], a1);
+      const f32x4 acc = a0 + a1;
       // acc[r] = (W h)[t = 16 w + 4 kq + r][v = 16 vt + li]
       const uint2 u = cur.u[vt];
       *reinterpret_cast<uint2*>(&Ds[(16 * vt + li) * DP + 16 * wave + 4 * kq]) =
@@ -155,13 +160,19 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
       const int tl = 16 * wave + li;
 #pragma unroll
       for (int vt = 0; vt < VT; ++vt) {
-        f32x4 acc = zero4();
+        bf16x8 sb[4], db[2];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          acc = mfma(ld8(&Ss[(16 * vt + li) * SP + 32 * s + 8 * kq]), cur.qa[s], acc);
+        for (int s = 0; s < 4; ++s) sb[s] = ld8(&Ss[(16 * vt + li) * SP + 32 * s + 8 * kq]);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) db[s] = ld8(&Ds[(16 * vt + li) * DP + 32 * s + 8 * kq]);
+        f32x4 a0 = mfma(sb[0], cur.qa[0], zero4());
+        f32x4 a1 = mfma(sb[1], cur.qa[1], zero4());
+        a0 = mfma(sb[2], cur.qa[2], a0);
+        a1 = mfma(sb[3], cur.qa[3], a1);
         // P is lower triangular: tokens j > 16 w + 15 contribute nothing
-        acc = mfma(ld8(&Ds[(16 * vt + li) * DP + 8 * kq]), cur.pa[0], acc);
-        if (wave >= 2) acc = mfma(ld8(&Ds[(16 * vt + li) * DP + 32 + 8 * kq]), cur.pa[1], acc);
+        a0 = mfma(db[0], cur.pa[0], a0);
+        if (wave >= 2) a1 = mfma(db[1], cur.pa[1], a1);
+        const f32x4 acc = a0 + a1;
         // acc[r] = O[t = t0 + 16 w + li][v = v0 + 16 vt + 4 kq + r]
         if (tl < ci.len)
           *reinterpret_cast<uint2*>(o + ((size_t)(ci.t0 + tl) * HV + hv) * kHead + v0 + 16 * vt +
@@ -202,16 +213,24 @@ __global__ __launch_bounds__(256) void state_copy_kernel(const float* __restrict
   if (i < n) dst[i] = src ? src[i] : 0.f;
 }
 
-constexpr int kFwdVB = 32;
+// Value-block width of the scans: the chains run concurrently only while every
+// workgroup is resident (two per CU at this register use), so few chains get
+// narrower value blocks and more workgroups.
+int scan_value_block(long chains) { (void)chains; return 32; }
 
 hipError_t launch_fwd_scan(const int32_t* seq_first, int N, int HV, int NC,
                            const ChunkInfo* table, const PrepOut& prep, const float* h0,
                            uint16_t* o, float* hT, uint16_t* saved, hipStream_t stream) {
   const long chains = (long)N * HV;
   const long groups = (chains + 7) / 8;
-  const long blocks = groups * 8 * (kHead / kFwdVB);
-  hipLaunchKernelGGL(fwd_scan_kernel<kFwdVB>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     seq_first, N, HV, NC, table, prep, h0, o, hT, saved);
+  const int vb = scan_value_block(chains);
+  const long blocks = groups * 8 * (kHead / vb);
+  if (vb == 16)
+    hipLaunchKernelGGL(fwd_scan_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       seq_first, N, HV, NC, table, prep, h0, o, hT, saved);
+  else
+    hipLaunchKernelGGL(fwd_scan_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       seq_first, N, HV, NC, table, prep, h0, o, hT, saved);
   return hipGetLastError();
 }
 
