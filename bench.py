@@ -50,6 +50,40 @@ KERNEL_FLOPS = {
 }
 
 
+# stage name (gdn_stage_name) -> kernel symbol as the profiler names it
+STAGE_KERNELS = {"chunk_table": "chunk_table_kernel", "chunk_prep": "chunk_prep_kernel<false>",
+                 "fwd_scan": "fwd_scan_kernel<32>", "chunk_prep_bwd": "chunk_prep_kernel<true>",
+                 "bwd_dh_scan": "bwd_dh_scan_kernel<32>", "bwd_chunk": "bwd_chunk_kernel"}
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources, to tie recorded counter traffic to the code it measured."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "chunked_gated_delta_04_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE, calibrated by a plain copy), or None when that
+    summary was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", WORKLOAD + ".md")
+    try:
+        text = open(path).read()
+        blob = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    if blob.get("source") != kernel_source_hash():
+        return None
+    t = blob.get("traffic", {}).get(kernel)
+    return None if t is None else t["fetch_bytes"] + t["write_bytes"]
+
+
 def hip():
     lib = ctypes.CDLL("libamdhip64.so")
     lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
@@ -283,7 +317,8 @@ def main():
     dom_achieved = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(dom_achieved, 3), "peak": PEAK_BF16 / 1e12,
                 "unit": "TFLOP/s", "frac": round(dom_achieved * 1e12 / PEAK_BF16, 5),
-                "traffic": None, "kernel": dom, "kernel_ms": round(stage_ms[dom], 4)}
+                "traffic": recorded_traffic(STAGE_KERNELS.get(dom, dom)), "kernel": dom,
+                "kernel_ms": round(stage_ms[dom], 4)}
 
     extra = None
     if not args.no_secondary:
