@@ -43,11 +43,13 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   const int c4 = tid & 31;
   const int r0 = tid >> 5;
 
-  // issue the state loads first: they are the whole cost of the step
-  float4 s[16];
+  // issue the state loads first: they are the whole cost of the step; the
+  // state is streamed exactly once in and once out, so the accesses are
+  // non-temporal
+  f32x4 s[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i)
-    s[i] = reinterpret_cast<const float4*>(S + (size_t)(r0 + 8 * i) * kHead)[c4];
+    s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (size_t)(r0 + 8 * i) * kHead) + c4);
 
   if (tid < 64) {
     // q and k rows of the key head: lane holds elements 2*lane, 2*lane + 1
@@ -75,20 +77,20 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   float outv[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    float4 x4 = s[i];
-    x4.x *= decay; x4.y *= decay; x4.z *= decay; x4.w *= decay;
-    float p = x4.x * kk.x + x4.y * kk.y + x4.z * kk.z + x4.w * kk.w;
+    f32x4 x4 = s[i];
+    x4[0] *= decay; x4[1] *= decay; x4[2] *= decay; x4[3] *= decay;
+    float p = x4[0] * kk.x + x4[1] * kk.y + x4[2] * kk.z + x4[3] * kk.w;
     p = group_sum<32>(p);
     const float delta = beta * (vs[r0 + 8 * i] - p);
-    x4.x += delta * kk.x; x4.y += delta * kk.y; x4.z += delta * kk.z; x4.w += delta * kk.w;
+    x4[0] += delta * kk.x; x4[1] += delta * kk.y; x4[2] += delta * kk.z; x4[3] += delta * kk.w;
     s[i] = x4;
-    outv[i] = x4.x * qq.x + x4.y * qq.y + x4.z * qq.z + x4.w * qq.w;
+    outv[i] = x4[0] * qq.x + x4[1] * qq.y + x4[2] * qq.z + x4[3] * qq.w;
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) outv[i] = group_sum<32>(outv[i]);
 #pragma unroll
   for (int i = 0; i < 16; ++i)
-    reinterpret_cast<float4*>(S + (size_t)(r0 + 8 * i) * kHead)[c4] = s[i];
+    __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(S + (size_t)(r0 + 8 * i) * kHead) + c4);
   if (c4 == 0) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) orow[r0 + 8 * i] = f2bf(outv[i]);
