@@ -227,19 +227,22 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
 // Per-chunk gradients: one 512-thread workgroup per (chunk, key head); the
 // value heads of the key head run in order. Wave w owns token tile tw = w & 3
 // (tokens 16 tw .. 16 tw + 15) and column half kh = w >> 2 (key or value
-// columns 64 kh .. 64 kh + 63) of every token-indexed result. Every matrix
-// that is contracted over the chunk's tokens is kept in LDS transposed as well
-// (bf16), so every MFMA operand is one 16-byte read. Per-token and per-column
-// partial sums go to LDS slots owned by one wave each and are added once per
-// value head in a fixed order.
+// columns 64 kh .. 64 kh + 63) of every token-indexed result. Matrices that
+// are contracted over the chunk's tokens are kept in LDS transposed as well
+// (bf16), so every MFMA operand is one 16-byte read. The operands each phase
+// reads from HBM are requested a phase ahead (the state h is staged into LDS
+// while dP and Z are formed, then the state gradient dh' takes its place), so
+// the workgroup - alone on its CU - does not stall on memory at every phase.
+// Per-token and per-column partial sums go to LDS slots owned by one wave each
+// and are added once per value head in a fixed order.
 namespace {
 constexpr int BP = 72;  // LDS pitch (bf16) of [64][64] tiles
 
 struct BwdLds {
-  uint16_t Ks[64 * KP], Qs[64 * KP];        // k^, q~ rows
+  uint16_t Ks[64 * KP];                     // k^ rows
   uint16_t KsT[128 * TP], QsT[128 * TP];    // k^, q~ transposed [k][tok]
-  uint16_t Tb[64 * BP], TbT[64 * BP];       // T, T^T
   uint16_t Pm[64 * BP], PmT[64 * BP];       // dP o Gamma and transpose; later M, M^T
+  uint16_t Hs[128 * KP];                    // h [k][v], then dh' [k][v]; dq staging at the end
   union {                                   // time-shared regions
     uint16_t Z[64 * KP];                    //   Z = T^T dD [tok][v]
     uint16_t dT[64 * BP];                   //   dT [i][m]
@@ -251,7 +254,7 @@ struct BwdLds {
   float gam[64], bet[64], eg[64], ebw[64];
   float nrm_k[64], nrm_q[64];
   float rowF[2][64], colF[8][64];           // F = dP o P
-  float rowG[2][64], rowB2[2][64];          // row terms of the key-column loop
+  float rowG[2][64], rowB2[2][64];          // row terms of the key-column passes
   float rowB[2][64];                        // dbeta of U
   float rowE[2][64], colE[8][64], rowB3[2][64];  // E = dA o A, dbeta of A
   float gl_part[8], hd_part[8];
@@ -265,10 +268,13 @@ __device__ __forceinline__ float4 ld4_bf16(const uint16_t* p) {  // 4 bf16 -> fp
   const uint2 u = *reinterpret_cast<const uint2*>(p);
   return make_float4(bf2f(u.x & 0xffffu), bf2f(u.x >> 16), bf2f(u.y & 0xffffu), bf2f(u.y >> 16));
 }
-__device__ __forceinline__ float dot8(const bf16x8& a, const bf16x8& b) {
+__device__ __forceinline__ float dot8u(const uint4& a, const uint4& b) {  // bf16 pairs
+  const uint32_t* x = reinterpret_cast<const uint32_t*>(&a);
+  const uint32_t* y = reinterpret_cast<const uint32_t*>(&b);
   float s = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) s += (float)a[e] * (float)b[e];
+  for (int e = 0; e < 4; ++e)
+    s += bf2f(x[e] & 0xffffu) * bf2f(y[e] & 0xffffu) + bf2f(x[e] >> 16) * bf2f(y[e] >> 16);
   return s;
 }
 }  // namespace
@@ -285,16 +291,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
   const ChunkInfo ci = table[c];
   if (ci.seq < 0) return;
   const int t0 = ci.t0, L = ci.len;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int li = lane & 15, kq = lane >> 4;
-  const int tw = wave & 3, kh = wave >> 2;
-  const int trow = 16 * tw + li;  // token row this lane supplies as an A operand
-  const bool trow_ok = trow < L;
 
   __shared__ __align__(16) BwdLds S;
 
-  // ---- q, k rows: L2 norm, bf16 copies in both layouts (8 threads per row)
+  // ---- q, k rows: L2 norm; k^ in both layouts, q~ transposed (8 threads per row)
   {
+    const int tid = threadIdx.x;
     const int r = tid >> 3, sg0 = (tid & 7) * 2;
     uint4 kr[2], qr[2];
     float sk = 0.f, sq = 0.f;
@@ -328,16 +330,14 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     for (int j = 0; j < 2; ++j) {
       const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[j]);
       const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qr[j]);
-      uint4 ko, qo;
+      uint4 ko;
       uint32_t* kow = reinterpret_cast<uint32_t*>(&ko);
-      uint32_t* qow = reinterpret_cast<uint32_t*>(&qo);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint16_t k0 = f2bf(bf2f(kw[e] & 0xffffu) / nk), k1 = f2bf(bf2f(kw[e] >> 16) / nk);
         const uint16_t q0 = f2bf((bf2f(qw[e] & 0xffffu) / nq) * scale);
         const uint16_t q1 = f2bf((bf2f(qw[e] >> 16) / nq) * scale);
         kow[e] = (uint32_t)k0 | ((uint32_t)k1 << 16);
-        qow[e] = (uint32_t)q0 | ((uint32_t)q1 << 16);
         const int d = (sg0 + j) * 8 + 2 * e;
         S.KsT[d * TP + r] = k0;
         S.KsT[(d + 1) * TP + r] = k1;
@@ -345,9 +345,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         S.QsT[(d + 1) * TP + r] = q1;
       }
       *reinterpret_cast<uint4*>(&S.Ks[r * KP + (sg0 + j) * 8]) = ko;
-      *reinterpret_cast<uint4*>(&S.Qs[r * KP + (sg0 + j) * 8]) = qo;
     }
   }
+  __syncthreads();
 
   // dq~, dk^ over the value heads: [j][r] = d[16 tw + 4 kq + r][16 (4 kh + j) + li]
   f32x4 adq[4], adk[4];
@@ -365,7 +365,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     // (they would not fit in the register budget of two waves per SIMD).
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    const int lane = tid & 63;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int tw = wave & 3, kh = wave >> 2;
     const int li = lane & 15, kq = lane >> 4;
     const int trow = 16 * tw + li;
     const bool trow_ok = trow < L;
@@ -376,10 +377,23 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     const uint16_t* dhb = bufs.dh + blk * (kHead * kHead);
     const uint16_t* dDb = bufs.dD + blk * 8192;          // dD [tok][v]
     const uint16_t* dDTb = bufs.dDT + blk * 8192;        // dD^T [v][tok]
+    const uint16_t* Tg = Tmat + blk * 8192;              // T, then T^T [64][64]
     const uint16_t* dOb = dO + ((size_t)t0 * HV + hv) * kHead;
     const uint16_t* vb = v + ((size_t)t0 * HV + hv) * kHead;
 
-    // ---- gates; T and T^T (from the WY pass of the backward) into LDS
+    // ---- requests for the dP phase: the own rows of dO and q, the D rows of
+    //      this wave's dP tiles
+    bf16x8 oa[4], qa[4], dfr[2][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      oa[s] = trow_ok ? ld8(dOb + (size_t)trow * rs + 32 * s + 8 * kq) : zero8();
+      qa[s] = trow_ok ? ld8(q + ((size_t)(t0 + trow) * H + h) * kHead + 32 * s + 8 * kq) : zero8();
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+        dfr[q2][s] = ld8(Db + (16 * (kh + 2 * q2) + li) * kHead + 32 * s + 8 * kq);
+    }
+
+    // ---- gates
     if (wave == 0) {
       float gv = lane < L ? g[(size_t)(t0 + lane) * HV + hv] : 0.f;
       const float bv = lane < L ? beta[(size_t)(t0 + lane) * HV + hv] : 0.f;
@@ -394,28 +408,23 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       S.eg[lane] = expf(gv);
       S.ebw[lane] = lane < L ? expf(gl - gv) : 0.f;
     }
-    {
-      const uint16_t* Tg = Tmat + blk * 8192;
-      const int i = (tid >> 3) & 63, j0 = (tid & 7) * 8;
-      *reinterpret_cast<uint4*>(&S.Tb[i * BP + j0]) =
-          *reinterpret_cast<const uint4*>(Tg + i * 64 + j0);
-      *reinterpret_cast<uint4*>(&S.TbT[i * BP + j0]) =
-          *reinterpret_cast<const uint4*>(Tg + 4096 + i * 64 + j0);
-    }
-    // clear the per-wave partial slots of this value head
     for (int e = tid; e < 8 * 64; e += 512) {
       (&S.colF[0][0])[e] = 0.f;
       (&S.colE[0][0])[e] = 0.f;
     }
     __syncthreads();
 
-    // ---- dP = dO D^T (i >= j) and P from Q~K^T: Pm = dP o Gamma (+ transpose);
+    // ---- dP = dO D^T (i >= j) and P = Gamma o Q~K^T: Pm = dP o Gamma (+ transpose);
     //      F = dP o P row / column partial sums. Wave: row tile tw, col tiles kh, kh + 2.
     {
-      bf16x8 oa[4];
+      const float nq = S.nrm_q[trow];
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        oa[s] = trow_ok ? ld8(dOb + (size_t)trow * rs + 32 * s + 8 * kq) : zero8();
+      for (int s = 0; s < 4; ++s) {
+        bf16x8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (__bf16)(((float)qa[s][e] / nq) * scale);
+        qa[s] = x;  // the q~ row exactly as in QsT
+      }
       float rowp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
@@ -426,9 +435,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
           f32x4 dp = zero4(), qk = zero4();
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            dp = mfma(oa[s], ld8(Db + (16 * jb + li) * kHead + 32 * s + 8 * kq), dp);
-            qk = mfma(ld8(&S.Qs[trow * KP + 32 * s + 8 * kq]),
-                      ld8(&S.Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), qk);
+            dp = mfma(oa[s], dfr[q2][s], dp);
+            qk = mfma(qa[s], ld8(&S.Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), qk);
           }
           float colp = 0.f;
 #pragma unroll
@@ -458,14 +466,31 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         for (int r = 0; r < 4; ++r) S.rowF[kh][16 * tw + 4 * kq + r] = rowp[r];
       }
     }
+    // requests for the Z phase: T^T rows of this wave's tokens, dD^T rows, v rows
+    bf16x8 tt[2], ddt[4][2];
+    uint2 vr[4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) tt[s] = ld8(Tg + 4096 + trow * 64 + 32 * s + 8 * kq);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int vt = 4 * kh + j;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) ddt[j][s] = ld8(dDTb + (16 * vt + li) * 64 + 32 * s + 8 * kq);
+      vr[j] = trow_ok ? *reinterpret_cast<const uint2*>(vb + (size_t)trow * rs + 16 * vt + 4 * kq)
+                      : make_uint2(0, 0);
+    }
+    // h, staged into LDS once the Z phase is done with its operands
+    uint4 hst[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 512 * i;
+      hst[i] = *reinterpret_cast<const uint4*>(hb + (e >> 4) * kHead + (e & 15) * 8);
+    }
 
     // ---- Z = T^T dD (written [tok][v]); dV = diag(beta) Z; dbeta of U.
     //      Wave: token columns of tile tw, value tiles 4 kh .. 4 kh + 3.
     {
       float bp = 0.f;
-      bf16x8 tt[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) tt[s] = ld8(&S.TbT[trow * BP + 32 * s + 8 * kq]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int vt = 4 * kh + j;
@@ -473,14 +498,14 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 #pragma unroll
         for (int s = 0; s < 2; ++s)
           if (32 * s + 31 >= 16 * tw)  // T[m][t] needs m >= t
-            z = mfma(ld8(dDTb + (16 * vt + li) * 64 + 32 * s + 8 * kq), tt[s], z);
+            z = mfma(ddt[j][s], tt[s], z);
         // z[r] = Z[t = trow][v = 16 vt + 4 kq + r]
         const int vv = 16 * vt + 4 * kq;
         *reinterpret_cast<uint2*>(&S.rz.Z[trow * KP + vv]) = pack4_bf16(z[0], z[1], z[2], z[3]);
         if (trow_ok) {
-          const uint2 vr = *reinterpret_cast<const uint2*>(vb + (size_t)trow * rs + vv);
-          bp += bf2f(vr.x & 0xffffu) * z[0] + bf2f(vr.x >> 16) * z[1] +
-                bf2f(vr.y & 0xffffu) * z[2] + bf2f(vr.y >> 16) * z[3];
+          const uint2 u = vr[j];
+          bp += bf2f(u.x & 0xffffu) * z[0] + bf2f(u.x >> 16) * z[1] +
+                bf2f(u.y & 0xffffu) * z[2] + bf2f(u.y >> 16) * z[3];
           const float bt = S.bet[trow];
           *reinterpret_cast<uint2*>(dv + ((size_t)(t0 + trow) * HV + hv) * kHead + vv) =
               pack4_bf16(bt * z[0], bt * z[1], bt * z[2], bt * z[3]);
@@ -490,97 +515,115 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       bp += __shfl_xor(bp, 32, 64);
       if (kq == 0) S.rowB[kh][trow] = bp;
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 512 * i;
+      *reinterpret_cast<uint4*>(&S.Hs[(e >> 4) * KP + (e & 15) * 8]) = hst[i];
+    }
     __syncthreads();
 
-    // ---- key-column loops (columns 16 kt + li, kt = 4 kh .. 4 kh + 3), in two
-    //      passes to bound the live operands:
+    // ---- key-column passes (columns 16 kt + li, kt = 4 kh .. 4 kh + 3), h from LDS:
     //      pass 1: x1 = dO h^T, x4 = Z h^T (= -T^T dW),
     //              y1 = (dP o Gamma) K^, y2 = (dP o Gamma)^T Q~
     //      pass 2: x3 = dD h^T (= -dW), stored for dT
-    //      pass 3: x2 = D dh'^T, and <h, dh'> for the state-decay gradient
+    //      then dh' replaces h in LDS; pass 3: x2 = D dh'^T
+    float gr[4] = {0.f, 0.f, 0.f, 0.f}, br[4] = {0.f, 0.f, 0.f, 0.f};
     {
-      float gr[4] = {0.f, 0.f, 0.f, 0.f}, br[4] = {0.f, 0.f, 0.f, 0.f};
-      float glp = 0.f, hd = 0.f;
-      {
-        bf16x8 oa[4], za[4], pa[2], pta[2];
+      bf16x8 za[4], pa[2], pta[2];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          oa[s] = trow_ok ? ld8(dOb + (size_t)trow * rs + 32 * s + 8 * kq) : zero8();
+      for (int s = 0; s < 4; ++s) za[s] = ld8(&S.rz.Z[trow * KP + 32 * s + 8 * kq]);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) za[s] = ld8(&S.rz.Z[trow * KP + 32 * s + 8 * kq]);
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          pa[s] = ld8(&S.Pm[trow * BP + 32 * s + 8 * kq]);
-          pta[s] = ld8(&S.PmT[trow * BP + 32 * s + 8 * kq]);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int kr = 16 * (4 * kh + j) + li;
-          bf16x8 hf[4];
-#pragma unroll
-          for (int s = 0; s < 4; ++s) hf[s] = ld8(hb + kr * kHead + 32 * s + 8 * kq);
-          f32x4 x1 = zero4(), x4 = zero4(), y1 = zero4(), y2 = zero4();
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            x1 = mfma(oa[s], hf[s], x1);
-            x4 = mfma(za[s], hf[s], x4);
-          }
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            if (32 * s <= 16 * tw + 15)  // (dP o Gamma)[t][j] needs j <= t
-              y1 = mfma(pa[s], ld8(&S.KsT[kr * TP + 32 * s + 8 * kq]), y1);
-            if (32 * s + 31 >= 16 * tw)  // (dP o Gamma)[i][t] needs i >= t
-              y2 = mfma(pta[s], ld8(&S.QsT[kr * TP + 32 * s + 8 * kq]), y2);
-          }
-          const int tr = 16 * tw + 4 * kq;
-          const float4 qv = ld4_bf16(&S.QsT[kr * TP + tr]);
-          const float4 kv = ld4_bf16(&S.KsT[kr * TP + tr]);
-          const float qa_[4] = {qv.x, qv.y, qv.z, qv.w};
-          const float ka_[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = tr + r;
-            const float e = S.eg[t], bt = S.bet[t];
-            adq[j][r] += e * x1[r] + y1[r];
-            gr[r] += e * qa_[r] * x1[r];               // inter-chunk output decay
-            adk[j][r] += y2[r] - bt * e * x4[r];
-            const float zk = -ka_[r] * x4[r];          // k^ . (T^T dW)
-            br[r] += e * zk;
-            gr[r] += bt * e * zk;
-          }
-        }
+      for (int s = 0; s < 2; ++s) {
+        pa[s] = ld8(&S.Pm[trow * BP + 32 * s + 8 * kq]);
+        pta[s] = ld8(&S.PmT[trow * BP + 32 * s + 8 * kq]);
       }
-      {
-        bf16x8 ea[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) ea[s] = ld8(dDb + trow * kHead + 32 * s + 8 * kq);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int kr = 16 * (4 * kh + j) + li;
-          f32x4 x3 = zero4();
-#pragma unroll
-          for (int s = 0; s < 4; ++s) x3 = mfma(ea[s], ld8(hb + kr * kHead + 32 * s + 8 * kq), x3);
-          const int tr = 16 * tw + 4 * kq;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) S.rw.dW[(tr + r) * KP + kr] = f2bf(-x3[r]);
-        }
-      }
-      bf16x8 da[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) da[s] = ld8(Db + trow * kHead + 32 * s + 8 * kq);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int kr = 16 * (4 * kh + j) + li;
-        bf16x8 df[4];
+        bf16x8 hf[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) df[s] = ld8(dhb + kr * kHead + 32 * s + 8 * kq);
+        for (int s = 0; s < 4; ++s) hf[s] = ld8(&S.Hs[kr * KP + 32 * s + 8 * kq]);
+        f32x4 x1 = zero4(), x4 = zero4(), y1 = zero4(), y2 = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          x1 = mfma(oa[s], hf[s], x1);
+          x4 = mfma(za[s], hf[s], x4);
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          if (32 * s <= 16 * tw + 15)  // (dP o Gamma)[t][j] needs j <= t
+            y1 = mfma(pa[s], ld8(&S.KsT[kr * TP + 32 * s + 8 * kq]), y1);
+          if (32 * s + 31 >= 16 * tw)  // (dP o Gamma)[i][t] needs i >= t
+            y2 = mfma(pta[s], ld8(&S.QsT[kr * TP + 32 * s + 8 * kq]), y2);
+        }
+        const int tr = 16 * tw + 4 * kq;
+        const float4 qv = ld4_bf16(&S.QsT[kr * TP + tr]);
+        const float4 kv = ld4_bf16(&S.KsT[kr * TP + tr]);
+        const float qa_[4] = {qv.x, qv.y, qv.z, qv.w};
+        const float ka_[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = tr + r;
+          const float e = S.eg[t], bt = S.bet[t];
+          adq[j][r] += e * x1[r] + y1[r];
+          gr[r] += e * qa_[r] * x1[r];               // inter-chunk output decay
+          adk[j][r] += y2[r] - bt * e * x4[r];
+          const float zk = -ka_[r] * x4[r];          // k^ . (T^T dW)
+          br[r] += e * zk;
+          gr[r] += bt * e * zk;
+        }
+      }
+    }
+    uint4 dst[4];  // dh' requests, staged into LDS once h is no longer read
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 512 * i;
+      dst[i] = *reinterpret_cast<const uint4*>(dhb + (e >> 4) * kHead + (e & 15) * 8);
+    }
+    {
+      bf16x8 ea[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) ea[s] = ld8(dDb + trow * kHead + 32 * s + 8 * kq);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kr = 16 * (4 * kh + j) + li;
+        f32x4 x3 = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) x3 = mfma(ea[s], ld8(&S.Hs[kr * KP + 32 * s + 8 * kq]), x3);
+        const int tr = 16 * tw + 4 * kq;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S.rw.dW[(tr + r) * KP + kr] = f2bf(-x3[r]);
+      }
+    }
+    {
+      // <h, dh'> over the whole state, from the staged elements of this thread
+      float hd = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = tid + 512 * i;
+        hd += dot8u(*reinterpret_cast<const uint4*>(&S.Hs[(e >> 4) * KP + (e & 15) * 8]), dst[i]);
+      }
+      hd = wave_sum(hd);
+      if (lane == 0) S.hd_part[wave] = hd;
+    }
+    __syncthreads();  // every wave is done with h
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 512 * i;
+      *reinterpret_cast<uint4*>(&S.Hs[(e >> 4) * KP + (e & 15) * 8]) = dst[i];
+    }
+    bf16x8 da[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) da[s] = ld8(Db + trow * kHead + 32 * s + 8 * kq);
+    __syncthreads();
+    {
+      float glp = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kr = 16 * (4 * kh + j) + li;
         f32x4 x2 = zero4();
 #pragma unroll
-        for (int s = 0; s < 4; ++s) x2 = mfma(da[s], df[s], x2);
-        if (tw == 0) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) hd += dot8(ld8(hb + kr * kHead + 32 * s + 8 * kq), df[s]);
-        }
+        for (int s = 0; s < 4; ++s) x2 = mfma(da[s], ld8(&S.Hs[kr * KP + 32 * s + 8 * kq]), x2);
         const int tr = 16 * tw + 4 * kq;
         const float4 kv = ld4_bf16(&S.KsT[kr * TP + tr]);
         const float ka_[4] = {kv.x, kv.y, kv.z, kv.w};
@@ -607,16 +650,19 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         }
       }
       glp = wave_sum(glp);
-      hd = wave_sum(hd);
-      if (lane == 0) {
-        S.gl_part[wave] = glp;
-        S.hd_part[wave] = hd;
-      }
+      if (lane == 0) S.gl_part[wave] = glp;
     }
-    __syncthreads();
 
     // ---- dT = dD (beta V)^T + dW (beta e^gamma K^)^T, strictly lower
     //      (wave: row tile tw, col tiles kh, kh + 2)
+    bf16x8 ty[2][2], tta[2];  // requests for Y1 (T rows) and dA (T^T rows)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      tta[s] = ld8(Tg + 4096 + trow * 64 + 32 * s + 8 * kq);
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+        ty[q2][s] = ld8(Tg + (16 * (kh + 2 * q2) + li) * 64 + 32 * s + 8 * kq);
+    }
     {
       bf16x8 wa[4], ea[4];
 #pragma unroll
@@ -666,8 +712,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         f32x4 acc = zero4();
         if (jb <= tw) {
 #pragma unroll
-          for (int s = 0; s < 2; ++s)
-            acc = mfma(ta[s], ld8(&S.Tb[(16 * jb + li) * BP + 32 * s + 8 * kq]), acc);
+          for (int s = 0; s < 2; ++s) acc = mfma(ta[s], ty[q2][s], acc);
         }
         const int j = 16 * jb + li;
         float y[4];
@@ -681,9 +726,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 
     // ---- dA = -T^T Y1 (i > j); M = dA o beta_i Gamma -> Pm, PmT; E = dA o A sums; dbeta of A
     {
-      bf16x8 ta[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) ta[s] = ld8(&S.TbT[trow * BP + 32 * s + 8 * kq]);
       float re[4] = {0.f, 0.f, 0.f, 0.f}, rb[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
@@ -695,7 +737,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 #pragma unroll
           for (int s = 0; s < 2; ++s)
             if (32 * s + 31 >= 16 * tw)
-              acc = mfma(ta[s], ld8(&S.rw.Y1T[(16 * jb + li) * BP + 32 * s + 8 * kq]), acc);
+              acc = mfma(tta[s], ld8(&S.rw.Y1T[(16 * jb + li) * BP + 32 * s + 8 * kq]), acc);
 #pragma unroll
           for (int s = 0; s < 4; ++s)
             kk = mfma(ld8(&S.Ks[trow * KP + 32 * s + 8 * kq]),
@@ -751,11 +793,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
                         (S.rowB3[0][t] + S.rowB3[1][t]);
       float x = t < L ? dgm : 0.f;
       if (t == L - 1) {
-        float glsum = 0.f;
+        float glsum = 0.f, hdsum = 0.f;
 #pragma unroll
-        for (int w = 0; w < 8; ++w) glsum += S.gl_part[w];
-        const float hdsum = (S.hd_part[0] + S.hd_part[1]) + (S.hd_part[4] + S.hd_part[5]) +
-                            (S.hd_part[2] + S.hd_part[3]) + (S.hd_part[6] + S.hd_part[7]);
+        for (int w = 0; w < 8; ++w) {
+          glsum += S.gl_part[w];
+          hdsum += S.hd_part[w];
+        }
         x += glsum + expf(S.gam[L - 1]) * hdsum;
       }
 #pragma unroll
@@ -794,8 +837,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
   }
 
   // ---- L2-norm backward and scale: x^ . dx^ over all 128 columns (two halves)
-  float xq[4][4], xk[4][4];
   {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tw = wave & 3, kh = wave >> 2;
+    const int li = lane & 15, kq = lane >> 4;
     float dq_[4] = {0.f, 0.f, 0.f, 0.f}, dk_[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -809,8 +854,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
           qv = bf2f(q[off]) / S.nrm_q[t];
           kv = bf2f(k[off]) / S.nrm_k[t];
         }
-        xq[j][r] = qv;
-        xk[j][r] = kv;
         dq_[r] += qv * scale * adq[j][r];
         dk_[r] += kv * adk[j][r];
       }
@@ -826,26 +869,32 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         S.dot_k[kh][16 * tw + 4 * kq + r] = dk_[r];
       }
     }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tw + 4 * kq + r;
+        const int kc = 16 * (4 * kh + j) + li;
+        float qv = 0.f, kv = 0.f;
+        if (t < L) {
+          const size_t off = ((size_t)(t0 + t) * H + h) * kHead + kc;
+          qv = bf2f(q[off]) / S.nrm_q[t];
+          kv = bf2f(k[off]) / S.nrm_k[t];
+        }
+        const float dotq = S.dot_q[0][t] + S.dot_q[1][t];
+        const float dotk = S.dot_k[0][t] + S.dot_k[1][t];
+        const float dqh = scale * adq[j][r];
+        S.Hs[t * KP + kc] = f2bf((dqh - qv * dotq) / S.nrm_q[t]);
+        S.Ks[t * KP + kc] = f2bf((adk[j][r] - kv * dotk) / S.nrm_k[t]);
+      }
   }
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * tw + 4 * kq + r;
-      const int kc = 16 * (4 * kh + j) + li;
-      const float dotq = S.dot_q[0][t] + S.dot_q[1][t];
-      const float dotk = S.dot_k[0][t] + S.dot_k[1][t];
-      const float dqh = scale * adq[j][r];
-      S.Qs[t * KP + kc] = f2bf((dqh - xq[j][r] * dotq) / S.nrm_q[t]);
-      S.Ks[t * KP + kc] = f2bf((adk[j][r] - xk[j][r] * dotk) / S.nrm_k[t]);
-    }
-  __syncthreads();
-  for (int e = tid; e < 64 * 16; e += 512) {
+  for (int e = threadIdx.x; e < 64 * 16; e += 512) {
     const int t = e >> 4, sg = e & 15;
     if (t < L) {
       const size_t off = ((size_t)(t0 + t) * H + h) * kHead + sg * 8;
-      *reinterpret_cast<uint4*>(dq + off) = *reinterpret_cast<const uint4*>(&S.Qs[t * KP + sg * 8]);
+      *reinterpret_cast<uint4*>(dq + off) = *reinterpret_cast<const uint4*>(&S.Hs[t * KP + sg * 8]);
       *reinterpret_cast<uint4*>(dk + off) = *reinterpret_cast<const uint4*>(&S.Ks[t * KP + sg * 8]);
     }
   }
