@@ -49,15 +49,20 @@ __device__ __forceinline__ float sum16(float x) { return group_sum<16>(x); }
 // ---------------------------------------------------------------------------
 // Reverse scan: dh (K x VB slice) in registers, chunks in reverse order.
 // Writes per (chunk, value head): dh' as [k][v], dD as [tok][v] and [v][tok].
-template <int VB>
+// As in the forward scan, two operand sets alternate and every chunk issues
+// the same loads and stores with no branch around them, so waiting for a set
+// never waits for a store; dO rows past the chunk's end come from a
+// range-checked buffer load, which returns zeros there.
 __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
     const int32_t* __restrict__ seq_first, int N, int HV, int NC,
     const ChunkInfo* __restrict__ table, PrepOut prep, const uint16_t* __restrict__ dO,
     const float* __restrict__ dhT, float* __restrict__ dh0, BwdBufs bufs) {
+  constexpr int VB = kScanVB;
   constexpr int NVB = kHead / VB;
   constexpr int VT = VB / 16;
   constexpr int SP = 136;
   constexpr int DP = 72;
+  static_assert(kChunk * (VB / 8) == 256 && VB * 8 == 256, "one 16-byte segment per thread");
 
   const int b = blockIdx.x;
   const int xcd = b & 7, slot = b >> 3;
@@ -89,15 +94,20 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
       }
     }
 
-  static_assert(kChunk * (VB / 8) <= 256, "at most one dO segment per thread");
-  const bool o_ok = tid < kChunk * (VB / 8);
   struct Ops {
     bf16x8 pa[2], ka[4], qa[2][2], wa[2][2];
     uint4 dO;
     float gl;
-    ChunkInfo ci;
   };
-  const int ot = tid / (VB / 8), osg = tid - ot * (VB / 8);  // dO segment of this thread
+  const int ot = tid >> 2, osg = tid & 3;  // dO segment of this thread
+  // chunk bounds from the sequence's bounds (consecutive 64-token chunks)
+  const int c_begin = seq_first[seq], c_end = seq_first[seq + 1];
+  int bos = 0, eos = 0;
+  if (c_begin < c_end) {
+    const ChunkInfo first = table[c_begin], lastc = table[c_end - 1];
+    bos = first.t0;
+    eos = lastc.t0 + lastc.len;
+  }
   auto load_ops = [&](int c, Ops& x) {
     const size_t blk = (size_t)hv * NC + c;
     const uint16_t* PTb = prep.P + blk * 4096;   // P^T: row i holds P[j][i], j >= i
@@ -118,21 +128,16 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
       }
     }
     x.gl = prep.gL[blk];
-    x.ci = table[c];
-    x.dO = make_uint4(0, 0, 0, 0);
-    if (o_ok && ot < x.ci.len)
-      x.dO = *reinterpret_cast<const uint4*>(dO + ((size_t)(x.ci.t0 + ot) * HV + hv) * kHead + v0 +
-                                             8 * osg);
+    const int t0 = bos + (c - c_begin) * kChunk;
+    const int len = min(kChunk, eos - t0);
+    const __amdgpu_buffer_rsrc_t rng = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(dO) + ((size_t)t0 * HV + hv) * kHead, 0, len * HV * kHead * 2,
+        kBufferWord3);
+    x.dO = load_b128(rng, (ot * HV * kHead + v0 + 8 * osg) * 2);
   };
 
-  const int c_begin = seq_first[seq], c_end = seq_first[seq + 1];
-  Ops nxt;
-  if (c_begin < c_end) load_ops(c_end - 1, nxt);
-  for (int c = c_end - 1; c >= c_begin; --c) {
-    const Ops cur = nxt;
-    if (c - 1 >= c_begin) load_ops(c - 1, nxt);
+  auto step = [&](int c, const Ops& cur) {
     const size_t blk = (size_t)hv * NC + c;
-
     // 1. dh -> LDS; stage dO^T for this value block
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
@@ -142,17 +147,19 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
         *reinterpret_cast<uint2*>(&Hs[(16 * vt + li) * SP + kk]) =
             pack4_bf16(dh[dt][vt][0], dh[dt][vt][1], dh[dt][vt][2], dh[dt][vt][3]);
       }
-    if (o_ok) {
+    {
       const uint16_t* xs = reinterpret_cast<const uint16_t*>(&cur.dO);
 #pragma unroll
       for (int u = 0; u < 8; ++u) Os[(8 * osg + u) * DP + ot] = xs[u];
     }
     __syncthreads();
-    // dh' (gradient of this chunk's end state) as [k][v]
+    // dh' (gradient of this chunk's end state) as [k][v]: two 16-byte stores per thread
     {
       uint16_t* dhb = bufs.dh + blk * (kHead * kHead);
-      for (int e = tid; e < kHead * (VB / 8); e += 256) {
-        const int kk = e / (VB / 8), vg = e - kk * (VB / 8);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int e = tid + 256 * i;
+        const int kk = e >> 2, vg = e & 3;
         *reinterpret_cast<uint4*>(dhb + kk * kHead + v0 + 8 * vg) = gather8(&Hs[(8 * vg) * SP + kk], SP);
       }
     }
@@ -178,19 +185,15 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
           pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
     }
     __syncthreads();
-    // dD to global as [v][tok] (row copies) and [tok][v] (column gathers)
+    // dD to global as [v][tok] (row copy) and [tok][v] (column gather): one each per thread
     {
       uint16_t* dDT = bufs.dDT + blk * 8192;
       uint16_t* dDr = bufs.dD + blk * 8192;
-      for (int e = tid; e < VB * 8; e += 256) {
-        const int vl = e >> 3, sg = e & 7;
-        *reinterpret_cast<uint4*>(dDT + (v0 + vl) * 64 + 8 * sg) =
-            *reinterpret_cast<const uint4*>(&Es[vl * DP + 8 * sg]);
-      }
-      for (int e = tid; e < kChunk * (VB / 8); e += 256) {
-        const int t = e / (VB / 8), vg = e - t * (VB / 8);
-        *reinterpret_cast<uint4*>(dDr + t * kHead + v0 + 8 * vg) = gather8(&Es[(8 * vg) * DP + t], DP);
-      }
+      const int vl = tid >> 3, sg = tid & 7;
+      *reinterpret_cast<uint4*>(dDT + (v0 + vl) * 64 + 8 * sg) =
+          *reinterpret_cast<const uint4*>(&Es[vl * DP + 8 * sg]);
+      const int t = tid >> 2, vg = tid & 3;
+      *reinterpret_cast<uint4*>(dDr + t * kHead + v0 + 8 * vg) = gather8(&Es[(8 * vg) * DP + t], DP);
     }
 
     // 3. dh <- e^gamma_L dh + Q_g^T dO - W^T dD; wave w owns key rows 32 w .. 32 w + 31
@@ -208,6 +211,22 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
         dh[dt][vt] = acc - acw;
       }
     __syncthreads();
+  };
+
+  if (c_begin < c_end) {
+    // chunks run from the last to the first; the request past the first chunk
+    // re-reads the first one
+    const int first = c_begin;
+    Ops A, B;
+    load_ops(c_end - 1, A);
+    for (int c = c_end - 1;; c -= 2) {
+      load_ops(max(c - 1, first), B);
+      step(c, A);
+      if (c - 1 < first) break;
+      load_ops(max(c - 2, first), A);
+      step(c - 1, B);
+      if (c - 2 < first) break;
+    }
   }
 
   if (dh0) {
@@ -900,22 +919,14 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
   }
 }
 
-int scan_value_block(long chains);  // shared with the forward scan
-
 hipError_t launch_bwd_dh_scan(const int32_t* seq_first, int N, int HV, int NC,
                               const ChunkInfo* table, const PrepOut& prep, const uint16_t* dO,
                               const float* dhT, float* dh0, const BwdBufs& bufs,
                               hipStream_t stream) {
   const long chains = (long)N * HV;
-  const long groups = (chains + 7) / 8;
-  const int vb = scan_value_block(chains);
-  const long blocks = groups * 8 * (kHead / vb);
-  if (vb == 16)
-    hipLaunchKernelGGL(bwd_dh_scan_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       seq_first, N, HV, NC, table, prep, dO, dhT, dh0, bufs);
-  else
-    hipLaunchKernelGGL(bwd_dh_scan_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       seq_first, N, HV, NC, table, prep, dO, dhT, dh0, bufs);
+  const long blocks = (chains + 7) / 8 * 8 * (kHead / kScanVB);
+  hipLaunchKernelGGL(bwd_dh_scan_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, seq_first,
+                     N, HV, NC, table, prep, dO, dhT, dh0, bufs);
   return hipGetLastError();
 }
 

@@ -24,11 +24,12 @@
 
 namespace gdn {
 
-template <int VB>
+template <bool kSave>
 __global__ __launch_bounds__(256) void fwd_scan_kernel(
     const int32_t* __restrict__ seq_first, int N, int HV, int NC,
     const ChunkInfo* __restrict__ table, PrepOut prep, const float* __restrict__ h0,
     uint16_t* __restrict__ o, float* __restrict__ hT, uint16_t* __restrict__ saved) {
+  constexpr int VB = kScanVB;
   constexpr int NVB = kHead / VB;  // value blocks per head
   constexpr int VT = VB / 16;      // 16-wide value tiles per block
   constexpr int SP = 136;          // LDS pitch of S rows (bf16)
@@ -64,13 +65,15 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
       }
     }
 
-  // Operands of one chunk in MFMA fragment layout; the next chunk's are loaded
-  // while the current one computes, so the chain never waits on memory.
+  // Operands of one chunk in MFMA fragment layout. Two sets alternate: the
+  // next chunk's set is requested before the current chunk computes. Every
+  // chunk issues the same number of loads and stores, with no branch around
+  // any of them, so the wait for a set counts exactly the memory operations
+  // issued after it and never waits for a store to finish.
   struct Ops {
     bf16x8 wa[4], qa[4], pa[2], ka[2][2];
     uint2 u[VT];
     float gl;
-    ChunkInfo ci;
   };
   auto load_ops = [&](int c, Ops& x) {
     const size_t blk = (size_t)hv * NC + c;
@@ -96,17 +99,22 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
       x.u[vt] = *reinterpret_cast<const uint2*>(Ub + (size_t)(v0 + 16 * vt + li) * 64 +
                                                 16 * wave + 4 * kq);
     x.gl = prep.gL[blk];
-    x.ci = table[c];
   };
 
+  // The chunks of one sequence are consecutive 64-token pieces, so a chunk's
+  // first token and length follow from the sequence's bounds without a table
+  // read on the chain's critical path.
   const int c_begin = seq_first[seq], c_end = seq_first[seq + 1];
-  Ops nxt;
-  if (c_begin < c_end) load_ops(c_begin, nxt);
-  for (int c = c_begin; c < c_end; ++c) {
-    const Ops cur = nxt;
-    if (c + 1 < c_end) load_ops(c + 1, nxt);
-    const ChunkInfo ci = cur.ci;
+  int bos = 0, eos = 0;
+  if (c_begin < c_end) {
+    const ChunkInfo first = table[c_begin], lastc = table[c_end - 1];
+    bos = first.t0;
+    eos = lastc.t0 + lastc.len;
+  }
 
+  auto step = [&](int c, const Ops& cur) {
+    const int t0 = bos + (c - c_begin) * kChunk;
+    const int len = min(kChunk, eos - t0);
     // 1. chunk-start state -> LDS (bf16)
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
@@ -118,11 +126,13 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
             pack4_bf16(h[dt][vt][0], h[dt][vt][1], h[dt][vt][2], h[dt][vt][3]);
       }
     __syncthreads();
-    // saved for the backward: h = S^T as [k][v] rows (16-byte column gathers of Ss)
-    uint16_t* sv = saved ? saved + blk_saved(c, hv, HV) : nullptr;
-    if (sv) {
-      for (int e = tid; e < kHead * (VB / 8); e += 256) {
-        const int kk = e / (VB / 8), vg = e - kk * (VB / 8);
+    uint16_t* sv = saved + blk_saved(c, hv, HV);
+    if constexpr (kSave) {
+      // h = S^T as [k][v] rows (16-byte column gathers of Ss): 2 per thread
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int e = tid + 256 * i;
+        const int kk = e >> 2, vg = e & 3;
         *reinterpret_cast<uint4*>(sv + kk * kHead + v0 + 8 * vg) = gather8(&Ss[(8 * vg) * SP + kk], SP);
       }
     }
@@ -146,18 +156,20 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
                      bf2f(u.y & 0xffffu) - acc[2], bf2f(u.y >> 16) - acc[3]);
     }
     __syncthreads();
-    // saved for the backward: D as [tok][v] rows
-    if (sv) {
-      for (int e = tid; e < kChunk * (VB / 8); e += 256) {
-        const int t = e / (VB / 8), vg = e - t * (VB / 8);
-        *reinterpret_cast<uint4*>(sv + kSavedH + t * kHead + v0 + 8 * vg) =
-            gather8(&Ds[(8 * vg) * DP + t], DP);
-      }
+    if constexpr (kSave) {
+      // D as [tok][v] rows: one 16-byte store per thread
+      const int t = tid >> 2, vg = tid & 3;
+      *reinterpret_cast<uint4*>(sv + kSavedH + t * kHead + v0 + 8 * vg) = gather8(&Ds[(8 * vg) * DP + t], DP);
     }
 
-    // 3. O^T = S Q_g^T + D^T P^T; wave w owns tokens 16 w .. 16 w + 15
+    // 3. O^T = S Q_g^T + D^T P^T; wave w owns tokens 16 w .. 16 w + 15. Rows at
+    //    or past the chunk length fall outside the store's buffer range, which
+    //    drops them.
     {
       const int tl = 16 * wave + li;
+      const __amdgpu_buffer_rsrc_t orng =
+          __builtin_amdgcn_make_buffer_rsrc(o + ((size_t)t0 * HV + hv) * kHead, 0,
+                                            len * HV * kHead * 2, kBufferWord3);
 #pragma unroll
       for (int vt = 0; vt < VT; ++vt) {
         bf16x8 sb[4], db[2];
@@ -174,9 +186,8 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
         if (wave >= 2) a1 = mfma(db[1], cur.pa[1], a1);
         const f32x4 acc = a0 + a1;
         // acc[r] = O[t = t0 + 16 w + li][v = v0 + 16 vt + 4 kq + r]
-        if (tl < ci.len)
-          *reinterpret_cast<uint2*>(o + ((size_t)(ci.t0 + tl) * HV + hv) * kHead + v0 + 16 * vt +
-                                    4 * kq) = pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
+        store_b64(pack4_bf16(acc[0], acc[1], acc[2], acc[3]), orng,
+                  (tl * HV * kHead + v0 + 16 * vt + 4 * kq) * 2);
       }
     }
 
@@ -192,6 +203,22 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
         h[dt][vt] = acc;
       }
     __syncthreads();
+  };
+
+  if (c_begin < c_end) {
+    // the request past the last chunk re-reads the last chunk: one extra set
+    // per chain keeps the memory operations of every chunk the same
+    const int last = c_end - 1;
+    Ops A, B;
+    load_ops(c_begin, A);
+    for (int c = c_begin;; c += 2) {
+      load_ops(min(c + 1, last), B);
+      step(c, A);
+      if (c + 1 > last) break;
+      load_ops(min(c + 2, last), A);
+      step(c + 1, B);
+      if (c + 2 > last) break;
+    }
   }
 
   if (hT) {
@@ -213,23 +240,16 @@ __global__ __launch_bounds__(256) void state_copy_kernel(const float* __restrict
   if (i < n) dst[i] = src ? src[i] : 0.f;
 }
 
-// Value-block width of the scans: the chains run concurrently only while every
-// workgroup is resident (two per CU at this register use), so few chains get
-// narrower value blocks and more workgroups.
-int scan_value_block(long chains) { (void)chains; return 32; }
-
 hipError_t launch_fwd_scan(const int32_t* seq_first, int N, int HV, int NC,
                            const ChunkInfo* table, const PrepOut& prep, const float* h0,
                            uint16_t* o, float* hT, uint16_t* saved, hipStream_t stream) {
   const long chains = (long)N * HV;
-  const long groups = (chains + 7) / 8;
-  const int vb = scan_value_block(chains);
-  const long blocks = groups * 8 * (kHead / vb);
-  if (vb == 16)
-    hipLaunchKernelGGL(fwd_scan_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream,
+  const long blocks = (chains + 7) / 8 * 8 * (kHead / kScanVB);
+  if (saved)
+    hipLaunchKernelGGL(fwd_scan_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
                        seq_first, N, HV, NC, table, prep, h0, o, hT, saved);
   else
-    hipLaunchKernelGGL(fwd_scan_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL(fwd_scan_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
                        seq_first, N, HV, NC, table, prep, h0, o, hT, saved);
   return hipGetLastError();
 }

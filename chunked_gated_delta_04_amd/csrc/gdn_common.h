@@ -20,6 +20,25 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kHead = 128;   // K = V
 constexpr int kChunk = 64;   // tokens per chunk
 constexpr float kNormEps = 1e-6f;
+constexpr int kScanVB = 32;  // value columns per workgroup of the state scans
+
+// Fourth word of a raw buffer resource on gfx9-family parts (32-bit data
+// format, no swizzle). A raw buffer store whose byte offset lies at or past
+// the resource's record count is discarded by the hardware, which lets a
+// kernel mask the rows past a chunk's end without a branch.
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ void store_b64(uint2 v, __amdgpu_buffer_rsrc_t r, int byte_off) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, r, byte_off, 0, 0);
+}
+
+// Raw buffer load of 16 bytes; zeros where the offset is past the record count.
+__device__ __forceinline__ uint4 load_b128(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
