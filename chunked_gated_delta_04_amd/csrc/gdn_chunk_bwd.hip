@@ -260,10 +260,12 @@ constexpr int BP = 72;  // LDS pitch (bf16) of [64][64] tiles
 struct BwdLds {
   uint16_t Ks[64 * KP];                     // k^ rows
   uint16_t KsT[128 * TP], QsT[128 * TP];    // k^, q~ transposed [k][tok]
-  uint16_t Pm[64 * BP], PmT[64 * BP];       // dP o Gamma and transpose; later M, M^T
+  uint16_t Pm[64 * BP], PmT[64 * BP];       // dP o Gamma and transpose; then T, T^T;
+                                            // then M, M^T
   uint16_t Hs[128 * KP];                    // h [k][v], then dh' [k][v]; dq staging at the end
   union {                                   // time-shared regions
     uint16_t Z[64 * KP];                    //   Z = T^T dD [tok][v]
+    uint16_t V[64 * KP];                    //   V rows of the chunk
     uint16_t dT[64 * BP];                   //   dT [i][m]
   } rz;
   union {
@@ -397,19 +399,38 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     const uint16_t* dDb = bufs.dD + blk * 8192;          // dD [tok][v]
     const uint16_t* dDTb = bufs.dDT + blk * 8192;        // dD^T [v][tok]
     const uint16_t* Tg = Tmat + blk * 8192;              // T, then T^T [64][64]
-    const uint16_t* dOb = dO + ((size_t)t0 * HV + hv) * kHead;
-    const uint16_t* vb = v + ((size_t)t0 * HV + hv) * kHead;
+    // Token rows of dO, v and q through range-checked buffer loads: rows at or
+    // past the chunk's end read as zeros, with no branch around the load.
+    const __amdgpu_buffer_rsrc_t rdO = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(dO) + ((size_t)t0 * HV + hv) * kHead, 0, L * (int)rs * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(v) + ((size_t)t0 * HV + hv) * kHead, 0, L * (int)rs * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(q) + ((size_t)t0 * H + h) * kHead, 0, L * H * kHead * 2, kBufferWord3);
 
     // ---- requests for the dP phase: the own rows of dO and q, the D rows of
     //      this wave's dP tiles
     bf16x8 oa[4], qa[4], dfr[2][4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      oa[s] = trow_ok ? ld8(dOb + (size_t)trow * rs + 32 * s + 8 * kq) : zero8();
-      qa[s] = trow_ok ? ld8(q + ((size_t)(t0 + trow) * H + h) * kHead + 32 * s + 8 * kq) : zero8();
+      oa[s] = ld8_buf(rdO, (trow * (int)rs + 32 * s + 8 * kq) * 2);
+      qa[s] = ld8_buf(rq, (trow * H * kHead + 32 * s + 8 * kq) * 2);
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2)
         dfr[q2][s] = ld8(Db + (16 * (kh + 2 * q2) + li) * kHead + 32 * s + 8 * kq);
+    }
+
+    // requests for the Z phase: T^T rows of this wave's tokens, dD^T rows, v rows
+    bf16x8 tt[2], ddt[4][2];
+    uint2 vr[4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) tt[s] = ld8(Tg + 4096 + trow * 64 + 32 * s + 8 * kq);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int vt = 4 * kh + j;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) ddt[j][s] = ld8(dDTb + (16 * vt + li) * 64 + 32 * s + 8 * kq);
+      vr[j] = load_b64(rv, (trow * (int)rs + 16 * vt + 4 * kq) * 2);
     }
 
     // ---- gates
@@ -485,19 +506,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         for (int r = 0; r < 4; ++r) S.rowF[kh][16 * tw + 4 * kq + r] = rowp[r];
       }
     }
-    // requests for the Z phase: T^T rows of this wave's tokens, dD^T rows, v rows
-    bf16x8 tt[2], ddt[4][2];
-    uint2 vr[4];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) tt[s] = ld8(Tg + 4096 + trow * 64 + 32 * s + 8 * kq);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int vt = 4 * kh + j;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) ddt[j][s] = ld8(dDTb + (16 * vt + li) * 64 + 32 * s + 8 * kq);
-      vr[j] = trow_ok ? *reinterpret_cast<const uint2*>(vb + (size_t)trow * rs + 16 * vt + 4 * kq)
-                      : make_uint2(0, 0);
-    }
     // h, staged into LDS once the Z phase is done with its operands
     uint4 hst[4];
 #pragma unroll
@@ -547,45 +555,54 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     //      pass 2: x3 = dD h^T (= -dW), stored for dT
     //      then dh' replaces h in LDS; pass 3: x2 = D dh'^T
     float gr[4] = {0.f, 0.f, 0.f, 0.f}, br[4] = {0.f, 0.f, 0.f, 0.f};
-    {
-      bf16x8 za[4], pa[2], pta[2];
+    {  // pass 1a: x1, y1 -> dq~
+      bf16x8 pa[2];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) za[s] = ld8(&S.rz.Z[trow * KP + 32 * s + 8 * kq]);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        pa[s] = ld8(&S.Pm[trow * BP + 32 * s + 8 * kq]);
-        pta[s] = ld8(&S.PmT[trow * BP + 32 * s + 8 * kq]);
-      }
+      for (int s = 0; s < 2; ++s) pa[s] = ld8(&S.Pm[trow * BP + 32 * s + 8 * kq]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int kr = 16 * (4 * kh + j) + li;
-        bf16x8 hf[4];
+        f32x4 x1 = zero4(), y1 = zero4();
 #pragma unroll
-        for (int s = 0; s < 4; ++s) hf[s] = ld8(&S.Hs[kr * KP + 32 * s + 8 * kq]);
-        f32x4 x1 = zero4(), x4 = zero4(), y1 = zero4(), y2 = zero4();
+        for (int s = 0; s < 4; ++s) x1 = mfma(oa[s], ld8(&S.Hs[kr * KP + 32 * s + 8 * kq]), x1);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          x1 = mfma(oa[s], hf[s], x1);
-          x4 = mfma(za[s], hf[s], x4);
-        }
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < 2; ++s)
           if (32 * s <= 16 * tw + 15)  // (dP o Gamma)[t][j] needs j <= t
             y1 = mfma(pa[s], ld8(&S.KsT[kr * TP + 32 * s + 8 * kq]), y1);
-          if (32 * s + 31 >= 16 * tw)  // (dP o Gamma)[i][t] needs i >= t
-            y2 = mfma(pta[s], ld8(&S.QsT[kr * TP + 32 * s + 8 * kq]), y2);
-        }
         const int tr = 16 * tw + 4 * kq;
         const float4 qv = ld4_bf16(&S.QsT[kr * TP + tr]);
-        const float4 kv = ld4_bf16(&S.KsT[kr * TP + tr]);
         const float qa_[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = S.eg[tr + r];
+          adq[j][r] += e * x1[r] + y1[r];
+          gr[r] += e * qa_[r] * x1[r];               // inter-chunk output decay
+        }
+      }
+    }
+    {  // pass 1b: x4, y2 -> dk^
+      bf16x8 za[4], pta[2];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) za[s] = ld8(&S.rz.Z[trow * KP + 32 * s + 8 * kq]);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) pta[s] = ld8(&S.PmT[trow * BP + 32 * s + 8 * kq]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kr = 16 * (4 * kh + j) + li;
+        f32x4 x4 = zero4(), y2 = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) x4 = mfma(za[s], ld8(&S.Hs[kr * KP + 32 * s + 8 * kq]), x4);
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          if (32 * s + 31 >= 16 * tw)  // (dP o Gamma)[i][t] needs i >= t
+            y2 = mfma(pta[s], ld8(&S.QsT[kr * TP + 32 * s + 8 * kq]), y2);
+        const int tr = 16 * tw + 4 * kq;
+        const float4 kv = ld4_bf16(&S.KsT[kr * TP + tr]);
         const float ka_[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = tr + r;
           const float e = S.eg[t], bt = S.bet[t];
-          adq[j][r] += e * x1[r] + y1[r];
-          gr[r] += e * qa_[r] * x1[r];               // inter-chunk output decay
           adk[j][r] += y2[r] - bt * e * x4[r];
           const float zk = -ka_[r] * x4[r];          // k^ . (T^T dW)
           br[r] += e * zk;
@@ -593,16 +610,26 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         }
       }
     }
-    uint4 dst[4];  // dh' requests, staged into LDS once h is no longer read
+    // Requests, oldest first: dh' (staged into LDS once h is no longer read),
+    // the own rows of dD (pass 2 and dT) and of D (pass 3), then the operands
+    // of the dT, Y1 and dA phases, so that each wait covers only what it needs.
+    uint4 dst[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = tid + 512 * i;
       dst[i] = *reinterpret_cast<const uint4*>(dhb + (e >> 4) * kHead + (e & 15) * 8);
     }
-    {
-      bf16x8 ea[4];
+    bf16x8 ea[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) ea[s] = ld8(dDb + trow * kHead + 32 * s + 8 * kq);
+    for (int s = 0; s < 4; ++s) ea[s] = ld8(dDb + trow * kHead + 32 * s + 8 * kq);
+    // V of the chunk, staged into LDS once Z is dead: two 16-byte pieces per thread
+    uint4 vst[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid + 512 * i;
+      vst[i] = load_b128(rv, ((e >> 4) * (int)rs + (e & 15) * 8) * 2);
+    }
+    {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int kr = 16 * (4 * kh + j) + li;
@@ -625,15 +652,24 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       hd = wave_sum(hd);
       if (lane == 0) S.hd_part[wave] = hd;
     }
-    __syncthreads();  // every wave is done with h
+    __syncthreads();  // every wave is done with h and Z
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = tid + 512 * i;
       *reinterpret_cast<uint4*>(&S.Hs[(e >> 4) * KP + (e & 15) * 8]) = dst[i];
     }
-    bf16x8 da[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid + 512 * i;
+      *reinterpret_cast<uint4*>(&S.rz.V[(e >> 4) * KP + (e & 15) * 8]) = vst[i];
+    }
+    bf16x8 da[4];  // own rows of D (pass 3)
 #pragma unroll
     for (int s = 0; s < 4; ++s) da[s] = ld8(Db + trow * kHead + 32 * s + 8 * kq);
+    // T and T^T, staged into LDS (P is dead) after pass 3
+    uint4 tst[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) tst[i] = *reinterpret_cast<const uint4*>(Tg + 8 * (tid + 512 * i));
     __syncthreads();
     {
       float glp = 0.f;
@@ -672,23 +708,16 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       if (lane == 0) S.gl_part[wave] = glp;
     }
 
+#pragma unroll
+    for (int i = 0; i < 2; ++i)  // T rows into Pm, T^T rows into PmT
+      *reinterpret_cast<uint4*>(&(i == 0 ? S.Pm : S.PmT)[(tid >> 3) * BP + (tid & 7) * 8]) = tst[i];
+
     // ---- dT = dD (beta V)^T + dW (beta e^gamma K^)^T, strictly lower
     //      (wave: row tile tw, col tiles kh, kh + 2)
-    bf16x8 ty[2][2], tta[2];  // requests for Y1 (T rows) and dA (T^T rows)
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      tta[s] = ld8(Tg + 4096 + trow * 64 + 32 * s + 8 * kq);
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2)
-        ty[q2][s] = ld8(Tg + (16 * (kh + 2 * q2) + li) * 64 + 32 * s + 8 * kq);
-    }
     {
-      bf16x8 wa[4], ea[4];
+      bf16x8 wa[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        wa[s] = ld8(&S.rw.dW[trow * KP + 32 * s + 8 * kq]);
-        ea[s] = ld8(dDb + trow * kHead + 32 * s + 8 * kq);
-      }
+      for (int s = 0; s < 4; ++s) wa[s] = ld8(&S.rw.dW[trow * KP + 32 * s + 8 * kq]);
       f32x4 acc[2];
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
@@ -696,10 +725,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         f32x4 a1 = zero4(), a2 = zero4();
         if (mb <= tw) {
           const int mrow = 16 * mb + li;
-          const bool mok = mrow < L;
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            a1 = mfma(ea[s], mok ? ld8(vb + (size_t)mrow * rs + 32 * s + 8 * kq) : zero8(), a1);
+            a1 = mfma(ea[s], ld8(&S.rz.V[mrow * KP + 32 * s + 8 * kq]), a1);
             a2 = mfma(wa[s], ld8(&S.Ks[mrow * KP + 32 * s + 8 * kq]), a2);
           }
         }
@@ -710,7 +738,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
           acc[q2][r] = i > m ? S.bet[m] * (a1[r] + S.eg[m] * a2[r]) : 0.f;
         }
       }
-      __syncthreads();  // every wave has read dW before dT overwrites the region
+      __syncthreads();  // every wave has read V and dW
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
         const int m = 16 * (kh + 2 * q2) + li;
@@ -731,7 +759,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         f32x4 acc = zero4();
         if (jb <= tw) {
 #pragma unroll
-          for (int s = 0; s < 2; ++s) acc = mfma(ta[s], ty[q2][s], acc);
+          for (int s = 0; s < 2; ++s)
+            acc = mfma(ta[s], ld8(&S.Pm[(16 * jb + li) * BP + 32 * s + 8 * kq]), acc);
         }
         const int j = 16 * jb + li;
         float y[4];
@@ -745,6 +774,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 
     // ---- dA = -T^T Y1 (i > j); M = dA o beta_i Gamma -> Pm, PmT; E = dA o A sums; dbeta of A
     {
+      bf16x8 tta[2];  // own rows of T^T, read before M overwrites them
+#pragma unroll
+      for (int s = 0; s < 2; ++s) tta[s] = ld8(&S.PmT[trow * BP + 32 * s + 8 * kq]);
+      __syncthreads();
       float re[4] = {0.f, 0.f, 0.f, 0.f}, rb[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {

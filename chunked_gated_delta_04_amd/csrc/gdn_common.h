@@ -33,11 +33,19 @@ __device__ __forceinline__ void store_b64(uint2 v, __amdgpu_buffer_rsrc_t r, int
   __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, r, byte_off, 0, 0);
 }
 
-// Raw buffer load of 16 bytes; zeros where the offset is past the record count.
+// Raw buffer loads; zeros where the offset is past the record count.
 __device__ __forceinline__ uint4 load_b128(__amdgpu_buffer_rsrc_t r, int byte_off) {
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
   return make_uint4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ uint2 load_b64(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
+  return make_uint2(x[0], x[1]);
+}
+__device__ __forceinline__ bf16x8 ld8_buf(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(bf16x8, load_b128(r, byte_off));
 }
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
