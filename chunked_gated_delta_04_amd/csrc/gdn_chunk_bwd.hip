@@ -115,16 +115,16 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
     const uint16_t* QgT = prep.Qg + blk * 8192;  // Q_g^T [k][tok]
     const uint16_t* WT = prep.W + blk * 8192;    // W^T [k][tok]
 #pragma unroll
-    for (int s = 0; s < 2; ++s) x.pa[s] = ld8(PTb + (16 * wave + li) * 64 + 32 * s + 8 * kq);
+    for (int s = 0; s < 2; ++s) x.pa[s] = ld8(PTb + kcm(16 * wave + li, 32 * s + 8 * kq, 64));
 #pragma unroll
-    for (int s = 0; s < 4; ++s) x.ka[s] = ld8(Kbb + (16 * wave + li) * kHead + 32 * s + 8 * kq);
+    for (int s = 0; s < 4; ++s) x.ka[s] = ld8(Kbb + kcm(16 * wave + li, 32 * s + 8 * kq, 64));
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) {
       const int kr = 16 * (2 * wave + dt) + li;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        x.qa[dt][s] = ld8(QgT + kr * 64 + 32 * s + 8 * kq);
-        x.wa[dt][s] = ld8(WT + kr * 64 + 32 * s + 8 * kq);
+        x.qa[dt][s] = ld8(QgT + kcm(kr, 32 * s + 8 * kq, 128));
+        x.wa[dt][s] = ld8(WT + kcm(kr, 32 * s + 8 * kq, 128));
       }
     }
     x.gl = prep.gL[blk];
@@ -153,14 +153,15 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
       for (int u = 0; u < 8; ++u) Os[(8 * osg + u) * DP + ot] = xs[u];
     }
     __syncthreads();
-    // dh' (gradient of this chunk's end state) as [k][v]: two 16-byte stores per thread
+    // dh' (gradient of this chunk's end state), value block by value block:
+    // [v / 32][k][v % 32]; two 16-byte stores per thread
     {
-      uint16_t* dhb = bufs.dh + blk * (kHead * kHead);
+      uint16_t* dhb = bufs.dh + blk * (kHead * kHead) + vb * (kHead * VB);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int e = tid + 256 * i;
         const int kk = e >> 2, vg = e & 3;
-        *reinterpret_cast<uint4*>(dhb + kk * kHead + v0 + 8 * vg) = gather8(&Hs[(8 * vg) * SP + kk], SP);
+        *reinterpret_cast<uint4*>(dhb + 8 * e) = gather8(&Hs[(8 * vg) * SP + kk], SP);
       }
     }
 
@@ -185,15 +186,16 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
           pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
     }
     __syncthreads();
-    // dD to global as [v][tok] (row copy) and [tok][v] (column gather): one each per thread
+    // dD to global as [v][tok] (row copy) and [tok][v] (column gather), both in
+    // the chunk-major tile layout: one 16-byte store each per thread
     {
       uint16_t* dDT = bufs.dDT + blk * 8192;
       uint16_t* dDr = bufs.dD + blk * 8192;
-      const int vl = tid >> 3, sg = tid & 7;
-      *reinterpret_cast<uint4*>(dDT + (v0 + vl) * 64 + 8 * sg) =
+      const int sg = tid >> 5, vl = tid & 31;
+      *reinterpret_cast<uint4*>(dDT + kcm(v0 + vl, 8 * sg, kHead)) =
           *reinterpret_cast<const uint4*>(&Es[vl * DP + 8 * sg]);
-      const int t = tid >> 2, vg = tid & 3;
-      *reinterpret_cast<uint4*>(dDr + t * kHead + v0 + 8 * vg) = gather8(&Es[(8 * vg) * DP + t], DP);
+      const int vg = tid >> 6, t = tid & 63;
+      *reinterpret_cast<uint4*>(dDr + kcm(t, v0 + 8 * vg, kChunk)) = gather8(&Es[(8 * vg) * DP + t], DP);
     }
 
     // 3. dh <- e^gamma_L dh + Q_g^T dO - W^T dD; wave w owns key rows 32 w .. 32 w + 31
@@ -288,6 +290,12 @@ __device__ __forceinline__ bf16x8 zero8() {
 __device__ __forceinline__ float4 ld4_bf16(const uint16_t* p) {  // 4 bf16 -> fp32
   const uint2 u = *reinterpret_cast<const uint2*>(p);
   return make_float4(bf2f(u.x & 0xffffu), bf2f(u.x >> 16), bf2f(u.y & 0xffffu), bf2f(u.y >> 16));
+}
+// LDS position (pitch KP, [k][v]) of 16-byte chunk e of a state stored value
+// block by value block, [v / 32][k][v % 32]
+__device__ __forceinline__ int state_pos(int e) {
+  const int vb = e >> 9, kk = (e >> 2) & 127, vg = e & 3;
+  return kk * KP + vb * kScanVB + vg * 8;
 }
 __device__ __forceinline__ float dot8u(const uint4& a, const uint4& b) {  // bf16 pairs
   const uint32_t* x = reinterpret_cast<const uint32_t*>(&a);
@@ -393,12 +401,13 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     const bool trow_ok = trow < L;
     const int hv = h * G + jg;
     const size_t blk = (size_t)hv * NC + c;
-    const uint16_t* hb = saved + blk_saved(c, hv, HV);  // h [k][v]
-    const uint16_t* Db = hb + kSavedH;                   // D [tok][v]
-    const uint16_t* dhb = bufs.dh + blk * (kHead * kHead);
-    const uint16_t* dDb = bufs.dD + blk * 8192;          // dD [tok][v]
-    const uint16_t* dDTb = bufs.dDT + blk * 8192;        // dD^T [v][tok]
-    const uint16_t* Tg = Tmat + blk * 8192;              // T, then T^T [64][64]
+    // (chunk-major tiles: see kcm; states: [v / 32][k][v % 32])
+    const uint16_t* hb = saved + blk_saved(c, hv, HV);  // h
+    const uint16_t* Db = hb + kSavedH;                   // D [tok][v], chunk-major
+    const uint16_t* dhb = bufs.dh + blk * (kHead * kHead);  // dh'
+    const uint16_t* dDb = bufs.dD + blk * 8192;          // dD [tok][v], chunk-major
+    const uint16_t* dDTb = bufs.dDT + blk * 8192;        // dD^T [v][tok], chunk-major
+    const uint16_t* Tg = Tmat + blk * 8192;              // T, then T^T, chunk-major
     // Token rows of dO, v and q through range-checked buffer loads: rows at or
     // past the chunk's end read as zeros, with no branch around the load.
     const __amdgpu_buffer_rsrc_t rdO = __builtin_amdgcn_make_buffer_rsrc(
@@ -417,19 +426,19 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       qa[s] = ld8_buf(rq, (trow * H * kHead + 32 * s + 8 * kq) * 2);
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2)
-        dfr[q2][s] = ld8(Db + (16 * (kh + 2 * q2) + li) * kHead + 32 * s + 8 * kq);
+        dfr[q2][s] = ld8(Db + kcm(16 * (kh + 2 * q2) + li, 32 * s + 8 * kq, kChunk));
     }
 
     // requests for the Z phase: T^T rows of this wave's tokens, dD^T rows, v rows
     bf16x8 tt[2], ddt[4][2];
     uint2 vr[4];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) tt[s] = ld8(Tg + 4096 + trow * 64 + 32 * s + 8 * kq);
+    for (int s = 0; s < 2; ++s) tt[s] = ld8(Tg + 4096 + kcm(trow, 32 * s + 8 * kq, 64));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int vt = 4 * kh + j;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) ddt[j][s] = ld8(dDTb + (16 * vt + li) * 64 + 32 * s + 8 * kq);
+      for (int s = 0; s < 2; ++s) ddt[j][s] = ld8(dDTb + kcm(16 * vt + li, 32 * s + 8 * kq, kHead));
       vr[j] = load_b64(rv, (trow * (int)rs + 16 * vt + 4 * kq) * 2);
     }
 
@@ -511,7 +520,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = tid + 512 * i;
-      hst[i] = *reinterpret_cast<const uint4*>(hb + (e >> 4) * kHead + (e & 15) * 8);
+      hst[i] = *reinterpret_cast<const uint4*>(hb + 8 * e);
     }
 
     // ---- Z = T^T dD (written [tok][v]); dV = diag(beta) Z; dbeta of U.
@@ -545,7 +554,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = tid + 512 * i;
-      *reinterpret_cast<uint4*>(&S.Hs[(e >> 4) * KP + (e & 15) * 8]) = hst[i];
+      *reinterpret_cast<uint4*>(&S.Hs[state_pos(e)]) = hst[i];
     }
     __syncthreads();
 
@@ -617,11 +626,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = tid + 512 * i;
-      dst[i] = *reinterpret_cast<const uint4*>(dhb + (e >> 4) * kHead + (e & 15) * 8);
+      dst[i] = *reinterpret_cast<const uint4*>(dhb + 8 * e);
     }
     bf16x8 ea[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) ea[s] = ld8(dDb + trow * kHead + 32 * s + 8 * kq);
+    for (int s = 0; s < 4; ++s) ea[s] = ld8(dDb + kcm(trow, 32 * s + 8 * kq, kChunk));
     // V of the chunk, staged into LDS once Z is dead: two 16-byte pieces per thread
     uint4 vst[2];
 #pragma unroll
@@ -647,7 +656,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = tid + 512 * i;
-        hd += dot8u(*reinterpret_cast<const uint4*>(&S.Hs[(e >> 4) * KP + (e & 15) * 8]), dst[i]);
+        hd += dot8u(*reinterpret_cast<const uint4*>(&S.Hs[state_pos(e)]), dst[i]);
       }
       hd = wave_sum(hd);
       if (lane == 0) S.hd_part[wave] = hd;
@@ -656,7 +665,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = tid + 512 * i;
-      *reinterpret_cast<uint4*>(&S.Hs[(e >> 4) * KP + (e & 15) * 8]) = dst[i];
+      *reinterpret_cast<uint4*>(&S.Hs[state_pos(e)]) = dst[i];
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -665,7 +674,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     }
     bf16x8 da[4];  // own rows of D (pass 3)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) da[s] = ld8(Db + trow * kHead + 32 * s + 8 * kq);
+    for (int s = 0; s < 4; ++s) da[s] = ld8(Db + kcm(trow, 32 * s + 8 * kq, kChunk));
     // T and T^T, staged into LDS (P is dead) after pass 3
     uint4 tst[2];
 #pragma unroll
@@ -710,7 +719,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 
 #pragma unroll
     for (int i = 0; i < 2; ++i)  // T rows into Pm, T^T rows into PmT
-      *reinterpret_cast<uint4*>(&(i == 0 ? S.Pm : S.PmT)[(tid >> 3) * BP + (tid & 7) * 8]) = tst[i];
+      *reinterpret_cast<uint4*>(&(i == 0 ? S.Pm : S.PmT)[(tid & 63) * BP + (tid >> 6) * 8]) = tst[i];
 
     // ---- dT = dD (beta V)^T + dW (beta e^gamma K^)^T, strictly lower
     //      (wave: row tile tw, col tiles kh, kh + 2)

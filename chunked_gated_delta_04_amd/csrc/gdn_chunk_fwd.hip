@@ -84,20 +84,19 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     const uint16_t* Kb = prep.Kb + blk * 8192;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      x.wa[s] = ld8(Wb + (16 * wave + li) * kHead + 32 * s + 8 * kq);
-      x.qa[s] = ld8(Qb + (16 * wave + li) * kHead + 32 * s + 8 * kq);
+      x.wa[s] = ld8(Wb + kcm(16 * wave + li, 32 * s + 8 * kq, 64));
+      x.qa[s] = ld8(Qb + kcm(16 * wave + li, 32 * s + 8 * kq, 64));
     }
 #pragma unroll
-    for (int s = 0; s < 2; ++s) x.pa[s] = ld8(Pb + (16 * wave + li) * 64 + 32 * s + 8 * kq);
+    for (int s = 0; s < 2; ++s) x.pa[s] = ld8(Pb + kcm(16 * wave + li, 32 * s + 8 * kq, 64));
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        x.ka[dt][s] = ld8(Kb + (16 * (2 * wave + dt) + li) * 64 + 32 * s + 8 * kq);
+        x.ka[dt][s] = ld8(Kb + kcm(16 * (2 * wave + dt) + li, 32 * s + 8 * kq, 128));
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt)
-      x.u[vt] = *reinterpret_cast<const uint2*>(Ub + (size_t)(v0 + 16 * vt + li) * 64 +
-                                                16 * wave + 4 * kq);
+      x.u[vt] = *reinterpret_cast<const uint2*>(Ub + kcm(v0 + 16 * vt + li, 16 * wave + 4 * kq, 128));
     x.gl = prep.gL[blk];
   };
 
@@ -128,12 +127,13 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     __syncthreads();
     uint16_t* sv = saved + blk_saved(c, hv, HV);
     if constexpr (kSave) {
-      // h = S^T as [k][v] rows (16-byte column gathers of Ss): 2 per thread
+      // h = S^T, value block by value block: [v / 32][k][v % 32] (16-byte
+      // column gathers of Ss; consecutive threads write consecutive chunks)
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int e = tid + 256 * i;
         const int kk = e >> 2, vg = e & 3;
-        *reinterpret_cast<uint4*>(sv + kk * kHead + v0 + 8 * vg) = gather8(&Ss[(8 * vg) * SP + kk], SP);
+        *reinterpret_cast<uint4*>(sv + vb * (kHead * VB) + 8 * e) = gather8(&Ss[(8 * vg) * SP + kk], SP);
       }
     }
 
@@ -157,9 +157,10 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     }
     __syncthreads();
     if constexpr (kSave) {
-      // D as [tok][v] rows: one 16-byte store per thread
-      const int t = tid >> 2, vg = tid & 3;
-      *reinterpret_cast<uint4*>(sv + kSavedH + t * kHead + v0 + 8 * vg) = gather8(&Ds[(8 * vg) * DP + t], DP);
+      // D [tok][v] in the chunk-major tile layout: one 16-byte store per thread
+      const int vg = tid >> 6, t = tid & 63;
+      *reinterpret_cast<uint4*>(sv + kSavedH + kcm(t, v0 + 8 * vg, kChunk)) =
+          gather8(&Ds[(8 * vg) * DP + t], DP);
     }
 
     // 3. O^T = S Q_g^T + D^T P^T; wave w owns tokens 16 w .. 16 w + 15. Rows at

@@ -224,7 +224,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             const int j = 16 * jb + 4 * kq + r;
             pv[r] = i >= j ? expf(gam[i] - gam[j]) * acc[r] : 0.f;
           }
-          *reinterpret_cast<uint2*>(Pb + i * 64 + 16 * jb + 4 * kq) =
+          *reinterpret_cast<uint2*>(Pb + kcm(i, 16 * jb + 4 * kq, 64)) =
               pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
         } else {
           // C = Q~ K^T tile: C[4kq+r][li] = P[i = 16 ib + 4kq + r][j = 16 jb + li] -> P^T[j][i..i+3]
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             const int i = 16 * ib + 4 * kq + r;
             pv[r] = i >= j ? expf(gam[i] - gam[j]) * acc[r] : 0.f;
           }
-          *reinterpret_cast<uint2*>(Pb + j * 64 + 16 * ib + 4 * kq) =
+          *reinterpret_cast<uint2*>(Pb + kcm(j, 16 * ib + 4 * kq, 64)) =
               pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
         }
       }
@@ -274,9 +274,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
       uint16_t* Qgb = out.Qg + blk * 8192;
       uint16_t* Kbb = out.Kb + blk * 8192;
       if (!kBwd) {
-        // Q_g [tok][k] (row segments) and K_bwd^T [k][tok] (column gathers)
+        // Q_g [tok][k] (row segments) and K_bwd^T [k][tok] (column gathers);
+        // consecutive threads write consecutive 16-byte chunks
         for (int e = tid; e < 64 * 16; e += 256) {
-          const int t = e >> 4, sg = e & 15;
+          const int sg = e >> 6, t = e & 63;
           const uint4 x = *reinterpret_cast<const uint4*>(&Qs[t * KP + sg * 8]);
           const uint32_t* xw = reinterpret_cast<const uint32_t*>(&x);
           uint4 o4;
@@ -285,10 +286,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
           for (int u = 0; u < 4; ++u)
             ow[u] = (uint32_t)f2bf(eg[t] * bf2f(xw[u] & 0xffffu)) |
                     ((uint32_t)f2bf(eg[t] * bf2f(xw[u] >> 16)) << 16);
-          *reinterpret_cast<uint4*>(Qgb + t * 128 + sg * 8) = o4;
+          *reinterpret_cast<uint4*>(Qgb + kcm(t, sg * 8, 64)) = o4;
         }
         for (int e = tid; e < 128 * 8; e += 256) {
-          const int d = e >> 3, tg = e & 7;
+          const int tg = e >> 7, d = e & 127;
           uint4 o4;
           uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
 #pragma unroll
@@ -297,12 +298,12 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             ow[u] = (uint32_t)f2bf(ebw[ta] * bf2f(Ks[ta * KP + d])) |
                     ((uint32_t)f2bf(ebw[tb] * bf2f(Ks[tb * KP + d])) << 16);
           }
-          *reinterpret_cast<uint4*>(Kbb + d * 64 + 8 * tg) = o4;
+          *reinterpret_cast<uint4*>(Kbb + kcm(d, 8 * tg, 128)) = o4;
         }
       } else {
         // Q_g^T [k][tok] (column gathers) and K_bwd [tok][k] (row segments)
         for (int e = tid; e < 128 * 8; e += 256) {
-          const int d = e >> 3, tg = e & 7;
+          const int tg = e >> 7, d = e & 127;
           uint4 o4;
           uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
 #pragma unroll
@@ -311,10 +312,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             ow[u] = (uint32_t)f2bf(eg[ta] * bf2f(Qs[ta * KP + d])) |
                     ((uint32_t)f2bf(eg[tb] * bf2f(Qs[tb * KP + d])) << 16);
           }
-          *reinterpret_cast<uint4*>(Qgb + d * 64 + 8 * tg) = o4;
+          *reinterpret_cast<uint4*>(Qgb + kcm(d, 8 * tg, 128)) = o4;
         }
         for (int e = tid; e < 64 * 16; e += 256) {
-          const int t = e >> 4, sg = e & 15;
+          const int sg = e >> 6, t = e & 63;
           const uint4 x = *reinterpret_cast<const uint4*>(&Ks[t * KP + sg * 8]);
           const uint32_t* xw = reinterpret_cast<const uint32_t*>(&x);
           uint4 o4;
@@ -323,31 +324,31 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
           for (int u = 0; u < 4; ++u)
             ow[u] = (uint32_t)f2bf(ebw[t] * bf2f(xw[u] & 0xffffu)) |
                     ((uint32_t)f2bf(ebw[t] * bf2f(xw[u] >> 16)) << 16);
-          *reinterpret_cast<uint4*>(Kbb + t * 128 + sg * 8) = o4;
+          *reinterpret_cast<uint4*>(Kbb + kcm(t, sg * 8, 64)) = o4;
         }
       }
     }
     __syncthreads();
 
-    // T and T^T in bf16 for the backward's gradient pass
+    // T and T^T in bf16 for the backward's gradient pass: chunk (kc, r) of each
+    // holds row r, columns 8 kc .. 8 kc + 7
     if (kBwd) {
       uint16_t* Tg = out.T + blk * 8192;
-      const int i = tid >> 2, j0 = (tid & 3) * 16;
 #pragma unroll
-      for (int hlf = 0; hlf < 2; ++hlf) {
+      for (int i = 0; i < 2; ++i) {
+        const int e = tid + 256 * i;
+        const int kc = e >> 6, r = e & 63;
         uint4 o4, t4;
         uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
         uint32_t* tw4 = reinterpret_cast<uint32_t*>(&t4);
-        const int jj = j0 + 8 * hlf;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          ow[u] = (uint32_t)f2bf(Ts[i * FP + jj + 2 * u]) |
-                  ((uint32_t)f2bf(Ts[i * FP + jj + 2 * u + 1]) << 16);
-          tw4[u] = (uint32_t)f2bf(Ts[(jj + 2 * u) * FP + i]) |
-                   ((uint32_t)f2bf(Ts[(jj + 2 * u + 1) * FP + i]) << 16);
+          const int ja = 8 * kc + 2 * u;
+          ow[u] = (uint32_t)f2bf(Ts[r * FP + ja]) | ((uint32_t)f2bf(Ts[r * FP + ja + 1]) << 16);
+          tw4[u] = (uint32_t)f2bf(Ts[ja * FP + r]) | ((uint32_t)f2bf(Ts[(ja + 1) * FP + r]) << 16);
         }
-        *reinterpret_cast<uint4*>(Tg + i * 64 + jj) = o4;
-        *reinterpret_cast<uint4*>(Tg + 4096 + i * 64 + jj) = t4;
+        *reinterpret_cast<uint4*>(Tg + kcm(r, 8 * kc, 64)) = o4;
+        *reinterpret_cast<uint4*>(Tg + 4096 + kcm(r, 8 * kc, 64)) = t4;
       }
     }
 
@@ -363,7 +364,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
           for (int s = 0; s < 2; ++s)
             acc = mfma(ld8(&Xt[(16 * db + li) * TP + 32 * s + 8 * kq]),
                        cvt8(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq]), acc);
-          *reinterpret_cast<uint2*>(Wb + (16 * tb + li) * 128 + 16 * db + 4 * kq) =
+          *reinterpret_cast<uint2*>(Wb + kcm(16 * tb + li, 16 * db + 4 * kq, 64)) =
               pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
         } else {
           // C = T Xt^T: C[4kq+r][li] = W[t = 16 tb + 4kq + r][k = 16 db + li] -> W^T[k][t..t+3]
@@ -373,7 +374,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
           for (int s = 0; s < 2; ++s)
             acc = mfma(cvt8(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq]),
                        ld8(&Xt[(16 * db + li) * TP + 32 * s + 8 * kq]), acc);
-          *reinterpret_cast<uint2*>(Wb + (16 * db + li) * 64 + 16 * tb + 4 * kq) =
+          *reinterpret_cast<uint2*>(Wb + kcm(16 * db + li, 16 * tb + 4 * kq, 128)) =
               pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
         }
       }
@@ -409,7 +410,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
         for (int s = 0; s < 2; ++s)
           acc = mfma(cvt8(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq]),
                      ld8(&Xt[(16 * vb + li) * TP + 32 * s + 8 * kq]), acc);
-        *reinterpret_cast<uint2*>(Ub + (16 * vb + li) * 64 + 16 * tb + 4 * kq) =
+        *reinterpret_cast<uint2*>(Ub + kcm(16 * vb + li, 16 * tb + 4 * kq, 128)) =
             pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
       }
     }

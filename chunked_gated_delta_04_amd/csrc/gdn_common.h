@@ -22,6 +22,18 @@ constexpr int kChunk = 64;   // tokens per chunk
 constexpr float kNormEps = 1e-6f;
 constexpr int kScanVB = 32;  // value columns per workgroup of the state scans
 
+// Tile layout of every intermediate matrix that a kernel reads as MFMA
+// operands from global memory: an R x C tile (C the contraction axis) is
+// stored as C/8 column chunks, each holding the R rows' 8 consecutive
+// elements (16 bytes) back to back. An operand fragment (16 rows, 8 columns
+// per lane) is then four runs of 256 contiguous bytes, and the stores of an
+// MFMA accumulator tile (4 consecutive contraction indices per lane) fill
+// whole cache lines. Row-major fragments, by contrast, touch 16 half lines
+// per instruction and stream about four times slower through a CU.
+__device__ __host__ __forceinline__ int kcm(int r, int c, int R) {
+  return ((c >> 3) * R + r) * 8 + (c & 7);
+}
+
 // Fourth word of a raw buffer resource on gfx9-family parts (32-bit data
 // format, no swizzle). A raw buffer store whose byte offset lies at or past
 // the resource's record count is discarded by the hardware, which lets a
@@ -163,7 +175,8 @@ __device__ __forceinline__ void invert_unit_lower_64(float* M, float* scratch, i
 }
 
 // Saved-for-backward block of one (chunk, value head): the chunk-start state
-// h = S^T as [k][v] bf16, then the chunk's D as [tok][v] bf16.
+// h = S^T in bf16, value block by value block ([v / 32][k][v % 32]), then the
+// chunk's D [tok][v] in bf16, chunk-major (kcm).
 constexpr int kSavedH = kHead * kHead;
 constexpr int kSavedBlock = kSavedH + kChunk * kHead;
 __device__ __host__ __forceinline__ size_t blk_saved(int c, int hv, int HV) {

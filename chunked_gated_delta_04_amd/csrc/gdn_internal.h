@@ -9,22 +9,23 @@
 namespace gdn {
 
 // Per (value head, chunk) blocks written by the WY pass; block index
-// blk = hv * NC + c, so the chunks of one chain are contiguous.
+// blk = hv * NC + c, so the chunks of one chain are contiguous. Every tile is
+// stored in the chunk-major layout of kcm() with its contraction axis chunked.
 struct PrepOut {
-  uint16_t* W;   // 64 x 128 per block
-  uint16_t* U;   // 128 x 64 per block (forward layout only)
-  uint16_t* Qg;  // 64 x 128
-  uint16_t* P;   // 64 x 64
-  uint16_t* Kb;  // 128 x 64
-  float* gL;     // 1 per block
-  uint16_t* T;   // T then T^T, 2 x 64 x 64 per block (backward layout only)
+  uint16_t* W;   // forward: W [tok][k]; backward: W^T [k][tok]
+  uint16_t* U;   // forward only: U^T [v][tok]
+  uint16_t* Qg;  // forward: Q_g [tok][k]; backward: Q_g^T [k][tok]
+  uint16_t* P;   // forward: P [i][j]; backward: P^T [j][i]
+  uint16_t* Kb;  // forward: K_bwd^T [k][tok]; backward: K_bwd [tok][k]
+  float* gL;     // e^gamma_L, 1 per block
+  uint16_t* T;   // backward only: T [i][j] then T^T [j][i], 2 x 64 x 64 per block
 };
 
 // Backward scratch per (value head, chunk) block, blk = hv * NC + c.
 struct BwdBufs {
-  uint16_t* dh;   // gradient of the chunk's end state, [k][v] (128 x 128)
-  uint16_t* dD;   // dD as [tok][v] (64 x 128)
-  uint16_t* dDT;  // dD as [v][tok] (128 x 64)
+  uint16_t* dh;   // gradient of the chunk's end state, [v / 32][k][v % 32] (128 x 128)
+  uint16_t* dD;   // dD [tok][v], chunk-major (64 x 128)
+  uint16_t* dDT;  // dD^T [v][tok], chunk-major (128 x 64)
 };
 
 hipError_t launch_chunk_table(const int32_t* cu, int N, int T, int NC, ChunkInfo* table,
