@@ -323,60 +323,91 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 
   __shared__ __align__(16) BwdLds S;
 
-  // ---- q, k rows: L2 norm; k^ in both layouts, q~ transposed (8 threads per row)
+  // ---- q, k rows: L2 norm; k^ as rows and transposed, q~ transposed and, for
+  //      the products below, as rows (in Hs, free until the first value head
+  //      stages h). 16 threads per row, so each request covers whole rows.
   {
     const int tid = threadIdx.x;
-    const int r = tid >> 3, sg0 = (tid & 7) * 2;
+    const int sg = tid & 15;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(k) + ((size_t)t0 * H + h) * kHead, 0, L * H * kHead * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rq0 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(q) + ((size_t)t0 * H + h) * kHead, 0, L * H * kHead * 2, kBufferWord3);
     uint4 kr[2], qr[2];
-    float sk = 0.f, sq = 0.f;
+    float sk[2], sq[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      kr[j] = make_uint4(0, 0, 0, 0);
-      qr[j] = make_uint4(0, 0, 0, 0);
-      if (r < L) {
-        const size_t off = ((size_t)(t0 + r) * H + h) * kHead + (sg0 + j) * 8;
-        kr[j] = *reinterpret_cast<const uint4*>(k + off);
-        qr[j] = *reinterpret_cast<const uint4*>(q + off);
-      }
+      const int r = (tid >> 4) + 32 * j;
+      kr[j] = load_b128(rk, (r * H * kHead + sg * 8) * 2);  // rows past the chunk read as 0
+      qr[j] = load_b128(rq0, (r * H * kHead + sg * 8) * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
       const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[j]);
       const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qr[j]);
+      sk[j] = 0.f;
+      sq[j] = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float a0 = bf2f(kw[e] & 0xffffu), a1 = bf2f(kw[e] >> 16);
         const float b0 = bf2f(qw[e] & 0xffffu), b1 = bf2f(qw[e] >> 16);
-        sk += a0 * a0 + a1 * a1;
-        sq += b0 * b0 + b1 * b1;
+        sk[j] += a0 * a0 + a1 * a1;
+        sq[j] += b0 * b0 + b1 * b1;
       }
-    }
-    sk = group_sum<8>(sk);
-    sq = group_sum<8>(sq);
-    const float nk = sqrtf(sk + kNormEps), nq = sqrtf(sq + kNormEps);
-    if ((tid & 7) == 0) {
-      S.nrm_k[r] = nk;
-      S.nrm_q[r] = nq;
+      sk[j] = group_sum<16>(sk[j]);
+      sq[j] = group_sum<16>(sq[j]);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
+      const int r = (tid >> 4) + 32 * j;
+      const float nk = sqrtf(sk[j] + kNormEps), nq = sqrtf(sq[j] + kNormEps);
+      if (sg == 0) {
+        S.nrm_k[r] = nk;
+        S.nrm_q[r] = nq;
+      }
       const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[j]);
       const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qr[j]);
-      uint4 ko;
+      uint4 ko, qo;
       uint32_t* kow = reinterpret_cast<uint32_t*>(&ko);
+      uint32_t* qow = reinterpret_cast<uint32_t*>(&qo);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint16_t k0 = f2bf(bf2f(kw[e] & 0xffffu) / nk), k1 = f2bf(bf2f(kw[e] >> 16) / nk);
         const uint16_t q0 = f2bf((bf2f(qw[e] & 0xffffu) / nq) * scale);
         const uint16_t q1 = f2bf((bf2f(qw[e] >> 16) / nq) * scale);
         kow[e] = (uint32_t)k0 | ((uint32_t)k1 << 16);
-        const int d = (sg0 + j) * 8 + 2 * e;
+        qow[e] = (uint32_t)q0 | ((uint32_t)q1 << 16);
+        const int d = sg * 8 + 2 * e;
         S.KsT[d * TP + r] = k0;
         S.KsT[(d + 1) * TP + r] = k1;
         S.QsT[d * TP + r] = q0;
         S.QsT[(d + 1) * TP + r] = q1;
       }
-      *reinterpret_cast<uint4*>(&S.Ks[r * KP + (sg0 + j) * 8]) = ko;
+      *reinterpret_cast<uint4*>(&S.Ks[r * KP + sg * 8]) = ko;
+      *reinterpret_cast<uint4*>(&S.Hs[r * KP + sg * 8]) = qo;
     }
   }
   __syncthreads();
+
+  // ---- Q~ K^T of the key head, the same for all its value heads, kept in
+  //      registers: qk[q2][r] = (Q~ K^T)[i][j] with i = 16 tw + 4 kq + r,
+  //      j = 16 (kh + 2 q2) + li (tiles with j's block <= i's)
+  f32x4 qk[2];
+  {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tw = wave & 3, kh = wave >> 2, li = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const int jb = kh + 2 * q2;
+      qk[q2] = zero4();
+      if (jb <= tw) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          qk[q2] = mfma(ld8(&S.Hs[(16 * tw + li) * KP + 32 * s + 8 * kq]),
+                        ld8(&S.Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), qk[q2]);
+      }
+    }
+  }
 
   // dq~, dk^ over the value heads: [j][r] = d[16 tw + 4 kq + r][16 (4 kh + j) + li]
   f32x4 adq[4], adk[4];
@@ -408,22 +439,19 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     const uint16_t* dDb = bufs.dD + blk * 8192;          // dD [tok][v], chunk-major
     const uint16_t* dDTb = bufs.dDT + blk * 8192;        // dD^T [v][tok], chunk-major
     const uint16_t* Tg = Tmat + blk * 8192;              // T, then T^T, chunk-major
-    // Token rows of dO, v and q through range-checked buffer loads: rows at or
+    // Token rows of dO and v through range-checked buffer loads: rows at or
     // past the chunk's end read as zeros, with no branch around the load.
     const __amdgpu_buffer_rsrc_t rdO = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(dO) + ((size_t)t0 * HV + hv) * kHead, 0, L * (int)rs * 2, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(v) + ((size_t)t0 * HV + hv) * kHead, 0, L * (int)rs * 2, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(q) + ((size_t)t0 * H + h) * kHead, 0, L * H * kHead * 2, kBufferWord3);
 
     // ---- requests for the dP phase: the own rows of dO and q, the D rows of
     //      this wave's dP tiles
-    bf16x8 oa[4], qa[4], dfr[2][4];
+    bf16x8 oa[4], dfr[2][4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       oa[s] = ld8_buf(rdO, (trow * (int)rs + 32 * s + 8 * kq) * 2);
-      qa[s] = ld8_buf(rq, (trow * H * kHead + 32 * s + 8 * kq) * 2);
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2)
         dfr[q2][s] = ld8(Db + kcm(16 * (kh + 2 * q2) + li, 32 * s + 8 * kq, kChunk));
@@ -466,14 +494,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     // ---- dP = dO D^T (i >= j) and P = Gamma o Q~K^T: Pm = dP o Gamma (+ transpose);
     //      F = dP o P row / column partial sums. Wave: row tile tw, col tiles kh, kh + 2.
     {
-      const float nq = S.nrm_q[trow];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bf16x8 x;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = (__bf16)(((float)qa[s][e] / nq) * scale);
-        qa[s] = x;  // the q~ row exactly as in QsT
-      }
       float rowp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
@@ -481,19 +501,16 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         const int j = 16 * jb + li;
         float pv[4] = {0.f, 0.f, 0.f, 0.f};
         if (jb <= tw) {
-          f32x4 dp = zero4(), qk = zero4();
+          f32x4 dp = zero4();
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            dp = mfma(oa[s], dfr[q2][s], dp);
-            qk = mfma(qa[s], ld8(&S.Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), qk);
-          }
+          for (int s = 0; s < 4; ++s) dp = mfma(oa[s], dfr[q2][s], dp);
           float colp = 0.f;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 16 * tw + 4 * kq + r;
             if (i >= j) {
               const float dpm = dp[r] * expf(S.gam[i] - S.gam[j]);
-              const float f = dpm * qk[r];
+              const float f = dpm * qk[q2][r];
               pv[r] = dpm;
               rowp[r] += f;
               colp += f;
