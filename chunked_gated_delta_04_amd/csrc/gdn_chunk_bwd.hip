@@ -409,6 +409,41 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     }
   }
 
+  // Gate gradients of value head hv_ (wave 0): fixed-order sums of the partial
+  // slots, then dg = reverse cumsum of dgamma inside the chunk. Run by wave 0
+  // at the top of the next value head (or after the last one): the slots and
+  // gamma are rewritten only after the next gate barrier, which wave 0 reaches
+  // after this, and the work overlaps the other waves' requests.
+  auto dg_out = [&](int hv_) {
+    const int t = threadIdx.x & 63;
+    const int w0 = 4 * ((t >> 4) & 1);  // the waves whose column tiles hold t
+    float dgm = (S.rowF[0][t] + S.rowF[1][t]) + (S.rowG[0][t] + S.rowG[1][t]) +
+                (S.rowE[0][t] + S.rowE[1][t]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) dgm -= S.colF[w0 + w][t] + S.colE[w0 + w][t];
+    const float dbt = (S.rowB[0][t] + S.rowB[1][t]) + (S.rowB2[0][t] + S.rowB2[1][t]) +
+                      (S.rowB3[0][t] + S.rowB3[1][t]);
+    float x = t < L ? dgm : 0.f;
+    if (t == L - 1) {
+      float glsum = 0.f, hdsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        glsum += S.gl_part[w];
+        hdsum += S.hd_part[w];
+      }
+      x += glsum + expf(S.gam[L - 1]) * hdsum;
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_down(x, off, 64);
+      if (t + off < 64) x += y;
+    }
+    if (t < L) {
+      dg[(size_t)(t0 + t) * HV + hv_] = x;
+      dbeta[(size_t)(t0 + t) * HV + hv_] = dbt;
+    }
+  };
+
   // dq~, dk^ over the value heads: [j][r] = d[16 tw + 4 kq + r][16 (4 kh + j) + li]
   f32x4 adq[4], adk[4];
 #pragma unroll
@@ -470,8 +505,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       vr[j] = load_b64(rv, (trow * (int)rs + 16 * vt + 4 * kq) * 2);
     }
 
-    // ---- gates
+    // ---- gates (wave 0, after the previous value head's gate gradients)
     if (wave == 0) {
+      if (jg > 0) dg_out(hv - 1);
       float gv = lane < L ? g[(size_t)(t0 + lane) * HV + hv] : 0.f;
       const float bv = lane < L ? beta[(size_t)(t0 + lane) * HV + hv] : 0.f;
 #pragma unroll
@@ -484,10 +520,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       const float gl = __shfl(gv, L - 1, 64);
       S.eg[lane] = expf(gv);
       S.ebw[lane] = lane < L ? expf(gl - gv) : 0.f;
-    }
-    for (int e = tid; e < 8 * 64; e += 512) {
-      (&S.colF[0][0])[e] = 0.f;
-      (&S.colE[0][0])[e] = 0.f;
     }
     __syncthreads();
 
@@ -519,6 +551,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
           colp += __shfl_xor(colp, 16, 64);
           colp += __shfl_xor(colp, 32, 64);
           if (kq == 0) S.colF[wave][j] = colp;
+        } else if (kq == 0) {
+          S.colF[wave][j] = 0.f;  // every slot of the wave's column tiles is written
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) S.Pm[(16 * tw + 4 * kq + r) * BP + j] = f2bf(pv[r]);
@@ -838,6 +872,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
           colp += __shfl_xor(colp, 16, 64);
           colp += __shfl_xor(colp, 32, 64);
           if (kq == 0) S.colE[wave][j] = colp;
+        } else if (kq == 0) {
+          S.colE[wave][j] = 0.f;
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) S.Pm[(16 * tw + 4 * kq + r) * BP + j] = f2bf(mv[r]);
@@ -858,37 +894,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       }
     }
     __syncthreads();
-
-    // ---- gate gradients of this value head: fixed-order sums of the partial slots,
-    //      then dg = reverse cumsum of dgamma inside the chunk
-    if (wave == 0) {
-      const int t = lane;
-      float dgm = (S.rowF[0][t] + S.rowF[1][t]) + (S.rowG[0][t] + S.rowG[1][t]) +
-                  (S.rowE[0][t] + S.rowE[1][t]);
-#pragma unroll
-      for (int w = 0; w < 8; ++w) dgm -= S.colF[w][t] + S.colE[w][t];
-      const float dbt = (S.rowB[0][t] + S.rowB[1][t]) + (S.rowB2[0][t] + S.rowB2[1][t]) +
-                        (S.rowB3[0][t] + S.rowB3[1][t]);
-      float x = t < L ? dgm : 0.f;
-      if (t == L - 1) {
-        float glsum = 0.f, hdsum = 0.f;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          glsum += S.gl_part[w];
-          hdsum += S.hd_part[w];
-        }
-        x += glsum + expf(S.gam[L - 1]) * hdsum;
-      }
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_down(x, off, 64);
-        if (lane + off < 64) x += y;
-      }
-      if (t < L) {
-        dg[(size_t)(t0 + t) * HV + hv] = x;
-        dbeta[(size_t)(t0 + t) * HV + hv] = dbt;
-      }
-    }
 
     // ---- dk^ += M K^ + M^T K^
     {
@@ -913,6 +918,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     }
     __syncthreads();  // everything is rewritten by the next value head
   }
+
+  if ((threadIdx.x >> 6) == 0) dg_out(h * G + G - 1);
 
   // ---- L2-norm backward and scale: x^ . dx^ over all 128 columns (two halves)
   {
