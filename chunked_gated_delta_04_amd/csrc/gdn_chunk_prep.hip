@@ -155,10 +155,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
       uint32_t* qow = reinterpret_cast<uint32_t*>(&qo);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        kow[e] = (uint32_t)f2bf(bf2f(kw[e] & 0xffffu) / nk) |
-                 ((uint32_t)f2bf(bf2f(kw[e] >> 16) / nk) << 16);
-        qow[e] = (uint32_t)f2bf((bf2f(qw[e] & 0xffffu) / nq) * scale) |
-                 ((uint32_t)f2bf((bf2f(qw[e] >> 16) / nq) * scale) << 16);
+        kow[e] = pk2(bf2f(kw[e] & 0xffffu) / nk, bf2f(kw[e] >> 16) / nk);
+        qow[e] = pk2((bf2f(qw[e] & 0xffffu) / nq) * scale, (bf2f(qw[e] >> 16) / nq) * scale);
       }
       *reinterpret_cast<uint4*>(&Ks[r * KP + (sg0 + j) * 8]) = ko;
       *reinterpret_cast<uint4*>(&Qs[r * KP + (sg0 + j) * 8]) = qo;
@@ -265,8 +263,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int ta = 8 * tg + 2 * u, tb = ta + 1;
-        ow[u] = (uint32_t)f2bf(bet[ta] * eg[ta] * bf2f(Ks[ta * KP + d])) |
-                ((uint32_t)f2bf(bet[tb] * eg[tb] * bf2f(Ks[tb * KP + d])) << 16);
+        ow[u] = pk2(bet[ta] * eg[ta] * bf2f(Ks[ta * KP + d]), bet[tb] * eg[tb] * bf2f(Ks[tb * KP + d]));
       }
       *reinterpret_cast<uint4*>(&Xt[d * TP + 8 * tg]) = o4;
     }
@@ -284,8 +281,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
           uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            ow[u] = (uint32_t)f2bf(eg[t] * bf2f(xw[u] & 0xffffu)) |
-                    ((uint32_t)f2bf(eg[t] * bf2f(xw[u] >> 16)) << 16);
+            ow[u] = pk2(eg[t] * bf2f(xw[u] & 0xffffu), eg[t] * bf2f(xw[u] >> 16));
           *reinterpret_cast<uint4*>(Qgb + kcm(t, sg * 8, 64)) = o4;
         }
         for (int e = tid; e < 128 * 8; e += 256) {
@@ -295,8 +291,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int ta = 8 * tg + 2 * u, tb = ta + 1;
-            ow[u] = (uint32_t)f2bf(ebw[ta] * bf2f(Ks[ta * KP + d])) |
-                    ((uint32_t)f2bf(ebw[tb] * bf2f(Ks[tb * KP + d])) << 16);
+            ow[u] = pk2(ebw[ta] * bf2f(Ks[ta * KP + d]), ebw[tb] * bf2f(Ks[tb * KP + d]));
           }
           *reinterpret_cast<uint4*>(Kbb + kcm(d, 8 * tg, 128)) = o4;
         }
@@ -309,8 +304,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int ta = 8 * tg + 2 * u, tb = ta + 1;
-            ow[u] = (uint32_t)f2bf(eg[ta] * bf2f(Qs[ta * KP + d])) |
-                    ((uint32_t)f2bf(eg[tb] * bf2f(Qs[tb * KP + d])) << 16);
+            ow[u] = pk2(eg[ta] * bf2f(Qs[ta * KP + d]), eg[tb] * bf2f(Qs[tb * KP + d]));
           }
           *reinterpret_cast<uint4*>(Qgb + kcm(d, 8 * tg, 128)) = o4;
         }
@@ -322,8 +316,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
           uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            ow[u] = (uint32_t)f2bf(ebw[t] * bf2f(xw[u] & 0xffffu)) |
-                    ((uint32_t)f2bf(ebw[t] * bf2f(xw[u] >> 16)) << 16);
+            ow[u] = pk2(ebw[t] * bf2f(xw[u] & 0xffffu), ebw[t] * bf2f(xw[u] >> 16));
           *reinterpret_cast<uint4*>(Kbb + kcm(t, sg * 8, 64)) = o4;
         }
       }
@@ -344,8 +337,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int ja = 8 * kc + 2 * u;
-          ow[u] = (uint32_t)f2bf(Ts[r * FP + ja]) | ((uint32_t)f2bf(Ts[r * FP + ja + 1]) << 16);
-          tw4[u] = (uint32_t)f2bf(Ts[ja * FP + r]) | ((uint32_t)f2bf(Ts[(ja + 1) * FP + r]) << 16);
+          ow[u] = pk2(Ts[r * FP + ja], Ts[r * FP + ja + 1]);
+          tw4[u] = pk2(Ts[ja * FP + r], Ts[(ja + 1) * FP + r]);
         }
         *reinterpret_cast<uint4*>(Tg + kcm(r, 8 * kc, 64)) = o4;
         *reinterpret_cast<uint4*>(Tg + 4096 + kcm(r, 8 * kc, 64)) = t4;

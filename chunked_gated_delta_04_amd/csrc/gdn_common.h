@@ -67,11 +67,16 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Two fp32 -> two bf16 (round to nearest even) in one 32-bit word, a in the
+// low half; one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pk2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
 __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
-  uint2 r;
-  r.x = (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
-  r.y = (uint32_t)f2bf(c) | ((uint32_t)f2bf(d) << 16);
-  return r;
+  return make_uint2(pk2(a, b), pk2(c, d));
 }
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -84,12 +89,9 @@ __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
 
 // 8 fp32 from LDS/global -> bf16x8 (round to nearest even)
 __device__ __forceinline__ bf16x8 cvt8(const float* p) {
-  float4 a = *reinterpret_cast<const float4*>(p);
-  float4 b = *reinterpret_cast<const float4*>(p + 4);
-  bf16x8 r;
-  r[0] = (__bf16)a.x; r[1] = (__bf16)a.y; r[2] = (__bf16)a.z; r[3] = (__bf16)a.w;
-  r[4] = (__bf16)b.x; r[5] = (__bf16)b.y; r[6] = (__bf16)b.z; r[7] = (__bf16)b.w;
-  return r;
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  return __builtin_bit_cast(bf16x8, make_uint4(pk2(a.x, a.y), pk2(a.z, a.w), pk2(b.x, b.y), pk2(b.z, b.w)));
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
