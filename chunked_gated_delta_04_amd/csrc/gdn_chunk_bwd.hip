@@ -153,15 +153,15 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
       for (int u = 0; u < 8; ++u) Os[(8 * osg + u) * DP + ot] = xs[u];
     }
     __syncthreads();
-    // dh' (gradient of this chunk's end state), value block by value block:
-    // [v / 32][k][v % 32]; two 16-byte stores per thread
+    // dh' (gradient of this chunk's end state) as [v / 32][v % 32 / 8][k][v % 8],
+    // read as columns of Hs with transposed reads (chunk e = 64 q + lane)
     {
       uint16_t* dhb = bufs.dh + blk * (kHead * kHead) + vb * (kHead * VB);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int e = tid + 256 * i;
-        const int kk = e >> 2, vg = e & 3;
-        *reinterpret_cast<uint4*>(dhb + 8 * e) = gather8(&Hs[(8 * vg) * SP + kk], SP);
+        const int q = wave + 4 * i;
+        *reinterpret_cast<uint4*>(dhb + 8 * (64 * q + lane)) =
+            lds_col8(Hs, SP, 8 * (q >> 1), 64 * (q & 1) + 16 * kq, lane);
       }
     }
 
@@ -194,8 +194,8 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
       const int sg = tid >> 5, vl = tid & 31;
       *reinterpret_cast<uint4*>(dDT + kcm(v0 + vl, 8 * sg, kHead)) =
           *reinterpret_cast<const uint4*>(&Es[vl * DP + 8 * sg]);
-      const int vg = tid >> 6, t = tid & 63;
-      *reinterpret_cast<uint4*>(dDr + kcm(t, v0 + 8 * vg, kChunk)) = gather8(&Es[(8 * vg) * DP + t], DP);
+      *reinterpret_cast<uint4*>(dDr + kcm(lane, v0 + 8 * wave, kChunk)) =
+          lds_col8(Es, DP, 8 * wave, 16 * kq, lane);
     }
 
     // 3. dh <- e^gamma_L dh + Q_g^T dO - W^T dD; wave w owns key rows 32 w .. 32 w + 31
@@ -291,10 +291,10 @@ __device__ __forceinline__ float4 ld4_bf16(const uint16_t* p) {  // 4 bf16 -> fp
   const uint2 u = *reinterpret_cast<const uint2*>(p);
   return make_float4(bf2f(u.x & 0xffffu), bf2f(u.x >> 16), bf2f(u.y & 0xffffu), bf2f(u.y >> 16));
 }
-// LDS position (pitch KP, [k][v]) of 16-byte chunk e of a state stored value
-// block by value block, [v / 32][k][v % 32]
+// LDS position (pitch KP, [k][v]) of 16-byte chunk e of a state stored as
+// [v / 32][v % 32 / 8][k][v % 8]
 __device__ __forceinline__ int state_pos(int e) {
-  const int vb = e >> 9, kk = (e >> 2) & 127, vg = e & 3;
+  const int vb = e >> 9, vg = (e >> 7) & 3, kk = e & 127;
   return kk * KP + vb * kScanVB + vg * 8;
 }
 __device__ __forceinline__ float dot8u(const uint4& a, const uint4& b) {  // bf16 pairs
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     const bool trow_ok = trow < L;
     const int hv = h * G + jg;
     const size_t blk = (size_t)hv * NC + c;
-    // (chunk-major tiles: see kcm; states: [v / 32][k][v % 32])
+    // (chunk-major tiles: see kcm; states: [v / 32][v % 32 / 8][k][v % 8])
     const uint16_t* hb = saved + blk_saved(c, hv, HV);  // h
     const uint16_t* Db = hb + kSavedH;                   // D [tok][v], chunk-major
     const uint16_t* dhb = bufs.dh + blk * (kHead * kHead);  // dh'

@@ -127,13 +127,14 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     __syncthreads();
     uint16_t* sv = saved + blk_saved(c, hv, HV);
     if constexpr (kSave) {
-      // h = S^T, value block by value block: [v / 32][k][v % 32] (16-byte
-      // column gathers of Ss; consecutive threads write consecutive chunks)
+      // h = S^T as [v / 32][v % 32 / 8][k][v % 8]: chunk e = 64 q + lane holds
+      // h[k = e % 128][8 (e / 128) ..], read as columns of Ss with transposed
+      // reads; consecutive lanes write consecutive chunks
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int e = tid + 256 * i;
-        const int kk = e >> 2, vg = e & 3;
-        *reinterpret_cast<uint4*>(sv + vb * (kHead * VB) + 8 * e) = gather8(&Ss[(8 * vg) * SP + kk], SP);
+        const int q = wave + 4 * i;
+        const uint4 x = lds_col8(Ss, SP, 8 * (q >> 1), 64 * (q & 1) + 16 * kq, lane);
+        *reinterpret_cast<uint4*>(sv + vb * (kHead * VB) + 8 * (64 * q + lane)) = x;
       }
     }
 
@@ -157,10 +158,10 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     }
     __syncthreads();
     if constexpr (kSave) {
-      // D [tok][v] in the chunk-major tile layout: one 16-byte store per thread
-      const int vg = tid >> 6, t = tid & 63;
-      *reinterpret_cast<uint4*>(sv + kSavedH + kcm(t, v0 + 8 * vg, kChunk)) =
-          gather8(&Ds[(8 * vg) * DP + t], DP);
+      // D [tok][v] in the chunk-major tile layout: wave w writes the chunks of
+      // value columns v0 + 8 w .. + 7, lane = token, read as columns of D^T
+      *reinterpret_cast<uint4*>(sv + kSavedH + kcm(lane, v0 + 8 * wave, kChunk)) =
+          lds_col8(Ds, DP, 8 * wave, 16 * kq, lane);
     }
 
     // 3. O^T = S Q_g^T + D^T P^T; wave w owns tokens 16 w .. 16 w + 15. Rows at

@@ -96,28 +96,27 @@ __device__ __forceinline__ bf16x8 cvt8(const float* p) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// 8 bf16 spaced `pitch` elements apart (a column of a row-major tile), packed
-// into 16 bytes.
-__device__ __forceinline__ uint4 gather8(const uint16_t* p, int pitch) {
-  uint4 r;
-  r.x = (uint32_t)p[0] | ((uint32_t)p[pitch] << 16);
-  r.y = (uint32_t)p[2 * pitch] | ((uint32_t)p[3 * pitch] << 16);
-  r.z = (uint32_t)p[4 * pitch] | ((uint32_t)p[5 * pitch] << 16);
-  r.w = (uint32_t)p[6 * pitch] | ((uint32_t)p[7 * pitch] << 16);
-  return r;
+// LDS transpose read (ds_read_b64_tr_b16, gfx950). Within each group of 16
+// lanes, lane j supplies the address of 4 consecutive 16-bit elements; lane i
+// of the group receives element i % 4 of lanes i / 4, 4 + i / 4, 8 + i / 4
+// and 12 + i / 4. When lanes 4 e .. 4 e + 3 read row e of a row-major tile in
+// four 4-element pieces, lane i therefore receives column i of those 4 rows.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(p));
+  return __builtin_bit_cast(uint2, r);
 }
 
-__device__ __forceinline__ bf16x8 gather8_bf16(const uint16_t* p, int pitch) {
-  const uint4 r = gather8(p, pitch);
-  return __builtin_bit_cast(bf16x8, r);
-}
-
-// 8 fp32 spaced `pitch` apart -> bf16x8
-__device__ __forceinline__ bf16x8 gather8_f32(const float* p, int pitch) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (__bf16)p[e * pitch];
-  return r;
+// Column c0 + (lane % 16) of rows r0 .. r0 + 7 of a row-major bf16 LDS tile
+// (pitch in elements, a multiple of 4; c0 a multiple of 16), as 16 bytes:
+// two transpose reads, each lane group of the wave taking its own r0, c0.
+__device__ __forceinline__ uint4 lds_col8(const uint16_t* tile, int pitch, int r0, int c0,
+                                          int lane) {
+  const int j = lane & 15;
+  const uint2 a = lds_tr16(tile + (r0 + (j >> 2)) * pitch + c0 + 4 * (j & 3));
+  const uint2 b = lds_tr16(tile + (r0 + 4 + (j >> 2)) * pitch + c0 + 4 * (j & 3));
+  return make_uint4(a.x, a.y, b.x, b.y);
 }
 
 // In-place inverse of I + A for a strictly lower-triangular 64 x 64 fp32 matrix A
@@ -177,8 +176,9 @@ __device__ __forceinline__ void invert_unit_lower_64(float* M, float* scratch, i
 }
 
 // Saved-for-backward block of one (chunk, value head): the chunk-start state
-// h = S^T in bf16, value block by value block ([v / 32][k][v % 32]), then the
-// chunk's D [tok][v] in bf16, chunk-major (kcm).
+// h = S^T in bf16 as [v / 32][v % 32 / 8][k][v % 8] (each scan workgroup
+// writes one contiguous 8 KiB piece), then the chunk's D [tok][v] in bf16,
+// chunk-major (kcm).
 constexpr int kSavedH = kHead * kHead;
 constexpr int kSavedBlock = kSavedH + kChunk * kHead;
 __device__ __host__ __forceinline__ size_t blk_saved(int c, int hv, int HV) {

@@ -23,7 +23,7 @@ struct PrepOut {
 
 // Backward scratch per (value head, chunk) block, blk = hv * NC + c.
 struct BwdBufs {
-  uint16_t* dh;   // gradient of the chunk's end state, [v / 32][k][v % 32] (128 x 128)
+  uint16_t* dh;   // gradient of the chunk's end state, [v / 32][v % 32 / 8][k][v % 8]
   uint16_t* dD;   // dD [tok][v], chunk-major (64 x 128)
   uint16_t* dDT;  // dD^T [v][tok], chunk-major (128 x 64)
 };
