@@ -75,7 +75,8 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
   const int li = lane & 15, kq = lane >> 4;
 
   __shared__ __align__(16) uint16_t Hs[VB * SP];  // dh as [v][k]
-  __shared__ __align__(16) uint16_t Os[VB * DP];  // dO^T [v][tok]
+  constexpr int OP = 40;  // LDS pitch of the dO rows (bf16)
+  __shared__ __align__(16) uint16_t Ot[kChunk * OP];  // dO [tok][v - v0]
   __shared__ __align__(16) uint16_t Es[VB * DP];  // dD^T [v][tok]
 
   f32x4 dh[2][VT];
@@ -147,11 +148,7 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
         *reinterpret_cast<uint2*>(&Hs[(16 * vt + li) * SP + kk]) =
             pack4_bf16(dh[dt][vt][0], dh[dt][vt][1], dh[dt][vt][2], dh[dt][vt][3]);
       }
-    {
-      const uint16_t* xs = reinterpret_cast<const uint16_t*>(&cur.dO);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) Os[(8 * osg + u) * DP + ot] = xs[u];
-    }
+    *reinterpret_cast<uint4*>(&Ot[ot * OP + 8 * osg]) = cur.dO;
     __syncthreads();
     // dh' (gradient of this chunk's end state) as [v / 32][v % 32 / 8][k][v % 8],
     // read as columns of Hs with transposed reads (chunk e = 64 q + lane)
@@ -165,12 +162,19 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
       }
     }
 
+    // dO as operand fragments (contraction over tokens), read as columns of
+    // the dO rows: ob[vt][s] = dO[32 s + 8 kq .. + 7][16 vt + li]
+    bf16x8 ob[VT][2];
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        ob[vt][s] = __builtin_bit_cast(bf16x8, lds_col8(Ot, OP, 32 * s + 8 * kq, 16 * vt, lane));
+
     // 2. dD = P^T dO + K_bwd dh; wave w owns tokens 16 w .. 16 w + 15
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt) {
-      bf16x8 ob[2], hb4[4];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) ob[s] = ld8(&Os[(16 * vt + li) * DP + 32 * s + 8 * kq]);
+      bf16x8 hb4[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) hb4[s] = ld8(&Hs[(16 * vt + li) * SP + 32 * s + 8 * kq]);
       // two independent partial sums, so the MFMAs do not wait on each other
@@ -178,8 +182,8 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
       f32x4 a1 = mfma(cur.ka[1], hb4[1], zero4());
       a0 = mfma(cur.ka[2], hb4[2], a0);
       a1 = mfma(cur.ka[3], hb4[3], a1);
-      a1 = mfma(cur.pa[1], ob[1], a1);
-      if (wave < 2) a0 = mfma(cur.pa[0], ob[0], a0);
+      a1 = mfma(cur.pa[1], ob[vt][1], a1);
+      if (wave < 2) a0 = mfma(cur.pa[0], ob[vt][0], a0);
       const f32x4 acc = a0 + a1;
       // acc[r] = dD[t = 16 w + 4 kq + r][v = 16 vt + li]
       *reinterpret_cast<uint2*>(&Es[(16 * vt + li) * DP + 16 * wave + 4 * kq]) =
@@ -207,7 +211,7 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
         f32x4 acw = zero4();
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          acc = mfma(cur.qa[dt][s], ld8(&Os[(16 * vt + li) * DP + 32 * s + 8 * kq]), acc);
+          acc = mfma(cur.qa[dt][s], ob[vt][s], acc);
           acw = mfma(cur.wa[dt][s], ld8(&Es[(16 * vt + li) * DP + 32 * s + 8 * kq]), acw);
         }
         dh[dt][vt] = acc - acw;
