@@ -171,8 +171,8 @@ def time_call(h, stream, fn, steps, warmup):
 
 
 def secondary(h, stream, steps, warmup):
-    """Forward-only throughput on the 4 x 4096 and the 12-sequence varlen packs, and
-    the decode step against the HBM roofline."""
+    """Forward-only throughput on the 4 x 4096 and the 12-sequence varlen packs, the
+    decode step against the HBM roofline, and the paged prefill."""
     import torch
     from chunked_gated_delta_04_amd import gdn, synth
     out = {}
@@ -212,7 +212,46 @@ def secondary(h, stream, steps, warmup):
     out[name] = {"ms": round(ms, 4), "rows_per_s": round(N / (ms * 1e-3), 1),
                  "algorithmic_bytes": bytes_, "achieved_GBps": round(gbs, 1),
                  "hbm_frac": round(gbs * 1e9 / PEAK_HBM, 4)}
+    out.update(paged_prefill(h, stream, steps, warmup))
     return out
+
+
+def paged_prefill(h, stream, steps, warmup):
+    """The paged prefill (8 x 512 tokens, 8 key / 16 value heads, 64-slot pool,
+    half the sequences fresh) in place on the pool, next to the same forward
+    with the start states gathered from the pool and the end states scattered
+    back by torch index copies."""
+    import torch
+    from chunked_gated_delta_04_amd import gdn, synth
+    name = "paged_8x512_h8_hv16_pool64"
+    inp = synth.workload_inputs(name)
+    d = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor)}
+    T, H, _ = inp["q"].shape
+    HV = inp["v"].shape[1]
+    N = inp["cu_seqlens"].numel() - 1
+    p = gdn.make_problem(N, T, H, HV, d["cu_seqlens"], inp["cu_seqlens"])
+    o = torch.empty(T, HV, 128, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(p), dtype=torch.uint8, device="cuda")
+    pool = d["state_pool"]
+    slots = pool.shape[0]
+    idx_l = d["ssm_state_indices"].long()
+    keep = d["has_initial_state"].float()[:, None, None, None]
+    h0 = torch.empty(N, HV, 128, 128, dtype=torch.float32, device="cuda")
+    hT = torch.empty_like(h0)
+    ms_paged = time_call(h, stream, lambda: gdn.gdn_chunk_fwd_paged(
+        p, d["q"], d["k"], d["v"], d["g"], d["beta"], pool, slots, d["ssm_state_indices"],
+        d["has_initial_state"], None, o, None, ws, stream), steps, warmup)
+
+    def copies():
+        torch.index_select(pool, 0, idx_l, out=h0)
+        h0.mul_(keep)
+        gdn.gdn_chunk_fwd(p, d["q"], d["k"], d["v"], d["g"], d["beta"], h0, o, hT, None, ws,
+                          stream)
+        pool.index_copy_(0, idx_l, hT)
+    with torch.cuda.stream(stream):
+        ms_copies = time_call(h, stream, copies, steps, warmup)
+    return {name: {"ms": round(ms_paged, 4), "tokens_per_s": round(T / (ms_paged * 1e-3), 1),
+                   "gather_scatter_ms": round(ms_copies, 4)}}
 
 
 def main():

@@ -62,7 +62,7 @@ gdn_status check_problem(const gdn_problem* p, int64_t* nc) {
   const int64_t c = chunk_slots(p);
   if (c > (int64_t)INT32_MAX / 2 || (int64_t)p->N * p->HV > (int64_t)INT32_MAX / 64)
     return GDN_ERR_SHAPE;
-  *nc = c;
+  if (nc) *nc = c;
   return GDN_OK;
 }
 
@@ -100,6 +100,23 @@ PrepOut prep_views(char* ws, const Layout& L, bool bwd) {
 
 float effective_scale(const gdn_problem* p) {
   return p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->K);
+}
+
+// Host copy of state-pool indices: every index in (0, slots) is active and
+// must be distinct; an index >= slots is an error; <= 0 means "no slot".
+gdn_status check_indices_host(int N, int slots, const int32_t* indices_host) {
+  if (!indices_host) return GDN_OK;
+  std::vector<int32_t> act;
+  act.reserve(N);
+  for (int n = 0; n < N; ++n) {
+    const int32_t x = indices_host[n];
+    if (x <= 0) continue;  // null block or negative: skipped, never an error
+    if (x >= slots) return GDN_ERR_INDEX;
+    act.push_back(x);
+  }
+  std::sort(act.begin(), act.end());
+  if (std::adjacent_find(act.begin(), act.end()) != act.end()) return GDN_ERR_INDEX;
+  return GDN_OK;
 }
 
 #define GDN_TRY(expr)                              \
@@ -166,25 +183,27 @@ struct StageClock {
 };
 
 static int chunk_fwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_t* k,
-                          const uint16_t* v, const float* g, const float* beta, const float* h0,
-                          uint16_t* o, float* hT, uint16_t* saved, void* workspace,
-                          size_t workspace_bytes, void* stream, void* const* events,
-                          int* n_stages) {
+                          const uint16_t* v, const float* g, const float* beta,
+                          const StateRef& sr, bool paged, uint16_t* o, uint16_t* saved,
+                          void* workspace, size_t workspace_bytes, void* stream,
+                          void* const* events, int* n_stages) {
   if (n_stages) *n_stages = 0;
   int64_t NC = 0;
   gdn_status st = check_problem(p, &NC);
   if (st != GDN_OK) return st;
   if (p->T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(h0) ||
-      !aligned16(hT) || !aligned16(saved) || !aligned16(workspace))
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(sr.h0) ||
+      !aligned16(sr.hT) || !aligned16(saved) || !aligned16(workspace))
     return GDN_ERR_ALIGN;
   const Layout L = make_layout(p, NC, false);
   if (!workspace || workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   StageClock clk{events, 0, s};
-  if (p->T == 0) {  // no tokens: the state passes through
-    if (hT)
-      GDN_TRY(clk.run([&] { return launch_state_copy(h0, hT, (size_t)p->N * p->HV * kState, s); }));
+  if (p->T == 0 && !paged) {  // no tokens: the state passes through
+    if (sr.hT)
+      GDN_TRY(clk.run([&] {
+        return launch_state_copy(sr.h0, sr.hT, (size_t)p->N * p->HV * kState, s);
+      }));
     if (n_stages) *n_stages = clk.n;
     return GDN_OK;
   }
@@ -195,12 +214,13 @@ static int chunk_fwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_
   GDN_TRY(clk.run([&] {
     return launch_chunk_table(p->cu_seqlens, p->N, p->T, (int)NC, table, seq_first, s);
   }));
+  if (NC > 0)
+    GDN_TRY(clk.run([&] {
+      return launch_chunk_prep(false, table, (int)NC, p->H, p->HV, effective_scale(p), q, k, v, g,
+                               beta, prep, s);
+    }));
   GDN_TRY(clk.run([&] {
-    return launch_chunk_prep(false, table, (int)NC, p->H, p->HV, effective_scale(p), q, k, v, g,
-                             beta, prep, s);
-  }));
-  GDN_TRY(clk.run([&] {
-    return launch_fwd_scan(seq_first, p->N, p->HV, (int)NC, table, prep, h0, o, hT, saved, s);
+    return launch_fwd_scan(seq_first, p->N, p->HV, (int)NC, table, prep, sr, o, saved, s);
   }));
   if (n_stages) *n_stages = clk.n;
   return GDN_OK;
@@ -210,8 +230,26 @@ GDN_API int gdn_chunk_fwd(const gdn_problem* p, const uint16_t* q, const uint16_
                           const uint16_t* v, const float* g, const float* beta, const float* h0,
                           uint16_t* o, float* hT, uint16_t* saved, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  return chunk_fwd_impl(p, q, k, v, g, beta, h0, o, hT, saved, workspace, workspace_bytes, stream,
-                        nullptr, nullptr);
+  const StateRef sr{h0, hT, nullptr, nullptr, 0};
+  return chunk_fwd_impl(p, q, k, v, g, beta, sr, false, o, saved, workspace, workspace_bytes,
+                        stream, nullptr, nullptr);
+}
+
+GDN_API int gdn_chunk_fwd_paged(const gdn_problem* p, const uint16_t* q, const uint16_t* k,
+                                const uint16_t* v, const float* g, const float* beta,
+                                float* state_pool, int32_t slots,
+                                const int32_t* ssm_state_indices,
+                                const int32_t* has_initial_state, const int32_t* indices_host,
+                                uint16_t* o, uint16_t* saved, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  const gdn_status ps = check_problem(p, nullptr);
+  if (ps != GDN_OK) return ps;
+  if (slots < 0) return GDN_ERR_SHAPE;
+  if (p->N > 0 && (!state_pool || !ssm_state_indices)) return GDN_ERR_NULL;
+  if (check_indices_host(p->N, slots, indices_host) != GDN_OK) return GDN_ERR_INDEX;
+  const StateRef sr{state_pool, state_pool, ssm_state_indices, has_initial_state, slots};
+  return chunk_fwd_impl(p, q, k, v, g, beta, sr, true, o, saved, workspace, workspace_bytes,
+                        stream, nullptr, nullptr);
 }
 
 GDN_API int gdn_chunk_fwd_timed(const gdn_problem* p, const uint16_t* q, const uint16_t* k,
@@ -220,8 +258,9 @@ GDN_API int gdn_chunk_fwd_timed(const gdn_problem* p, const uint16_t* q, const u
                                 void* workspace, size_t workspace_bytes, void* stream,
                                 void* const* events, int* n_stages) {
   if (!events || !n_stages) return GDN_ERR_NULL;
-  return chunk_fwd_impl(p, q, k, v, g, beta, h0, o, hT, saved, workspace, workspace_bytes, stream,
-                        events, n_stages);
+  const StateRef sr{h0, hT, nullptr, nullptr, 0};
+  return chunk_fwd_impl(p, q, k, v, g, beta, sr, false, o, saved, workspace, workspace_bytes,
+                        stream, events, n_stages);
 }
 
 static int chunk_bwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_t* k,
@@ -320,18 +359,7 @@ GDN_API int gdn_recurrent_step(int32_t N, int32_t H, int32_t HV, int32_t K, int3
     return GDN_ERR_NULL;
   if (!aligned16(state_pool) || !aligned16(o) || ((uintptr_t)q & 3u) || ((uintptr_t)k & 3u))
     return GDN_ERR_ALIGN;
-  if (indices_host) {
-    std::vector<int32_t> act;
-    act.reserve(N);
-    for (int n = 0; n < N; ++n) {
-      const int32_t x = indices_host[n];
-      if (x <= 0) continue;  // null block or negative: skipped, never an error
-      if (x >= slots) return GDN_ERR_INDEX;
-      act.push_back(x);
-    }
-    std::sort(act.begin(), act.end());
-    if (std::adjacent_find(act.begin(), act.end()) != act.end()) return GDN_ERR_INDEX;
-  }
+  if (check_indices_host(N, slots, indices_host) != GDN_OK) return GDN_ERR_INDEX;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)K);
   if (launch_decode_step(N, H, HV, sc, q, k, v, a, b, A_log, dt_bias, state_pool, slots,
                          ssm_state_indices, o, reinterpret_cast<hipStream_t>(stream)) !=

@@ -27,8 +27,8 @@ namespace gdn {
 template <bool kSave>
 __global__ __launch_bounds__(256) void fwd_scan_kernel(
     const int32_t* __restrict__ seq_first, int N, int HV, int NC,
-    const ChunkInfo* __restrict__ table, PrepOut prep, const float* __restrict__ h0,
-    uint16_t* __restrict__ o, float* __restrict__ hT, uint16_t* __restrict__ saved) {
+    const ChunkInfo* __restrict__ table, PrepOut prep, StateRef st,
+    uint16_t* __restrict__ o, uint16_t* __restrict__ saved) {
   constexpr int VB = kScanVB;
   constexpr int NVB = kHead / VB;  // value blocks per head
   constexpr int VT = VB / 16;      // 16-wide value tiles per block
@@ -48,9 +48,22 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
   __shared__ __align__(16) uint16_t Ss[VB * SP];  // S[v][k] of the chunk start (bf16)
   __shared__ __align__(16) uint16_t Ds[VB * DP];  // D^T[v][tok] (bf16)
 
+  // start and end state of this chain (the paged form reads and writes one
+  // pool slot in place: each thread reads its own elements before the scan
+  // and writes the same elements after it)
+  const float* h0 = st.h0;
+  float* hT = st.hT;
+  size_t state_base = ((size_t)seq * HV + hv) * kHead * kHead;
+  if (st.idx) {
+    const int sl = st.idx[seq];
+    const bool live = sl > 0 && sl < st.slots;
+    state_base = live ? ((size_t)sl * HV + hv) * kHead * kHead : 0;
+    h0 = live && (!st.init || st.init[seq] != 0) ? st.h0 : nullptr;
+    hT = live ? st.hT : nullptr;
+  }
+
   // h[dt][vt][r] = h[k = 16 (2 wave + dt) + 4 kq + r][v = v0 + 16 vt + li]
   f32x4 h[2][VT];
-  const size_t state_base = ((size_t)seq * HV + hv) * kHead * kHead;
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -243,16 +256,16 @@ __global__ __launch_bounds__(256) void state_copy_kernel(const float* __restrict
 }
 
 hipError_t launch_fwd_scan(const int32_t* seq_first, int N, int HV, int NC,
-                           const ChunkInfo* table, const PrepOut& prep, const float* h0,
-                           uint16_t* o, float* hT, uint16_t* saved, hipStream_t stream) {
+                           const ChunkInfo* table, const PrepOut& prep, const StateRef& st,
+                           uint16_t* o, uint16_t* saved, hipStream_t stream) {
   const long chains = (long)N * HV;
   const long blocks = (chains + 7) / 8 * 8 * (kHead / kScanVB);
   if (saved)
     hipLaunchKernelGGL(fwd_scan_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       seq_first, N, HV, NC, table, prep, h0, o, hT, saved);
+                       seq_first, N, HV, NC, table, prep, st, o, saved);
   else
     hipLaunchKernelGGL(fwd_scan_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       seq_first, N, HV, NC, table, prep, h0, o, hT, saved);
+                       seq_first, N, HV, NC, table, prep, st, o, saved);
   return hipGetLastError();
 }
 

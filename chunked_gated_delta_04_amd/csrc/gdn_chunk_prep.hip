@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t* __restr
   for (int base = 0; base < N; base += 256) {
     const int n = base + tid;
     int cnt = 0, bos = 0, eos = 0;
-    if (n < N) {  // clamp so that device boundaries can never address outside [0, T)
+    if (n < N && T > 0) {  // clamp so that device boundaries can never address outside [0, T)
       bos = min(max(cu[n], 0), T);
       eos = min(max(cu[n + 1], bos), T);
       cnt = (eos - bos + kChunk - 1) / kChunk;

@@ -36,9 +36,22 @@ hipError_t launch_chunk_prep(bool bwd_layout, const ChunkInfo* table, int NC, in
                              const uint16_t* v, const float* g, const float* beta,
                              const PrepOut& out, hipStream_t stream);
 
+// Where the forward scan takes each chain's start state and leaves its end
+// state. Direct: h0 / hT are [N, HV, V, K] (either NULL). Paged: h0 == hT is a
+// pool [slots, HV, V, K] updated in place; sequence n uses slot idx[n] when
+// 0 < idx[n] < slots (else it starts from zero and writes nothing), starting
+// from the slot when init is NULL or init[n] != 0 and from zero otherwise.
+struct StateRef {
+  const float* h0;
+  float* hT;
+  const int32_t* idx;   // paged only
+  const int32_t* init;  // paged only, nullable
+  int slots;
+};
+
 hipError_t launch_fwd_scan(const int32_t* seq_first, int N, int HV, int NC,
-                           const ChunkInfo* table, const PrepOut& prep, const float* h0,
-                           uint16_t* o, float* hT, uint16_t* saved, hipStream_t stream);
+                           const ChunkInfo* table, const PrepOut& prep, const StateRef& st,
+                           uint16_t* o, uint16_t* saved, hipStream_t stream);
 
 hipError_t launch_bwd_dh_scan(const int32_t* seq_first, int N, int HV, int NC,
                               const ChunkInfo* table, const PrepOut& prep, const uint16_t* dO,

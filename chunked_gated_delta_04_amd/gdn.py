@@ -30,7 +30,7 @@ STATUS_NAMES = {
 EXPORTED = (
     "gdn_status_string", "gdn_num_chunks", "gdn_chunk_saved_size",
     "gdn_chunk_fwd_workspace_size", "gdn_chunk_bwd_workspace_size",
-    "gdn_chunk_fwd", "gdn_chunk_bwd", "gdn_recurrent_step",
+    "gdn_chunk_fwd", "gdn_chunk_fwd_paged", "gdn_chunk_bwd", "gdn_recurrent_step",
     "gdn_chunk_fwd_timed", "gdn_chunk_bwd_timed", "gdn_stage_name",
 )
 GDN_MAX_STAGES = 8
@@ -66,6 +66,8 @@ for _n in ("gdn_chunk_saved_size", "gdn_chunk_fwd_workspace_size", "gdn_chunk_bw
     getattr(_lib, _n).argtypes = [_P]
 _lib.gdn_chunk_fwd.restype = ctypes.c_int
 _lib.gdn_chunk_fwd.argtypes = [_P] + [_vp] * 10 + [_sz, _vp]
+_lib.gdn_chunk_fwd_paged.restype = ctypes.c_int
+_lib.gdn_chunk_fwd_paged.argtypes = [_P] + [_vp] * 6 + [_i32] + [_vp] * 6 + [_sz, _vp]
 _lib.gdn_chunk_bwd.restype = ctypes.c_int
 _lib.gdn_chunk_bwd.argtypes = [_P] + [_vp] * 15 + [_sz, _vp]
 _lib.gdn_chunk_fwd_timed.restype = ctypes.c_int
@@ -94,6 +96,13 @@ def _ptr(t, dtype=None, name="tensor"):
     return t.data_ptr() if t.numel() > 0 else None
 
 
+def _host_ptr(t, name):
+    """Pointer of a host-side int32 tensor (None -> NULL)."""
+    if t is not None and isinstance(t, torch.Tensor) and t.device.type != "cpu":
+        raise ValueError(f"{name} must be a CPU tensor")
+    return _ptr(t, torch.int32, name)
+
+
 def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
@@ -113,7 +122,7 @@ def make_problem(N, T, H, HV, cu_seqlens, cu_seqlens_host=None, scale=0.0, K=128
     if cu_seqlens_host is not None:
         if cu_seqlens_host.device.type != "cpu":
             raise ValueError("cu_seqlens_host must be a CPU tensor")
-        p.cu_seqlens_host = _ptr(cu_seqlens_host, torch.int32, "cu_seqlens_host")
+        p.cu_seqlens_host = _host_ptr(cu_seqlens_host, "cu_seqlens_host")
     return p
 
 
@@ -151,6 +160,20 @@ def gdn_chunk_fwd(problem, q, k, v, g, beta, h0, o, hT, saved, workspace, stream
         _ptr(hT, f32, "hT"), _ptr(saved, None, "saved"), _ptr(workspace, None, "workspace"),
         ws_bytes, _stream(stream))
     _check(st, "gdn_chunk_fwd")
+
+
+def gdn_chunk_fwd_paged(problem, q, k, v, g, beta, state_pool, slots, ssm_state_indices,
+                        has_initial_state, indices_host, o, saved, workspace, stream=None):
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.gdn_chunk_fwd_paged(
+        ctypes.byref(problem), _ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"),
+        _ptr(g, f32, "g"), _ptr(beta, f32, "beta"), _ptr(state_pool, f32, "state_pool"),
+        int(slots), _ptr(ssm_state_indices, i32, "ssm_state_indices"),
+        _ptr(has_initial_state, i32, "has_initial_state"),
+        _host_ptr(indices_host, "indices_host"), _ptr(o, bf, "o"), _ptr(saved, None, "saved"),
+        _ptr(workspace, None, "workspace"), ws_bytes, _stream(stream))
+    _check(st, "gdn_chunk_fwd_paged")
 
 
 def gdn_stage_name(op, stage):
@@ -210,7 +233,7 @@ def gdn_recurrent_step(N, H, HV, K, V, scale, q, k, v, a, b, A_log, dt_bias, sta
         _ptr(a, bf, "a"), _ptr(b, bf, "b"), _ptr(A_log, f32, "A_log"),
         _ptr(dt_bias, f32, "dt_bias"), _ptr(state_pool, f32, "state_pool"), slots,
         _ptr(ssm_state_indices, torch.int32, "ssm_state_indices"),
-        _ptr(indices_host, torch.int32, "indices_host"), _ptr(o, bf, "o"), _stream(stream))
+        _host_ptr(indices_host, "indices_host"), _ptr(o, bf, "o"), _stream(stream))
     _check(st, "gdn_recurrent_step")
 
 
@@ -237,6 +260,24 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, scale=0.0, cu_seqlens_host=
     ws = _ws(gdn_chunk_fwd_workspace_size(p), dev)
     gdn_chunk_fwd(p, q, k, v, g, beta, h0, o, hT, saved, ws, stream)
     return o, hT, saved
+
+
+def chunk_fwd_paged(q, k, v, g, beta, cu_seqlens, state_pool, ssm_state_indices,
+                    has_initial_state=None, indices_host=None, scale=0.0, cu_seqlens_host=None,
+                    save_for_backward=False, stream=None):
+    """Allocate o (and saved, workspace) and run gdn_chunk_fwd_paged; the pool
+    [slots, HV, 128, 128] fp32 is updated in place. Returns (o, saved or None)."""
+    T, H, _ = q.shape
+    HV = v.shape[1]
+    N = cu_seqlens.numel() - 1
+    p = make_problem(N, T, H, HV, cu_seqlens, cu_seqlens_host, scale)
+    dev = q.device
+    o = torch.empty(T, HV, 128, dtype=torch.bfloat16, device=dev)
+    saved = _ws(gdn_chunk_saved_size(p), dev) if save_for_backward else None
+    ws = _ws(gdn_chunk_fwd_workspace_size(p), dev)
+    gdn_chunk_fwd_paged(p, q, k, v, g, beta, state_pool, state_pool.shape[0], ssm_state_indices,
+                        has_initial_state, indices_host, o, saved, ws, stream)
+    return o, saved
 
 
 def chunk_bwd(q, k, v, g, beta, cu_seqlens, saved, dO, dhT=None, scale=0.0,

@@ -18,6 +18,9 @@ Recipes (the workloads the chunk and decode kernels are measured on):
                    dt_bias = 0 in fp32 per value head, pool 0.1 * N(0, 1) fp32,
                    indices: a random permutation of 1..slots-1, the first
                    rows of it, with some rows set to 0 (the null block).
+  paged prefill    the chunk recipe without h0, a decode-style pool and
+                   indices, and a has_initial_state mix of resumed (1) and
+                   fresh (0) sequences.
 Every draw comes from one CPU torch.Generator seeded explicitly.
 """
 import math
@@ -109,7 +112,26 @@ def decode_inputs(N, H, HV, slots, n_null, seed, K=K_DIM, V=V_DIM, pool=True):
     return out
 
 
-# The five workloads, by name. Sizes as measured and parity-tested.
+def paged_inputs(lens, H, HV, slots, n_null, n_fresh, seed, K=K_DIM, V=V_DIM):
+    """Inputs of one paged chunk call: those of ``chunk_inputs`` (without h0)
+    plus state_pool [slots, HV, V, K] fp32 = 0.1 * N(0, 1), ssm_state_indices
+    [N] int32 (the first N entries of a random permutation of 1..slots-1, with
+    ``n_null`` random rows set to 0, the null block) and has_initial_state [N]
+    int32 (1, with ``n_fresh`` random rows set to 0: fresh prompts).
+    """
+    out = chunk_inputs(lens, H, HV, seed, h0_std=None, K=K, V=V)
+    gen = torch.Generator().manual_seed(seed + 500)
+    N = len(lens)
+    idx = torch.randperm(slots - 1, generator=gen)[:N] + 1
+    idx[torch.randperm(N, generator=gen)[:n_null]] = 0
+    init = torch.ones(N, dtype=torch.int32)
+    init[torch.randperm(N, generator=gen)[:n_fresh]] = 0
+    out.update(state_pool=0.1 * torch.randn(slots, HV, V, K, generator=gen, dtype=torch.float32),
+               ssm_state_indices=idx.to(torch.int32), has_initial_state=init)
+    return out
+
+
+# The workloads, by name. Sizes as measured and parity-tested.
 WORKLOADS = {
     "fwd_1x256_h1": dict(kind="fwd", lens=[256], H=1, HV=1, h0_std=None, seed=BASE_SEED + 0),
     "fwd_4x4096_h16_hv32": dict(kind="fwd", lens=[4096] * 4, H=16, HV=32, h0_std=0.1,
@@ -120,6 +142,8 @@ WORKLOADS = {
                                    seed=BASE_SEED + 3),
     "decode_256_pool512_h16_hv32": dict(kind="decode", N=256, H=16, HV=32, slots=512, n_null=16,
                                         seed=BASE_SEED + 4),
+    "paged_8x512_h8_hv16_pool64": dict(kind="paged", lens=[512] * 8, H=8, HV=16, slots=64,
+                                       n_null=0, n_fresh=4, seed=BASE_SEED + 5),
 }
 
 
@@ -135,5 +159,8 @@ def workload_inputs(name):
     w = WORKLOADS[name]
     if w["kind"] == "decode":
         return decode_inputs(w["N"], w["H"], w["HV"], w["slots"], w["n_null"], w["seed"])
+    if w["kind"] == "paged":
+        return paged_inputs(workload_lengths(name), w["H"], w["HV"], w["slots"], w["n_null"],
+                            w["n_fresh"], w["seed"])
     return chunk_inputs(workload_lengths(name), w["H"], w["HV"], w["seed"], h0_std=w["h0_std"],
                         with_do=(w["kind"] == "fwdbwd"))

@@ -59,7 +59,7 @@ typedef enum {
   GDN_ERR_SHAPE = 2,       /* a negative or inconsistent extent                  */
   GDN_ERR_UNSUPPORTED = 3, /* K or V != 128, chunk != 64, HV % H != 0            */
   GDN_ERR_SEQLENS = 4,     /* cu_seqlens_host not 0 .. T and non-decreasing      */
-  GDN_ERR_INDEX = 5,       /* an active decode index >= slots, or repeated       */
+  GDN_ERR_INDEX = 5,       /* an active state-pool index >= slots, or repeated   */
   GDN_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the size query      */
   GDN_ERR_HIP = 7,         /* a HIP launch failed                                */
   GDN_ERR_ALIGN = 8        /* a tensor or workspace pointer not 16-byte aligned  */
@@ -120,20 +120,55 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_problem* p);
  *   saved     gdn_chunk_saved_size(p) bytes kept for gdn_chunk_bwd, or NULL
  *             when no backward follows. For chunk slot c and value head hv
  *             the block at element offset (c * HV + hv) * (K*V + 64*V) holds
- *             the chunk's start state, the fp32 running state rounded to
- *             nearest-even bf16 and stored transposed (element (k, v) at
- *             k * V + v is S[v][k]), then the chunk's 64 x V corrected values
- *             D = U - W h (bf16, rows past the chunk's end are zero).
+ *             the chunk's start state (the fp32 running state rounded to
+ *             nearest-even bf16) and then the chunk's 64 x V corrected
+ *             values D = U - W h in bf16 (rows past the chunk's end are
+ *             zero), both in tile orders internal to this library: only
+ *             gdn_chunk_bwd of the same build reads them.
  * A sequence of length 0 gets hT = h0 (or 0). T = 0 is valid: nothing is
  * read from the token tensors and hT = h0 (or 0).
  * Errors: GDN_ERR_NULL (p, q, k, v, g, beta, o, cu_seqlens when T > 0, or
  * workspace), GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_SEQLENS,
- * GDN_ERR_WORKSPACE, GDN_ERR_HIP. */
+ * GDN_ERR_WORKSPACE, GDN_ERR_ALIGN, GDN_ERR_HIP. */
 int gdn_chunk_fwd(const gdn_problem* p,
                   const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   const float* g, const float* beta, const float* h0,
                   uint16_t* o, float* hT, uint16_t* saved,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Chunked forward (prefill) whose start and end states live in a state pool,
+ * updated in place: the paged prefill of a serving stack, sharing the pool
+ * [slots, HV, V, K] of gdn_recurrent_step, without gather / scatter copies.
+ * The torchtitan PR #4389 page (the serving-path and paged-state continuity
+ * sections) describes a serving path whose cache slots are advanced in place
+ * and checks that a prefix resumed from its slot continues the sequence.
+ * Same p, q, k, v, g, beta, o, saved and workspace as gdn_chunk_fwd, and:
+ *   state_pool fp32 [slots, HV, V, K]
+ *   ssm_state_indices int32 [N] (device): sequence n reads and writes block
+ *             ssm_state_indices[n]. An index <= 0 (0 is the null block), or
+ *             one >= slots, gives the sequence no block: it starts from a
+ *             zero state and its end state is not written anywhere.
+ *   has_initial_state int32 [N] (device) or NULL: a sequence with a block
+ *             starts from the block's contents when the flag is nonzero (a
+ *             resumed prefix) and from zero when it is 0 (a fresh prompt);
+ *             NULL resumes every sequence. Its end state replaces the block.
+ *   indices_host optional host copy of the indices, validated as for
+ *             gdn_recurrent_step (GDN_ERR_INDEX); without it the caller
+ *             guarantees that active indices are distinct.
+ * A sequence of length 0 leaves a resumed block unchanged and zeroes a fresh
+ * one. Every other block of the pool is neither read nor written. The results
+ * (o, the end states, saved) equal gdn_chunk_fwd with h0 / hT gathered from
+ * and scattered to the pool, bit for bit.
+ * Errors: those of gdn_chunk_fwd, GDN_ERR_NULL for state_pool or
+ * ssm_state_indices when N > 0, GDN_ERR_SHAPE for slots < 0, GDN_ERR_INDEX. */
+int gdn_chunk_fwd_paged(const gdn_problem* p,
+                        const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const float* g, const float* beta,
+                        float* state_pool, int32_t slots,
+                        const int32_t* ssm_state_indices, const int32_t* has_initial_state,
+                        const int32_t* indices_host,
+                        uint16_t* o, uint16_t* saved,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Chunked backward of gdn_chunk_fwd (same p, q, k, v, g, beta).
  *   saved     as written by gdn_chunk_fwd for the same problem and inputs
@@ -196,7 +231,7 @@ const char* gdn_stage_name(int op, int stage);
  * Each (row, value head) is computed alone, so a row's output and state do
  * not depend on the other rows of the batch.
  * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_INDEX,
- * GDN_ERR_HIP. N = 0 is valid and enqueues nothing. */
+ * GDN_ERR_ALIGN, GDN_ERR_HIP. N = 0 is valid and enqueues nothing. */
 int gdn_recurrent_step(int32_t N, int32_t H, int32_t HV, int32_t K, int32_t V, float scale,
                        const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        const uint16_t* a, const uint16_t* b,

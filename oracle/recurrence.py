@@ -29,6 +29,14 @@ What it computes, and where the pages define it
   ssm_state_indices; every index <= 0 is skipped (zero output, state block
   untouched) and an active index out of range or repeated raises (RL-Kernel
   PR #469, "What" section, the state-contract bullet).
+* Paged prefill. The forward above with each sequence's start state read
+  from, and its end state written back to, block ssm_state_indices[n] of the
+  decode pool, in place of a gathered h0 and a scattered hT; a sequence whose
+  has_initial_state flag is 0 starts from zero (a fresh prompt), one with a
+  flag of 1 resumes from the block (the torchtitan PR #4389 page, its
+  serving-path section and the paged-state continuity results). The pages
+  leave open what a sequence with the null index does; here it runs from a
+  zero state and its end state is dropped.
 * Backward. The manual adjoint of the recurrence, taken in reverse token
   order, gives dq, dk, dv, dg, dbeta and dh0 (the gradient set required by
   the cake_gdn page, miles PR #3597, "Summary" and "Tests").
@@ -262,4 +270,34 @@ def decode_step(q, k, v, a, b, A_log, dt_bias, state_pool, ssm_state_indices, sc
                       np.arange(active.size + 1), h0=pool[ai], scale=scale)
     o[active] = o_a
     pool[ai] = hT
+    return o, pool
+
+
+def paged_forward(q, k, v, g, beta, cu_seqlens, state_pool, ssm_state_indices,
+                  has_initial_state=None, scale=None):
+    """Forward over a varlen pack whose states live in a pool [slots, HV, V, K].
+
+    Sequence n uses block ssm_state_indices[n]: it starts from that block when
+    has_initial_state[n] is nonzero (None: every flag is 1) and from zero
+    otherwise, and its end state replaces the block. An index <= 0 names no
+    block: zero start, end state dropped. An active index >= slots, or one
+    used twice, raises ValueError. Returns (o [T, HV, V], new_pool) in float64;
+    the input pool is not modified.
+    """
+    idx = np.asarray(ssm_state_indices, dtype=np.int64).reshape(-1)
+    pool = _f64(state_pool).copy()
+    slots = pool.shape[0]
+    N = idx.size
+    init = np.ones(N, dtype=np.int64) if has_initial_state is None else \
+        np.asarray(has_initial_state, dtype=np.int64).reshape(-1)
+    live = np.nonzero(idx > 0)[0]
+    if np.any(idx[live] >= slots):
+        raise ValueError("active state index out of range")
+    if np.unique(idx[live]).size != live.size:
+        raise ValueError("repeated active state index")
+    h0 = np.zeros((N,) + pool.shape[1:])
+    resumed = live[init[live] != 0]
+    h0[resumed] = pool[idx[resumed]]
+    o, hT = forward(q, k, v, g, beta, cu_seqlens, h0=h0, scale=scale)
+    pool[idx[live]] = hT[live]
     return o, pool

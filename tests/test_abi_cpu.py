@@ -168,3 +168,37 @@ def test_decode_index_rules_on_the_host_copy(G):
     assert decode(G, host=[1, 8, 2, 3]) == 5
     assert decode(G, host=[1, 2, 2, 3]) == 5
     assert decode(G, host=[1, 2, 7, 7]) == 5
+
+
+def paged(G, p, slots=8, host=None, ws_bytes=1 << 40, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, pool=FAKE, idx=FAKE, init=None,
+                o=FAKE, saved=None, ws=FAKE)
+    args.update(over)
+    keep = None
+    hp = None
+    if host is not None:
+        keep = (ctypes.c_int32 * len(host))(*host)
+        hp = ctypes.cast(keep, ctypes.c_void_p)
+    return G._lib.gdn_chunk_fwd_paged(ctypes.byref(p), args["q"], args["k"], args["v"],
+                                      args["g"], args["beta"], args["pool"], slots, args["idx"],
+                                      args["init"], hp, args["o"], args["saved"], args["ws"],
+                                      ws_bytes, None)
+
+
+def test_paged_forward_rejects_bad_arguments(G):
+    p = problem(G)
+    assert paged(G, problem(G, K=64)) == 3
+    assert paged(G, problem(G, cu_host=(0, 70, 131))) == 4
+    assert paged(G, p, slots=-1) == 2
+    for name in ("pool", "idx", "q", "o"):
+        assert paged(G, p, **{name: None}) == 1, name
+    assert paged(G, p, pool=FAKE_MISALIGNED) == 8
+    assert paged(G, p, ws=None) == 6
+    assert paged(G, p, ws_bytes=G.gdn_chunk_fwd_workspace_size(p) - 1) == 6
+
+
+def test_paged_forward_index_rules_on_the_host_copy(G):
+    p = problem(G)
+    assert paged(G, p, host=[1, 8]) == 5      # past the pool
+    assert paged(G, p, host=[3, 3]) == 5      # one block for two sequences
+    assert paged(G, p, host=[-2, 9], idx=FAKE, pool=None) == 1   # null checks come first

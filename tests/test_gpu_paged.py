@@ -1,0 +1,191 @@
+"""GPU parity of the paged chunk prefill (gdn_chunk_fwd_paged through the C ABI):
+bitwise equal to the direct forward with gathered / scattered states, within
+the bar of the fp64 oracle, and the pages' prefix-continuation sweep."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from chunked_gated_delta_04_amd import synth
+from tests.gpu_helpers import assert_bar, f64, head_slice, to_dev
+from oracle import recurrence as R
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from chunked_gated_delta_04_amd import gdn
+else:
+    gdn = None
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def gathered_h0(inp):
+    """Start states as the direct forward needs them: the block for a resumed
+    sequence with a block, zero otherwise."""
+    pool, idx = inp["state_pool"], inp["ssm_state_indices"].tolist()
+    init = inp["has_initial_state"]
+    init = [1] * len(idx) if init is None else init.tolist()
+    h0 = torch.zeros((len(idx),) + tuple(pool.shape[1:]), dtype=torch.float32)
+    for n, (s, f) in enumerate(zip(idx, init)):
+        if s > 0 and f:
+            h0[n] = pool[s]
+    return h0
+
+
+def run_paged(inp, save=False, host_idx=True, init=True):
+    d = to_dev(inp)
+    pool = d["state_pool"].clone()
+    o, saved = gdn.chunk_fwd_paged(
+        d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], pool,
+        d["ssm_state_indices"], has_initial_state=d["has_initial_state"] if init else None,
+        indices_host=inp["ssm_state_indices"] if host_idx else None,
+        cu_seqlens_host=inp["cu_seqlens"], save_for_backward=save)
+    return o, pool, saved
+
+
+def oracle_paged(inp, init=True):
+    return R.paged_forward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["g"]),
+                           f64(inp["beta"]), inp["cu_seqlens"].tolist(), f64(inp["state_pool"]),
+                           inp["ssm_state_indices"].numpy(),
+                           inp["has_initial_state"].numpy() if init else None)
+
+
+SMALL = [1, 63, 64, 65, 200, 0, 130]
+
+
+@pytest.mark.parametrize("host_idx", [True, False])
+def test_paged_equals_the_direct_forward_with_gather_and_scatter_bitwise(host_idx):
+    _say(f"paged vs direct host_idx={host_idx}")
+    inp = synth.paged_inputs(SMALL, H=2, HV=4, slots=16, n_null=1, n_fresh=3, seed=71)
+    o, pool, saved = run_paged(inp, save=True, host_idx=host_idx)
+    d = to_dev(inp)
+    h0 = gathered_h0(inp).cuda()
+    o_d, hT_d, saved_d = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                       d["cu_seqlens"], h0=h0, cu_seqlens_host=inp["cu_seqlens"],
+                                       save_for_backward=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_d)
+    assert torch.equal(saved, saved_d)
+    idx = inp["ssm_state_indices"].tolist()
+    before = inp["state_pool"]
+    pool = pool.cpu()
+    for n, s in enumerate(idx):
+        if s > 0:
+            assert torch.equal(pool[s], hT_d[n].cpu()), n
+    touched = {s for s in idx if s > 0}
+    for s in range(pool.shape[0]):
+        if s not in touched:
+            assert torch.equal(pool[s], before[s]), s
+
+
+def test_paged_matches_the_oracle_with_fresh_resumed_and_null_rows():
+    _say("paged vs oracle small")
+    inp = synth.paged_inputs(SMALL, H=2, HV=4, slots=16, n_null=2, n_fresh=2, seed=72)
+    o, pool, _ = run_paged(inp)
+    o_ref, pool_ref = oracle_paged(inp)
+    assert_bar("o", f64(o), o_ref)
+    assert_bar("pool", f64(pool), pool_ref)
+
+
+def test_paged_without_flags_resumes_every_block():
+    inp = synth.paged_inputs([70, 33], H=1, HV=2, slots=5, n_null=0, n_fresh=1, seed=73)
+    o, pool, _ = run_paged(inp, init=False)
+    o_ref, pool_ref = oracle_paged(inp, init=False)
+    assert_bar("o", f64(o), o_ref)
+    assert_bar("pool", f64(pool), pool_ref)
+
+
+def test_paged_continuity_sweep_of_the_pages():
+    """Prefixes of 528 / 1056 / 1584 tokens prefilled fresh into their blocks,
+    then continuations of 1 / 63 / 64 / 65 / 527 tokens resumed from them, in
+    two batched calls; the outputs and end states match one oracle pass over
+    the whole sequences."""
+    _say("paged continuity sweep")
+    cases = [(P, C) for P in (528, 1056, 1584) for C in (1, 63, 64, 65, 527)]
+    N = len(cases)
+    full = synth.paged_inputs([P + C for P, C in cases], H=1, HV=2, slots=2 * N + 1, n_null=0,
+                              n_fresh=0, seed=74)
+    cu = full["cu_seqlens"].tolist()
+    first = torch.cat([torch.arange(cu[i], cu[i] + P) for i, (P, C) in enumerate(cases)])
+    second = torch.cat([torch.arange(cu[i] + P, cu[i + 1]) for i, (P, C) in enumerate(cases)])
+
+    def part(rows, lens, init):
+        return dict(q=full["q"][rows], k=full["k"][rows], v=full["v"][rows],
+                    g=full["g"][rows], beta=full["beta"][rows],
+                    cu_seqlens=synth.cu_from_lengths(lens), state_pool=None,
+                    ssm_state_indices=full["ssm_state_indices"],
+                    has_initial_state=torch.full((N,), init, dtype=torch.int32))
+
+    a = part(first, [P for P, _ in cases], 0)
+    b = part(second, [C for _, C in cases], 1)
+    a["state_pool"] = full["state_pool"]
+    o1, pool1, _ = run_paged(a)
+    b["state_pool"] = pool1.cpu()
+    o2, pool2, _ = run_paged(b)
+    ref_in = dict(full, has_initial_state=torch.zeros(N, dtype=torch.int32))
+    o_ref, pool_ref = oracle_paged(ref_in)
+    assert_bar("o prefix", f64(o1), o_ref[first.numpy()])
+    assert_bar("o continuation", f64(o2), o_ref[second.numpy()])
+    assert_bar("pool", f64(pool2), pool_ref)
+    # the fresh prefill ignored what the blocks held before
+    idx = full["ssm_state_indices"].tolist()
+    others = [s for s in range(2 * N + 1) if s not in idx]
+    assert torch.equal(pool2.cpu()[others], full["state_pool"][others])
+
+
+def test_paged_zero_length_and_no_token_calls():
+    _say("paged zero-length")
+    inp = synth.paged_inputs([0, 70, 0], H=1, HV=2, slots=6, n_null=0, n_fresh=0, seed=75)
+    inp["ssm_state_indices"] = torch.tensor([2, 4, 5], dtype=torch.int32)
+    inp["has_initial_state"] = torch.tensor([1, 1, 0], dtype=torch.int32)
+    o, pool, _ = run_paged(inp)
+    pool = pool.cpu()
+    assert torch.equal(pool[2], inp["state_pool"][2])
+    assert torch.equal(pool[5], torch.zeros_like(pool[5]))
+    o_ref, pool_ref = oracle_paged(inp)
+    assert_bar("o", f64(o), o_ref)
+    assert_bar("pool", f64(pool), pool_ref)
+    # T = 0: no token at all, one resumed and one fresh block
+    H, HV = 1, 2
+    e = torch.empty(0, H, 128, dtype=torch.bfloat16, device="cuda")
+    ev = torch.empty(0, HV, 128, dtype=torch.bfloat16, device="cuda")
+    eg = torch.empty(0, HV, dtype=torch.float32, device="cuda")
+    pool0 = inp["state_pool"].cuda()
+    cu = torch.zeros(3, dtype=torch.int32)
+    idx = torch.tensor([3, 0], dtype=torch.int32)
+    o, _ = gdn.chunk_fwd_paged(e, e, ev, eg, eg, cu.cuda(), pool0, idx.cuda(),
+                               has_initial_state=torch.tensor([0, 1], dtype=torch.int32).cuda(),
+                               indices_host=idx, cu_seqlens_host=cu)
+    torch.cuda.synchronize()
+    p = pool0.cpu()
+    assert o.numel() == 0 and torch.equal(p[3], torch.zeros_like(p[3]))
+    keep = [s for s in range(6) if s != 3]
+    assert torch.equal(p[keep], inp["state_pool"][keep])
+
+
+def test_paged_workload_sampled_heads():
+    """The measured paged workload (8 x 512 tokens, 8 key heads, 16 value heads,
+    64-slot pool, half the sequences fresh): sampled heads against the oracle
+    and every other block untouched."""
+    _say("paged workload")
+    inp = synth.workload_inputs("paged_8x512_h8_hv16_pool64")
+    o, pool, _ = run_paged(inp)
+    o, pool = o.cpu(), pool.cpu()
+    H, HV = inp["q"].shape[1], inp["v"].shape[1]
+    idx = inp["ssm_state_indices"].tolist()
+    init = inp["has_initial_state"].tolist()
+    rng = np.random.default_rng(1)
+    h0 = gathered_h0(inp)
+    for seq, hv in [(0, 0), (7, HV - 1)] + [(int(rng.integers(8)), int(rng.integers(HV)))
+                                           for _ in range(2)]:
+        s, (t0, t1), h, hvs = head_slice(dict(inp, h0=h0), seq, hv, H, HV)
+        o_ref, hT_ref = R.forward(s["q"], s["k"], s["v"], s["g"], s["beta"], s["cu"], s["h0"])
+        j = hvs.index(hv)
+        assert_bar(f"o[{seq},{hv}] init={init[seq]}", f64(o[t0:t1, hv]), o_ref[:, j])
+        assert_bar(f"pool[{idx[seq]},{hv}]", f64(pool[idx[seq], hv]), hT_ref[0, j])
+    others = [s for s in range(pool.shape[0]) if s not in idx]
+    assert torch.equal(pool[others], inp["state_pool"][others])

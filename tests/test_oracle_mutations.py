@@ -58,7 +58,31 @@ def _head_map_modulo(H, HV):
     return np.arange(HV) % H
 
 
+_paged = R.paged_forward
+
+
+def _paged_ignores_fresh_flags(q, k, v, g, beta, cu, pool, idx, init=None, scale=None):
+    return _paged(q, k, v, g, beta, cu, pool, idx, None, scale)
+
+
+def _paged_drops_end_states(q, k, v, g, beta, cu, pool, idx, init=None, scale=None):
+    o, _ = _paged(q, k, v, g, beta, cu, pool, idx, init, scale)
+    return o, np.asarray(pool, np.float64).copy()
+
+
+def _paged_writes_the_start_state(q, k, v, g, beta, cu, pool, idx, init=None, scale=None):
+    o, new = _paged(q, k, v, g, beta, cu, pool, idx, init, scale)
+    live = np.asarray(idx) > 0
+    if init is not None:
+        live &= np.asarray(init) != 0
+    new[np.asarray(idx)[live]] = np.asarray(pool, np.float64)[np.asarray(idx)[live]]
+    return o, new
+
+
 MUTATIONS = {
+    "paged: fresh sequences resume from their block": ("paged_forward", _paged_ignores_fresh_flags),
+    "paged: end states not written back": ("paged_forward", _paged_drops_end_states),
+    "paged: start state written back": ("paged_forward", _paged_writes_the_start_state),
     "delta sign": ("_step", _step_sign),
     "prediction from the undecayed state": ("_step", _step_undecayed_pred),
     "decay after the write": ("_step", _step_decay_after_write),
@@ -77,6 +101,8 @@ PINS = [
     lambda c: P.test_forget_all_decay(),
     lambda c: P.test_grouped_heads_equal_repeated_key_heads(),
     lambda c: P.test_decode_is_one_recurrence_step_with_the_fused_gates(),
+    lambda c: P.test_paged_prefix_then_continuation_equals_one_pass(),
+    lambda c: P.test_paged_fresh_resumed_and_null_sequences(),
 ]
 
 

@@ -355,3 +355,83 @@ def test_decode_steps_equal_the_chunk_forward():
                                  A_log, dt_bias, cur, np.array([2]))
         assert rel_err(o_t[0], o_ref[t]) < 1e-12
     assert rel_err(cur[2], hT[0]) < 1e-12
+
+
+# ---------------------------------------------------------------- paged prefill
+def _paged_case(rng, lens, H=1, HV=2, K=8, V=8, slots=40):
+    q, k, v, g, beta, cu, _ = rand_inputs(rng, lens, H, HV, K, V, h0=False, g_scale=0.05)
+    pool = 0.1 * rng.standard_normal((slots, HV, V, K))
+    return q, k, v, g, beta, cu, pool
+
+
+def test_paged_prefix_then_continuation_equals_one_pass():
+    """The pages' continuity sweep (torchtitan PR #4389, 'Paged-state continuity':
+    prefixes 528/1056/1584 tokens, continuations 1/63/64/65/527): a fresh
+    prefill of the prefix into a block, then a resumed prefill of the
+    continuation from it, equals one pass over the whole sequence."""
+    rng = np.random.default_rng(61)
+    cases = [(P, C) for P in (528, 1056, 1584) for C in (1, 63, 64, 65, 527)]
+    full = [P + C for P, C in cases]
+    q, k, v, g, beta, cu, pool = _paged_case(rng, full)
+    o_ref, h_ref = R.forward(q, k, v, g, beta, cu)
+    first = np.concatenate([np.arange(cu[i], cu[i] + P) for i, (P, C) in enumerate(cases)])
+    second = np.concatenate([np.arange(cu[i] + P, cu[i + 1]) for i, (P, C) in enumerate(cases)])
+    idx = rng.permutation(np.arange(1, 40))[:len(cases)]
+    sel = lambda x, t: x[t]  # noqa: E731
+    cu1 = np.concatenate([[0], np.cumsum([P for P, _ in cases])])
+    cu2 = np.concatenate([[0], np.cumsum([C for _, C in cases])])
+    o1, pool1 = R.paged_forward(sel(q, first), sel(k, first), sel(v, first), sel(g, first),
+                                sel(beta, first), cu1, pool, idx, np.zeros(len(cases)))
+    o2, pool2 = R.paged_forward(sel(q, second), sel(k, second), sel(v, second), sel(g, second),
+                                sel(beta, second), cu2, pool1, idx, np.ones(len(cases)))
+    assert rel_err(o1, o_ref[first]) < 1e-12 and rel_err(o2, o_ref[second]) < 1e-12
+    assert rel_err(pool2[idx], h_ref) < 1e-12
+    others = np.setdiff1d(np.arange(40), idx)
+    assert np.array_equal(pool2[others], pool[others])
+
+
+def test_paged_fresh_resumed_and_null_sequences():
+    rng = np.random.default_rng(62)
+    lens = [70, 5, 130, 64, 1]
+    q, k, v, g, beta, cu, pool = _paged_case(rng, lens, H=2, HV=4, slots=10)
+    idx = np.array([3, 0, 7, -1, 9])
+    init = np.array([1, 1, 0, 1, 1])
+    o, new = R.paged_forward(q, k, v, g, beta, cu, pool, idx, init)
+    for n in range(len(lens)):
+        t0, t1 = cu[n], cu[n + 1]
+        start = pool[idx[n]:idx[n] + 1] if idx[n] > 0 and init[n] else None
+        o_n, h_n = R.forward(q[t0:t1], k[t0:t1], v[t0:t1], g[t0:t1], beta[t0:t1], [0, t1 - t0],
+                             start)
+        assert np.array_equal(o[t0:t1], o_n), n
+        if idx[n] > 0:
+            assert np.array_equal(new[idx[n]], h_n[0]), n
+    untouched = [s for s in range(10) if s not in (3, 7, 9)]
+    assert np.array_equal(new[untouched], pool[untouched])
+    # a fresh sequence does not depend on what its block held
+    pool_b = pool.copy()
+    pool_b[7] = 5.0
+    o_b, new_b = R.paged_forward(q, k, v, g, beta, cu, pool_b, idx, init)
+    assert np.array_equal(o_b, o) and np.array_equal(new_b[7], new[7])
+    # no flags: every sequence with a block resumes
+    o_all, _ = R.paged_forward(q, k, v, g, beta, cu, pool, idx, None)
+    o_res, _ = R.paged_forward(q, k, v, g, beta, cu, pool, idx, np.ones(5))
+    assert np.array_equal(o_all, o_res)
+
+
+def test_paged_zero_length_sequences():
+    rng = np.random.default_rng(63)
+    q, k, v, g, beta, cu, pool = _paged_case(rng, [0, 9, 0], slots=6)
+    o, new = R.paged_forward(q, k, v, g, beta, cu, pool, [2, 4, 5], [1, 1, 0])
+    assert np.array_equal(new[2], pool[2])            # resumed, no tokens: unchanged
+    assert np.array_equal(new[5], np.zeros_like(pool[5]))  # fresh, no tokens: zero state
+    assert not np.array_equal(new[4], pool[4])
+
+
+def test_paged_rejects_bad_active_indices():
+    rng = np.random.default_rng(64)
+    q, k, v, g, beta, cu, pool = _paged_case(rng, [3, 4], slots=6)
+    with pytest.raises(ValueError):
+        R.paged_forward(q, k, v, g, beta, cu, pool, [2, 2])
+    with pytest.raises(ValueError):
+        R.paged_forward(q, k, v, g, beta, cu, pool, [2, 6])
+    R.paged_forward(q, k, v, g, beta, cu, pool, [0, 0])
