@@ -213,6 +213,52 @@ def secondary(h, stream, steps, warmup):
                  "algorithmic_bytes": bytes_, "achieved_GBps": round(gbs, 1),
                  "hbm_frac": round(gbs * 1e9 / PEAK_HBM, 4)}
     out.update(paged_prefill(h, stream, steps, warmup))
+    out.update(recompute_and_transition(h, stream, steps, warmup))
+    return out
+
+
+def recompute_and_transition(h, stream, steps, warmup):
+    """On the fwd+bwd pack (2 x 8192 tokens, 16 / 32 heads): the step with the
+    recomputing backward (a forward that saves nothing, then
+    gdn_chunk_bwd_recompute), and the local transitions of the pack cut into 8
+    shards of 2048 tokens (one context-parallel rank's work per shard)."""
+    import torch
+    from chunked_gated_delta_04_amd import gdn, synth
+    inp = synth.workload_inputs("fwdbwd_2x8192_h16_hv32")
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    T, H, _ = inp["q"].shape
+    HV = inp["v"].shape[1]
+    N = inp["cu_seqlens"].numel() - 1
+    p = gdn.make_problem(N, T, H, HV, d["cu_seqlens"], inp["cu_seqlens"])
+    o = torch.empty(T, HV, 128, dtype=torch.bfloat16, device="cuda")
+    hT = torch.empty(N, HV, 128, 128, dtype=torch.float32, device="cuda")
+    fws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(p), dtype=torch.uint8, device="cuda")
+    bws = torch.empty(gdn.gdn_chunk_bwd_recompute_workspace_size(p), dtype=torch.uint8,
+                      device="cuda")
+    g_ = dict(dq=torch.empty_like(d["q"]), dk=torch.empty_like(d["k"]), dv=torch.empty_like(d["v"]),
+              dg=torch.empty_like(d["g"]), dbeta=torch.empty_like(d["beta"]),
+              dh0=torch.empty_like(d["h0"]))
+
+    def step():
+        gdn.gdn_chunk_fwd(p, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], o, hT, None,
+                          fws, stream)
+        gdn.gdn_chunk_bwd_recompute(p, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"],
+                                    d["do"], None, g_["dq"], g_["dk"], g_["dv"], g_["dg"],
+                                    g_["dbeta"], g_["dh0"], bws, stream)
+    ms = time_call(h, stream, step, steps, warmup)
+    out = {"fwdbwd_2x8192_h16_hv32_recompute": {
+        "ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "workspace_bytes": bws.numel(), "saved_bytes_avoided": gdn.gdn_chunk_saved_size(p)}}
+    del bws, g_
+    cu8 = torch.arange(0, T + 1, 2048, dtype=torch.int32)
+    p8 = gdn.make_problem(8, T, H, HV, cu8.cuda(), cu8)
+    M = torch.empty(8, HV, 128, 128, dtype=torch.float32, device="cuda")
+    sT = torch.empty_like(M)
+    tws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(p8), dtype=torch.uint8, device="cuda")
+    ms = time_call(h, stream, lambda: gdn.gdn_chunk_transition(
+        p8, d["q"], d["k"], d["v"], d["g"], d["beta"], M, sT, tws, stream), steps, warmup)
+    out["transition_8x2048_h16_hv32"] = {"ms": round(ms, 4),
+                                         "tokens_per_s": round(T / (ms * 1e-3), 1)}
     return out
 
 

@@ -164,6 +164,12 @@ GDN_API size_t gdn_chunk_bwd_workspace_size(const gdn_problem* p) {
   return make_layout(p, nc, true).total;
 }
 
+GDN_API size_t gdn_chunk_bwd_recompute_workspace_size(const gdn_problem* p) {
+  int64_t nc = 0;
+  if (check_problem(p, &nc) != GDN_OK) return 0;
+  return align_up(make_layout(p, nc, true).total) + gdn_chunk_saved_size(p);
+}
+
 // Records events[2 i] / events[2 i + 1] around stage i when events are given.
 struct StageClock {
   void* const* ev;
@@ -220,7 +226,8 @@ static int chunk_fwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_
                                beta, prep, s);
     }));
   GDN_TRY(clk.run([&] {
-    return launch_fwd_scan(seq_first, p->N, p->HV, (int)NC, table, prep, sr, o, saved, s);
+    return launch_fwd_scan(saved ? ScanMode::kOutSave : ScanMode::kOut, seq_first, p->N, p->HV,
+                           (int)NC, table, prep, sr, o, saved, s);
   }));
   if (n_stages) *n_stages = clk.n;
   return GDN_OK;
@@ -263,25 +270,64 @@ GDN_API int gdn_chunk_fwd_timed(const gdn_problem* p, const uint16_t* q, const u
                         stream, events, n_stages);
 }
 
+GDN_API int gdn_chunk_transition(const gdn_problem* p, const uint16_t* q, const uint16_t* k,
+                                 const uint16_t* v, const float* g, const float* beta, float* M,
+                                 float* s_end, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  int64_t NC = 0;
+  const gdn_status st = check_problem(p, &NC);
+  if (st != GDN_OK) return st;
+  if (p->T > 0 && (!q || !k || !v || !g || !beta)) return GDN_ERR_NULL;
+  if (p->N > 0 && (!M || !s_end)) return GDN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(M) || !aligned16(s_end) ||
+      !aligned16(workspace))
+    return GDN_ERR_ALIGN;
+  const Layout L = make_layout(p, NC, false);
+  if (!workspace || workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
+  if (p->N == 0) return GDN_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  ChunkInfo* table = reinterpret_cast<ChunkInfo*>(ws + L.table);
+  int32_t* seq_first = reinterpret_cast<int32_t*>(ws + L.seq_first);
+  const PrepOut prep = prep_views(ws, L, false);
+  if (launch_chunk_table(p->cu_seqlens, p->N, p->T, (int)NC, table, seq_first, s) != hipSuccess)
+    return GDN_ERR_HIP;
+  if (NC > 0 && launch_chunk_prep(false, table, (int)NC, p->H, p->HV, effective_scale(p), q, k,
+                                  v, g, beta, prep, s) != hipSuccess)
+    return GDN_ERR_HIP;
+  StateRef sr{};
+  sr.hT = s_end;
+  sr.M = M;
+  if (launch_fwd_scan(ScanMode::kTransition, seq_first, p->N, p->HV, (int)NC, table, prep, sr,
+                      nullptr, nullptr, s) != hipSuccess)
+    return GDN_ERR_HIP;
+  return GDN_OK;
+}
+
+// The backward; with recompute_h0 != nullptr (the recomputing form) it first
+// reruns the forward scan from that start state to rebuild the saved states
+// and D in the workspace, after the backward's own buffers.
 static int chunk_bwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_t* k,
                           const uint16_t* v, const float* g, const float* beta,
                           const uint16_t* saved, const uint16_t* dO, const float* dhT,
                           uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dg, float* dbeta,
                           float* dh0, void* workspace, size_t workspace_bytes, void* stream,
-                          void* const* events, int* n_stages) {
+                          void* const* events, int* n_stages, bool recompute = false,
+                          const float* recompute_h0 = nullptr) {
   if (n_stages) *n_stages = 0;
   int64_t NC = 0;
   gdn_status st = check_problem(p, &NC);
   if (st != GDN_OK) return st;
-  if (p->T > 0 && (!q || !k || !v || !g || !beta || !saved || !dO || !dq || !dk || !dv ||
-                   !dg || !dbeta))
+  if (p->T > 0 && (!q || !k || !v || !g || !beta || (!saved && !recompute) || !dO || !dq ||
+                   !dk || !dv || !dg || !dbeta))
     return GDN_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(saved) ||
       !aligned16(dO) || !aligned16(dhT) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
-      !aligned16(dh0) || !aligned16(workspace))
+      !aligned16(dh0) || !aligned16(workspace) || !aligned16(recompute_h0))
     return GDN_ERR_ALIGN;
   const Layout L = make_layout(p, NC, true);
-  if (!workspace || workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
+  const size_t need = recompute ? gdn_chunk_bwd_recompute_workspace_size(p) : L.total;
+  if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   StageClock clk{events, 0, s};
   if (p->T == 0) {  // no tokens: the state cotangent passes through
@@ -302,6 +348,24 @@ static int chunk_bwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_
   GDN_TRY(clk.run([&] {
     return launch_chunk_table(p->cu_seqlens, p->N, p->T, (int)NC, table, seq_first, s);
   }));
+  if (recompute) {
+    // forward WY pass and scan, saving only: the forward's operands live in the
+    // workspace's first bytes (the same offsets as the forward's own layout)
+    // until the backward's WY pass below overwrites them
+    uint16_t* rebuilt = reinterpret_cast<uint16_t*>(ws + align_up(L.total));
+    const PrepOut fprep = prep_views(ws, make_layout(p, NC, false), false);
+    GDN_TRY(clk.run([&] {
+      return launch_chunk_prep(false, table, (int)NC, p->H, p->HV, scale, q, k, v, g, beta, fprep,
+                               s);
+    }));
+    StateRef sr{};
+    sr.h0 = recompute_h0;
+    GDN_TRY(clk.run([&] {
+      return launch_fwd_scan(ScanMode::kSave, seq_first, p->N, p->HV, (int)NC, table, fprep, sr,
+                             nullptr, rebuilt, s);
+    }));
+    saved = rebuilt;
+  }
   GDN_TRY(clk.run([&] {
     return launch_chunk_prep(true, table, (int)NC, p->H, p->HV, scale, q, k, v, g, beta, prep, s);
   }));
@@ -323,6 +387,16 @@ GDN_API int gdn_chunk_bwd(const gdn_problem* p, const uint16_t* q, const uint16_
                           float* dh0, void* workspace, size_t workspace_bytes, void* stream) {
   return chunk_bwd_impl(p, q, k, v, g, beta, saved, dO, dhT, dq, dk, dv, dg, dbeta, dh0, workspace,
                         workspace_bytes, stream, nullptr, nullptr);
+}
+
+GDN_API int gdn_chunk_bwd_recompute(const gdn_problem* p, const uint16_t* q, const uint16_t* k,
+                                    const uint16_t* v, const float* g, const float* beta,
+                                    const float* h0, const uint16_t* dO, const float* dhT,
+                                    uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dg,
+                                    float* dbeta, float* dh0, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return chunk_bwd_impl(p, q, k, v, g, beta, nullptr, dO, dhT, dq, dk, dv, dg, dbeta, dh0,
+                        workspace, workspace_bytes, stream, nullptr, nullptr, true, h0);
 }
 
 GDN_API int gdn_chunk_bwd_timed(const gdn_problem* p, const uint16_t* q, const uint16_t* k,

@@ -30,7 +30,6 @@ namespace gdn {
 namespace {
 constexpr int KP = 136;  // LDS pitch (bf16) of [64][128] tiles
 constexpr int TP = 72;   // LDS pitch (bf16) of [128][64] tiles
-constexpr int FP = 68;   // LDS pitch (fp32) of [64][64] tiles
 
 __device__ __forceinline__ void lower_tile(int t, int& ib, int& jb) {
   ib = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;

@@ -19,12 +19,21 @@
 // read. All operands come straight from global memory in MFMA fragment
 // layout (16 bytes per lane per operand); only S (bf16) and D pass through
 // LDS, where every wave needs all of them.
+//
+// Transition mode (one GPU's share of a context-parallel forward): the end
+// state is affine in the start state, h_end = M_h h_0 + s, and the chunk map
+// is h -> (e^gamma_L I - K_bwd^T W) h + K_bwd^T U (the chunk transition of the
+// maxtext page "Qwen3.5-397B RL trainer on 128 v7x", its gdn_cp_m_scan
+// commit). M_h is the same scan run on a K x K "state" that starts at the
+// identity with U = 0, and s the ordinary scan from zero; the launch runs both
+// as 2 x 128/VB value blocks per chain and writes M_h transposed, i.e. the
+// matrix M with S_end = S_0 M + s in the S = h^T layout of the states.
 #include "gdn_common.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
-template <bool kSave>
+template <bool kSave, bool kOut, bool kTrans>
 __global__ __launch_bounds__(256) void fwd_scan_kernel(
     const int32_t* __restrict__ seq_first, int N, int HV, int NC,
     const ChunkInfo* __restrict__ table, PrepOut prep, StateRef st,
@@ -35,10 +44,12 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
   constexpr int SP = 136;          // LDS pitch of S rows (bf16)
   constexpr int DP = 72;           // LDS pitch of D^T rows (bf16)
 
+  constexpr int NVBL = kTrans ? 2 * NVB : NVB;  // blocks per chain
   const int b = blockIdx.x;
   const int xcd = b & 7, slot = b >> 3;
   const int vb = slot % NVB;
-  const int chain = (slot / NVB) * 8 + xcd;
+  const bool mblk = kTrans && slot % NVBL < NVB;  // a block of M's columns
+  const int chain = (slot / NVBL) * 8 + xcd;
   if (chain >= N * HV) return;
   const int seq = chain / HV, hv = chain - seq * HV;
   const int v0 = vb * VB;
@@ -70,7 +81,13 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     for (int vt = 0; vt < VT; ++vt) {
       const int kk = 16 * (2 * wave + dt) + 4 * kq;
       const int vv = v0 + 16 * vt + li;
-      if (h0) {
+      if constexpr (kTrans) {
+        h[dt][vt] = zero4();
+        if (mblk) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) h[dt][vt][r] = kk + r == vv ? 1.f : 0.f;
+        }
+      } else if (h0) {
         const float4 x = *reinterpret_cast<const float4*>(h0 + state_base + (size_t)vv * kHead + kk);
         h[dt][vt] = f32x4{x.x, x.y, x.z, x.w};
       } else {
@@ -98,10 +115,12 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       x.wa[s] = ld8(Wb + kcm(16 * wave + li, 32 * s + 8 * kq, 64));
-      x.qa[s] = ld8(Qb + kcm(16 * wave + li, 32 * s + 8 * kq, 64));
+      if constexpr (kOut) x.qa[s] = ld8(Qb + kcm(16 * wave + li, 32 * s + 8 * kq, 64));
     }
+    if constexpr (kOut) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) x.pa[s] = ld8(Pb + kcm(16 * wave + li, 32 * s + 8 * kq, 64));
+      for (int s = 0; s < 2; ++s) x.pa[s] = ld8(Pb + kcm(16 * wave + li, 32 * s + 8 * kq, 64));
+    }
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -164,7 +183,7 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
       a1 = mfma(cur.wa[3], sb[3], a1);
       const f32x4 acc = a0 + a1;
       // acc[r] = (W h)[t = 16 w + 4 kq + r][v = 16 vt + li]
-      const uint2 u = cur.u[vt];
+      const uint2 u = mblk ? make_uint2(0u, 0u) : cur.u[vt];
       *reinterpret_cast<uint2*>(&Ds[(16 * vt + li) * DP + 16 * wave + 4 * kq]) =
           pack4_bf16(bf2f(u.x & 0xffffu) - acc[0], bf2f(u.x >> 16) - acc[1],
                      bf2f(u.y & 0xffffu) - acc[2], bf2f(u.y >> 16) - acc[3]);
@@ -180,7 +199,7 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     // 3. O^T = S Q_g^T + D^T P^T; wave w owns tokens 16 w .. 16 w + 15. Rows at
     //    or past the chunk length fall outside the store's buffer range, which
     //    drops them.
-    {
+    if constexpr (kOut) {
       const int tl = 16 * wave + li;
       const __amdgpu_buffer_rsrc_t orng =
           __builtin_amdgcn_make_buffer_rsrc(o + ((size_t)t0 * HV + hv) * kHead, 0,
@@ -236,6 +255,7 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     }
   }
 
+  if constexpr (kTrans) hT = mblk ? st.M : st.hT;
   if (hT) {
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
@@ -255,17 +275,30 @@ __global__ __launch_bounds__(256) void state_copy_kernel(const float* __restrict
   if (i < n) dst[i] = src ? src[i] : 0.f;
 }
 
-hipError_t launch_fwd_scan(const int32_t* seq_first, int N, int HV, int NC,
+hipError_t launch_fwd_scan(ScanMode mode, const int32_t* seq_first, int N, int HV, int NC,
                            const ChunkInfo* table, const PrepOut& prep, const StateRef& st,
                            uint16_t* o, uint16_t* saved, hipStream_t stream) {
   const long chains = (long)N * HV;
-  const long blocks = (chains + 7) / 8 * 8 * (kHead / kScanVB);
-  if (saved)
-    hipLaunchKernelGGL(fwd_scan_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       seq_first, N, HV, NC, table, prep, st, o, saved);
-  else
-    hipLaunchKernelGGL(fwd_scan_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       seq_first, N, HV, NC, table, prep, st, o, saved);
+  const long per_chain = (kHead / kScanVB) * (mode == ScanMode::kTransition ? 2 : 1);
+  const dim3 grid((unsigned)((chains + 7) / 8 * 8 * per_chain));
+  switch (mode) {
+    case ScanMode::kOut:
+      hipLaunchKernelGGL((fwd_scan_kernel<false, true, false>), grid, dim3(256), 0, stream,
+                         seq_first, N, HV, NC, table, prep, st, o, saved);
+      break;
+    case ScanMode::kOutSave:
+      hipLaunchKernelGGL((fwd_scan_kernel<true, true, false>), grid, dim3(256), 0, stream,
+                         seq_first, N, HV, NC, table, prep, st, o, saved);
+      break;
+    case ScanMode::kSave:
+      hipLaunchKernelGGL((fwd_scan_kernel<true, false, false>), grid, dim3(256), 0, stream,
+                         seq_first, N, HV, NC, table, prep, st, o, saved);
+      break;
+    case ScanMode::kTransition:
+      hipLaunchKernelGGL((fwd_scan_kernel<false, false, true>), grid, dim3(256), 0, stream,
+                         seq_first, N, HV, NC, table, prep, st, o, saved);
+      break;
+  }
   return hipGetLastError();
 }
 

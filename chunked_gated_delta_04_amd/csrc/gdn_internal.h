@@ -41,15 +41,26 @@ hipError_t launch_chunk_prep(bool bwd_layout, const ChunkInfo* table, int NC, in
 // pool [slots, HV, V, K] updated in place; sequence n uses slot idx[n] when
 // 0 < idx[n] < slots (else it starts from zero and writes nothing), starting
 // from the slot when init is NULL or init[n] != 0 and from zero otherwise.
+// Transition: M receives each chain's transition product and hT its end state
+// from a zero start (h0 unused).
 struct StateRef {
   const float* h0;
   float* hT;
   const int32_t* idx;   // paged only
   const int32_t* init;  // paged only, nullable
   int slots;
+  float* M;             // transition only
 };
 
-hipError_t launch_fwd_scan(const int32_t* seq_first, int N, int HV, int NC,
+// What one forward-scan launch produces.
+enum class ScanMode {
+  kOut,         // o (and hT)
+  kOutSave,     // o, the saved states and D for the backward (and hT)
+  kSave,        // only the saved states and D (the recomputing backward)
+  kTransition,  // M and the zero-start end state, no o
+};
+
+hipError_t launch_fwd_scan(ScanMode mode, const int32_t* seq_first, int N, int HV, int NC,
                            const ChunkInfo* table, const PrepOut& prep, const StateRef& st,
                            uint16_t* o, uint16_t* saved, hipStream_t stream);
 

@@ -30,7 +30,9 @@ STATUS_NAMES = {
 EXPORTED = (
     "gdn_status_string", "gdn_num_chunks", "gdn_chunk_saved_size",
     "gdn_chunk_fwd_workspace_size", "gdn_chunk_bwd_workspace_size",
-    "gdn_chunk_fwd", "gdn_chunk_fwd_paged", "gdn_chunk_bwd", "gdn_recurrent_step",
+    "gdn_chunk_bwd_recompute_workspace_size",
+    "gdn_chunk_fwd", "gdn_chunk_fwd_paged", "gdn_chunk_bwd", "gdn_chunk_bwd_recompute",
+    "gdn_chunk_transition", "gdn_recurrent_step",
     "gdn_chunk_fwd_timed", "gdn_chunk_bwd_timed", "gdn_stage_name",
 )
 GDN_MAX_STAGES = 8
@@ -61,7 +63,8 @@ _lib.gdn_status_string.restype = ctypes.c_char_p
 _lib.gdn_status_string.argtypes = [ctypes.c_int]
 _lib.gdn_num_chunks.restype = ctypes.c_int64
 _lib.gdn_num_chunks.argtypes = [_P]
-for _n in ("gdn_chunk_saved_size", "gdn_chunk_fwd_workspace_size", "gdn_chunk_bwd_workspace_size"):
+for _n in ("gdn_chunk_saved_size", "gdn_chunk_fwd_workspace_size", "gdn_chunk_bwd_workspace_size",
+           "gdn_chunk_bwd_recompute_workspace_size"):
     getattr(_lib, _n).restype = _sz
     getattr(_lib, _n).argtypes = [_P]
 _lib.gdn_chunk_fwd.restype = ctypes.c_int
@@ -70,6 +73,10 @@ _lib.gdn_chunk_fwd_paged.restype = ctypes.c_int
 _lib.gdn_chunk_fwd_paged.argtypes = [_P] + [_vp] * 6 + [_i32] + [_vp] * 6 + [_sz, _vp]
 _lib.gdn_chunk_bwd.restype = ctypes.c_int
 _lib.gdn_chunk_bwd.argtypes = [_P] + [_vp] * 15 + [_sz, _vp]
+_lib.gdn_chunk_bwd_recompute.restype = ctypes.c_int
+_lib.gdn_chunk_bwd_recompute.argtypes = [_P] + [_vp] * 15 + [_sz, _vp]
+_lib.gdn_chunk_transition.restype = ctypes.c_int
+_lib.gdn_chunk_transition.argtypes = [_P] + [_vp] * 8 + [_sz, _vp]
 _lib.gdn_chunk_fwd_timed.restype = ctypes.c_int
 _lib.gdn_chunk_fwd_timed.argtypes = ([_P] + [_vp] * 10 + [_sz, _vp] +
                                      [ctypes.POINTER(_vp), ctypes.POINTER(ctypes.c_int)])
@@ -144,6 +151,10 @@ def gdn_chunk_fwd_workspace_size(problem):
 
 def gdn_chunk_bwd_workspace_size(problem):
     return int(_lib.gdn_chunk_bwd_workspace_size(ctypes.byref(problem)))
+
+
+def gdn_chunk_bwd_recompute_workspace_size(problem):
+    return int(_lib.gdn_chunk_bwd_recompute_workspace_size(ctypes.byref(problem)))
 
 
 def _check(status, where):
@@ -225,6 +236,29 @@ def gdn_chunk_bwd(problem, q, k, v, g, beta, saved, dO, dhT, dq, dk, dv, dg, dbe
     _check(st, "gdn_chunk_bwd")
 
 
+def gdn_chunk_bwd_recompute(problem, q, k, v, g, beta, h0, dO, dhT, dq, dk, dv, dg, dbeta, dh0,
+                            workspace, stream=None):
+    bf, f32 = torch.bfloat16, torch.float32
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.gdn_chunk_bwd_recompute(
+        ctypes.byref(problem), _ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"),
+        _ptr(g, f32, "g"), _ptr(beta, f32, "beta"), _ptr(h0, f32, "h0"),
+        _ptr(dO, bf, "dO"), _ptr(dhT, f32, "dhT"), _ptr(dq, bf, "dq"), _ptr(dk, bf, "dk"),
+        _ptr(dv, bf, "dv"), _ptr(dg, f32, "dg"), _ptr(dbeta, f32, "dbeta"),
+        _ptr(dh0, f32, "dh0"), _ptr(workspace, None, "workspace"), ws_bytes, _stream(stream))
+    _check(st, "gdn_chunk_bwd_recompute")
+
+
+def gdn_chunk_transition(problem, q, k, v, g, beta, M, s, workspace, stream=None):
+    bf, f32 = torch.bfloat16, torch.float32
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.gdn_chunk_transition(
+        ctypes.byref(problem), _ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"),
+        _ptr(g, f32, "g"), _ptr(beta, f32, "beta"), _ptr(M, f32, "M"), _ptr(s, f32, "s"),
+        _ptr(workspace, None, "workspace"), ws_bytes, _stream(stream))
+    _check(st, "gdn_chunk_transition")
+
+
 def gdn_recurrent_step(N, H, HV, K, V, scale, q, k, v, a, b, A_log, dt_bias, state_pool, slots,
                        ssm_state_indices, indices_host, o, stream=None):
     bf, f32 = torch.bfloat16, torch.float32
@@ -301,6 +335,43 @@ def chunk_bwd(q, k, v, g, beta, cu_seqlens, saved, dO, dhT=None, scale=0.0,
     gdn_chunk_bwd(p, q, k, v, g, beta, saved, dO, dhT, out["dq"], out["dk"], out["dv"],
                   out["dg"], out["dbeta"], out["dh0"], ws, stream)
     return out
+
+
+def chunk_bwd_recompute(q, k, v, g, beta, cu_seqlens, dO, h0=None, dhT=None, scale=0.0,
+                        cu_seqlens_host=None, want_dh0=True, stream=None):
+    """Allocate gradients and workspace and run gdn_chunk_bwd_recompute (no saved
+    buffer: the per-chunk states are rebuilt from h0). Returns the dict of chunk_bwd."""
+    T, H, _ = q.shape
+    HV = v.shape[1]
+    N = cu_seqlens.numel() - 1
+    p = make_problem(N, T, H, HV, cu_seqlens, cu_seqlens_host, scale)
+    dev = q.device
+    out = dict(
+        dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+        dg=torch.empty(T, HV, dtype=torch.float32, device=dev),
+        dbeta=torch.empty(T, HV, dtype=torch.float32, device=dev),
+        dh0=torch.empty(N, HV, 128, 128, dtype=torch.float32, device=dev) if want_dh0 else None,
+    )
+    ws = _ws(gdn_chunk_bwd_recompute_workspace_size(p), dev)
+    gdn_chunk_bwd_recompute(p, q, k, v, g, beta, h0, dO, dhT, out["dq"], out["dk"], out["dv"],
+                            out["dg"], out["dbeta"], out["dh0"], ws, stream)
+    return out
+
+
+def chunk_transition(q, k, v, g, beta, cu_seqlens, scale=0.0, cu_seqlens_host=None,
+                     stream=None):
+    """Allocate M [N, HV, 128, 128] and s [N, HV, 128, 128] (fp32) and run
+    gdn_chunk_transition: each sequence's end state is S_0 @ M + s."""
+    T, H, _ = q.shape
+    HV = v.shape[1]
+    N = cu_seqlens.numel() - 1
+    p = make_problem(N, T, H, HV, cu_seqlens, cu_seqlens_host, scale)
+    dev = q.device
+    M = torch.empty(N, HV, 128, 128, dtype=torch.float32, device=dev)
+    s = torch.empty(N, HV, 128, 128, dtype=torch.float32, device=dev)
+    ws = _ws(gdn_chunk_fwd_workspace_size(p), dev)
+    gdn_chunk_transition(p, q, k, v, g, beta, M, s, ws, stream)
+    return M, s
 
 
 def recurrent_step(q, k, v, a, b, A_log, dt_bias, state_pool, ssm_state_indices,

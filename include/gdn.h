@@ -108,6 +108,9 @@ size_t gdn_chunk_saved_size(const gdn_problem* p);
  * 256-byte aligned, used only during the call, and need not be zeroed. */
 size_t gdn_chunk_fwd_workspace_size(const gdn_problem* p);
 size_t gdn_chunk_bwd_workspace_size(const gdn_problem* p);
+/* Workspace bytes of gdn_chunk_bwd_recompute: the backward's workspace plus
+ * room for the per-chunk states it rebuilds (gdn_chunk_saved_size). */
+size_t gdn_chunk_bwd_recompute_workspace_size(const gdn_problem* p);
 
 /* Chunked forward.
  *   q, k      bf16 [T, H, K]
@@ -127,8 +130,8 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_problem* p);
  *             gdn_chunk_bwd of the same build reads them.
  * A sequence of length 0 gets hT = h0 (or 0). T = 0 is valid: nothing is
  * read from the token tensors and hT = h0 (or 0).
- * Errors: GDN_ERR_NULL (p, q, k, v, g, beta, o, cu_seqlens when T > 0, or
- * workspace), GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_SEQLENS,
+ * Errors: GDN_ERR_NULL (p, or q, k, v, g, beta, o, cu_seqlens when T > 0),
+ * GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_SEQLENS,
  * GDN_ERR_WORKSPACE, GDN_ERR_ALIGN, GDN_ERR_HIP. */
 int gdn_chunk_fwd(const gdn_problem* p,
                   const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -185,6 +188,50 @@ int gdn_chunk_bwd(const gdn_problem* p,
                   uint16_t* dq, uint16_t* dk, uint16_t* dv,
                   float* dg, float* dbeta, float* dh0,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward that recomputes the per-chunk states instead of reading them from
+ * a `saved` buffer (the recompute-state form of the Cake page "[Cake 1/13]
+ * gdn", miles-ext-kernels PR #1, variant routing and its recompute-state
+ * switch): the forward then needs no `saved` buffer at all. Same arguments as
+ * gdn_chunk_bwd with `saved` replaced by
+ *   h0        fp32 [N, HV, V, K] the forward's initial states, or NULL (zero)
+ * and a workspace of gdn_chunk_bwd_recompute_workspace_size(p) bytes. It
+ * reruns the forward's WY pass and state scan (without the output) into the
+ * workspace, then runs the backward; the gradients equal those of
+ * gdn_chunk_fwd(saved) + gdn_chunk_bwd bit for bit.
+ * Errors: as gdn_chunk_bwd. */
+int gdn_chunk_bwd_recompute(const gdn_problem* p,
+                            const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const float* g, const float* beta, const float* h0,
+                            const uint16_t* dO, const float* dhT,
+                            uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                            float* dg, float* dbeta, float* dh0,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Local transition of each sequence of the pack: the piece of a context-
+ * parallel forward that one GPU computes on its share of a long sequence
+ * (the maxtext page "Qwen3.5-397B RL trainer on 128 v7x", the commit adding
+ * the gdn_cp_m_scan forward transition product: the product of the chunk
+ * transitions e^gamma_L I - K_bwd^T W, and the end state from a zero start).
+ * For every start state S_0 [V, K] the sequence's end state is
+ *   S_end = S_0 M + s
+ * with
+ *   M         fp32 [N, HV, K, K] (row j, column k: M[n][hv][j][k])
+ *   s         fp32 [N, HV, V, K] the end state from S_0 = 0
+ * both written, never read. A length-0 sequence gets M = I and s = 0. Same
+ * p, q, k, v, g, beta and workspace (gdn_chunk_fwd_workspace_size) as
+ * gdn_chunk_fwd; no output o is produced. A rank of a context-parallel run
+ * combines the (M, s) of the ranks before it into its start state and then
+ * calls gdn_chunk_fwd from that state; the backward mirrors it with
+ * gdn_chunk_bwd, whose dh0 is linear in dhT (dh0 = dhT M^T + dh0 at dhT = 0).
+ * Errors: GDN_ERR_NULL (p, q, k, v, g, beta when T > 0, M and s when N > 0),
+ * GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_SEQLENS,
+ * GDN_ERR_WORKSPACE, GDN_ERR_ALIGN, GDN_ERR_HIP. */
+int gdn_chunk_transition(const gdn_problem* p,
+                         const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const float* g, const float* beta,
+                         float* M, float* s,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Per-kernel timing, for measurement tools. Same as gdn_chunk_fwd /
  * gdn_chunk_bwd, plus `events`: 2 * GDN_MAX_STAGES hipEvent_t handles created

@@ -37,6 +37,12 @@ What it computes, and where the pages define it
   serving-path section and the paged-state continuity results). The pages
   leave open what a sequence with the null index does; here it runs from a
   zero state and its end state is dropped.
+* Transition (one GPU's share of a context-parallel forward). Over a
+  sequence the end state is affine in the start state, S_end = S_0 M + s,
+  where M is the product, in token order, of the per-token maps
+  e^{g_t} (I - beta_t k_t k_t^T) (K x K) and s is the end state from a zero
+  start (the maxtext page "Qwen3.5-397B RL trainer on 128 v7x", the commit
+  adding the gdn_cp_m_scan transition product and pass 1's end state).
 * Backward. The manual adjoint of the recurrence, taken in reverse token
   order, gives dq, dk, dv, dg, dbeta and dh0 (the gradient set required by
   the cake_gdn page, miles PR #3597, "Summary" and "Tests").
@@ -301,3 +307,26 @@ def paged_forward(q, k, v, g, beta, cu_seqlens, state_pool, ssm_state_indices,
     o, hT = forward(q, k, v, g, beta, cu_seqlens, h0=h0, scale=scale)
     pool[idx[live]] = hT[live]
     return o, pool
+
+
+def transition(q, k, v, g, beta, cu_seqlens, scale=None):
+    """Per sequence and value head, M [K, K] and s [V, K] with S_end = S_0 @ M + s.
+
+    M multiplies the token maps e^{g_t} (I - beta_t k_t k_t^T) in token order;
+    s is the forward's end state from a zero start. A sequence without tokens
+    gets M = I and s = 0. Returns (M [N, HV, K, K], s [N, HV, V, K]) in float64.
+    """
+    q, k, v, g, beta, cu, hmap, scale, qt, kh = _prepare(q, k, v, g, beta, cu_seqlens, scale)
+    T, HV, V = v.shape
+    K = q.shape[2]
+    N = cu.size - 1
+    M = np.broadcast_to(np.eye(K), (N, HV, K, K)).copy()
+    eye = np.eye(K)
+    for n in range(N):
+        for t in range(cu[n], cu[n + 1]):
+            kt = kh[t]                                        # [HV, K]
+            step = np.exp(g[t])[:, None, None] * (
+                eye[None] - beta[t][:, None, None] * kt[:, :, None] * kt[:, None, :])
+            M[n] = M[n] @ step
+    _, s = forward(q, k, v, g, beta, cu, None, scale)
+    return M, s

@@ -202,3 +202,41 @@ def test_paged_forward_index_rules_on_the_host_copy(G):
     assert paged(G, p, host=[1, 8]) == 5      # past the pool
     assert paged(G, p, host=[3, 3]) == 5      # one block for two sequences
     assert paged(G, p, host=[-2, 9], idx=FAKE, pool=None) == 1   # null checks come first
+
+
+def transition(G, p, ws_bytes=1 << 40, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, M=FAKE, s=FAKE, ws=FAKE)
+    args.update(over)
+    return G._lib.gdn_chunk_transition(ctypes.byref(p), *[args[n] for n in (
+        "q", "k", "v", "g", "beta", "M", "s", "ws")], ws_bytes, None)
+
+
+def bwd_recompute(G, p, ws_bytes=1 << 40, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, dO=FAKE, dhT=None,
+                dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, dbeta=FAKE, dh0=None, ws=FAKE)
+    args.update(over)
+    return G._lib.gdn_chunk_bwd_recompute(ctypes.byref(p), *[args[n] for n in (
+        "q", "k", "v", "g", "beta", "h0", "dO", "dhT", "dq", "dk", "dv", "dg", "dbeta",
+        "dh0", "ws")], ws_bytes, None)
+
+
+def test_transition_rejects_bad_arguments(G):
+    p = problem(G)
+    assert transition(G, problem(G, K=64)) == 3
+    assert transition(G, problem(G, cu_host=(0, 70, 131))) == 4
+    for name in ("q", "k", "v", "g", "beta", "M", "s"):
+        assert transition(G, p, **{name: None}) == 1, name
+    assert transition(G, p, M=FAKE_MISALIGNED) == 8
+    assert transition(G, p, ws=None) == 6
+    assert transition(G, p, ws_bytes=G.gdn_chunk_fwd_workspace_size(p) - 1) == 6
+
+
+def test_recomputing_backward_rejects_bad_arguments(G):
+    p = problem(G)
+    need = G.gdn_chunk_bwd_recompute_workspace_size(p)
+    assert need == G.gdn_chunk_bwd_workspace_size(p) + G.gdn_chunk_saved_size(p)
+    assert bwd_recompute(G, p, ws_bytes=need - 1) == 6
+    assert bwd_recompute(G, problem(G, V=64)) == 3
+    for name in ("q", "k", "v", "g", "beta", "dO", "dq", "dk", "dv", "dg", "dbeta"):
+        assert bwd_recompute(G, p, **{name: None}) == 1, name
+    assert bwd_recompute(G, p, h0=FAKE_MISALIGNED) == 8

@@ -79,7 +79,17 @@ def _paged_writes_the_start_state(q, k, v, g, beta, cu, pool, idx, init=None, sc
     return o, new
 
 
+_transition = R.transition
+
+
+def _transition_reverse_order(q, k, v, g, beta, cu, scale=None):
+    M, s = _transition(q, k, v, g, beta, cu, scale)
+    return np.swapaxes(M, -1, -2), s
+
+
 MUTATIONS = {
+    "transition product transposed (reverse token order)": ("transition",
+                                                            _transition_reverse_order),
     "paged: fresh sequences resume from their block": ("paged_forward", _paged_ignores_fresh_flags),
     "paged: end states not written back": ("paged_forward", _paged_drops_end_states),
     "paged: start state written back": ("paged_forward", _paged_writes_the_start_state),
@@ -103,6 +113,7 @@ PINS = [
     lambda c: P.test_decode_is_one_recurrence_step_with_the_fused_gates(),
     lambda c: P.test_paged_prefix_then_continuation_equals_one_pass(),
     lambda c: P.test_paged_fresh_resumed_and_null_sequences(),
+    lambda c: P.test_transition_reproduces_the_end_state_of_any_start_state(),
 ]
 
 

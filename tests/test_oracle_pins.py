@@ -435,3 +435,54 @@ def test_paged_rejects_bad_active_indices():
     with pytest.raises(ValueError):
         R.paged_forward(q, k, v, g, beta, cu, pool, [2, 6])
     R.paged_forward(q, k, v, g, beta, cu, pool, [0, 0])
+
+
+# ---------------------------------------------------------------- transition (CP share)
+def test_transition_reproduces_the_end_state_of_any_start_state():
+    rng = np.random.default_rng(71)
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, [5, 70, 0, 131], H=2, HV=4, K=8, V=6,
+                                           g_scale=0.2)
+    M, s = R.transition(q, k, v, g, beta, cu)
+    _, hT = R.forward(q, k, v, g, beta, cu, S0)
+    assert rel_err(np.einsum("nhvj,nhjk->nhvk", S0, M) + s, hT) < 1e-12
+    _, hz = R.forward(q, k, v, g, beta, cu)
+    assert np.array_equal(s, hz)
+    assert np.array_equal(M[2], np.broadcast_to(np.eye(8), (4, 8, 8)))   # no tokens
+    assert np.array_equal(s[2], np.zeros_like(s[2]))
+
+
+def test_transition_equals_the_chunk_transition_product():
+    """The product of the chunk maps e^gamma_L I - K_bwd^T W (the maxtext page,
+    gdn_cp_m_scan commit) equals the token product, transposed to the S form."""
+    rng = np.random.default_rng(72)
+    q, k, v, g, beta, cu, _ = rand_inputs(rng, [150], H=1, HV=2, K=8, V=8, g_scale=0.2)
+    M, _ = R.transition(q, k, v, g, beta, cu)
+    qt, kh, vv = chunked._normed(q, k, v, 1, 2, None)
+    for hv in range(2):
+        Mh = np.eye(8)
+        for c0 in range(0, 150, 64):
+            c1 = min(c0 + 64, 150)
+            m = chunked._chunk_terms(qt[c0:c1, hv], kh[c0:c1, hv], vv[c0:c1, hv], g[c0:c1, hv],
+                                     beta[c0:c1, hv])
+            Mh = (m["gL"] * np.eye(8) - m["Kbwd"].T @ m["W"]) @ Mh
+        assert rel_err(Mh.T, M[0, hv]) < 1e-12
+
+
+def test_transition_of_two_segments_composes():
+    rng = np.random.default_rng(73)
+    q, k, v, g, beta, cu, _ = rand_inputs(rng, [90], H=1, HV=2, K=6, V=5, g_scale=0.3)
+    M, s = R.transition(q, k, v, g, beta, cu)
+    a, b = slice(0, 37), slice(37, 90)
+    M1, s1 = R.transition(q[a], k[a], v[a], g[a], beta[a], [0, 37])
+    M2, s2 = R.transition(q[b], k[b], v[b], g[b], beta[b], [0, 53])
+    assert rel_err(M1[0] @ M2[0], M[0]) < 1e-12
+    assert rel_err(np.einsum("hvj,hjk->hvk", s1[0], M2[0]) + s2[0], s[0]) < 1e-12
+
+
+def test_transition_without_writes_is_pure_decay():
+    rng = np.random.default_rng(74)
+    q, k, v, g, beta, cu, _ = rand_inputs(rng, [40], H=1, HV=3, K=4, V=4)
+    M, s = R.transition(q, k, v, g, np.zeros_like(beta), cu)
+    for hv in range(3):
+        assert rel_err(M[0, hv], np.exp(g[:, hv].sum()) * np.eye(4)) < 1e-12
+    assert np.array_equal(s, np.zeros_like(s))
