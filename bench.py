@@ -214,6 +214,60 @@ def secondary(h, stream, steps, warmup):
                  "hbm_frac": round(gbs * 1e9 / PEAK_HBM, 4)}
     out.update(paged_prefill(h, stream, steps, warmup))
     out.update(recompute_and_transition(h, stream, steps, warmup))
+    out.update(short_conv(h, stream, steps, warmup))
+    return out
+
+
+def short_conv(h, stream, steps, warmup):
+    """The short convolution at the fwd+bwd pack's channels (2 x 8192 tokens,
+    8192 channels, width 4, SiLU) against the HBM roofline, its decode update
+    (256 rows, pool of 512) and its paged prefill (8 x 512 tokens, 4096
+    channels, pool of 64)."""
+    import torch
+    from chunked_gated_delta_04_amd import gdn, synth
+    name = "conv_2x8192_c8192_w4"
+    inp = synth.workload_inputs(name)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    T, C = inp["x"].shape
+    W = inp["weight"].shape[1]
+    p = gdn.make_conv_problem(2, T, C, W, d["cu_seqlens"], inp["cu_seqlens"], "silu")
+    y = torch.empty_like(d["x"])
+    ms_f = time_call(h, stream, lambda: gdn.gdn_conv_fwd(p, d["x"], d["weight"], None, None, y,
+                                                         None, stream), steps, warmup)
+    dx = torch.empty_like(d["x"])
+    dw = torch.empty(C, W, dtype=torch.float32, device="cuda")
+    ws = torch.empty(gdn.gdn_conv_bwd_workspace_size(p), dtype=torch.uint8, device="cuda")
+    ms_b = time_call(h, stream, lambda: gdn.gdn_conv_bwd(
+        p, d["x"], d["weight"], None, None, d["dy"], dx, dw, None, None, ws, stream),
+        steps, warmup)
+    row = T * C * 2
+    bf, bb = 2 * row + C * W * 2, 3 * row + C * W * 2 + C * W * 4
+    out = {name + "_fwd": {"ms": round(ms_f, 4), "algorithmic_bytes": bf,
+                           "achieved_GBps": round(bf / (ms_f * 1e-3) / 1e9, 1),
+                           "hbm_frac": round(bf / (ms_f * 1e-3) / PEAK_HBM, 4)},
+           name + "_bwd": {"ms": round(ms_b, 4), "algorithmic_bytes": bb,
+                           "achieved_GBps": round(bb / (ms_b * 1e-3) / 1e9, 1),
+                           "hbm_frac": round(bb / (ms_b * 1e-3) / PEAK_HBM, 4)}}
+    del d, y, dx, ws
+    pool, idx = synth.conv_pool_inputs(256, 8192, 4, slots=512, n_null=16, seed=synth.BASE_SEED + 7)
+    x1 = synth.conv_inputs([256], 8192, 4, seed=synth.BASE_SEED + 8)
+    pd, idd = pool.cuda(), idx.cuda()
+    xd, wd = x1["x"].cuda(), x1["weight"].cuda()
+    yd = torch.empty_like(xd)
+    ms_u = time_call(h, stream, lambda: gdn.gdn_conv_update(
+        256, 8192, 4, "silu", xd, wd, None, pd, 512, idd, None, yd, stream), steps, warmup)
+    out["conv_update_256_c8192_w4_pool512"] = {"ms": round(ms_u, 4)}
+    lens = [512] * 8
+    xp = synth.conv_inputs(lens, 4096, 4, seed=synth.BASE_SEED + 9)
+    pool, idx = synth.conv_pool_inputs(8, 4096, 4, slots=64, n_null=0, seed=synth.BASE_SEED + 10)
+    init = torch.tensor([1, 0] * 4, dtype=torch.int32, device="cuda")
+    cu = xp["cu_seqlens"]
+    pp = gdn.make_conv_problem(8, 4096, 4096, 4, cu.cuda(), cu, "silu")
+    xpd, wpd, ppd, ipd = xp["x"].cuda(), xp["weight"].cuda(), pool.cuda(), idx.cuda()
+    ypd = torch.empty_like(xpd)
+    ms_p = time_call(h, stream, lambda: gdn.gdn_conv_fwd_paged(
+        pp, xpd, wpd, None, ppd, 64, ipd, init, None, ypd, stream), steps, warmup)
+    out["conv_paged_8x512_c4096_w4_pool64"] = {"ms": round(ms_p, 4)}
     return out
 
 

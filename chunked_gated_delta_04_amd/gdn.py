@@ -33,6 +33,8 @@ EXPORTED = (
     "gdn_chunk_bwd_recompute_workspace_size",
     "gdn_chunk_fwd", "gdn_chunk_fwd_paged", "gdn_chunk_bwd", "gdn_chunk_bwd_recompute",
     "gdn_chunk_transition", "gdn_recurrent_step",
+    "gdn_conv_fwd", "gdn_conv_fwd_paged", "gdn_conv_bwd", "gdn_conv_bwd_workspace_size",
+    "gdn_conv_update",
     "gdn_chunk_fwd_timed", "gdn_chunk_bwd_timed", "gdn_stage_name",
 )
 GDN_MAX_STAGES = 8
@@ -43,6 +45,14 @@ class GdnProblem(ctypes.Structure):
         ("N", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
         ("HV", ctypes.c_int32), ("K", ctypes.c_int32), ("V", ctypes.c_int32),
         ("chunk", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p),
+    ]
+
+
+class GdnConvProblem(ctypes.Structure):
+    _fields_ = [
+        ("N", ctypes.c_int32), ("T", ctypes.c_int32), ("C", ctypes.c_int32),
+        ("W", ctypes.c_int32), ("activation", ctypes.c_int32),
         ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p),
     ]
 
@@ -83,6 +93,17 @@ _lib.gdn_chunk_fwd_timed.argtypes = ([_P] + [_vp] * 10 + [_sz, _vp] +
 _lib.gdn_chunk_bwd_timed.restype = ctypes.c_int
 _lib.gdn_chunk_bwd_timed.argtypes = ([_P] + [_vp] * 15 + [_sz, _vp] +
                                      [ctypes.POINTER(_vp), ctypes.POINTER(ctypes.c_int)])
+_CP = ctypes.POINTER(GdnConvProblem)
+_lib.gdn_conv_fwd.restype = ctypes.c_int
+_lib.gdn_conv_fwd.argtypes = [_CP] + [_vp] * 7
+_lib.gdn_conv_fwd_paged.restype = ctypes.c_int
+_lib.gdn_conv_fwd_paged.argtypes = [_CP] + [_vp] * 4 + [_i32] + [_vp] * 5
+_lib.gdn_conv_bwd_workspace_size.restype = _sz
+_lib.gdn_conv_bwd_workspace_size.argtypes = [_CP]
+_lib.gdn_conv_bwd.restype = ctypes.c_int
+_lib.gdn_conv_bwd.argtypes = [_CP] + [_vp] * 10 + [_sz, _vp]
+_lib.gdn_conv_update.restype = ctypes.c_int
+_lib.gdn_conv_update.argtypes = [_i32] * 4 + [_vp] * 4 + [_i32] + [_vp] * 4
 _lib.gdn_stage_name.restype = ctypes.c_char_p
 _lib.gdn_stage_name.argtypes = [ctypes.c_int, ctypes.c_int]
 _lib.gdn_recurrent_step.restype = ctypes.c_int
@@ -383,3 +404,124 @@ def recurrent_step(q, k, v, a, b, A_log, dt_bias, state_pool, ssm_state_indices,
     gdn_recurrent_step(N, H, HV, K, V, scale, q, k, v, a, b, A_log, dt_bias, state_pool,
                        state_pool.shape[0], ssm_state_indices, indices_host, o, stream)
     return o
+
+
+# ---------------------------------------------------------------- short convolution
+_ACT = {None: 0, "none": 0, "silu": 1}
+
+
+def make_conv_problem(N, T, C, W, cu_seqlens, cu_seqlens_host=None, activation="silu"):
+    """Descriptor of one short-convolution call (cu_seqlens: int32 device [N+1];
+    cu_seqlens_host: optional int32 CPU copy, kept alive by the caller)."""
+    p = GdnConvProblem()
+    p.N, p.T, p.C, p.W = N, T, C, W
+    p.activation = _ACT[activation]
+    p.cu_seqlens = _ptr(cu_seqlens, torch.int32, "cu_seqlens")
+    if cu_seqlens_host is not None:
+        p.cu_seqlens_host = _host_ptr(cu_seqlens_host, "cu_seqlens_host")
+    return p
+
+
+def gdn_conv_fwd(problem, x, weight, bias, state_in, y, state_out, stream=None):
+    bf = torch.bfloat16
+    st = _lib.gdn_conv_fwd(ctypes.byref(problem), _ptr(x, bf, "x"), _ptr(weight, bf, "weight"),
+                           _ptr(bias, bf, "bias"), _ptr(state_in, bf, "state_in"),
+                           _ptr(y, bf, "y"), _ptr(state_out, bf, "state_out"), _stream(stream))
+    _check(st, "gdn_conv_fwd")
+
+
+def gdn_conv_fwd_paged(problem, x, weight, bias, state_pool, slots, indices, has_initial_state,
+                       indices_host, y, stream=None):
+    bf, i32 = torch.bfloat16, torch.int32
+    st = _lib.gdn_conv_fwd_paged(
+        ctypes.byref(problem), _ptr(x, bf, "x"), _ptr(weight, bf, "weight"),
+        _ptr(bias, bf, "bias"), _ptr(state_pool, bf, "state_pool"), int(slots),
+        _ptr(indices, i32, "indices"), _ptr(has_initial_state, i32, "has_initial_state"),
+        _host_ptr(indices_host, "indices_host"), _ptr(y, bf, "y"), _stream(stream))
+    _check(st, "gdn_conv_fwd_paged")
+
+
+def gdn_conv_bwd_workspace_size(problem):
+    return int(_lib.gdn_conv_bwd_workspace_size(ctypes.byref(problem)))
+
+
+def gdn_conv_bwd(problem, x, weight, bias, state_in, dy, dx, dweight, dbias, dstate_in,
+                 workspace, stream=None):
+    bf, f32 = torch.bfloat16, torch.float32
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.gdn_conv_bwd(
+        ctypes.byref(problem), _ptr(x, bf, "x"), _ptr(weight, bf, "weight"),
+        _ptr(bias, bf, "bias"), _ptr(state_in, bf, "state_in"), _ptr(dy, bf, "dy"),
+        _ptr(dx, bf, "dx"), _ptr(dweight, f32, "dweight"), _ptr(dbias, f32, "dbias"),
+        _ptr(dstate_in, f32, "dstate_in"), _ptr(workspace, None, "workspace"), ws_bytes,
+        _stream(stream))
+    _check(st, "gdn_conv_bwd")
+
+
+def gdn_conv_update(N, C, W, activation, x, weight, bias, state_pool, slots, indices,
+                    indices_host, y, stream=None):
+    bf, i32 = torch.bfloat16, torch.int32
+    st = _lib.gdn_conv_update(
+        int(N), int(C), int(W), _ACT[activation], _ptr(x, bf, "x"), _ptr(weight, bf, "weight"),
+        _ptr(bias, bf, "bias"), _ptr(state_pool, bf, "state_pool"), int(slots),
+        _ptr(indices, i32, "indices"), _host_ptr(indices_host, "indices_host"), _ptr(y, bf, "y"),
+        _stream(stream))
+    _check(st, "gdn_conv_update")
+
+
+def conv_fwd(x, weight, bias, cu_seqlens, state_in=None, activation="silu",
+             cu_seqlens_host=None, want_state=True, stream=None):
+    """x [T, C] bf16, weight [C, W] bf16, bias [C] bf16 or None (device).
+    Returns (y [T, C] bf16, end states [N, C, W-1] bf16 or None)."""
+    T, C = x.shape
+    W = weight.shape[1]
+    N = cu_seqlens.numel() - 1
+    p = make_conv_problem(N, T, C, W, cu_seqlens, cu_seqlens_host, activation)
+    y = torch.empty_like(x)
+    so = torch.empty(N, C, W - 1, dtype=torch.bfloat16, device=x.device) if want_state else None
+    gdn_conv_fwd(p, x, weight, bias, state_in, y, so, stream)
+    return y, so
+
+
+def conv_fwd_paged(x, weight, bias, cu_seqlens, state_pool, indices, has_initial_state=None,
+                   indices_host=None, activation="silu", cu_seqlens_host=None, stream=None):
+    """Paged forward: state_pool [slots, C, W-1] bf16 is read and updated in place."""
+    T, C = x.shape
+    W = weight.shape[1]
+    N = cu_seqlens.numel() - 1
+    p = make_conv_problem(N, T, C, W, cu_seqlens, cu_seqlens_host, activation)
+    y = torch.empty_like(x)
+    gdn_conv_fwd_paged(p, x, weight, bias, state_pool, state_pool.shape[0], indices,
+                       has_initial_state, indices_host, y, stream)
+    return y
+
+
+def conv_bwd(x, weight, bias, cu_seqlens, dy, state_in=None, activation="silu",
+             cu_seqlens_host=None, want_dstate=True, stream=None):
+    """Returns dict dx [T, C] bf16, dweight [C, W] fp32, dbias [C] fp32 (None
+    without a bias), dstate [N, C, W-1] fp32 (None unless want_dstate)."""
+    T, C = x.shape
+    W = weight.shape[1]
+    N = cu_seqlens.numel() - 1
+    dev = x.device
+    p = make_conv_problem(N, T, C, W, cu_seqlens, cu_seqlens_host, activation)
+    out = dict(dx=torch.empty_like(x),
+               dweight=torch.empty(C, W, dtype=torch.float32, device=dev),
+               dbias=torch.empty(C, dtype=torch.float32, device=dev) if bias is not None else None,
+               dstate=torch.empty(N, C, W - 1, dtype=torch.float32, device=dev)
+               if want_dstate else None)
+    ws = _ws(gdn_conv_bwd_workspace_size(p), dev)
+    gdn_conv_bwd(p, x, weight, bias, state_in, dy, out["dx"], out["dweight"], out["dbias"],
+                 out["dstate"], ws, stream)
+    return out
+
+
+def conv_update(x, weight, bias, state_pool, indices, indices_host=None, activation="silu",
+                stream=None):
+    """One decode token per row; state_pool [slots, C, W-1] bf16 updated in place."""
+    N, C = x.shape
+    W = weight.shape[1]
+    y = torch.empty_like(x)
+    gdn_conv_update(N, C, W, activation, x, weight, bias, state_pool, state_pool.shape[0],
+                    indices, indices_host, y, stream)
+    return y

@@ -18,6 +18,11 @@ Recipes (the workloads the chunk and decode kernels are measured on):
                    dt_bias = 0 in fp32 per value head, pool 0.1 * N(0, 1) fp32,
                    indices: a random permutation of 1..slots-1, the first
                    rows of it, with some rows set to 0 (the null block).
+  short conv       x, dy ~ N(0, 1) bf16 [T, C]; weight ~ U(-1/sqrt(W), 1/sqrt(W))
+                   bf16 [C, W] (the default init of a depthwise conv layer);
+                   bias (when used) ~ U(-0.5, 0.5) bf16; carried states
+                   ~ N(0, 1) bf16 [N or slots, C, W - 1]; pool indices as for
+                   the decode step, 0 the null block.
   paged prefill    the chunk recipe without h0, a decode-style pool and
                    indices, and a has_initial_state mix of resumed (1) and
                    fresh (0) sequences.
@@ -131,6 +136,37 @@ def paged_inputs(lens, H, HV, slots, n_null, n_fresh, seed, K=K_DIM, V=V_DIM):
     return out
 
 
+def conv_inputs(lens, C, W, seed, bias=False, state=False, with_dy=False):
+    """Inputs of one short-convolution call on a varlen pack. Returns a dict of
+    CPU tensors: x [T, C] bf16, weight [C, W] bf16, bias [C] bf16 or None,
+    cu_seqlens [N+1] int32, state_in [N, C, W-1] bf16 or None, dy [T, C] bf16
+    when ``with_dy``."""
+    gen = torch.Generator().manual_seed(seed)
+    T, N = int(sum(lens)), len(lens)
+    bound = 1.0 / math.sqrt(W)
+    out = dict(
+        x=torch.randn(T, C, generator=gen).to(torch.bfloat16),
+        weight=torch.empty(C, W).uniform_(-bound, bound, generator=gen).to(torch.bfloat16),
+        bias=torch.empty(C).uniform_(-0.5, 0.5, generator=gen).to(torch.bfloat16) if bias else None,
+        cu_seqlens=cu_from_lengths(lens),
+        state_in=torch.randn(N, C, W - 1, generator=gen).to(torch.bfloat16) if state else None,
+    )
+    if with_dy:
+        out["dy"] = torch.randn(T, C, generator=gen).to(torch.bfloat16)
+    return out
+
+
+def conv_pool_inputs(N, C, W, slots, n_null, seed):
+    """A conv state pool [slots, C, W-1] bf16 ~ N(0, 1) and indices [N] int32:
+    the first N entries of a random permutation of 1..slots-1 with ``n_null``
+    random rows set to 0 (the null block)."""
+    gen = torch.Generator().manual_seed(seed)
+    pool = torch.randn(slots, C, W - 1, generator=gen).to(torch.bfloat16)
+    idx = torch.randperm(slots - 1, generator=gen)[:N] + 1
+    idx[torch.randperm(N, generator=gen)[:n_null]] = 0
+    return pool, idx.to(torch.int32)
+
+
 # The workloads, by name. Sizes as measured and parity-tested.
 WORKLOADS = {
     "fwd_1x256_h1": dict(kind="fwd", lens=[256], H=1, HV=1, h0_std=None, seed=BASE_SEED + 0),
@@ -144,6 +180,9 @@ WORKLOADS = {
                                         seed=BASE_SEED + 4),
     "paged_8x512_h8_hv16_pool64": dict(kind="paged", lens=[512] * 8, H=8, HV=16, slots=64,
                                        n_null=0, n_fresh=4, seed=BASE_SEED + 5),
+    # the short convolution over the q, k, v channels of the fwd+bwd pack
+    # (2 x 128 x 16 key-head channels + 128 x 32 value-head channels), width 4
+    "conv_2x8192_c8192_w4": dict(kind="conv", lens=[8192] * 2, C=8192, W=4, seed=BASE_SEED + 6),
 }
 
 
@@ -159,6 +198,8 @@ def workload_inputs(name):
     w = WORKLOADS[name]
     if w["kind"] == "decode":
         return decode_inputs(w["N"], w["H"], w["HV"], w["slots"], w["n_null"], w["seed"])
+    if w["kind"] == "conv":
+        return conv_inputs(w["lens"], w["C"], w["W"], w["seed"], with_dy=True)
     if w["kind"] == "paged":
         return paged_inputs(workload_lengths(name), w["H"], w["HV"], w["slots"], w["n_null"],
                             w["n_fresh"], w["seed"])

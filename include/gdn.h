@@ -287,6 +287,91 @@ int gdn_recurrent_step(int32_t N, int32_t H, int32_t HV, int32_t K, int32_t V, f
                        const int32_t* ssm_state_indices, const int32_t* indices_host,
                        uint16_t* o, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Causal short convolution (the depthwise convolution in front of the gated
+ * delta rule). Per channel c of C, for the tokens of each sequence preceded by
+ * its W - 1 carried inputs xe (the conv state, zero when none is given):
+ *   pre_t = bias[c] + sum_{i<W} weight[c][i] * xe[t - (W - 1) + i]
+ *   y_t   = silu(pre_t) = pre_t / (1 + e^-pre_t)   (activation 1) or pre_t (0)
+ * accumulated in fp32 from the bf16 inputs, y rounded to bf16. The state of a
+ * sequence is its last W - 1 inputs, [C, W - 1] in bf16. Definitions: the
+ * goldens page ("[WS1][CUDA][Qwen3-Next] C6: GDN decode-step goldens and
+ * recurrent/conv state contract", RL-Kernel PR #469, "What": the conv update
+ * golden with bias and SiLU, the state [num_blocks, dim, W - 1], the null
+ * block 0 and the error on a negative index); the cake_gdn page (miles PR
+ * #3597) for a conv weight gradient without atomics; the torchtitan PR #4389
+ * page for the paged convolution prefill.
+ * Layouts: x, y, dy, dx bf16 [T, C] (row-major, token rows); weight bf16
+ * [C, W]; bias bf16 [C] or NULL; states bf16 [N or slots, C, W - 1].
+ * Supported: 2 <= W <= 4, C a multiple of 4 (GDN_ERR_UNSUPPORTED otherwise).
+ * Token tensors must be 8-byte aligned (GDN_ERR_ALIGN). */
+typedef struct {
+  int32_t N;            /* sequences                                         */
+  int32_t T;            /* total tokens                                      */
+  int32_t C;            /* channels                                          */
+  int32_t W;            /* filter width                                      */
+  int32_t activation;   /* 0 none, 1 SiLU                                    */
+  const int32_t* cu_seqlens;       /* device [N + 1]                         */
+  const int32_t* cu_seqlens_host;  /* optional host copy, validated          */
+} gdn_conv_problem;
+
+/* Varlen forward. state_in [N, C, W - 1] or NULL (zero start); state_out
+ * [N, C, W - 1] or NULL (not written): each sequence's last W - 1 inputs,
+ * reaching into state_in when the sequence is shorter than W - 1.
+ * Errors: GDN_ERR_NULL (p, weight; x, y, cu_seqlens when T > 0),
+ * GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_SEQLENS, GDN_ERR_ALIGN,
+ * GDN_ERR_HIP. */
+int gdn_conv_fwd(const gdn_conv_problem* p, const uint16_t* x, const uint16_t* weight,
+                 const uint16_t* bias, const uint16_t* state_in, uint16_t* y,
+                 uint16_t* state_out, void* stream);
+
+/* Paged forward: the carried inputs come from, and the end states go back to,
+ * blocks of state_pool [slots, C, W - 1] (in place). Sequence n uses block
+ * indices[n] (device int32 [N]); index 0 is the null block: zero start,
+ * nothing written. has_initial_state (device int32 [N], nullable: all
+ * resume) selects a resumed (nonzero) or fresh (0, zero start) sequence.
+ * indices_host, optional: validated (GDN_ERR_INDEX for a negative index, one
+ * >= slots, or an active index used twice); without it the caller guarantees
+ * that, and a bad index is treated as the null block. Results equal
+ * gdn_conv_fwd with the states gathered and scattered, bit for bit.
+ * Errors: as gdn_conv_fwd, GDN_ERR_NULL for state_pool or indices when
+ * N > 0, GDN_ERR_SHAPE for slots < 0, GDN_ERR_INDEX. */
+int gdn_conv_fwd_paged(const gdn_conv_problem* p, const uint16_t* x, const uint16_t* weight,
+                       const uint16_t* bias, uint16_t* state_pool, int32_t slots,
+                       const int32_t* indices, const int32_t* has_initial_state,
+                       const int32_t* indices_host, uint16_t* y, void* stream);
+
+/* Workspace bytes of gdn_conv_bwd (0 on a bad problem). */
+size_t gdn_conv_bwd_workspace_size(const gdn_conv_problem* p);
+
+/* Backward of gdn_conv_fwd (same p, x, weight, bias, state_in):
+ *   dy        bf16 [T, C] cotangent of y
+ *   dx        bf16 [T, C]
+ *   dweight   fp32 [C, W]
+ *   dbias     fp32 [C] or NULL
+ *   dstate_in fp32 [N, C, W - 1] cotangent of state_in, or NULL
+ * The weight and bias gradients are sums over all tokens taken in a fixed
+ * order (per-tile partial sums, then two ordered passes): no atomics, the
+ * same bits on every call. Workspace: gdn_conv_bwd_workspace_size bytes,
+ * 16-byte aligned. Errors: as gdn_conv_fwd, GDN_ERR_NULL for dweight (and dy,
+ * dx when T > 0), GDN_ERR_WORKSPACE. */
+int gdn_conv_bwd(const gdn_conv_problem* p, const uint16_t* x, const uint16_t* weight,
+                 const uint16_t* bias, const uint16_t* state_in, const uint16_t* dy,
+                 uint16_t* dx, float* dweight, float* dbias, float* dstate_in,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Decode update: one token per row. x [N, C] bf16; row n uses block
+ * indices[n] of state_pool [slots, C, W - 1] (device int32 [N]): y_n from
+ * the block's W - 1 inputs and x_n, then the block shifts by one input (x_n
+ * enters last), in place. Index 0 (the null block): zero output row, no
+ * block touched. indices_host as for gdn_conv_fwd_paged. N = 0 is valid.
+ * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_INDEX,
+ * GDN_ERR_ALIGN, GDN_ERR_HIP. */
+int gdn_conv_update(int32_t N, int32_t C, int32_t W, int32_t activation, const uint16_t* x,
+                    const uint16_t* weight, const uint16_t* bias, uint16_t* state_pool,
+                    int32_t slots, const int32_t* indices, const int32_t* indices_host,
+                    uint16_t* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

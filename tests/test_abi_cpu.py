@@ -240,3 +240,83 @@ def test_recomputing_backward_rejects_bad_arguments(G):
     for name in ("q", "k", "v", "g", "beta", "dO", "dq", "dk", "dv", "dg", "dbeta"):
         assert bwd_recompute(G, p, **{name: None}) == 1, name
     assert bwd_recompute(G, p, h0=FAKE_MISALIGNED) == 8
+
+
+def conv_problem(G, N=2, T=130, C=64, W=4, act=1, cu_host=(0, 70, 130), dev=FAKE):
+    p = G.GdnConvProblem()
+    p.N, p.T, p.C, p.W, p.activation = N, T, C, W, act
+    p.cu_seqlens = dev
+    keep = None
+    if cu_host is not None:
+        keep = (ctypes.c_int32 * len(cu_host))(*cu_host)
+        p.cu_seqlens_host = ctypes.cast(keep, ctypes.c_void_p)
+    p._keep = keep
+    return p
+
+
+def conv_fwd(G, p, **over):
+    a = dict(x=FAKE, w=FAKE, b=None, si=None, y=FAKE, so=None)
+    a.update(over)
+    return G._lib.gdn_conv_fwd(ctypes.byref(p), a["x"], a["w"], a["b"], a["si"], a["y"], a["so"],
+                               None)
+
+
+def conv_bwd(G, p, ws_bytes=1 << 40, **over):
+    a = dict(x=FAKE, w=FAKE, b=None, si=None, dy=FAKE, dx=FAKE, dw=FAKE, db=None, ds=None,
+             ws=FAKE)
+    a.update(over)
+    return G._lib.gdn_conv_bwd(ctypes.byref(p), *[a[n] for n in (
+        "x", "w", "b", "si", "dy", "dx", "dw", "db", "ds", "ws")], ws_bytes, None)
+
+
+def test_conv_rejects_bad_problems(G):
+    for kw, status in ((dict(W=5), 3), (dict(W=1), 3), (dict(C=66), 3), (dict(act=2), 3),
+                       (dict(C=0), 2), (dict(N=-1), 2), (dict(N=0), 2),
+                       (dict(cu_host=(0, 70, 131)), 4), (dict(cu_host=(0, 90, 80)[:3]), 4)):
+        p = conv_problem(G, **kw)
+        assert conv_fwd(G, p) == status, kw
+        assert conv_bwd(G, p) == status, kw
+    assert G._lib.gdn_conv_fwd(None, FAKE, FAKE, None, None, FAKE, None, None) == 1
+
+
+def test_conv_null_alignment_and_workspace(G):
+    p = conv_problem(G)
+    for name in ("x", "w", "y"):
+        assert conv_fwd(G, p, **{name: None}) == 1, name
+    for name in ("x", "w", "dy", "dx", "dw"):
+        assert conv_bwd(G, p, **{name: None}) == 1, name
+    assert conv_fwd(G, p, x=FAKE + 4) == 8
+    assert conv_bwd(G, p, dx=FAKE + 2) == 8
+    need = G.gdn_conv_bwd_workspace_size(p)
+    assert need > 0 and conv_bwd(G, p, ws_bytes=need - 1) == 6 and conv_bwd(G, p, ws=None) == 6
+    q = conv_problem(G)
+    q.cu_seqlens = None
+    assert conv_fwd(G, q) == 1
+
+
+def test_conv_paged_and_update_index_rules(G):
+    p = conv_problem(G)
+
+    def paged(host, slots=8, **over):
+        a = dict(pool=FAKE, idx=FAKE)
+        a.update(over)
+        keep = (ctypes.c_int32 * len(host))(*host)
+        return G._lib.gdn_conv_fwd_paged(ctypes.byref(p), FAKE, FAKE, None, a["pool"], slots,
+                                         a["idx"], None, ctypes.cast(keep, ctypes.c_void_p),
+                                         FAKE, None)
+
+    assert paged([1, -1]) == 5 and paged([1, 8]) == 5 and paged([3, 3]) == 5
+    assert paged([0, 0], pool=None) == 1 and paged([0, 0], slots=-1) == 2
+
+    def upd(host, N=3, C=64, W=4, slots=8, **over):
+        a = dict(x=FAKE, w=FAKE, pool=FAKE, idx=FAKE, y=FAKE)
+        a.update(over)
+        keep = (ctypes.c_int32 * len(host))(*host)
+        return G._lib.gdn_conv_update(N, C, W, 1, a["x"], a["w"], None, a["pool"], slots,
+                                      a["idx"], ctypes.cast(keep, ctypes.c_void_p), a["y"], None)
+
+    assert upd([1, 0, -3]) == 5 and upd([1, 0, 8]) == 5 and upd([2, 0, 2]) == 5
+    assert upd([1, 0, 0], W=5) == 3 and upd([1, 0, 0], C=62) == 3
+    assert upd([1, 0, 0], N=0) == 0
+    for name in ("x", "w", "pool", "idx", "y"):
+        assert upd([1, 0, 2], **{name: None}) == 1, name
