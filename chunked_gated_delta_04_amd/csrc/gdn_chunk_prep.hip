@@ -88,7 +88,6 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t* __restr
 
 namespace {
 constexpr int KP = 136;  // LDS row pitch (bf16) of [64][128] tiles
-constexpr int TP = 72;   // LDS row pitch (bf16) of [128][64] tiles
 constexpr int FP = 68;   // LDS row pitch (fp32) of [64][64] tiles
 
 // lower-including 16x16 tile t (0..9) of a 64x64 matrix -> (row block, col block)
@@ -114,11 +113,13 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
   __shared__ __align__(16) uint16_t Ks[64 * KP];   // k^ rows (bf16)
   __shared__ __align__(16) uint16_t Qs[64 * KP];   // q~ rows (bf16)
   __shared__ __align__(16) float Ts[64 * FP];      // A (strictly lower), inverted in place into T
-  __shared__ __align__(16) uint16_t Xt[128 * TP];  // (beta e^gamma K^)^T, then (beta V)^T
-  __shared__ float gam[64], bet[64], eg[64], ebw[64];
+  __shared__ __align__(16) uint16_t Vs[64 * KP];   // v rows of the value head (bf16)
+  // gates of the value head; gam is the cumulative log-decay in base 2
+  __shared__ __align__(16) float gam[64], bet[64], eg[64], ebw[64], fw[64];
   __shared__ float Xs[3 * 256];  // solve scratch
 
-  // ---- 1. load and L2-normalise q, k rows (thread: row tid/4, 32 columns)
+  // ---- 1. load and L2-normalise q, k rows (thread: row tid/4, 32 columns);
+  //      one division per row, then products with the reciprocal
   {
     const int r = tid >> 2, sg0 = (tid & 3) * 4;
     uint4 kr[4], qr[4];
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     }
     sk = group_sum<4>(sk);
     sq = group_sum<4>(sq);
-    const float nk = sqrtf(sk + kNormEps), nq = sqrtf(sq + kNormEps);
+    const float rk = 1.f / sqrtf(sk + kNormEps), rq = scale / sqrtf(sq + kNormEps);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[j]);
@@ -155,8 +156,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
       uint32_t* qow = reinterpret_cast<uint32_t*>(&qo);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        kow[e] = pk2(bf2f(kw[e] & 0xffffu) / nk, bf2f(kw[e] >> 16) / nk);
-        qow[e] = pk2((bf2f(qw[e] & 0xffffu) / nq) * scale, (bf2f(qw[e] >> 16) / nq) * scale);
+        kow[e] = pk2(bf2f(kw[e] & 0xffffu) * rk, bf2f(kw[e] >> 16) * rk);
+        qow[e] = pk2(bf2f(qw[e] & 0xffffu) * rq, bf2f(qw[e] >> 16) * rq);
       }
       *reinterpret_cast<uint4*>(&Ks[r * KP + (sg0 + j) * 8]) = ko;
       *reinterpret_cast<uint4*>(&Qs[r * KP + (sg0 + j) * 8]) = qo;
@@ -169,7 +170,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     const int hv = h * G + jg;
     const size_t blk = (size_t)hv * NC + c;
 
-    // ---- 2. gates: gamma = inclusive cumsum of g inside the chunk
+    // ---- 2. gates: gamma = inclusive cumsum of g inside the chunk (kept in
+    //      base 2); the value rows go to LDS as they are
     if (wave == 0) {
       float gv = lane < L ? g[(size_t)(t0 + lane) * HV + hv] : 0.f;
       const float bv = lane < L ? beta[(size_t)(t0 + lane) * HV + hv] : 0.f;
@@ -178,18 +180,32 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
         const float y = __shfl_up(gv, off, 64);
         if (lane >= off) gv += y;
       }
-      gam[lane] = gv;
+      const float g2 = gv * kLog2e;
+      const float gl2 = __shfl(g2, L - 1, 64);
+      gam[lane] = g2;
       bet[lane] = bv;
-      const float gl = __shfl(gv, L - 1, 64);
-      eg[lane] = expf(gv);
-      ebw[lane] = lane < L ? expf(gl - gv) : 0.f;
-      if (lane == 0) out.gL[blk] = expf(gl);
+      const float e = exp2_fast(g2);
+      eg[lane] = e;
+      fw[lane] = bv * e;
+      ebw[lane] = lane < L ? exp2_fast(gl2 - g2) : 0.f;
+      if (lane == 0) out.gL[blk] = exp2_fast(gl2);
+    }
+    if (!kBwd) {
+      const int r = tid >> 2, sg0 = (tid & 3) * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (r < L)
+          x = *reinterpret_cast<const uint4*>(v + ((size_t)(t0 + r) * HV + hv) * kHead + (sg0 + j) * 8);
+        *reinterpret_cast<uint4*>(&Vs[r * KP + (sg0 + j) * 8]) = x;
+      }
     }
     __syncthreads();
 
-    // ---- 3. A (fp32, LDS) and P (bf16, global): 10 lower tiles of A, 16 tiles of P
+    // ---- 3. A (fp32, LDS: 10 lower tiles, 6 zero upper tiles) and P (bf16,
+    //      global: 16 tiles), 32 jobs over the 4 waves
     uint16_t* Pb = out.P + blk * (64 * 64);
-    for (int job = wave; job < 26; job += 4) {
+    for (int job = wave; job < 32; job += 4) {
       if (job < 10) {
         int ib, jb;
         lower_tile(job, ib, jb);
@@ -202,10 +218,17 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 16 * ib + 4 * kq + r;
-          Ts[i * FP + j] = i > j ? bet[i] * expf(gam[i] - gam[j]) * acc[r] : 0.f;
+          Ts[i * FP + j] = i > j ? bet[i] * exp2_fast(gam[i] - gam[j]) * acc[r] : 0.f;
         }
+      } else if (job < 16) {
+        // strictly upper 16 x 16 blocks: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+        const int u = job - 10;
+        const int ib = u < 3 ? 0 : u < 5 ? 1 : 2;
+        const int jb = u < 3 ? u + 1 : u < 5 ? u - 1 : 3;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ts[(16 * ib + 4 * kq + r) * FP + 16 * jb + li] = 0.f;
       } else {
-        const int pt = job - 10, ib = pt >> 2, jb = pt & 3;  // P tile (row block ib, col block jb)
+        const int pt = job - 16, ib = pt >> 2, jb = pt & 3;  // P tile (row block ib, col block jb)
         if (!kBwd) {
           // C = K^ Q~^T tile: C[4kq+r][li] = P-row i = 16 ib + li, cols j = 16 jb + 4kq + r
           f32x4 acc = zero4();
@@ -220,7 +243,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int j = 16 * jb + 4 * kq + r;
-            pv[r] = i >= j ? expf(gam[i] - gam[j]) * acc[r] : 0.f;
+            pv[r] = i >= j ? exp2_fast(gam[i] - gam[j]) * acc[r] : 0.f;
           }
           *reinterpret_cast<uint2*>(Pb + kcm(i, 16 * jb + 4 * kq, 64)) =
               pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
@@ -238,90 +261,56 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 16 * ib + 4 * kq + r;
-            pv[r] = i >= j ? expf(gam[i] - gam[j]) * acc[r] : 0.f;
+            pv[r] = i >= j ? exp2_fast(gam[i] - gam[j]) * acc[r] : 0.f;
           }
           *reinterpret_cast<uint2*>(Pb + kcm(j, 16 * ib + 4 * kq, 64)) =
               pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
         }
       }
     }
-    // zero the strictly upper blocks of T
-    for (int e = tid; e < 64 * 64; e += 256) {
-      const int i = e >> 6, j = e & 63;
-      if ((j >> 4) > (i >> 4)) Ts[i * FP + j] = 0.f;
-    }
     __syncthreads();
 
     // ---- 4. T = (I + A)^-1 in place
     invert_unit_lower_64(Ts, Xs, tid, 256);
 
-    // ---- 5. Xt = (beta e^gamma K^)^T  [k][tok]; Q_g and K_bwd to global
-    for (int e = tid; e < 128 * 8; e += 256) {
-      const int d = e >> 3, tg = e & 7;
-      uint4 o4;
-      uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int ta = 8 * tg + 2 * u, tb = ta + 1;
-        ow[u] = pk2(bet[ta] * eg[ta] * bf2f(Ks[ta * KP + d]), bet[tb] * eg[tb] * bf2f(Ks[tb * KP + d]));
-      }
-      *reinterpret_cast<uint4*>(&Xt[d * TP + 8 * tg]) = o4;
-    }
+    // ---- 5. Q_g and K_bwd to global. The transposed pieces (column chunks
+    //      of 8 tokens) come from the row tiles with transposing LDS reads:
+    //      a wave covers one token group tg and 64 consecutive features.
     {
       uint16_t* Qgb = out.Qg + blk * 8192;
       uint16_t* Kbb = out.Kb + blk * 8192;
-      if (!kBwd) {
-        // Q_g [tok][k] (row segments) and K_bwd^T [k][tok] (column gathers);
-        // consecutive threads write consecutive 16-byte chunks
-        for (int e = tid; e < 64 * 16; e += 256) {
-          const int sg = e >> 6, t = e & 63;
-          const uint4 x = *reinterpret_cast<const uint4*>(&Qs[t * KP + sg * 8]);
-          const uint32_t* xw = reinterpret_cast<const uint32_t*>(&x);
-          uint4 o4;
-          uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
+      const uint16_t* rowsrc = kBwd ? Ks : Qs;  // written as row segments
+      const float* rowf = kBwd ? ebw : eg;
+      const uint16_t* colsrc = kBwd ? Qs : Ks;  // written as column chunks
+      const float* colf = kBwd ? eg : ebw;
+      uint16_t* rowdst = kBwd ? Kbb : Qgb;
+      uint16_t* coldst = kBwd ? Qgb : Kbb;
+      for (int e = tid; e < 64 * 16; e += 256) {
+        const int sg = e >> 6, t = e & 63;
+        const uint4 x = *reinterpret_cast<const uint4*>(&rowsrc[t * KP + sg * 8]);
+        const uint32_t* xw = reinterpret_cast<const uint32_t*>(&x);
+        const float f = rowf[t];
+        uint4 o4;
+        uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            ow[u] = pk2(eg[t] * bf2f(xw[u] & 0xffffu), eg[t] * bf2f(xw[u] >> 16));
-          *reinterpret_cast<uint4*>(Qgb + kcm(t, sg * 8, 64)) = o4;
-        }
-        for (int e = tid; e < 128 * 8; e += 256) {
-          const int tg = e >> 7, d = e & 127;
-          uint4 o4;
-          uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
+        for (int u = 0; u < 4; ++u) ow[u] = pk2(f * bf2f(xw[u] & 0xffffu), f * bf2f(xw[u] >> 16));
+        *reinterpret_cast<uint4*>(rowdst + kcm(t, sg * 8, 64)) = o4;
+      }
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int ta = 8 * tg + 2 * u, tb = ta + 1;
-            ow[u] = pk2(ebw[ta] * bf2f(Ks[ta * KP + d]), ebw[tb] * bf2f(Ks[tb * KP + d]));
-          }
-          *reinterpret_cast<uint4*>(Kbb + kcm(d, 8 * tg, 128)) = o4;
-        }
-      } else {
-        // Q_g^T [k][tok] (column gathers) and K_bwd [tok][k] (row segments)
-        for (int e = tid; e < 128 * 8; e += 256) {
-          const int tg = e >> 7, d = e & 127;
-          uint4 o4;
-          uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int ta = 8 * tg + 2 * u, tb = ta + 1;
-            ow[u] = pk2(eg[ta] * bf2f(Qs[ta * KP + d]), eg[tb] * bf2f(Qs[tb * KP + d]));
-          }
-          *reinterpret_cast<uint4*>(Qgb + kcm(d, 8 * tg, 128)) = o4;
-        }
-        for (int e = tid; e < 64 * 16; e += 256) {
-          const int sg = e >> 6, t = e & 63;
-          const uint4 x = *reinterpret_cast<const uint4*>(&Ks[t * KP + sg * 8]);
-          const uint32_t* xw = reinterpret_cast<const uint32_t*>(&x);
-          uint4 o4;
-          uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            ow[u] = pk2(ebw[t] * bf2f(xw[u] & 0xffffu), ebw[t] * bf2f(xw[u] >> 16));
-          *reinterpret_cast<uint4*>(Kbb + kcm(t, sg * 8, 64)) = o4;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int e0 = 256 * i + 64 * wave;           // wave-uniform
+        const int tg = e0 >> 7, d0 = (e0 & 127) + 16 * kq;
+        const uint4 x = lds_col8(colsrc, KP, 8 * tg, d0, lane);
+        const uint32_t* xw = reinterpret_cast<const uint32_t*>(&x);
+        const float4 fa = *reinterpret_cast<const float4*>(&colf[8 * tg]);
+        const float4 fb = *reinterpret_cast<const float4*>(&colf[8 * tg + 4]);
+        const uint4 o4 = make_uint4(pk2(fa.x * bf2f(xw[0] & 0xffffu), fa.y * bf2f(xw[0] >> 16)),
+                                    pk2(fa.z * bf2f(xw[1] & 0xffffu), fa.w * bf2f(xw[1] >> 16)),
+                                    pk2(fb.x * bf2f(xw[2] & 0xffffu), fb.y * bf2f(xw[2] >> 16)),
+                                    pk2(fb.z * bf2f(xw[3] & 0xffffu), fb.w * bf2f(xw[3] >> 16)));
+        *reinterpret_cast<uint4*>(coldst + kcm(d0 + li, 8 * tg, 128)) = o4;
       }
     }
-    __syncthreads();
 
     // T and T^T in bf16 for the backward's gradient pass: chunk (kc, r) of each
     // holds row r, columns 8 kc .. 8 kc + 7
@@ -345,28 +334,34 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
       }
     }
 
-    // ---- 6. W: 32 tiles of 16x16 over 4 waves, contraction over the chunk (2 steps)
+    // ---- 6. W = (T diag(beta e^gamma)) K^: the factor scales T's columns as
+    //      T becomes an MFMA operand, K^ is read by columns from its row tile.
+    //      32 tiles of 16 x 16 over 4 waves, contraction over the chunk.
     {
       uint16_t* Wb = out.W + blk * 8192;
       for (int tt = wave; tt < 32; tt += 4) {
         if (!kBwd) {
-          // C = Xt T^T: C[4kq+r][li] = W[t = 16 tb + li][k = 16 db + 4kq + r]
+          // C = K^T (T')^T: C[4kq+r][li] = W[t = 16 tb + li][k = 16 db + 4kq + r]
           const int db = tt >> 2, tb = tt & 3;
           f32x4 acc = zero4();
 #pragma unroll
-          for (int s = 0; s < 2; ++s)
-            acc = mfma(ld8(&Xt[(16 * db + li) * TP + 32 * s + 8 * kq]),
-                       cvt8(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq]), acc);
+          for (int s = 0; s < 2; ++s) {
+            const uint4 kc = lds_col8(Ks, KP, 32 * s + 8 * kq, 16 * db, lane);
+            acc = mfma(__builtin_bit_cast(bf16x8, kc),
+                       cvt8s(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq], &fw[32 * s + 8 * kq]), acc);
+          }
           *reinterpret_cast<uint2*>(Wb + kcm(16 * tb + li, 16 * db + 4 * kq, 64)) =
               pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
         } else {
-          // C = T Xt^T: C[4kq+r][li] = W[t = 16 tb + 4kq + r][k = 16 db + li] -> W^T[k][t..t+3]
+          // C = T' K^: C[4kq+r][li] = W[t = 16 tb + 4kq + r][k = 16 db + li] -> W^T[k][t..t+3]
           const int tb = tt >> 3, db = tt & 7;
           f32x4 acc = zero4();
 #pragma unroll
-          for (int s = 0; s < 2; ++s)
-            acc = mfma(cvt8(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq]),
-                       ld8(&Xt[(16 * db + li) * TP + 32 * s + 8 * kq]), acc);
+          for (int s = 0; s < 2; ++s) {
+            const uint4 kc = lds_col8(Ks, KP, 32 * s + 8 * kq, 16 * db, lane);
+            acc = mfma(cvt8s(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq], &fw[32 * s + 8 * kq]),
+                       __builtin_bit_cast(bf16x8, kc), acc);
+          }
           *reinterpret_cast<uint2*>(Wb + kcm(16 * db + li, 16 * tb + 4 * kq, 128)) =
               pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
         }
@@ -374,40 +369,23 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     }
 
     if (!kBwd) {
-      // ---- 7. U = T diag(beta) V, written as U^T [v][tok]
-      __syncthreads();  // Xt is rewritten
-      {
-        const int r = tid >> 2, sg0 = (tid & 3) * 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint4 x = make_uint4(0, 0, 0, 0);
-          if (r < L) x = *reinterpret_cast<const uint4*>(v + ((size_t)(t0 + r) * HV + hv) * kHead +
-                                                           (sg0 + j) * 8);
-          const uint32_t* xw = reinterpret_cast<const uint32_t*>(&x);
-          const float br = bet[r];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int d = (sg0 + j) * 8 + 2 * e;
-            Xt[d * TP + r] = f2bf(br * bf2f(xw[e] & 0xffffu));
-            Xt[(d + 1) * TP + r] = f2bf(br * bf2f(xw[e] >> 16));
-          }
-        }
-      }
-      __syncthreads();
+      // ---- 7. U = (T diag(beta)) V, written as U^T [v][tok]
       uint16_t* Ub = out.U + blk * 8192;
       for (int tt = wave; tt < 32; tt += 4) {
-        // C = T Xt^T: C[4kq+r][li] = U[t = 16 tb + 4kq + r][v = 16 vb + li] -> U^T[v][t..t+3]
+        // C = T' V: C[4kq+r][li] = U[t = 16 tb + 4kq + r][v = 16 vb + li] -> U^T[v][t..t+3]
         const int tb = tt >> 3, vb = tt & 7;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-          acc = mfma(cvt8(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq]),
-                     ld8(&Xt[(16 * vb + li) * TP + 32 * s + 8 * kq]), acc);
+        for (int s = 0; s < 2; ++s) {
+          const uint4 vc = lds_col8(Vs, KP, 32 * s + 8 * kq, 16 * vb, lane);
+          acc = mfma(cvt8s(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq], &bet[32 * s + 8 * kq]),
+                     __builtin_bit_cast(bf16x8, vc), acc);
+        }
         *reinterpret_cast<uint2*>(Ub + kcm(16 * vb + li, 16 * tb + 4 * kq, 128)) =
             pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
       }
     }
-    __syncthreads();  // gates, A, T and Xt are rewritten for the next value head
+    __syncthreads();  // gates, A, T and V are rewritten for the next value head
   }
 }
 

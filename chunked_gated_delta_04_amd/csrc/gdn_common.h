@@ -94,6 +94,20 @@ __device__ __forceinline__ bf16x8 cvt8(const float* p) {
   return __builtin_bit_cast(bf16x8, make_uint4(pk2(a.x, a.y), pk2(a.z, a.w), pk2(b.x, b.y), pk2(b.z, b.w)));
 }
 
+// 8 fp32 values times 8 per-column factors, as a bf16 MFMA operand fragment
+__device__ __forceinline__ bf16x8 cvt8s(const float* p, const float* f) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  const float4 fa = *reinterpret_cast<const float4*>(f);
+  const float4 fb = *reinterpret_cast<const float4*>(f + 4);
+  return __builtin_bit_cast(bf16x8, make_uint4(pk2(a.x * fa.x, a.y * fa.y), pk2(a.z * fa.z, a.w * fa.w),
+                                               pk2(b.x * fb.x, b.y * fb.y), pk2(b.z * fb.z, b.w * fb.w)));
+}
+
+// log2(e): decays are kept as base-2 exponents so that e^x is one v_exp_f32
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // LDS transpose read (ds_read_b64_tr_b16, gfx950). Within each group of 16
