@@ -278,7 +278,7 @@ struct BwdLds {
     uint16_t Y1T[64 * BP];                  //   (dT T^T)^T
   } rw;
   float gam[64], bet[64], eg[64], ebw[64];
-  float nrm_k[64], nrm_q[64];
+  float inv_k[64], inv_q[64];  // 1 / |k|, 1 / |q| per token
   float rowF[2][64], colF[8][64];           // F = dP o P
   float rowG[2][64], rowB2[2][64];          // row terms of the key-column passes
   float rowB[2][64];                        // dbeta of U
@@ -363,10 +363,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int r = (tid >> 4) + 32 * j;
-      const float nk = sqrtf(sk[j] + kNormEps), nq = sqrtf(sq[j] + kNormEps);
+      const float ik = 1.f / sqrtf(sk[j] + kNormEps), iq = 1.f / sqrtf(sq[j] + kNormEps);
+      const float iqs = iq * scale;
       if (sg == 0) {
-        S.nrm_k[r] = nk;
-        S.nrm_q[r] = nq;
+        S.inv_k[r] = ik;
+        S.inv_q[r] = iq;
       }
       const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[j]);
       const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qr[j]);
@@ -375,11 +376,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       uint32_t* qow = reinterpret_cast<uint32_t*>(&qo);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint16_t k0 = f2bf(bf2f(kw[e] & 0xffffu) / nk), k1 = f2bf(bf2f(kw[e] >> 16) / nk);
-        const uint16_t q0 = f2bf((bf2f(qw[e] & 0xffffu) / nq) * scale);
-        const uint16_t q1 = f2bf((bf2f(qw[e] >> 16) / nq) * scale);
-        kow[e] = (uint32_t)k0 | ((uint32_t)k1 << 16);
-        qow[e] = (uint32_t)q0 | ((uint32_t)q1 << 16);
+        kow[e] = pk2(bf2f(kw[e] & 0xffffu) * ik, bf2f(kw[e] >> 16) * ik);
+        qow[e] = pk2(bf2f(qw[e] & 0xffffu) * iqs, bf2f(qw[e] >> 16) * iqs);
+        const uint16_t k0 = kow[e] & 0xffffu, k1 = kow[e] >> 16;
+        const uint16_t q0 = qow[e] & 0xffffu, q1 = qow[e] >> 16;
         const int d = sg * 8 + 2 * e;
         S.KsT[d * TP + r] = k0;
         S.KsT[(d + 1) * TP + r] = k1;
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         glsum += S.gl_part[w];
         hdsum += S.hd_part[w];
       }
-      x += glsum + expf(S.gam[L - 1]) * hdsum;
+      x += glsum + exp2_fast(S.gam[L - 1]) * hdsum;
     }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -518,11 +518,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         const float y = __shfl_up(gv, off, 64);
         if (lane >= off) gv += y;
       }
-      S.gam[lane] = gv;
+      const float g2 = gv * kLog2e;  // base-2 exponent
+      S.gam[lane] = g2;
       S.bet[lane] = bv;
-      const float gl = __shfl(gv, L - 1, 64);
-      S.eg[lane] = expf(gv);
-      S.ebw[lane] = lane < L ? expf(gl - gv) : 0.f;
+      const float gl2 = __shfl(g2, L - 1, 64);
+      S.eg[lane] = exp2_fast(g2);
+      S.ebw[lane] = lane < L ? exp2_fast(gl2 - g2) : 0.f;
     }
     __syncthreads();
 
@@ -544,7 +545,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
           for (int r = 0; r < 4; ++r) {
             const int i = 16 * tw + 4 * kq + r;
             if (i >= j) {
-              const float dpm = dp[r] * expf(S.gam[i] - S.gam[j]);
+              const float dpm = dp[r] * exp2_fast(S.gam[i] - S.gam[j]);
               const float f = dpm * qk[q2][r];
               pv[r] = dpm;
               rowp[r] += f;
@@ -863,7 +864,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
             const int i = 16 * tw + 4 * kq + r;
             if (i > j) {
               const float da_ = -acc[r];
-              const float dec = expf(S.gam[i] - S.gam[j]);
+              const float dec = exp2_fast(S.gam[i] - S.gam[j]);
               const float m_ = da_ * S.bet[i] * dec;
               const float e_ = m_ * kk[r];
               mv[r] = m_;
@@ -930,6 +931,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     const int tw = wave & 3, kh = wave >> 2;
     const int li = lane & 15, kq = lane >> 4;
     float dq_[4] = {0.f, 0.f, 0.f, 0.f}, dk_[4] = {0.f, 0.f, 0.f, 0.f};
+    float qh[4][4], kh_[4][4];  // q^, k^ of the thread's 16 elements (fp32)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -939,9 +941,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         float qv = 0.f, kv = 0.f;
         if (t < L) {
           const size_t off = ((size_t)(t0 + t) * H + h) * kHead + kc;
-          qv = bf2f(q[off]) / S.nrm_q[t];
-          kv = bf2f(k[off]) / S.nrm_k[t];
+          qv = bf2f(q[off]) * S.inv_q[t];
+          kv = bf2f(k[off]) * S.inv_k[t];
         }
+        qh[j][r] = qv;
+        kh_[j][r] = kv;
         dq_[r] += qv * scale * adq[j][r];
         dk_[r] += kv * adk[j][r];
       }
@@ -964,17 +968,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * tw + 4 * kq + r;
         const int kc = 16 * (4 * kh + j) + li;
-        float qv = 0.f, kv = 0.f;
-        if (t < L) {
-          const size_t off = ((size_t)(t0 + t) * H + h) * kHead + kc;
-          qv = bf2f(q[off]) / S.nrm_q[t];
-          kv = bf2f(k[off]) / S.nrm_k[t];
-        }
         const float dotq = S.dot_q[0][t] + S.dot_q[1][t];
         const float dotk = S.dot_k[0][t] + S.dot_k[1][t];
         const float dqh = scale * adq[j][r];
-        S.Hs[t * KP + kc] = f2bf((dqh - qv * dotq) / S.nrm_q[t]);
-        S.Ks[t * KP + kc] = f2bf((adk[j][r] - kv * dotk) / S.nrm_k[t]);
+        S.Hs[t * KP + kc] = f2bf((dqh - qh[j][r] * dotq) * S.inv_q[t]);
+        S.Ks[t * KP + kc] = f2bf((adk[j][r] - kh_[j][r] * dotk) * S.inv_k[t]);
       }
   }
   __syncthreads();
