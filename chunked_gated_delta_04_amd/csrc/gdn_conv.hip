@@ -80,15 +80,21 @@ __device__ __forceinline__ uint2 ld_row4(const uint16_t* p) {
   return *reinterpret_cast<const uint2*>(p);
 }
 
+// sigmoid with one v_exp_f32 and one v_rcp_f32 (about 1 ulp each); for
+// p -> -inf, e^-p overflows to inf and the reciprocal gives 0, never NaN
+__device__ __forceinline__ float sigmoid_fast(float p) {
+  return __builtin_amdgcn_rcpf(1.f + exp2_fast(-p * kLog2e));
+}
+
 template <bool kSilu>
 __device__ __forceinline__ float act(float p) {
-  return kSilu ? p / (1.f + expf(-p)) : p;
+  return kSilu ? p * sigmoid_fast(p) : p;
 }
 
 template <bool kSilu>
 __device__ __forceinline__ float act_grad(float p) {
   if (!kSilu) return 1.f;
-  const float s = 1.f / (1.f + expf(-p));
+  const float s = sigmoid_fast(p);
   return s * (1.f + p * (1.f - s));
 }
 
