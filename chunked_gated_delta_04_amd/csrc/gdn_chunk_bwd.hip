@@ -61,7 +61,8 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
   constexpr int VT = VB / 16;
   constexpr int SP = 136;
   constexpr int DP = 72;
-  static_assert(kChunk * (VB / 8) == 256 && VB * 8 == 256, "one 16-byte segment per thread");
+  constexpr int SPT = VB / 8;  // 16-byte dO segments per token row of the block
+  static_assert(kChunk * SPT <= 256 && VB * 8 <= 256, "at most one 16-byte segment per thread");
 
   const int b = blockIdx.x;
   const int xcd = b & 7, slot = b >> 3;
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
     uint4 dO;
     float gl;
   };
-  const int ot = tid >> 2, osg = tid & 3;  // dO segment of this thread
+  const int ot = tid / SPT, osg = tid % SPT;  // dO segment of this thread (ot < 64 holds one)
   // chunk bounds from the sequence's bounds (consecutive 64-token chunks)
   const int c_begin = seq_first[seq], c_end = seq_first[seq + 1];
   int bos = 0, eos = 0;
@@ -147,14 +148,14 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
         *reinterpret_cast<uint2*>(&Hs[(16 * vt + li) * SP + kk]) =
             pack4_bf16(dh[dt][vt][0], dh[dt][vt][1], dh[dt][vt][2], dh[dt][vt][3]);
       }
-    *reinterpret_cast<uint4*>(&Ot[ot * OP + 8 * osg]) = cur.dO;
+    if (ot < kChunk) *reinterpret_cast<uint4*>(&Ot[ot * OP + 8 * osg]) = cur.dO;
     __syncthreads();
     // dh' (gradient of this chunk's end state) as [v / 32][v % 32 / 8][k][v % 8],
     // read as columns of Hs with transposed reads (chunk e = 64 q + lane)
     {
-      uint16_t* dhb = bufs.dh + blk * (kHead * kHead) + vb * (kHead * VB);
+      uint16_t* dhb = bufs.dh + blk * (kHead * kHead) + v0 * kHead;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < VB / 16; ++i) {
         const int q = wave + 4 * i;
         *reinterpret_cast<uint4*>(dhb + 8 * (64 * q + lane)) =
             lds_col8(Hs, SP, 8 * (q >> 1), 64 * (q & 1) + 16 * kq, lane);
@@ -194,11 +195,13 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
     {
       uint16_t* dDT = bufs.dDT + blk * 8192;
       uint16_t* dDr = bufs.dD + blk * 8192;
-      const int sg = tid >> 5, vl = tid & 31;
-      *reinterpret_cast<uint4*>(dDT + kcm(v0 + vl, 8 * sg, kHead)) =
-          *reinterpret_cast<const uint4*>(&Es[vl * DP + 8 * sg]);
-      *reinterpret_cast<uint4*>(dDr + kcm(lane, v0 + 8 * wave, kChunk)) =
-          lds_col8(Es, DP, 8 * wave, 16 * kq, lane);
+      const int sg = tid / VB, vl = tid % VB;
+      if (tid < VB * 8)
+        *reinterpret_cast<uint4*>(dDT + kcm(v0 + vl, 8 * sg, kHead)) =
+            *reinterpret_cast<const uint4*>(&Es[vl * DP + 8 * sg]);
+      if (wave < VB / 8)
+        *reinterpret_cast<uint4*>(dDr + kcm(lane, v0 + 8 * wave, kChunk)) =
+            lds_col8(Es, DP, 8 * wave, 16 * kq, lane);
     }
 
     // 3. dh <- e^gamma_L dh + Q_g^T dO - W^T dD; wave w owns key rows 32 w .. 32 w + 31
@@ -298,7 +301,7 @@ __device__ __forceinline__ float4 ld4_bf16(const uint16_t* p) {  // 4 bf16 -> fp
 // [v / 32][v % 32 / 8][k][v % 8]
 __device__ __forceinline__ int state_pos(int e) {
   const int vb = e >> 9, vg = (e >> 7) & 3, kk = e & 127;
-  return kk * KP + vb * kScanVB + vg * 8;
+  return kk * KP + vb * 32 + vg * 8;
 }
 __device__ __forceinline__ float dot8u(const uint4& a, const uint4& b) {  // bf16 pairs
   const uint32_t* x = reinterpret_cast<const uint32_t*>(&a);

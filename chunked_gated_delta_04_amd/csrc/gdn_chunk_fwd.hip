@@ -163,10 +163,10 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
       // h[k = e % 128][8 (e / 128) ..], read as columns of Ss with transposed
       // reads; consecutive lanes write consecutive chunks
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < VB / 16; ++i) {
         const int q = wave + 4 * i;
         const uint4 x = lds_col8(Ss, SP, 8 * (q >> 1), 64 * (q & 1) + 16 * kq, lane);
-        *reinterpret_cast<uint4*>(sv + vb * (kHead * VB) + 8 * (64 * q + lane)) = x;
+        *reinterpret_cast<uint4*>(sv + v0 * kHead + 8 * (64 * q + lane)) = x;
       }
     }
 
@@ -192,8 +192,9 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     if constexpr (kSave) {
       // D [tok][v] in the chunk-major tile layout: wave w writes the chunks of
       // value columns v0 + 8 w .. + 7, lane = token, read as columns of D^T
-      *reinterpret_cast<uint4*>(sv + kSavedH + kcm(lane, v0 + 8 * wave, kChunk)) =
-          lds_col8(Ds, DP, 8 * wave, 16 * kq, lane);
+      if (wave < VB / 8)
+        *reinterpret_cast<uint4*>(sv + kSavedH + kcm(lane, v0 + 8 * wave, kChunk)) =
+            lds_col8(Ds, DP, 8 * wave, 16 * kq, lane);
     }
 
     // 3. O^T = S Q_g^T + D^T P^T; wave w owns tokens 16 w .. 16 w + 15. Rows at

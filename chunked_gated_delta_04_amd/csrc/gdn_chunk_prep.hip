@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t* __restr
                                                           int T, int NC,
                                                           ChunkInfo* __restrict__ table,
                                                           int32_t* __restrict__ seq_first) {
-  __shared__ int s_scan[256];
+  __shared__ int s_scan[256], s_bos[256], s_eos[256];
   __shared__ int s_carry;
   const int tid = threadIdx.x;
   if (tid == 0) s_carry = 0;
@@ -62,16 +62,27 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t* __restr
       __syncthreads();
     }
     const int excl = s_carry + s_scan[tid] - cnt;
-    if (n < N) {
-      seq_first[n] = min(excl, NC);
-      for (int j = 0; j < cnt && excl + j < NC; ++j) {
-        ChunkInfo ci;
-        ci.seq = n;
-        ci.t0 = bos + kChunk * j;
-        ci.len = min(kChunk, eos - ci.t0);
-        ci.pos = j;
-        table[excl + j] = ci;
+    if (n < N) seq_first[n] = min(excl, NC);
+    s_bos[tid] = bos;
+    s_eos[tid] = eos;
+    __syncthreads();
+    // the chunks of these sequences, one per thread: chunk m of the block
+    // belongs to the first sequence whose inclusive count exceeds m
+    const int end = min(s_carry + s_scan[255], NC);
+    for (int c = s_carry + tid; c < end; c += 256) {
+      const int m = c - s_carry;
+      int a = 0, b = 255;
+      while (a < b) {
+        const int mid = (a + b) >> 1;
+        if (s_scan[mid] > m) b = mid; else a = mid + 1;
       }
+      const int j = m - (a > 0 ? s_scan[a - 1] : 0);
+      ChunkInfo ci;
+      ci.seq = base + a;
+      ci.t0 = s_bos[a] + kChunk * j;
+      ci.len = min(kChunk, s_eos[a] - ci.t0);
+      ci.pos = j;
+      table[c] = ci;
     }
     __syncthreads();
     if (tid == 255) s_carry += s_scan[255];

@@ -356,22 +356,27 @@ __global__ __launch_bounds__(kThreads) void conv_dstate_empty_kernel(
 }
 
 // Fixed-order reduction of the tiles' partial sums: rows [tile][W + 1][C].
-// Pass 1 adds groups of kGroup consecutive tiles, pass 2 adds the groups.
+// Pass 1 adds groups of kGroup consecutive tiles (one row of one group per
+// thread, all kGroup loads in flight), pass 2 adds the groups in order.
 __global__ __launch_bounds__(kThreads) void conv_reduce_pass1(const float* __restrict__ part,
                                                               int ntiles, int rows, int C,
                                                               float* __restrict__ part2) {
   const int c0 = (blockIdx.x * kThreads + threadIdx.x) * kCpt;
   if (c0 >= C) return;
-  const int g = blockIdx.y;
-  const int a = g * kGroup, b = min(a + kGroup, ntiles);
-  for (int r = 0; r < rows; ++r) {
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int t = a; t < b; ++t) {
-      const float4 v = *reinterpret_cast<const float4*>(part + ((size_t)t * rows + r) * C + c0);
-      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-    }
-    *reinterpret_cast<float4*>(part2 + ((size_t)g * rows + r) * C + c0) = s;
+  const int g = blockIdx.y, r = blockIdx.z;
+  float4 v[kGroup];
+#pragma unroll
+  for (int u = 0; u < kGroup; ++u) {
+    const int t = g * kGroup + u;
+    v[u] = t < ntiles ? *reinterpret_cast<const float4*>(part + ((size_t)t * rows + r) * C + c0)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  float4 s = v[0];
+#pragma unroll
+  for (int u = 1; u < kGroup; ++u) {
+    s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+  }
+  *reinterpret_cast<float4*>(part2 + ((size_t)g * rows + r) * C + c0) = s;
 }
 
 template <int W>
@@ -381,22 +386,30 @@ __global__ __launch_bounds__(kThreads) void conv_reduce_pass2(const float* __res
                                                               float* __restrict__ db) {
   const int c0 = (blockIdx.x * kThreads + threadIdx.x) * kCpt;
   if (c0 >= C) return;
-  float s[W + 1][kCpt];
+  const int r = blockIdx.y;  // 0 .. W - 1: taps, W: bias
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int g0 = 0; g0 < ngroups; g0 += 8) {
+    float4 v[8];
 #pragma unroll
-  for (int r = 0; r <= W; ++r)
+    for (int u = 0; u < 8; ++u)
+      v[u] = g0 + u < ngroups
+                 ? *reinterpret_cast<const float4*>(part2 + ((size_t)(g0 + u) * (W + 1) + r) * C + c0)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int j = 0; j < kCpt; ++j) s[r][j] = 0.f;
-  for (int g = 0; g < ngroups; ++g)
-#pragma unroll
-    for (int r = 0; r <= W; ++r) {
-      const float4 v = *reinterpret_cast<const float4*>(part2 + ((size_t)g * (W + 1) + r) * C + c0);
-      s[r][0] += v.x; s[r][1] += v.y; s[r][2] += v.z; s[r][3] += v.w;
+    for (int u = 0; u < 8; ++u) {
+      s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
     }
-#pragma unroll
-  for (int j = 0; j < kCpt; ++j) {
-#pragma unroll
-    for (int i = 0; i < W; ++i) dw[(size_t)(c0 + j) * W + i] = s[i][j];
-    if (db) db[c0 + j] = s[W][j];
+  }
+  if (r < W) {
+    dw[(size_t)(c0 + 0) * W + r] = s.x;
+    dw[(size_t)(c0 + 1) * W + r] = s.y;
+    dw[(size_t)(c0 + 2) * W + r] = s.z;
+    dw[(size_t)(c0 + 3) * W + r] = s.w;
+  } else if (db) {
+    db[c0] = s.x;
+    db[c0 + 1] = s.y;
+    db[c0 + 2] = s.z;
+    db[c0 + 3] = s.w;
   }
 }
 
@@ -484,14 +497,14 @@ struct BwdLaunch {
     if (T > 0) {
       hipLaunchKernelGGL((conv_bwd_kernel<W, S>), dim3(ntiles_of(T), cblocks(C)), dim3(kThreads),
                          0, s, cu, N, T, C, x, w, b, st, dy, dx, dstate, part);
-      hipLaunchKernelGGL(conv_reduce_pass1, dim3(cblocks(C), ngroups_of(T)), dim3(kThreads), 0,
-                         s, part, ntiles_of(T), W + 1, C, part2);
-      hipLaunchKernelGGL((conv_reduce_pass2<W>), dim3(cblocks(C)), dim3(kThreads), 0, s, part2,
-                         ngroups_of(T), C, dw, db);
+      hipLaunchKernelGGL(conv_reduce_pass1, dim3(cblocks(C), ngroups_of(T), W + 1),
+                         dim3(kThreads), 0, s, part, ntiles_of(T), W + 1, C, part2);
+      hipLaunchKernelGGL((conv_reduce_pass2<W>), dim3(cblocks(C), W + 1), dim3(kThreads), 0, s,
+                         part2, ngroups_of(T), C, dw, db);
     } else {
       // no tokens: zero weight and bias gradients through the same reduction
-      hipLaunchKernelGGL((conv_reduce_pass2<W>), dim3(cblocks(C)), dim3(kThreads), 0, s, part2,
-                         0, C, dw, db);
+      hipLaunchKernelGGL((conv_reduce_pass2<W>), dim3(cblocks(C), W + 1), dim3(kThreads), 0, s,
+                         part2, 0, C, dw, db);
     }
     return hipGetLastError();
   }
