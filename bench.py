@@ -40,19 +40,20 @@ F_STATE = 2 * C * D * D                     # one 64x128 by 128x128 product
 F_FWD = F_KKT + F_TSOLVE + 4 * F_TRI + 3 * F_STATE     # 9,024,853
 F_FWDBWD = 3 * F_FWD
 # per-kernel shares of the model (forward: WY pass vs scan; backward: its two kernels
-# split the 2 * F_FWD gradient work as the gradient contractions are assigned to them)
+# split the 2 * F_FWD gradient work as the gradient contractions are assigned to them;
+# the WY pass of a forward that saves also lays out W and P for the backward, which
+# the model does not count again)
 KERNEL_FLOPS = {
     "chunk_prep": F_KKT + F_TSOLVE + 3 * F_TRI,                 # K K^T, T, W, U, Q K^T
     "fwd_scan": F_TRI + 3 * F_STATE,                            # attn D, W h, Q h, K^T D
-    "chunk_prep_bwd": F_KKT + F_TSOLVE + 2 * F_TRI,             # K K^T, T, W, Q K^T
     "bwd_dh_scan": F_TRI + 3 * F_STATE,                         # P^T dO, K dh, Q^T dO, W^T dD
     "bwd_chunk": 2 * F_FWD - (F_TRI + 3 * F_STATE),             # the remaining gradient work
 }
 
 
 # stage name (gdn_stage_name) -> kernel symbol as the profiler names it
-STAGE_KERNELS = {"chunk_table": "chunk_table_kernel", "chunk_prep": "chunk_prep_kernel<false>",
-                 "fwd_scan": "fwd_scan_kernel<true, true, false>", "chunk_prep_bwd": "chunk_prep_kernel<true>",
+STAGE_KERNELS = {"chunk_table": "chunk_table_kernel", "chunk_prep": "chunk_prep_kernel<true, true>",
+                 "fwd_scan": "fwd_scan_kernel<true, true, false>",
                  "bwd_dh_scan": "bwd_dh_scan_kernel", "bwd_chunk": "bwd_chunk_kernel"}
 
 

@@ -66,35 +66,64 @@ gdn_status check_problem(const gdn_problem* p, int64_t* nc) {
   return GDN_OK;
 }
 
+// Forward workspace: chunk table, then the forward scan's operands. Backward
+// workspace: chunk table, then the scratch of the dh scan (its operands come
+// from `saved`, written by the forward's WY pass).
 Layout make_layout(const gdn_problem* p, int64_t NC, bool bwd) {
   Layout L;
   const size_t blocks = (size_t)p->HV * (size_t)NC;
   size_t off = 0;
   L.table = off;     off = align_up(off + sizeof(ChunkInfo) * (size_t)NC);
   L.seq_first = off; off = align_up(off + sizeof(int32_t) * (size_t)(p->N + 1));
-  L.W = off;         off = align_up(off + 2 * kBlk64x128 * blocks);
-  L.U = off;         off = bwd ? off : align_up(off + 2 * kBlk64x128 * blocks);
-  L.Qg = off;        off = align_up(off + 2 * kBlk64x128 * blocks);
-  L.P = off;         off = align_up(off + 2 * kBlk64x64 * blocks);
-  L.Kb = off;        off = align_up(off + 2 * kBlk64x128 * blocks);
-  L.gL = off;        off = align_up(off + sizeof(float) * blocks);
-  L.T = off;         off = bwd ? align_up(off + 2 * 2 * kBlk64x64 * blocks) : off;
-  L.dh = off;        off = bwd ? align_up(off + 2 * kState * blocks) : off;
-  L.dD = off;        off = bwd ? align_up(off + 2 * kBlk64x128 * blocks) : off;
-  L.dDT = off;       off = bwd ? align_up(off + 2 * kBlk64x128 * blocks) : off;
+  L.W = L.U = L.Qg = L.P = L.Kb = L.gL = off;
+  if (!bwd) {
+    L.W = off;       off = align_up(off + 2 * kBlk64x128 * blocks);
+    L.U = off;       off = align_up(off + 2 * kBlk64x128 * blocks);
+    L.Qg = off;      off = align_up(off + 2 * kBlk64x128 * blocks);
+    L.P = off;       off = align_up(off + 2 * kBlk64x64 * blocks);
+    L.Kb = off;      off = align_up(off + 2 * kBlk64x128 * blocks);
+    L.gL = off;      off = align_up(off + sizeof(float) * blocks);
+  }
+  L.T = L.dh = L.dD = L.dDT = off;
+  if (bwd) {
+    L.dh = off;      off = align_up(off + 2 * kState * blocks);
+    L.dD = off;      off = align_up(off + 2 * kBlk64x128 * blocks);
+    L.dDT = off;     off = align_up(off + 2 * kBlk64x128 * blocks);
+  }
   L.total = off;
   return L;
 }
 
-PrepOut prep_views(char* ws, const Layout& L, bool bwd) {
+PrepOut prep_views(char* ws, const Layout& L) {
   PrepOut o;
   o.W = reinterpret_cast<uint16_t*>(ws + L.W);
-  o.U = bwd ? nullptr : reinterpret_cast<uint16_t*>(ws + L.U);
+  o.U = reinterpret_cast<uint16_t*>(ws + L.U);
   o.Qg = reinterpret_cast<uint16_t*>(ws + L.Qg);
   o.P = reinterpret_cast<uint16_t*>(ws + L.P);
   o.Kb = reinterpret_cast<uint16_t*>(ws + L.Kb);
   o.gL = reinterpret_cast<float*>(ws + L.gL);
-  o.T = bwd ? reinterpret_cast<uint16_t*>(ws + L.T) : nullptr;
+  o.T = nullptr;
+  return o;
+}
+
+// `saved`: per (chunk, value head) the bf16 start state and D (kSavedBlock
+// elements each), then the backward's WY operands per (value head, chunk):
+// W^T, Q_g^T (64 x 128 each), P^T (64 x 64), K_bwd (64 x 128), T and T^T
+// (2 x 64 x 64), and e^gamma_L (fp32).
+constexpr size_t kSavedPrepElems = 3 * kBlk64x128 + 3 * kBlk64x64;
+size_t saved_bytes(size_t blocks) {
+  return blocks * ((size_t)kSavedBlock + kSavedPrepElems) * 2 + blocks * sizeof(float);
+}
+PrepOut saved_bwd_views(uint16_t* saved, size_t blocks) {
+  PrepOut o;
+  uint16_t* b = saved + blocks * (size_t)kSavedBlock;
+  o.W = b;                              b += blocks * kBlk64x128;
+  o.Qg = b;                             b += blocks * kBlk64x128;
+  o.P = b;                              b += blocks * kBlk64x64;
+  o.Kb = b;                             b += blocks * kBlk64x128;
+  o.T = b;                              b += blocks * 2 * kBlk64x64;
+  o.gL = reinterpret_cast<float*>(b);
+  o.U = nullptr;
   return o;
 }
 
@@ -149,7 +178,7 @@ GDN_API int64_t gdn_num_chunks(const gdn_problem* p) {
 GDN_API size_t gdn_chunk_saved_size(const gdn_problem* p) {
   int64_t nc = 0;
   if (check_problem(p, &nc) != GDN_OK) return 0;
-  return sizeof(uint16_t) * (size_t)kSavedBlock * (size_t)p->HV * (size_t)nc;
+  return saved_bytes((size_t)p->HV * (size_t)nc);
 }
 
 GDN_API size_t gdn_chunk_fwd_workspace_size(const gdn_problem* p) {
@@ -164,10 +193,18 @@ GDN_API size_t gdn_chunk_bwd_workspace_size(const gdn_problem* p) {
   return make_layout(p, nc, true).total;
 }
 
+// The recomputing backward holds the forward's operands (forward layout, at
+// the workspace's start), the rebuilt `saved` after the larger of the two
+// layouts, and the backward's scratch (backward layout, at the start again,
+// once the forward's operands are consumed).
+static size_t recompute_saved_offset(const gdn_problem* p, int64_t nc) {
+  return align_up(std::max(make_layout(p, nc, true).total, make_layout(p, nc, false).total));
+}
+
 GDN_API size_t gdn_chunk_bwd_recompute_workspace_size(const gdn_problem* p) {
   int64_t nc = 0;
   if (check_problem(p, &nc) != GDN_OK) return 0;
-  return align_up(make_layout(p, nc, true).total) + gdn_chunk_saved_size(p);
+  return recompute_saved_offset(p, nc) + gdn_chunk_saved_size(p);
 }
 
 // Records events[2 i] / events[2 i + 1] around stage i when events are given.
@@ -216,14 +253,15 @@ static int chunk_fwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_
   char* ws = static_cast<char*>(workspace);
   ChunkInfo* table = reinterpret_cast<ChunkInfo*>(ws + L.table);
   int32_t* seq_first = reinterpret_cast<int32_t*>(ws + L.seq_first);
-  const PrepOut prep = prep_views(ws, L, false);
+  const PrepOut prep = prep_views(ws, L);
+  const PrepOut bprep = saved ? saved_bwd_views(saved, (size_t)p->HV * NC) : PrepOut{};
   GDN_TRY(clk.run([&] {
     return launch_chunk_table(p->cu_seqlens, p->N, p->T, (int)NC, table, seq_first, s);
   }));
   if (NC > 0)
     GDN_TRY(clk.run([&] {
-      return launch_chunk_prep(false, table, (int)NC, p->H, p->HV, effective_scale(p), q, k, v, g,
-                               beta, prep, s);
+      return launch_chunk_prep(saved ? PrepMode::kBoth : PrepMode::kForward, table, (int)NC, p->H,
+                               p->HV, effective_scale(p), q, k, v, g, beta, prep, bprep, s);
     }));
   GDN_TRY(clk.run([&] {
     return launch_fwd_scan(saved ? ScanMode::kOutSave : ScanMode::kOut, seq_first, p->N, p->HV,
@@ -289,11 +327,12 @@ GDN_API int gdn_chunk_transition(const gdn_problem* p, const uint16_t* q, const 
   char* ws = static_cast<char*>(workspace);
   ChunkInfo* table = reinterpret_cast<ChunkInfo*>(ws + L.table);
   int32_t* seq_first = reinterpret_cast<int32_t*>(ws + L.seq_first);
-  const PrepOut prep = prep_views(ws, L, false);
+  const PrepOut prep = prep_views(ws, L);
   if (launch_chunk_table(p->cu_seqlens, p->N, p->T, (int)NC, table, seq_first, s) != hipSuccess)
     return GDN_ERR_HIP;
-  if (NC > 0 && launch_chunk_prep(false, table, (int)NC, p->H, p->HV, effective_scale(p), q, k,
-                                  v, g, beta, prep, s) != hipSuccess)
+  if (NC > 0 && launch_chunk_prep(PrepMode::kForward, table, (int)NC, p->H, p->HV,
+                                  effective_scale(p), q, k, v, g, beta, prep, PrepOut{}, s) !=
+                    hipSuccess)
     return GDN_ERR_HIP;
   StateRef sr{};
   sr.hT = s_end;
@@ -339,24 +378,25 @@ static int chunk_bwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_
   char* ws = static_cast<char*>(workspace);
   ChunkInfo* table = reinterpret_cast<ChunkInfo*>(ws + L.table);
   int32_t* seq_first = reinterpret_cast<int32_t*>(ws + L.seq_first);
-  const PrepOut prep = prep_views(ws, L, true);
   BwdBufs bufs;
   bufs.dh = reinterpret_cast<uint16_t*>(ws + L.dh);
   bufs.dD = reinterpret_cast<uint16_t*>(ws + L.dD);
   bufs.dDT = reinterpret_cast<uint16_t*>(ws + L.dDT);
   const float scale = effective_scale(p);
+  const size_t blocks = (size_t)p->HV * NC;
   GDN_TRY(clk.run([&] {
     return launch_chunk_table(p->cu_seqlens, p->N, p->T, (int)NC, table, seq_first, s);
   }));
   if (recompute) {
-    // forward WY pass and scan, saving only: the forward's operands live in the
-    // workspace's first bytes (the same offsets as the forward's own layout)
-    // until the backward's WY pass below overwrites them
-    uint16_t* rebuilt = reinterpret_cast<uint16_t*>(ws + align_up(L.total));
-    const PrepOut fprep = prep_views(ws, make_layout(p, NC, false), false);
+    // the forward's WY pass (both layouts) and a save-only scan rebuild
+    // `saved` after both workspace layouts; the forward's operands occupy the
+    // workspace's start until the scan has read them, then the backward's
+    // scratch takes that place
+    uint16_t* rebuilt = reinterpret_cast<uint16_t*>(ws + recompute_saved_offset(p, NC));
+    const PrepOut fprep = prep_views(ws, make_layout(p, NC, false));
     GDN_TRY(clk.run([&] {
-      return launch_chunk_prep(false, table, (int)NC, p->H, p->HV, scale, q, k, v, g, beta, fprep,
-                               s);
+      return launch_chunk_prep(PrepMode::kBoth, table, (int)NC, p->H, p->HV, scale, q, k, v, g,
+                               beta, fprep, saved_bwd_views(rebuilt, blocks), s);
     }));
     StateRef sr{};
     sr.h0 = recompute_h0;
@@ -366,9 +406,8 @@ static int chunk_bwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_
     }));
     saved = rebuilt;
   }
-  GDN_TRY(clk.run([&] {
-    return launch_chunk_prep(true, table, (int)NC, p->H, p->HV, scale, q, k, v, g, beta, prep, s);
-  }));
+  // the backward's WY operands were written by the forward, behind the states
+  const PrepOut prep = saved_bwd_views(const_cast<uint16_t*>(saved), blocks);
   GDN_TRY(clk.run([&] {
     return launch_bwd_dh_scan(seq_first, p->N, p->HV, (int)NC, table, prep, dO, dhT, dh0, bufs, s);
   }));
@@ -413,9 +452,9 @@ GDN_API int gdn_chunk_bwd_timed(const gdn_problem* p, const uint16_t* q, const u
 
 GDN_API const char* gdn_stage_name(int op, int stage) {
   static const char* fwd[] = {"chunk_table", "chunk_prep", "fwd_scan"};
-  static const char* bwd[] = {"chunk_table", "chunk_prep_bwd", "bwd_dh_scan", "bwd_chunk"};
+  static const char* bwd[] = {"chunk_table", "bwd_dh_scan", "bwd_chunk"};
   if (op == 0 && stage >= 0 && stage < 3) return fwd[stage];
-  if (op == 1 && stage >= 0 && stage < 4) return bwd[stage];
+  if (op == 1 && stage >= 0 && stage < 3) return bwd[stage];
   return "";
 }
 

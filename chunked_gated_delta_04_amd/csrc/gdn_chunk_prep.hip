@@ -23,8 +23,9 @@
 // e^x of x <= 0 (i >= j) is formed, so strong decays underflow to 0.
 //
 // Outputs per (value head, chunk) block, bf16 unless noted, in the layouts
-// the scans read with one 16-byte load per MFMA operand:
-//            forward scan (kBwd = false)     dh scan (kBwd = true)
+// the scans read with one 16-byte load per MFMA operand (a forward that saves
+// for a backward writes both sets in one pass):
+//            forward scan                    dh scan and gradient pass
 //   W        [64 tok][128 k]                 W^T   [128 k][64 tok]
 //   U        U^T [128 v][64 tok]             (not written)
 //   Q_g      [64 tok][128 k]                 Q_g^T [128 k][64 tok]
@@ -108,12 +109,15 @@ __device__ __forceinline__ void lower_tile(int t, int& ib, int& jb) {
 }
 }  // namespace
 
-template <bool kBwd>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(
+// kF: write the forward scan's operands to fo; kB: write the backward's to bo
+// (both when the forward saves for a backward, so that the backward does not
+// form them again).
+template <bool kF, bool kB>
+__global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     const ChunkInfo* __restrict__ table, int NC, int H, int HV, float scale,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ g,
-    const float* __restrict__ beta, PrepOut out) {
+    const float* __restrict__ beta, PrepOut fo, PrepOut bo) {
   const int c = blockIdx.x, h = blockIdx.y;
   const ChunkInfo ci = table[c];
   if (ci.seq < 0) return;
@@ -178,6 +182,13 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 
   const int G = HV / H;
   for (int jg = 0; jg < G; ++jg) {
+    // Re-derive the thread coordinates from an opaque copy each iteration, so
+    // that the many LDS and global addresses built from them are formed where
+    // they are used instead of being hoisted and kept live across the loop.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 15, kq = lane >> 4;
     const int hv = h * G + jg;
     const size_t blk = (size_t)hv * NC + c;
 
@@ -199,9 +210,12 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
       eg[lane] = e;
       fw[lane] = bv * e;
       ebw[lane] = lane < L ? exp2_fast(gl2 - g2) : 0.f;
-      if (lane == 0) out.gL[blk] = exp2_fast(gl2);
+      if (lane == 0) {
+        if (kF) fo.gL[blk] = exp2_fast(gl2);
+        if (kB) bo.gL[blk] = exp2_fast(gl2);
+      }
     }
-    if (!kBwd) {
+    if (kF) {
       const int r = tid >> 2, sg0 = (tid & 3) * 4;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -214,9 +228,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     __syncthreads();
 
     // ---- 3. A (fp32, LDS: 10 lower tiles, 6 zero upper tiles) and P (bf16,
-    //      global: 16 tiles), 32 jobs over the 4 waves
-    uint16_t* Pb = out.P + blk * (64 * 64);
-    for (int job = wave; job < 32; job += 4) {
+    //      global: 16 tiles per layout), jobs over the 4 waves
+    constexpr int kJobs = 16 + 16 * ((kF ? 1 : 0) + (kB ? 1 : 0));
+        for (int job = wave; job < kJobs; job += 4) {
       if (job < 10) {
         int ib, jb;
         lower_tile(job, ib, jb);
@@ -239,8 +253,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) Ts[(16 * ib + 4 * kq + r) * FP + 16 * jb + li] = 0.f;
       } else {
-        const int pt = job - 16, ib = pt >> 2, jb = pt & 3;  // P tile (row block ib, col block jb)
-        if (!kBwd) {
+        const int pt = (job - 16) & 15, ib = pt >> 2, jb = pt & 3;  // P tile (row block ib, col block jb)
+        if (kF && job < 32) {
+          uint16_t* Pb = fo.P + blk * (64 * 64);
           // C = K^ Q~^T tile: C[4kq+r][li] = P-row i = 16 ib + li, cols j = 16 jb + 4kq + r
           f32x4 acc = zero4();
           if (jb <= ib) {
@@ -259,6 +274,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
           *reinterpret_cast<uint2*>(Pb + kcm(i, 16 * jb + 4 * kq, 64)) =
               pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
         } else {
+          uint16_t* Pb = bo.P + blk * (64 * 64);
           // C = Q~ K^T tile: C[4kq+r][li] = P[i = 16 ib + 4kq + r][j = 16 jb + li] -> P^T[j][i..i+3]
           f32x4 acc = zero4();
           if (jb <= ib) {
@@ -288,45 +304,49 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     //      of 8 tokens) come from the row tiles with transposing LDS reads:
     //      a wave covers one token group tg and 64 consecutive features.
     {
-      uint16_t* Qgb = out.Qg + blk * 8192;
-      uint16_t* Kbb = out.Kb + blk * 8192;
-      const uint16_t* rowsrc = kBwd ? Ks : Qs;  // written as row segments
-      const float* rowf = kBwd ? ebw : eg;
-      const uint16_t* colsrc = kBwd ? Qs : Ks;  // written as column chunks
-      const float* colf = kBwd ? eg : ebw;
-      uint16_t* rowdst = kBwd ? Kbb : Qgb;
-      uint16_t* coldst = kBwd ? Qgb : Kbb;
-      for (int e = tid; e < 64 * 16; e += 256) {
-        const int sg = e >> 6, t = e & 63;
-        const uint4 x = *reinterpret_cast<const uint4*>(&rowsrc[t * KP + sg * 8]);
-        const uint32_t* xw = reinterpret_cast<const uint32_t*>(&x);
-        const float f = rowf[t];
-        uint4 o4;
-        uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
+      auto rows_out = [&](const uint16_t* src, const float* f, uint16_t* dst) {
+        for (int e = tid; e < 64 * 16; e += 256) {
+          const int sg = e >> 6, t = e & 63;
+          const uint4 x = *reinterpret_cast<const uint4*>(&src[t * KP + sg * 8]);
+          const uint32_t* xw = reinterpret_cast<const uint32_t*>(&x);
+          const float ft = f[t];
+          uint4 o4;
+          uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) ow[u] = pk2(f * bf2f(xw[u] & 0xffffu), f * bf2f(xw[u] >> 16));
-        *reinterpret_cast<uint4*>(rowdst + kcm(t, sg * 8, 64)) = o4;
+          for (int u = 0; u < 4; ++u) ow[u] = pk2(ft * bf2f(xw[u] & 0xffffu), ft * bf2f(xw[u] >> 16));
+          *reinterpret_cast<uint4*>(dst + kcm(t, sg * 8, 64)) = o4;
+        }
+      };
+      auto cols_out = [&](const uint16_t* src, const float* f, uint16_t* dst) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e0 = 256 * i + 64 * wave;           // wave-uniform
+          const int tg = e0 >> 7, d0 = (e0 & 127) + 16 * kq;
+          const uint4 x = lds_col8(src, KP, 8 * tg, d0, lane);
+          const uint32_t* xw = reinterpret_cast<const uint32_t*>(&x);
+          const float4 fa = *reinterpret_cast<const float4*>(&f[8 * tg]);
+          const float4 fb = *reinterpret_cast<const float4*>(&f[8 * tg + 4]);
+          const uint4 o4 = make_uint4(pk2(fa.x * bf2f(xw[0] & 0xffffu), fa.y * bf2f(xw[0] >> 16)),
+                                      pk2(fa.z * bf2f(xw[1] & 0xffffu), fa.w * bf2f(xw[1] >> 16)),
+                                      pk2(fb.x * bf2f(xw[2] & 0xffffu), fb.y * bf2f(xw[2] >> 16)),
+                                      pk2(fb.z * bf2f(xw[3] & 0xffffu), fb.w * bf2f(xw[3] >> 16)));
+          *reinterpret_cast<uint4*>(dst + kcm(d0 + li, 8 * tg, 128)) = o4;
+        }
+      };
+      if (kF) {  // Q_g [tok][k], K_bwd^T [k][tok]
+        rows_out(Qs, eg, fo.Qg + blk * 8192);
+        cols_out(Ks, ebw, fo.Kb + blk * 8192);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e0 = 256 * i + 64 * wave;           // wave-uniform
-        const int tg = e0 >> 7, d0 = (e0 & 127) + 16 * kq;
-        const uint4 x = lds_col8(colsrc, KP, 8 * tg, d0, lane);
-        const uint32_t* xw = reinterpret_cast<const uint32_t*>(&x);
-        const float4 fa = *reinterpret_cast<const float4*>(&colf[8 * tg]);
-        const float4 fb = *reinterpret_cast<const float4*>(&colf[8 * tg + 4]);
-        const uint4 o4 = make_uint4(pk2(fa.x * bf2f(xw[0] & 0xffffu), fa.y * bf2f(xw[0] >> 16)),
-                                    pk2(fa.z * bf2f(xw[1] & 0xffffu), fa.w * bf2f(xw[1] >> 16)),
-                                    pk2(fb.x * bf2f(xw[2] & 0xffffu), fb.y * bf2f(xw[2] >> 16)),
-                                    pk2(fb.z * bf2f(xw[3] & 0xffffu), fb.w * bf2f(xw[3] >> 16)));
-        *reinterpret_cast<uint4*>(coldst + kcm(d0 + li, 8 * tg, 128)) = o4;
+      if (kB) {  // K_bwd [tok][k], Q_g^T [k][tok]
+        rows_out(Ks, ebw, bo.Kb + blk * 8192);
+        cols_out(Qs, eg, bo.Qg + blk * 8192);
       }
     }
 
     // T and T^T in bf16 for the backward's gradient pass: chunk (kc, r) of each
     // holds row r, columns 8 kc .. 8 kc + 7
-    if (kBwd) {
-      uint16_t* Tg = out.T + blk * 8192;
+    if (kB) {
+      uint16_t* Tg = bo.T + blk * 8192;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int e = tid + 256 * i;
@@ -349,9 +369,11 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     //      T becomes an MFMA operand, K^ is read by columns from its row tile.
     //      32 tiles of 16 x 16 over 4 waves, contraction over the chunk.
     {
-      uint16_t* Wb = out.W + blk * 8192;
-      for (int tt = wave; tt < 32; tt += 4) {
-        if (!kBwd) {
+      constexpr int kWJobs = 32 * ((kF ? 1 : 0) + (kB ? 1 : 0));
+            for (int job = wave; job < kWJobs; job += 4) {
+        const int tt = job & 31;
+        if (kF && job < 32) {
+          uint16_t* Wb = fo.W + blk * 8192;
           // C = K^T (T')^T: C[4kq+r][li] = W[t = 16 tb + li][k = 16 db + 4kq + r]
           const int db = tt >> 2, tb = tt & 3;
           f32x4 acc = zero4();
@@ -364,6 +386,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
           *reinterpret_cast<uint2*>(Wb + kcm(16 * tb + li, 16 * db + 4 * kq, 64)) =
               pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
         } else {
+          uint16_t* Wb = bo.W + blk * 8192;
           // C = T' K^: C[4kq+r][li] = W[t = 16 tb + 4kq + r][k = 16 db + li] -> W^T[k][t..t+3]
           const int tb = tt >> 3, db = tt & 7;
           f32x4 acc = zero4();
@@ -379,10 +402,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
       }
     }
 
-    if (!kBwd) {
+    if (kF) {
       // ---- 7. U = (T diag(beta)) V, written as U^T [v][tok]
-      uint16_t* Ub = out.U + blk * 8192;
-      for (int tt = wave; tt < 32; tt += 4) {
+      uint16_t* Ub = fo.U + blk * 8192;
+            for (int tt = wave; tt < 32; tt += 4) {
         // C = T' V: C[4kq+r][li] = U[t = 16 tb + 4kq + r][v = 16 vb + li] -> U^T[v][t..t+3]
         const int tb = tt >> 3, vb = tt & 7;
         f32x4 acc = zero4();
@@ -407,16 +430,21 @@ hipError_t launch_chunk_table(const int32_t* cu, int N, int T, int NC, ChunkInfo
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_prep(bool bwd_layout, const ChunkInfo* table, int NC, int H, int HV,
+hipError_t launch_chunk_prep(PrepMode mode, const ChunkInfo* table, int NC, int H, int HV,
                              float scale, const uint16_t* q, const uint16_t* k,
                              const uint16_t* v, const float* g, const float* beta,
-                             const PrepOut& out, hipStream_t stream) {
-  if (bwd_layout)
-    hipLaunchKernelGGL(chunk_prep_kernel<true>, dim3(NC, H), dim3(256), 0, stream, table, NC, H,
-                       HV, scale, q, k, v, g, beta, out);
-  else
-    hipLaunchKernelGGL(chunk_prep_kernel<false>, dim3(NC, H), dim3(256), 0, stream, table, NC, H,
-                       HV, scale, q, k, v, g, beta, out);
+                             const PrepOut& fwd_out, const PrepOut& bwd_out, hipStream_t stream) {
+  const dim3 grid(NC, H);
+  switch (mode) {
+    case PrepMode::kForward:
+      hipLaunchKernelGGL((chunk_prep_kernel<true, false>), grid, dim3(256), 0, stream, table, NC,
+                         H, HV, scale, q, k, v, g, beta, fwd_out, bwd_out);
+      break;
+    case PrepMode::kBoth:
+      hipLaunchKernelGGL((chunk_prep_kernel<true, true>), grid, dim3(256), 0, stream, table, NC,
+                         H, HV, scale, q, k, v, g, beta, fwd_out, bwd_out);
+      break;
+  }
   return hipGetLastError();
 }
 

@@ -31,10 +31,14 @@ struct BwdBufs {
 hipError_t launch_chunk_table(const int32_t* cu, int N, int T, int NC, ChunkInfo* table,
                               int32_t* seq_first, hipStream_t stream);
 
-hipError_t launch_chunk_prep(bool bwd_layout, const ChunkInfo* table, int NC, int H, int HV,
+// Which operand layouts the WY pass writes: the forward scan's only, or also
+// the backward's (dh scan and gradient pass) when the forward saves for it.
+enum class PrepMode { kForward, kBoth };
+
+hipError_t launch_chunk_prep(PrepMode mode, const ChunkInfo* table, int NC, int H, int HV,
                              float scale, const uint16_t* q, const uint16_t* k,
                              const uint16_t* v, const float* g, const float* beta,
-                             const PrepOut& out, hipStream_t stream);
+                             const PrepOut& fwd_out, const PrepOut& bwd_out, hipStream_t stream);
 
 // Where the forward scan takes each chain's start state and leaves its end
 // state. Direct: h0 / hT are [N, HV, V, K] (either NULL). Paged: h0 == hT is a
