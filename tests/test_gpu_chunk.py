@@ -160,16 +160,20 @@ def test_value_heads_of_one_key_head_with_equal_inputs_agree_bitwise():
 
 
 def test_state_carry_across_two_calls():
-    lens = [600]
+    """One call equals two calls with the end state carried, at the split points
+    of the pages' continuity sweep (AttnGym, 'Paged-state continuity') and
+    around chunk edges."""
+    TOT = 1700
+    lens = [TOT]
     inp = small_inputs(lens=lens, H=1, HV=2)
     o, hT, _ = run_fwd(inp)
-    for p in (1, 63, 64, 65, 527):
+    for p in (1, 63, 64, 65, 527, 528, 1056, 1584):
         a = dict(q=inp["q"][:p], k=inp["k"][:p], v=inp["v"][:p], g=inp["g"][:p],
                  beta=inp["beta"][:p], cu_seqlens=torch.tensor([0, p], dtype=torch.int32),
                  h0=inp["h0"])
         oa, ha, _ = run_fwd(a)
         b = dict(q=inp["q"][p:], k=inp["k"][p:], v=inp["v"][p:], g=inp["g"][p:],
-                 beta=inp["beta"][p:], cu_seqlens=torch.tensor([0, 600 - p], dtype=torch.int32),
+                 beta=inp["beta"][p:], cu_seqlens=torch.tensor([0, TOT - p], dtype=torch.int32),
                  h0=ha.cpu())
         ob, hb, _ = run_fwd(b)
         assert_bar(f"o split {p}", f64(torch.cat([oa, ob])), f64(o))
@@ -237,3 +241,34 @@ def test_backward_repeats_bitwise_many_times_and_on_a_side_stream():
         assert torch.equal(o, o2) and torch.equal(hT, hT2)
         for kname in g0:
             assert torch.equal(g0[kname], g2[kname]), (i, kname)
+
+
+_CHILD = r"""
+import hashlib, sys, torch
+sys.path.insert(0, {root!r})
+from tests.test_gpu_chunk import small_inputs, run_fwd_bwd
+inp = small_inputs(with_do=True)
+o, hT, grads = run_fwd_bwd(inp)
+h = hashlib.sha256()
+for t in [o, hT] + [grads[k] for k in sorted(grads)]:
+    h.update(t.detach().cpu().contiguous().view(torch.uint8).numpy().tobytes())
+print(h.hexdigest())
+"""
+
+
+def test_backward_repeats_bitwise_in_a_fresh_process():
+    """The same inputs in a new process (a fresh context, fresh allocations)
+    give the same bits (cake_gdn, 'Tests': bit-identical across processes)."""
+    import hashlib
+    import subprocess
+    _say("bwd fresh process")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    inp = small_inputs(with_do=True)
+    o, hT, grads = run_fwd_bwd(inp)
+    h = hashlib.sha256()
+    for t in [o, hT] + [grads[k] for k in sorted(grads)]:
+        h.update(t.detach().cpu().contiguous().view(torch.uint8).numpy().tobytes())
+    r = subprocess.run([sys.executable, "-c", _CHILD.format(root=root)], capture_output=True,
+                       text=True, timeout=240, cwd=root)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.strip().splitlines()[-1] == h.hexdigest()
