@@ -101,6 +101,17 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t* __restr
 namespace {
 constexpr int KP = 136;  // LDS row pitch (bf16) of [64][128] tiles
 constexpr int FP = 68;   // LDS row pitch (fp32) of [64][64] tiles
+constexpr int XPP = 24;  // LDS row pitch (bf16) of a wave's 16 x 16 transpose tile
+
+// A 16 x 16 bf16 tile held as MFMA accumulator pieces (lane 16 kq + li: row li,
+// columns 4 kq .. 4 kq + 3) read back by columns: lane 16 kq + li (kq < 2)
+// gets column li, rows 8 kq .. 8 kq + 7. The wave's own LDS tile, written and
+// read by the wave alone (its LDS operations complete in order).
+__device__ __forceinline__ uint4 tile_transpose(uint16_t* xp, uint2 piece, int lane) {
+  const int li = lane & 15, kq = lane >> 4;
+  *reinterpret_cast<uint2*>(&xp[li * XPP + 4 * kq]) = piece;
+  return lds_col8(xp, XPP, 8 * (kq & 1), 0, lane);
+}
 
 // lower-including 16x16 tile t (0..9) of a 64x64 matrix -> (row block, col block)
 __device__ __forceinline__ void lower_tile(int t, int& ib, int& jb) {
@@ -109,10 +120,10 @@ __device__ __forceinline__ void lower_tile(int t, int& ib, int& jb) {
 }
 }  // namespace
 
-// kF: write the forward scan's operands to fo; kB: write the backward's to bo
-// (both when the forward saves for a backward, so that the backward does not
-// form them again).
-template <bool kF, bool kB>
+// Writes the forward scan's operands to fo and, with kB (a forward that saves
+// for a backward), the backward's to bo, so that the backward does not form
+// them again.
+template <bool kB>
 __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     const ChunkInfo* __restrict__ table, int NC, int H, int HV, float scale,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -122,8 +133,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
   const ChunkInfo ci = table[c];
   if (ci.seq < 0) return;
   const int t0 = ci.t0, L = ci.len;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int li = lane & 15, kq = lane >> 4;
+  const int tid = threadIdx.x;
 
   __shared__ __align__(16) uint16_t Ks[64 * KP];   // k^ rows (bf16)
   __shared__ __align__(16) uint16_t Qs[64 * KP];   // q~ rows (bf16)
@@ -132,6 +142,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
   // gates of the value head; gam is the cumulative log-decay in base 2
   __shared__ __align__(16) float gam[64], bet[64], eg[64], ebw[64], fw[64];
   __shared__ float Xs[3 * 256];  // solve scratch
+  __shared__ __align__(16) uint16_t Xp[4][16 * XPP];  // per-wave 16 x 16 transpose tile
 
   // ---- 1. load and L2-normalise q, k rows (thread: row tid/4, 32 columns);
   //      one division per row, then products with the reciprocal
@@ -211,11 +222,11 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
       fw[lane] = bv * e;
       ebw[lane] = lane < L ? exp2_fast(gl2 - g2) : 0.f;
       if (lane == 0) {
-        if (kF) fo.gL[blk] = exp2_fast(gl2);
+        fo.gL[blk] = exp2_fast(gl2);
         if (kB) bo.gL[blk] = exp2_fast(gl2);
       }
     }
-    if (kF) {
+    {
       const int r = tid >> 2, sg0 = (tid & 3) * 4;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -228,9 +239,9 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     __syncthreads();
 
     // ---- 3. A (fp32, LDS: 10 lower tiles, 6 zero upper tiles) and P (bf16,
-    //      global: 16 tiles per layout), jobs over the 4 waves
-    constexpr int kJobs = 16 + 16 * ((kF ? 1 : 0) + (kB ? 1 : 0));
-        for (int job = wave; job < kJobs; job += 4) {
+    //      global: 16 tiles), 32 jobs over the 4 waves. A tile of P also goes
+    //      to the backward's P^T through the wave's LDS transpose tile.
+    for (int job = wave; job < 32; job += 4) {
       if (job < 10) {
         int ib, jb;
         lower_tile(job, ib, jb);
@@ -253,45 +264,28 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) Ts[(16 * ib + 4 * kq + r) * FP + 16 * jb + li] = 0.f;
       } else {
-        const int pt = (job - 16) & 15, ib = pt >> 2, jb = pt & 3;  // P tile (row block ib, col block jb)
-        if (kF && job < 32) {
-          uint16_t* Pb = fo.P + blk * (64 * 64);
-          // C = K^ Q~^T tile: C[4kq+r][li] = P-row i = 16 ib + li, cols j = 16 jb + 4kq + r
-          f32x4 acc = zero4();
-          if (jb <= ib) {
+        const int pt = job - 16, ib = pt >> 2, jb = pt & 3;  // P tile (row block ib, col block jb)
+        // C = K^ Q~^T tile: C[4kq+r][li] = P-row i = 16 ib + li, cols j = 16 jb + 4kq + r
+        f32x4 acc = zero4();
+        if (jb <= ib) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-              acc = mfma(ld8(&Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]),
-                         ld8(&Qs[(16 * ib + li) * KP + 32 * s + 8 * kq]), acc);
-          }
-          const int i = 16 * ib + li;
-          float pv[4];
+          for (int s = 0; s < 4; ++s)
+            acc = mfma(ld8(&Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]),
+                       ld8(&Qs[(16 * ib + li) * KP + 32 * s + 8 * kq]), acc);
+        }
+        const int i = 16 * ib + li;
+        float pv[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = 16 * jb + 4 * kq + r;
-            pv[r] = i >= j ? exp2_fast(gam[i] - gam[j]) * acc[r] : 0.f;
-          }
-          *reinterpret_cast<uint2*>(Pb + kcm(i, 16 * jb + 4 * kq, 64)) =
-              pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
-        } else {
-          uint16_t* Pb = bo.P + blk * (64 * 64);
-          // C = Q~ K^T tile: C[4kq+r][li] = P[i = 16 ib + 4kq + r][j = 16 jb + li] -> P^T[j][i..i+3]
-          f32x4 acc = zero4();
-          if (jb <= ib) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-              acc = mfma(ld8(&Qs[(16 * ib + li) * KP + 32 * s + 8 * kq]),
-                         ld8(&Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), acc);
-          }
-          const int j = 16 * jb + li;
-          float pv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 16 * ib + 4 * kq + r;
-            pv[r] = i >= j ? exp2_fast(gam[i] - gam[j]) * acc[r] : 0.f;
-          }
-          *reinterpret_cast<uint2*>(Pb + kcm(j, 16 * ib + 4 * kq, 64)) =
-              pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * jb + 4 * kq + r;
+          pv[r] = i >= j ? exp2_fast(gam[i] - gam[j]) * acc[r] : 0.f;
+        }
+        const uint2 pk = pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
+        *reinterpret_cast<uint2*>(fo.P + blk * (64 * 64) + kcm(i, 16 * jb + 4 * kq, 64)) = pk;
+        if (kB) {  // P^T[j][i .. i + 7]: columns of the tile, 16-byte pieces from 32 lanes
+          const uint4 x = tile_transpose(Xp[wave], pk, lane);
+          if (kq < 2)
+            *reinterpret_cast<uint4*>(bo.P + blk * (64 * 64) + kcm(16 * jb + li, 16 * ib + 8 * kq, 64)) = x;
         }
       }
     }
@@ -333,10 +327,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
           *reinterpret_cast<uint4*>(dst + kcm(d0 + li, 8 * tg, 128)) = o4;
         }
       };
-      if (kF) {  // Q_g [tok][k], K_bwd^T [k][tok]
-        rows_out(Qs, eg, fo.Qg + blk * 8192);
-        cols_out(Ks, ebw, fo.Kb + blk * 8192);
-      }
+      rows_out(Qs, eg, fo.Qg + blk * 8192);   // Q_g [tok][k]
+      cols_out(Ks, ebw, fo.Kb + blk * 8192);  // K_bwd^T [k][tok]
       if (kB) {  // K_bwd [tok][k], Q_g^T [k][tok]
         rows_out(Ks, ebw, bo.Kb + blk * 8192);
         cols_out(Qs, eg, bo.Qg + blk * 8192);
@@ -367,42 +359,28 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
 
     // ---- 6. W = (T diag(beta e^gamma)) K^: the factor scales T's columns as
     //      T becomes an MFMA operand, K^ is read by columns from its row tile.
-    //      32 tiles of 16 x 16 over 4 waves, contraction over the chunk.
-    {
-      constexpr int kWJobs = 32 * ((kF ? 1 : 0) + (kB ? 1 : 0));
-            for (int job = wave; job < kWJobs; job += 4) {
-        const int tt = job & 31;
-        if (kF && job < 32) {
-          uint16_t* Wb = fo.W + blk * 8192;
-          // C = K^T (T')^T: C[4kq+r][li] = W[t = 16 tb + li][k = 16 db + 4kq + r]
-          const int db = tt >> 2, tb = tt & 3;
-          f32x4 acc = zero4();
+    //      32 tiles of 16 x 16 over 4 waves, contraction over the chunk; a
+    //      tile also goes to the backward's W^T through the LDS transpose tile.
+    for (int tt = wave; tt < 32; tt += 4) {
+      // C = K^T (T')^T: C[4kq+r][li] = W[t = 16 tb + li][k = 16 db + 4kq + r]
+      const int db = tt >> 2, tb = tt & 3;
+      f32x4 acc = zero4();
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const uint4 kc = lds_col8(Ks, KP, 32 * s + 8 * kq, 16 * db, lane);
-            acc = mfma(__builtin_bit_cast(bf16x8, kc),
-                       cvt8s(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq], &fw[32 * s + 8 * kq]), acc);
-          }
-          *reinterpret_cast<uint2*>(Wb + kcm(16 * tb + li, 16 * db + 4 * kq, 64)) =
-              pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
-        } else {
-          uint16_t* Wb = bo.W + blk * 8192;
-          // C = T' K^: C[4kq+r][li] = W[t = 16 tb + 4kq + r][k = 16 db + li] -> W^T[k][t..t+3]
-          const int tb = tt >> 3, db = tt & 7;
-          f32x4 acc = zero4();
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const uint4 kc = lds_col8(Ks, KP, 32 * s + 8 * kq, 16 * db, lane);
-            acc = mfma(cvt8s(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq], &fw[32 * s + 8 * kq]),
-                       __builtin_bit_cast(bf16x8, kc), acc);
-          }
-          *reinterpret_cast<uint2*>(Wb + kcm(16 * db + li, 16 * tb + 4 * kq, 128)) =
-              pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
-        }
+      for (int s = 0; s < 2; ++s) {
+        const uint4 kc = lds_col8(Ks, KP, 32 * s + 8 * kq, 16 * db, lane);
+        acc = mfma(__builtin_bit_cast(bf16x8, kc),
+                   cvt8s(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq], &fw[32 * s + 8 * kq]), acc);
+      }
+      const uint2 pk = pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
+      *reinterpret_cast<uint2*>(fo.W + blk * 8192 + kcm(16 * tb + li, 16 * db + 4 * kq, 64)) = pk;
+      if (kB) {  // W^T[k][t .. t + 7]
+        const uint4 x = tile_transpose(Xp[wave], pk, lane);
+        if (kq < 2)
+          *reinterpret_cast<uint4*>(bo.W + blk * 8192 + kcm(16 * db + li, 16 * tb + 8 * kq, 128)) = x;
       }
     }
 
-    if (kF) {
+    {
       // ---- 7. U = (T diag(beta)) V, written as U^T [v][tok]
       uint16_t* Ub = fo.U + blk * 8192;
             for (int tt = wave; tt < 32; tt += 4) {
@@ -437,12 +415,12 @@ hipError_t launch_chunk_prep(PrepMode mode, const ChunkInfo* table, int NC, int 
   const dim3 grid(NC, H);
   switch (mode) {
     case PrepMode::kForward:
-      hipLaunchKernelGGL((chunk_prep_kernel<true, false>), grid, dim3(256), 0, stream, table, NC,
-                         H, HV, scale, q, k, v, g, beta, fwd_out, bwd_out);
+      hipLaunchKernelGGL((chunk_prep_kernel<false>), grid, dim3(256), 0, stream, table, NC, H, HV,
+                         scale, q, k, v, g, beta, fwd_out, bwd_out);
       break;
     case PrepMode::kBoth:
-      hipLaunchKernelGGL((chunk_prep_kernel<true, true>), grid, dim3(256), 0, stream, table, NC,
-                         H, HV, scale, q, k, v, g, beta, fwd_out, bwd_out);
+      hipLaunchKernelGGL((chunk_prep_kernel<true>), grid, dim3(256), 0, stream, table, NC, H, HV,
+                         scale, q, k, v, g, beta, fwd_out, bwd_out);
       break;
   }
   return hipGetLastError();
