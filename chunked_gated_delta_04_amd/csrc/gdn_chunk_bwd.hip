@@ -1,5 +1,7 @@
 // Backward of the chunked gated delta rule: reverse state-gradient scan and
-// the per-chunk gradient pass.
+// the per-chunk gradient pass. Their per-chunk operands (W^T, Q_g^T, P^T,
+// K_bwd, T, T^T, e^gamma_L) are the ones the forward's WY pass wrote behind
+// the saved states (gdn_chunk_prep.hip), so no WY pass runs here.
 //
 // Chunk form (see gdn_chunk_prep.hip): D = U - W h, O = Q_g h + P D,
 // h' = e^gamma_L h + K_bwd^T D, with U = T diag(beta) V,
