@@ -292,7 +292,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     __syncthreads();
 
     // ---- 4. T = (I + A)^-1 in place
-    invert_unit_lower_64(Ts, Xs, tid, 256);
+    invert_unit_lower_64(Ts, Xs, tid);
 
     // ---- 5. Q_g and K_bwd to global. The transposed pieces (column chunks
     //      of 8 tokens) come from the row tiles with transposing LDS reads:

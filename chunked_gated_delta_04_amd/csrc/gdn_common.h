@@ -133,15 +133,21 @@ __device__ __forceinline__ uint4 lds_col8(const uint16_t* tile, int pitch, int r
   return make_uint4(a.x, a.y, b.x, b.y);
 }
 
+// One fp32 MFMA step (16 x 16 x 4): lane 16 kk + i supplies A[i][kk] and
+// B[kk][i]; the accumulator holds C[4 kk + r][i] in element r.
+__device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // In-place inverse of I + A for a strictly lower-triangular 64 x 64 fp32 matrix A
 // in LDS (row pitch 68): on return T = (I + A)^-1, unit lower triangular, with
 // zeros above the diagonal blocks as on entry. Blocked in 16 x 16: each
-// diagonal block by forward substitution (one column per thread), then block
-// rows i = 1..3 from T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj. scratch: 768
-// floats. Must be called by every thread of the workgroup (it synchronises);
-// threads with tid >= 256 only take part in the barriers. Fixed summation order.
-__device__ __forceinline__ void invert_unit_lower_64(float* M, float* scratch, int tid,
-                                                     int nthreads) {
+// diagonal block by forward substitution (one column per thread of wave 0),
+// then block rows i = 1..3 from T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj, block
+// j of row i on wave j with fp32 MFMA (the sum into the wave's scratch tile,
+// a barrier, then the product with T_ii). scratch: 768 floats. Must be called
+// by all 256 threads of the workgroup (it synchronises). Fixed summation order.
+__device__ __forceinline__ void invert_unit_lower_64(float* M, float* scratch, int tid) {
   constexpr int P = 68;
   float x[16];
   if (tid < 64) {
@@ -161,32 +167,31 @@ __device__ __forceinline__ void invert_unit_lower_64(float* M, float* scratch, i
     for (int i = 0; i < 16; ++i) M[(o16 + i) * P + o16 + jc] = x[i];
   }
   __syncthreads();
-  const int r = (tid >> 4) & 15, cc = tid & 15;
+  const int jb = tid >> 6, lane = tid & 63, li = lane & 15, kk = lane >> 4;
+  float* St = scratch + 256 * (jb < 3 ? jb : 0);
   for (int ib = 1; ib < 4; ++ib) {
-    if (tid < 256) {
-      for (int jb = 0; jb < ib; ++jb) {
-        float a4[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int mb = jb; mb < ib; ++mb) {
+    if (jb < ib) {  // S = sum_m A_(ib, m) T_(m, jb)
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int mb = jb; mb < ib; ++mb) {
 #pragma unroll
-          for (int u = 0; u < 16; ++u)
-            a4[u & 3] += M[(16 * ib + r) * P + 16 * mb + u] * M[(16 * mb + u) * P + 16 * jb + cc];
-        }
-        scratch[jb * 256 + r * 16 + cc] = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+        for (int s = 0; s < 4; ++s)
+          acc = mfma_f32_k4(M[(16 * ib + li) * P + 16 * mb + 4 * s + kk],
+                            M[(16 * mb + 4 * s + kk) * P + 16 * jb + li], acc);
       }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) St[(4 * kk + r) * 16 + li] = acc[r];
     }
     __syncthreads();
-    if (tid < 256) {
-      for (int jb = 0; jb < ib; ++jb) {
-        float a4[4] = {0.f, 0.f, 0.f, 0.f};
+    if (jb < ib) {  // T_(ib, jb) = -T_(ib, ib) S
+      f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 16; ++u)
-          a4[u & 3] += M[(16 * ib + r) * P + 16 * ib + u] * scratch[jb * 256 + u * 16 + cc];
-        M[(16 * ib + r) * P + 16 * jb + cc] = -((a4[0] + a4[1]) + (a4[2] + a4[3]));
-      }
+      for (int s = 0; s < 4; ++s)
+        d = mfma_f32_k4(M[(16 * ib + li) * P + 16 * ib + 4 * s + kk], St[(4 * s + kk) * 16 + li], d);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) M[(16 * ib + 4 * kk + r) * P + 16 * jb + li] = -d[r];
     }
     __syncthreads();
   }
-  (void)nthreads;
 }
 
 // Saved-for-backward block of one (chunk, value head): the chunk-start state
