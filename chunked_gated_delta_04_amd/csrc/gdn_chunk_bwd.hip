@@ -259,9 +259,10 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
 // columns 64 kh .. 64 kh + 63) of every token-indexed result. Matrices that
 // are contracted over the chunk's tokens are kept in LDS transposed as well
 // (bf16), so every MFMA operand is one 16-byte read. The operands each phase
-// reads from HBM are requested a phase ahead (the state h is staged into LDS
-// while dP and Z are formed, then the state gradient dh' takes its place), so
-// the workgroup - alone on its CU - does not stall on memory at every phase.
+// reads from HBM are requested a phase ahead (the state h is copied straight
+// into LDS with the first requests of a value head, then the state gradient
+// dh' takes its place), so the workgroup - alone on its CU - does not stall on
+// memory at every phase.
 // Per-token and per-column partial sums go to LDS slots owned by one wave each
 // and are added once per value head in a fixed order.
 namespace {
@@ -272,7 +273,6 @@ struct BwdLds {
   uint16_t KsT[128 * TP], QsT[128 * TP];    // k^, q~ transposed [k][tok]
   uint16_t Pm[64 * BP], PmT[64 * BP];       // dP o Gamma and transpose; then T, T^T;
                                             // then M, M^T
-  uint16_t Hs[128 * KP];                    // h [k][v], then dh' [k][v]; dq staging at the end
   union {                                   // time-shared regions
     uint16_t Z[64 * KP];                    //   Z = T^T dD [tok][v]
     uint16_t V[64 * KP];                    //   V rows of the chunk
@@ -299,12 +299,6 @@ __device__ __forceinline__ float4 ld4_bf16(const uint16_t* p) {  // 4 bf16 -> fp
   const uint2 u = *reinterpret_cast<const uint2*>(p);
   return make_float4(bf2f(u.x & 0xffffu), bf2f(u.x >> 16), bf2f(u.y & 0xffffu), bf2f(u.y >> 16));
 }
-// LDS position (pitch KP, [k][v]) of 16-byte chunk e of a state stored as
-// [v / 32][v % 32 / 8][k][v % 8]
-__device__ __forceinline__ int state_pos(int e) {
-  const int vb = e >> 9, vg = (e >> 7) & 3, kk = e & 127;
-  return kk * KP + vb * 32 + vg * 8;
-}
 __device__ __forceinline__ float dot8u(const uint4& a, const uint4& b) {  // bf16 pairs
   const uint32_t* x = reinterpret_cast<const uint32_t*>(&a);
   const uint32_t* y = reinterpret_cast<const uint32_t*>(&b);
@@ -330,10 +324,14 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
   const int t0 = ci.t0, L = ci.len;
 
   __shared__ __align__(16) BwdLds S;
+  // h, then dh', in the layout both have in global memory ([v / 8][k][v % 8]),
+  // so h arrives by direct global-to-LDS copies; a separate array, so that
+  // those copies are not taken to alias the tiles in S. dq staging at the end.
+  __shared__ __align__(16) uint16_t Hs[kHead * kHead];
 
   // ---- q, k rows: L2 norm; k^ as rows and transposed, q~ transposed and, for
-  //      the products below, as rows (in Hs, free until the first value head
-  //      stages h). 16 threads per row, so each request covers whole rows.
+  //      the products below, as rows (in the Z tile, free until the first
+  //      value head forms Z). 16 threads per row, so each request covers whole rows.
   {
     const int tid = threadIdx.x;
     const int sg = tid & 15;
@@ -392,7 +390,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         S.QsT[(d + 1) * TP + r] = q1;
       }
       *reinterpret_cast<uint4*>(&S.Ks[r * KP + sg * 8]) = ko;
-      *reinterpret_cast<uint4*>(&S.Hs[r * KP + sg * 8]) = qo;
+      *reinterpret_cast<uint4*>(&S.rz.Z[r * KP + sg * 8]) = qo;
     }
   }
   __syncthreads();
@@ -411,7 +409,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       if (jb <= tw) {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          qk[q2] = mfma(ld8(&S.Hs[(16 * tw + li) * KP + 32 * s + 8 * kq]),
+          qk[q2] = mfma(ld8(&S.rz.Z[(16 * tw + li) * KP + 32 * s + 8 * kq]),
                         ld8(&S.Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), qk[q2]);
       }
     }
@@ -421,9 +419,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
   // slots, then dg = reverse cumsum of dgamma inside the chunk. Run by wave 0
   // at the top of the next value head (or after the last one): the slots and
   // gamma are rewritten only after the next gate barrier, which wave 0 reaches
-  // after this, and the work overlaps the other waves' requests.
-  auto dg_out = [&](int hv_) {
-    const int t = threadIdx.x & 63;
+  // after this, and the work overlaps the other waves' requests. t: the lane,
+  // from an opaque copy of the thread index (see the value-head loop), so that
+  // none of the addresses below is hoisted out of the loop.
+  auto dg_out = [&](int hv_, int t) {
     const int w0 = 4 * ((t >> 4) & 1);  // the waves whose column tiles hold t
     float dgm = (S.rowF[0][t] + S.rowF[1][t]) + (S.rowG[0][t] + S.rowG[1][t]) +
                 (S.rowE[0][t] + S.rowE[1][t]);
@@ -442,8 +441,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       x += glsum + exp2_fast(S.gam[L - 1]) * hdsum;
     }
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_down(x, off, 64);
+    for (int off = 1; off < 64; off <<= 1) {  // suffix sums; lane t reads lane t + off
+      const float y = __int_as_float(__builtin_amdgcn_ds_bpermute(((t + off) & 63) << 2,
+                                                                  __float_as_int(x)));
       if (t + off < 64) x += y;
     }
     if (t < L) {
@@ -489,6 +489,16 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(v) + ((size_t)t0 * HV + hv) * kHead, 0, L * (int)rs * 2, kBufferWord3);
 
+    // ---- h straight into LDS: each wave copies 1 KiB per request (lane l
+    //      the 16 bytes at offset 16 l), oldest of this value head's requests
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e0 = 512 * i + 64 * wave;  // first 16-byte chunk of the copy
+      __builtin_amdgcn_global_load_lds(hb + 8 * (e0 + lane),
+                                       (__attribute__((address_space(3))) void*)(Hs + 8 * e0),
+                                       16, 0, 0);
+    }
+
     // ---- requests for the dP phase: the own rows of dO and q, the D rows of
     //      this wave's dP tiles
     bf16x8 oa[4], dfr[2][4];
@@ -515,7 +525,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 
     // ---- gates (wave 0, after the previous value head's gate gradients)
     if (wave == 0) {
-      if (jg > 0) dg_out(hv - 1);
+      if (jg > 0) dg_out(hv - 1, lane);
       float gv = lane < L ? g[(size_t)(t0 + lane) * HV + hv] : 0.f;
       const float bv = lane < L ? beta[(size_t)(t0 + lane) * HV + hv] : 0.f;
 #pragma unroll
@@ -575,16 +585,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         for (int r = 0; r < 4; ++r) S.rowF[kh][16 * tw + 4 * kq + r] = rowp[r];
       }
     }
-    // h, staged into LDS once the Z phase is done with its operands
-    uint4 hst[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + 512 * i;
-      hst[i] = *reinterpret_cast<const uint4*>(hb + 8 * e);
-    }
-
     // ---- Z = T^T dD (written [tok][v]); dV = diag(beta) Z; dbeta of U.
     //      Wave: token columns of tile tw, value tiles 4 kh .. 4 kh + 3.
+    //      First every request of this wave is waited for: the Z operands are
+    //      the youngest, and the copies of h, older, are then in LDS too (for
+    //      the other waves after the barrier below).
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     {
       float bp = 0.f;
 #pragma unroll
@@ -611,11 +617,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       bp += __shfl_xor(bp, 32, 64);
       if (kq == 0) S.rowB[kh][trow] = bp;
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + 512 * i;
-      *reinterpret_cast<uint4*>(&S.Hs[state_pos(e)]) = hst[i];
-    }
     __syncthreads();
 
     // ---- key-column passes (columns 16 kt + li, kt = 4 kh .. 4 kh + 3), h from LDS:
@@ -633,7 +634,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         const int kr = 16 * (4 * kh + j) + li;
         f32x4 x1 = zero4(), y1 = zero4();
 #pragma unroll
-        for (int s = 0; s < 4; ++s) x1 = mfma(oa[s], ld8(&S.Hs[kr * KP + 32 * s + 8 * kq]), x1);
+        for (int s = 0; s < 4; ++s) x1 = mfma(oa[s], ld8(&Hs[kcm(kr, 32 * s + 8 * kq, kHead)]), x1);
 #pragma unroll
         for (int s = 0; s < 2; ++s)
           if (32 * s <= 16 * tw + 15)  // (dP o Gamma)[t][j] needs j <= t
@@ -660,7 +661,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         const int kr = 16 * (4 * kh + j) + li;
         f32x4 x4 = zero4(), y2 = zero4();
 #pragma unroll
-        for (int s = 0; s < 4; ++s) x4 = mfma(za[s], ld8(&S.Hs[kr * KP + 32 * s + 8 * kq]), x4);
+        for (int s = 0; s < 4; ++s) x4 = mfma(za[s], ld8(&Hs[kcm(kr, 32 * s + 8 * kq, kHead)]), x4);
 #pragma unroll
         for (int s = 0; s < 2; ++s)
           if (32 * s + 31 >= 16 * tw)  // (dP o Gamma)[i][t] needs i >= t
@@ -704,7 +705,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         const int kr = 16 * (4 * kh + j) + li;
         f32x4 x3 = zero4();
 #pragma unroll
-        for (int s = 0; s < 4; ++s) x3 = mfma(ea[s], ld8(&S.Hs[kr * KP + 32 * s + 8 * kq]), x3);
+        for (int s = 0; s < 4; ++s) x3 = mfma(ea[s], ld8(&Hs[kcm(kr, 32 * s + 8 * kq, kHead)]), x3);
         const int tr = 16 * tw + 4 * kq;
 #pragma unroll
         for (int r = 0; r < 4; ++r) S.rw.dW[(tr + r) * KP + kr] = f2bf(-x3[r]);
@@ -716,7 +717,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = tid + 512 * i;
-        hd += dot8u(*reinterpret_cast<const uint4*>(&S.Hs[state_pos(e)]), dst[i]);
+        hd += dot8u(*reinterpret_cast<const uint4*>(&Hs[8 * e]), dst[i]);
       }
       hd = wave_sum(hd);
       if (lane == 0) S.hd_part[wave] = hd;
@@ -725,7 +726,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = tid + 512 * i;
-      *reinterpret_cast<uint4*>(&S.Hs[state_pos(e)]) = dst[i];
+      *reinterpret_cast<uint4*>(&Hs[8 * e]) = dst[i];
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -747,7 +748,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         const int kr = 16 * (4 * kh + j) + li;
         f32x4 x2 = zero4();
 #pragma unroll
-        for (int s = 0; s < 4; ++s) x2 = mfma(da[s], ld8(&S.Hs[kr * KP + 32 * s + 8 * kq]), x2);
+        for (int s = 0; s < 4; ++s) x2 = mfma(da[s], ld8(&Hs[kcm(kr, 32 * s + 8 * kq, kHead)]), x2);
         const int tr = 16 * tw + 4 * kq;
         const float4 kv = ld4_bf16(&S.KsT[kr * TP + tr]);
         const float ka_[4] = {kv.x, kv.y, kv.z, kv.w};
@@ -928,7 +929,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     __syncthreads();  // everything is rewritten by the next value head
   }
 
-  if ((threadIdx.x >> 6) == 0) dg_out(h * G + G - 1);
+  {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    if ((tid >> 6) == 0) dg_out(h * G + G - 1, tid & 63);
+  }
 
   // ---- L2-norm backward and scale: x^ . dx^ over all 128 columns (two halves)
   {
@@ -976,7 +981,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         const float dotq = S.dot_q[0][t] + S.dot_q[1][t];
         const float dotk = S.dot_k[0][t] + S.dot_k[1][t];
         const float dqh = scale * adq[j][r];
-        S.Hs[t * KP + kc] = f2bf((dqh - qh[j][r] * dotq) * S.inv_q[t]);
+        Hs[t * KP + kc] = f2bf((dqh - qh[j][r] * dotq) * S.inv_q[t]);
         S.Ks[t * KP + kc] = f2bf((adk[j][r] - kh_[j][r] * dotk) * S.inv_k[t]);
       }
   }
@@ -985,7 +990,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     const int t = e >> 4, sg = e & 15;
     if (t < L) {
       const size_t off = ((size_t)(t0 + t) * H + h) * kHead + sg * 8;
-      *reinterpret_cast<uint4*>(dq + off) = *reinterpret_cast<const uint4*>(&S.Hs[t * KP + sg * 8]);
+      *reinterpret_cast<uint4*>(dq + off) = *reinterpret_cast<const uint4*>(&Hs[t * KP + sg * 8]);
       *reinterpret_cast<uint4*>(dk + off) = *reinterpret_cast<const uint4*>(&S.Ks[t * KP + sg * 8]);
     }
   }

@@ -108,6 +108,11 @@ __device__ __forceinline__ bf16x8 cvt8s(const float* p, const float* f) {
 constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt operand that waits for every vector-memory request of the wave
+// (vmcnt = 0) and leaves the export and LDS counters alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // LDS transpose read (ds_read_b64_tr_b16, gfx950). Within each group of 16
