@@ -31,7 +31,6 @@ namespace gdn {
 
 namespace {
 constexpr int KP = 136;  // LDS pitch (bf16) of [64][128] tiles
-constexpr int TP = 72;   // LDS pitch (bf16) of [128][64] tiles
 
 __device__ __forceinline__ void lower_tile(int t, int& ib, int& jb) {
   ib = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
@@ -270,7 +269,8 @@ constexpr int BP = 72;  // LDS pitch (bf16) of [64][64] tiles
 
 struct BwdLds {
   uint16_t Ks[64 * KP];                     // k^ rows
-  uint16_t KsT[128 * TP], QsT[128 * TP];    // k^, q~ transposed [k][tok]
+  uint16_t Qs[64 * KP];                     // q~ rows (columns of both come from
+                                            // transpose reads)
   uint16_t Pm[64 * BP], PmT[64 * BP];       // dP o Gamma and transpose; then T, T^T;
                                             // then M, M^T
   union {                                   // time-shared regions
@@ -295,8 +295,14 @@ struct BwdLds {
 __device__ __forceinline__ bf16x8 zero8() {
   return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
 }
-__device__ __forceinline__ float4 ld4_bf16(const uint16_t* p) {  // 4 bf16 -> fp32
-  const uint2 u = *reinterpret_cast<const uint2*>(p);
+// Column c0 + lane % 16 of a [64][KP] row tile: rows r0 .. r0 + 7 as an MFMA
+// operand, or rows r0 .. r0 + 3 in fp32 (r0 may differ between lane groups).
+__device__ __forceinline__ bf16x8 col8(const uint16_t* tile, int r0, int c0, int lane) {
+  return __builtin_bit_cast(bf16x8, lds_col8(tile, KP, r0, c0, lane));
+}
+__device__ __forceinline__ float4 col4_bf16(const uint16_t* tile, int r0, int c0, int lane) {
+  const int j = lane & 15;
+  const uint2 u = lds_tr16(tile + (r0 + (j >> 2)) * KP + c0 + 4 * (j & 3));
   return make_float4(bf2f(u.x & 0xffffu), bf2f(u.x >> 16), bf2f(u.y & 0xffffu), bf2f(u.y >> 16));
 }
 __device__ __forceinline__ float dot8u(const uint4& a, const uint4& b) {  // bf16 pairs
@@ -324,10 +330,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
   const int t0 = ci.t0, L = ci.len;
 
   __shared__ __align__(16) BwdLds S;
-  // h, then dh', in the layout both have in global memory ([v / 8][k][v % 8]),
-  // so h arrives by direct global-to-LDS copies; a separate array, so that
-  // those copies are not taken to alias the tiles in S. dq staging at the end.
+  // h and dh' in the layout both have in global memory ([v / 8][k][v % 8]),
+  // filled by direct global-to-LDS copies; arrays of their own, so that those
+  // copies are not taken to alias the tiles in S. dq staging at the end.
   __shared__ __align__(16) uint16_t Hs[kHead * kHead];
+  __shared__ __align__(16) uint16_t Gs[kHead * kHead];
 
   // ---- q, k rows: L2 norm; k^ as rows and transposed, q~ transposed and, for
   //      the products below, as rows (in the Z tile, free until the first
@@ -381,16 +388,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       for (int e = 0; e < 4; ++e) {
         kow[e] = pk2(bf2f(kw[e] & 0xffffu) * ik, bf2f(kw[e] >> 16) * ik);
         qow[e] = pk2(bf2f(qw[e] & 0xffffu) * iqs, bf2f(qw[e] >> 16) * iqs);
-        const uint16_t k0 = kow[e] & 0xffffu, k1 = kow[e] >> 16;
-        const uint16_t q0 = qow[e] & 0xffffu, q1 = qow[e] >> 16;
-        const int d = sg * 8 + 2 * e;
-        S.KsT[d * TP + r] = k0;
-        S.KsT[(d + 1) * TP + r] = k1;
-        S.QsT[d * TP + r] = q0;
-        S.QsT[(d + 1) * TP + r] = q1;
       }
       *reinterpret_cast<uint4*>(&S.Ks[r * KP + sg * 8]) = ko;
-      *reinterpret_cast<uint4*>(&S.rz.Z[r * KP + sg * 8]) = qo;
+      *reinterpret_cast<uint4*>(&S.Qs[r * KP + sg * 8]) = qo;
     }
   }
   __syncthreads();
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       if (jb <= tw) {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          qk[q2] = mfma(ld8(&S.rz.Z[(16 * tw + li) * KP + 32 * s + 8 * kq]),
+          qk[q2] = mfma(ld8(&S.Qs[(16 * tw + li) * KP + 32 * s + 8 * kq]),
                         ld8(&S.Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), qk[q2]);
       }
     }
@@ -462,6 +462,35 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 
   const int G = HV / H;
   const size_t rs = (size_t)HV * kHead;  // token stride of dO, v, dv
+
+  // h and dh' of value head hv_ straight into LDS (Hs, Gs): each wave copies
+  // 1 KiB per request, lane l the 16 bytes at offset 16 l. Issued for the
+  // first value head here and for the next one as soon as the current one is
+  // done with Hs and Gs, so the copies overlap the rest of its work.
+  auto copy_states = [&](int hv_, int wave, int lane) {
+    const uint16_t* hb_ = saved + blk_saved(c, hv_, HV);
+    const uint16_t* dhb_ = bufs.dh + ((size_t)hv_ * NC + c) * (kHead * kHead);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e0 = 512 * i + 64 * wave;  // first 16-byte chunk of the copy
+      __builtin_amdgcn_global_load_lds(hb_ + 8 * (e0 + lane),
+                                       (__attribute__((address_space(3))) void*)(Hs + 8 * e0),
+                                       16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e0 = 512 * i + 64 * wave;
+      __builtin_amdgcn_global_load_lds(dhb_ + 8 * (e0 + lane),
+                                       (__attribute__((address_space(3))) void*)(Gs + 8 * e0),
+                                       16, 0, 0);
+    }
+  };
+  {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    copy_states(h * G, tid >> 6, tid & 63);
+  }
+
   for (int jg = 0; jg < G; ++jg) {
     // Re-derive the thread coordinates each iteration from an opaque copy, so
     // the many LDS addresses built from them are not hoisted out of the loop
@@ -478,7 +507,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     // (chunk-major tiles: see kcm; states: [v / 32][v % 32 / 8][k][v % 8])
     const uint16_t* hb = saved + blk_saved(c, hv, HV);  // h
     const uint16_t* Db = hb + kSavedH;                   // D [tok][v], chunk-major
-    const uint16_t* dhb = bufs.dh + blk * (kHead * kHead);  // dh'
     const uint16_t* dDb = bufs.dD + blk * 8192;          // dD [tok][v], chunk-major
     const uint16_t* dDTb = bufs.dDT + blk * 8192;        // dD^T [v][tok], chunk-major
     const uint16_t* Tg = Tmat + blk * 8192;              // T, then T^T, chunk-major
@@ -489,15 +517,14 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(v) + ((size_t)t0 * HV + hv) * kHead, 0, L * (int)rs * 2, kBufferWord3);
 
-    // ---- h straight into LDS: each wave copies 1 KiB per request (lane l
-    //      the 16 bytes at offset 16 l), oldest of this value head's requests
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e0 = 512 * i + 64 * wave;  // first 16-byte chunk of the copy
-      __builtin_amdgcn_global_load_lds(hb + 8 * (e0 + lane),
-                                       (__attribute__((address_space(3))) void*)(Hs + 8 * e0),
-                                       16, 0, 0);
-    }
+    // ---- gate requests first (every wave; wave 0 uses them), so that their
+    //      wait does not cover the operand requests below
+    const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(g) + (size_t)t0 * HV + hv, 0, L * HV * 4, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(beta) + (size_t)t0 * HV + hv, 0, L * HV * 4, kBufferWord3);
+    float gv = load_f32(rg, lane * HV * 4);  // 0 past the chunk's end
+    const float bv = load_f32(rb, lane * HV * 4);
 
     // ---- requests for the dP phase: the own rows of dO and q, the D rows of
     //      this wave's dP tiles
@@ -526,8 +553,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     // ---- gates (wave 0, after the previous value head's gate gradients)
     if (wave == 0) {
       if (jg > 0) dg_out(hv - 1, lane);
-      float gv = lane < L ? g[(size_t)(t0 + lane) * HV + hv] : 0.f;
-      const float bv = lane < L ? beta[(size_t)(t0 + lane) * HV + hv] : 0.f;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(gv, off, 64);
@@ -540,7 +565,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       S.eg[lane] = exp2_fast(g2);
       S.ebw[lane] = lane < L ? exp2_fast(gl2 - g2) : 0.f;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- dP = dO D^T (i >= j) and P = Gamma o Q~K^T: Pm = dP o Gamma (+ transpose);
     //      F = dP o P row / column partial sums. Wave: row tile tw, col tiles kh, kh + 2.
@@ -588,8 +613,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     // ---- Z = T^T dD (written [tok][v]); dV = diag(beta) Z; dbeta of U.
     //      Wave: token columns of tile tw, value tiles 4 kh .. 4 kh + 3.
     //      First every request of this wave is waited for: the Z operands are
-    //      the youngest, and the copies of h, older, are then in LDS too (for
-    //      the other waves after the barrier below).
+    //      the youngest, and the copies of h and dh', issued before them, are
+    //      then in LDS too (for the other waves after the barrier below).
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     {
       float bp = 0.f;
@@ -617,7 +642,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       bp += __shfl_xor(bp, 32, 64);
       if (kq == 0) S.rowB[kh][trow] = bp;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- key-column passes (columns 16 kt + li, kt = 4 kh .. 4 kh + 3), h from LDS:
     //      pass 1: x1 = dO h^T, x4 = Z h^T (= -T^T dW),
@@ -638,9 +663,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 #pragma unroll
         for (int s = 0; s < 2; ++s)
           if (32 * s <= 16 * tw + 15)  // (dP o Gamma)[t][j] needs j <= t
-            y1 = mfma(pa[s], ld8(&S.KsT[kr * TP + 32 * s + 8 * kq]), y1);
+            y1 = mfma(pa[s], col8(S.Ks, 32 * s + 8 * kq, kr - li, lane), y1);
         const int tr = 16 * tw + 4 * kq;
-        const float4 qv = ld4_bf16(&S.QsT[kr * TP + tr]);
+        const float4 qv = col4_bf16(S.Qs, tr, kr - li, lane);
         const float qa_[4] = {qv.x, qv.y, qv.z, qv.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -665,9 +690,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 #pragma unroll
         for (int s = 0; s < 2; ++s)
           if (32 * s + 31 >= 16 * tw)  // (dP o Gamma)[i][t] needs i >= t
-            y2 = mfma(pta[s], ld8(&S.QsT[kr * TP + 32 * s + 8 * kq]), y2);
+            y2 = mfma(pta[s], col8(S.Qs, 32 * s + 8 * kq, kr - li, lane), y2);
         const int tr = 16 * tw + 4 * kq;
-        const float4 kv = ld4_bf16(&S.KsT[kr * TP + tr]);
+        const float4 kv = col4_bf16(S.Ks, tr, kr - li, lane);
         const float ka_[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -680,26 +705,22 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         }
       }
     }
-    // Requests, oldest first: dh' (staged into LDS once h is no longer read),
-    // the own rows of dD (pass 2 and dT) and of D (pass 3), then the operands
-    // of the dT, Y1 and dA phases, so that each wait covers only what it needs.
-    uint4 dst[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + 512 * i;
-      dst[i] = *reinterpret_cast<const uint4*>(dhb + 8 * e);
-    }
-    bf16x8 ea[4];
+    // Requests, oldest first: the own rows of dD (pass 2 and dT) and of D
+    // (pass 3), then V and T, T^T, staged into LDS once Z and the P tiles are
+    // dead, so that each wait covers only what it needs.
+    bf16x8 ea[4], da[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) ea[s] = ld8(dDb + kcm(trow, 32 * s + 8 * kq, kChunk));
-    // V of the chunk, staged into LDS once Z is dead: two 16-byte pieces per thread
-    uint4 vst[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int e = tid + 512 * i;
-      vst[i] = load_b128(rv, ((e >> 4) * (int)rs + (e & 15) * 8) * 2);
-    }
-    {
+    for (int s = 0; s < 4; ++s) da[s] = ld8(Db + kcm(trow, 32 * s + 8 * kq, kChunk));
+    // two 16-byte pieces per thread of each (named, not an array, so that
+    // they stay in registers)
+    const int ve0 = tid, ve1 = tid + 512;
+    const uint4 vst0 = load_b128(rv, ((ve0 >> 4) * (int)rs + (ve0 & 15) * 8) * 2);
+    const uint4 vst1 = load_b128(rv, ((ve1 >> 4) * (int)rs + (ve1 & 15) * 8) * 2);
+    const uint4 tst0 = *reinterpret_cast<const uint4*>(Tg + 8 * tid);          // T
+    const uint4 tst1 = *reinterpret_cast<const uint4*>(Tg + 8 * (tid + 512));  // T^T
+    {  // pass 2: x3 -> dW
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int kr = 16 * (4 * kh + j) + li;
@@ -712,45 +733,27 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       }
     }
     {
-      // <h, dh'> over the whole state, from the staged elements of this thread
+      // <h, dh'> over the whole state
       float hd = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = tid + 512 * i;
-        hd += dot8u(*reinterpret_cast<const uint4*>(&Hs[8 * e]), dst[i]);
+        hd += dot8u(*reinterpret_cast<const uint4*>(&Hs[8 * e]),
+                    *reinterpret_cast<const uint4*>(&Gs[8 * e]));
       }
       hd = wave_sum(hd);
       if (lane == 0) S.hd_part[wave] = hd;
     }
-    __syncthreads();  // every wave is done with h and Z
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + 512 * i;
-      *reinterpret_cast<uint4*>(&Hs[8 * e]) = dst[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int e = tid + 512 * i;
-      *reinterpret_cast<uint4*>(&S.rz.V[(e >> 4) * KP + (e & 15) * 8]) = vst[i];
-    }
-    bf16x8 da[4];  // own rows of D (pass 3)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) da[s] = ld8(Db + kcm(trow, 32 * s + 8 * kq, kChunk));
-    // T and T^T, staged into LDS (P is dead) after pass 3
-    uint4 tst[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) tst[i] = *reinterpret_cast<const uint4*>(Tg + 8 * (tid + 512 * i));
-    __syncthreads();
-    {
+    {  // pass 3: x2 -> dk^
       float glp = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int kr = 16 * (4 * kh + j) + li;
         f32x4 x2 = zero4();
 #pragma unroll
-        for (int s = 0; s < 4; ++s) x2 = mfma(da[s], ld8(&Hs[kcm(kr, 32 * s + 8 * kq, kHead)]), x2);
+        for (int s = 0; s < 4; ++s) x2 = mfma(da[s], ld8(&Gs[kcm(kr, 32 * s + 8 * kq, kHead)]), x2);
         const int tr = 16 * tw + 4 * kq;
-        const float4 kv = ld4_bf16(&S.KsT[kr * TP + tr]);
+        const float4 kv = col4_bf16(S.Ks, tr, kr - li, lane);
         const float ka_[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -777,10 +780,15 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       glp = wave_sum(glp);
       if (lane == 0) S.gl_part[wave] = glp;
     }
-
-#pragma unroll
-    for (int i = 0; i < 2; ++i)  // T rows into Pm, T^T rows into PmT
-      *reinterpret_cast<uint4*>(&(i == 0 ? S.Pm : S.PmT)[(tid & 63) * BP + (tid >> 6) * 8]) = tst[i];
+    lds_barrier();  // every wave is done with Z, the P tiles, Hs and Gs, and dW is whole
+    *reinterpret_cast<uint4*>(&S.rz.V[(ve0 >> 4) * KP + (ve0 & 15) * 8]) = vst0;
+    *reinterpret_cast<uint4*>(&S.rz.V[(ve1 >> 4) * KP + (ve1 & 15) * 8]) = vst1;
+    // T rows into Pm, T^T rows into PmT (chunk e = tid: row tid % 64, columns 8 (tid / 64) ..)
+    *reinterpret_cast<uint4*>(&S.Pm[(tid & 63) * BP + (tid >> 6) * 8]) = tst0;
+    *reinterpret_cast<uint4*>(&S.PmT[(tid & 63) * BP + (tid >> 6) * 8]) = tst1;
+    // (after the stores above, which wait for their own requests only)
+    if (jg + 1 < G) copy_states(hv + 1, wave, lane);
+    lds_barrier();
 
     // ---- dT = dD (beta V)^T + dW (beta e^gamma K^)^T, strictly lower
     //      (wave: row tile tw, col tiles kh, kh + 2)
@@ -808,7 +816,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
           acc[q2][r] = i > m ? S.bet[m] * (a1[r] + S.eg[m] * a2[r]) : 0.f;
         }
       }
-      __syncthreads();  // every wave has read V and dW
+      lds_barrier();  // every wave has read V and dW
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
         const int m = 16 * (kh + 2 * q2) + li;
@@ -816,7 +824,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         for (int r = 0; r < 4; ++r) S.rz.dT[(16 * tw + 4 * kq + r) * BP + m] = f2bf(acc[q2][r]);
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- Y1 = dT T^T (i > j), stored transposed
     {
@@ -840,14 +848,14 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
             pack4_bf16(y[0], y[1], y[2], y[3]);
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- dA = -T^T Y1 (i > j); M = dA o beta_i Gamma -> Pm, PmT; E = dA o A sums; dbeta of A
     {
       bf16x8 tta[2];  // own rows of T^T, read before M overwrites them
 #pragma unroll
       for (int s = 0; s < 2; ++s) tta[s] = ld8(&S.PmT[trow * BP + 32 * s + 8 * kq]);
-      __syncthreads();
+      lds_barrier();
       float re[4] = {0.f, 0.f, 0.f, 0.f}, rb[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
@@ -903,7 +911,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- dk^ += M K^ + M^T K^
     {
@@ -919,14 +927,14 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         f32x4 acc = adk[j];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const bf16x8 kc = ld8(&S.KsT[kr * TP + 32 * s + 8 * kq]);
+          const bf16x8 kc = col8(S.Ks, 32 * s + 8 * kq, kr - li, lane);
           if (32 * s <= 16 * tw + 15) acc = mfma(ma[s], kc, acc);
           if (32 * s + 31 >= 16 * tw) acc = mfma(mta[s], kc, acc);
         }
         adk[j] = acc;
       }
     }
-    __syncthreads();  // everything is rewritten by the next value head
+    lds_barrier();  // everything is rewritten by the next value head
   }
 
   {

@@ -56,6 +56,9 @@ __device__ __forceinline__ uint2 load_b64(__amdgpu_buffer_rsrc_t r, int byte_off
   const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
   return make_uint2(x[0], x[1]);
 }
+__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
 __device__ __forceinline__ bf16x8 ld8_buf(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(bf16x8, load_b128(r, byte_off));
 }
@@ -112,6 +115,23 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // (vmcnt = 0) and leaves the export and LDS counters alone (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
+
+// s_waitcnt operand that waits for every LDS (and scalar-memory) request of
+// the wave (lgkmcnt = 0) and leaves the vector-memory and export counters alone.
+constexpr int kWaitLgkm0 = 0xF | (7 << 4) | (3 << 14);
+
+// Workgroup barrier for LDS traffic only: this wave's LDS reads and writes are
+// complete, then all waves meet. Unlike __syncthreads() it does not wait for
+// the wave's global requests - in particular not for global-to-LDS copies
+// still in flight, whose readers wait for them (s_waitcnt vmcnt) themselves.
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
