@@ -51,6 +51,27 @@ KERNEL_FLOPS = {
 }
 
 
+
+def kernel_bytes(stage, T, N, H, HV, units):
+    """Algorithmic HBM bytes of one launch of a stage of the step: every input,
+    workspace hand-off and output read or written once (bf16 tensors and tiles,
+    fp32 gates and states). units = (chunk, value head) pairs."""
+    qk, vv, gb = T * H * D * 2, T * HV * D * 2, T * HV * 4
+    st = N * HV * D * D * 4                               # fp32 states of the sequences
+    t_cd, t_cc, s_bf = C * D * 2, C * C * 2, D * D * 2    # 64x128 and 64x64 tiles, bf16 state
+    fwd_ops = 4 * t_cd + t_cc + 4                         # W, U, Q_g, K_bwd; P; e^gamma_L
+    bwd_ops = 3 * t_cd + 3 * t_cc + 4                     # W^T, Q_g^T, K_bwd; P^T, T, T^T; e^gamma_L
+    return {
+        "chunk_prep": 2 * qk + vv + 2 * gb + units * (fwd_ops + bwd_ops),
+        # reads the forward operands, h0; writes o, hT, the saved state and D
+        "fwd_scan": units * fwd_ops + 2 * st + vv + units * (s_bf + t_cd),
+        # reads W^T, Q_g^T, K_bwd, P^T, e^gamma_L, dO; writes dh0, dh', dD, dD^T
+        "bwd_dh_scan": units * (3 * t_cd + t_cc + 4) + vv + st + units * (s_bf + 2 * t_cd),
+        # reads q, k, v, dO, g, beta, h, D, dh', dD, dD^T, T, T^T; writes dq, dk, dv, dg, dbeta
+        "bwd_chunk": 4 * qk + 3 * vv + 4 * gb + units * (2 * s_bf + 3 * t_cd + 2 * t_cc),
+    }.get(stage, 0)
+
+
 # stage name (gdn_stage_name) -> kernel symbol as the profiler names it
 STAGE_KERNELS = {"chunk_table": "chunk_table_kernel", "chunk_prep": "chunk_prep_kernel<true>",
                  "fwd_scan": "fwd_scan_kernel<true, true, false>",
@@ -453,12 +474,26 @@ def main():
     step_flops = F_FWDBWD * units
     tokens_per_s = T / (ms_per_step * 1e-3)
     mfma_frac = step_flops / (ms_per_step * 1e-3) / PEAK_BF16
+    # Roofline of the dominant kernel: its algorithmic flops and bytes per
+    # launch; below the chip's balance point (peak flops / peak bandwidth) the
+    # roof is HBM bandwidth, above it the bf16 MFMA rate.
+    t_dom = stage_ms[dom] * 1e-3
     dom_flops = KERNEL_FLOPS.get(dom, 0) * units
-    dom_achieved = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "achieved": round(dom_achieved, 3), "peak": PEAK_BF16 / 1e12,
-                "unit": "TFLOP/s", "frac": round(dom_achieved * 1e12 / PEAK_BF16, 5),
-                "traffic": recorded_traffic(STAGE_KERNELS.get(dom, dom)), "kernel": dom,
-                "kernel_ms": round(stage_ms[dom], 4)}
+    dom_bytes = kernel_bytes(dom, T, N, H, HV, units)
+    flops_frac = dom_flops / t_dom / PEAK_BF16
+    if dom_bytes and dom_flops / dom_bytes < PEAK_BF16 / PEAK_HBM:
+        achieved = dom_bytes / t_dom / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9,
+                    "unit": "GB/s", "frac": round(achieved * 1e9 / PEAK_HBM, 5)}
+    else:
+        achieved = dom_flops / t_dom / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16 / 1e12,
+                    "unit": "TFLOP/s", "frac": round(flops_frac, 5)}
+    roofline.update({"traffic": recorded_traffic(STAGE_KERNELS.get(dom, dom)), "kernel": dom,
+                     "kernel_ms": round(stage_ms[dom], 4), "algorithmic_bytes": dom_bytes,
+                     "algorithmic_flops": dom_flops,
+                     "flop_per_byte": round(dom_flops / dom_bytes, 2) if dom_bytes else None,
+                     "mfma_frac": round(flops_frac, 5)})
 
     extra = None
     if not args.no_secondary:
