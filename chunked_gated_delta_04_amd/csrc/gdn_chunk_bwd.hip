@@ -42,8 +42,22 @@ __device__ __forceinline__ bf16x8 ld8_or0(const uint16_t* p, bool ok) {
   return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
 }
 
-// sum over the 16 lanes of a 16-lane group (lanes sharing kq)
-__device__ __forceinline__ float sum16(float x) { return group_sum<16>(x); }
+// Sum over the 16 lanes of a 16-lane group (lanes sharing kq), complete in
+// the group's first lane only (the others hold partial sums): DPP row shifts
+// within the 16-lane row, lane i adding lane i + 1, 2, 4, 8 (lanes past the
+// row's end read as zero) - VALU work in a fixed order, instead of four LDS
+// swizzles.
+template <int N>
+__device__ __forceinline__ float row_shl(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + N, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float sum16_lane0(float x) {
+  x += row_shl<1>(x);
+  x += row_shl<2>(x);
+  x += row_shl<4>(x);
+  x += row_shl<8>(x);
+  return x;
+}
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -604,7 +618,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
             pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) rowp[r] = sum16(rowp[r]);
+      for (int r = 0; r < 4; ++r) rowp[r] = sum16_lane0(rowp[r]);
       if (li == 0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) S.rowF[kh][16 * tw + 4 * kq + r] = rowp[r];
@@ -767,8 +781,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        gr[r] = sum16(gr[r]);
-        br[r] = sum16(br[r]);
+        gr[r] = sum16_lane0(gr[r]);
+        br[r] = sum16_lane0(br[r]);
       }
       if (li == 0) {
 #pragma unroll
@@ -900,8 +914,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        re[r] = sum16(re[r]);
-        rb[r] = sum16(rb[r]);
+        re[r] = sum16_lane0(re[r]);
+        rb[r] = sum16_lane0(rb[r]);
       }
       if (li == 0) {
 #pragma unroll
@@ -969,8 +983,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      dq_[r] = sum16(dq_[r]);
-      dk_[r] = sum16(dk_[r]);
+      dq_[r] = sum16_lane0(dq_[r]);
+      dk_[r] = sum16_lane0(dk_[r]);
     }
     if (li == 0) {
 #pragma unroll

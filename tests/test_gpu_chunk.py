@@ -201,6 +201,20 @@ def test_backward_matches_oracle_small_varlen(with_dhT):
     _check_grads(grads, ref, "small")
 
 
+@pytest.mark.parametrize("H,HV", [(2, 2), (1, 3), (1, 4)])
+def test_backward_matches_oracle_for_other_head_groups(H, HV):
+    """One, three and four value heads per key head: the gradient kernel
+    walks the value heads of a key head in order, copying the next one's
+    states in while it finishes the current one."""
+    _say(f"bwd head groups H={H} HV={HV}")
+    lens = [1, 64, 130]
+    inp = small_inputs(lens=lens, H=H, HV=HV, seed=11, with_do=True)
+    dhT = 0.1 * torch.randn(len(lens), HV, 128, 128, generator=torch.Generator().manual_seed(5))
+    o, hT, grads = run_fwd_bwd(inp, dhT=dhT)
+    ref = oracle_backward(inp, dhT=dhT)
+    _check_grads(grads, ref, f"H{H}HV{HV}")
+
+
 def test_backward_full_size_sampled_heads_and_determinism():
     _say("bwd full 2x8192")
     inp = synth.workload_inputs("fwdbwd_2x8192_h16_hv32")
