@@ -43,21 +43,9 @@ __device__ __forceinline__ bf16x8 ld8_or0(const uint16_t* p, bool ok) {
 }
 
 // Sum over the 16 lanes of a 16-lane group (lanes sharing kq), complete in
-// the group's first lane only (the others hold partial sums): DPP row shifts
-// within the 16-lane row, lane i adding lane i + 1, 2, 4, 8 (lanes past the
-// row's end read as zero) - VALU work in a fixed order, instead of four LDS
-// swizzles.
-template <int N>
-__device__ __forceinline__ float row_shl(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + N, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float sum16_lane0(float x) {
-  x += row_shl<1>(x);
-  x += row_shl<2>(x);
-  x += row_shl<4>(x);
-  x += row_shl<8>(x);
-  return x;
-}
+// the group's first lane only: DPP row shifts (VALU work in a fixed order)
+// instead of four LDS swizzles.
+__device__ __forceinline__ float sum16_lane0(float x) { return row_sum_first_lane(x); }
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -454,12 +442,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       }
       x += glsum + exp2_fast(S.gam[L - 1]) * hdsum;
     }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {  // suffix sums; lane t reads lane t + off
-      const float y = __int_as_float(__builtin_amdgcn_ds_bpermute(((t + off) & 63) << 2,
-                                                                  __float_as_int(x)));
-      if (t + off < 64) x += y;
-    }
+    x = wave_suffix_sum(x, t);
     if (t < L) {
       dg[(size_t)(t0 + t) * HV + hv_] = x;
       dbeta[(size_t)(t0 + t) * HV + hv_] = dbt;
@@ -567,15 +550,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     // ---- gates (wave 0, after the previous value head's gate gradients)
     if (wave == 0) {
       if (jg > 0) dg_out(hv - 1, lane);
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(gv, off, 64);
-        if (lane >= off) gv += y;
-      }
+      gv = wave_prefix_sum(gv, lane);  // as in the forward's WY pass
       const float g2 = gv * kLog2e;  // base-2 exponent
       S.gam[lane] = g2;
       S.bet[lane] = bv;
-      const float gl2 = __shfl(g2, L - 1, 64);
+      const float gl2 = lane_value(g2, L - 1);
       S.eg[lane] = exp2_fast(g2);
       S.ebw[lane] = lane < L ? exp2_fast(gl2 - g2) : 0.f;
     }
@@ -755,7 +734,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         hd += dot8u(*reinterpret_cast<const uint4*>(&Hs[8 * e]),
                     *reinterpret_cast<const uint4*>(&Gs[8 * e]));
       }
-      hd = wave_sum(hd);
+      hd = wave_sum_uniform(hd);
       if (lane == 0) S.hd_part[wave] = hd;
     }
     {  // pass 3: x2 -> dk^
@@ -791,7 +770,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
           S.rowB2[kh][16 * tw + 4 * kq + r] = br[r];
         }
       }
-      glp = wave_sum(glp);
+      glp = wave_sum_uniform(glp);
       if (lane == 0) S.gl_part[wave] = glp;
     }
     lds_barrier();  // every wave is done with Z, the P tiles, Hs and Gs, and dW is whole

@@ -208,13 +208,9 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     if (wave == 0) {
       float gv = lane < L ? g[(size_t)(t0 + lane) * HV + hv] : 0.f;
       const float bv = lane < L ? beta[(size_t)(t0 + lane) * HV + hv] : 0.f;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(gv, off, 64);
-        if (lane >= off) gv += y;
-      }
+      gv = wave_prefix_sum(gv, lane);
       const float g2 = gv * kLog2e;
-      const float gl2 = __shfl(g2, L - 1, 64);
+      const float gl2 = lane_value(g2, L - 1);
       gam[lane] = g2;
       bet[lane] = bv;
       const float e = exp2_fast(g2);

@@ -236,6 +236,64 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// DPP row shifts inside each 16-lane row of the wave; a lane whose source
+// falls outside its row reads 0.
+template <int N>
+__device__ __forceinline__ float dpp_row_shr(float x) {  // lane i <- lane i - N
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xF, 0xF, true));
+}
+template <int N>
+__device__ __forceinline__ float dpp_row_shl(float x) {  // lane i <- lane i + N
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + N, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float lane_value(float x, int l) {  // x of lane l (l uniform)
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// Sum of each 16-lane row, complete in the row's first lane (the others hold
+// partial sums): lane i adds lane i + 1, 2, 4, 8.
+__device__ __forceinline__ float row_sum_first_lane(float x) {
+  x += dpp_row_shl<1>(x);
+  x += dpp_row_shl<2>(x);
+  x += dpp_row_shl<4>(x);
+  x += dpp_row_shl<8>(x);
+  return x;
+}
+
+// Inclusive prefix sum over the 64 lanes, in a fixed order: a scan inside
+// each 16-lane row, then the totals of the earlier rows, nearest first.
+// lane: the caller's lane index.
+__device__ __forceinline__ float wave_prefix_sum(float x, int lane) {
+  x += dpp_row_shr<1>(x);
+  x += dpp_row_shr<2>(x);
+  x += dpp_row_shr<4>(x);
+  x += dpp_row_shr<8>(x);
+  const float r0 = lane_value(x, 15), r1 = lane_value(x, 31), r2 = lane_value(x, 47);
+  const int row = lane >> 4;
+  if (row == 3) x += r2;
+  if (row >= 2) x += r1;
+  if (row >= 1) x += r0;
+  return x;
+}
+
+// Suffix sum (lane t: lanes t .. 63) in a fixed order: a reverse scan inside
+// each row, then the totals of the later rows, nearest first.
+__device__ __forceinline__ float wave_suffix_sum(float x, int lane) {
+  x = row_sum_first_lane(x);
+  const float r1 = lane_value(x, 16), r2 = lane_value(x, 32), r3 = lane_value(x, 48);
+  const int row = lane >> 4;
+  if (row == 0) x += r1;
+  if (row <= 1) x += r2;
+  if (row <= 2) x += r3;
+  return x;
+}
+
+// Sum over the 64 lanes, the same value in every lane, in a fixed order.
+__device__ __forceinline__ float wave_sum_uniform(float x) {
+  x = row_sum_first_lane(x);
+  return ((lane_value(x, 0) + lane_value(x, 16)) + lane_value(x, 32)) + lane_value(x, 48);
+}
+
 // Sum over groups of `W` consecutive lanes (W a power of two <= 64).
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {
