@@ -585,8 +585,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
               colp += f;
             }
           }
-          colp += __shfl_xor(colp, 16, 64);
-          colp += __shfl_xor(colp, 32, 64);
+          colp = sum_over_rows(colp);
           if (kq == 0) S.colF[wave][j] = colp;
         } else if (kq == 0) {
           S.colF[wave][j] = 0.f;  // every slot of the wave's column tiles is written
@@ -631,8 +630,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
               pack4_bf16(bt * z[0], bt * z[1], bt * z[2], bt * z[3]);
         }
       }
-      bp += __shfl_xor(bp, 16, 64);
-      bp += __shfl_xor(bp, 32, 64);
+      bp = sum_over_rows(bp);
       if (kq == 0) S.rowB[kh][trow] = bp;
     }
     lds_barrier();
@@ -880,8 +878,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
               colp += e_;
             }
           }
-          colp += __shfl_xor(colp, 16, 64);
-          colp += __shfl_xor(colp, 32, 64);
+          colp = sum_over_rows(colp);
           if (kq == 0) S.colE[wave][j] = colp;
         } else if (kq == 0) {
           S.colE[wave][j] = 0.f;

@@ -294,6 +294,16 @@ __device__ __forceinline__ float wave_sum_uniform(float x) {
   return ((lane_value(x, 0) + lane_value(x, 16)) + lane_value(x, 32)) + lane_value(x, 48);
 }
 
+// Sum over the four 16-lane rows of the wave (lanes i, i + 16, i + 32,
+// i + 48), the same value in all four: the gfx950 row swaps (32-lane halves,
+// then 16-lane rows) as VALU operations, (r0 + r2) + (r1 + r3) in every lane.
+__device__ __forceinline__ float sum_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Sum over groups of `W` consecutive lanes (W a power of two <= 64).
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {
