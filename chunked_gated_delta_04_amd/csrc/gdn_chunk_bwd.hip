@@ -524,26 +524,42 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     const float bv = load_f32(rb, lane * HV * 4);
 
     // ---- requests for the dP phase: the own rows of dO and q, the D rows of
-    //      this wave's dP tiles
+    //      this wave's dP tiles. Operand pieces the wave does not use (tiles
+    //      above the diagonal, token blocks before its own) are requested past
+    //      the end of a range-checked buffer, which returns zeros and moves no
+    //      data, so every wave issues the same requests with no branch.
+    constexpr int kTileBytes = kChunk * kHead * 2, kTBytes = kChunk * kChunk * 2;
+    const __amdgpu_buffer_rsrc_t rD = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(Db), 0, kTileBytes, kBufferWord3);
     bf16x8 oa[4], dfr[2][4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       oa[s] = ld8_buf(rdO, (trow * (int)rs + 32 * s + 8 * kq) * 2);
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2)
-        dfr[q2][s] = ld8(Db + kcm(16 * (kh + 2 * q2) + li, 32 * s + 8 * kq, kChunk));
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const int jb = kh + 2 * q2;
+        dfr[q2][s] = ld8_buf(rD, jb <= tw ? kcm(16 * jb + li, 32 * s + 8 * kq, kChunk) * 2 : kTileBytes);
+      }
     }
 
     // requests for the Z phase: T^T rows of this wave's tokens, dD^T rows, v rows
+    // (token blocks s with 32 s + 31 < 16 tw meet only zeros of T)
+    const __amdgpu_buffer_rsrc_t rTT = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(Tg) + 4096, 0, kTBytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rDDT = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(dDTb), 0, kTileBytes, kBufferWord3);
     bf16x8 tt[2], ddt[4][2];
     uint2 vr[4];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) tt[s] = ld8(Tg + 4096 + kcm(trow, 32 * s + 8 * kq, 64));
+    for (int s = 0; s < 2; ++s)
+      tt[s] = ld8_buf(rTT, 32 * s + 31 >= 16 * tw ? kcm(trow, 32 * s + 8 * kq, 64) * 2 : kTBytes);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int vt = 4 * kh + j;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) ddt[j][s] = ld8(dDTb + kcm(16 * vt + li, 32 * s + 8 * kq, kHead));
+      for (int s = 0; s < 2; ++s)
+        ddt[j][s] = ld8_buf(rDDT, 32 * s + 31 >= 16 * tw
+                                      ? kcm(16 * vt + li, 32 * s + 8 * kq, kHead) * 2 : kTileBytes);
       vr[j] = load_b64(rv, (trow * (int)rs + 16 * vt + 4 * kq) * 2);
     }
 
