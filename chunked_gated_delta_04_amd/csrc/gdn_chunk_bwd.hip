@@ -338,6 +338,37 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
   __shared__ __align__(16) uint16_t Hs[kHead * kHead];
   __shared__ __align__(16) uint16_t Gs[kHead * kHead];
 
+  const int G = HV / H;
+
+  // h and dh' of value head hv_ straight into LDS (Hs, Gs): each wave copies
+  // 1 KiB per request, lane l the 16 bytes at offset 16 l. Issued for the
+  // first value head before anything else (so the copies overlap the q, k
+  // loads and norms) and for the next one as soon as the current one is done
+  // with Hs and Gs, so the copies overlap the rest of its work.
+  auto copy_states = [&](int hv_, int wave, int lane) {
+    const uint16_t* hb_ = saved + blk_saved(c, hv_, HV);
+    const uint16_t* dhb_ = bufs.dh + ((size_t)hv_ * NC + c) * (kHead * kHead);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e0 = 512 * i + 64 * wave;  // first 16-byte chunk of the copy
+      __builtin_amdgcn_global_load_lds(hb_ + 8 * (e0 + lane),
+                                       (__attribute__((address_space(3))) void*)(Hs + 8 * e0),
+                                       16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e0 = 512 * i + 64 * wave;
+      __builtin_amdgcn_global_load_lds(dhb_ + 8 * (e0 + lane),
+                                       (__attribute__((address_space(3))) void*)(Gs + 8 * e0),
+                                       16, 0, 0);
+    }
+  };
+  {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    copy_states(h * G, tid >> 6, tid & 63);
+  }
+
   // ---- q, k rows: L2 norm; k^ as rows and transposed, q~ transposed and, for
   //      the products below, as rows (in the Z tile, free until the first
   //      value head forms Z). 16 threads per row, so each request covers whole rows.
@@ -395,7 +426,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       *reinterpret_cast<uint4*>(&S.Qs[r * KP + sg * 8]) = qo;
     }
   }
-  __syncthreads();
+  lds_barrier();  // (not __syncthreads: that would wait for the state copies)
 
   // ---- Q~ K^T of the key head, the same for all its value heads, kept in
   //      registers: qk[q2][r] = (Q~ K^T)[i][j] with i = 16 tw + 4 kq + r,
@@ -457,36 +488,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     adk[j] = zero4();
   }
 
-  const int G = HV / H;
   const size_t rs = (size_t)HV * kHead;  // token stride of dO, v, dv
 
-  // h and dh' of value head hv_ straight into LDS (Hs, Gs): each wave copies
-  // 1 KiB per request, lane l the 16 bytes at offset 16 l. Issued for the
-  // first value head here and for the next one as soon as the current one is
-  // done with Hs and Gs, so the copies overlap the rest of its work.
-  auto copy_states = [&](int hv_, int wave, int lane) {
-    const uint16_t* hb_ = saved + blk_saved(c, hv_, HV);
-    const uint16_t* dhb_ = bufs.dh + ((size_t)hv_ * NC + c) * (kHead * kHead);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e0 = 512 * i + 64 * wave;  // first 16-byte chunk of the copy
-      __builtin_amdgcn_global_load_lds(hb_ + 8 * (e0 + lane),
-                                       (__attribute__((address_space(3))) void*)(Hs + 8 * e0),
-                                       16, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e0 = 512 * i + 64 * wave;
-      __builtin_amdgcn_global_load_lds(dhb_ + 8 * (e0 + lane),
-                                       (__attribute__((address_space(3))) void*)(Gs + 8 * e0),
-                                       16, 0, 0);
-    }
-  };
-  {
-    int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));
-    copy_states(h * G, tid >> 6, tid & 63);
-  }
 
   for (int jg = 0; jg < G; ++jg) {
     // Re-derive the thread coordinates each iteration from an opaque copy, so
