@@ -258,12 +258,13 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
 // value heads of the key head run in order. Wave w owns token tile tw = w & 3
 // (tokens 16 tw .. 16 tw + 15) and column half kh = w >> 2 (key or value
 // columns 64 kh .. 64 kh + 63) of every token-indexed result. Matrices that
-// are contracted over the chunk's tokens are kept in LDS transposed as well
-// (bf16), so every MFMA operand is one 16-byte read. The operands each phase
-// reads from HBM are requested a phase ahead (the state h is copied straight
-// into LDS with the first requests of a value head, then the state gradient
-// dh' takes its place), so the workgroup - alone on its CU - does not stall on
-// memory at every phase.
+// are contracted over the chunk's tokens are kept in LDS as bf16 rows (tiles
+// of 64 x 64 also transposed); their columns come from transposing LDS reads,
+// so every MFMA operand is one or two LDS reads. The state h and its gradient
+// dh' are copied straight from HBM into LDS (first thing for the first value
+// head, and for the next one as soon as the current one is done with them);
+// each phase's other operands are requested a phase ahead, so the workgroup -
+// alone on its CU - does not stall on memory at every phase.
 // Per-token and per-column partial sums go to LDS slots owned by one wave each
 // and are added once per value head in a fixed order.
 namespace {
@@ -369,9 +370,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     copy_states(h * G, tid >> 6, tid & 63);
   }
 
-  // ---- q, k rows: L2 norm; k^ as rows and transposed, q~ transposed and, for
-  //      the products below, as rows (in the Z tile, free until the first
-  //      value head forms Z). 16 threads per row, so each request covers whole rows.
+  // ---- q, k rows: L2 norm; k^ and q~ as rows (Ks, Qs). 16 threads per row,
+  //      so each request covers whole rows.
   {
     const int tid = threadIdx.x;
     const int sg = tid & 15;
