@@ -652,6 +652,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       bp = sum_over_rows(bp);
       if (kq == 0) S.rowB[kh][trow] = bp;
     }
+    // the own rows of dD (pass 2 and dT), requested as soon as the Z operands
+    // are dead, so that passes 1a and 1b cover their wait
+    bf16x8 ea[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) ea[s] = ld8(dDb + kcm(trow, 32 * s + 8 * kq, kChunk));
     lds_barrier();
 
     // ---- key-column passes (columns 16 kt + li, kt = 4 kh .. 4 kh + 3), h from LDS:
@@ -715,15 +720,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         }
       }
     }
-    // Requests, oldest first: the own rows of dD (pass 2 and dT) and of D
-    // (pass 3), then V and T, T^T, staged into LDS once Z and the P tiles are
-    // dead, so that each wait covers only what it needs.
-    bf16x8 ea[4], da[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) ea[s] = ld8(dDb + kcm(trow, 32 * s + 8 * kq, kChunk));
+    // Requests: the own rows of D (pass 3), then V and T, T^T, staged into
+    // LDS once Z and the P tiles are dead.
+    bf16x8 da[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) da[s] = ld8(Db + kcm(trow, 32 * s + 8 * kq, kChunk));
-    // two 16-byte pieces per thread of each (named, not an array, so that
+    // Two 16-byte pieces per thread of each (named, not an array, so that
     // they stay in registers)
     const int ve0 = tid, ve1 = tid + 512;
     const uint4 vst0 = load_b128(rv, ((ve0 >> 4) * (int)rs + (ve0 & 15) * 8) * 2);
