@@ -241,6 +241,33 @@ def test_backward_full_size_sampled_heads_and_determinism():
                        atol=1e-2 * float(np.abs(dg_ref).max()))
 
 
+def test_backward_with_device_only_boundaries_matches_host_route_bitwise():
+    """Without a host copy of cu_seqlens the chunk count is the bound T/64 + N,
+    so the table holds unused slots that every backward kernel must skip; the
+    results equal those of the exactly sized call bit for bit."""
+    _say("bwd device-only boundaries")
+    lens = [1, 63, 64, 65, 0, 130]
+    inp = small_inputs(lens=lens, seed=13, with_do=True)
+    d = to_dev(inp)
+    host = inp["cu_seqlens"].to(torch.int32)
+
+    def run(hc):
+        o, hT, saved = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                                     h0=d["h0"], cu_seqlens_host=hc, save_for_backward=True)
+        gr = gdn.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], saved,
+                           d["do"], cu_seqlens_host=hc)
+        rc = gdn.chunk_bwd_recompute(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                                     d["do"], h0=d["h0"], cu_seqlens_host=hc)
+        return o, hT, gr, rc
+    o1, h1, g1, r1 = run(host)
+    o2, h2, g2, r2 = run(None)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    for name in g1:
+        assert torch.equal(g1[name], g2[name]), name
+        assert torch.equal(r1[name], r2[name]), name
+        assert torch.equal(g1[name], r1[name]), name
+
+
 def test_backward_repeats_bitwise_many_times_and_on_a_side_stream():
     inp = small_inputs(with_do=True)
     o, hT, g0 = run_fwd_bwd(inp)

@@ -168,6 +168,24 @@ def test_paged_forward_equals_gathered_states_bitwise_and_continues():
     assert np.array_equal(f64(p), pool_ref)
 
 
+def test_device_only_boundaries_match_the_host_route_bitwise():
+    _say("conv device-only boundaries")
+    inp = synth.conv_inputs(LENS, 64, 4, seed=104, bias=True, state=True, with_dy=True)
+    d = to_dev(inp)
+
+    def run(hc):
+        y, so = gdn.conv_fwd(d["x"], d["weight"], d["bias"], d["cu_seqlens"], state_in=d["state_in"],
+                             cu_seqlens_host=hc)
+        gr = gdn.conv_bwd(d["x"], d["weight"], d["bias"], d["cu_seqlens"], d["dy"],
+                          state_in=d["state_in"], cu_seqlens_host=hc)
+        return y, so, gr
+    y1, s1, g1 = run(inp["cu_seqlens"])
+    y2, s2, g2 = run(None)
+    assert torch.equal(y1, y2) and torch.equal(s1, s2)
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), k
+
+
 def test_no_tokens():
     C, W = 64, 4
     e = torch.empty(0, C, dtype=torch.bfloat16, device="cuda")
