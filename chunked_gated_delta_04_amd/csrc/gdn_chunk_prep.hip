@@ -204,10 +204,24 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     const size_t blk = (size_t)hv * NC + c;
 
     // ---- 2. gates: gamma = inclusive cumsum of g inside the chunk (kept in
-    //      base 2); the value rows go to LDS as they are
+    //      base 2); the value rows go to LDS as they are. All rows through
+    //      range-checked buffer loads (rows at or past the chunk's end read as
+    //      zeros, no branch), the value rows requested before anything waits.
+    const int vr0 = tid >> 2, vsg0 = (tid & 3) * 4;
+    uint4 vx[4];
+    {
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(v) + ((size_t)t0 * HV + hv) * kHead, 0, L * HV * kHead * 2, kBufferWord3);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vx[j] = load_b128(rv, (vr0 * HV * kHead + (vsg0 + j) * 8) * 2);
+    }
     if (wave == 0) {
-      float gv = lane < L ? g[(size_t)(t0 + lane) * HV + hv] : 0.f;
-      const float bv = lane < L ? beta[(size_t)(t0 + lane) * HV + hv] : 0.f;
+      const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(g) + (size_t)t0 * HV + hv, 0, L * HV * 4, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(beta) + (size_t)t0 * HV + hv, 0, L * HV * 4, kBufferWord3);
+      float gv = load_f32(rg, lane * HV * 4);
+      const float bv = load_f32(rb, lane * HV * 4);
       gv = wave_prefix_sum(gv, lane);
       const float g2 = gv * kLog2e;
       const float gl2 = lane_value(g2, L - 1);
@@ -222,16 +236,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
         if (kB) bo.gL[blk] = exp2_fast(gl2);
       }
     }
-    {
-      const int r = tid >> 2, sg0 = (tid & 3) * 4;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (r < L)
-          x = *reinterpret_cast<const uint4*>(v + ((size_t)(t0 + r) * HV + hv) * kHead + (sg0 + j) * 8);
-        *reinterpret_cast<uint4*>(&Vs[r * KP + (sg0 + j) * 8]) = x;
-      }
-    }
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&Vs[vr0 * KP + (vsg0 + j) * 8]) = vx[j];
     __syncthreads();
 
     // ---- 3. A (fp32, LDS: 10 lower tiles, 6 zero upper tiles) and P (bf16,
