@@ -55,18 +55,22 @@ KERNEL_FLOPS = {
 def kernel_bytes(stage, T, N, H, HV, units):
     """Algorithmic HBM bytes of one launch of a stage of the step: every input,
     workspace hand-off and output read or written once (bf16 tensors and tiles,
-    fp32 gates and states). units = (chunk, value head) pairs."""
+    fp32 gates and states). units = (chunk, value head) pairs; the normalised
+    q and k tiles exist once per (chunk, key head), units * H / HV of them."""
     qk, vv, gb = T * H * D * 2, T * HV * D * 2, T * HV * 4
     st = N * HV * D * D * 4                               # fp32 states of the sequences
     t_cd, t_cc, s_bf = C * D * 2, C * C * 2, D * D * 2    # 64x128 and 64x64 tiles, bf16 state
-    fwd_ops = 4 * t_cd + t_cc + 4                         # W, U, Q_g, K_bwd; P; e^gamma_L
-    bwd_ops = 3 * t_cd + 3 * t_cc + 4                     # W^T, Q_g^T, K_bwd; P^T, T, T^T; e^gamma_L
+    kunits = units * H // HV                              # (chunk, key head) pairs
+    gates = 4 + 2 * C * 4                                 # e^gamma_L, e^gamma, e^(gamma_L - gamma)
+    fwd_ops = units * (2 * t_cd + t_cc + gates) + kunits * 2 * t_cd    # W, U^T, P; Q~, K^T
+    bwd_ops = units * (t_cd + 3 * t_cc + gates) + kunits * 2 * t_cd    # W^T, P^T, T, T^T; Q~^T, K^
     return {
-        "chunk_prep": 2 * qk + vv + 2 * gb + units * (fwd_ops + bwd_ops),
+        "chunk_prep": 2 * qk + vv + 2 * gb + fwd_ops + bwd_ops,
         # reads the forward operands, h0; writes o, hT, the saved state and D
-        "fwd_scan": units * fwd_ops + 2 * st + vv + units * (s_bf + t_cd),
-        # reads W^T, Q_g^T, K_bwd, P^T, e^gamma_L, dO; writes dh0, dh', dD, dD^T
-        "bwd_dh_scan": units * (3 * t_cd + t_cc + 4) + vv + st + units * (s_bf + 2 * t_cd),
+        "fwd_scan": fwd_ops + 2 * st + vv + units * (s_bf + t_cd),
+        # reads W^T, P^T, the gates, Q~^T, K^, dO; writes dh0, dh', dD, dD^T
+        "bwd_dh_scan": units * (t_cd + t_cc + gates) + kunits * 2 * t_cd + vv + st
+                       + units * (s_bf + 2 * t_cd),
         # reads q, k, v, dO, g, beta, h, D, dh', dD, dD^T, T, T^T; writes dq, dk, dv, dg, dbeta
         "bwd_chunk": 4 * qk + 3 * vv + 4 * gb + units * (2 * s_bf + 3 * t_cd + 2 * t_cc),
     }.get(stage, 0)

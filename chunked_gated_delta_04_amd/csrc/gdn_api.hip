@@ -27,7 +27,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
-  size_t table, seq_first, W, U, Qg, P, Kb, gL, T, dh, dD, dDT, total;
+  size_t table, seq_first, W, U, Qn, P, Kn, gL, gE, T, dh, dD, dDT, total;
 };
 
 // Chunk slots: exact with a host copy of the boundaries, else T/64 + N.
@@ -72,17 +72,19 @@ gdn_status check_problem(const gdn_problem* p, int64_t* nc) {
 Layout make_layout(const gdn_problem* p, int64_t NC, bool bwd) {
   Layout L;
   const size_t blocks = (size_t)p->HV * (size_t)NC;
+  const size_t kblocks = (size_t)p->H * (size_t)NC;
   size_t off = 0;
   L.table = off;     off = align_up(off + sizeof(ChunkInfo) * (size_t)NC);
   L.seq_first = off; off = align_up(off + sizeof(int32_t) * (size_t)(p->N + 1));
-  L.W = L.U = L.Qg = L.P = L.Kb = L.gL = off;
+  L.W = L.U = L.Qn = L.P = L.Kn = L.gL = L.gE = off;
   if (!bwd) {
     L.W = off;       off = align_up(off + 2 * kBlk64x128 * blocks);
     L.U = off;       off = align_up(off + 2 * kBlk64x128 * blocks);
-    L.Qg = off;      off = align_up(off + 2 * kBlk64x128 * blocks);
+    L.Qn = off;      off = align_up(off + 2 * kBlk64x128 * kblocks);
     L.P = off;       off = align_up(off + 2 * kBlk64x64 * blocks);
-    L.Kb = off;      off = align_up(off + 2 * kBlk64x128 * blocks);
+    L.Kn = off;      off = align_up(off + 2 * kBlk64x128 * kblocks);
     L.gL = off;      off = align_up(off + sizeof(float) * blocks);
+    L.gE = off;      off = align_up(off + sizeof(float) * kGates * blocks);
   }
   L.T = L.dh = L.dD = L.dDT = off;
   if (bwd) {
@@ -94,36 +96,46 @@ Layout make_layout(const gdn_problem* p, int64_t NC, bool bwd) {
   return L;
 }
 
-PrepOut prep_views(char* ws, const Layout& L) {
+PrepOut prep_views(char* ws, const Layout& L, const gdn_problem* p) {
   PrepOut o;
   o.W = reinterpret_cast<uint16_t*>(ws + L.W);
   o.U = reinterpret_cast<uint16_t*>(ws + L.U);
-  o.Qg = reinterpret_cast<uint16_t*>(ws + L.Qg);
+  o.Qn = reinterpret_cast<uint16_t*>(ws + L.Qn);
   o.P = reinterpret_cast<uint16_t*>(ws + L.P);
-  o.Kb = reinterpret_cast<uint16_t*>(ws + L.Kb);
+  o.Kn = reinterpret_cast<uint16_t*>(ws + L.Kn);
   o.gL = reinterpret_cast<float*>(ws + L.gL);
+  o.gE = reinterpret_cast<float*>(ws + L.gE);
   o.T = nullptr;
+  o.G = p->HV / p->H;
   return o;
 }
 
 // `saved`: per (chunk, value head) the bf16 start state and D (kSavedBlock
-// elements each), then the backward's WY operands per (value head, chunk):
-// W^T, Q_g^T (64 x 128 each), P^T (64 x 64), K_bwd (64 x 128), T and T^T
-// (2 x 64 x 64), and e^gamma_L (fp32).
-constexpr size_t kSavedPrepElems = 3 * kBlk64x128 + 3 * kBlk64x64;
-size_t saved_bytes(size_t blocks) {
-  return blocks * ((size_t)kSavedBlock + kSavedPrepElems) * 2 + blocks * sizeof(float);
+// elements each); then the backward's WY operands: per (value head, chunk)
+// W^T (64 x 128) and P^T (64 x 64), per (key head, chunk) Q~^T and K^
+// (64 x 128 each), per (value head, chunk) T and T^T (2 x 64 x 64); then in
+// fp32 per (value head, chunk) e^gamma_L and the kGates gate factors.
+// the gate factors start 16-byte aligned after the e^gamma_L values
+size_t gates_offset(size_t blocks) { return (blocks + 3) / 4 * 4; }
+size_t saved_bytes(const gdn_problem* p, int64_t NC) {
+  const size_t blocks = (size_t)p->HV * (size_t)NC, kblocks = (size_t)p->H * (size_t)NC;
+  return (blocks * ((size_t)kSavedBlock + kBlk64x128 + 3 * kBlk64x64) +
+          kblocks * 2 * kBlk64x128) * 2 +
+         (gates_offset(blocks) + blocks * kGates) * sizeof(float);
 }
-PrepOut saved_bwd_views(uint16_t* saved, size_t blocks) {
+PrepOut saved_bwd_views(uint16_t* saved, const gdn_problem* p, int64_t NC) {
+  const size_t blocks = (size_t)p->HV * (size_t)NC, kblocks = (size_t)p->H * (size_t)NC;
   PrepOut o;
   uint16_t* b = saved + blocks * (size_t)kSavedBlock;
   o.W = b;                              b += blocks * kBlk64x128;
-  o.Qg = b;                             b += blocks * kBlk64x128;
   o.P = b;                              b += blocks * kBlk64x64;
-  o.Kb = b;                             b += blocks * kBlk64x128;
+  o.Qn = b;                             b += kblocks * kBlk64x128;
+  o.Kn = b;                             b += kblocks * kBlk64x128;
   o.T = b;                              b += blocks * 2 * kBlk64x64;
   o.gL = reinterpret_cast<float*>(b);
+  o.gE = o.gL + gates_offset(blocks);
   o.U = nullptr;
+  o.G = p->HV / p->H;
   return o;
 }
 
@@ -178,7 +190,7 @@ GDN_API int64_t gdn_num_chunks(const gdn_problem* p) {
 GDN_API size_t gdn_chunk_saved_size(const gdn_problem* p) {
   int64_t nc = 0;
   if (check_problem(p, &nc) != GDN_OK) return 0;
-  return saved_bytes((size_t)p->HV * (size_t)nc);
+  return saved_bytes(p, nc);
 }
 
 GDN_API size_t gdn_chunk_fwd_workspace_size(const gdn_problem* p) {
@@ -253,8 +265,8 @@ static int chunk_fwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_
   char* ws = static_cast<char*>(workspace);
   ChunkInfo* table = reinterpret_cast<ChunkInfo*>(ws + L.table);
   int32_t* seq_first = reinterpret_cast<int32_t*>(ws + L.seq_first);
-  const PrepOut prep = prep_views(ws, L);
-  const PrepOut bprep = saved ? saved_bwd_views(saved, (size_t)p->HV * NC) : PrepOut{};
+  const PrepOut prep = prep_views(ws, L, p);
+  const PrepOut bprep = saved ? saved_bwd_views(saved, p, NC) : PrepOut{};
   GDN_TRY(clk.run([&] {
     return launch_chunk_table(p->cu_seqlens, p->N, p->T, (int)NC, table, seq_first, s);
   }));
@@ -327,7 +339,7 @@ GDN_API int gdn_chunk_transition(const gdn_problem* p, const uint16_t* q, const 
   char* ws = static_cast<char*>(workspace);
   ChunkInfo* table = reinterpret_cast<ChunkInfo*>(ws + L.table);
   int32_t* seq_first = reinterpret_cast<int32_t*>(ws + L.seq_first);
-  const PrepOut prep = prep_views(ws, L);
+  const PrepOut prep = prep_views(ws, L, p);
   if (launch_chunk_table(p->cu_seqlens, p->N, p->T, (int)NC, table, seq_first, s) != hipSuccess)
     return GDN_ERR_HIP;
   if (NC > 0 && launch_chunk_prep(PrepMode::kForward, table, (int)NC, p->H, p->HV,
@@ -383,7 +395,6 @@ static int chunk_bwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_
   bufs.dD = reinterpret_cast<uint16_t*>(ws + L.dD);
   bufs.dDT = reinterpret_cast<uint16_t*>(ws + L.dDT);
   const float scale = effective_scale(p);
-  const size_t blocks = (size_t)p->HV * NC;
   GDN_TRY(clk.run([&] {
     return launch_chunk_table(p->cu_seqlens, p->N, p->T, (int)NC, table, seq_first, s);
   }));
@@ -393,10 +404,10 @@ static int chunk_bwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_
     // workspace's start until the scan has read them, then the backward's
     // scratch takes that place
     uint16_t* rebuilt = reinterpret_cast<uint16_t*>(ws + recompute_saved_offset(p, NC));
-    const PrepOut fprep = prep_views(ws, make_layout(p, NC, false));
+    const PrepOut fprep = prep_views(ws, make_layout(p, NC, false), p);
     GDN_TRY(clk.run([&] {
       return launch_chunk_prep(PrepMode::kBoth, table, (int)NC, p->H, p->HV, scale, q, k, v, g,
-                               beta, fprep, saved_bwd_views(rebuilt, blocks), s);
+                               beta, fprep, saved_bwd_views(rebuilt, p, NC), s);
     }));
     StateRef sr{};
     sr.h0 = recompute_h0;
@@ -407,7 +418,7 @@ static int chunk_bwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_
     saved = rebuilt;
   }
   // the backward's WY operands were written by the forward, behind the states
-  const PrepOut prep = saved_bwd_views(const_cast<uint16_t*>(saved), blocks);
+  const PrepOut prep = saved_bwd_views(const_cast<uint16_t*>(saved), p, NC);
   GDN_TRY(clk.run([&] {
     return launch_bwd_dh_scan(seq_first, p->N, p->HV, (int)NC, table, prep, dO, dhT, dh0, bufs, s);
   }));

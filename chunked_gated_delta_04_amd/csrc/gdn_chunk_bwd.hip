@@ -1,7 +1,8 @@
 // Backward of the chunked gated delta rule: reverse state-gradient scan and
-// the per-chunk gradient pass. Their per-chunk operands (W^T, Q_g^T, P^T,
-// K_bwd, T, T^T, e^gamma_L) are the ones the forward's WY pass wrote behind
-// the saved states (gdn_chunk_prep.hip), so no WY pass runs here.
+// the per-chunk gradient pass. Their per-chunk operands (W^T, P^T, T, T^T,
+// e^gamma_L and the per-token decays per value head; Q~^T and K^ per key head)
+// are the ones the forward's WY pass wrote behind the saved states
+// (gdn_chunk_prep.hip), so no WY pass runs here.
 //
 // Chunk form (see gdn_chunk_prep.hip): D = U - W h, O = Q_g h + P D,
 // h' = e^gamma_L h + K_bwd^T D, with U = T diag(beta) V,
@@ -51,6 +52,9 @@ __device__ __forceinline__ float sum16_lane0(float x) { return row_sum_first_lan
 // ---------------------------------------------------------------------------
 // Reverse scan: dh (K x VB slice) in registers, chunks in reverse order.
 // Writes per (chunk, value head): dh' as [k][v], dD as [tok][v] and [v][tok].
+// The decays of Q_g = diag(e^gamma) Q~ and K_bwd = diag(e^(gamma_L - gamma)) K^
+// are applied in fp32: to the dO rows for Q_g^T dO = Q~^T (diag(e^gamma) dO)
+// and to the rows of K^ dh' for K_bwd dh'.
 // As in the forward scan, two operand sets alternate and every chunk issues
 // the same loads and stores with no branch around them, so waiting for a set
 // never waits for a store; dO rows past the chunk's end come from a
@@ -70,7 +74,8 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
   const int b = blockIdx.x;
   const int xcd = b & 7, slot = b >> 3;
   const int vb = slot % NVB;
-  const int chain = (slot / NVB) * 8 + xcd;
+  const int m = slot / NVB, G = prep.G;  // a key head's value heads on one XCD
+  const int chain = ((m / G) * 8 + xcd) * G + m % G;
   if (chain >= N * HV) return;
   const int seq = chain / HV, hv = chain - seq * HV;
   const int v0 = vb * VB;
@@ -80,6 +85,7 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
   __shared__ __align__(16) uint16_t Hs[VB * SP];  // dh as [v][k]
   constexpr int OP = 40;  // LDS pitch of the dO rows (bf16)
   __shared__ __align__(16) uint16_t Ot[kChunk * OP];  // dO [tok][v - v0]
+  __shared__ __align__(16) uint16_t Og[kChunk * OP];  // diag(e^gamma) dO [tok][v - v0]
   __shared__ __align__(16) uint16_t Es[VB * DP];  // dD^T [v][tok]
 
   f32x4 dh[2][VT];
@@ -102,6 +108,8 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
     bf16x8 pa[2], ka[4], qa[2][2], wa[2][2];
     uint4 dO;
     float gl;
+    float eg;    // e^gamma of token ot (the dO row this thread stages)
+    float4 ebw;  // e^(gamma_L - gamma) of tokens 16 wave + 4 kq .. + 3 (dD rows)
   };
   const int ot = tid / SPT, osg = tid % SPT;  // dO segment of this thread (ot < 64 holds one)
   // chunk bounds from the sequence's bounds (consecutive 64-token chunks)
@@ -114,10 +122,11 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
   }
   auto load_ops = [&](int c, Ops& x) {
     const size_t blk = (size_t)hv * NC + c;
-    const uint16_t* PTb = prep.P + blk * 4096;   // P^T: row i holds P[j][i], j >= i
-    const uint16_t* Kbb = prep.Kb + blk * 8192;  // K_bwd [tok][k]
-    const uint16_t* QgT = prep.Qg + blk * 8192;  // Q_g^T [k][tok]
-    const uint16_t* WT = prep.W + blk * 8192;    // W^T [k][tok]
+    const size_t kblk = (size_t)(hv / prep.G) * NC + c;
+    const uint16_t* PTb = prep.P + blk * 4096;    // P^T: row i holds P[j][i], j >= i
+    const uint16_t* Kbb = prep.Kn + kblk * 8192;  // K^ [tok][k]
+    const uint16_t* QgT = prep.Qn + kblk * 8192;  // Q~^T [k][tok]
+    const uint16_t* WT = prep.W + blk * 8192;     // W^T [k][tok]
 #pragma unroll
     for (int s = 0; s < 2; ++s) x.pa[s] = ld8(PTb + kcm(16 * wave + li, 32 * s + 8 * kq, 64));
 #pragma unroll
@@ -132,6 +141,9 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
       }
     }
     x.gl = prep.gL[blk];
+    const float* ge = prep.gE + blk * kGates;
+    x.eg = ge[ot & (kChunk - 1)];
+    x.ebw = *reinterpret_cast<const float4*>(ge + kChunk + 16 * wave + 4 * kq);
     const int t0 = bos + (c - c_begin) * kChunk;
     const int len = min(kChunk, eos - t0);
     const __amdgpu_buffer_rsrc_t rng = __builtin_amdgcn_make_buffer_rsrc(
@@ -151,7 +163,16 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
         *reinterpret_cast<uint2*>(&Hs[(16 * vt + li) * SP + kk]) =
             pack4_bf16(dh[dt][vt][0], dh[dt][vt][1], dh[dt][vt][2], dh[dt][vt][3]);
       }
-    if (ot < kChunk) *reinterpret_cast<uint4*>(&Ot[ot * OP + 8 * osg]) = cur.dO;
+    if (ot < kChunk) {
+      *reinterpret_cast<uint4*>(&Ot[ot * OP + 8 * osg]) = cur.dO;
+      const uint32_t* xw = reinterpret_cast<const uint32_t*>(&cur.dO);
+      const float e = cur.eg;
+      *reinterpret_cast<uint4*>(&Og[ot * OP + 8 * osg]) =
+          make_uint4(pk2(e * bf2f(xw[0] & 0xffffu), e * bf2f(xw[0] >> 16)),
+                     pk2(e * bf2f(xw[1] & 0xffffu), e * bf2f(xw[1] >> 16)),
+                     pk2(e * bf2f(xw[2] & 0xffffu), e * bf2f(xw[2] >> 16)),
+                     pk2(e * bf2f(xw[3] & 0xffffu), e * bf2f(xw[3] >> 16)));
+    }
     __syncthreads();
     // dh' (gradient of this chunk's end state) as [v / 32][v % 32 / 8][k][v % 8],
     // read as columns of Hs with transposed reads (chunk e = 64 q + lane)
@@ -174,7 +195,8 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
       for (int s = 0; s < 2; ++s)
         ob[vt][s] = __builtin_bit_cast(bf16x8, lds_col8(Ot, OP, 32 * s + 8 * kq, 16 * vt, lane));
 
-    // 2. dD = P^T dO + K_bwd dh; wave w owns tokens 16 w .. 16 w + 15
+    // 2. dD = P^T dO + diag(e^(gamma_L - gamma)) K^ dh; wave w owns tokens
+    //    16 w .. 16 w + 15
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt) {
       bf16x8 hb4[4];
@@ -183,11 +205,13 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
       // two independent partial sums, so the MFMAs do not wait on each other
       f32x4 a0 = mfma(cur.ka[0], hb4[0], zero4());
       f32x4 a1 = mfma(cur.ka[1], hb4[1], zero4());
+      f32x4 ap = mfma(cur.pa[1], ob[vt][1], zero4());
       a0 = mfma(cur.ka[2], hb4[2], a0);
       a1 = mfma(cur.ka[3], hb4[3], a1);
-      a1 = mfma(cur.pa[1], ob[vt][1], a1);
-      if (wave < 2) a0 = mfma(cur.pa[0], ob[vt][0], a0);
-      const f32x4 acc = a0 + a1;
+      if (wave < 2) ap = mfma(cur.pa[0], ob[vt][0], ap);
+      const f32x4 ak = a0 + a1;
+      const f32x4 acc = f32x4{ak[0] * cur.ebw.x, ak[1] * cur.ebw.y, ak[2] * cur.ebw.z,
+                              ak[3] * cur.ebw.w} + ap;
       // acc[r] = dD[t = 16 w + 4 kq + r][v = 16 vt + li]
       *reinterpret_cast<uint2*>(&Es[(16 * vt + li) * DP + 16 * wave + 4 * kq]) =
           pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
@@ -207,7 +231,14 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
             lds_col8(Es, DP, 8 * wave, 16 * kq, lane);
     }
 
-    // 3. dh <- e^gamma_L dh + Q_g^T dO - W^T dD; wave w owns key rows 32 w .. 32 w + 31
+    // 3. dh <- e^gamma_L dh + Q~^T (diag(e^gamma) dO) - W^T dD; wave w owns key
+    //    rows 32 w .. 32 w + 31
+    bf16x8 og[VT][2];
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        og[vt][s] = __builtin_bit_cast(bf16x8, lds_col8(Og, OP, 32 * s + 8 * kq, 16 * vt, lane));
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -216,7 +247,7 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
         f32x4 acw = zero4();
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          acc = mfma(cur.qa[dt][s], ob[vt][s], acc);
+          acc = mfma(cur.qa[dt][s], og[vt][s], acc);
           acw = mfma(cur.wa[dt][s], ld8(&Es[(16 * vt + li) * DP + 32 * s + 8 * kq]), acw);
         }
         dh[dt][vt] = acc - acw;
@@ -1020,7 +1051,8 @@ hipError_t launch_bwd_dh_scan(const int32_t* seq_first, int N, int HV, int NC,
                               const float* dhT, float* dh0, const BwdBufs& bufs,
                               hipStream_t stream) {
   const long chains = (long)N * HV;
-  const long blocks = (chains + 7) / 8 * 8 * (kHead / kScanVB);
+  const long group = 8L * prep.G;
+  const long blocks = (chains + group - 1) / group * group * (kHead / kScanVB);
   hipLaunchKernelGGL(bwd_dh_scan_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, seq_first,
                      N, HV, NC, table, prep, dO, dhT, dh0, bufs);
   return hipGetLastError();

@@ -4,6 +4,9 @@
 //   D  = U - W h                     corrected values of the chunk
 //   O  = Q_g h + P D                 inter-chunk plus intra-chunk output
 //   h <- e^gamma_L h + K_bwd^T D     state at the next chunk's start
+// where Q_g = diag(e^gamma) Q~ and K_bwd = diag(e^(gamma_L - gamma)) K^: the
+// scan reads the key head's Q~ and K^ (shared by its value heads) and applies
+// the per-token decays in fp32, to the rows of Q~ h and to the rows of D.
 // (the chunk form of the recurrence; the scan and the output are the
 // forward stages named on the cake_gdn page, miles PR #3597, "What the
 // commits add"; the start state of every chunk is stored in bf16 for the
@@ -49,7 +52,10 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
   const int xcd = b & 7, slot = b >> 3;
   const int vb = slot % NVB;
   const bool mblk = kTrans && slot % NVBL < NVB;  // a block of M's columns
-  const int chain = (slot / NVBL) * 8 + xcd;
+  // the value heads of one key head (consecutive chains) share an XCD too,
+  // so the key head's Q~ and K^ tiles they all read come from one L2
+  const int m = slot / NVBL, G = prep.G;
+  const int chain = ((m / G) * 8 + xcd) * G + m % G;
   if (chain >= N * HV) return;
   const int seq = chain / HV, hv = chain - seq * HV;
   const int v0 = vb * VB;
@@ -58,6 +64,7 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
 
   __shared__ __align__(16) uint16_t Ss[VB * SP];  // S[v][k] of the chunk start (bf16)
   __shared__ __align__(16) uint16_t Ds[VB * DP];  // D^T[v][tok] (bf16)
+  __shared__ __align__(16) uint16_t Es[VB * DP];  // (diag(e^(gamma_L - gamma)) D)^T (bf16)
 
   // start and end state of this chain (the paged form reads and writes one
   // pool slot in place: each thread reads its own elements before the scan
@@ -104,14 +111,17 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     bf16x8 wa[4], qa[4], pa[2], ka[2][2];
     uint2 u[VT];
     float gl;
+    float eg;    // e^gamma of token 16 wave + li (output rows)
+    float4 ebw;  // e^(gamma_L - gamma) of tokens 16 wave + 4 kq .. + 3 (D rows)
   };
   auto load_ops = [&](int c, Ops& x) {
     const size_t blk = (size_t)hv * NC + c;
+    const size_t kblk = (size_t)(hv / prep.G) * NC + c;
     const uint16_t* Wb = prep.W + blk * 8192;
     const uint16_t* Ub = prep.U + blk * 8192;
-    const uint16_t* Qb = prep.Qg + blk * 8192;
+    const uint16_t* Qb = prep.Qn + kblk * 8192;  // Q~ [tok][k]
     const uint16_t* Pb = prep.P + blk * 4096;
-    const uint16_t* Kb = prep.Kb + blk * 8192;
+    const uint16_t* Kb = prep.Kn + kblk * 8192;  // K^T [k][tok]
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       x.wa[s] = ld8(Wb + kcm(16 * wave + li, 32 * s + 8 * kq, 64));
@@ -130,6 +140,9 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     for (int vt = 0; vt < VT; ++vt)
       x.u[vt] = *reinterpret_cast<const uint2*>(Ub + kcm(v0 + 16 * vt + li, 16 * wave + 4 * kq, 128));
     x.gl = prep.gL[blk];
+    const float* ge = prep.gE + blk * kGates;
+    if constexpr (kOut) x.eg = ge[16 * wave + li];
+    x.ebw = *reinterpret_cast<const float4*>(ge + kChunk + 16 * wave + 4 * kq);
   };
 
   // The chunks of one sequence are consecutive 64-token pieces, so a chunk's
@@ -184,9 +197,12 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
       const f32x4 acc = a0 + a1;
       // acc[r] = (W h)[t = 16 w + 4 kq + r][v = 16 vt + li]
       const uint2 u = mblk ? make_uint2(0u, 0u) : cur.u[vt];
-      *reinterpret_cast<uint2*>(&Ds[(16 * vt + li) * DP + 16 * wave + 4 * kq]) =
-          pack4_bf16(bf2f(u.x & 0xffffu) - acc[0], bf2f(u.x >> 16) - acc[1],
-                     bf2f(u.y & 0xffffu) - acc[2], bf2f(u.y >> 16) - acc[3]);
+      const float d0 = bf2f(u.x & 0xffffu) - acc[0], d1 = bf2f(u.x >> 16) - acc[1];
+      const float d2 = bf2f(u.y & 0xffffu) - acc[2], d3 = bf2f(u.y >> 16) - acc[3];
+      const int ds = (16 * vt + li) * DP + 16 * wave + 4 * kq;
+      *reinterpret_cast<uint2*>(&Ds[ds]) = pack4_bf16(d0, d1, d2, d3);
+      *reinterpret_cast<uint2*>(&Es[ds]) = pack4_bf16(cur.ebw.x * d0, cur.ebw.y * d1,
+                                                      cur.ebw.z * d2, cur.ebw.w * d3);
     }
     __syncthreads();
     if constexpr (kSave) {
@@ -197,7 +213,8 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
             lds_col8(Ds, DP, 8 * wave, 16 * kq, lane);
     }
 
-    // 3. O^T = S Q_g^T + D^T P^T; wave w owns tokens 16 w .. 16 w + 15. Rows at
+    // 3. O^T = (S Q~^T) diag(e^gamma) + D^T P^T; wave w owns tokens 16 w ..
+    //    16 w + 15 (lane li: token 16 w + li, so e^gamma is one factor). Rows at
     //    or past the chunk length fall outside the store's buffer range, which
     //    drops them.
     if constexpr (kOut) {
@@ -214,19 +231,20 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
         for (int s = 0; s < 2; ++s) db[s] = ld8(&Ds[(16 * vt + li) * DP + 32 * s + 8 * kq]);
         f32x4 a0 = mfma(sb[0], cur.qa[0], zero4());
         f32x4 a1 = mfma(sb[1], cur.qa[1], zero4());
+        // P is lower triangular: tokens j > 16 w + 15 contribute nothing
+        f32x4 ap = mfma(db[0], cur.pa[0], zero4());
         a0 = mfma(sb[2], cur.qa[2], a0);
         a1 = mfma(sb[3], cur.qa[3], a1);
-        // P is lower triangular: tokens j > 16 w + 15 contribute nothing
-        a0 = mfma(db[0], cur.pa[0], a0);
-        if (wave >= 2) a1 = mfma(db[1], cur.pa[1], a1);
-        const f32x4 acc = a0 + a1;
+        if (wave >= 2) ap = mfma(db[1], cur.pa[1], ap);
+        const f32x4 acc = (a0 + a1) * cur.eg + ap;
         // acc[r] = O[t = t0 + 16 w + li][v = v0 + 16 vt + 4 kq + r]
         store_b64(pack4_bf16(acc[0], acc[1], acc[2], acc[3]), orng,
                   (tl * HV * kHead + v0 + 16 * vt + 4 * kq) * 2);
       }
     }
 
-    // 4. h <- e^gamma_L h + K_bwd^T D; wave w owns key rows 32 w .. 32 w + 31
+    // 4. h <- e^gamma_L h + K^T (diag(e^(gamma_L - gamma)) D); wave w owns key
+    //    rows 32 w .. 32 w + 31
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -234,7 +252,7 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
         f32x4 acc = h[dt][vt] * cur.gl;
 #pragma unroll
         for (int s = 0; s < 2; ++s)
-          acc = mfma(cur.ka[dt][s], ld8(&Ds[(16 * vt + li) * DP + 32 * s + 8 * kq]), acc);
+          acc = mfma(cur.ka[dt][s], ld8(&Es[(16 * vt + li) * DP + 32 * s + 8 * kq]), acc);
         h[dt][vt] = acc;
       }
     __syncthreads();
@@ -281,7 +299,8 @@ hipError_t launch_fwd_scan(ScanMode mode, const int32_t* seq_first, int N, int H
                            uint16_t* o, uint16_t* saved, hipStream_t stream) {
   const long chains = (long)N * HV;
   const long per_chain = (kHead / kScanVB) * (mode == ScanMode::kTransition ? 2 : 1);
-  const dim3 grid((unsigned)((chains + 7) / 8 * 8 * per_chain));
+  const long group = 8L * prep.G;  // chains per XCD round: whole key heads on each XCD
+  const dim3 grid((unsigned)((chains + group - 1) / group * group * per_chain));
   switch (mode) {
     case ScanMode::kOut:
       hipLaunchKernelGGL((fwd_scan_kernel<false, true, false>), grid, dim3(256), 0, stream,

@@ -22,16 +22,22 @@
 // head of the key head gets its gates, A, T and the products above. Only
 // e^x of x <= 0 (i >= j) is formed, so strong decays underflow to 0.
 //
-// Outputs per (value head, chunk) block, bf16 unless noted, in the layouts
-// the scans read with one 16-byte load per MFMA operand (a forward that saves
-// for a backward writes both sets in one pass):
+// Outputs, bf16 unless noted, in the layouts the scans read with one 16-byte
+// load per MFMA operand (a forward that saves for a backward writes both sets
+// in one pass). Per (value head, chunk) block:
 //            forward scan                    dh scan and gradient pass
 //   W        [64 tok][128 k]                 W^T   [128 k][64 tok]
 //   U        U^T [128 v][64 tok]             (not written)
-//   Q_g      [64 tok][128 k]                 Q_g^T [128 k][64 tok]
 //   P        [64 i][64 j]                    P^T   [64 j][64 i]
-//   K_bwd    K_bwd^T [128 k][64 tok]         K_bwd [64 tok][128 k]
+//   T        (not written)                   T [i][j] and T^T [j][i]
 //   gL       e^gamma_L (fp32)                same
+//   gE       e^gamma and e^(gamma_L - gamma) per token (fp32), same
+// and per (key head, chunk) block, shared by the key head's value heads:
+//   Q~       [64 tok][128 k]                 Q~^T  [128 k][64 tok]
+//   K^       K^T [128 k][64 tok]             K^    [64 tok][128 k]
+// The scans apply the per-token decays that turn Q~ into Q_g and K^ into
+// K_bwd in fp32: Q_g h = diag(e^gamma) (Q~ h) and K_bwd^T D = K^T (diag(e^(gamma_L
+// - gamma)) D), and likewise in the backward.
 #include "gdn_common.h"
 #include "gdn_internal.h"
 
@@ -140,7 +146,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
   __shared__ __align__(16) float Ts[64 * FP];      // A (strictly lower), inverted in place into T
   __shared__ __align__(16) uint16_t Vs[64 * KP];   // v rows of the value head (bf16)
   // gates of the value head; gam is the cumulative log-decay in base 2
-  __shared__ __align__(16) float gam[64], bet[64], eg[64], ebw[64], fw[64];
+  __shared__ __align__(16) float gam[64], bet[64], fw[64];
   __shared__ float Xs[3 * 256];  // solve scratch
   __shared__ __align__(16) uint16_t Xp[4][16 * XPP];  // per-wave 16 x 16 transpose tile
 
@@ -191,6 +197,37 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
   }
   __syncthreads();
 
+  // ---- Q~ and K^ of the key head (and their transposes for the backward).
+  //      The transposed pieces (column chunks of 8 tokens) come from the row
+  //      tiles with transposing LDS reads: a wave covers one token group tg
+  //      and 64 consecutive features.
+  {
+    const int wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 15, kq = lane >> 4;
+    const size_t kblk = (size_t)h * NC + c;
+    auto rows_out = [&](const uint16_t* src, uint16_t* dst) {
+      for (int e = tid; e < 64 * 16; e += 256) {
+        const int sg = e >> 6, t = e & 63;
+        *reinterpret_cast<uint4*>(dst + kcm(t, sg * 8, 64)) =
+            *reinterpret_cast<const uint4*>(&src[t * KP + sg * 8]);
+      }
+    };
+    auto cols_out = [&](const uint16_t* src, uint16_t* dst) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e0 = 256 * i + 64 * wave;  // wave-uniform
+        const int tg = e0 >> 7, d0 = (e0 & 127) + 16 * kq;
+        *reinterpret_cast<uint4*>(dst + kcm(d0 + li, 8 * tg, 128)) = lds_col8(src, KP, 8 * tg, d0, lane);
+      }
+    };
+    rows_out(Qs, fo.Qn + kblk * 8192);   // Q~ [tok][k]
+    cols_out(Ks, fo.Kn + kblk * 8192);   // K^T [k][tok]
+    if (kB) {
+      rows_out(Ks, bo.Kn + kblk * 8192);  // K^ [tok][k]
+      cols_out(Qs, bo.Qn + kblk * 8192);  // Q~^T [k][tok]
+    }
+  }
+
   const int G = HV / H;
   for (int jg = 0; jg < G; ++jg) {
     // Re-derive the thread coordinates from an opaque copy each iteration, so
@@ -228,9 +265,14 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
       gam[lane] = g2;
       bet[lane] = bv;
       const float e = exp2_fast(g2);
-      eg[lane] = e;
       fw[lane] = bv * e;
-      ebw[lane] = lane < L ? exp2_fast(gl2 - g2) : 0.f;
+      const float bw = lane < L ? exp2_fast(gl2 - g2) : 0.f;
+      fo.gE[blk * kGates + lane] = e;
+      fo.gE[blk * kGates + kChunk + lane] = bw;
+      if (kB) {
+        bo.gE[blk * kGates + lane] = e;
+        bo.gE[blk * kGates + kChunk + lane] = bw;
+      }
       if (lane == 0) {
         fo.gL[blk] = exp2_fast(gl2);
         if (kB) bo.gL[blk] = exp2_fast(gl2);
@@ -296,47 +338,6 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     // ---- 4. T = (I + A)^-1 in place
     invert_unit_lower_64(Ts, Xs, tid);
 
-    // ---- 5. Q_g and K_bwd to global. The transposed pieces (column chunks
-    //      of 8 tokens) come from the row tiles with transposing LDS reads:
-    //      a wave covers one token group tg and 64 consecutive features.
-    {
-      auto rows_out = [&](const uint16_t* src, const float* f, uint16_t* dst) {
-        for (int e = tid; e < 64 * 16; e += 256) {
-          const int sg = e >> 6, t = e & 63;
-          const uint4 x = *reinterpret_cast<const uint4*>(&src[t * KP + sg * 8]);
-          const uint32_t* xw = reinterpret_cast<const uint32_t*>(&x);
-          const float ft = f[t];
-          uint4 o4;
-          uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) ow[u] = pk2(ft * bf2f(xw[u] & 0xffffu), ft * bf2f(xw[u] >> 16));
-          *reinterpret_cast<uint4*>(dst + kcm(t, sg * 8, 64)) = o4;
-        }
-      };
-      auto cols_out = [&](const uint16_t* src, const float* f, uint16_t* dst) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e0 = 256 * i + 64 * wave;           // wave-uniform
-          const int tg = e0 >> 7, d0 = (e0 & 127) + 16 * kq;
-          const uint4 x = lds_col8(src, KP, 8 * tg, d0, lane);
-          const uint32_t* xw = reinterpret_cast<const uint32_t*>(&x);
-          const float4 fa = *reinterpret_cast<const float4*>(&f[8 * tg]);
-          const float4 fb = *reinterpret_cast<const float4*>(&f[8 * tg + 4]);
-          const uint4 o4 = make_uint4(pk2(fa.x * bf2f(xw[0] & 0xffffu), fa.y * bf2f(xw[0] >> 16)),
-                                      pk2(fa.z * bf2f(xw[1] & 0xffffu), fa.w * bf2f(xw[1] >> 16)),
-                                      pk2(fb.x * bf2f(xw[2] & 0xffffu), fb.y * bf2f(xw[2] >> 16)),
-                                      pk2(fb.z * bf2f(xw[3] & 0xffffu), fb.w * bf2f(xw[3] >> 16)));
-          *reinterpret_cast<uint4*>(dst + kcm(d0 + li, 8 * tg, 128)) = o4;
-        }
-      };
-      rows_out(Qs, eg, fo.Qg + blk * 8192);   // Q_g [tok][k]
-      cols_out(Ks, ebw, fo.Kb + blk * 8192);  // K_bwd^T [k][tok]
-      if (kB) {  // K_bwd [tok][k], Q_g^T [k][tok]
-        rows_out(Ks, ebw, bo.Kb + blk * 8192);
-        cols_out(Qs, eg, bo.Qg + blk * 8192);
-      }
-    }
-
     // T and T^T in bf16 for the backward's gradient pass: chunk (kc, r) of each
     // holds row r, columns 8 kc .. 8 kc + 7
     if (kB) {
@@ -359,7 +360,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
       }
     }
 
-    // ---- 6. W = (T diag(beta e^gamma)) K^: the factor scales T's columns as
+    // ---- 5. W = (T diag(beta e^gamma)) K^: the factor scales T's columns as
     //      T becomes an MFMA operand, K^ is read by columns from its row tile.
     //      32 tiles of 16 x 16 over 4 waves, contraction over the chunk; a
     //      tile also goes to the backward's W^T through the LDS transpose tile.
@@ -383,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     }
 
     {
-      // ---- 7. U = (T diag(beta)) V, written as U^T [v][tok]
+      // ---- 6. U = (T diag(beta)) V, written as U^T [v][tok]
       uint16_t* Ub = fo.U + blk * 8192;
             for (int tt = wave; tt < 32; tt += 4) {
         // C = T' V: C[4kq+r][li] = U[t = 16 tb + 4kq + r][v = 16 vb + li] -> U^T[v][t..t+3]

@@ -21,6 +21,7 @@ constexpr int kHead = 128;   // K = V
 constexpr int kChunk = 64;   // tokens per chunk
 constexpr float kNormEps = 1e-6f;
 constexpr int kScanVB = 32;  // value columns per workgroup of the state scans
+constexpr int kGates = 2 * kChunk;  // per-token gate factors of a block: e^gamma, e^(gamma_L - gamma)
 
 // Tile layout of every intermediate matrix that a kernel reads as MFMA
 // operands from global memory: an R x C tile (C the contraction axis) is

@@ -8,17 +8,22 @@
 
 namespace gdn {
 
-// Per (value head, chunk) blocks written by the WY pass; block index
-// blk = hv * NC + c, so the chunks of one chain are contiguous. Every tile is
-// stored in the chunk-major layout of kcm() with its contraction axis chunked.
+// Blocks written by the WY pass. Value-head blocks: blk = hv * NC + c, so the
+// chunks of one chain are contiguous. Key-head blocks (the normalised q and k,
+// which do not depend on the gates and so serve every value head of their key
+// head): kblk = (hv / G) * NC + c. Every tile is stored in the chunk-major
+// layout of kcm() with its contraction axis chunked.
 struct PrepOut {
-  uint16_t* W;   // forward: W [tok][k]; backward: W^T [k][tok]
-  uint16_t* U;   // forward only: U^T [v][tok]
-  uint16_t* Qg;  // forward: Q_g [tok][k]; backward: Q_g^T [k][tok]
-  uint16_t* P;   // forward: P [i][j]; backward: P^T [j][i]
-  uint16_t* Kb;  // forward: K_bwd^T [k][tok]; backward: K_bwd [tok][k]
-  float* gL;     // e^gamma_L, 1 per block
-  uint16_t* T;   // backward only: T [i][j] then T^T [j][i], 2 x 64 x 64 per block
+  uint16_t* W;   // value head; forward: W [tok][k]; backward: W^T [k][tok]
+  uint16_t* U;   // value head; forward only: U^T [v][tok]
+  uint16_t* Qn;  // key head; forward: Q~ [tok][k]; backward: Q~^T [k][tok]
+  uint16_t* P;   // value head; forward: P [i][j]; backward: P^T [j][i]
+  uint16_t* Kn;  // key head; forward: K^T [k][tok]; backward: K^ [tok][k]
+  float* gL;     // value head: e^gamma_L, 1 per block
+  float* gE;     // value head: e^gamma (64), then e^(gamma_L - gamma) (64, zero past
+                 // the chunk's end), 128 per block
+  uint16_t* T;   // value head, backward only: T [i][j] then T^T [j][i], 2 x 64 x 64
+  int G;         // value heads per key head
 };
 
 // Backward scratch per (value head, chunk) block, blk = hv * NC + c.
