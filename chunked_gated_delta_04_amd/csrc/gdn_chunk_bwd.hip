@@ -216,6 +216,25 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
       *reinterpret_cast<uint2*>(&Es[(16 * vt + li) * DP + 16 * wave + 4 * kq]) =
           pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
     }
+    // The part of step 3 that needs no dD, while the other waves finish theirs:
+    // dh <- e^gamma_L dh + Q~^T (diag(e^gamma) dO) (dh was copied to LDS above)
+    {
+      bf16x8 og[VT][2];
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          og[vt][s] = __builtin_bit_cast(bf16x8, lds_col8(Og, OP, 32 * s + 8 * kq, 16 * vt, lane));
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt) {
+          f32x4 acc = dh[dt][vt] * cur.gl;
+#pragma unroll
+          for (int s = 0; s < 2; ++s) acc = mfma(cur.qa[dt][s], og[vt][s], acc);
+          dh[dt][vt] = acc;
+        }
+    }
     __syncthreads();
     // dD to global as [v][tok] (row copy) and [tok][v] (column gather), both in
     // the chunk-major tile layout: one 16-byte store each per thread
@@ -231,28 +250,21 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
             lds_col8(Es, DP, 8 * wave, 16 * kq, lane);
     }
 
-    // 3. dh <- e^gamma_L dh + Q~^T (diag(e^gamma) dO) - W^T dD; wave w owns key
-    //    rows 32 w .. 32 w + 31
-    bf16x8 og[VT][2];
-#pragma unroll
-    for (int vt = 0; vt < VT; ++vt)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        og[vt][s] = __builtin_bit_cast(bf16x8, lds_col8(Og, OP, 32 * s + 8 * kq, 16 * vt, lane));
+    // 3. dh <- (e^gamma_L dh + Q~^T (diag(e^gamma) dO), from above) - W^T dD;
+    //    wave w owns key rows 32 w .. 32 w + 31
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int vt = 0; vt < VT; ++vt) {
-        f32x4 acc = dh[dt][vt] * cur.gl;
         f32x4 acw = zero4();
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          acc = mfma(cur.qa[dt][s], og[vt][s], acc);
+        for (int s = 0; s < 2; ++s)
           acw = mfma(cur.wa[dt][s], ld8(&Es[(16 * vt + li) * DP + 32 * s + 8 * kq]), acw);
-        }
-        dh[dt][vt] = acc - acw;
+        dh[dt][vt] = dh[dt][vt] - acw;
       }
-    __syncthreads();
+    // No barrier here: Hs, Ot and Og are last read before the barrier above,
+    // and Es is rewritten only after the next chunk's first barrier, which
+    // every wave reaches after its reads of it.
   };
 
   if (c_begin < c_end) {

@@ -183,7 +183,10 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
       }
     }
 
-    // 2. D = U - W h; wave w owns tokens 16 w .. 16 w + 15
+    // 2. D = U - W h; wave w owns tokens 16 w .. 16 w + 15. The state part of
+    //    the output, (S Q~^T) diag(e^gamma), needs no D: it is formed here from
+    //    the same S fragments, ahead of the barrier that D needs.
+    f32x4 oq[VT];
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt) {
       bf16x8 sb[4];
@@ -192,6 +195,13 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
       // two independent partial sums, so the MFMAs do not wait on each other
       f32x4 a0 = mfma(cur.wa[0], sb[0], zero4());
       f32x4 a1 = mfma(cur.wa[1], sb[1], zero4());
+      if constexpr (kOut) {
+        f32x4 q0 = mfma(sb[0], cur.qa[0], zero4());
+        f32x4 q1 = mfma(sb[1], cur.qa[1], zero4());
+        q0 = mfma(sb[2], cur.qa[2], q0);
+        q1 = mfma(sb[3], cur.qa[3], q1);
+        oq[vt] = (q0 + q1) * cur.eg;  // [v = 16 vt + 4 kq + r][t = 16 w + li]
+      }
       a0 = mfma(cur.wa[2], sb[2], a0);
       a1 = mfma(cur.wa[3], sb[3], a1);
       const f32x4 acc = a0 + a1;
@@ -213,8 +223,9 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
             lds_col8(Ds, DP, 8 * wave, 16 * kq, lane);
     }
 
-    // 3. O^T = (S Q~^T) diag(e^gamma) + D^T P^T; wave w owns tokens 16 w ..
-    //    16 w + 15 (lane li: token 16 w + li, so e^gamma is one factor). Rows at
+    // 3. O^T = (S Q~^T) diag(e^gamma) + D^T P^T, the first term from step 2;
+    //    wave w owns tokens 16 w .. 16 w + 15 (lane li: token 16 w + li, so
+    //    e^gamma is one factor). Rows at
     //    or past the chunk length fall outside the store's buffer range, which
     //    drops them.
     if constexpr (kOut) {
@@ -224,19 +235,12 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
                                             len * HV * kHead * 2, kBufferWord3);
 #pragma unroll
       for (int vt = 0; vt < VT; ++vt) {
-        bf16x8 sb[4], db[2];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) sb[s] = ld8(&Ss[(16 * vt + li) * SP + 32 * s + 8 * kq]);
+        bf16x8 db[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) db[s] = ld8(&Ds[(16 * vt + li) * DP + 32 * s + 8 * kq]);
-        f32x4 a0 = mfma(sb[0], cur.qa[0], zero4());
-        f32x4 a1 = mfma(sb[1], cur.qa[1], zero4());
         // P is lower triangular: tokens j > 16 w + 15 contribute nothing
-        f32x4 ap = mfma(db[0], cur.pa[0], zero4());
-        a0 = mfma(sb[2], cur.qa[2], a0);
-        a1 = mfma(sb[3], cur.qa[3], a1);
-        if (wave >= 2) ap = mfma(db[1], cur.pa[1], ap);
-        const f32x4 acc = (a0 + a1) * cur.eg + ap;
+        f32x4 acc = mfma(db[0], cur.pa[0], oq[vt]);
+        if (wave >= 2) acc = mfma(db[1], cur.pa[1], acc);
         // acc[r] = O[t = t0 + 16 w + li][v = v0 + 16 vt + 4 kq + r]
         store_b64(pack4_bf16(acc[0], acc[1], acc[2], acc[3]), orng,
                   (tl * HV * kHead + v0 + 16 * vt + 4 * kq) * 2);
@@ -255,6 +259,9 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
           acc = mfma(cur.ka[dt][s], ld8(&Es[(16 * vt + li) * DP + 32 * s + 8 * kq]), acc);
         h[dt][vt] = acc;
       }
+    // (Not needed for the LDS tiles - no wave reads Ss after the barrier
+    // above, and Ds, Es are rewritten only after the next chunk's first
+    // barrier - but keeping the waves in step is faster: measured.)
     __syncthreads();
   };
 
