@@ -881,7 +881,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     }
     lds_barrier();
 
-    // ---- Y1 = dT T^T (i > j), stored transposed
+    // ---- Y1 = dT T^T (i > j), stored transposed. Also the own rows of T^T
+    //      for dA, read here so that the barrier below orders them before M
+    //      overwrites the tile.
+    bf16x8 tta[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) tta[s] = ld8(&S.PmT[trow * BP + 32 * s + 8 * kq]);
     {
       bf16x8 ta[2];
 #pragma unroll
@@ -907,10 +912,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 
     // ---- dA = -T^T Y1 (i > j); M = dA o beta_i Gamma -> Pm, PmT; E = dA o A sums; dbeta of A
     {
-      bf16x8 tta[2];  // own rows of T^T, read before M overwrites them
-#pragma unroll
-      for (int s = 0; s < 2; ++s) tta[s] = ld8(&S.PmT[trow * BP + 32 * s + 8 * kq]);
-      lds_barrier();
       float re[4] = {0.f, 0.f, 0.f, 0.f}, rb[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
@@ -988,7 +989,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         adk[j] = acc;
       }
     }
-    lds_barrier();  // everything is rewritten by the next value head
+    // No barrier here: up to its first barrier the next value head writes
+    // only the gates (wave 0), which nothing after the barrier above reads;
+    // its later writes follow that first barrier, which every wave reaches
+    // after the reads above.
   }
 
   {
