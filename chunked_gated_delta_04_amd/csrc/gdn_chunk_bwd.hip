@@ -407,6 +407,20 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
                                        16, 0, 0);
     }
   };
+  // After the last value head is done with Gs: the chunk's raw q rows, then
+  // its raw k rows, into Gs ([64][128] each, unpadded) for the norm backward.
+  // Rows past the chunk's end copy its last row (read, never used).
+  auto copy_qk_rows = [&](int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e0 = 512 * i + 64 * wave;  // first 16-byte chunk of the copy (wave-uniform)
+      const int e = e0 + lane;
+      const int r = min((e & 1023) >> 4, L - 1);
+      const uint16_t* src = (e0 < 1024 ? q : k) + ((size_t)(t0 + r) * H + h) * kHead + 8 * (e & 15);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(Gs + 8 * e0),
+                                       16, 0, 0);
+    }
+  };
   {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
@@ -843,6 +857,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     *reinterpret_cast<uint4*>(&S.PmT[(tid & 63) * BP + (tid >> 6) * 8]) = tst1;
     // (after the stores above, which wait for their own requests only)
     if (jg + 1 < G) copy_states(hv + 1, wave, lane);
+    else copy_qk_rows(wave, lane);
     lds_barrier();
 
     // ---- dT = dD (beta V)^T + dW (beta e^gamma K^)^T, strictly lower
@@ -1001,7 +1016,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     if ((tid >> 6) == 0) dg_out(h * G + G - 1, tid & 63);
   }
 
-  // ---- L2-norm backward and scale: x^ . dx^ over all 128 columns (two halves)
+  // ---- L2-norm backward and scale: x^ . dx^ over all 128 columns (two halves).
+  //      The raw q, k rows come from Gs (copied during the last value head).
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
   {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int tw = wave & 3, kh = wave >> 2;
@@ -1016,9 +1034,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         const int kc = 16 * (4 * kh + j) + li;
         float qv = 0.f, kv = 0.f;
         if (t < L) {
-          const size_t off = ((size_t)(t0 + t) * H + h) * kHead + kc;
-          qv = bf2f(q[off]) * S.inv_q[t];
-          kv = bf2f(k[off]) * S.inv_k[t];
+          qv = bf2f(Gs[t * kHead + kc]) * S.inv_q[t];
+          kv = bf2f(Gs[kChunk * kHead + t * kHead + kc]) * S.inv_k[t];
         }
         qh[j][r] = qv;
         kh_[j][r] = kv;
