@@ -150,22 +150,50 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
   __shared__ float Xs[3 * 256];  // solve scratch
   __shared__ __align__(16) uint16_t Xp[4][16 * XPP];  // per-wave 16 x 16 transpose tile
 
+  // A value head's own inputs - its v rows (thread: row tid / 4, 32 columns)
+  // and gates (every wave requests them; wave 0 uses them) - through
+  // range-checked buffer loads: rows at or past the chunk's end read as zeros,
+  // and a zero range (live = false) moves no data. Requested one value head
+  // ahead, before the current head's stores: waiting for a load also waits
+  // for every store issued before it.
+  const int G = HV / H;
+  uint4 vx[4];
+  float gq, bq;
+  auto request = [&](int hv_, bool live) {
+    const int n = live ? L : 0;
+    const int vr0 = tid >> 2, vsg0 = (tid & 3) * 4, lane = tid & 63;
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(v) + ((size_t)t0 * HV + hv_) * kHead, 0, n * HV * kHead * 2, kBufferWord3);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vx[j] = load_b128(rv, (vr0 * HV * kHead + (vsg0 + j) * 8) * 2);
+    const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(g) + (size_t)t0 * HV + hv_, 0, n * HV * 4, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(beta) + (size_t)t0 * HV + hv_, 0, n * HV * 4, kBufferWord3);
+    gq = load_f32(rg, lane * HV * 4);
+    bq = load_f32(rb, lane * HV * 4);
+  };
+
   // ---- 1. load and L2-normalise q, k rows (thread: row tid/4, 32 columns);
-  //      one division per row, then products with the reciprocal
+  //      one division per row, then products with the reciprocal. The first
+  //      value head's requests follow the q, k rows, so the norms wait only
+  //      for those.
   {
     const int r = tid >> 2, sg0 = (tid & 3) * 4;
     uint4 kr[4], qr[4];
     float sk = 0.f, sq = 0.f;
+    const __amdgpu_buffer_rsrc_t krng = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(k) + ((size_t)t0 * H + h) * kHead, 0, L * H * kHead * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t qrng = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(q) + ((size_t)t0 * H + h) * kHead, 0, L * H * kHead * 2, kBufferWord3);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (r < L) {
-        const size_t off = ((size_t)(t0 + r) * H + h) * kHead + (sg0 + j) * 8;
-        kr[j] = *reinterpret_cast<const uint4*>(k + off);
-        qr[j] = *reinterpret_cast<const uint4*>(q + off);
-      } else {
-        kr[j] = make_uint4(0, 0, 0, 0);
-        qr[j] = make_uint4(0, 0, 0, 0);
-      }
+      kr[j] = load_b128(krng, (r * H * kHead + (sg0 + j) * 8) * 2);
+      qr[j] = load_b128(qrng, (r * H * kHead + (sg0 + j) * 8) * 2);
+    }
+    request(h * G, true);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
       const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[j]);
       const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qr[j]);
 #pragma unroll
@@ -197,38 +225,6 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
   }
   __syncthreads();
 
-  // ---- Q~ and K^ of the key head (and their transposes for the backward).
-  //      The transposed pieces (column chunks of 8 tokens) come from the row
-  //      tiles with transposing LDS reads: a wave covers one token group tg
-  //      and 64 consecutive features.
-  {
-    const int wave = tid >> 6, lane = tid & 63;
-    const int li = lane & 15, kq = lane >> 4;
-    const size_t kblk = (size_t)h * NC + c;
-    auto rows_out = [&](const uint16_t* src, uint16_t* dst) {
-      for (int e = tid; e < 64 * 16; e += 256) {
-        const int sg = e >> 6, t = e & 63;
-        *reinterpret_cast<uint4*>(dst + kcm(t, sg * 8, 64)) =
-            *reinterpret_cast<const uint4*>(&src[t * KP + sg * 8]);
-      }
-    };
-    auto cols_out = [&](const uint16_t* src, uint16_t* dst) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e0 = 256 * i + 64 * wave;  // wave-uniform
-        const int tg = e0 >> 7, d0 = (e0 & 127) + 16 * kq;
-        *reinterpret_cast<uint4*>(dst + kcm(d0 + li, 8 * tg, 128)) = lds_col8(src, KP, 8 * tg, d0, lane);
-      }
-    };
-    rows_out(Qs, fo.Qn + kblk * 8192);   // Q~ [tok][k]
-    cols_out(Ks, fo.Kn + kblk * 8192);   // K^T [k][tok]
-    if (kB) {
-      rows_out(Ks, bo.Kn + kblk * 8192);  // K^ [tok][k]
-      cols_out(Qs, bo.Qn + kblk * 8192);  // Q~^T [k][tok]
-    }
-  }
-
-  const int G = HV / H;
   for (int jg = 0; jg < G; ++jg) {
     // Re-derive the thread coordinates from an opaque copy each iteration, so
     // that the many LDS and global addresses built from them are formed where
@@ -241,24 +237,14 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     const size_t blk = (size_t)hv * NC + c;
 
     // ---- 2. gates: gamma = inclusive cumsum of g inside the chunk (kept in
-    //      base 2); the value rows go to LDS as they are. All rows through
-    //      range-checked buffer loads (rows at or past the chunk's end read as
-    //      zeros, no branch), the value rows requested before anything waits.
+    //      base 2); the value rows go to LDS as they are. This head's v rows
+    //      and gates were requested before; the next head's are requested now.
     const int vr0 = tid >> 2, vsg0 = (tid & 3) * 4;
-    uint4 vx[4];
-    {
-      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(v) + ((size_t)t0 * HV + hv) * kHead, 0, L * HV * kHead * 2, kBufferWord3);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vx[j] = load_b128(rv, (vr0 * HV * kHead + (vsg0 + j) * 8) * 2);
-    }
+    const uint4 vc0 = vx[0], vc1 = vx[1], vc2 = vx[2], vc3 = vx[3];
+    float gv = gq;
+    const float bv = bq;
+    request(min(hv + 1, h * G + G - 1), jg + 1 < G);
     if (wave == 0) {
-      const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<float*>(g) + (size_t)t0 * HV + hv, 0, L * HV * 4, kBufferWord3);
-      const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<float*>(beta) + (size_t)t0 * HV + hv, 0, L * HV * 4, kBufferWord3);
-      float gv = load_f32(rg, lane * HV * 4);
-      const float bv = load_f32(rb, lane * HV * 4);
       gv = wave_prefix_sum(gv, lane);
       const float g2 = gv * kLog2e;
       const float gl2 = lane_value(g2, L - 1);
@@ -278,8 +264,10 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
         if (kB) bo.gL[blk] = exp2_fast(gl2);
       }
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&Vs[vr0 * KP + (vsg0 + j) * 8]) = vx[j];
+    *reinterpret_cast<uint4*>(&Vs[vr0 * KP + (vsg0 + 0) * 8]) = vc0;
+    *reinterpret_cast<uint4*>(&Vs[vr0 * KP + (vsg0 + 1) * 8]) = vc1;
+    *reinterpret_cast<uint4*>(&Vs[vr0 * KP + (vsg0 + 2) * 8]) = vc2;
+    *reinterpret_cast<uint4*>(&Vs[vr0 * KP + (vsg0 + 3) * 8]) = vc3;
     __syncthreads();
 
     // ---- 3. A (fp32, LDS: 10 lower tiles, 6 zero upper tiles) and P (bf16,
@@ -401,6 +389,38 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
       }
     }
     __syncthreads();  // gates, A, T and V are rewritten for the next value head
+  }
+
+  // ---- Q~ and K^ of the key head (and their transposes for the backward),
+  //      after the value heads so that no load waits for these stores.
+  //      The transposed pieces (column chunks of 8 tokens) come from the row
+  //      tiles with transposing LDS reads: a wave covers one token group tg
+  //      and 64 consecutive features.
+  {
+    const int wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 15, kq = lane >> 4;
+    const size_t kblk = (size_t)h * NC + c;
+    auto rows_out = [&](const uint16_t* src, uint16_t* dst) {
+      for (int e = tid; e < 64 * 16; e += 256) {
+        const int sg = e >> 6, t = e & 63;
+        *reinterpret_cast<uint4*>(dst + kcm(t, sg * 8, 64)) =
+            *reinterpret_cast<const uint4*>(&src[t * KP + sg * 8]);
+      }
+    };
+    auto cols_out = [&](const uint16_t* src, uint16_t* dst) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e0 = 256 * i + 64 * wave;  // wave-uniform
+        const int tg = e0 >> 7, d0 = (e0 & 127) + 16 * kq;
+        *reinterpret_cast<uint4*>(dst + kcm(d0 + li, 8 * tg, 128)) = lds_col8(src, KP, 8 * tg, d0, lane);
+      }
+    };
+    rows_out(Qs, fo.Qn + kblk * 8192);   // Q~ [tok][k]
+    cols_out(Ks, fo.Kn + kblk * 8192);   // K^T [k][tok]
+    if (kB) {
+      rows_out(Ks, bo.Kn + kblk * 8192);  // K^ [tok][k]
+      cols_out(Qs, bo.Qn + kblk * 8192);  // Q~^T [k][tok]
+    }
   }
 }
 
