@@ -397,14 +397,14 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       const int e0 = 512 * i + 64 * wave;  // first 16-byte chunk of the copy
       __builtin_amdgcn_global_load_lds(hb_ + 8 * (e0 + lane),
                                        (__attribute__((address_space(3))) void*)(Hs + 8 * e0),
-                                       16, 0, 0);
+                                       16, 0, kNonTemporal);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e0 = 512 * i + 64 * wave;
       __builtin_amdgcn_global_load_lds(dhb_ + 8 * (e0 + lane),
                                        (__attribute__((address_space(3))) void*)(Gs + 8 * e0),
-                                       16, 0, 0);
+                                       16, 0, kNonTemporal);
     }
   };
   // After the last value head is done with Gs: the chunk's raw q rows, then
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       const int r = min((e & 1023) >> 4, L - 1);
       const uint16_t* src = (e0 < 1024 ? q : k) + ((size_t)(t0 + r) * H + h) * kHead + 8 * (e & 15);
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(Gs + 8 * e0),
-                                       16, 0, 0);
+                                       16, 0, kNonTemporal);
     }
   };
   {
@@ -713,7 +713,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     // are dead, so that passes 1a and 1b cover their wait
     bf16x8 ea[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) ea[s] = ld8(dDb + kcm(trow, 32 * s + 8 * kq, kChunk));
+    for (int s = 0; s < 4; ++s)
+      ea[s] = __builtin_bit_cast(bf16x8, ld16_nt(dDb + kcm(trow, 32 * s + 8 * kq, kChunk)));
     lds_barrier();
 
     // ---- key-column passes (columns 16 kt + li, kt = 4 kh .. 4 kh + 3), h from LDS:
@@ -781,14 +782,16 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     // LDS once Z and the P tiles are dead.
     bf16x8 da[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) da[s] = ld8(Db + kcm(trow, 32 * s + 8 * kq, kChunk));
+    for (int s = 0; s < 4; ++s)
+      da[s] = __builtin_bit_cast(bf16x8, ld16_nt(Db + kcm(trow, 32 * s + 8 * kq, kChunk)));
     // Two 16-byte pieces per thread of each (named, not an array, so that
     // they stay in registers)
     const int ve0 = tid, ve1 = tid + 512;
-    const uint4 vst0 = load_b128(rv, ((ve0 >> 4) * (int)rs + (ve0 & 15) * 8) * 2);
-    const uint4 vst1 = load_b128(rv, ((ve1 >> 4) * (int)rs + (ve1 & 15) * 8) * 2);
-    const uint4 tst0 = *reinterpret_cast<const uint4*>(Tg + 8 * tid);          // T
-    const uint4 tst1 = *reinterpret_cast<const uint4*>(Tg + 8 * (tid + 512));  // T^T
+    // (last reads of D, V, T and T^T in this kernel: non-temporal)
+    const uint4 vst0 = load_b128_nt(rv, ((ve0 >> 4) * (int)rs + (ve0 & 15) * 8) * 2);
+    const uint4 vst1 = load_b128_nt(rv, ((ve1 >> 4) * (int)rs + (ve1 & 15) * 8) * 2);
+    const uint4 tst0 = ld16_nt(Tg + 8 * tid);          // T
+    const uint4 tst1 = ld16_nt(Tg + 8 * (tid + 512));  // T^T
     {  // pass 2: x3 -> dW
 #pragma unroll
       for (int j = 0; j < 4; ++j) {

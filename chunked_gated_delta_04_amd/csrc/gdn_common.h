@@ -40,6 +40,9 @@ __device__ __host__ __forceinline__ int kcm(int r, int c, int R) {
 // the resource's record count is discarded by the hardware, which lets a
 // kernel mask the rows past a chunk's end without a branch.
 constexpr int kBufferWord3 = 0x00020000;
+// Cache policy of a load: non-temporal (streamed data read once, kept from
+// displacing reused lines in L2).
+constexpr int kNonTemporal = 2;
 
 __device__ __forceinline__ void store_b64(uint2 v, __amdgpu_buffer_rsrc_t r, int byte_off) {
   typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -62,6 +65,17 @@ __device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, int byte_off
 }
 __device__ __forceinline__ bf16x8 ld8_buf(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(bf16x8, load_b128(r, byte_off));
+}
+// The same, non-temporal (the last read of the data in the kernel).
+__device__ __forceinline__ uint4 load_b128_nt(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kNonTemporal);
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ uint4 ld16_nt(const uint16_t* p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(x[0], x[1], x[2], x[3]);
 }
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
