@@ -156,7 +156,7 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     eos = lastc.t0 + lastc.len;
   }
 
-  auto step = [&](int c, const Ops& cur) {
+  auto step = [&](int c, const Ops& cur, int cn, Ops& nxt) {
     const int t0 = bos + (c - c_begin) * kChunk;
     const int len = min(kChunk, eos - t0);
     // 1. chunk-start state -> LDS (bf16)
@@ -170,6 +170,9 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
             pack4_bf16(h[dt][vt][0], h[dt][vt][1], h[dt][vt][2], h[dt][vt][3]);
       }
     __syncthreads();
+    // the next set's requests, issued by all waves together right after the
+    // barrier (waves that issue them together share the lines they fetch)
+    load_ops(cn, nxt);
     uint16_t* sv = saved + blk_saved(c, hv, HV);
     if constexpr (kSave) {
       // h = S^T as [v / 32][v % 32 / 8][k][v % 8]: chunk e = 64 q + lane holds
@@ -259,10 +262,9 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
           acc = mfma(cur.ka[dt][s], ld8(&Es[(16 * vt + li) * DP + 32 * s + 8 * kq]), acc);
         h[dt][vt] = acc;
       }
-    // (Not needed for the LDS tiles - no wave reads Ss after the barrier
-    // above, and Ds, Es are rewritten only after the next chunk's first
-    // barrier - but keeping the waves in step is faster: measured.)
-    __syncthreads();
+    // No barrier here: no wave reads Ss after the barrier above, and Ds, Es
+    // are rewritten only after the next chunk's first barrier, which every
+    // wave reaches after its reads of them.
   };
 
   if (c_begin < c_end) {
@@ -272,11 +274,9 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     Ops A, B;
     load_ops(c_begin, A);
     for (int c = c_begin;; c += 2) {
-      load_ops(min(c + 1, last), B);
-      step(c, A);
+      step(c, A, min(c + 1, last), B);
       if (c + 1 > last) break;
-      load_ops(min(c + 2, last), A);
-      step(c + 1, B);
+      step(c + 1, B, min(c + 2, last), A);
       if (c + 2 > last) break;
     }
   }
