@@ -61,6 +61,20 @@ def test_forward_matches_oracle_small_varlen(h0):
     assert_bar("hT", f64(hT), hT_ref)
 
 
+@pytest.mark.parametrize("H,HV,lens", [(1, 1, [200]), (2, 2, [70, 1]), (3, 9, [130, 64]),
+                                        (1, 4, [65, 128, 3])])
+def test_forward_matches_oracle_for_head_groups(H, HV, lens):
+    """One to four value heads per key head, including chain counts that leave
+    part of the last XCD round of the scan grid empty: the value heads of a key
+    head share its normalised q, k tiles, and each applies its own decays."""
+    _say(f"fwd head groups H={H} HV={HV} lens={lens}")
+    inp = small_inputs(lens=lens, H=H, HV=HV, seed=13)
+    o, hT, _ = run_fwd(inp)
+    o_ref, hT_ref = oracle_forward(inp)
+    assert_bar("o", f64(o), o_ref)
+    assert_bar("hT", f64(hT), hT_ref)
+
+
 def test_forward_matches_oracle_single_head_workload():
     _say("fwd 1x256 h1")
     inp = synth.workload_inputs("fwd_1x256_h1")
@@ -211,6 +225,9 @@ def test_backward_matches_oracle_for_other_head_groups(H, HV):
     inp = small_inputs(lens=lens, H=H, HV=HV, seed=11, with_do=True)
     dhT = 0.1 * torch.randn(len(lens), HV, 128, 128, generator=torch.Generator().manual_seed(5))
     o, hT, grads = run_fwd_bwd(inp, dhT=dhT)
+    o_ref, hT_ref = oracle_forward(inp)
+    assert_bar("o", f64(o), o_ref)
+    assert_bar("hT", f64(hT), hT_ref)
     ref = oracle_backward(inp, dhT=dhT)
     _check_grads(grads, ref, f"H{H}HV{HV}")
 

@@ -51,6 +51,17 @@ def test_transition_matches_the_oracle_small_varlen():
     assert torch.equal(M[5], eye) and torch.equal(s[5], torch.zeros_like(s[5]))
 
 
+def test_transition_matches_the_oracle_three_value_heads_per_key_head():
+    """Three value heads per key head: the scan grid's last XCD round is only
+    partly filled, and M's and s's columns run as separate blocks."""
+    _say("transition H=3 HV=9")
+    inp = synth.chunk_inputs([130, 64, 1], 3, 9, seed=87, h0_std=None)
+    M, s = run_transition(inp)
+    M_ref, s_ref = oracle_transition(inp)
+    assert_bar("M", f64(M), M_ref)
+    assert_bar("s", f64(s), s_ref)
+
+
 def test_transition_end_state_is_the_forward_from_zero_bitwise():
     inp = synth.chunk_inputs(SMALL_LENS, 2, 4, seed=82, h0_std=None)
     _, s = run_transition(inp)
