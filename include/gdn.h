@@ -127,11 +127,13 @@ size_t gdn_chunk_bwd_recompute_workspace_size(const gdn_problem* p);
  *             nearest-even bf16) and then the chunk's 64 x V corrected
  *             values D = U - W h in bf16 (rows past the chunk's end are
  *             zero); after all those blocks come the chunk quantities the
- *             backward contracts with (W, Q_g, P, K_bwd, T in bf16 and
- *             e^gamma_L in fp32, per value head and chunk), written by the
- *             same WY pass that feeds the forward scan so that the backward
- *             does not form them again. All in tile orders internal to this
- *             library: only gdn_chunk_bwd of the same build reads them.
+ *             backward contracts with (W, P, T in bf16 per value head and
+ *             chunk; the normalised q and k in bf16 per key head and chunk;
+ *             e^gamma_L and the per-token decays e^gamma, e^(gamma_L - gamma)
+ *             in fp32 per value head and chunk), written by the same WY pass
+ *             that feeds the forward scan so that the backward does not form
+ *             them again. All in tile orders internal to this library: only
+ *             gdn_chunk_bwd of the same build reads them.
  * A sequence of length 0 gets hT = h0 (or 0). T = 0 is valid: nothing is
  * read from the token tensors and hT = h0 (or 0).
  * Errors: GDN_ERR_NULL (p, or q, k, v, g, beta, o, cu_seqlens when T > 0),
