@@ -306,7 +306,7 @@ hipError_t launch_fwd_scan(ScanMode mode, const int32_t* seq_first, int N, int H
                            uint16_t* o, uint16_t* saved, hipStream_t stream) {
   const long chains = (long)N * HV;
   const long per_chain = (kHead / kScanVB) * (mode == ScanMode::kTransition ? 2 : 1);
-  const long group = 8L * prep.G;  // chains per XCD round: whole key heads on each XCD
+  const long group = 8L * prep.G;  // chains per cycle over the XCDs (whole key heads)
   const dim3 grid((unsigned)((chains + group - 1) / group * group * per_chain));
   switch (mode) {
     case ScanMode::kOut:

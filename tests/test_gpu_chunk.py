@@ -65,7 +65,7 @@ def test_forward_matches_oracle_small_varlen(h0):
                                         (1, 4, [65, 128, 3])])
 def test_forward_matches_oracle_for_head_groups(H, HV, lens):
     """One to four value heads per key head, including chain counts that leave
-    part of the last XCD round of the scan grid empty: the value heads of a key
+    part of the scan grid's last cycle over the XCDs empty: the value heads of a key
     head share its normalised q, k tiles, and each applies its own decays."""
     _say(f"fwd head groups H={H} HV={HV} lens={lens}")
     inp = small_inputs(lens=lens, H=H, HV=HV, seed=13)

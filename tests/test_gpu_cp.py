@@ -52,7 +52,7 @@ def test_transition_matches_the_oracle_small_varlen():
 
 
 def test_transition_matches_the_oracle_three_value_heads_per_key_head():
-    """Three value heads per key head: the scan grid's last XCD round is only
+    """Three value heads per key head: the scan grid's last cycle over the XCDs is only
     partly filled, and M's and s's columns run as separate blocks."""
     _say("transition H=3 HV=9")
     inp = synth.chunk_inputs([130, 64, 1], 3, 9, seed=87, h0_std=None)
