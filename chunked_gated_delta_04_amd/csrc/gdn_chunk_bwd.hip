@@ -485,26 +485,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
   }
   lds_barrier();  // (not __syncthreads: that would wait for the state copies)
 
-  // ---- Q~ K^T of the key head, the same for all its value heads, kept in
-  //      registers: qk[q2][r] = (Q~ K^T)[i][j] with i = 16 tw + 4 kq + r,
-  //      j = 16 (kh + 2 q2) + li (tiles with j's block <= i's)
-  f32x4 qk[2];
-  {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int tw = wave & 3, kh = wave >> 2, li = lane & 15, kq = lane >> 4;
-#pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) {
-      const int jb = kh + 2 * q2;
-      qk[q2] = zero4();
-      if (jb <= tw) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          qk[q2] = mfma(ld8(&S.Qs[(16 * tw + li) * KP + 32 * s + 8 * kq]),
-                        ld8(&S.Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), qk[q2]);
-      }
-    }
-  }
-
   // Gate gradients of value head hv_ (wave 0): fixed-order sums of the partial
   // slots, then dg = reverse cumsum of dgamma inside the chunk. Run by wave 0
   // at the top of the next value head (or after the last one): the slots and
@@ -646,16 +626,22 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         const int j = 16 * jb + li;
         float pv[4] = {0.f, 0.f, 0.f, 0.f};
         if (jb <= tw) {
-          f32x4 dp = zero4();
+          // dP tile and the Q~ K^T tile at the same place (formed here, per
+          // value head, rather than kept in registers across them)
+          f32x4 dp = zero4(), qk = zero4();
 #pragma unroll
-          for (int s = 0; s < 4; ++s) dp = mfma(oa[s], dfr[q2][s], dp);
+          for (int s = 0; s < 4; ++s) {
+            dp = mfma(oa[s], dfr[q2][s], dp);
+            qk = mfma(ld8(&S.Qs[trow * KP + 32 * s + 8 * kq]),
+                      ld8(&S.Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), qk);
+          }
           float colp = 0.f;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 16 * tw + 4 * kq + r;
             if (i >= j) {
               const float dpm = dp[r] * exp2_fast(S.gam[i] - S.gam[j]);
-              const float f = dpm * qk[q2][r];
+              const float f = dpm * qk[r];
               pv[r] = dpm;
               rowp[r] += f;
               colp += f;
@@ -784,12 +770,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       da[s] = __builtin_bit_cast(bf16x8, ld16_nt(Db + kcm(trow, 32 * s + 8 * kq, kChunk)));
-    // Two 16-byte pieces per thread of each (named, not an array, so that
-    // they stay in registers)
-    const int ve0 = tid, ve1 = tid + 512;
-    // (last reads of D, V, T and T^T in this kernel: non-temporal)
-    const uint4 vst0 = load_b128_nt(rv, ((ve0 >> 4) * (int)rs + (ve0 & 15) * 8) * 2);
-    const uint4 vst1 = load_b128_nt(rv, ((ve1 >> 4) * (int)rs + (ve1 & 15) * 8) * 2);
+    // (last reads of D, T and T^T in this kernel: non-temporal)
     const uint4 tst0 = ld16_nt(Tg + 8 * tid);          // T
     const uint4 tst1 = ld16_nt(Tg + 8 * (tid + 512));  // T^T
     {  // pass 2: x3 -> dW
@@ -853,8 +834,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       if (lane == 0) S.gl_part[wave] = glp;
     }
     lds_barrier();  // every wave is done with Z, the P tiles, Hs and Gs, and dW is whole
-    *reinterpret_cast<uint4*>(&S.rz.V[(ve0 >> 4) * KP + (ve0 & 15) * 8]) = vst0;
-    *reinterpret_cast<uint4*>(&S.rz.V[(ve1 >> 4) * KP + (ve1 & 15) * 8]) = vst1;
+    // V rows from the pieces the waves read for dbeta (together the whole tile)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<uint2*>(&S.rz.V[trow * KP + 16 * (4 * kh + j) + 4 * kq]) = vr[j];
     // T rows into Pm, T^T rows into PmT (chunk e = tid: row tid % 64, columns 8 (tid / 64) ..)
     *reinterpret_cast<uint4*>(&S.Pm[(tid & 63) * BP + (tid >> 6) * 8]) = tst0;
     *reinterpret_cast<uint4*>(&S.PmT[(tid & 63) * BP + (tid >> 6) * 8]) = tst1;
