@@ -63,7 +63,8 @@ def kernel_bytes(stage, T, N, H, HV, units):
     kunits = units * H // HV                              # (chunk, key head) pairs
     gates = 4 + 2 * C * 4                                 # e^gamma_L, e^gamma, e^(gamma_L - gamma)
     fwd_ops = units * (2 * t_cd + t_cc + gates) + kunits * 2 * t_cd    # W, U^T, P; Q~, K^T
-    bwd_ops = units * (t_cd + 3 * t_cc + gates) + kunits * 2 * t_cd    # W^T, P^T, T, T^T; Q~^T, K^
+    bwd_ops = units * (t_cd + 3 * t_cc + gates + 2 * C * 4) + kunits * 2 * t_cd  # W^T, P^T, T,
+    #                                                   T^T, gates, gamma and beta; Q~^T, K^
     return {
         "chunk_prep": 2 * qk + vv + 2 * gb + fwd_ops + bwd_ops,
         # reads the forward operands, h0; writes o, hT, the saved state and D
@@ -71,8 +72,10 @@ def kernel_bytes(stage, T, N, H, HV, units):
         # reads W^T, P^T, the gates, Q~^T, K^, dO; writes dh0, dh', dD, dD^T
         "bwd_dh_scan": units * (t_cd + t_cc + gates) + kunits * 2 * t_cd + vv + st
                        + units * (s_bf + 2 * t_cd),
-        # reads q, k, v, dO, g, beta, h, D, dh', dD, dD^T, T, T^T; writes dq, dk, dv, dg, dbeta
-        "bwd_chunk": 4 * qk + 3 * vv + 4 * gb + units * (2 * s_bf + 3 * t_cd + 2 * t_cc),
+        # reads q, k, v, dO, h, D, dh', dD, dD^T, T, T^T and the saved gates (gamma, beta,
+        # e^gamma, e^(gamma_L - gamma)); writes dq, dk, dv, dg, dbeta
+        "bwd_chunk": 4 * qk + 3 * vv + 2 * gb
+                     + units * (2 * s_bf + 3 * t_cd + 2 * t_cc + 4 * C * 4),
     }.get(stage, 0)
 
 

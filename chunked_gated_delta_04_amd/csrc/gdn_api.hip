@@ -106,6 +106,7 @@ PrepOut prep_views(char* ws, const Layout& L, const gdn_problem* p) {
   o.gL = reinterpret_cast<float*>(ws + L.gL);
   o.gE = reinterpret_cast<float*>(ws + L.gE);
   o.T = nullptr;
+  o.gB = nullptr;
   o.G = p->HV / p->H;
   return o;
 }
@@ -114,14 +115,15 @@ PrepOut prep_views(char* ws, const Layout& L, const gdn_problem* p) {
 // elements each); then the backward's WY operands: per (value head, chunk)
 // W^T (64 x 128) and P^T (64 x 64), per (key head, chunk) Q~^T and K^
 // (64 x 128 each), per (value head, chunk) T and T^T (2 x 64 x 64); then in
-// fp32 per (value head, chunk) e^gamma_L and the kGates gate factors.
+// fp32 per (value head, chunk) e^gamma_L, the kGates gate factors, and the
+// cumulative decay gamma (base 2) and beta (kGates more).
 // the gate factors start 16-byte aligned after the e^gamma_L values
 size_t gates_offset(size_t blocks) { return (blocks + 3) / 4 * 4; }
 size_t saved_bytes(const gdn_problem* p, int64_t NC) {
   const size_t blocks = (size_t)p->HV * (size_t)NC, kblocks = (size_t)p->H * (size_t)NC;
   return (blocks * ((size_t)kSavedBlock + kBlk64x128 + 3 * kBlk64x64) +
           kblocks * 2 * kBlk64x128) * 2 +
-         (gates_offset(blocks) + blocks * kGates) * sizeof(float);
+         (gates_offset(blocks) + 2 * blocks * kGates) * sizeof(float);
 }
 PrepOut saved_bwd_views(uint16_t* saved, const gdn_problem* p, int64_t NC) {
   const size_t blocks = (size_t)p->HV * (size_t)NC, kblocks = (size_t)p->H * (size_t)NC;
@@ -134,6 +136,7 @@ PrepOut saved_bwd_views(uint16_t* saved, const gdn_problem* p, int64_t NC) {
   o.T = b;                              b += blocks * 2 * kBlk64x64;
   o.gL = reinterpret_cast<float*>(b);
   o.gE = o.gL + gates_offset(blocks);
+  o.gB = o.gE + blocks * kGates;
   o.U = nullptr;
   o.G = p->HV / p->H;
   return o;
@@ -424,7 +427,7 @@ static int chunk_bwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_
   }));
   GDN_TRY(clk.run([&] {
     return launch_bwd_chunk(table, (int)NC, p->H, p->HV, scale, q, k, v, g, beta, saved, prep.T,
-                            bufs, dO, dq, dk, dv, dg, dbeta, s);
+                            prep.gE, prep.gB, bufs, dO, dq, dk, dv, dg, dbeta, s);
   }));
   if (n_stages) *n_stages = clk.n;
   return GDN_OK;

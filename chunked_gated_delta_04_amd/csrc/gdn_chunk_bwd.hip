@@ -367,7 +367,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ g,
     const float* __restrict__ beta, const uint16_t* __restrict__ saved,
-    const uint16_t* __restrict__ Tmat, BwdBufs bufs, const uint16_t* __restrict__ dO,
+    const uint16_t* __restrict__ Tmat, const float* __restrict__ gE,
+    const float* __restrict__ gB, BwdBufs bufs, const uint16_t* __restrict__ dO,
     uint16_t* __restrict__ dq, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
     float* __restrict__ dg, float* __restrict__ dbeta) {
   const int c = blockIdx.x, h = blockIdx.y;
@@ -555,13 +556,13 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         const_cast<uint16_t*>(v) + ((size_t)t0 * HV + hv) * kHead, 0, L * (int)rs * 2, kBufferWord3);
 
     // ---- gate requests first (every wave; wave 0 uses them), so that their
-    //      wait does not cover the operand requests below
-    const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(g) + (size_t)t0 * HV + hv, 0, L * HV * 4, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(beta) + (size_t)t0 * HV + hv, 0, L * HV * 4, kBufferWord3);
-    float gv = load_f32(rg, lane * HV * 4);  // 0 past the chunk's end
-    const float bv = load_f32(rb, lane * HV * 4);
+    //      wait does not cover the operand requests below: gamma (base 2),
+    //      beta, e^gamma and e^(gamma_L - gamma) of each token as the forward's
+    //      WY pass formed them, four contiguous 256-byte rows
+    const float gam_t = gB[blk * kGates + lane];
+    const float bet_t = gB[blk * kGates + kChunk + lane];
+    const float eg_t = gE[blk * kGates + lane];
+    const float ebw_t = gE[blk * kGates + kChunk + lane];
 
     // ---- requests for the dP phase: the own rows of dO and q, the D rows of
     //      this wave's dP tiles. Operand pieces the wave does not use (tiles
@@ -606,13 +607,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     // ---- gates (wave 0, after the previous value head's gate gradients)
     if (wave == 0) {
       if (jg > 0) dg_out(hv - 1, lane);
-      gv = wave_prefix_sum(gv, lane);  // as in the forward's WY pass
-      const float g2 = gv * kLog2e;  // base-2 exponent
-      S.gam[lane] = g2;
-      S.bet[lane] = bv;
-      const float gl2 = lane_value(g2, L - 1);
-      S.eg[lane] = exp2_fast(g2);
-      S.ebw[lane] = lane < L ? exp2_fast(gl2 - g2) : 0.f;
+      S.gam[lane] = gam_t;
+      S.bet[lane] = bet_t;
+      S.eg[lane] = eg_t;
+      S.ebw[lane] = ebw_t;
     }
     lds_barrier();
 
@@ -1080,11 +1078,12 @@ hipError_t launch_bwd_dh_scan(const int32_t* seq_first, int N, int HV, int NC,
 hipError_t launch_bwd_chunk(const ChunkInfo* table, int NC, int H, int HV, float scale,
                             const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const float* g, const float* beta, const uint16_t* saved,
-                            const uint16_t* Tmat, const BwdBufs& bufs, const uint16_t* dO,
+                            const uint16_t* Tmat, const float* gE, const float* gB,
+                            const BwdBufs& bufs, const uint16_t* dO,
                             uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dg, float* dbeta,
                             hipStream_t stream) {
   hipLaunchKernelGGL(bwd_chunk_kernel, dim3(NC, H), dim3(512), 0, stream, table, NC, H, HV, scale,
-                     q, k, v, g, beta, saved, Tmat, bufs, dO, dq, dk, dv, dg, dbeta);
+                     q, k, v, g, beta, saved, Tmat, gE, gB, bufs, dO, dq, dk, dv, dg, dbeta);
   return hipGetLastError();
 }
 

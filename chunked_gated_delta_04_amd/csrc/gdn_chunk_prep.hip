@@ -32,6 +32,7 @@
 //   T        (not written)                   T [i][j] and T^T [j][i]
 //   gL       e^gamma_L (fp32)                same
 //   gE       e^gamma and e^(gamma_L - gamma) per token (fp32), same
+//   gB       (not written)                   gamma (base 2) and beta per token (fp32)
 // and per (key head, chunk) block, shared by the key head's value heads:
 //   Q~       [64 tok][128 k]                 Q~^T  [128 k][64 tok]
 //   K^       K^T [128 k][64 tok]             K^    [64 tok][128 k]
@@ -258,6 +259,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
       if (kB) {
         bo.gE[blk * kGates + lane] = e;
         bo.gE[blk * kGates + kChunk + lane] = bw;
+        bo.gB[blk * kGates + lane] = g2;  // the gradient pass reads these as they are
+        bo.gB[blk * kGates + kChunk + lane] = bv;
       }
       if (lane == 0) {
         fo.gL[blk] = exp2_fast(gl2);

@@ -23,6 +23,8 @@ struct PrepOut {
   float* gE;     // value head: e^gamma (64), then e^(gamma_L - gamma) (64, zero past
                  // the chunk's end), 128 per block
   uint16_t* T;   // value head, backward only: T [i][j] then T^T [j][i], 2 x 64 x 64
+  float* gB;     // value head, backward only: the cumulative decay gamma in base 2
+                 // (64), then beta (64, zero past the chunk's end), 128 per block
   int G;         // value heads per key head
 };
 
@@ -81,7 +83,8 @@ hipError_t launch_bwd_dh_scan(const int32_t* seq_first, int N, int HV, int NC,
 hipError_t launch_bwd_chunk(const ChunkInfo* table, int NC, int H, int HV, float scale,
                             const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const float* g, const float* beta, const uint16_t* saved,
-                            const uint16_t* Tmat, const BwdBufs& bufs, const uint16_t* dO,
+                            const uint16_t* Tmat, const float* gE, const float* gB,
+                            const BwdBufs& bufs, const uint16_t* dO,
                             uint16_t* dq, uint16_t* dk,
                             uint16_t* dv, float* dg, float* dbeta, hipStream_t stream);
 
