@@ -502,6 +502,26 @@ def main():
                      "flop_per_byte": round(dom_flops / dom_bytes, 2) if dom_bytes else None,
                      "mfma_frac": round(flops_frac, 5)})
 
+    # Cold caches: the same step timed alone, rep by rep (HIP events on the
+    # stream), after a 512 MiB device fill that evicts L2 and the 256 MB
+    # Infinity Cache; the fill is outside the events. The back-to-back steps
+    # above reuse the same inputs, so their first kernel may find part of
+    # them still cached from the previous step.
+    flush = torch.empty(512 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+    cold_ev = make_events(h, 2 * args.steps)
+    for i in range(args.steps):
+        flush.fill_(float(i))
+        h.hipEventRecord(cold_ev[2 * i], ctypes.c_void_p(stream.cuda_stream))
+        step()
+        h.hipEventRecord(cold_ev[2 * i + 1], ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    cold = sorted(elapsed_ms(h, cold_ev[2 * i], cold_ev[2 * i + 1]) for i in range(args.steps))
+    cold_ms = cold[len(cold) // 2]
+    cold_cache = {"ms_median": round(cold_ms, 4), "ms_min": round(cold[0], 4),
+                  "ms_max": round(cold[-1], 4), "tokens_per_s": round(T / (cold_ms * 1e-3), 1),
+                  "reps": args.steps, "flush_bytes": 512 * 2 ** 20}
+    del flush
+
     extra = None
     if not args.no_secondary:
         del d, saved, wsf, wsb
@@ -525,6 +545,7 @@ def main():
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "roofline": roofline,
+        "cold_cache": cold_cache,
         "cpu_baseline": cpu,
         "secondary": extra,
     }
