@@ -8,11 +8,19 @@ to dq/dk/dv/dg/dbeta/dh0. Inputs are seeded synthetic tensors already resident
 in HBM when timing starts. Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+                    [--no-secondary] [--fresh-processes 4] [--profile-step]
 
-Per-kernel durations come from HIP events that the library records around
-each kernel it launches, on the stream it launches on. The roofline object is
-for the kernel with the largest average duration. The CPU baseline times the
-fp64 oracle on a bounded sample of the same workload.
+The headline is the mean of `steps` back-to-back steps between two events.
+Beside it: the pages' operator protocol (each rep alone after a 512 MiB fill
+that evicts the caches, median of the reps) in this process and in fresh
+processes (median of their medians). Per-kernel durations come from HIP events
+that the library records around each kernel it launches, on the stream it
+launches on. Rooflines use the method's own bytes and flops (inputs, outputs
+and the bf16 per-chunk states; no hand-off of this library), the roofline
+object for the kernel with the largest average duration; the HBM bytes the
+counters saw for it (committed profile summary) stand beside them. The CPU
+baseline times the fp64 oracle on all host cores on a bounded sample of the
+4 x 4096 and varlen forwards, the fwd+bwd step and the decode step.
 """
 import argparse
 import ctypes
@@ -40,9 +48,7 @@ F_STATE = 2 * C * D * D                     # one 64x128 by 128x128 product
 F_FWD = F_KKT + F_TSOLVE + 4 * F_TRI + 3 * F_STATE     # 9,024,853
 F_FWDBWD = 3 * F_FWD
 # per-kernel shares of the model (forward: WY pass vs scan; backward: its two kernels
-# split the 2 * F_FWD gradient work as the gradient contractions are assigned to them;
-# the WY pass of a forward that saves also lays out W and P for the backward, which
-# the model does not count again)
+# split the 2 * F_FWD gradient work as the gradient contractions are assigned to them)
 KERNEL_FLOPS = {
     "chunk_prep": F_KKT + F_TSOLVE + 3 * F_TRI,                 # K K^T, T, W, U, Q K^T
     "fwd_scan": F_TRI + 3 * F_STATE,                            # attn D, W h, Q h, K^T D
@@ -51,32 +57,30 @@ KERNEL_FLOPS = {
 }
 
 
-
-def kernel_bytes(stage, T, N, H, HV, units):
-    """Algorithmic HBM bytes of one launch of a stage of the step: every input,
-    workspace hand-off and output read or written once (bf16 tensors and tiles,
-    fp32 gates and states). units = (chunk, value head) pairs; the normalised
-    q and k tiles exist once per (chunk, key head), units * H / HV of them."""
-    qk, vv, gb = T * H * D * 2, T * HV * D * 2, T * HV * 4
-    st = N * HV * D * D * 4                               # fp32 states of the sequences
-    t_cd, t_cc, s_bf = C * D * 2, C * C * 2, D * D * 2    # 64x128 and 64x64 tiles, bf16 state
-    kunits = units * H // HV                              # (chunk, key head) pairs
-    gates = 4 + 2 * C * 4                                 # e^gamma_L, e^gamma, e^(gamma_L - gamma)
-    fwd_ops = units * (2 * t_cd + t_cc + gates) + kunits * 2 * t_cd    # W, U^T, P; Q~, K^T
-    bwd_ops = units * (t_cd + 3 * t_cc + gates + 2 * C * 4) + kunits * 2 * t_cd  # W^T, P^T, T,
-    #                                                   T^T, gates, gamma and beta; Q~^T, K^
-    return {
-        "chunk_prep": 2 * qk + vv + 2 * gb + fwd_ops + bwd_ops,
-        # reads the forward operands, h0; writes o, hT, the saved state and D
-        "fwd_scan": fwd_ops + 2 * st + vv + units * (s_bf + t_cd),
-        # reads W^T, P^T, the gates, Q~^T, K^, dO; writes dh0, dh', dD, dD^T
-        "bwd_dh_scan": units * (t_cd + t_cc + gates) + kunits * 2 * t_cd + vv + st
-                       + units * (s_bf + 2 * t_cd),
-        # reads q, k, v, dO, h, D, dh', dD, dD^T, T, T^T and the saved gates (gamma, beta,
-        # e^gamma, e^(gamma_L - gamma)); writes dq, dk, dv, dg, dbeta
-        "bwd_chunk": 4 * qk + 3 * vv + 2 * gb
-                     + units * (2 * s_bf + 3 * t_cd + 2 * t_cc + 4 * C * 4),
-    }.get(stage, 0)
+def method_bytes(T, N, H, HV, n_chunks):
+    """The method's own HBM bytes (nothing of this library's hand-offs): every
+    input read once, every output written once, and the per-chunk states h_c
+    (bf16) written by the forward and read by the backward. Per kernel, the part
+    of those the kernel's job needs - what it could not avoid moving whatever
+    the design: the WY pass reads q, k, v, g, beta; the forward scan reads h0
+    and writes o, hT, h_c; the dh scan reads q, k, g, beta and dO and writes
+    dh0; the gradient pass reads q, k, v, g, beta, dO and h_c and writes dq, dk,
+    dv, dg, dbeta. The step counts each tensor once per pass that must move it
+    (the forward reads the inputs, the backward reads them again)."""
+    qk = T * H * D * 2                   # q or k (or dq, dk), bf16
+    vv = T * HV * D * 2                  # v, o, dO or dv, bf16
+    gb = T * HV * 4                      # g, beta, dg or dbeta, fp32
+    st = N * HV * D * D * 4              # h0, hT, dh0 (fp32 states)
+    hc = n_chunks * HV * D * D * 2       # per-chunk start states, bf16
+    per = {
+        "chunk_prep": 2 * qk + vv + 2 * gb,
+        "fwd_scan": st + vv + st + hc,
+        "bwd_dh_scan": 2 * qk + 2 * gb + vv + st,
+        "bwd_chunk": 2 * qk + vv + 2 * gb + vv + hc + 2 * qk + vv + 2 * gb,
+    }
+    fwd = 2 * qk + vv + 2 * gb + st + vv + st + hc
+    bwd = 2 * qk + vv + 2 * gb + hc + vv + 2 * qk + vv + 2 * gb + st
+    return per, {"fwd": fwd, "bwd": bwd, "step": fwd + bwd}
 
 
 # stage name (gdn_stage_name) -> kernel symbol as the profiler names it
@@ -86,7 +90,7 @@ STAGE_KERNELS = {"chunk_table": "chunk_table_kernel", "chunk_prep": "chunk_prep_
 
 
 def kernel_source_hash():
-    """Hash of the HIP sources, to tie recorded counter traffic to the code it measured."""
+    """Hash of the HIP sources, to tie recorded counters to the code they measured."""
     import glob
     import hashlib
     h = hashlib.sha256()
@@ -97,20 +101,20 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed counter summary
-    (FETCH_SIZE and WRITE_SIZE, calibrated by a plain copy), or None when that
-    summary was taken on other kernel sources."""
+def recorded_counters():
+    """Per-kernel counter figures of the committed summary of this workload (HBM
+    bytes from FETCH_SIZE / WRITE_SIZE calibrated by a plain copy; MFMA busy
+    fraction and bf16 MFMA work), or {} when that summary was taken on other
+    kernel sources."""
     path = os.path.join(ROOT, "profiles", WORKLOAD + ".md")
     try:
         text = open(path).read()
         blob = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
     except (OSError, IndexError, ValueError):
-        return None
+        return {}
     if blob.get("source") != kernel_source_hash():
-        return None
-    t = blob.get("traffic", {}).get(kernel)
-    return None if t is None else t["fetch_bytes"] + t["write_bytes"]
+        return {}
+    return blob.get("kernels", {})
 
 
 def hip():
@@ -141,34 +145,148 @@ def elapsed_ms(h, a, b):
     return ms.value
 
 
-def cpu_baseline(inp, target_s):
-    """fp64 oracle forward + backward on the first tokens of the first sequence,
-    all heads; tokens per second on this host. A 32-token probe sizes the
-    sample to about `target_s` seconds of oracle work."""
-    import torch
+# ---------------------------------------------------------------- CPU baseline
+# The fp64 oracle as it stands, timed on the host cores: every (sequence, key
+# head) slice of a workload is an independent task (its value heads read only
+# that key head), run by a pool of spawned worker processes, one numpy thread
+# each. The tasks are top-level functions so that the workers can import them.
+def _oracle_fwd_task(a):
     from oracle import recurrence as R
+    q, k, v, g, beta, cu, h0 = a
+    R.forward(q, k, v, g, beta, cu, h0)
+    return q.shape[0]
+
+
+def _oracle_fwdbwd_task(a):
+    from oracle import recurrence as R
+    q, k, v, g, beta, cu, h0, do = a
+    R.forward(q, k, v, g, beta, cu, h0)
+    R.backward(q, k, v, g, beta, cu, do, h0)
+    return q.shape[0]
+
+
+def _oracle_decode_task(a):
+    """One decode step over a group of rows; returns the seconds of the oracle
+    call alone (the rows' pool blocks are large, and shipping them to the worker
+    is not oracle work)."""
+    from oracle import recurrence as R
+    t = time.perf_counter()
+    R.decode_step(*a)
+    return time.perf_counter() - t
+
+
+def _noop(_):
+    return os.getpid()
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def _host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(target_s):
+    """The oracle on the host's cores, on a bounded sample of each workload the
+    pages' plan names: the forward of the 4 x 4096 pack and of the 12-sequence
+    varlen pack, forward + backward of the 2 x 8192 pack (the headline's step)
+    and one decode step of the 256-row batch. A sample is the first n tokens of
+    every sequence over all heads; a 64-token probe of the same tasks sizes n
+    to about `target_s` seconds. Returns the bench line's cpu_baseline object
+    (value: the fwd+bwd tokens/s, the metric of the headline)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    import numpy as np
+
+    from chunked_gated_delta_04_amd import synth
+
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    workers = max(1, min(16, _host_cores()))
 
     def f64(t):
-        return t.to(torch.float64).numpy()
+        return t.double().numpy()
 
-    def run(n):
-        sl = slice(0, n)
-        args = [f64(inp[k][sl]) for k in ("q", "k", "v", "g", "beta")]
-        h0 = f64(inp["h0"][0:1])
-        do = f64(inp["do"][sl])
-        t0 = time.perf_counter()
-        R.forward(*args, [0, n], h0)
-        R.backward(*args, [0, n], do, h0)
-        return time.perf_counter() - t0
+    def slices(inp, n, with_do):
+        H = inp["q"].shape[1]
+        G = inp["v"].shape[1] // H
+        cu = inp["cu_seqlens"].tolist()
+        tasks, tokens = [], 0
+        for s in range(len(cu) - 1):
+            t0, t1 = cu[s], min(cu[s + 1], cu[s] + n)
+            tokens += t1 - t0
+            for h in range(H):
+                hv = slice(h * G, (h + 1) * G)
+                a = [f64(inp["q"][t0:t1, h:h + 1]), f64(inp["k"][t0:t1, h:h + 1]),
+                     f64(inp["v"][t0:t1, hv]), f64(inp["g"][t0:t1, hv]),
+                     f64(inp["beta"][t0:t1, hv]), [0, t1 - t0],
+                     None if inp.get("h0") is None else f64(inp["h0"][s:s + 1, hv])]
+                if with_do:
+                    a.append(f64(inp["do"][t0:t1, hv]))
+                tasks.append(tuple(a))
+        return tasks, tokens
 
-    probe = run(32)
-    n = int(max(32, min(8192, 32 * target_s / max(probe, 1e-3))))
-    dt = run(n)
-    return dict(value=n / dt, unit="tokens/s", cores=1, kind="oracle",
-                sample=(f"fp64 oracle forward + backward over the first {n} tokens of sequence 0 "
-                        f"of {WORKLOAD} (all 16 key / 32 value heads), {dt:.1f} s on "
-                        f"{platform.processor() or platform.machine()} ({os.cpu_count()} host cores "
-                        f"visible; numpy einsum runs on 1)"))
+    def timed(ex, fn, tasks):
+        t = time.perf_counter()
+        list(ex.map(fn, tasks))
+        return time.perf_counter() - t
+
+    out = {}
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
+        list(ex.map(_noop, range(4 * workers)))           # workers up before any timing
+        for name, fn, with_do in (("fwd_4x4096_h16_hv32", _oracle_fwd_task, False),
+                                  ("fwd_varlen12_32768_h16_hv32", _oracle_fwd_task, False),
+                                  (WORKLOAD, _oracle_fwdbwd_task, True)):
+            inp = synth.workload_inputs(name)
+            probe, ptok = slices(inp, 64, with_do)
+            dt = timed(ex, fn, probe)
+            longest = max(np.diff(inp["cu_seqlens"].numpy()))
+            n = int(min(longest, max(64, 64 * target_s / max(dt, 1e-3))))
+            tasks, tokens = slices(inp, n, with_do)
+            dt = timed(ex, fn, tasks)
+            out[name] = {"tokens_per_s": round(tokens / dt, 2), "tokens": tokens,
+                         "first_tokens_per_sequence": n, "seconds": round(dt, 2),
+                         "tasks": len(tasks), "what": "forward + backward" if with_do else "forward"}
+            del inp, probe, tasks
+        name = "decode_256_pool512_h16_hv32"
+        inp = synth.workload_inputs(name)
+        idx = inp["ssm_state_indices"].numpy()
+        pool = inp["state_pool"]
+        tasks = []
+        for rows in np.array_split(np.arange(idx.size), workers):
+            # the rows' own pool blocks, renumbered 1..n (0 stays the null block)
+            act = [int(i) for i in idx[rows] if i > 0]
+            sub = np.zeros((len(act) + 1,) + tuple(pool.shape[1:]))
+            sub[1:] = f64(pool[act])
+            ren = np.array([act.index(int(i)) + 1 if i > 0 else int(i) for i in idx[rows]],
+                           dtype=np.int64)
+            tasks.append((f64(inp["q"][rows]), f64(inp["k"][rows]), f64(inp["v"][rows]),
+                          f64(inp["a"][rows]), f64(inp["b"][rows]), f64(inp["A_log"]),
+                          f64(inp["dt_bias"]), sub, ren))
+        # the groups run at once, one per worker: the step takes the slowest group's time
+        dt = max(ex.map(_oracle_decode_task, tasks))
+        out[name] = {"rows_per_s": round(idx.size / dt, 2), "rows": int(idx.size),
+                     "seconds": round(dt, 3), "tasks": len(tasks),
+                     "what": "one decode step (row groups in parallel, oracle time per group)"}
+    head = out[WORKLOAD]
+    return dict(
+        value=head["tokens_per_s"], unit="tokens/s", cores=workers, kind="oracle",
+        cpu_model=_cpu_model(), host_cores=_host_cores(),
+        sample=(f"fp64 oracle forward + backward over the first "
+                f"{head['first_tokens_per_sequence']} tokens of both sequences of {WORKLOAD} "
+                f"(all 16 key / 32 value heads, {head['tasks']} (sequence, key head) tasks, "
+                f"{head['seconds']} s) on {workers} worker processes of one thread each"),
+        per_workload=out)
 
 
 def copy_probe(mib):
@@ -199,13 +317,45 @@ def time_call(h, stream, fn, steps, warmup):
     return elapsed_ms(h, ev[0], ev[1]) / steps
 
 
+def fwdbwd_step_ms(h, stream, name, steps, warmup):
+    """Mean ms of a forward (saving for the backward) + backward step on a workload."""
+    import torch
+    from chunked_gated_delta_04_amd import gdn, synth
+    inp = synth.workload_inputs(name)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    T, H, _ = inp["q"].shape
+    HV = inp["v"].shape[1]
+    N = inp["cu_seqlens"].numel() - 1
+    p = gdn.make_problem(N, T, H, HV, d["cu_seqlens"], inp["cu_seqlens"])
+    o = torch.empty(T, HV, 128, dtype=torch.bfloat16, device="cuda")
+    hT = torch.empty(N, HV, 128, 128, dtype=torch.float32, device="cuda")
+    saved = torch.empty(gdn.gdn_chunk_saved_size(p), dtype=torch.uint8, device="cuda")
+    wsf = torch.empty(gdn.gdn_chunk_fwd_workspace_size(p), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(gdn.gdn_chunk_bwd_workspace_size(p), dtype=torch.uint8, device="cuda")
+    g_ = dict(dq=torch.empty_like(d["q"]), dk=torch.empty_like(d["k"]), dv=torch.empty_like(d["v"]),
+              dg=torch.empty_like(d["g"]), dbeta=torch.empty_like(d["beta"]),
+              dh0=torch.empty(N, HV, 128, 128, dtype=torch.float32, device="cuda"))
+
+    def step():
+        gdn.gdn_chunk_fwd(p, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], o, hT, saved,
+                          wsf, stream)
+        gdn.gdn_chunk_bwd(p, d["q"], d["k"], d["v"], d["g"], d["beta"], saved, d["do"], None,
+                          g_["dq"], g_["dk"], g_["dv"], g_["dg"], g_["dbeta"], g_["dh0"], wsb,
+                          stream)
+    ms = time_call(h, stream, step, steps, warmup)
+    return T, ms
+
+
 def secondary(h, stream, steps, warmup):
     """Forward-only throughput on the 4 x 4096 and the 12-sequence varlen packs, the
-    decode step against the HBM roofline, and the paged prefill."""
+    decode step against the HBM roofline, the paged prefill, the same packs at one
+    GPU's share of a TP = 2 head split (8 key / 16 value heads), and one long
+    sequence of 65,536 and 131,072 tokens."""
     import torch
     from chunked_gated_delta_04_amd import gdn, synth
     out = {}
-    for name in ("fwd_4x4096_h16_hv32", "fwd_varlen12_32768_h16_hv32"):
+    for name in ("fwd_4x4096_h16_hv32", "fwd_varlen12_32768_h16_hv32",
+                 "fwd_4x4096_h8_hv16", "fwd_varlen12_32768_h8_hv16"):
         inp = synth.workload_inputs(name)
         d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
         T, H, _ = inp["q"].shape
@@ -244,6 +394,11 @@ def secondary(h, stream, steps, warmup):
     out.update(paged_prefill(h, stream, steps, warmup))
     out.update(recompute_and_transition(h, stream, steps, warmup))
     out.update(short_conv(h, stream, steps, warmup))
+    for name, reps in (("fwdbwd_2x8192_h8_hv16", steps), ("fwdbwd_1x65536_h16_hv32", steps),
+                       ("fwdbwd_1x131072_h16_hv32", max(3, steps // 4))):
+        T, ms = fwdbwd_step_ms(h, stream, name, reps, min(warmup, 2))
+        out[name] = {"ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1)}
+        torch.cuda.empty_cache()
     return out
 
 
@@ -383,31 +538,12 @@ def paged_prefill(h, stream, steps, warmup):
                    "gather_scatter_ms": round(ms_copies, 4)}}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the forward-only and decode timings")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="only run a plain copy of this many MiB (counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
-              f"(--gpus {args.gpus} requested)", file=sys.stderr)
-        sys.exit(2)
-    if args.copy_probe_mib:
-        copy_probe(args.copy_probe_mib)
-        return
-
+def setup_step(dev):
+    """Inputs, outputs and workspaces of the fwd+bwd step, resident on `dev`;
+    returns (meta, step) where step(ev_f, ev_b) runs one forward (saving for the
+    backward) and one backward, recording per-kernel events when given."""
     import torch
     from chunked_gated_delta_04_amd import gdn, synth
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     inp = synth.workload_inputs(WORKLOAD)
     d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     T, H, _ = inp["q"].shape
@@ -415,8 +551,8 @@ def main():
     N = inp["cu_seqlens"].numel() - 1
     host = inp["cu_seqlens"].to(torch.int32)
     p = gdn.make_problem(N, T, H, HV, d["cu_seqlens"], host)
-    NC = gdn.gdn_num_chunks(p)
-
+    lens = (host[1:] - host[:-1]).tolist()
+    n_chunks = sum((L + 63) // 64 for L in lens)
     o = torch.empty(T, HV, 128, dtype=torch.bfloat16, device=dev)
     hT = torch.empty(N, HV, 128, 128, dtype=torch.float32, device=dev)
     saved = torch.empty(gdn.gdn_chunk_saved_size(p), dtype=torch.uint8, device=dev)
@@ -441,7 +577,108 @@ def main():
                                      None, dq, dk, dv, dg, dbeta, dh0, wsb, ev_b, stream)
         return nf, nb
 
+    meta = dict(T=T, H=H, HV=HV, N=N, n_chunks=n_chunks, stream=stream,
+                saved_bytes=saved.numel(), workspace_bytes=wsf.numel() + wsb.numel())
+    return meta, step
+
+
+FLUSH_BYTES = 512 * 2 ** 20
+
+
+def cold_protocol(h, stream, step, reps, warmup, dev):
+    """The pages' operator timing (cake_gdn page, 'Performance', operator level):
+    `warmup` untimed steps, then `reps` steps timed one by one with events, each
+    after a 512 MiB device fill (outside the events) that evicts L2 and the
+    Infinity Cache. Returns the sorted per-rep ms."""
+    import torch
+    for _ in range(warmup):
+        step()
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    ev = make_events(h, 2 * reps)
+    for i in range(reps):
+        flush.fill_(float(i))
+        h.hipEventRecord(ev[2 * i], ctypes.c_void_p(stream.cuda_stream))
+        step()
+        h.hipEventRecord(ev[2 * i + 1], ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    del flush
+    return sorted(elapsed_ms(h, ev[2 * i], ev[2 * i + 1]) for i in range(reps))
+
+
+def child_protocol(reps, warmup):
+    """One fresh process's run of the cold protocol; prints its median."""
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    meta, step = setup_step(dev)
+    ms = cold_protocol(hip(), meta["stream"], step, reps, warmup, dev)
+    print(json.dumps({"median_ms": ms[len(ms) // 2], "min_ms": ms[0], "max_ms": ms[-1]}),
+          flush=True)
+
+
+def fresh_processes(n, reps, warmup):
+    """The cold protocol in `n` fresh processes, one after another (the Cake page's
+    protocol: fresh processes, the median of their medians)."""
+    import subprocess
+    meds = []
+    for _ in range(n):
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--child-protocol",
+                            "--steps", str(reps), "--warmup", str(warmup)],
+                           capture_output=True, text=True, timeout=300)
+        if r.returncode != 0:
+            raise RuntimeError(f"fresh-process timing failed:\n{r.stderr[-2000:]}")
+        meds.append(json.loads(r.stdout.strip().splitlines()[-1])["median_ms"])
+    s = sorted(meds)
+    return {"processes": n, "reps_per_process": reps, "medians_ms": [round(x, 4) for x in meds],
+            "median_of_medians_ms": round(s[len(s) // 2] if n % 2 else
+                                          0.5 * (s[n // 2 - 1] + s[n // 2]), 4)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the timings of the other workloads")
+    ap.add_argument("--cpu-seconds", type=float, default=5.0,
+                    help="target oracle seconds per CPU-baseline workload")
+    ap.add_argument("--fresh-processes", type=int, default=4,
+                    help="fresh processes for the median-of-medians timing (0: skip)")
+    ap.add_argument("--profile-step", action="store_true",
+                    help="only run warmup + steps of the fwd+bwd step (for rocprofv3)")
+    ap.add_argument("--child-protocol", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
+    if args.child_protocol:
+        child_protocol(args.steps, args.warmup)
+        return
+
+    import torch
+
+    from chunked_gated_delta_04_amd import gdn
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    meta, step = setup_step(dev)
+    T, H, HV, N, stream = meta["T"], meta["H"], meta["HV"], meta["N"], meta["stream"]
     h = hip()
+    if args.profile_step:
+        for _ in range(args.warmup + args.steps):
+            step()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_step": WORKLOAD, "steps": args.warmup + args.steps}), flush=True)
+        return
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -475,62 +712,71 @@ def main():
                 name = "chunk_table_bwd"
             stages.setdefault(name, []).append(elapsed_ms(h, evb[i][2 * j], evb[i][2 * j + 1]))
     stage_ms = {k: sum(v) / len(v) for k, v in stages.items()}
-    dom = max(stage_ms, key=stage_ms.get)
 
-    units = NC * HV                                   # (chunk, value head) pairs per launch
+    # Rooflines on the method's own bytes and flops (no hand-offs of this library).
+    n_chunks = meta["n_chunks"]
+    units = n_chunks * HV                            # (chunk, value head) pairs
+    per_bytes, totals = method_bytes(T, N, H, HV, n_chunks)
+    counters = recorded_counters()
+    kernels = {}
+    for stage, ms in stage_ms.items():
+        b = per_bytes.get(stage)
+        f = KERNEL_FLOPS.get(stage, 0) * units
+        row = {"ms": round(ms, 4)}
+        if b:
+            row.update(algorithmic_bytes=b, GBps=round(b / (ms * 1e-3) / 1e9, 1),
+                       hbm_frac=round(b / (ms * 1e-3) / PEAK_HBM, 4),
+                       flops=f, mfma_frac=round(f / (ms * 1e-3) / PEAK_BF16, 4))
+            c = counters.get(STAGE_KERNELS.get(stage, stage))
+            if c:
+                tb = c.get("fetch_bytes", 0) + c.get("write_bytes", 0)
+                row.update(traffic_bytes=tb, traffic_over_algorithmic=round(tb / b, 3))
+                for key in ("mfma_busy_frac", "mfma_bf16_flops_counted"):
+                    if key in c:
+                        row[key] = c[key]
+        kernels[stage] = row
+    dom = max((k for k in stage_ms if k in per_bytes), key=stage_ms.get)
+    dk_ = kernels[dom]
+    # every kernel of the step is below the chip's balance point (2.5e15 / 8e12 =
+    # 312 flop per byte) on these bytes, so HBM bandwidth is the roof
+    roofline = {"bound": "hbm", "achieved": dk_["GBps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                "frac": dk_["hbm_frac"], "traffic": dk_.get("traffic_bytes"),
+                "kernel": dom, "kernel_ms": dk_["ms"], "algorithmic_bytes": dk_["algorithmic_bytes"],
+                "traffic_over_algorithmic": dk_.get("traffic_over_algorithmic"),
+                "mfma_frac": dk_["mfma_frac"], "mfma_busy_frac": dk_.get("mfma_busy_frac")}
     step_flops = F_FWDBWD * units
+    t_attain = max(step_flops / PEAK_BF16, totals["step"] / PEAK_HBM)
+    step_roof = {"algorithmic_bytes": totals["step"], "fwd_bytes": totals["fwd"],
+                 "bwd_bytes": totals["bwd"],
+                 "achieved_GBps": round(totals["step"] / (ms_per_step * 1e-3) / 1e9, 1),
+                 "hbm_frac": round(totals["step"] / (ms_per_step * 1e-3) / PEAK_HBM, 4),
+                 "flops": step_flops,
+                 "mfma_frac": round(step_flops / (ms_per_step * 1e-3) / PEAK_BF16, 4),
+                 "attainable_ms": round(t_attain * 1e3, 4),
+                 "frac_of_attainable": round(t_attain / (ms_per_step * 1e-3), 4)}
     tokens_per_s = T / (ms_per_step * 1e-3)
-    mfma_frac = step_flops / (ms_per_step * 1e-3) / PEAK_BF16
-    # Roofline of the dominant kernel: its algorithmic flops and bytes per
-    # launch; below the chip's balance point (peak flops / peak bandwidth) the
-    # roof is HBM bandwidth, above it the bf16 MFMA rate.
-    t_dom = stage_ms[dom] * 1e-3
-    dom_flops = KERNEL_FLOPS.get(dom, 0) * units
-    dom_bytes = kernel_bytes(dom, T, N, H, HV, units)
-    flops_frac = dom_flops / t_dom / PEAK_BF16
-    if dom_bytes and dom_flops / dom_bytes < PEAK_BF16 / PEAK_HBM:
-        achieved = dom_bytes / t_dom / 1e9
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9,
-                    "unit": "GB/s", "frac": round(achieved * 1e9 / PEAK_HBM, 5)}
-    else:
-        achieved = dom_flops / t_dom / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16 / 1e12,
-                    "unit": "TFLOP/s", "frac": round(flops_frac, 5)}
-    roofline.update({"traffic": recorded_traffic(STAGE_KERNELS.get(dom, dom)), "kernel": dom,
-                     "kernel_ms": round(stage_ms[dom], 4), "algorithmic_bytes": dom_bytes,
-                     "algorithmic_flops": dom_flops,
-                     "flop_per_byte": round(dom_flops / dom_bytes, 2) if dom_bytes else None,
-                     "mfma_frac": round(flops_frac, 5)})
 
-    # Cold caches: the same step timed alone, rep by rep (HIP events on the
-    # stream), after a 512 MiB device fill that evicts L2 and the 256 MB
-    # Infinity Cache; the fill is outside the events. The back-to-back steps
-    # above reuse the same inputs, so their first kernel may find part of
-    # them still cached from the previous step.
-    flush = torch.empty(512 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
-    cold_ev = make_events(h, 2 * args.steps)
-    for i in range(args.steps):
-        flush.fill_(float(i))
-        h.hipEventRecord(cold_ev[2 * i], ctypes.c_void_p(stream.cuda_stream))
-        step()
-        h.hipEventRecord(cold_ev[2 * i + 1], ctypes.c_void_p(stream.cuda_stream))
-    torch.cuda.synchronize()
-    cold = sorted(elapsed_ms(h, cold_ev[2 * i], cold_ev[2 * i + 1]) for i in range(args.steps))
+    cold = cold_protocol(h, stream, step, args.steps, args.warmup, dev)
     cold_ms = cold[len(cold) // 2]
-    cold_cache = {"ms_median": round(cold_ms, 4), "ms_min": round(cold[0], 4),
-                  "ms_max": round(cold[-1], 4), "tokens_per_s": round(T / (cold_ms * 1e-3), 1),
-                  "reps": args.steps, "flush_bytes": 512 * 2 ** 20}
-    del flush
+    protocol = {"cold_cache": {"ms_median": round(cold_ms, 4), "ms_min": round(cold[0], 4),
+                               "ms_max": round(cold[-1], 4),
+                               "tokens_per_s": round(T / (cold_ms * 1e-3), 1),
+                               "reps": args.steps, "warmup": args.warmup,
+                               "flush_bytes": FLUSH_BYTES}}
+    if args.fresh_processes > 0:
+        fp = fresh_processes(args.fresh_processes, args.steps, args.warmup)
+        fp["tokens_per_s"] = round(T / (fp["median_of_medians_ms"] * 1e-3), 1)
+        protocol["fresh_processes"] = fp
 
     extra = None
     if not args.no_secondary:
-        del d, saved, wsf, wsb
+        del step
+        torch.cuda.empty_cache()
         extra = secondary(h, stream, args.steps, args.warmup)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args.cpu_seconds)
-        cpu["value"] = round(cpu["value"], 3)
+        cpu = cpu_baseline(args.cpu_seconds)
 
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -540,12 +786,14 @@ def main():
         "config": {"workload": WORKLOAD, "global_batch": N, "seq_len": T // N,
                    "tokens_per_step": T, "H": H, "HV": HV, "K": 128, "V": 128, "chunk": 64,
                    "parallelism": "single-gpu"},
-        "mfma_frac_of_bf16_peak": round(mfma_frac, 5),
+        "mfma_frac_of_bf16_peak": step_roof["mfma_frac"],
         "algorithmic_tflops": round(step_flops / (ms_per_step * 1e-3) / 1e12, 3),
-        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "roofline": roofline,
-        "cold_cache": cold_cache,
+        "step_roofline": step_roof,
+        "kernels": kernels,
+        "timing_protocol": protocol,
+        "memory": {"saved_bytes": meta["saved_bytes"], "workspace_bytes": meta["workspace_bytes"]},
         "cpu_baseline": cpu,
         "secondary": extra,
     }

@@ -30,18 +30,11 @@ struct Layout {
   size_t table, seq_first, W, U, Qn, P, Kn, gL, gE, T, dh, dD, dDT, total;
 };
 
-// Chunk slots: exact with a host copy of the boundaries, else T/64 + N.
-int64_t chunk_slots(const gdn_problem* p) {
-  if (p->cu_seqlens_host) {
-    int64_t nc = 0;
-    for (int n = 0; n < p->N; ++n) {
-      const int64_t L = (int64_t)p->cu_seqlens_host[n + 1] - p->cu_seqlens_host[n];
-      nc += (L + kChunk - 1) / kChunk;
-    }
-    return nc;
-  }
-  return (int64_t)p->T / kChunk + p->N;
-}
+// Chunk slots: the bound T/64 + N (sum of ceil(L_n / 64) <= T/64 + N), with or
+// without a host copy of the boundaries, so that every size and layout - in
+// particular the `saved` buffer a forward hands to a backward - depends on
+// (N, T, H, HV) only; slots past the pack's chunks exit at once.
+int64_t chunk_slots(const gdn_problem* p) { return (int64_t)p->T / kChunk + p->N; }
 
 gdn_status check_problem(const gdn_problem* p, int64_t* nc) {
   if (!p) return GDN_ERR_NULL;
@@ -257,6 +250,7 @@ static int chunk_fwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_
   if (!workspace || workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   StageClock clk{events, 0, s};
+  if (p->N == 0) return GDN_OK;  // no sequences: nothing to read or write
   if (p->T == 0 && !paged) {  // no tokens: the state passes through
     if (sr.hT)
       GDN_TRY(clk.run([&] {

@@ -183,8 +183,21 @@ def _check(status, where):
         raise GdnError(status, where)
 
 
+def _check_saved(problem, saved, where):
+    """The C calls take `saved` as a bare pointer; refuse a buffer smaller than
+    the layout the library reads and writes for this problem."""
+    if saved is None:
+        return
+    have = saved.numel() * saved.element_size()
+    need = gdn_chunk_saved_size(problem)
+    if have < need:
+        raise ValueError(f"{where}: saved holds {have} bytes, the problem needs {need} "
+                         "(gdn_chunk_saved_size)")
+
+
 def gdn_chunk_fwd(problem, q, k, v, g, beta, h0, o, hT, saved, workspace, stream=None):
     bf, f32 = torch.bfloat16, torch.float32
+    _check_saved(problem, saved, "gdn_chunk_fwd")
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = _lib.gdn_chunk_fwd(
         ctypes.byref(problem), _ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"),
@@ -197,6 +210,7 @@ def gdn_chunk_fwd(problem, q, k, v, g, beta, h0, o, hT, saved, workspace, stream
 def gdn_chunk_fwd_paged(problem, q, k, v, g, beta, state_pool, slots, ssm_state_indices,
                         has_initial_state, indices_host, o, saved, workspace, stream=None):
     bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    _check_saved(problem, saved, "gdn_chunk_fwd_paged")
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = _lib.gdn_chunk_fwd_paged(
         ctypes.byref(problem), _ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"),
@@ -217,6 +231,7 @@ def gdn_chunk_fwd_timed(problem, q, k, v, g, beta, h0, o, hT, saved, workspace, 
     """gdn_chunk_fwd recording events (a ctypes array of 2*GDN_MAX_STAGES hipEvent_t)
     around each stage. Returns the number of stages launched."""
     bf, f32 = torch.bfloat16, torch.float32
+    _check_saved(problem, saved, "gdn_chunk_fwd_timed")
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     n = ctypes.c_int(0)
     st = _lib.gdn_chunk_fwd_timed(
@@ -231,6 +246,7 @@ def gdn_chunk_fwd_timed(problem, q, k, v, g, beta, h0, o, hT, saved, workspace, 
 def gdn_chunk_bwd_timed(problem, q, k, v, g, beta, saved, dO, dhT, dq, dk, dv, dg, dbeta, dh0,
                         workspace, events, stream=None):
     bf, f32 = torch.bfloat16, torch.float32
+    _check_saved(problem, saved, "gdn_chunk_bwd_timed")
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     n = ctypes.c_int(0)
     st = _lib.gdn_chunk_bwd_timed(
@@ -247,6 +263,7 @@ def gdn_chunk_bwd_timed(problem, q, k, v, g, beta, saved, dO, dhT, dq, dk, dv, d
 def gdn_chunk_bwd(problem, q, k, v, g, beta, saved, dO, dhT, dq, dk, dv, dg, dbeta, dh0,
                   workspace, stream=None):
     bf, f32 = torch.bfloat16, torch.float32
+    _check_saved(problem, saved, "gdn_chunk_bwd")
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = _lib.gdn_chunk_bwd(
         ctypes.byref(problem), _ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"),

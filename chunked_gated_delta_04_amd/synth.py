@@ -180,6 +180,18 @@ WORKLOADS = {
                                         seed=BASE_SEED + 4),
     "paged_8x512_h8_hv16_pool64": dict(kind="paged", lens=[512] * 8, H=8, HV=16, slots=64,
                                        n_null=0, n_fresh=4, seed=BASE_SEED + 5),
+    # one long sequence (the long-context rows of the Cake page's tests)
+    "fwdbwd_1x65536_h16_hv32": dict(kind="fwdbwd", lens=[65536], H=16, HV=32, h0_std=0.1,
+                                    seed=BASE_SEED + 11),
+    "fwdbwd_1x131072_h16_hv32": dict(kind="fwdbwd", lens=[131072], H=16, HV=32, h0_std=0.1,
+                                     seed=BASE_SEED + 12),
+    # one GPU's share of the head-sharded layer at TP = 2 (8 key / 16 value heads)
+    "fwd_4x4096_h8_hv16": dict(kind="fwd", lens=[4096] * 4, H=8, HV=16, h0_std=0.1,
+                               seed=BASE_SEED + 21),
+    "fwd_varlen12_32768_h8_hv16": dict(kind="fwd", lens=None, total=32768, nseq=12, H=8, HV=16,
+                                       h0_std=None, seed=BASE_SEED + 22, lens_from=BASE_SEED + 2),
+    "fwdbwd_2x8192_h8_hv16": dict(kind="fwdbwd", lens=[8192] * 2, H=8, HV=16, h0_std=0.1,
+                                  seed=BASE_SEED + 23),
     # the short convolution over the q, k, v channels of the fwd+bwd pack
     # (2 x 128 x 16 key-head channels + 128 x 32 value-head channels), width 4
     "conv_2x8192_c8192_w4": dict(kind="conv", lens=[8192] * 2, C=8192, W=4, seed=BASE_SEED + 6),
@@ -190,7 +202,8 @@ def workload_lengths(name):
     w = WORKLOADS[name]
     if w.get("lens") is not None:
         return list(w["lens"])
-    gen = torch.Generator().manual_seed(w["seed"] + 1000)
+    # (the TP = 2 share of the varlen pack keeps the full pack's lengths)
+    gen = torch.Generator().manual_seed(w.get("lens_from", w["seed"]) + 1000)
     return varlen_lengths(w["total"], w["nseq"], 256, 8192, gen)
 
 

@@ -79,12 +79,10 @@ const char* gdn_status_string(int status);
  *                    [cu[n], cu[n+1]). Read by the kernels, never copied to
  *                    the host (no device-to-host synchronisation).
  *   cu_seqlens_host  optional host copy of the same boundaries. When given,
- *                    it is validated (0 = cu[0] <= ... <= cu[N] = T) and the
- *                    grids are sized exactly; when NULL the grids are sized
- *                    for the bound T/64 + N chunks and chunks that do not
- *                    exist exit at once. Device boundaries that are not
- *                    monotone or leave [0, T] are clamped, never
- *                    dereferenced out of range.
+ *                    it is validated (0 = cu[0] <= ... <= cu[N] = T) before
+ *                    any launch. Device boundaries that are not monotone or
+ *                    leave [0, T] are clamped, never dereferenced out of
+ *                    range.
  * Chunks restart at every sequence start; the last chunk of a sequence may be
  * shorter than 64. Chunks are numbered sequence by sequence in token order;
  * chunk c of the pack is the slot index used by the saved buffer. */
@@ -95,8 +93,11 @@ typedef struct {
   const int32_t* cu_seqlens_host;
 } gdn_problem;
 
-/* Number of chunk slots the chunk calls index: exact sum of ceil(L_n / 64)
- * when cu_seqlens_host is given, else the bound T/64 + N. 0 on a bad problem. */
+/* Number of chunk slots the chunk calls index: the bound T/64 + N on the sum
+ * of ceil(L_n / 64), whether or not cu_seqlens_host is given, so that every
+ * size query below depends on (N, T, H, HV) only and a `saved` buffer written
+ * by a forward always has the layout its backward expects. Slots past the
+ * pack's chunks are skipped by the kernels. 0 on a bad problem. */
 int64_t gdn_num_chunks(const gdn_problem* p);
 
 /* Bytes of the `saved` buffer that gdn_chunk_fwd fills for gdn_chunk_bwd

@@ -81,12 +81,14 @@ def bwd(G, p, ws_bytes=1 << 40, **over):
 
 def test_chunk_counts_and_sizes(G):
     p = problem(G)
-    assert G.gdn_num_chunks(p) == 2 + 1       # ceil(70/64) + ceil(60/64)
+    # the slot count is the bound T/64 + N (>= ceil(70/64) + ceil(60/64) = 3 chunks),
+    # with or without the host copy of the boundaries
+    assert G.gdn_num_chunks(p) == 130 // 64 + 2
     p2 = problem(G, cu_host=None)
     assert G.gdn_num_chunks(p2) == 130 // 64 + 2
     s = G.gdn_chunk_saved_size(p)
-    blocks = 4 * 3  # value heads x chunk slots
-    kblocks = 2 * 3  # key heads x chunk slots
+    blocks = 4 * 4  # value heads x chunk slots
+    kblocks = 2 * 4  # key heads x chunk slots
     # per value-head block: the bf16 start state and D, the backward's W^T, P^T, T, T^T
     # in bf16, e^gamma_L, 128 per-token gate factors and 128 per-token gamma, beta in
     # fp32 (the factors start 16-byte aligned); per key-head block: Q~^T and K^ in bf16
@@ -97,6 +99,26 @@ def test_chunk_counts_and_sizes(G):
     assert G.gdn_chunk_fwd_workspace_size(p) == G.gdn_chunk_fwd_workspace_size(p)
     bad = problem(G, K=64)
     assert G.gdn_num_chunks(bad) == 0 and G.gdn_chunk_fwd_workspace_size(bad) == 0
+
+
+@pytest.mark.parametrize("cu", [(0, 70, 130), (0, 64, 130), (0, 0, 130), (0, 130, 130)])
+def test_saved_layout_does_not_depend_on_the_host_copy(G, cu):
+    """A forward given the host copy of the boundaries and a backward given only
+    the device copy (or the reverse) must agree on the saved buffer's layout:
+    every size query depends on (N, T, H, HV) alone."""
+    a, b = problem(G, cu_host=cu), problem(G, cu_host=None)
+    for q in ("gdn_num_chunks", "gdn_chunk_saved_size", "gdn_chunk_fwd_workspace_size",
+              "gdn_chunk_bwd_workspace_size", "gdn_chunk_bwd_recompute_workspace_size"):
+        assert getattr(G, q)(a) == getattr(G, q)(b), q
+
+
+def test_binding_refuses_a_short_saved_buffer(G):
+    import torch
+    p = problem(G)
+    short = torch.empty(G.gdn_chunk_saved_size(p) - 16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="saved"):
+        G.gdn_chunk_bwd(p, None, None, None, None, None, short, None, None, None, None, None,
+                        None, None, None, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -201,6 +223,15 @@ def test_paged_forward_rejects_bad_arguments(G):
     assert paged(G, p, pool=FAKE_MISALIGNED) == 8
     assert paged(G, p, ws=None) == 6
     assert paged(G, p, ws_bytes=G.gdn_chunk_fwd_workspace_size(p) - 1) == 6
+
+
+def test_paged_forward_with_no_sequences_is_a_no_op(G):
+    """N = 0, T = 0: nothing to read or write, OK before any launch (as for
+    gdn_chunk_fwd, the transition and the decode step)."""
+    p = problem(G, N=0, T=0, cu_host=(0,))
+    assert paged(G, p, q=None, k=None, v=None, g=None, beta=None, o=None, pool=None,
+                 idx=None) == 0
+    assert fwd(G, p, q=None, k=None, v=None, g=None, beta=None, o=None) == 0
 
 
 def test_paged_forward_index_rules_on_the_host_copy(G):

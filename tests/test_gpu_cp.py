@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from chunked_gated_delta_04_amd import synth
-from tests.gpu_helpers import assert_bar, f64, oracle_backward, oracle_forward, to_dev
+from tests.gpu_helpers import assert_bar, assert_dg_bar, f64, oracle_backward, oracle_forward, to_dev
 from oracle import recurrence as R
 
 pytestmark = pytest.mark.gpu
@@ -188,6 +188,7 @@ def test_recomputing_backward_equals_the_saved_one_bitwise(h0):
     ref = oracle_backward(inp, dhT=dhT)
     for name in ("dq", "dk", "dv", "dbeta", "dh0"):
         assert_bar(name, f64(b[name]), ref[name])
+    assert_dg_bar("dg", f64(b["dg"]), ref["dg"])
 
 
 def test_recomputing_backward_full_size_bitwise():

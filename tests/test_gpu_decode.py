@@ -40,7 +40,7 @@ def test_decode_small_matches_oracle_and_skip_rules(contract):
     o = _run(inp, pool)
     o_ref, pool_ref = _oracle(inp, f64(pool0))
     o, pool = o.cpu(), pool.cpu()
-    assert_bar("o", f64(o), o_ref)
+    assert_bar("o", f64(o), o_ref, atol=contract["decode_out_bar_fp32_state"]["value"], rtol=0.0)
     assert np.abs(f64(pool) - pool_ref).max() <= contract["decode_state_bar_fp32_state"]["value"]
     skipped = (idx <= 0).nonzero().flatten().tolist()
     for n in skipped:
@@ -60,7 +60,7 @@ def test_decode_full_workload(contract):
     o = _run(inp, pool)
     o_ref, pool_ref = _oracle(inp, f64(pool0))
     o, pool = o.cpu(), pool.cpu()
-    assert_bar("o", f64(o), o_ref)
+    assert_bar("o", f64(o), o_ref, atol=contract["decode_out_bar_fp32_state"]["value"], rtol=0.0)
     dstate = float(np.abs(f64(pool) - pool_ref).max())
     assert dstate <= contract["decode_state_bar_fp32_state"]["value"], dstate
     idx = inp["ssm_state_indices"]
@@ -128,7 +128,9 @@ def test_decode_steps_track_the_chunk_forward(contract):
                                     torch.tensor(g, dtype=torch.float32).cuda(),
                                     torch.tensor(beta, dtype=torch.float32).cuda(), cu.cuda(),
                                     cu_seqlens_host=cu)
+        # the upper end of the pages' measured 0.5-1 % band
+        bar = max(contract["decode_vs_chunk_rel"]["value"])
         rel = float((o_dec - o_ch.float()).abs().max() / o_ch.float().abs().max())
-        assert rel < 0.02, (T, rel)
+        assert rel < bar, (T, rel)
         srel = float((pool[1] - hT[0]).abs().max() / hT[0].abs().max())
-        assert srel < 0.02, (T, srel)
+        assert srel < bar, (T, srel)
