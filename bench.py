@@ -577,8 +577,10 @@ def setup_step(dev):
                                      None, dq, dk, dv, dg, dbeta, dh0, wsb, ev_b, stream)
         return nf, nb
 
-    meta = dict(T=T, H=H, HV=HV, N=N, n_chunks=n_chunks, stream=stream,
+    # `host` must outlive the problem descriptor, which points at it
+    meta = dict(T=T, H=H, HV=HV, N=N, n_chunks=n_chunks, stream=stream, host=host,
                 saved_bytes=saved.numel(), workspace_bytes=wsf.numel() + wsb.numel())
+    step.keep = (host, p)
     return meta, step
 
 

@@ -3,6 +3,7 @@ fp64 oracle, plus the bitwise invariants the method implies."""
 import os
 import sys
 
+import numpy as np
 import pytest
 import torch
 
@@ -150,7 +151,24 @@ def test_backward_with_all_zero_q_and_k_rows_matches_oracle():
     o_ref, hT_ref = oracle_forward(inp)
     assert_bar("o", f64(o), o_ref)
     assert_bar("hT", f64(hT), hT_ref)
-    _check_grads(grads, oracle_backward(inp), "zero rows")
+    ref = oracle_backward(inp)
+    for name in ("dv", "dbeta", "dh0"):
+        assert_bar(f"zero rows {name}", f64(grads[name]), ref[name])
+    assert_dg_bar("zero rows dg", f64(grads["dg"]), ref["dg"])
+    # dq, dk: a zero row's norm is sqrt(1e-6) = 1e-3, and the norm backward
+    # multiplies that row's gradient by its inverse, 1e3 - the fp32-accumulated
+    # bf16-operand error of the normalised gradient with it. Such rows are compared
+    # in the normalised coordinates (both sides times the row's norm, which undoes
+    # exactly that factor); every other row against the plain bar.
+    for name, x in (("dq", "q"), ("dk", "k")):
+        xv = f64(inp[x])
+        norm = np.sqrt((xv * xv).sum(-1, keepdims=True) + 1e-6)
+        zero = (xv == 0).all(-1)
+        got, want = f64(grads[name]), ref[name]
+        assert zero.sum() > 0
+        assert_bar(f"zero rows {name} (nonzero rows)", got[~zero], want[~zero])
+        assert_bar(f"zero rows {name} (zero rows, times the row norm)",
+                   (got * norm)[zero], (want * norm)[zero])
 
 
 # ------------------------------------------------------------------ edge cases
