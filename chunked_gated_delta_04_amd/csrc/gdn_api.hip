@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "gdn.h"
@@ -174,6 +175,8 @@ GDN_API const char* gdn_status_string(int status) {
     case GDN_ERR_WORKSPACE: return "workspace missing or smaller than the size query";
     case GDN_ERR_HIP: return "a HIP launch failed";
     case GDN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case GDN_ERR_SCRATCH:
+      return "the problem needs more scratch than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }
@@ -233,6 +236,32 @@ struct StageClock {
   }
 };
 
+// Argument checks of the forward (everything but the workspace).
+static gdn_status check_fwd_args(const gdn_problem* p, const uint16_t* q, const uint16_t* k,
+                                 const uint16_t* v, const float* g, const float* beta,
+                                 const StateRef& sr, const uint16_t* o, const uint16_t* saved,
+                                 int64_t* NC) {
+  gdn_status st = check_problem(p, NC);
+  if (st != GDN_OK) return st;
+  if (p->T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(sr.h0) ||
+      !aligned16(sr.hT) || !aligned16(saved))
+    return GDN_ERR_ALIGN;
+  return GDN_OK;
+}
+
+// Argument checks of the paged forward beyond those of the forward.
+static gdn_status check_paged_args(const gdn_problem* p, float* state_pool, int32_t slots,
+                                   const int32_t* ssm_state_indices,
+                                   const int32_t* indices_host) {
+  const gdn_status ps = check_problem(p, nullptr);
+  if (ps != GDN_OK) return ps;
+  if (slots < 0) return GDN_ERR_SHAPE;
+  if (p->N > 0 && (!state_pool || !ssm_state_indices)) return GDN_ERR_NULL;
+  if (check_indices_host(p->N, slots, indices_host) != GDN_OK) return GDN_ERR_INDEX;
+  return GDN_OK;
+}
+
 static int chunk_fwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_t* k,
                           const uint16_t* v, const float* g, const float* beta,
                           const StateRef& sr, bool paged, uint16_t* o, uint16_t* saved,
@@ -240,12 +269,9 @@ static int chunk_fwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_
                           void* const* events, int* n_stages) {
   if (n_stages) *n_stages = 0;
   int64_t NC = 0;
-  gdn_status st = check_problem(p, &NC);
+  gdn_status st = check_fwd_args(p, q, k, v, g, beta, sr, o, saved, &NC);
   if (st != GDN_OK) return st;
-  if (p->T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(sr.h0) ||
-      !aligned16(sr.hT) || !aligned16(saved) || !aligned16(workspace))
-    return GDN_ERR_ALIGN;
+  if (!aligned16(workspace)) return GDN_ERR_ALIGN;
   const Layout L = make_layout(p, NC, false);
   if (!workspace || workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -296,14 +322,68 @@ GDN_API int gdn_chunk_fwd_paged(const gdn_problem* p, const uint16_t* q, const u
                                 const int32_t* has_initial_state, const int32_t* indices_host,
                                 uint16_t* o, uint16_t* saved, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-  const gdn_status ps = check_problem(p, nullptr);
+  const gdn_status ps = check_paged_args(p, state_pool, slots, ssm_state_indices, indices_host);
   if (ps != GDN_OK) return ps;
-  if (slots < 0) return GDN_ERR_SHAPE;
-  if (p->N > 0 && (!state_pool || !ssm_state_indices)) return GDN_ERR_NULL;
-  if (check_indices_host(p->N, slots, indices_host) != GDN_OK) return GDN_ERR_INDEX;
   const StateRef sr{state_pool, state_pool, ssm_state_indices, has_initial_state, slots};
   return chunk_fwd_impl(p, q, k, v, g, beta, sr, true, o, saved, workspace, workspace_bytes,
                         stream, nullptr, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// The allocation-free paged prefill: the same kernels with their workspace in
+// a file-scope device array instead of a caller's buffer. Each GPU holds its
+// own copy of the array from the library's first use on it until the process
+// ends. In host code `scratch` names a host-side stand-in, not device memory:
+// the device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address is handed to kernels.
+namespace {
+constexpr size_t kScratchBytes = (size_t)96 << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of this device's scratch array, looked up on first use.
+static hipError_t scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+GDN_API size_t gdn_chunk_fwd_paged_noalloc_max_bytes(void) { return kScratchBytes; }
+
+GDN_API int gdn_chunk_fwd_paged_noalloc(const gdn_problem* p, const uint16_t* q,
+                                        const uint16_t* k, const uint16_t* v, const float* g,
+                                        const float* beta, float* state_pool, int32_t slots,
+                                        const int32_t* ssm_state_indices,
+                                        const int32_t* has_initial_state,
+                                        const int32_t* indices_host, uint16_t* o,
+                                        uint16_t* saved, void* stream) {
+  // every argument check first, so that an argument error touches no device
+  const gdn_status ps = check_paged_args(p, state_pool, slots, ssm_state_indices, indices_host);
+  if (ps != GDN_OK) return ps;
+  int64_t NC = 0;
+  const StateRef sr{state_pool, state_pool, ssm_state_indices, has_initial_state, slots};
+  const gdn_status fs = check_fwd_args(p, q, k, v, g, beta, sr, o, saved, &NC);
+  if (fs != GDN_OK) return fs;
+  if (make_layout(p, NC, false).total > kScratchBytes) return GDN_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (scratch_for_current_device(&ws) != hipSuccess) return GDN_ERR_HIP;
+  return gdn_chunk_fwd_paged(p, q, k, v, g, beta, state_pool, slots, ssm_state_indices,
+                             has_initial_state, indices_host, o, saved, ws, kScratchBytes, stream);
 }
 
 GDN_API int gdn_chunk_fwd_timed(const gdn_problem* p, const uint16_t* q, const uint16_t* k,

@@ -25,7 +25,7 @@ GDN_OK = 0
 STATUS_NAMES = {
     0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
     4: "GDN_ERR_SEQLENS", 5: "GDN_ERR_INDEX", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP",
-    8: "GDN_ERR_ALIGN",
+    8: "GDN_ERR_ALIGN", 9: "GDN_ERR_SCRATCH",
 }
 EXPORTED = (
     "gdn_status_string", "gdn_num_chunks", "gdn_chunk_saved_size",
@@ -36,6 +36,7 @@ EXPORTED = (
     "gdn_conv_fwd", "gdn_conv_fwd_paged", "gdn_conv_bwd", "gdn_conv_bwd_workspace_size",
     "gdn_conv_update",
     "gdn_chunk_fwd_timed", "gdn_chunk_bwd_timed", "gdn_stage_name",
+    "gdn_chunk_fwd_paged_noalloc", "gdn_chunk_fwd_paged_noalloc_max_bytes",
 )
 GDN_MAX_STAGES = 8
 
@@ -81,6 +82,10 @@ _lib.gdn_chunk_fwd.restype = ctypes.c_int
 _lib.gdn_chunk_fwd.argtypes = [_P] + [_vp] * 10 + [_sz, _vp]
 _lib.gdn_chunk_fwd_paged.restype = ctypes.c_int
 _lib.gdn_chunk_fwd_paged.argtypes = [_P] + [_vp] * 6 + [_i32] + [_vp] * 6 + [_sz, _vp]
+_lib.gdn_chunk_fwd_paged_noalloc.restype = ctypes.c_int
+_lib.gdn_chunk_fwd_paged_noalloc.argtypes = [_P] + [_vp] * 6 + [_i32] + [_vp] * 6
+_lib.gdn_chunk_fwd_paged_noalloc_max_bytes.restype = _sz
+_lib.gdn_chunk_fwd_paged_noalloc_max_bytes.argtypes = []
 _lib.gdn_chunk_bwd.restype = ctypes.c_int
 _lib.gdn_chunk_bwd.argtypes = [_P] + [_vp] * 15 + [_sz, _vp]
 _lib.gdn_chunk_bwd_recompute.restype = ctypes.c_int
@@ -220,6 +225,24 @@ def gdn_chunk_fwd_paged(problem, q, k, v, g, beta, state_pool, slots, ssm_state_
         _host_ptr(indices_host, "indices_host"), _ptr(o, bf, "o"), _ptr(saved, None, "saved"),
         _ptr(workspace, None, "workspace"), ws_bytes, _stream(stream))
     _check(st, "gdn_chunk_fwd_paged")
+
+
+def gdn_chunk_fwd_paged_noalloc_max_bytes():
+    return int(_lib.gdn_chunk_fwd_paged_noalloc_max_bytes())
+
+
+def gdn_chunk_fwd_paged_noalloc(problem, q, k, v, g, beta, state_pool, slots, ssm_state_indices,
+                                has_initial_state, indices_host, o, saved, stream=None):
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    _check_saved(problem, saved, "gdn_chunk_fwd_paged_noalloc")
+    st = _lib.gdn_chunk_fwd_paged_noalloc(
+        ctypes.byref(problem), _ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"),
+        _ptr(g, f32, "g"), _ptr(beta, f32, "beta"), _ptr(state_pool, f32, "state_pool"),
+        int(slots), _ptr(ssm_state_indices, i32, "ssm_state_indices"),
+        _ptr(has_initial_state, i32, "has_initial_state"),
+        _host_ptr(indices_host, "indices_host"), _ptr(o, bf, "o"), _ptr(saved, None, "saved"),
+        _stream(stream))
+    _check(st, "gdn_chunk_fwd_paged_noalloc")
 
 
 def gdn_stage_name(op, stage):

@@ -62,7 +62,8 @@ typedef enum {
   GDN_ERR_INDEX = 5,       /* an active state-pool index >= slots, or repeated   */
   GDN_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the size query      */
   GDN_ERR_HIP = 7,         /* a HIP launch failed                                */
-  GDN_ERR_ALIGN = 8        /* a tensor or workspace pointer not 16-byte aligned  */
+  GDN_ERR_ALIGN = 8,       /* a tensor or workspace pointer not 16-byte aligned  */
+  GDN_ERR_SCRATCH = 9      /* too large for the allocation-free entry point      */
 } gdn_status;
 
 /* Human-readable text of a status code; never NULL. */
@@ -180,6 +181,31 @@ int gdn_chunk_fwd_paged(const gdn_problem* p,
                         const int32_t* indices_host,
                         uint16_t* o, uint16_t* saved,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* The paged prefill without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Same arguments, results and errors as
+ * gdn_chunk_fwd_paged minus `workspace` / `workspace_bytes`: the kernels use a
+ * scratch array inside the library instead, of
+ * gdn_chunk_fwd_paged_noalloc_max_bytes() bytes (96 MiB) per GPU, held from
+ * the first call on a GPU until the process ends. A problem whose
+ * gdn_chunk_fwd_workspace_size exceeds that returns GDN_ERR_SCRATCH before any
+ * launch (for example 16 value / 8 key heads fit 8 x 512 tokens; the limit
+ * scales with (T / 64 + N) x (HV x 40.5 KiB + H x 32 KiB)). The call allocates
+ * nothing (no hipMalloc, no allocating library routine); its first call on a
+ * GPU looks the array's device address up once. Every call on one GPU shares
+ * that GPU's array: calls that may overlap on one GPU (different streams,
+ * different host threads) race and must be serialised by the caller. Nothing
+ * in the array needs to start at zero. */
+size_t gdn_chunk_fwd_paged_noalloc_max_bytes(void);
+int gdn_chunk_fwd_paged_noalloc(const gdn_problem* p,
+                                const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const float* g, const float* beta,
+                                float* state_pool, int32_t slots,
+                                const int32_t* ssm_state_indices,
+                                const int32_t* has_initial_state,
+                                const int32_t* indices_host,
+                                uint16_t* o, uint16_t* saved, void* stream);
 
 /* Chunked backward of gdn_chunk_fwd (same p, q, k, v, g, beta).
  *   saved     as written by gdn_chunk_fwd for the same problem and inputs

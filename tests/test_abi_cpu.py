@@ -359,3 +359,34 @@ def test_conv_paged_and_update_index_rules(G):
     assert upd([1, 0, 0], N=0) == 0
     for name in ("x", "w", "pool", "idx", "y"):
         assert upd([1, 0, 2], **{name: None}) == 1, name
+
+
+def test_allocation_free_paged_prefill_checks_before_touching_the_device(G):
+    """Argument errors and a problem past the scratch array are returned before
+    the entry point looks up its device array (so nothing here needs a GPU)."""
+    assert G.gdn_chunk_fwd_paged_noalloc_max_bytes() == 96 << 20
+
+    def na(p, slots=8, host=None, **over):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, pool=FAKE, idx=FAKE, init=None,
+                 o=FAKE, saved=None)
+        a.update(over)
+        keep = None
+        hp = None
+        if host is not None:
+            keep = (ctypes.c_int32 * len(host))(*host)
+            hp = ctypes.cast(keep, ctypes.c_void_p)
+        return G._lib.gdn_chunk_fwd_paged_noalloc(
+            ctypes.byref(p), a["q"], a["k"], a["v"], a["g"], a["beta"], a["pool"], slots,
+            a["idx"], a["init"], hp, a["o"], a["saved"], None)
+
+    p = problem(G)
+    assert na(problem(G, K=64)) == 3
+    assert na(p, slots=-1) == 2
+    for name in ("pool", "idx", "q", "o"):
+        assert na(p, **{name: None}) == 1, name
+    assert na(p, host=[1, 8]) == 5
+    assert na(p, q=FAKE_MISALIGNED) == 8
+    T = 64 * 1024
+    big = problem(G, N=2, T=T, H=16, HV=32, cu_host=(0, T // 2, T))
+    assert G.gdn_chunk_fwd_workspace_size(big) > G.gdn_chunk_fwd_paged_noalloc_max_bytes()
+    assert na(big) == 9
