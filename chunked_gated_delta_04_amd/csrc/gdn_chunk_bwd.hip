@@ -110,6 +110,7 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
     float gl;
     float eg;    // e^gamma of token ot (the dO row this thread stages)
     float4 ebw;  // e^(gamma_L - gamma) of tokens 16 wave + 4 kq .. + 3 (dD rows)
+    uint32_t pf;  // L2 warm-up word of a later chunk (see touch_line)
   };
   const int ot = tid / SPT, osg = tid % SPT;  // dO segment of this thread (ot < 64 holds one)
   // chunk bounds from the sequence's bounds (consecutive 64-token chunks)
@@ -120,7 +121,34 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
     bos = first.t0;
     eos = lastc.t0 + lastc.len;
   }
-  auto load_ops = [&](int c, Ops& x) {
+  // This workgroup's share of a chunk's operand lines for the L2 warm-up: the
+  // value head's W^T, P^T, gate-factor and dO lines (324) split over its value
+  // blocks, the key head's Q~^T and K^ lines (256) over the workgroups of all its
+  // value heads. Lanes past the share touch a line of the share again; dO rows
+  // past the chunk's end touch its last row.
+  const int vlines = (324 + NVB - 1) / NVB;
+  const int kshares = NVB * prep.G, kpos = (hv % prep.G) * NVB + vb;
+  const int klines = (256 + kshares - 1) / kshares;
+  auto warm_line = [&](int c) -> const void* {
+    const size_t blk = (size_t)hv * NC + c;
+    const size_t kblk = (size_t)(hv / prep.G) * NC + c;
+    const int i = tid < vlines + klines ? tid : tid % vlines;
+    if (i < vlines) {
+      const int l = min(vb * vlines + i, 323);
+      if (l < 128) return prep.W + blk * 8192 + l * kLineElems16;
+      if (l < 192) return prep.P + blk * 4096 + (l - 128) * kLineElems16;
+      if (l < 196) return prep.gE + blk * kGates + (l - 192) * kLineElems32;
+      const int t0 = bos + (c - c_begin) * kChunk;
+      const int r = min((l - 196) >> 1, eos - t0 - 1);
+      return dO + ((size_t)(t0 + r) * HV + hv) * kHead + ((l - 196) & 1) * kLineElems16;
+    }
+    const int l = min(kpos * klines + (i - vlines), 255);
+    if (l < 128) return prep.Qn + kblk * 8192 + l * kLineElems16;
+    return prep.Kn + kblk * 8192 + (l - 128) * kLineElems16;
+  };
+  uint32_t sink = 0;
+  // pc: the chunk whose lines the set's L2 warm-up word touches
+  auto load_ops = [&](int c, Ops& x, int pc) {
     const size_t blk = (size_t)hv * NC + c;
     const size_t kblk = (size_t)(hv / prep.G) * NC + c;
     const uint16_t* PTb = prep.P + blk * 4096;    // P^T: row i holds P[j][i], j >= i
@@ -150,6 +178,7 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
         const_cast<uint16_t*>(dO) + ((size_t)t0 * HV + hv) * kHead, 0, len * HV * kHead * 2,
         kBufferWord3);
     x.dO = load_b128(rng, (ot * HV * kHead + v0 + 8 * osg) * 2);
+    x.pf = touch_line(warm_line(pc));
   };
 
   auto step = [&](int c, const Ops& cur) {
@@ -272,16 +301,20 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
     // re-reads the first one
     const int first = c_begin;
     Ops A, B;
-    load_ops(c_end - 1, A);
+    B.pf = 0;
+    load_ops(c_end - 1, A, max(c_end - 3, first));
     for (int c = c_end - 1;; c -= 2) {
-      load_ops(max(c - 1, first), B);
+      sink ^= B.pf;  // requested two sets ago
+      load_ops(max(c - 1, first), B, max(c - 3, first));
       step(c, A);
       if (c - 1 < first) break;
-      load_ops(max(c - 2, first), A);
+      sink ^= A.pf;
+      load_ops(max(c - 2, first), A, max(c - 4, first));
       step(c - 1, B);
       if (c - 2 < first) break;
     }
   }
+  consume(sink);
 
   if (dh0) {
 #pragma unroll

@@ -113,8 +113,37 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     float gl;
     float eg;    // e^gamma of token 16 wave + li (output rows)
     float4 ebw;  // e^(gamma_L - gamma) of tokens 16 wave + 4 kq .. + 3 (D rows)
+    uint32_t pf;  // L2 warm-up word of a later chunk (see touch_line)
   };
-  auto load_ops = [&](int c, Ops& x) {
+  // This workgroup's share of a chunk's operand lines for the L2 warm-up: the
+  // value head's W, U^T, P and gate-factor lines (324) split over its value
+  // blocks, the key head's Q~ and K^T lines (256) over the workgroups of all its
+  // value heads. Lanes past the share touch a line of the share again.
+  const int vshare = (kTrans ? 2 * NVB : NVB);
+  const int vpos = kTrans ? slot % NVBL : vb;
+  const int vlines = (324 + vshare - 1) / vshare;
+  const int kshares = NVBL * prep.G, kpos = (hv % prep.G) * NVBL + vpos;
+  const int klines = (256 + kshares - 1) / kshares;
+  auto warm_line = [&](int c) -> const void* {
+    const size_t blk = (size_t)hv * NC + c;
+    const size_t kblk = (size_t)(hv / prep.G) * NC + c;
+    int i = tid < vlines + klines ? tid : tid % vlines;
+    if (i < vlines) {
+      const int l = min(vpos * vlines + i, 323);
+      if (l < 128) return prep.W + blk * 8192 + l * kLineElems16;
+      if (l < 256) return prep.U + blk * 8192 + (l - 128) * kLineElems16;
+      if (l < 320) return kOut ? (const void*)(prep.P + blk * 4096 + (l - 256) * kLineElems16)
+                               : (const void*)(prep.W + blk * 8192);
+      return prep.gE + blk * kGates + (l - 320) * kLineElems32;
+    }
+    const int l = min(kpos * klines + (i - vlines), 255);
+    if (l < 128) return kOut ? (const void*)(prep.Qn + kblk * 8192 + l * kLineElems16)
+                             : (const void*)(prep.Kn + kblk * 8192);
+    return prep.Kn + kblk * 8192 + (l - 128) * kLineElems16;
+  };
+  uint32_t sink = 0;
+  // pc: the chunk whose lines the set's L2 warm-up word touches
+  auto load_ops = [&](int c, Ops& x, int pc) {
     const size_t blk = (size_t)hv * NC + c;
     const size_t kblk = (size_t)(hv / prep.G) * NC + c;
     const uint16_t* Wb = prep.W + blk * 8192;
@@ -143,6 +172,7 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     const float* ge = prep.gE + blk * kGates;
     if constexpr (kOut) x.eg = ge[16 * wave + li];
     x.ebw = *reinterpret_cast<const float4*>(ge + kChunk + 16 * wave + 4 * kq);
+    x.pf = touch_line(warm_line(pc));
   };
 
   // The chunks of one sequence are consecutive 64-token pieces, so a chunk's
@@ -159,6 +189,8 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
   auto step = [&](int c, const Ops& cur, int cn, Ops& nxt) {
     const int t0 = bos + (c - c_begin) * kChunk;
     const int len = min(kChunk, eos - t0);
+    // the warm-up word nxt carries was requested two steps ago
+    sink ^= nxt.pf;
     // 1. chunk-start state -> LDS (bf16)
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
@@ -171,8 +203,9 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
       }
     __syncthreads();
     // the next set's requests, issued by all waves together right after the
-    // barrier (waves that issue them together share the lines they fetch)
-    load_ops(cn, nxt);
+    // barrier (waves that issue them together share the lines they fetch),
+    // and the L2 warm-up of the chunk three steps ahead
+    load_ops(cn, nxt, min(cn + 2, c_end - 1));
     uint16_t* sv = saved + blk_saved(c, hv, HV);
     if constexpr (kSave) {
       // h = S^T as [v / 32][v % 32 / 8][k][v % 8]: chunk e = 64 q + lane holds
@@ -272,7 +305,8 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     // per chain keeps the memory operations of every chunk the same
     const int last = c_end - 1;
     Ops A, B;
-    load_ops(c_begin, A);
+    B.pf = 0;
+    load_ops(c_begin, A, min(c_begin + 2, last));
     for (int c = c_begin;; c += 2) {
       step(c, A, min(c + 1, last), B);
       if (c + 1 > last) break;
@@ -281,6 +315,7 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     }
   }
 
+  consume(sink);
   if constexpr (kTrans) hT = mblk ? st.M : st.hT;
   if (hT) {
 #pragma unroll

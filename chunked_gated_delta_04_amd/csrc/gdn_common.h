@@ -327,6 +327,22 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// L2 warm-up for the sequential scans. A chain's chunk operands come from HBM
+// when they are first requested, a latency of the order of a whole chunk step
+// under load; requesting them one chunk ahead therefore still stalls every
+// step. Each workgroup instead touches its share of the operand lines of the
+// chunk three steps ahead - one 4-byte load per 128-byte line and lane - so
+// that the real requests one chunk ahead hit L2. The loaded words are folded
+// into a sink two steps after they were requested (by then they have arrived,
+// as the counter of outstanding loads drains in order, so the fold waits for
+// nothing) and the sink is consumed once at the end of the kernel.
+constexpr int kLineElems16 = 64;  // bf16 elements per 128-byte line
+constexpr int kLineElems32 = 32;  // fp32 elements per 128-byte line
+__device__ __forceinline__ uint32_t touch_line(const void* p) {
+  return *reinterpret_cast<const uint32_t*>(p);
+}
+__device__ __forceinline__ void consume(uint32_t sink) { asm volatile("" ::"v"(sink)); }
+
 // One chunk of the packed token axis: sequence, first token, length, and
 // the chunk's position inside its sequence. seq < 0 marks an unused slot.
 struct ChunkInfo {
