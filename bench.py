@@ -346,16 +346,12 @@ def fwdbwd_step_ms(h, stream, name, steps, warmup):
     return T, ms
 
 
-def secondary(h, stream, steps, warmup):
-    """Forward-only throughput on the 4 x 4096 and the 12-sequence varlen packs, the
-    decode step against the HBM roofline, the paged prefill, the same packs at one
-    GPU's share of a TP = 2 head split (8 key / 16 value heads), and one long
-    sequence of 65,536 and 131,072 tokens."""
+def forward_packs(h, stream, names, steps, warmup):
+    """Forward-only throughput (nothing saved for a backward) on varlen packs."""
     import torch
     from chunked_gated_delta_04_amd import gdn, synth
     out = {}
-    for name in ("fwd_4x4096_h16_hv32", "fwd_varlen12_32768_h16_hv32",
-                 "fwd_4x4096_h8_hv16", "fwd_varlen12_32768_h8_hv16"):
+    for name in names:
         inp = synth.workload_inputs(name)
         d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
         T, H, _ = inp["q"].shape
@@ -370,6 +366,14 @@ def secondary(h, stream, steps, warmup):
             steps, warmup)
         out[name] = {"ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1)}
         del d, o, hT, ws
+    return out
+
+
+def decode_step(h, stream, steps, warmup):
+    """The decode step (256 rows, 16 of them on the null block, pool of 512
+    states) against the HBM roofline."""
+    import torch
+    from chunked_gated_delta_04_amd import gdn, synth
     name = "decode_256_pool512_h16_hv32"
     inp = synth.workload_inputs(name)
     d = {k: v.cuda() for k, v in inp.items()}
@@ -388,17 +392,40 @@ def secondary(h, stream, steps, warmup):
     io = active * (2 * H * 128 * 2 + HV * 128 * 2 + 2 * HV * 2) + N * HV * 128 * 2 + N * 4 + HV * 8
     bytes_ = state + io
     gbs = bytes_ / (ms * 1e-3) / 1e9
-    out[name] = {"ms": round(ms, 4), "rows_per_s": round(N / (ms * 1e-3), 1),
-                 "algorithmic_bytes": bytes_, "achieved_GBps": round(gbs, 1),
-                 "hbm_frac": round(gbs * 1e9 / PEAK_HBM, 4)}
-    out.update(paged_prefill(h, stream, steps, warmup))
-    out.update(recompute_and_transition(h, stream, steps, warmup))
-    out.update(short_conv(h, stream, steps, warmup))
+    return {name: {"ms": round(ms, 4), "rows_per_s": round(N / (ms * 1e-3), 1),
+                   "algorithmic_bytes": bytes_, "achieved_GBps": round(gbs, 1),
+                   "hbm_frac": round(gbs * 1e9 / PEAK_HBM, 4)}}
+
+
+FWD_PACKS = ("fwd_4x4096_h16_hv32", "fwd_varlen12_32768_h16_hv32")
+FWD_PACKS_TP2 = ("fwd_4x4096_h8_hv16", "fwd_varlen12_32768_h8_hv16")
+
+
+def long_and_tp2_steps(h, stream, steps, warmup):
+    """The fwd+bwd step at one GPU's share of a TP = 2 head split (8 key / 16
+    value heads) and on one long sequence of 65,536 and 131,072 tokens."""
+    import torch
+    out = {}
     for name, reps in (("fwdbwd_2x8192_h8_hv16", steps), ("fwdbwd_1x65536_h16_hv32", steps),
                        ("fwdbwd_1x131072_h16_hv32", max(3, steps // 4))):
         T, ms = fwdbwd_step_ms(h, stream, name, reps, min(warmup, 2))
         out[name] = {"ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1)}
         torch.cuda.empty_cache()
+    return out
+
+
+def secondary(h, stream, steps, warmup):
+    """Forward-only throughput on the 4 x 4096 and the 12-sequence varlen packs, the
+    decode step against the HBM roofline, the paged prefill, the recomputing
+    backward and the local transitions, the short convolution, the same packs
+    at one GPU's share of a TP = 2 head split (8 key / 16 value heads), and one
+    long sequence of 65,536 and 131,072 tokens."""
+    out = forward_packs(h, stream, FWD_PACKS + FWD_PACKS_TP2, steps, warmup)
+    out.update(decode_step(h, stream, steps, warmup))
+    out.update(paged_prefill(h, stream, steps, warmup))
+    out.update(recompute_and_transition(h, stream, steps, warmup))
+    out.update(short_conv(h, stream, steps, warmup))
+    out.update(long_and_tp2_steps(h, stream, steps, warmup))
     return out
 
 
@@ -636,6 +663,17 @@ def fresh_processes(n, reps, warmup):
                                           0.5 * (s[n // 2 - 1] + s[n // 2]), 4)}
 
 
+# --profile SECTION: run one section alone (warmup + steps calls of each of its
+# operations), so that every dispatch a profiler records belongs to it
+PROFILE_SECTIONS = {
+    "fwd": lambda h, s, n, w: forward_packs(h, s, FWD_PACKS, n, w),
+    "decode": decode_step,
+    "paged": lambda h, s, n, w: paged_prefill(h, s, n, w),
+    "recompute": lambda h, s, n, w: recompute_and_transition(h, s, n, w),
+    "conv": lambda h, s, n, w: short_conv(h, s, n, w),
+}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -650,6 +688,9 @@ def main():
                     help="fresh processes for the median-of-medians timing (0: skip)")
     ap.add_argument("--profile-step", action="store_true",
                     help="only run warmup + steps of the fwd+bwd step (for rocprofv3)")
+    ap.add_argument("--profile", default=None, choices=["step"] + sorted(PROFILE_SECTIONS),
+                    help="only run warmup + steps calls of one section (step: the fwd+bwd "
+                         "step, as --profile-step), for rocprofv3")
     ap.add_argument("--child-protocol", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration)")
@@ -671,10 +712,16 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.profile in PROFILE_SECTIONS:
+        res = PROFILE_SECTIONS[args.profile](hip(), torch.cuda.current_stream(), args.steps,
+                                             args.warmup)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": args.profile, "result": res}), flush=True)
+        return
     meta, step = setup_step(dev)
     T, H, HV, N, stream = meta["T"], meta["H"], meta["HV"], meta["N"], meta["stream"]
     h = hip()
-    if args.profile_step:
+    if args.profile_step or args.profile == "step":
         for _ in range(args.warmup + args.steps):
             step()
         torch.cuda.synchronize()
