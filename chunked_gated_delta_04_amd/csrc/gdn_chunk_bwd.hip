@@ -441,20 +441,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
                                        16, 0, kNonTemporal);
     }
   };
-  // After the last value head is done with Gs: the chunk's raw q rows, then
-  // its raw k rows, into Gs ([64][128] each, unpadded) for the norm backward.
-  // Rows past the chunk's end copy its last row (read, never used).
-  auto copy_qk_rows = [&](int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e0 = 512 * i + 64 * wave;  // first 16-byte chunk of the copy (wave-uniform)
-      const int e = e0 + lane;
-      const int r = min((e & 1023) >> 4, L - 1);
-      const uint16_t* src = (e0 < 1024 ? q : k) + ((size_t)(t0 + r) * H + h) * kHead + 8 * (e & 15);
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(Gs + 8 * e0),
-                                       16, 0, kNonTemporal);
-    }
-  };
   {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
@@ -874,7 +860,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     *reinterpret_cast<uint4*>(&S.PmT[(tid & 63) * BP + (tid >> 6) * 8]) = tst1;
     // (after the stores above, which wait for their own requests only)
     if (jg + 1 < G) copy_states(hv + 1, wave, lane);
-    else copy_qk_rows(wave, lane);
     lds_barrier();
 
     // ---- dT = dD (beta V)^T + dW (beta e^gamma K^)^T, strictly lower
@@ -1034,29 +1019,27 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
   }
 
   // ---- L2-norm backward and scale: x^ . dx^ over all 128 columns (two halves).
-  //      The raw q, k rows come from Gs (copied during the last value head).
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();
+  //      x^ are the normalised rows every product above used (Ks; Qs holds
+  //      q~ = scale q^), so the raw rows are not read again.
+  lds_barrier();
   {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int tw = wave & 3, kh = wave >> 2;
     const int li = lane & 15, kq = lane >> 4;
     float dq_[4] = {0.f, 0.f, 0.f, 0.f}, dk_[4] = {0.f, 0.f, 0.f, 0.f};
-    float qh[4][4], kh_[4][4];  // q^, k^ of the thread's 16 elements (fp32)
+    float qh[4][4], kh_[4][4];  // q^, k^ of the thread's 16 elements
+    const float inv_scale = 1.f / scale;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * tw + 4 * kq + r;
         const int kc = 16 * (4 * kh + j) + li;
-        float qv = 0.f, kv = 0.f;
-        if (t < L) {
-          qv = bf2f(Gs[t * kHead + kc]) * S.inv_q[t];
-          kv = bf2f(Gs[kChunk * kHead + t * kHead + kc]) * S.inv_k[t];
-        }
-        qh[j][r] = qv;
+        // (rows past the chunk's end hold zeros)
+        const float qs = bf2f(S.Qs[t * KP + kc]), kv = bf2f(S.Ks[t * KP + kc]);
+        qh[j][r] = qs * inv_scale;
         kh_[j][r] = kv;
-        dq_[r] += qv * scale * adq[j][r];
+        dq_[r] += qs * adq[j][r];
         dk_[r] += kv * adk[j][r];
       }
 #pragma unroll
