@@ -316,11 +316,11 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
           pv[r] = i >= j ? exp2_fast(gam[i] - gam[j]) * acc[r] : 0.f;
         }
         const uint2 pk = pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
-        *reinterpret_cast<uint2*>(fo.P + blk * (64 * 64) + kcm(i, 16 * jb + 4 * kq, 64)) = pk;
+        st8_nt(fo.P + blk * (64 * 64) + kcm(i, 16 * jb + 4 * kq, 64), pk);
         if (kB) {  // P^T[j][i .. i + 7]: columns of the tile, 16-byte pieces from 32 lanes
           const uint4 x = tile_transpose(Xp[wave], pk, lane);
           if (kq < 2)
-            *reinterpret_cast<uint4*>(bo.P + blk * (64 * 64) + kcm(16 * jb + li, 16 * ib + 8 * kq, 64)) = x;
+            st16_nt(bo.P + blk * (64 * 64) + kcm(16 * jb + li, 16 * ib + 8 * kq, 64), x);
         }
       }
     }
@@ -346,8 +346,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
           ow[u] = pk2(Ts[r * FP + ja], Ts[r * FP + ja + 1]);
           tw4[u] = pk2(Ts[ja * FP + r], Ts[(ja + 1) * FP + r]);
         }
-        *reinterpret_cast<uint4*>(Tg + kcm(r, 8 * kc, 64)) = o4;
-        *reinterpret_cast<uint4*>(Tg + 4096 + kcm(r, 8 * kc, 64)) = t4;
+        st16_nt(Tg + kcm(r, 8 * kc, 64), o4);
+        st16_nt(Tg + 4096 + kcm(r, 8 * kc, 64), t4);
       }
     }
 
@@ -366,11 +366,11 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
                    cvt8s(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq], &fw[32 * s + 8 * kq]), acc);
       }
       const uint2 pk = pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
-      *reinterpret_cast<uint2*>(fo.W + blk * 8192 + kcm(16 * tb + li, 16 * db + 4 * kq, 64)) = pk;
+      st8_nt(fo.W + blk * 8192 + kcm(16 * tb + li, 16 * db + 4 * kq, 64), pk);
       if (kB) {  // W^T[k][t .. t + 7]
         const uint4 x = tile_transpose(Xp[wave], pk, lane);
         if (kq < 2)
-          *reinterpret_cast<uint4*>(bo.W + blk * 8192 + kcm(16 * db + li, 16 * tb + 8 * kq, 128)) = x;
+          st16_nt(bo.W + blk * 8192 + kcm(16 * db + li, 16 * tb + 8 * kq, 128), x);
       }
     }
 
@@ -387,8 +387,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
           acc = mfma(cvt8s(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq], &bet[32 * s + 8 * kq]),
                      __builtin_bit_cast(bf16x8, vc), acc);
         }
-        *reinterpret_cast<uint2*>(Ub + kcm(16 * vb + li, 16 * tb + 4 * kq, 128)) =
-            pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
+        st8_nt(Ub + kcm(16 * vb + li, 16 * tb + 4 * kq, 128), pack4_bf16(acc[0], acc[1], acc[2], acc[3]));
       }
     }
     __syncthreads();  // gates, A, T and V are rewritten for the next value head
@@ -406,8 +405,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     auto rows_out = [&](const uint16_t* src, uint16_t* dst) {
       for (int e = tid; e < 64 * 16; e += 256) {
         const int sg = e >> 6, t = e & 63;
-        *reinterpret_cast<uint4*>(dst + kcm(t, sg * 8, 64)) =
-            *reinterpret_cast<const uint4*>(&src[t * KP + sg * 8]);
+        st16_nt(dst + kcm(t, sg * 8, 64), *reinterpret_cast<const uint4*>(&src[t * KP + sg * 8]));
       }
     };
     auto cols_out = [&](const uint16_t* src, uint16_t* dst) {
@@ -415,7 +413,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
       for (int i = 0; i < 4; ++i) {
         const int e0 = 256 * i + 64 * wave;  // wave-uniform
         const int tg = e0 >> 7, d0 = (e0 & 127) + 16 * kq;
-        *reinterpret_cast<uint4*>(dst + kcm(d0 + li, 8 * tg, 128)) = lds_col8(src, KP, 8 * tg, d0, lane);
+        st16_nt(dst + kcm(d0 + li, 8 * tg, 128), lds_col8(src, KP, 8 * tg, d0, lane));
       }
     };
     rows_out(Qs, fo.Qn + kblk * 8192);   // Q~ [tok][k]

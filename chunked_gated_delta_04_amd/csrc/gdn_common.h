@@ -78,6 +78,26 @@ __device__ __forceinline__ uint4 ld16_nt(const uint16_t* p) {
   return make_uint4(x[0], x[1], x[2], x[3]);
 }
 
+// Non-temporal (streaming) stores of 8 and 16 bytes: for outputs that the
+// writing kernel does not read again, so that they do not displace lines it
+// reuses.
+__device__ __forceinline__ void st8_nt(uint16_t* p, uint2 x) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 v;
+  v[0] = x.x;
+  v[1] = x.y;
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void st16_nt(uint16_t* p, uint4 x) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 v;
+  v[0] = x.x;
+  v[1] = x.y;
+  v[2] = x.z;
+  v[3] = x.w;
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 // fp32 -> bf16, round to nearest even.
