@@ -403,10 +403,12 @@ FWD_PACKS_TP2 = ("fwd_4x4096_h8_hv16", "fwd_varlen12_32768_h8_hv16")
 
 def long_and_tp2_steps(h, stream, steps, warmup):
     """The fwd+bwd step at one GPU's share of a TP = 2 head split (8 key / 16
-    value heads) and on one long sequence of 65,536 and 131,072 tokens."""
+    value heads), on the same 16384 tokens as 32 x 512 and 128 x 128 short
+    sequences, and on one long sequence of 65,536 and 131,072 tokens."""
     import torch
     out = {}
-    for name, reps in (("fwdbwd_2x8192_h8_hv16", steps), ("fwdbwd_1x65536_h16_hv32", steps),
+    for name, reps in (("fwdbwd_2x8192_h8_hv16", steps), ("fwdbwd_32x512_h16_hv32", steps),
+                       ("fwdbwd_128x128_h16_hv32", steps), ("fwdbwd_1x65536_h16_hv32", steps),
                        ("fwdbwd_1x131072_h16_hv32", max(3, steps // 4))):
         T, ms = fwdbwd_step_ms(h, stream, name, reps, min(warmup, 2))
         out[name] = {"ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1)}
@@ -418,8 +420,9 @@ def secondary(h, stream, steps, warmup):
     """Forward-only throughput on the 4 x 4096 and the 12-sequence varlen packs, the
     decode step against the HBM roofline, the paged prefill, the recomputing
     backward and the local transitions, the short convolution, the same packs
-    at one GPU's share of a TP = 2 head split (8 key / 16 value heads), and one
-    long sequence of 65,536 and 131,072 tokens."""
+    at one GPU's share of a TP = 2 head split (8 key / 16 value heads), the
+    fwd+bwd step on packs of short sequences (32 x 512, 128 x 128 tokens), and
+    one long sequence of 65,536 and 131,072 tokens."""
     out = forward_packs(h, stream, FWD_PACKS + FWD_PACKS_TP2, steps, warmup)
     out.update(decode_step(h, stream, steps, warmup))
     out.update(paged_prefill(h, stream, steps, warmup))

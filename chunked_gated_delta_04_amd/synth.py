@@ -181,6 +181,11 @@ WORKLOADS = {
     "paged_8x512_h8_hv16_pool64": dict(kind="paged", lens=[512] * 8, H=8, HV=16, slots=64,
                                        n_null=0, n_fresh=4, seed=BASE_SEED + 5),
     # one long sequence (the long-context rows of the Cake page's tests)
+    # many short sequences: the pages' 32 x 512 and 128 x 128 packs of 16384 tokens
+    "fwdbwd_32x512_h16_hv32": dict(kind="fwdbwd", lens=[512] * 32, H=16, HV=32, h0_std=0.1,
+                                   seed=BASE_SEED + 13),
+    "fwdbwd_128x128_h16_hv32": dict(kind="fwdbwd", lens=[128] * 128, H=16, HV=32, h0_std=0.1,
+                                    seed=BASE_SEED + 14),
     "fwdbwd_1x65536_h16_hv32": dict(kind="fwdbwd", lens=[65536], H=16, HV=32, h0_std=0.1,
                                     seed=BASE_SEED + 11),
     "fwdbwd_1x131072_h16_hv32": dict(kind="fwdbwd", lens=[131072], H=16, HV=32, h0_std=0.1,
