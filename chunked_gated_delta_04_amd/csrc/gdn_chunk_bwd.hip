@@ -33,16 +33,6 @@ namespace gdn {
 namespace {
 constexpr int KP = 136;  // LDS pitch (bf16) of [64][128] tiles
 
-__device__ __forceinline__ void lower_tile(int t, int& ib, int& jb) {
-  ib = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
-  jb = t - (ib * (ib + 1)) / 2;
-}
-
-__device__ __forceinline__ bf16x8 ld8_or0(const uint16_t* p, bool ok) {
-  if (ok) return ld8(p);
-  return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-}
-
 // Sum over the 16 lanes of a 16-lane group (lanes sharing kq), complete in
 // the group's first lane only: DPP row shifts (VALU work in a fixed order)
 // instead of four LDS swizzles.
@@ -371,9 +361,6 @@ struct BwdLds {
   float dot_q[2][64], dot_k[2][64];
 };
 
-__device__ __forceinline__ bf16x8 zero8() {
-  return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-}
 // Column c0 + lane % 16 of a [64][KP] row tile: rows r0 .. r0 + 7 as an MFMA
 // operand, or rows r0 .. r0 + 3 in fp32 (r0 may differ between lane groups).
 __device__ __forceinline__ bf16x8 col8(const uint16_t* tile, int r0, int c0, int lane) {
