@@ -320,17 +320,20 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Per-chunk gradients: one 512-thread workgroup per (chunk, key head); the
-// value heads of the key head run in order. Wave w owns token tile tw = w & 3
-// (tokens 16 tw .. 16 tw + 15) and column half kh = w >> 2 (key or value
-// columns 64 kh .. 64 kh + 63) of every token-indexed result. Matrices that
-// are contracted over the chunk's tokens are kept in LDS as bf16 rows (tiles
-// of 64 x 64 also transposed); their columns come from transposing LDS reads,
-// so every MFMA operand is one or two LDS reads. The state h and its gradient
-// dh' are copied straight from HBM into LDS (first thing for the first value
-// head, and for the next one as soon as the current one is done with them);
-// each phase's other operands are requested a phase ahead, so the workgroup -
-// alone on its CU - does not stall on memory at every phase.
+// Per-chunk gradients: one 512-thread workgroup per CU (its LDS leaves room
+// for no second one), each taking the items (chunk, key head) c H + h in
+// steps of the grid size; the value heads of an item run in order. Wave w owns
+// token tile tw = w & 3 (tokens 16 tw .. 16 tw + 15) and column half
+// kh = w >> 2 (key or value columns 64 kh .. 64 kh + 63) of every
+// token-indexed result. Matrices that are contracted over the chunk's tokens
+// are kept in LDS as bf16 rows (tiles of 64 x 64 also transposed); their
+// columns come from transposing LDS reads, so every MFMA operand is one or two
+// LDS reads. The state h and its gradient dh' are copied straight from HBM
+// into LDS - for an item's first value head, together with its raw q and k
+// rows, while the previous item finishes (norm backward, output stores); for
+// the next value head as soon as the current one is done with them - and each
+// phase's other operands are requested a phase ahead, so the workgroup, alone
+// on its CU, does not stall on memory at every phase.
 // Per-token and per-column partial sums go to LDS slots owned by one wave each
 // and are added once per value head in a fixed order.
 namespace {
@@ -340,17 +343,12 @@ struct BwdLds {
   uint16_t Ks[64 * KP];                     // k^ rows
   uint16_t Qs[64 * KP];                     // q~ rows (columns of both come from
                                             // transpose reads)
-  uint16_t Pm[64 * BP], PmT[64 * BP];       // dP o Gamma and transpose; then T, T^T;
-                                            // then M, M^T
   union {                                   // time-shared regions
     uint16_t Z[64 * KP];                    //   Z = T^T dD [tok][v]
     uint16_t V[64 * KP];                    //   V rows of the chunk
     uint16_t dT[64 * BP];                   //   dT [i][m]
+    uint16_t dq[64 * KP];                   //   dq rows before they are stored
   } rz;
-  union {
-    uint16_t dW[64 * KP];                   //   dW [tok][k]
-    uint16_t Y1T[64 * BP];                  //   (dT T^T)^T
-  } rw;
   float gam[64], bet[64], eg[64], ebw[64];
   float inv_k[64], inv_q[64];  // 1 / |k|, 1 / |q| per token
   float rowF[2][64], colF[8][64];           // F = dP o P
@@ -391,28 +389,32 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     const float* __restrict__ gB, BwdBufs bufs, const uint16_t* __restrict__ dO,
     uint16_t* __restrict__ dq, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
     float* __restrict__ dg, float* __restrict__ dbeta) {
-  const int c = blockIdx.x, h = blockIdx.y;
-  const ChunkInfo ci = table[c];
-  if (ci.seq < 0) return;
-  const int t0 = ci.t0, L = ci.len;
-
   __shared__ __align__(16) BwdLds S;
   // h and dh' in the layout both have in global memory ([v / 8][k][v % 8]),
   // filled by direct global-to-LDS copies; arrays of their own, so that those
-  // copies are not taken to alias the tiles in S. dq staging at the end.
+  // copies are not taken to alias the tiles in S.
   __shared__ __align__(16) uint16_t Hs[kHead * kHead];
   __shared__ __align__(16) uint16_t Gs[kHead * kHead];
+  // The [64][64] tiles dP o Gamma and its transpose (then T, T^T; then M, M^T)
+  // and the dW / Y1^T region: arrays of their own as well, because between
+  // two items they receive the next item's raw q and k rows by direct copies.
+  __shared__ __align__(16) uint16_t PP[2 * 64 * BP];
+  __shared__ __align__(16) uint16_t RW[64 * KP];
+  uint16_t* const Pm = PP;
+  uint16_t* const PmT = PP + 64 * BP;
+  uint16_t* const dWs = RW;   // dW [tok][k], pitch KP
+  uint16_t* const Y1T = RW;   // (dT T^T)^T [j][i], pitch BP
+  uint16_t* const Qraw = PP;  // raw q rows [tok][k], pitch 128
+  uint16_t* const Kraw = RW;  // raw k rows [tok][k], pitch 128
 
   const int G = HV / H;
+  const int NI = NC * H;  // items: (chunk c, key head h) is item c H + h
 
-  // h and dh' of value head hv_ straight into LDS (Hs, Gs): each wave copies
-  // 1 KiB per request, lane l the 16 bytes at offset 16 l. Issued for the
-  // first value head before anything else (so the copies overlap the q, k
-  // loads and norms) and for the next one as soon as the current one is done
-  // with Hs and Gs, so the copies overlap the rest of its work.
-  auto copy_states = [&](int hv_, int wave, int lane) {
-    const uint16_t* hb_ = saved + blk_saved(c, hv_, HV);
-    const uint16_t* dhb_ = bufs.dh + ((size_t)hv_ * NC + c) * (kHead * kHead);
+  // h and dh' of chunk c_, value head hv_ straight into LDS (Hs, Gs): each
+  // wave copies 1 KiB per request, lane l the 16 bytes at offset 16 l.
+  auto copy_states = [&](int c_, int hv_, int wave, int lane) {
+    const uint16_t* hb_ = saved + blk_saved(c_, hv_, HV);
+    const uint16_t* dhb_ = bufs.dh + ((size_t)hv_ * NC + c_) * (kHead * kHead);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e0 = 512 * i + 64 * wave;  // first 16-byte chunk of the copy
@@ -428,640 +430,710 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
                                        16, 0, kNonTemporal);
     }
   };
-  {
+
+  // What item it_ needs before its first value head, copied straight into
+  // LDS: h and dh' of its first value head (Hs, Gs) and its raw q and k rows
+  // (Qraw, Kraw; wave copy i of wave w covers rows 8 w + 4 i .. + 3, lane l
+  // the 16 bytes of row + l / 16 at column 8 (l % 16); rows past the chunk's
+  // end repeat its last row and are masked where they are read). Issued for
+  // the workgroup's first item on entry and for its next item as soon as the
+  // current one is done with those regions, so that the copies overlap the
+  // current item's norm backward and output stores.
+  auto prefetch = [&](int it_) {
+    if (it_ >= NI) return;
+    const int c_ = it_ / H, h_ = it_ - c_ * H;
+    const ChunkInfo cn = table[c_];
+    if (cn.seq < 0) return;
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    copy_states(h * G, tid >> 6, tid & 63);
-  }
-
-  // ---- q, k rows: L2 norm; k^ and q~ as rows (Ks, Qs). 16 threads per row,
-  //      so each request covers whole rows.
-  {
-    const int tid = threadIdx.x;
-    const int sg = tid & 15;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(k) + ((size_t)t0 * H + h) * kHead, 0, L * H * kHead * 2, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rq0 = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(q) + ((size_t)t0 * H + h) * kHead, 0, L * H * kHead * 2, kBufferWord3);
-    uint4 kr[2], qr[2];
-    float sk[2], sq[2];
+    const int wave = tid >> 6, lane = tid & 63;
+    copy_states(c_, h_ * G, wave, lane);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = (tid >> 4) + 32 * j;
-      kr[j] = load_b128(rk, (r * H * kHead + sg * 8) * 2);  // rows past the chunk read as 0
-      qr[j] = load_b128(rq0, (r * H * kHead + sg * 8) * 2);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[j]);
-      const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qr[j]);
-      sk[j] = 0.f;
-      sq[j] = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float a0 = bf2f(kw[e] & 0xffffu), a1 = bf2f(kw[e] >> 16);
-        const float b0 = bf2f(qw[e] & 0xffffu), b1 = bf2f(qw[e] >> 16);
-        sk[j] += a0 * a0 + a1 * a1;
-        sq[j] += b0 * b0 + b1 * b1;
-      }
-      sk[j] = group_sum<16>(sk[j]);
-      sq[j] = group_sum<16>(sq[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = (tid >> 4) + 32 * j;
-      const float ik = 1.f / sqrtf(sk[j] + kNormEps), iq = 1.f / sqrtf(sq[j] + kNormEps);
-      const float iqs = iq * scale;
-      if (sg == 0) {
-        S.inv_k[r] = ik;
-        S.inv_q[r] = iq;
-      }
-      const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[j]);
-      const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qr[j]);
-      uint4 ko, qo;
-      uint32_t* kow = reinterpret_cast<uint32_t*>(&ko);
-      uint32_t* qow = reinterpret_cast<uint32_t*>(&qo);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kow[e] = pk2(bf2f(kw[e] & 0xffffu) * ik, bf2f(kw[e] >> 16) * ik);
-        qow[e] = pk2(bf2f(qw[e] & 0xffffu) * iqs, bf2f(qw[e] >> 16) * iqs);
-      }
-      *reinterpret_cast<uint4*>(&S.Ks[r * KP + sg * 8]) = ko;
-      *reinterpret_cast<uint4*>(&S.Qs[r * KP + sg * 8]) = qo;
-    }
-  }
-  lds_barrier();  // (not __syncthreads: that would wait for the state copies)
-
-  // Gate gradients of value head hv_ (wave 0): fixed-order sums of the partial
-  // slots, then dg = reverse cumsum of dgamma inside the chunk. Run by wave 0
-  // at the top of the next value head (or after the last one): the slots and
-  // gamma are rewritten only after the next gate barrier, which wave 0 reaches
-  // after this, and the work overlaps the other waves' requests. t: the lane,
-  // from an opaque copy of the thread index (see the value-head loop), so that
-  // none of the addresses below is hoisted out of the loop.
-  auto dg_out = [&](int hv_, int t) {
-    const int w0 = 4 * ((t >> 4) & 1);  // the waves whose column tiles hold t
-    float dgm = (S.rowF[0][t] + S.rowF[1][t]) + (S.rowG[0][t] + S.rowG[1][t]) +
-                (S.rowE[0][t] + S.rowE[1][t]);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) dgm -= S.colF[w0 + w][t] + S.colE[w0 + w][t];
-    const float dbt = (S.rowB[0][t] + S.rowB[1][t]) + (S.rowB2[0][t] + S.rowB2[1][t]) +
-                      (S.rowB3[0][t] + S.rowB3[1][t]);
-    float x = t < L ? dgm : 0.f;
-    if (t == L - 1) {
-      float glsum = 0.f, hdsum = 0.f;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        glsum += S.gl_part[w];
-        hdsum += S.hd_part[w];
-      }
-      x += glsum + exp2_fast(S.gam[L - 1]) * hdsum;
-    }
-    x = wave_suffix_sum(x, t);
-    if (t < L) {
-      dg[(size_t)(t0 + t) * HV + hv_] = x;
-      dbeta[(size_t)(t0 + t) * HV + hv_] = dbt;
+    for (int i = 0; i < 2; ++i) {
+      const int r0 = 8 * wave + 4 * i;
+      const int r = min(r0 + (lane >> 4), cn.len - 1);
+      const size_t off = ((size_t)(cn.t0 + r) * H + h_) * kHead + 8 * (lane & 15);
+      __builtin_amdgcn_global_load_lds(q + off,
+                                       (__attribute__((address_space(3))) void*)(Qraw + 128 * r0),
+                                       16, 0, kNonTemporal);
+      __builtin_amdgcn_global_load_lds(k + off,
+                                       (__attribute__((address_space(3))) void*)(Kraw + 128 * r0),
+                                       16, 0, kNonTemporal);
     }
   };
 
-  // dq~, dk^ over the value heads: [j][r] = d[16 tw + 4 kq + r][16 (4 kh + j) + li]
-  f32x4 adq[4], adk[4];
+  prefetch(blockIdx.x);
+  for (int it = blockIdx.x; it < NI; it += gridDim.x) {
+    const int c = it / H, h = it - c * H;
+    const ChunkInfo ci = table[c];
+    // the chunk slots past the pack's chunks are the last ones, so every later
+    // item of this workgroup is past them too
+    if (ci.seq < 0) break;
+    const int t0 = ci.t0, L = ci.len;
+
+    // every wave's copies for this item have landed
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    lds_barrier();
+
+    // ---- q, k rows (copied into Qraw, Kraw): L2 norm; k^ and q~ as rows (Ks,
+    //      Qs). 16 threads per row.
+    {
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));  // (opaque: nothing here is hoisted out of the item loop)
+      const int sg = tid & 15;
+      uint4 kr[2], qr[2];
+      float sk[2], sq[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    adq[j] = zero4();
-    adk[j] = zero4();
-  }
-
-  const size_t rs = (size_t)HV * kHead;  // token stride of dO, v, dv
-
-
-  for (int jg = 0; jg < G; ++jg) {
-    // Re-derive the thread coordinates each iteration from an opaque copy, so
-    // the many LDS addresses built from them are not hoisted out of the loop
-    // (they would not fit in the register budget of two waves per SIMD).
-    int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));
-    const int lane = tid & 63, wave = tid >> 6;
-    const int tw = wave & 3, kh = wave >> 2;
-    const int li = lane & 15, kq = lane >> 4;
-    const int trow = 16 * tw + li;
-    const bool trow_ok = trow < L;
-    const int hv = h * G + jg;
-    const size_t blk = (size_t)hv * NC + c;
-    // (chunk-major tiles: see kcm; states: [v / 32][v % 32 / 8][k][v % 8])
-    const uint16_t* hb = saved + blk_saved(c, hv, HV);  // h
-    const uint16_t* Db = hb + kSavedH;                   // D [tok][v], chunk-major
-    const uint16_t* dDb = bufs.dD + blk * 8192;          // dD [tok][v], chunk-major
-    const uint16_t* dDTb = bufs.dDT + blk * 8192;        // dD^T [v][tok], chunk-major
-    const uint16_t* Tg = Tmat + blk * 8192;              // T, then T^T, chunk-major
-    // Token rows of dO and v through range-checked buffer loads: rows at or
-    // past the chunk's end read as zeros, with no branch around the load.
-    const __amdgpu_buffer_rsrc_t rdO = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(dO) + ((size_t)t0 * HV + hv) * kHead, 0, L * (int)rs * 2, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(v) + ((size_t)t0 * HV + hv) * kHead, 0, L * (int)rs * 2, kBufferWord3);
-
-    // ---- gate requests first (every wave; wave 0 uses them), so that their
-    //      wait does not cover the operand requests below: gamma (base 2),
-    //      beta, e^gamma and e^(gamma_L - gamma) of each token as the forward's
-    //      WY pass formed them, four contiguous 256-byte rows
-    const float gam_t = gB[blk * kGates + lane];
-    const float bet_t = gB[blk * kGates + kChunk + lane];
-    const float eg_t = gE[blk * kGates + lane];
-    const float ebw_t = gE[blk * kGates + kChunk + lane];
-
-    // ---- requests for the dP phase: the own rows of dO and q, the D rows of
-    //      this wave's dP tiles. Operand pieces the wave does not use (tiles
-    //      above the diagonal, token blocks before its own) are requested past
-    //      the end of a range-checked buffer, which returns zeros and moves no
-    //      data, so every wave issues the same requests with no branch.
-    constexpr int kTileBytes = kChunk * kHead * 2, kTBytes = kChunk * kChunk * 2;
-    const __amdgpu_buffer_rsrc_t rD = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(Db), 0, kTileBytes, kBufferWord3);
-    bf16x8 oa[4], dfr[2][4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      oa[s] = ld8_buf(rdO, (trow * (int)rs + 32 * s + 8 * kq) * 2);
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        const int jb = kh + 2 * q2;
-        dfr[q2][s] = ld8_buf(rD, jb <= tw ? kcm(16 * jb + li, 32 * s + 8 * kq, kChunk) * 2 : kTileBytes);
+      for (int j = 0; j < 2; ++j) {
+        const int r = (tid >> 4) + 32 * j;
+        const uint32_t m = r < L ? 0xffffffffu : 0u;  // rows past the chunk's end: zeros
+        const uint4 kx = *reinterpret_cast<const uint4*>(&Kraw[128 * r + 8 * sg]);
+        const uint4 qx = *reinterpret_cast<const uint4*>(&Qraw[128 * r + 8 * sg]);
+        kr[j] = make_uint4(kx.x & m, kx.y & m, kx.z & m, kx.w & m);
+        qr[j] = make_uint4(qx.x & m, qx.y & m, qx.z & m, qx.w & m);
       }
-    }
-
-    // requests for the Z phase: T^T rows of this wave's tokens, dD^T rows, v rows
-    // (token blocks s with 32 s + 31 < 16 tw meet only zeros of T)
-    const __amdgpu_buffer_rsrc_t rTT = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(Tg) + 4096, 0, kTBytes, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rDDT = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(dDTb), 0, kTileBytes, kBufferWord3);
-    bf16x8 tt[2], ddt[4][2];
-    uint2 vr[4];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-      tt[s] = ld8_buf(rTT, 32 * s + 31 >= 16 * tw ? kcm(trow, 32 * s + 8 * kq, 64) * 2 : kTBytes);
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[j]);
+        const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qr[j]);
+        sk[j] = 0.f;
+        sq[j] = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int vt = 4 * kh + j;
+        for (int e = 0; e < 4; ++e) {
+          const float a0 = bf2f(kw[e] & 0xffffu), a1 = bf2f(kw[e] >> 16);
+          const float b0 = bf2f(qw[e] & 0xffffu), b1 = bf2f(qw[e] >> 16);
+          sk[j] += a0 * a0 + a1 * a1;
+          sq[j] += b0 * b0 + b1 * b1;
+        }
+        sk[j] = group_sum<16>(sk[j]);
+        sq[j] = group_sum<16>(sq[j]);
+      }
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-        ddt[j][s] = ld8_buf(rDDT, 32 * s + 31 >= 16 * tw
-                                      ? kcm(16 * vt + li, 32 * s + 8 * kq, kHead) * 2 : kTileBytes);
-      vr[j] = load_b64(rv, (trow * (int)rs + 16 * vt + 4 * kq) * 2);
-    }
-
-    // ---- gates (wave 0, after the previous value head's gate gradients)
-    if (wave == 0) {
-      if (jg > 0) dg_out(hv - 1, lane);
-      S.gam[lane] = gam_t;
-      S.bet[lane] = bet_t;
-      S.eg[lane] = eg_t;
-      S.ebw[lane] = ebw_t;
+      for (int j = 0; j < 2; ++j) {
+        const int r = (tid >> 4) + 32 * j;
+        const float ik = 1.f / sqrtf(sk[j] + kNormEps), iq = 1.f / sqrtf(sq[j] + kNormEps);
+        const float iqs = iq * scale;
+        if (sg == 0) {
+          S.inv_k[r] = ik;
+          S.inv_q[r] = iq;
+        }
+        const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[j]);
+        const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qr[j]);
+        uint4 ko, qo;
+        uint32_t* kow = reinterpret_cast<uint32_t*>(&ko);
+        uint32_t* qow = reinterpret_cast<uint32_t*>(&qo);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kow[e] = pk2(bf2f(kw[e] & 0xffffu) * ik, bf2f(kw[e] >> 16) * ik);
+          qow[e] = pk2(bf2f(qw[e] & 0xffffu) * iqs, bf2f(qw[e] >> 16) * iqs);
+        }
+        *reinterpret_cast<uint4*>(&S.Ks[r * KP + sg * 8]) = ko;
+        *reinterpret_cast<uint4*>(&S.Qs[r * KP + sg * 8]) = qo;
+      }
     }
     lds_barrier();
 
-    // ---- dP = dO D^T (i >= j) and P = Gamma o Q~K^T: Pm = dP o Gamma (+ transpose);
-    //      F = dP o P row / column partial sums. Wave: row tile tw, col tiles kh, kh + 2.
-    {
-      float rowp[4] = {0.f, 0.f, 0.f, 0.f};
+    // Gate gradients of value head hv_ (wave 0): fixed-order sums of the partial
+    // slots, then dg = reverse cumsum of dgamma inside the chunk. Run by wave 0
+    // at the top of the next value head (or after the last one): the slots and
+    // gamma are rewritten only after the next gate barrier, which wave 0 reaches
+    // after this, and the work overlaps the other waves' requests. t: the lane,
+    // from an opaque copy of the thread index (see the value-head loop), so that
+    // none of the addresses below is hoisted out of the loop.
+    auto dg_out = [&](int hv_, int t) {
+      const int w0 = 4 * ((t >> 4) & 1);  // the waves whose column tiles hold t
+      float dgm = (S.rowF[0][t] + S.rowF[1][t]) + (S.rowG[0][t] + S.rowG[1][t]) +
+                  (S.rowE[0][t] + S.rowE[1][t]);
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        const int jb = kh + 2 * q2;
-        const int j = 16 * jb + li;
-        float pv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (jb <= tw) {
-          // dP tile and the Q~ K^T tile at the same place (formed here, per
-          // value head, rather than kept in registers across them)
-          f32x4 dp = zero4(), qk = zero4();
+      for (int w = 0; w < 4; ++w) dgm -= S.colF[w0 + w][t] + S.colE[w0 + w][t];
+      const float dbt = (S.rowB[0][t] + S.rowB[1][t]) + (S.rowB2[0][t] + S.rowB2[1][t]) +
+                        (S.rowB3[0][t] + S.rowB3[1][t]);
+      float x = t < L ? dgm : 0.f;
+      if (t == L - 1) {
+        float glsum = 0.f, hdsum = 0.f;
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            dp = mfma(oa[s], dfr[q2][s], dp);
-            qk = mfma(ld8(&S.Qs[trow * KP + 32 * s + 8 * kq]),
-                      ld8(&S.Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), qk);
-          }
-          float colp = 0.f;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 16 * tw + 4 * kq + r;
-            if (i >= j) {
-              const float dpm = dp[r] * exp2_fast(S.gam[i] - S.gam[j]);
-              const float f = dpm * qk[r];
-              pv[r] = dpm;
-              rowp[r] += f;
-              colp += f;
-            }
-          }
-          colp = sum_over_rows(colp);
-          if (kq == 0) S.colF[wave][j] = colp;
-        } else if (kq == 0) {
-          S.colF[wave][j] = 0.f;  // every slot of the wave's column tiles is written
+        for (int w = 0; w < 8; ++w) {
+          glsum += S.gl_part[w];
+          hdsum += S.hd_part[w];
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S.Pm[(16 * tw + 4 * kq + r) * BP + j] = f2bf(pv[r]);
-        *reinterpret_cast<uint2*>(&S.PmT[j * BP + 16 * tw + 4 * kq]) =
-            pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
+        x += glsum + exp2_fast(S.gam[L - 1]) * hdsum;
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) rowp[r] = sum16_lane0(rowp[r]);
-      if (li == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S.rowF[kh][16 * tw + 4 * kq + r] = rowp[r];
+      x = wave_suffix_sum(x, t);
+      if (t < L) {
+        dg[(size_t)(t0 + t) * HV + hv_] = x;
+        dbeta[(size_t)(t0 + t) * HV + hv_] = dbt;
       }
+    };
+
+    // dq~, dk^ over the value heads: [j][r] = d[16 tw + 4 kq + r][16 (4 kh + j) + li]
+    f32x4 adq[4], adk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      adq[j] = zero4();
+      adk[j] = zero4();
     }
-    // ---- Z = T^T dD (written [tok][v]); dV = diag(beta) Z; dbeta of U.
-    //      Wave: token columns of tile tw, value tiles 4 kh .. 4 kh + 3.
-    //      First every request of this wave is waited for: the Z operands are
-    //      the youngest, and the copies of h and dh', issued before them, are
-    //      then in LDS too (for the other waves after the barrier below).
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    {
-      float bp = 0.f;
+
+    const size_t rs = (size_t)HV * kHead;  // token stride of dO, v, dv
+
+
+    for (int jg = 0; jg < G; ++jg) {
+      // Re-derive the thread coordinates each iteration from an opaque copy, so
+      // the many LDS addresses built from them are not hoisted out of the loop
+      // (they would not fit in the register budget of two waves per SIMD).
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      const int lane = tid & 63, wave = tid >> 6;
+      const int tw = wave & 3, kh = wave >> 2;
+      const int li = lane & 15, kq = lane >> 4;
+      const int trow = 16 * tw + li;
+      const bool trow_ok = trow < L;
+      const int hv = h * G + jg;
+      const size_t blk = (size_t)hv * NC + c;
+      // (chunk-major tiles: see kcm; states: [v / 32][v % 32 / 8][k][v % 8])
+      const uint16_t* hb = saved + blk_saved(c, hv, HV);  // h
+      const uint16_t* Db = hb + kSavedH;                   // D [tok][v], chunk-major
+      const uint16_t* dDb = bufs.dD + blk * 8192;          // dD [tok][v], chunk-major
+      const uint16_t* dDTb = bufs.dDT + blk * 8192;        // dD^T [v][tok], chunk-major
+      const uint16_t* Tg = Tmat + blk * 8192;              // T, then T^T, chunk-major
+      // Token rows of dO and v through range-checked buffer loads: rows at or
+      // past the chunk's end read as zeros, with no branch around the load.
+      const __amdgpu_buffer_rsrc_t rdO = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(dO) + ((size_t)t0 * HV + hv) * kHead, 0, L * (int)rs * 2, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(v) + ((size_t)t0 * HV + hv) * kHead, 0, L * (int)rs * 2, kBufferWord3);
+
+      // ---- gate requests first (every wave; wave 0 uses them), so that their
+      //      wait does not cover the operand requests below: gamma (base 2),
+      //      beta, e^gamma and e^(gamma_L - gamma) of each token as the forward's
+      //      WY pass formed them, four contiguous 256-byte rows
+      const float gam_t = gB[blk * kGates + lane];
+      const float bet_t = gB[blk * kGates + kChunk + lane];
+      const float eg_t = gE[blk * kGates + lane];
+      const float ebw_t = gE[blk * kGates + kChunk + lane];
+
+      // ---- requests for the dP phase: the own rows of dO and q, the D rows of
+      //      this wave's dP tiles. Operand pieces the wave does not use (tiles
+      //      above the diagonal, token blocks before its own) are requested past
+      //      the end of a range-checked buffer, which returns zeros and moves no
+      //      data, so every wave issues the same requests with no branch.
+      constexpr int kTileBytes = kChunk * kHead * 2, kTBytes = kChunk * kChunk * 2;
+      const __amdgpu_buffer_rsrc_t rD = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(Db), 0, kTileBytes, kBufferWord3);
+      bf16x8 oa[4], dfr[2][4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        oa[s] = ld8_buf(rdO, (trow * (int)rs + 32 * s + 8 * kq) * 2);
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const int jb = kh + 2 * q2;
+          dfr[q2][s] = ld8_buf(rD, jb <= tw ? kcm(16 * jb + li, 32 * s + 8 * kq, kChunk) * 2 : kTileBytes);
+        }
+      }
+
+      // requests for the Z phase: T^T rows of this wave's tokens, dD^T rows, v rows
+      // (token blocks s with 32 s + 31 < 16 tw meet only zeros of T)
+      const __amdgpu_buffer_rsrc_t rTT = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(Tg) + 4096, 0, kTBytes, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t rDDT = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(dDTb), 0, kTileBytes, kBufferWord3);
+      bf16x8 tt[2], ddt[4][2];
+      uint2 vr[4];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        tt[s] = ld8_buf(rTT, 32 * s + 31 >= 16 * tw ? kcm(trow, 32 * s + 8 * kq, 64) * 2 : kTBytes);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int vt = 4 * kh + j;
-        f32x4 z = zero4();
 #pragma unroll
         for (int s = 0; s < 2; ++s)
-          if (32 * s + 31 >= 16 * tw)  // T[m][t] needs m >= t
-            z = mfma(ddt[j][s], tt[s], z);
-        // z[r] = Z[t = trow][v = 16 vt + 4 kq + r]
-        const int vv = 16 * vt + 4 * kq;
-        *reinterpret_cast<uint2*>(&S.rz.Z[trow * KP + vv]) = pack4_bf16(z[0], z[1], z[2], z[3]);
-        if (trow_ok) {
-          const uint2 u = vr[j];
-          bp += bf2f(u.x & 0xffffu) * z[0] + bf2f(u.x >> 16) * z[1] +
-                bf2f(u.y & 0xffffu) * z[2] + bf2f(u.y >> 16) * z[3];
-          const float bt = S.bet[trow];
-          *reinterpret_cast<uint2*>(dv + ((size_t)(t0 + trow) * HV + hv) * kHead + vv) =
-              pack4_bf16(bt * z[0], bt * z[1], bt * z[2], bt * z[3]);
-        }
+          ddt[j][s] = ld8_buf(rDDT, 32 * s + 31 >= 16 * tw
+                                        ? kcm(16 * vt + li, 32 * s + 8 * kq, kHead) * 2 : kTileBytes);
+        vr[j] = load_b64(rv, (trow * (int)rs + 16 * vt + 4 * kq) * 2);
       }
-      bp = sum_over_rows(bp);
-      if (kq == 0) S.rowB[kh][trow] = bp;
-    }
-    // the own rows of dD (pass 2 and dT), requested as soon as the Z operands
-    // are dead, so that passes 1a and 1b cover their wait
-    bf16x8 ea[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      ea[s] = __builtin_bit_cast(bf16x8, ld16_nt(dDb + kcm(trow, 32 * s + 8 * kq, kChunk)));
-    lds_barrier();
 
-    // ---- key-column passes (columns 16 kt + li, kt = 4 kh .. 4 kh + 3), h from LDS:
-    //      pass 1: x1 = dO h^T, x4 = Z h^T (= -T^T dW),
-    //              y1 = (dP o Gamma) K^, y2 = (dP o Gamma)^T Q~
-    //      pass 2: x3 = dD h^T (= -dW), stored for dT
-    //      then dh' replaces h in LDS; pass 3: x2 = D dh'^T
-    float gr[4] = {0.f, 0.f, 0.f, 0.f}, br[4] = {0.f, 0.f, 0.f, 0.f};
-    {  // pass 1a: x1, y1 -> dq~
-      bf16x8 pa[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) pa[s] = ld8(&S.Pm[trow * BP + 32 * s + 8 * kq]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kr = 16 * (4 * kh + j) + li;
-        f32x4 x1 = zero4(), y1 = zero4();
-#pragma unroll
-        for (int s = 0; s < 4; ++s) x1 = mfma(oa[s], ld8(&Hs[kcm(kr, 32 * s + 8 * kq, kHead)]), x1);
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          if (32 * s <= 16 * tw + 15)  // (dP o Gamma)[t][j] needs j <= t
-            y1 = mfma(pa[s], col8(S.Ks, 32 * s + 8 * kq, kr - li, lane), y1);
-        const int tr = 16 * tw + 4 * kq;
-        const float4 qv = col4_bf16(S.Qs, tr, kr - li, lane);
-        const float qa_[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = S.eg[tr + r];
-          adq[j][r] += e * x1[r] + y1[r];
-          gr[r] += e * qa_[r] * x1[r];               // inter-chunk output decay
-        }
+      // ---- gates (wave 0, after the previous value head's gate gradients)
+      if (wave == 0) {
+        if (jg > 0) dg_out(hv - 1, lane);
+        S.gam[lane] = gam_t;
+        S.bet[lane] = bet_t;
+        S.eg[lane] = eg_t;
+        S.ebw[lane] = ebw_t;
       }
-    }
-    {  // pass 1b: x4, y2 -> dk^
-      bf16x8 za[4], pta[2];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) za[s] = ld8(&S.rz.Z[trow * KP + 32 * s + 8 * kq]);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) pta[s] = ld8(&S.PmT[trow * BP + 32 * s + 8 * kq]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kr = 16 * (4 * kh + j) + li;
-        f32x4 x4 = zero4(), y2 = zero4();
-#pragma unroll
-        for (int s = 0; s < 4; ++s) x4 = mfma(za[s], ld8(&Hs[kcm(kr, 32 * s + 8 * kq, kHead)]), x4);
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          if (32 * s + 31 >= 16 * tw)  // (dP o Gamma)[i][t] needs i >= t
-            y2 = mfma(pta[s], col8(S.Qs, 32 * s + 8 * kq, kr - li, lane), y2);
-        const int tr = 16 * tw + 4 * kq;
-        const float4 kv = col4_bf16(S.Ks, tr, kr - li, lane);
-        const float ka_[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = tr + r;
-          const float e = S.eg[t], bt = S.bet[t];
-          adk[j][r] += y2[r] - bt * e * x4[r];
-          const float zk = -ka_[r] * x4[r];          // k^ . (T^T dW)
-          br[r] += e * zk;
-          gr[r] += bt * e * zk;
-        }
-      }
-    }
-    // Requests: the own rows of D (pass 3), then V and T, T^T, staged into
-    // LDS once Z and the P tiles are dead.
-    bf16x8 da[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      da[s] = __builtin_bit_cast(bf16x8, ld16_nt(Db + kcm(trow, 32 * s + 8 * kq, kChunk)));
-    // (last reads of D, T and T^T in this kernel: non-temporal)
-    const uint4 tst0 = ld16_nt(Tg + 8 * tid);          // T
-    const uint4 tst1 = ld16_nt(Tg + 8 * (tid + 512));  // T^T
-    {  // pass 2: x3 -> dW
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kr = 16 * (4 * kh + j) + li;
-        f32x4 x3 = zero4();
-#pragma unroll
-        for (int s = 0; s < 4; ++s) x3 = mfma(ea[s], ld8(&Hs[kcm(kr, 32 * s + 8 * kq, kHead)]), x3);
-        const int tr = 16 * tw + 4 * kq;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S.rw.dW[(tr + r) * KP + kr] = f2bf(-x3[r]);
-      }
-    }
-    {
-      // <h, dh'> over the whole state
-      float hd = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = tid + 512 * i;
-        hd += dot8u(*reinterpret_cast<const uint4*>(&Hs[8 * e]),
-                    *reinterpret_cast<const uint4*>(&Gs[8 * e]));
-      }
-      hd = wave_sum_uniform(hd);
-      if (lane == 0) S.hd_part[wave] = hd;
-    }
-    {  // pass 3: x2 -> dk^
-      float glp = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kr = 16 * (4 * kh + j) + li;
-        f32x4 x2 = zero4();
-#pragma unroll
-        for (int s = 0; s < 4; ++s) x2 = mfma(da[s], ld8(&Gs[kcm(kr, 32 * s + 8 * kq, kHead)]), x2);
-        const int tr = 16 * tw + 4 * kq;
-        const float4 kv = col4_bf16(S.Ks, tr, kr - li, lane);
-        const float ka_[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = tr + r;
-          const float bw = S.ebw[t];
-          adk[j][r] += bw * x2[r];
-          const float dc = ka_[r] * x2[r];
-          gr[r] -= bw * dc;                            // K_bwd decay, token side
-          glp += bw * dc;                              // K_bwd decay, gamma_L side
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        gr[r] = sum16_lane0(gr[r]);
-        br[r] = sum16_lane0(br[r]);
-      }
-      if (li == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          S.rowG[kh][16 * tw + 4 * kq + r] = gr[r];
-          S.rowB2[kh][16 * tw + 4 * kq + r] = br[r];
-        }
-      }
-      glp = wave_sum_uniform(glp);
-      if (lane == 0) S.gl_part[wave] = glp;
-    }
-    lds_barrier();  // every wave is done with Z, the P tiles, Hs and Gs, and dW is whole
-    // V rows from the pieces the waves read for dbeta (together the whole tile)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<uint2*>(&S.rz.V[trow * KP + 16 * (4 * kh + j) + 4 * kq]) = vr[j];
-    // T rows into Pm, T^T rows into PmT (chunk e = tid: row tid % 64, columns 8 (tid / 64) ..)
-    *reinterpret_cast<uint4*>(&S.Pm[(tid & 63) * BP + (tid >> 6) * 8]) = tst0;
-    *reinterpret_cast<uint4*>(&S.PmT[(tid & 63) * BP + (tid >> 6) * 8]) = tst1;
-    // (after the stores above, which wait for their own requests only)
-    if (jg + 1 < G) copy_states(hv + 1, wave, lane);
-    lds_barrier();
+      lds_barrier();
 
-    // ---- dT = dD (beta V)^T + dW (beta e^gamma K^)^T, strictly lower
-    //      (wave: row tile tw, col tiles kh, kh + 2)
-    {
-      bf16x8 wa[4];
+      // ---- dP = dO D^T (i >= j) and P = Gamma o Q~K^T: Pm = dP o Gamma (+ transpose);
+      //      F = dP o P row / column partial sums. Wave: row tile tw, col tiles kh, kh + 2.
+      {
+        float rowp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) wa[s] = ld8(&S.rw.dW[trow * KP + 32 * s + 8 * kq]);
-      f32x4 acc[2];
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const int jb = kh + 2 * q2;
+          const int j = 16 * jb + li;
+          float pv[4] = {0.f, 0.f, 0.f, 0.f};
+          if (jb <= tw) {
+            // dP tile and the Q~ K^T tile at the same place (formed here, per
+            // value head, rather than kept in registers across them)
+            f32x4 dp = zero4(), qk = zero4();
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        const int mb = kh + 2 * q2;
-        f32x4 a1 = zero4(), a2 = zero4();
-        if (mb <= tw) {
-          const int mrow = 16 * mb + li;
+            for (int s = 0; s < 4; ++s) {
+              dp = mfma(oa[s], dfr[q2][s], dp);
+              qk = mfma(ld8(&S.Qs[trow * KP + 32 * s + 8 * kq]),
+                        ld8(&S.Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), qk);
+            }
+            float colp = 0.f;
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            a1 = mfma(ea[s], ld8(&S.rz.V[mrow * KP + 32 * s + 8 * kq]), a1);
-            a2 = mfma(wa[s], ld8(&S.Ks[mrow * KP + 32 * s + 8 * kq]), a2);
+            for (int r = 0; r < 4; ++r) {
+              const int i = 16 * tw + 4 * kq + r;
+              if (i >= j) {
+                const float dpm = dp[r] * exp2_fast(S.gam[i] - S.gam[j]);
+                const float f = dpm * qk[r];
+                pv[r] = dpm;
+                rowp[r] += f;
+                colp += f;
+              }
+            }
+            colp = sum_over_rows(colp);
+            if (kq == 0) S.colF[wave][j] = colp;
+          } else if (kq == 0) {
+            S.colF[wave][j] = 0.f;  // every slot of the wave's column tiles is written
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Pm[(16 * tw + 4 * kq + r) * BP + j] = f2bf(pv[r]);
+          *reinterpret_cast<uint2*>(&PmT[j * BP + 16 * tw + 4 * kq]) =
+              pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rowp[r] = sum16_lane0(rowp[r]);
+        if (li == 0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S.rowF[kh][16 * tw + 4 * kq + r] = rowp[r];
+        }
+      }
+      // ---- Z = T^T dD (written [tok][v]); dV = diag(beta) Z; dbeta of U.
+      //      Wave: token columns of tile tw, value tiles 4 kh .. 4 kh + 3.
+      //      First every request of this wave is waited for: the Z operands are
+      //      the youngest, and the copies of h and dh', issued before them, are
+      //      then in LDS too (for the other waves after the barrier below).
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      {
+        float bp = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int vt = 4 * kh + j;
+          f32x4 z = zero4();
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            if (32 * s + 31 >= 16 * tw)  // T[m][t] needs m >= t
+              z = mfma(ddt[j][s], tt[s], z);
+          // z[r] = Z[t = trow][v = 16 vt + 4 kq + r]
+          const int vv = 16 * vt + 4 * kq;
+          *reinterpret_cast<uint2*>(&S.rz.Z[trow * KP + vv]) = pack4_bf16(z[0], z[1], z[2], z[3]);
+          if (trow_ok) {
+            const uint2 u = vr[j];
+            bp += bf2f(u.x & 0xffffu) * z[0] + bf2f(u.x >> 16) * z[1] +
+                  bf2f(u.y & 0xffffu) * z[2] + bf2f(u.y >> 16) * z[3];
+            const float bt = S.bet[trow];
+            *reinterpret_cast<uint2*>(dv + ((size_t)(t0 + trow) * HV + hv) * kHead + vv) =
+                pack4_bf16(bt * z[0], bt * z[1], bt * z[2], bt * z[3]);
           }
         }
-        const int m = 16 * mb + li;
+        bp = sum_over_rows(bp);
+        if (kq == 0) S.rowB[kh][trow] = bp;
+      }
+      // the own rows of dD (pass 2 and dT), requested as soon as the Z operands
+      // are dead, so that passes 1a and 1b cover their wait
+      bf16x8 ea[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        ea[s] = __builtin_bit_cast(bf16x8, ld16_nt(dDb + kcm(trow, 32 * s + 8 * kq, kChunk)));
+      lds_barrier();
+
+      // ---- key-column passes (columns 16 kt + li, kt = 4 kh .. 4 kh + 3), h from LDS:
+      //      pass 1: x1 = dO h^T, x4 = Z h^T (= -T^T dW),
+      //              y1 = (dP o Gamma) K^, y2 = (dP o Gamma)^T Q~
+      //      pass 2: x3 = dD h^T (= -dW), stored for dT
+      //      then dh' replaces h in LDS; pass 3: x2 = D dh'^T
+      float gr[4] = {0.f, 0.f, 0.f, 0.f}, br[4] = {0.f, 0.f, 0.f, 0.f};
+      {  // pass 1a: x1, y1 -> dq~
+        bf16x8 pa[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) pa[s] = ld8(&Pm[trow * BP + 32 * s + 8 * kq]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kr = 16 * (4 * kh + j) + li;
+          f32x4 x1 = zero4(), y1 = zero4();
+#pragma unroll
+          for (int s = 0; s < 4; ++s) x1 = mfma(oa[s], ld8(&Hs[kcm(kr, 32 * s + 8 * kq, kHead)]), x1);
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            if (32 * s <= 16 * tw + 15)  // (dP o Gamma)[t][j] needs j <= t
+              y1 = mfma(pa[s], col8(S.Ks, 32 * s + 8 * kq, kr - li, lane), y1);
+          const int tr = 16 * tw + 4 * kq;
+          const float4 qv = col4_bf16(S.Qs, tr, kr - li, lane);
+          const float qa_[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = S.eg[tr + r];
+            adq[j][r] += e * x1[r] + y1[r];
+            gr[r] += e * qa_[r] * x1[r];               // inter-chunk output decay
+          }
+        }
+      }
+      {  // pass 1b: x4, y2 -> dk^
+        bf16x8 za[4], pta[2];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) za[s] = ld8(&S.rz.Z[trow * KP + 32 * s + 8 * kq]);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) pta[s] = ld8(&PmT[trow * BP + 32 * s + 8 * kq]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kr = 16 * (4 * kh + j) + li;
+          f32x4 x4 = zero4(), y2 = zero4();
+#pragma unroll
+          for (int s = 0; s < 4; ++s) x4 = mfma(za[s], ld8(&Hs[kcm(kr, 32 * s + 8 * kq, kHead)]), x4);
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            if (32 * s + 31 >= 16 * tw)  // (dP o Gamma)[i][t] needs i >= t
+              y2 = mfma(pta[s], col8(S.Qs, 32 * s + 8 * kq, kr - li, lane), y2);
+          const int tr = 16 * tw + 4 * kq;
+          const float4 kv = col4_bf16(S.Ks, tr, kr - li, lane);
+          const float ka_[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = tr + r;
+            const float e = S.eg[t], bt = S.bet[t];
+            adk[j][r] += y2[r] - bt * e * x4[r];
+            const float zk = -ka_[r] * x4[r];          // k^ . (T^T dW)
+            br[r] += e * zk;
+            gr[r] += bt * e * zk;
+          }
+        }
+      }
+      // Requests: the own rows of D (pass 3), then V and T, T^T, staged into
+      // LDS once Z and the P tiles are dead.
+      bf16x8 da[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        da[s] = __builtin_bit_cast(bf16x8, ld16_nt(Db + kcm(trow, 32 * s + 8 * kq, kChunk)));
+      // (last reads of D, T and T^T in this kernel: non-temporal)
+      const uint4 tst0 = ld16_nt(Tg + 8 * tid);          // T
+      const uint4 tst1 = ld16_nt(Tg + 8 * (tid + 512));  // T^T
+      {  // pass 2: x3 -> dW
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kr = 16 * (4 * kh + j) + li;
+          f32x4 x3 = zero4();
+#pragma unroll
+          for (int s = 0; s < 4; ++s) x3 = mfma(ea[s], ld8(&Hs[kcm(kr, 32 * s + 8 * kq, kHead)]), x3);
+          const int tr = 16 * tw + 4 * kq;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dWs[(tr + r) * KP + kr] = f2bf(-x3[r]);
+        }
+      }
+      {
+        // <h, dh'> over the whole state
+        float hd = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = tid + 512 * i;
+          hd += dot8u(*reinterpret_cast<const uint4*>(&Hs[8 * e]),
+                      *reinterpret_cast<const uint4*>(&Gs[8 * e]));
+        }
+        hd = wave_sum_uniform(hd);
+        if (lane == 0) S.hd_part[wave] = hd;
+      }
+      {  // pass 3: x2 -> dk^
+        float glp = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kr = 16 * (4 * kh + j) + li;
+          f32x4 x2 = zero4();
+#pragma unroll
+          for (int s = 0; s < 4; ++s) x2 = mfma(da[s], ld8(&Gs[kcm(kr, 32 * s + 8 * kq, kHead)]), x2);
+          const int tr = 16 * tw + 4 * kq;
+          const float4 kv = col4_bf16(S.Ks, tr, kr - li, lane);
+          const float ka_[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = tr + r;
+            const float bw = S.ebw[t];
+            adk[j][r] += bw * x2[r];
+            const float dc = ka_[r] * x2[r];
+            gr[r] -= bw * dc;                            // K_bwd decay, token side
+            glp += bw * dc;                              // K_bwd decay, gamma_L side
+          }
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int i = 16 * tw + 4 * kq + r;
-          acc[q2][r] = i > m ? S.bet[m] * (a1[r] + S.eg[m] * a2[r]) : 0.f;
+          gr[r] = sum16_lane0(gr[r]);
+          br[r] = sum16_lane0(br[r]);
         }
-      }
-      lds_barrier();  // every wave has read V and dW
+        if (li == 0) {
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        const int m = 16 * (kh + 2 * q2) + li;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S.rz.dT[(16 * tw + 4 * kq + r) * BP + m] = f2bf(acc[q2][r]);
-      }
-    }
-    lds_barrier();
-
-    // ---- Y1 = dT T^T (i > j), stored transposed. Also the own rows of T^T
-    //      for dA, read here so that the barrier below orders them before M
-    //      overwrites the tile.
-    bf16x8 tta[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) tta[s] = ld8(&S.PmT[trow * BP + 32 * s + 8 * kq]);
-    {
-      bf16x8 ta[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) ta[s] = ld8(&S.rz.dT[trow * BP + 32 * s + 8 * kq]);
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        const int jb = kh + 2 * q2;
-        f32x4 acc = zero4();
-        if (jb <= tw) {
-#pragma unroll
-          for (int s = 0; s < 2; ++s)
-            acc = mfma(ta[s], ld8(&S.Pm[(16 * jb + li) * BP + 32 * s + 8 * kq]), acc);
+          for (int r = 0; r < 4; ++r) {
+            S.rowG[kh][16 * tw + 4 * kq + r] = gr[r];
+            S.rowB2[kh][16 * tw + 4 * kq + r] = br[r];
+          }
         }
-        const int j = 16 * jb + li;
-        float y[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = (16 * tw + 4 * kq + r) > j ? acc[r] : 0.f;
-        *reinterpret_cast<uint2*>(&S.rw.Y1T[j * BP + 16 * tw + 4 * kq]) =
-            pack4_bf16(y[0], y[1], y[2], y[3]);
+        glp = wave_sum_uniform(glp);
+        if (lane == 0) S.gl_part[wave] = glp;
       }
-    }
-    lds_barrier();
+      lds_barrier();  // every wave is done with Z, the P tiles, Hs and Gs, and dW is whole
+      // V rows from the pieces the waves read for dbeta (together the whole tile)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint2*>(&S.rz.V[trow * KP + 16 * (4 * kh + j) + 4 * kq]) = vr[j];
+      // T rows into Pm, T^T rows into PmT (chunk e = tid: row tid % 64, columns 8 (tid / 64) ..)
+      *reinterpret_cast<uint4*>(&Pm[(tid & 63) * BP + (tid >> 6) * 8]) = tst0;
+      *reinterpret_cast<uint4*>(&PmT[(tid & 63) * BP + (tid >> 6) * 8]) = tst1;
+      // (after the stores above, which wait for their own requests only)
+      if (jg + 1 < G) copy_states(c, hv + 1, wave, lane);
+      lds_barrier();
 
-    // ---- dA = -T^T Y1 (i > j); M = dA o beta_i Gamma -> Pm, PmT; E = dA o A sums; dbeta of A
-    {
-      float re[4] = {0.f, 0.f, 0.f, 0.f}, rb[4] = {0.f, 0.f, 0.f, 0.f};
+      // ---- dT = dD (beta V)^T + dW (beta e^gamma K^)^T, strictly lower
+      //      (wave: row tile tw, col tiles kh, kh + 2)
+      {
+        bf16x8 wa[4];
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        const int jb = kh + 2 * q2;
-        const int j = 16 * jb + li;
-        float mv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (jb <= tw) {
-          f32x4 acc = zero4(), kk = zero4();
+        for (int s = 0; s < 4; ++s) wa[s] = ld8(&dWs[trow * KP + 32 * s + 8 * kq]);
+        f32x4 acc[2];
 #pragma unroll
-          for (int s = 0; s < 2; ++s)
-            if (32 * s + 31 >= 16 * tw)
-              acc = mfma(tta[s], ld8(&S.rw.Y1T[(16 * jb + li) * BP + 32 * s + 8 * kq]), acc);
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const int mb = kh + 2 * q2;
+          f32x4 a1 = zero4(), a2 = zero4();
+          if (mb <= tw) {
+            const int mrow = 16 * mb + li;
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
-            kk = mfma(ld8(&S.Ks[trow * KP + 32 * s + 8 * kq]),
-                      ld8(&S.Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), kk);
-          float colp = 0.f;
+            for (int s = 0; s < 4; ++s) {
+              a1 = mfma(ea[s], ld8(&S.rz.V[mrow * KP + 32 * s + 8 * kq]), a1);
+              a2 = mfma(wa[s], ld8(&S.Ks[mrow * KP + 32 * s + 8 * kq]), a2);
+            }
+          }
+          const int m = 16 * mb + li;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 16 * tw + 4 * kq + r;
-            if (i > j) {
-              const float da_ = -acc[r];
-              const float dec = exp2_fast(S.gam[i] - S.gam[j]);
-              const float m_ = da_ * S.bet[i] * dec;
-              const float e_ = m_ * kk[r];
-              mv[r] = m_;
-              rb[r] += da_ * dec * kk[r];
-              re[r] += e_;
-              colp += e_;
-            }
+            acc[q2][r] = i > m ? S.bet[m] * (a1[r] + S.eg[m] * a2[r]) : 0.f;
           }
-          colp = sum_over_rows(colp);
-          if (kq == 0) S.colE[wave][j] = colp;
-        } else if (kq == 0) {
-          S.colE[wave][j] = 0.f;
+        }
+        lds_barrier();  // every wave has read V and dW
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const int m = 16 * (kh + 2 * q2) + li;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S.rz.dT[(16 * tw + 4 * kq + r) * BP + m] = f2bf(acc[q2][r]);
+        }
+      }
+      lds_barrier();
+
+      // ---- Y1 = dT T^T (i > j), stored transposed. Also the own rows of T^T
+      //      for dA, read here so that the barrier below orders them before M
+      //      overwrites the tile.
+      bf16x8 tta[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) tta[s] = ld8(&PmT[trow * BP + 32 * s + 8 * kq]);
+      {
+        bf16x8 ta[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) ta[s] = ld8(&S.rz.dT[trow * BP + 32 * s + 8 * kq]);
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const int jb = kh + 2 * q2;
+          f32x4 acc = zero4();
+          if (jb <= tw) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+              acc = mfma(ta[s], ld8(&Pm[(16 * jb + li) * BP + 32 * s + 8 * kq]), acc);
+          }
+          const int j = 16 * jb + li;
+          float y[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) y[r] = (16 * tw + 4 * kq + r) > j ? acc[r] : 0.f;
+          *reinterpret_cast<uint2*>(&Y1T[j * BP + 16 * tw + 4 * kq]) =
+              pack4_bf16(y[0], y[1], y[2], y[3]);
+        }
+      }
+      lds_barrier();
+
+      // ---- dA = -T^T Y1 (i > j); M = dA o beta_i Gamma -> Pm, PmT; E = dA o A sums; dbeta of A
+      {
+        float re[4] = {0.f, 0.f, 0.f, 0.f}, rb[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const int jb = kh + 2 * q2;
+          const int j = 16 * jb + li;
+          float mv[4] = {0.f, 0.f, 0.f, 0.f};
+          if (jb <= tw) {
+            f32x4 acc = zero4(), kk = zero4();
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+              if (32 * s + 31 >= 16 * tw)
+                acc = mfma(tta[s], ld8(&Y1T[(16 * jb + li) * BP + 32 * s + 8 * kq]), acc);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              kk = mfma(ld8(&S.Ks[trow * KP + 32 * s + 8 * kq]),
+                        ld8(&S.Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), kk);
+            float colp = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int i = 16 * tw + 4 * kq + r;
+              if (i > j) {
+                const float da_ = -acc[r];
+                const float dec = exp2_fast(S.gam[i] - S.gam[j]);
+                const float m_ = da_ * S.bet[i] * dec;
+                const float e_ = m_ * kk[r];
+                mv[r] = m_;
+                rb[r] += da_ * dec * kk[r];
+                re[r] += e_;
+                colp += e_;
+              }
+            }
+            colp = sum_over_rows(colp);
+            if (kq == 0) S.colE[wave][j] = colp;
+          } else if (kq == 0) {
+            S.colE[wave][j] = 0.f;
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Pm[(16 * tw + 4 * kq + r) * BP + j] = f2bf(mv[r]);
+          *reinterpret_cast<uint2*>(&PmT[j * BP + 16 * tw + 4 * kq]) =
+              pack4_bf16(mv[0], mv[1], mv[2], mv[3]);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S.Pm[(16 * tw + 4 * kq + r) * BP + j] = f2bf(mv[r]);
-        *reinterpret_cast<uint2*>(&S.PmT[j * BP + 16 * tw + 4 * kq]) =
-            pack4_bf16(mv[0], mv[1], mv[2], mv[3]);
+        for (int r = 0; r < 4; ++r) {
+          re[r] = sum16_lane0(re[r]);
+          rb[r] = sum16_lane0(rb[r]);
+        }
+        if (li == 0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            S.rowE[kh][16 * tw + 4 * kq + r] = re[r];
+            S.rowB3[kh][16 * tw + 4 * kq + r] = rb[r];
+          }
+        }
       }
+      lds_barrier();
+
+      // ---- dk^ += M K^ + M^T K^
+      {
+        bf16x8 ma[2], mta[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          ma[s] = ld8(&Pm[trow * BP + 32 * s + 8 * kq]);
+          mta[s] = ld8(&PmT[trow * BP + 32 * s + 8 * kq]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kr = 16 * (4 * kh + j) + li;
+          f32x4 acc = adk[j];
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const bf16x8 kc = col8(S.Ks, 32 * s + 8 * kq, kr - li, lane);
+            if (32 * s <= 16 * tw + 15) acc = mfma(ma[s], kc, acc);
+            if (32 * s + 31 >= 16 * tw) acc = mfma(mta[s], kc, acc);
+          }
+          adk[j] = acc;
+        }
+      }
+      // No barrier here: up to its first barrier the next value head writes
+      // only the gates (wave 0), which nothing after the barrier above reads;
+      // its later writes follow that first barrier, which every wave reaches
+      // after the reads above.
+    }
+
+    {
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      if ((tid >> 6) == 0) dg_out(h * G + G - 1, tid & 63);
+    }
+
+    // every wave is done with Hs, Gs, the P tiles and the dW / Y1^T region:
+    // the next item's copies go out now
+    lds_barrier();
+    prefetch(it + (int)gridDim.x);
+
+    // ---- L2-norm backward and scale: x^ . dx^ over all 128 columns (two halves).
+    //      x^ are the normalised rows every product above used (Ks; Qs holds
+    //      q~ = scale q^), so the raw rows are not read again. (LDS barriers
+    //      only, so that nothing here waits for the copies just issued.)
+    {
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      const int lane = tid & 63, wave = tid >> 6;
+      const int tw = wave & 3, kh = wave >> 2;
+      const int li = lane & 15, kq = lane >> 4;
+      float dq_[4] = {0.f, 0.f, 0.f, 0.f}, dk_[4] = {0.f, 0.f, 0.f, 0.f};
+      float qh[4][4], kh_[4][4];  // q^, k^ of the thread's 16 elements
+      const float inv_scale = 1.f / scale;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * tw + 4 * kq + r;
+          const int kc = 16 * (4 * kh + j) + li;
+          // (rows past the chunk's end hold zeros)
+          const float qs = bf2f(S.Qs[t * KP + kc]), kv = bf2f(S.Ks[t * KP + kc]);
+          qh[j][r] = qs * inv_scale;
+          kh_[j][r] = kv;
+          dq_[r] += qs * adq[j][r];
+          dk_[r] += kv * adk[j][r];
+        }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        re[r] = sum16_lane0(re[r]);
-        rb[r] = sum16_lane0(rb[r]);
+        dq_[r] = sum16_lane0(dq_[r]);
+        dk_[r] = sum16_lane0(dk_[r]);
       }
       if (li == 0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          S.rowE[kh][16 * tw + 4 * kq + r] = re[r];
-          S.rowB3[kh][16 * tw + 4 * kq + r] = rb[r];
+          S.dot_q[kh][16 * tw + 4 * kq + r] = dq_[r];
+          S.dot_k[kh][16 * tw + 4 * kq + r] = dk_[r];
         }
       }
+      lds_barrier();
+      // (every LDS read of this step before its first write: in that order the
+      // compiler places no wait for the copies just issued inside the step)
+      float dotq[4], dotk[4], iq[4], ik[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tw + 4 * kq + r;
+        dotq[r] = S.dot_q[0][t] + S.dot_q[1][t];
+        dotk[r] = S.dot_k[0][t] + S.dot_k[1][t];
+        iq[r] = S.inv_q[t];
+        ik[r] = S.inv_k[t];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * tw + 4 * kq + r;
+          const int kc = 16 * (4 * kh + j) + li;
+          const float dqh = scale * adq[j][r];
+          S.rz.dq[t * KP + kc] = f2bf((dqh - qh[j][r] * dotq[r]) * iq[r]);
+          S.Ks[t * KP + kc] = f2bf((adk[j][r] - kh_[j][r] * dotk[r]) * ik[r]);
+        }
     }
     lds_barrier();
-
-    // ---- dk^ += M K^ + M^T K^
     {
-      bf16x8 ma[2], mta[2];
+      // rows tid / 16 and tid / 16 + 32, columns 8 (tid % 16) ..
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      const int sg = tid & 15;
+      uint4 xq[2], xk[2];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        ma[s] = ld8(&S.Pm[trow * BP + 32 * s + 8 * kq]);
-        mta[s] = ld8(&S.PmT[trow * BP + 32 * s + 8 * kq]);
+      for (int j = 0; j < 2; ++j) {
+        const int t = (tid >> 4) + 32 * j;
+        xq[j] = *reinterpret_cast<const uint4*>(&S.rz.dq[t * KP + sg * 8]);
+        xk[j] = *reinterpret_cast<const uint4*>(&S.Ks[t * KP + sg * 8]);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kr = 16 * (4 * kh + j) + li;
-        f32x4 acc = adk[j];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const bf16x8 kc = col8(S.Ks, 32 * s + 8 * kq, kr - li, lane);
-          if (32 * s <= 16 * tw + 15) acc = mfma(ma[s], kc, acc);
-          if (32 * s + 31 >= 16 * tw) acc = mfma(mta[s], kc, acc);
+      for (int j = 0; j < 2; ++j) {
+        const int t = (tid >> 4) + 32 * j;
+        if (t < L) {
+          const size_t off = ((size_t)(t0 + t) * H + h) * kHead + sg * 8;
+          *reinterpret_cast<uint4*>(dq + off) = xq[j];
+          *reinterpret_cast<uint4*>(dk + off) = xk[j];
         }
-        adk[j] = acc;
       }
-    }
-    // No barrier here: up to its first barrier the next value head writes
-    // only the gates (wave 0), which nothing after the barrier above reads;
-    // its later writes follow that first barrier, which every wave reaches
-    // after the reads above.
-  }
-
-  {
-    int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));
-    if ((tid >> 6) == 0) dg_out(h * G + G - 1, tid & 63);
-  }
-
-  // ---- L2-norm backward and scale: x^ . dx^ over all 128 columns (two halves).
-  //      x^ are the normalised rows every product above used (Ks; Qs holds
-  //      q~ = scale q^), so the raw rows are not read again.
-  lds_barrier();
-  {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int tw = wave & 3, kh = wave >> 2;
-    const int li = lane & 15, kq = lane >> 4;
-    float dq_[4] = {0.f, 0.f, 0.f, 0.f}, dk_[4] = {0.f, 0.f, 0.f, 0.f};
-    float qh[4][4], kh_[4][4];  // q^, k^ of the thread's 16 elements
-    const float inv_scale = 1.f / scale;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * tw + 4 * kq + r;
-        const int kc = 16 * (4 * kh + j) + li;
-        // (rows past the chunk's end hold zeros)
-        const float qs = bf2f(S.Qs[t * KP + kc]), kv = bf2f(S.Ks[t * KP + kc]);
-        qh[j][r] = qs * inv_scale;
-        kh_[j][r] = kv;
-        dq_[r] += qs * adq[j][r];
-        dk_[r] += kv * adk[j][r];
-      }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      dq_[r] = sum16_lane0(dq_[r]);
-      dk_[r] = sum16_lane0(dk_[r]);
-    }
-    if (li == 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        S.dot_q[kh][16 * tw + 4 * kq + r] = dq_[r];
-        S.dot_k[kh][16 * tw + 4 * kq + r] = dk_[r];
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * tw + 4 * kq + r;
-        const int kc = 16 * (4 * kh + j) + li;
-        const float dotq = S.dot_q[0][t] + S.dot_q[1][t];
-        const float dotk = S.dot_k[0][t] + S.dot_k[1][t];
-        const float dqh = scale * adq[j][r];
-        Hs[t * KP + kc] = f2bf((dqh - qh[j][r] * dotq) * S.inv_q[t]);
-        S.Ks[t * KP + kc] = f2bf((adk[j][r] - kh_[j][r] * dotk) * S.inv_k[t]);
-      }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < 64 * 16; e += 512) {
-    const int t = e >> 4, sg = e & 15;
-    if (t < L) {
-      const size_t off = ((size_t)(t0 + t) * H + h) * kHead + sg * 8;
-      *reinterpret_cast<uint4*>(dq + off) = *reinterpret_cast<const uint4*>(&Hs[t * KP + sg * 8]);
-      *reinterpret_cast<uint4*>(dk + off) = *reinterpret_cast<const uint4*>(&S.Ks[t * KP + sg * 8]);
     }
   }
 }
@@ -1085,7 +1157,16 @@ hipError_t launch_bwd_chunk(const ChunkInfo* table, int NC, int H, int HV, float
                             const BwdBufs& bufs, const uint16_t* dO,
                             uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dg, float* dbeta,
                             hipStream_t stream) {
-  hipLaunchKernelGGL(bwd_chunk_kernel, dim3(NC, H), dim3(512), 0, stream, table, NC, H, HV, scale,
+  // one workgroup per CU (its LDS allows no second one), each looping over
+  // the items c H + h, c H + h + grid, ...
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const long items = (long)NC * H;
+  if (items <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::max(1L, std::min(items, (long)cus));
+  hipLaunchKernelGGL(bwd_chunk_kernel, dim3(grid), dim3(512), 0, stream, table, NC, H, HV, scale,
                      q, k, v, g, beta, saved, Tmat, gE, gB, bufs, dO, dq, dk, dv, dg, dbeta);
   return hipGetLastError();
 }
