@@ -218,18 +218,20 @@ GDN_API size_t gdn_chunk_bwd_recompute_workspace_size(const gdn_problem* p) {
   return recompute_saved_offset(p, nc) + gdn_chunk_saved_size(p);
 }
 
-// Records events[2 i] / events[2 i + 1] around stage i when events are given.
+// Records events[2 i] / events[2 i + 1] around stage i when events are given
+// (a NULL handle is skipped).
 struct StageClock {
   void* const* ev;
   int n;
   hipStream_t s;
   template <typename F>
   hipError_t run(F&& launch) {
-    if (ev && hipEventRecord(reinterpret_cast<hipEvent_t>(ev[2 * n]), s) != hipSuccess)
+    if (ev && ev[2 * n] && hipEventRecord(reinterpret_cast<hipEvent_t>(ev[2 * n]), s) != hipSuccess)
       return hipErrorUnknown;
     hipError_t e = launch();
     if (e != hipSuccess) return e;
-    if (ev && hipEventRecord(reinterpret_cast<hipEvent_t>(ev[2 * n + 1]), s) != hipSuccess)
+    if (ev && ev[2 * n + 1] &&
+        hipEventRecord(reinterpret_cast<hipEvent_t>(ev[2 * n + 1]), s) != hipSuccess)
       return hipErrorUnknown;
     ++n;
     return hipSuccess;

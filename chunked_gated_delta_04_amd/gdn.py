@@ -251,8 +251,8 @@ def gdn_stage_name(op, stage):
 
 def gdn_chunk_fwd_timed(problem, q, k, v, g, beta, h0, o, hT, saved, workspace, events,
                         stream=None):
-    """gdn_chunk_fwd recording events (a ctypes array of 2*GDN_MAX_STAGES hipEvent_t)
-    around each stage. Returns the number of stages launched."""
+    """gdn_chunk_fwd recording events (a ctypes array of 2*GDN_MAX_STAGES hipEvent_t;
+    NULL entries are skipped) around each stage. Returns the number of stages launched."""
     bf, f32 = torch.bfloat16, torch.float32
     _check_saved(problem, saved, "gdn_chunk_fwd_timed")
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0

@@ -272,8 +272,10 @@ int gdn_chunk_transition(const gdn_problem* p,
  * by the caller (hipEventCreate). The library records events[2 i] before and
  * events[2 i + 1] after launching stage i on `stream` and stores the number of
  * stages it launched in *n_stages; gdn_stage_name(op, i) names stage i
- * (op 0: forward, 1: backward; "" past the last stage). Results are the same
- * bits as the untimed calls. GDN_ERR_NULL if events or n_stages is NULL. */
+ * (op 0: forward, 1: backward; "" past the last stage). A NULL handle in
+ * `events` is not recorded, so that a caller can time one stage without
+ * markers between the others. Results are the same bits as the untimed calls.
+ * GDN_ERR_NULL if events or n_stages is NULL. */
 #define GDN_MAX_STAGES 8
 int gdn_chunk_fwd_timed(const gdn_problem* p,
                         const uint16_t* q, const uint16_t* k, const uint16_t* v,
