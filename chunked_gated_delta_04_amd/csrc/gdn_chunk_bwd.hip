@@ -145,8 +145,14 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
     const uint16_t* Kbb = prep.Kn + kblk * 8192;  // K^ [tok][k]
     const uint16_t* QgT = prep.Qn + kblk * 8192;  // Q~^T [k][tok]
     const uint16_t* WT = prep.W + blk * 8192;     // W^T [k][tok]
+    // P^T's tiles below the diagonal are not stored: those pieces come from
+    // past the end of a range-checked buffer, as zeros
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(PTb), 0, kChunk * kChunk * 2, kBufferWord3);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) x.pa[s] = ld8(PTb + kcm(16 * wave + li, 32 * s + 8 * kq, 64));
+    for (int s = 0; s < 2; ++s)
+      x.pa[s] = ld8_buf(rp, 2 * s + (kq >> 1) >= wave ? kcm(16 * wave + li, 32 * s + 8 * kq, 64) * 2
+                                                     : kChunk * kChunk * 2);
 #pragma unroll
     for (int s = 0; s < 4; ++s) x.ka[s] = ld8(Kbb + kcm(16 * wave + li, 32 * s + 8 * kq, 64));
 #pragma unroll
@@ -631,7 +637,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       }
 
       // requests for the Z phase: T^T rows of this wave's tokens, dD^T rows, v rows
-      // (token blocks s with 32 s + 31 < 16 tw meet only zeros of T)
+      // (token blocks s with 32 s + 31 < 16 tw meet only zeros of T; T^T's
+      // tiles below the diagonal are not stored, so those pieces are zeros
+      // from past the end of the buffer too)
       const __amdgpu_buffer_rsrc_t rTT = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint16_t*>(Tg) + 4096, 0, kTBytes, kBufferWord3);
       const __amdgpu_buffer_rsrc_t rDDT = __builtin_amdgcn_make_buffer_rsrc(
@@ -640,7 +648,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       uint2 vr[4];
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        tt[s] = ld8_buf(rTT, 32 * s + 31 >= 16 * tw ? kcm(trow, 32 * s + 8 * kq, 64) * 2 : kTBytes);
+        tt[s] = ld8_buf(rTT, 2 * s + (kq >> 1) >= tw ? kcm(trow, 32 * s + 8 * kq, 64) * 2 : kTBytes);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int vt = 4 * kh + j;
@@ -815,9 +823,15 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         da[s] = __builtin_bit_cast(bf16x8, ld16_nt(Db + kcm(trow, 32 * s + 8 * kq, kChunk)));
-      // (last reads of D, T and T^T in this kernel: non-temporal)
-      const uint4 tst0 = ld16_nt(Tg + 8 * tid);          // T
-      const uint4 tst1 = ld16_nt(Tg + 8 * (tid + 512));  // T^T
+      // (last reads of D, T and T^T in this kernel: non-temporal; the chunks of
+      // the zero tiles, which are not stored, come from past the end of a
+      // range-checked buffer as zeros: chunk tid is row tid % 64, columns
+      // 8 (tid / 64) ..)
+      const __amdgpu_buffer_rsrc_t rT = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(Tg), 0, 2 * kTBytes, kBufferWord3);
+      const int tcb = tid >> 7, trb = (tid & 63) >> 4;  // column and row tile of the chunk
+      const uint4 tst0 = load_b128_nt(rT, tcb <= trb ? 16 * tid : 2 * kTBytes);             // T
+      const uint4 tst1 = load_b128_nt(rT, tcb >= trb ? kTBytes + 16 * tid : 2 * kTBytes);   // T^T
       {  // pass 2: x3 -> dW
 #pragma unroll
         for (int j = 0; j < 4; ++j) {

@@ -157,8 +157,14 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
       if constexpr (kOut) x.qa[s] = ld8(Qb + kcm(16 * wave + li, 32 * s + 8 * kq, 64));
     }
     if constexpr (kOut) {
+      // P's tiles above the diagonal are not stored: those pieces come from
+      // past the end of a range-checked buffer, as zeros
+      const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(Pb), 0, kChunk * kChunk * 2, kBufferWord3);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) x.pa[s] = ld8(Pb + kcm(16 * wave + li, 32 * s + 8 * kq, 64));
+      for (int s = 0; s < 2; ++s)
+        x.pa[s] = ld8_buf(rp, 2 * s + (kq >> 1) <= wave ? kcm(16 * wave + li, 32 * s + 8 * kq, 64) * 2
+                                                       : kChunk * kChunk * 2);
     }
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)

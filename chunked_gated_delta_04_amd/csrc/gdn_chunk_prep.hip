@@ -315,12 +315,16 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
           const int j = 16 * jb + 4 * kq + r;
           pv[r] = i >= j ? exp2_fast(gam[i] - gam[j]) * acc[r] : 0.f;
         }
-        const uint2 pk = pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
-        st8_nt(fo.P + blk * (64 * 64) + kcm(i, 16 * jb + 4 * kq, 64), pk);
-        if (kB) {  // P^T[j][i .. i + 7]: columns of the tile, 16-byte pieces from 32 lanes
-          const uint4 x = tile_transpose(Xp[wave], pk, lane);
-          if (kq < 2)
-            st16_nt(bo.P + blk * (64 * 64) + kcm(16 * jb + li, 16 * ib + 8 * kq, 64), x);
+        // (the tiles above the diagonal are zero and are not stored: their
+        // readers take zeros from past the end of a range-checked buffer)
+        if (jb <= ib) {
+          const uint2 pk = pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
+          st8_nt(fo.P + blk * (64 * 64) + kcm(i, 16 * jb + 4 * kq, 64), pk);
+          if (kB) {  // P^T[j][i .. i + 7]: columns of the tile, 16-byte pieces from 32 lanes
+            const uint4 x = tile_transpose(Xp[wave], pk, lane);
+            if (kq < 2)
+              st16_nt(bo.P + blk * (64 * 64) + kcm(16 * jb + li, 16 * ib + 8 * kq, 64), x);
+          }
         }
       }
     }
@@ -330,7 +334,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     invert_unit_lower_64(Ts, Xs, tid);
 
     // T and T^T in bf16 for the backward's gradient pass: chunk (kc, r) of each
-    // holds row r, columns 8 kc .. 8 kc + 7
+    // holds row r, columns 8 kc .. 8 kc + 7 (the chunks of their zero 16 x 16
+    // tiles, above the diagonal of T and below that of T^T, are not stored)
     if (kB) {
       uint16_t* Tg = bo.T + blk * 8192;
 #pragma unroll
@@ -346,8 +351,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
           ow[u] = pk2(Ts[r * FP + ja], Ts[r * FP + ja + 1]);
           tw4[u] = pk2(Ts[ja * FP + r], Ts[(ja + 1) * FP + r]);
         }
-        st16_nt(Tg + kcm(r, 8 * kc, 64), o4);
-        st16_nt(Tg + 4096 + kcm(r, 8 * kc, 64), t4);
+        if ((kc >> 1) <= (r >> 4)) st16_nt(Tg + kcm(r, 8 * kc, 64), o4);
+        if ((kc >> 1) >= (r >> 4)) st16_nt(Tg + 4096 + kcm(r, 8 * kc, 64), t4);
       }
     }
 
