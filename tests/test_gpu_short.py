@@ -53,3 +53,31 @@ def test_many_short_sequences_forward_and_backward(n):
     assert empty
     assert torch.equal(hT[empty].cpu(), inp["h0"][empty])
     assert torch.equal(gr["dh0"][empty].cpu(), torch.zeros_like(inp["h0"][empty]))
+
+
+def test_three_value_heads_per_key_head_over_many_items():
+    """An odd number of value heads per key head (2 key, 6 value heads) over
+    more (chunk, key head) items than the gradient pass has workgroups, so that
+    workgroups take several items in turn, against the fp64 oracle."""
+    gen = np.random.default_rng(9)
+    lens = [int(x) for x in gen.integers(0, 41, size=120)]
+    H, HV = 2, 6
+    items = (sum(lens) // 64 + len(lens)) * H
+    _say(f"head groups of 3: {len(lens)} sequences, {sum(lens)} tokens, H={H} HV={HV}, "
+         f"{items} items")
+    assert items > 256
+    inp = synth.chunk_inputs(lens, H, HV, seed=33, h0_std=0.1, with_do=True)
+    d = to_dev(inp)
+    host = inp["cu_seqlens"].to(torch.int32)
+    o, hT, saved = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                                 h0=d["h0"], cu_seqlens_host=host, save_for_backward=True)
+    gr = gdn.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], saved,
+                       d["do"], cu_seqlens_host=host, want_dh0=True)
+    torch.cuda.synchronize()
+    o_ref, hT_ref = oracle_forward(inp)
+    assert_bar("o", f64(o), o_ref)
+    assert_bar("hT", f64(hT), hT_ref)
+    ref = oracle_backward(inp)
+    for name in ("dq", "dk", "dv", "dbeta", "dh0"):
+        assert_bar(name, f64(gr[name]), ref[name])
+    assert_dg_bar("dg", f64(gr["dg"]), ref["dg"])
