@@ -127,11 +127,15 @@ __device__ __forceinline__ void lower_tile(int t, int& ib, int& jb) {
 }
 }  // namespace
 
+constexpr int kPrepThreads = 512;               // 8 waves per workgroup
+constexpr int kPrepWaves = kPrepThreads / 64;
+constexpr int kRowThreads = kPrepThreads / 64;  // threads per token row, 2 x 16 bytes each
+
 // Writes the forward scan's operands to fo and, with kB (a forward that saves
 // for a backward), the backward's to bo, so that the backward does not form
 // them again.
 template <bool kB>
-__global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
+__global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
     const ChunkInfo* __restrict__ table, int NC, int H, int HV, float scale,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ g,
@@ -149,24 +153,24 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
   // gates of the value head; gam is the cumulative log-decay in base 2
   __shared__ __align__(16) float gam[64], bet[64], fw[64];
   __shared__ float Xs[3 * 256];  // solve scratch
-  __shared__ __align__(16) uint16_t Xp[4][16 * XPP];  // per-wave 16 x 16 transpose tile
+  __shared__ __align__(16) uint16_t Xp[kPrepWaves][16 * XPP];  // per-wave 16 x 16 transpose tile
 
-  // A value head's own inputs - its v rows (thread: row tid / 4, 32 columns)
+  // A value head's own inputs - its v rows (thread: row tid / 8, 16 columns)
   // and gates (every wave requests them; wave 0 uses them) - through
   // range-checked buffer loads: rows at or past the chunk's end read as zeros,
   // and a zero range (live = false) moves no data. Requested one value head
   // ahead, before the current head's stores: waiting for a load also waits
   // for every store issued before it.
   const int G = HV / H;
-  uint4 vx[4];
+  uint4 vx[2];
   float gq, bq;
   auto request = [&](int hv_, bool live) {
     const int n = live ? L : 0;
-    const int vr0 = tid >> 2, vsg0 = (tid & 3) * 4, lane = tid & 63;
+    const int vr0 = tid / kRowThreads, vsg0 = (tid % kRowThreads) * 2, lane = tid & 63;
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(v) + ((size_t)t0 * HV + hv_) * kHead, 0, n * HV * kHead * 2, kBufferWord3);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vx[j] = load_b128(rv, (vr0 * HV * kHead + (vsg0 + j) * 8) * 2);
+    for (int j = 0; j < 2; ++j) vx[j] = load_b128(rv, (vr0 * HV * kHead + (vsg0 + j) * 8) * 2);
     const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(g) + (size_t)t0 * HV + hv_, 0, n * HV * 4, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
@@ -175,26 +179,26 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     bq = load_f32(rb, lane * HV * 4);
   };
 
-  // ---- 1. load and L2-normalise q, k rows (thread: row tid/4, 32 columns);
+  // ---- 1. load and L2-normalise q, k rows (thread: row tid / 8, 16 columns);
   //      one division per row, then products with the reciprocal. The first
   //      value head's requests follow the q, k rows, so the norms wait only
   //      for those.
   {
-    const int r = tid >> 2, sg0 = (tid & 3) * 4;
-    uint4 kr[4], qr[4];
+    const int r = tid / kRowThreads, sg0 = (tid % kRowThreads) * 2;
+    uint4 kr[2], qr[2];
     float sk = 0.f, sq = 0.f;
     const __amdgpu_buffer_rsrc_t krng = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(k) + ((size_t)t0 * H + h) * kHead, 0, L * H * kHead * 2, kBufferWord3);
     const __amdgpu_buffer_rsrc_t qrng = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(q) + ((size_t)t0 * H + h) * kHead, 0, L * H * kHead * 2, kBufferWord3);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       kr[j] = load_b128(krng, (r * H * kHead + (sg0 + j) * 8) * 2);
       qr[j] = load_b128(qrng, (r * H * kHead + (sg0 + j) * 8) * 2);
     }
     request(h * G, true);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[j]);
       const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qr[j]);
 #pragma unroll
@@ -205,11 +209,11 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
         sq += b0 * b0 + b1 * b1;
       }
     }
-    sk = group_sum<4>(sk);
-    sq = group_sum<4>(sq);
+    sk = group_sum<kRowThreads>(sk);
+    sq = group_sum<kRowThreads>(sq);
     const float rk = 1.f / sqrtf(sk + kNormEps), rq = scale / sqrtf(sq + kNormEps);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[j]);
       const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qr[j]);
       uint4 ko, qo;
@@ -240,8 +244,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     // ---- 2. gates: gamma = inclusive cumsum of g inside the chunk (kept in
     //      base 2); the value rows go to LDS as they are. This head's v rows
     //      and gates were requested before; the next head's are requested now.
-    const int vr0 = tid >> 2, vsg0 = (tid & 3) * 4;
-    const uint4 vc0 = vx[0], vc1 = vx[1], vc2 = vx[2], vc3 = vx[3];
+    const int vr0 = tid / kRowThreads, vsg0 = (tid % kRowThreads) * 2;
+    const uint4 vc0 = vx[0], vc1 = vx[1];
     float gv = gq;
     const float bv = bq;
     request(min(hv + 1, h * G + G - 1), jg + 1 < G);
@@ -269,14 +273,12 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     }
     *reinterpret_cast<uint4*>(&Vs[vr0 * KP + (vsg0 + 0) * 8]) = vc0;
     *reinterpret_cast<uint4*>(&Vs[vr0 * KP + (vsg0 + 1) * 8]) = vc1;
-    *reinterpret_cast<uint4*>(&Vs[vr0 * KP + (vsg0 + 2) * 8]) = vc2;
-    *reinterpret_cast<uint4*>(&Vs[vr0 * KP + (vsg0 + 3) * 8]) = vc3;
     __syncthreads();
 
     // ---- 3. A (fp32, LDS: 10 lower tiles, 6 zero upper tiles) and P (bf16,
     //      global: 16 tiles), 32 jobs over the 4 waves. A tile of P also goes
     //      to the backward's P^T through the wave's LDS transpose tile.
-    for (int job = wave; job < 32; job += 4) {
+    for (int job = wave; job < 32; job += kPrepWaves) {
       if (job < 10) {
         int ib, jb;
         lower_tile(job, ib, jb);
@@ -339,8 +341,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     if (kB) {
       uint16_t* Tg = bo.T + blk * 8192;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int e = tid + 256 * i;
+      for (int i = 0; i < 512 / kPrepThreads; ++i) {
+        const int e = tid + kPrepThreads * i;
         const int kc = e >> 6, r = e & 63;
         uint4 o4, t4;
         uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
@@ -360,7 +362,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     //      T becomes an MFMA operand, K^ is read by columns from its row tile.
     //      32 tiles of 16 x 16 over 4 waves, contraction over the chunk; a
     //      tile also goes to the backward's W^T through the LDS transpose tile.
-    for (int tt = wave; tt < 32; tt += 4) {
+    for (int tt = wave; tt < 32; tt += kPrepWaves) {
       // C = K^T (T')^T: C[4kq+r][li] = W[t = 16 tb + li][k = 16 db + 4kq + r]
       const int db = tt >> 2, tb = tt & 3;
       f32x4 acc = zero4();
@@ -382,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     {
       // ---- 6. U = (T diag(beta)) V, written as U^T [v][tok]
       uint16_t* Ub = fo.U + blk * 8192;
-            for (int tt = wave; tt < 32; tt += 4) {
+            for (int tt = wave; tt < 32; tt += kPrepWaves) {
         // C = T' V: C[4kq+r][li] = U[t = 16 tb + 4kq + r][v = 16 vb + li] -> U^T[v][t..t+3]
         const int tb = tt >> 3, vb = tt & 7;
         f32x4 acc = zero4();
@@ -408,15 +410,15 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     const int li = lane & 15, kq = lane >> 4;
     const size_t kblk = (size_t)h * NC + c;
     auto rows_out = [&](const uint16_t* src, uint16_t* dst) {
-      for (int e = tid; e < 64 * 16; e += 256) {
+      for (int e = tid; e < 64 * 16; e += kPrepThreads) {
         const int sg = e >> 6, t = e & 63;
         st16_nt(dst + kcm(t, sg * 8, 64), *reinterpret_cast<const uint4*>(&src[t * KP + sg * 8]));
       }
     };
     auto cols_out = [&](const uint16_t* src, uint16_t* dst) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e0 = 256 * i + 64 * wave;  // wave-uniform
+      for (int i = 0; i < 1024 / kPrepThreads; ++i) {
+        const int e0 = kPrepThreads * i + 64 * wave;  // wave-uniform
         const int tg = e0 >> 7, d0 = (e0 & 127) + 16 * kq;
         st16_nt(dst + kcm(d0 + li, 8 * tg, 128), lds_col8(src, KP, 8 * tg, d0, lane));
       }
@@ -444,11 +446,11 @@ hipError_t launch_chunk_prep(PrepMode mode, const ChunkInfo* table, int NC, int 
   const dim3 grid(NC, H);
   switch (mode) {
     case PrepMode::kForward:
-      hipLaunchKernelGGL((chunk_prep_kernel<false>), grid, dim3(256), 0, stream, table, NC, H, HV,
+      hipLaunchKernelGGL((chunk_prep_kernel<false>), grid, dim3(kPrepThreads), 0, stream, table, NC, H, HV,
                          scale, q, k, v, g, beta, fwd_out, bwd_out);
       break;
     case PrepMode::kBoth:
-      hipLaunchKernelGGL((chunk_prep_kernel<true>), grid, dim3(256), 0, stream, table, NC, H, HV,
+      hipLaunchKernelGGL((chunk_prep_kernel<true>), grid, dim3(kPrepThreads), 0, stream, table, NC, H, HV,
                          scale, q, k, v, g, beta, fwd_out, bwd_out);
       break;
   }
