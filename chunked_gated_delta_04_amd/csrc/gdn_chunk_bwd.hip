@@ -114,7 +114,8 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
   // This workgroup's share of a chunk's operand lines for the L2 warm-up: the
   // value head's W^T, P^T, gate-factor and dO lines (324) split over its value
   // blocks, the key head's Q~^T and K^ lines (256) over the workgroups of all its
-  // value heads. Lanes past the share touch a line of the share again; dO rows
+  // value heads. Lanes past the share all touch its first line (one request per
+  // wave instruction, the lanes' addresses being the same); dO rows
   // past the chunk's end touch its last row.
   const int vlines = (324 + NVB - 1) / NVB;
   const int kshares = NVB * prep.G, kpos = (hv % prep.G) * NVB + vb;
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
   auto warm_line = [&](int c) -> const void* {
     const size_t blk = (size_t)hv * NC + c;
     const size_t kblk = (size_t)(hv / prep.G) * NC + c;
-    const int i = tid < vlines + klines ? tid : tid % vlines;
+    const int i = tid < vlines + klines ? tid : 0;
     if (i < vlines) {
       const int l = min(vb * vlines + i, 323);
       if (l < 128) return prep.W + blk * 8192 + l * kLineElems16;

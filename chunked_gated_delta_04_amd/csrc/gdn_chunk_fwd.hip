@@ -118,7 +118,8 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
   // This workgroup's share of a chunk's operand lines for the L2 warm-up: the
   // value head's W, U^T, P and gate-factor lines (324) split over its value
   // blocks, the key head's Q~ and K^T lines (256) over the workgroups of all its
-  // value heads. Lanes past the share touch a line of the share again.
+  // value heads. Lanes past the share all touch its first line (one request per
+  // wave instruction, the lanes' addresses being the same).
   const int vshare = (kTrans ? 2 * NVB : NVB);
   const int vpos = kTrans ? slot % NVBL : vb;
   const int vlines = (324 + vshare - 1) / vshare;
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
   auto warm_line = [&](int c) -> const void* {
     const size_t blk = (size_t)hv * NC + c;
     const size_t kblk = (size_t)(hv / prep.G) * NC + c;
-    int i = tid < vlines + klines ? tid : tid % vlines;
+    int i = tid < vlines + klines ? tid : 0;
     if (i < vlines) {
       const int l = min(vpos * vlines + i, 323);
       if (l < 128) return prep.W + blk * 8192 + l * kLineElems16;
