@@ -276,6 +276,7 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
       const __amdgpu_buffer_rsrc_t orng =
           __builtin_amdgcn_make_buffer_rsrc(o + ((size_t)t0 * HV + hv) * kHead, 0,
                                             len * HV * kHead * 2, kBufferWord3);
+      uint2 pk[VT];
 #pragma unroll
       for (int vt = 0; vt < VT; ++vt) {
         bf16x8 db[2];
@@ -285,9 +286,21 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
         f32x4 acc = mfma(db[0], cur.pa[0], oq[vt]);
         if (wave >= 2) acc = mfma(db[1], cur.pa[1], acc);
         // acc[r] = O[t = t0 + 16 w + li][v = v0 + 16 vt + 4 kq + r]
-        store_b64(pack4_bf16(acc[0], acc[1], acc[2], acc[3]), orng,
-                  (tl * HV * kHead + v0 + 16 * vt + 4 * kq) * 2);
+        pk[vt] = pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
       }
+      // Lanes 16 kq + li and 16 (kq ^ 1) + li swap one of their two pieces: an
+      // even kq keeps its vt = 0 piece and takes its partner's, an odd kq
+      // keeps its vt = 1 piece and takes its partner's, so that each lane holds
+      // 8 consecutive columns of its token's row and a wave's 16 rows x 64
+      // bytes go out in one 16-byte store (one request per row, not two).
+      static_assert(VT == 2, "two 16-column value tiles per block");
+      const bool ev = (kq & 1) == 0;
+      const uint2 send = ev ? pk[1] : pk[0];
+      const uint2 recv = make_uint2(__shfl_xor(send.x, 16, 64), __shfl_xor(send.y, 16, 64));
+      const uint4 x = ev ? make_uint4(pk[0].x, pk[0].y, recv.x, recv.y)
+                         : make_uint4(recv.x, recv.y, pk[1].x, pk[1].y);
+      const int col = ev ? 4 * kq : 16 + 4 * (kq - 1);
+      store_b128(x, orng, (tl * HV * kHead + v0 + col) * 2);
     }
 
     // 4. h <- e^gamma_L h + K^T (diag(e^(gamma_L - gamma)) D); wave w owns key

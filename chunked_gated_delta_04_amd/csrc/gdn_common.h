@@ -49,6 +49,11 @@ __device__ __forceinline__ void store_b64(uint2 v, __amdgpu_buffer_rsrc_t r, int
   __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, r, byte_off, 0, 0);
 }
 
+__device__ __forceinline__ void store_b128(uint4 v, __amdgpu_buffer_rsrc_t r, int byte_off) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, byte_off, 0, 0);
+}
+
 // Raw buffer loads; zeros where the offset is past the record count.
 __device__ __forceinline__ uint4 load_b128(__amdgpu_buffer_rsrc_t r, int byte_off) {
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
