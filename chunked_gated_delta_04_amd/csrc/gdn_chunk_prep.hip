@@ -130,6 +130,8 @@ __device__ __forceinline__ void lower_tile(int t, int& ib, int& jb) {
 constexpr int kPrepThreads = 512;               // 8 waves per workgroup
 constexpr int kPrepWaves = kPrepThreads / 64;
 constexpr int kRowThreads = kPrepThreads / 64;  // threads per token row, 2 x 16 bytes each
+                                                // (thread m: bytes 16 m and 16 (m + 8) of the
+                                                // row, so a request covers whole lines)
 
 // Writes the forward scan's operands to fo and, with kB (a forward that saves
 // for a backward), the backward's to bo, so that the backward does not form
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
   __shared__ float Xs[3 * 256];  // solve scratch
   __shared__ __align__(16) uint16_t Xp[kPrepWaves][16 * XPP];  // per-wave 16 x 16 transpose tile
 
-  // A value head's own inputs - its v rows (thread: row tid / 8, 16 columns)
+  // A value head's own inputs - its v rows (thread: row tid / 8, 2 x 8 columns)
   // and gates (every wave requests them; wave 0 uses them) - through
   // range-checked buffer loads: rows at or past the chunk's end read as zeros,
   // and a zero range (live = false) moves no data. Requested one value head
@@ -166,11 +168,12 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
   float gq, bq;
   auto request = [&](int hv_, bool live) {
     const int n = live ? L : 0;
-    const int vr0 = tid / kRowThreads, vsg0 = (tid % kRowThreads) * 2, lane = tid & 63;
+    const int vr0 = tid / kRowThreads, vsg0 = tid % kRowThreads, lane = tid & 63;
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(v) + ((size_t)t0 * HV + hv_) * kHead, 0, n * HV * kHead * 2, kBufferWord3);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) vx[j] = load_b128(rv, (vr0 * HV * kHead + (vsg0 + j) * 8) * 2);
+    for (int j = 0; j < 2; ++j)
+      vx[j] = load_b128(rv, (vr0 * HV * kHead + (vsg0 + kRowThreads * j) * 8) * 2);
     const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(g) + (size_t)t0 * HV + hv_, 0, n * HV * 4, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
@@ -179,12 +182,12 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
     bq = load_f32(rb, lane * HV * 4);
   };
 
-  // ---- 1. load and L2-normalise q, k rows (thread: row tid / 8, 16 columns);
+  // ---- 1. load and L2-normalise q, k rows (thread: row tid / 8, 2 x 8 columns);
   //      one division per row, then products with the reciprocal. The first
   //      value head's requests follow the q, k rows, so the norms wait only
   //      for those.
   {
-    const int r = tid / kRowThreads, sg0 = (tid % kRowThreads) * 2;
+    const int r = tid / kRowThreads, sg0 = tid % kRowThreads;
     uint4 kr[2], qr[2];
     float sk = 0.f, sq = 0.f;
     const __amdgpu_buffer_rsrc_t krng = __builtin_amdgcn_make_buffer_rsrc(
@@ -193,8 +196,8 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
         const_cast<uint16_t*>(q) + ((size_t)t0 * H + h) * kHead, 0, L * H * kHead * 2, kBufferWord3);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      kr[j] = load_b128(krng, (r * H * kHead + (sg0 + j) * 8) * 2);
-      qr[j] = load_b128(qrng, (r * H * kHead + (sg0 + j) * 8) * 2);
+      kr[j] = load_b128(krng, (r * H * kHead + (sg0 + kRowThreads * j) * 8) * 2);
+      qr[j] = load_b128(qrng, (r * H * kHead + (sg0 + kRowThreads * j) * 8) * 2);
     }
     request(h * G, true);
 #pragma unroll
@@ -224,8 +227,8 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
         kow[e] = pk2(bf2f(kw[e] & 0xffffu) * rk, bf2f(kw[e] >> 16) * rk);
         qow[e] = pk2(bf2f(qw[e] & 0xffffu) * rq, bf2f(qw[e] >> 16) * rq);
       }
-      *reinterpret_cast<uint4*>(&Ks[r * KP + (sg0 + j) * 8]) = ko;
-      *reinterpret_cast<uint4*>(&Qs[r * KP + (sg0 + j) * 8]) = qo;
+      *reinterpret_cast<uint4*>(&Ks[r * KP + (sg0 + kRowThreads * j) * 8]) = ko;
+      *reinterpret_cast<uint4*>(&Qs[r * KP + (sg0 + kRowThreads * j) * 8]) = qo;
     }
   }
   __syncthreads();
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
     // ---- 2. gates: gamma = inclusive cumsum of g inside the chunk (kept in
     //      base 2); the value rows go to LDS as they are. This head's v rows
     //      and gates were requested before; the next head's are requested now.
-    const int vr0 = tid / kRowThreads, vsg0 = (tid % kRowThreads) * 2;
+    const int vr0 = tid / kRowThreads, vsg0 = tid % kRowThreads;
     const uint4 vc0 = vx[0], vc1 = vx[1];
     float gv = gq;
     const float bv = bq;
@@ -271,8 +274,8 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
         if (kB) bo.gL[blk] = exp2_fast(gl2);
       }
     }
-    *reinterpret_cast<uint4*>(&Vs[vr0 * KP + (vsg0 + 0) * 8]) = vc0;
-    *reinterpret_cast<uint4*>(&Vs[vr0 * KP + (vsg0 + 1) * 8]) = vc1;
+    *reinterpret_cast<uint4*>(&Vs[vr0 * KP + vsg0 * 8]) = vc0;
+    *reinterpret_cast<uint4*>(&Vs[vr0 * KP + (vsg0 + kRowThreads) * 8]) = vc1;
     __syncthreads();
 
     // ---- 3. A (fp32, LDS: 10 lower tiles, 6 zero upper tiles) and P (bf16,
