@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
   __shared__ __align__(16) uint16_t Xp[kPrepWaves][16 * XPP];  // per-wave 16 x 16 transpose tile
 
   // A value head's own inputs - its v rows (thread: row tid / 8, 2 x 8 columns)
-  // and gates (every wave requests them; wave 0 uses them) - through
+  // and gates (wave 0) - through
   // range-checked buffer loads: rows at or past the chunk's end read as zeros,
   // and a zero range (live = false) moves no data. Requested one value head
   // ahead, before the current head's stores: waiting for a load also waits
@@ -178,8 +178,11 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
         const_cast<float*>(g) + (size_t)t0 * HV + hv_, 0, n * HV * 4, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(beta) + (size_t)t0 * HV + hv_, 0, n * HV * 4, kBufferWord3);
-    gq = load_f32(rg, lane * HV * 4);
-    bq = load_f32(rb, lane * HV * 4);
+    // (wave 0 alone uses the gates; the other waves' requests fall past the end
+    // of the range and move nothing: a gate load touches one line per token)
+    const int goff = tid < 64 ? lane * HV * 4 : n * HV * 4;
+    gq = load_f32(rg, goff);
+    bq = load_f32(rb, goff);
   };
 
   // ---- 1. load and L2-normalise q, k rows (thread: row tid / 8, 2 x 8 columns);
