@@ -106,11 +106,13 @@ PrepOut prep_views(char* ws, const Layout& L, const gdn_problem* p) {
 }
 
 // `saved`: per (chunk, value head) the bf16 start state and D (kSavedBlock
-// elements each); then the backward's WY operands: per (value head, chunk)
-// W^T (64 x 128) and P^T (64 x 64), per (key head, chunk) Q~^T and K^
-// (64 x 128 each), per (value head, chunk) T and T^T (2 x 64 x 64); then in
-// fp32 per (value head, chunk) e^gamma_L, the kGates gate factors, and the
-// cumulative decay gamma (base 2) and beta (kGates more).
+// elements each); then the WY operands the forward scan reads and the
+// backward reads again: per (value head, chunk) W [tok][k] (64 x 128) and
+// P [i][j] (64 x 64), per (key head, chunk) Q~ [tok][k] and K^T [k][tok]
+// (64 x 128 each); then, for the backward only, per (value head, chunk) T and
+// T^T (2 x 64 x 64); then in fp32 per (value head, chunk) e^gamma_L, the
+// kGates gate factors, and the cumulative decay gamma (base 2) and beta
+// (kGates more).
 // the gate factors start 16-byte aligned after the e^gamma_L values
 size_t gates_offset(size_t blocks) { return (blocks + 3) / 4 * 4; }
 size_t saved_bytes(const gdn_problem* p, int64_t NC) {
@@ -119,7 +121,7 @@ size_t saved_bytes(const gdn_problem* p, int64_t NC) {
           kblocks * 2 * kBlk64x128) * 2 +
          (gates_offset(blocks) + 2 * blocks * kGates) * sizeof(float);
 }
-PrepOut saved_bwd_views(uint16_t* saved, const gdn_problem* p, int64_t NC) {
+PrepOut saved_views(uint16_t* saved, const gdn_problem* p, int64_t NC) {
   const size_t blocks = (size_t)p->HV * (size_t)NC, kblocks = (size_t)p->H * (size_t)NC;
   PrepOut o;
   uint16_t* b = saved + blocks * (size_t)kSavedBlock;
@@ -134,6 +136,19 @@ PrepOut saved_bwd_views(uint16_t* saved, const gdn_problem* p, int64_t NC) {
   o.U = nullptr;
   o.G = p->HV / p->H;
   return o;
+}
+
+// The forward's WY pass views when it saves for a backward: the operands both
+// passes read (W, P, Q~, K^T and the gate factors) go to `saved`, U stays in
+// the workspace.
+PrepOut forward_views_saving(PrepOut f, const PrepOut& sv) {
+  f.W = sv.W;
+  f.P = sv.P;
+  f.Qn = sv.Qn;
+  f.Kn = sv.Kn;
+  f.gL = sv.gL;
+  f.gE = sv.gE;
+  return f;
 }
 
 float effective_scale(const gdn_problem* p) {
@@ -290,8 +305,9 @@ static int chunk_fwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_
   char* ws = static_cast<char*>(workspace);
   ChunkInfo* table = reinterpret_cast<ChunkInfo*>(ws + L.table);
   int32_t* seq_first = reinterpret_cast<int32_t*>(ws + L.seq_first);
-  const PrepOut prep = prep_views(ws, L, p);
-  const PrepOut bprep = saved ? saved_bwd_views(saved, p, NC) : PrepOut{};
+  const PrepOut bprep = saved ? saved_views(saved, p, NC) : PrepOut{};
+  const PrepOut prep =
+      saved ? forward_views_saving(prep_views(ws, L, p), bprep) : prep_views(ws, L, p);
   GDN_TRY(clk.run([&] {
     return launch_chunk_table(p->cu_seqlens, p->N, p->T, (int)NC, table, seq_first, s);
   }));
@@ -478,15 +494,16 @@ static int chunk_bwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_
     return launch_chunk_table(p->cu_seqlens, p->N, p->T, (int)NC, table, seq_first, s);
   }));
   if (recompute) {
-    // the forward's WY pass (both layouts) and a save-only scan rebuild
-    // `saved` after both workspace layouts; the forward's operands occupy the
-    // workspace's start until the scan has read them, then the backward's
-    // scratch takes that place
+    // the forward's WY pass (saving) and a save-only scan rebuild `saved`
+    // after both workspace layouts; the forward's U occupies the workspace's
+    // start until the scan has read it, then the backward's scratch takes
+    // that place
     uint16_t* rebuilt = reinterpret_cast<uint16_t*>(ws + recompute_saved_offset(p, NC));
-    const PrepOut fprep = prep_views(ws, make_layout(p, NC, false), p);
+    const PrepOut rv = saved_views(rebuilt, p, NC);
+    const PrepOut fprep = forward_views_saving(prep_views(ws, make_layout(p, NC, false), p), rv);
     GDN_TRY(clk.run([&] {
       return launch_chunk_prep(PrepMode::kBoth, table, (int)NC, p->H, p->HV, scale, q, k, v, g,
-                               beta, fprep, saved_bwd_views(rebuilt, p, NC), s);
+                               beta, fprep, rv, s);
     }));
     StateRef sr{};
     sr.h0 = recompute_h0;
@@ -496,8 +513,8 @@ static int chunk_bwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_
     }));
     saved = rebuilt;
   }
-  // the backward's WY operands were written by the forward, behind the states
-  const PrepOut prep = saved_bwd_views(const_cast<uint16_t*>(saved), p, NC);
+  // the WY operands were written by the forward, behind the states
+  const PrepOut prep = saved_views(const_cast<uint16_t*>(saved), p, NC);
   GDN_TRY(clk.run([&] {
     return launch_bwd_dh_scan(seq_first, p->N, p->HV, (int)NC, table, prep, dO, dhT, dh0, bufs, s);
   }));

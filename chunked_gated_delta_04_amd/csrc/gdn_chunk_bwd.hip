@@ -1,6 +1,6 @@
 // Backward of the chunked gated delta rule: reverse state-gradient scan and
-// the per-chunk gradient pass. Their per-chunk operands (W^T, P^T, T, T^T,
-// e^gamma_L and the per-token decays per value head; Q~^T and K^ per key head)
+// the per-chunk gradient pass. Their per-chunk operands (W, P, T, T^T,
+// e^gamma_L and the per-token decays per value head; Q~ and K^T per key head)
 // are the ones the forward's WY pass wrote behind the saved states
 // (gdn_chunk_prep.hip), so no WY pass runs here.
 //
@@ -77,6 +77,14 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
   __shared__ __align__(16) uint16_t Ot[kChunk * OP];  // dO [tok][v - v0]
   __shared__ __align__(16) uint16_t Og[kChunk * OP];  // diag(e^gamma) dO [tok][v - v0]
   __shared__ __align__(16) uint16_t Es[VB * DP];  // dD^T [v][tok]
+  // The chunk operands each wave contracts, in the forward's layouts (P [i][j],
+  // K^T [k][tok], Q~ [tok][k], W [tok][k], all chunk-major): per wave
+  // kOpBlocks column groups of 64 rows x 16 bytes, loaded into registers a
+  // chunk ahead, written to the wave's own region at the start of the chunk
+  // and read back transposed (lds_col8_cm). Only the wave that writes a
+  // region reads it, so no barrier orders them.
+  constexpr int kOpBlocks = 14, kOpStride = 512;
+  __shared__ __align__(16) uint16_t Lop[4 * kOpBlocks * kOpStride];
 
   f32x4 dh[2][VT];
   const size_t state_base = ((size_t)seq * HV + hv) * kHead * kHead;
@@ -95,7 +103,7 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
     }
 
   struct Ops {
-    bf16x8 pa[2], ka[4], qa[2][2], wa[2][2];
+    u32v4 op[kOpBlocks];  // row `lane` of each column group (see load_ops)
     uint4 dO;
     float gl;
     float eg;    // e^gamma of token ot (the dO row this thread stages)
@@ -112,8 +120,8 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
     eos = lastc.t0 + lastc.len;
   }
   // This workgroup's share of a chunk's operand lines for the L2 warm-up: the
-  // value head's W^T, P^T, gate-factor and dO lines (324) split over its value
-  // blocks, the key head's Q~^T and K^ lines (256) over the workgroups of all its
+  // value head's W, P, gate-factor and dO lines (324) split over its value
+  // blocks, the key head's Q~ and K^T lines (256) over the workgroups of all its
   // value heads. Lanes past the share all touch its first line (one request per
   // wave instruction, the lanes' addresses being the same); dO rows
   // past the chunk's end touch its last row.
@@ -138,32 +146,32 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
     return prep.Kn + kblk * 8192 + (l - 128) * kLineElems16;
   };
   uint32_t sink = 0;
-  // pc: the chunk whose lines the set's L2 warm-up word touches
+  // pc: the chunk whose lines the set's L2 warm-up word touches. Wave w takes
+  // the column groups it contracts: P's columns 16 w .. 16 w + 15 (groups
+  // 2 w, 2 w + 1; pieces 0, 1), K^T's token columns 16 w .. (groups 2 w,
+  // 2 w + 1, each as key rows 0-63 and 64-127; pieces 2-5), and the key
+  // columns 32 w .. 32 w + 31 of Q~ and W (groups 4 w .. ; pieces 6-9 and
+  // 10-13). Each piece is one 1 KiB request: lane l holds the 16 bytes of row l.
   auto load_ops = [&](int c, Ops& x, int pc) {
     const size_t blk = (size_t)hv * NC + c;
     const size_t kblk = (size_t)(hv / prep.G) * NC + c;
-    const uint16_t* PTb = prep.P + blk * 4096;    // P^T: row i holds P[j][i], j >= i
-    const uint16_t* Kbb = prep.Kn + kblk * 8192;  // K^ [tok][k]
-    const uint16_t* QgT = prep.Qn + kblk * 8192;  // Q~^T [k][tok]
-    const uint16_t* WT = prep.W + blk * 8192;     // W^T [k][tok]
-    // P^T's tiles below the diagonal are not stored: those pieces come from
-    // past the end of a range-checked buffer, as zeros
-    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(PTb), 0, kChunk * kChunk * 2, kBufferWord3);
+    const uint16_t* Pb = prep.P + blk * 4096;     // P [i][j]
+    const uint16_t* Kb = prep.Kn + kblk * 8192;   // K^T [k][tok]
+    const uint16_t* Qb = prep.Qn + kblk * 8192;   // Q~ [tok][k]
+    const uint16_t* Wb = prep.W + blk * 8192;     // W [tok][k]
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-      x.pa[s] = ld8_buf(rp, 2 * s + (kq >> 1) >= wave ? kcm(16 * wave + li, 32 * s + 8 * kq, 64) * 2
-                                                     : kChunk * kChunk * 2);
+    for (int g = 0; g < 2; ++g)
+      x.op[g] = *reinterpret_cast<const u32v4*>(Pb + (2 * wave + g) * 512 + 8 * lane);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) x.ka[s] = ld8(Kbb + kcm(16 * wave + li, 32 * s + 8 * kq, 64));
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) {
-      const int kr = 16 * (2 * wave + dt) + li;
+      for (int hh = 0; hh < 2; ++hh)
+        x.op[2 + 2 * g + hh] =
+            *reinterpret_cast<const u32v4*>(Kb + (2 * wave + g) * 1024 + hh * 512 + 8 * lane);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        x.qa[dt][s] = ld8(QgT + kcm(kr, 32 * s + 8 * kq, 128));
-        x.wa[dt][s] = ld8(WT + kcm(kr, 32 * s + 8 * kq, 128));
-      }
+    for (int g = 0; g < 4; ++g) {
+      x.op[6 + g] = *reinterpret_cast<const u32v4*>(Qb + (4 * wave + g) * 512 + 8 * lane);
+      x.op[10 + g] = *reinterpret_cast<const u32v4*>(Wb + (4 * wave + g) * 512 + 8 * lane);
     }
     x.gl = prep.gL[blk];
     const float* ge = prep.gE + blk * kGates;
@@ -180,6 +188,12 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
 
   auto step = [&](int c, const Ops& cur) {
     const size_t blk = (size_t)hv * NC + c;
+    uint16_t* const R = Lop + wave * (kOpBlocks * kOpStride);
+    // the wave's operand pieces into its own region (the previous chunk's
+    // transposed reads of it have completed: their MFMAs consumed them)
+#pragma unroll
+    for (int i = 0; i < kOpBlocks; ++i)
+      *reinterpret_cast<u32v4*>(R + i * kOpStride + 8 * lane) = cur.op[i];
     // 1. dh -> LDS; stage dO^T for this value block
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
@@ -222,19 +236,32 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
         ob[vt][s] = __builtin_bit_cast(bf16x8, lds_col8(Ot, OP, 32 * s + 8 * kq, 16 * vt, lane));
 
     // 2. dD = P^T dO + diag(e^(gamma_L - gamma)) K^ dh; wave w owns tokens
-    //    16 w .. 16 w + 15
+    //    16 w .. 16 w + 15. Operands: pa[s] = P[32 s + 8 kq ..][16 w + li]
+    //    (P^T's rows), zero where that 16 x 16 tile of P lies above its
+    //    diagonal (those tiles are not stored); ka[s] = K^[16 w + li][32 s + 8 kq ..]
+    bf16x8 pa[2], ka[4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint4 x = lds_col8_cm(R, R + kOpStride, 32 * s + 8 * kq, lane);
+      pa[s] = __builtin_bit_cast(bf16x8, 2 * s + (kq >> 1) >= wave ? x : make_uint4(0u, 0u, 0u, 0u));
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      ka[s] = __builtin_bit_cast(bf16x8, lds_col8_cm(R + (2 + (s >> 1)) * kOpStride,
+                                                     R + (4 + (s >> 1)) * kOpStride,
+                                                     (32 * s + 8 * kq) & 63, lane));
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt) {
       bf16x8 hb4[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) hb4[s] = ld8(&Hs[(16 * vt + li) * SP + 32 * s + 8 * kq]);
       // two independent partial sums, so the MFMAs do not wait on each other
-      f32x4 a0 = mfma(cur.ka[0], hb4[0], zero4());
-      f32x4 a1 = mfma(cur.ka[1], hb4[1], zero4());
-      f32x4 ap = mfma(cur.pa[1], ob[vt][1], zero4());
-      a0 = mfma(cur.ka[2], hb4[2], a0);
-      a1 = mfma(cur.ka[3], hb4[3], a1);
-      if (wave < 2) ap = mfma(cur.pa[0], ob[vt][0], ap);
+      f32x4 a0 = mfma(ka[0], hb4[0], zero4());
+      f32x4 a1 = mfma(ka[1], hb4[1], zero4());
+      f32x4 ap = mfma(pa[1], ob[vt][1], zero4());
+      a0 = mfma(ka[2], hb4[2], a0);
+      a1 = mfma(ka[3], hb4[3], a1);
+      if (wave < 2) ap = mfma(pa[0], ob[vt][0], ap);
       const f32x4 ak = a0 + a1;
       const f32x4 acc = f32x4{ak[0] * cur.ebw.x, ak[1] * cur.ebw.y, ak[2] * cur.ebw.z,
                               ak[3] * cur.ebw.w} + ap;
@@ -245,6 +272,15 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
     // The part of step 3 that needs no dD, while the other waves finish theirs:
     // dh <- e^gamma_L dh + Q~^T (diag(e^gamma) dO) (dh was copied to LDS above)
     {
+      // qa[dt][s] = Q~^T[16 (2 w + dt) + li][32 s + 8 kq ..], columns of Q~
+      bf16x8 qa[2][2];
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          qa[dt][s] = __builtin_bit_cast(bf16x8, lds_col8_cm(R + (6 + 2 * dt) * kOpStride,
+                                                             R + (7 + 2 * dt) * kOpStride,
+                                                             32 * s + 8 * kq, lane));
       bf16x8 og[VT][2];
 #pragma unroll
       for (int vt = 0; vt < VT; ++vt)
@@ -257,7 +293,7 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
         for (int vt = 0; vt < VT; ++vt) {
           f32x4 acc = dh[dt][vt] * cur.gl;
 #pragma unroll
-          for (int s = 0; s < 2; ++s) acc = mfma(cur.qa[dt][s], og[vt][s], acc);
+          for (int s = 0; s < 2; ++s) acc = mfma(qa[dt][s], og[vt][s], acc);
           dh[dt][vt] = acc;
         }
     }
@@ -277,7 +313,16 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
     }
 
     // 3. dh <- (e^gamma_L dh + Q~^T (diag(e^gamma) dO), from above) - W^T dD;
-    //    wave w owns key rows 32 w .. 32 w + 31
+    //    wave w owns key rows 32 w .. 32 w + 31;
+    //    wa[dt][s] = W^T[16 (2 w + dt) + li][32 s + 8 kq ..], columns of W
+    bf16x8 wa[2][2];
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        wa[dt][s] = __builtin_bit_cast(bf16x8, lds_col8_cm(R + (10 + 2 * dt) * kOpStride,
+                                                           R + (11 + 2 * dt) * kOpStride,
+                                                           32 * s + 8 * kq, lane));
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -285,7 +330,7 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
         f32x4 acw = zero4();
 #pragma unroll
         for (int s = 0; s < 2; ++s)
-          acw = mfma(cur.wa[dt][s], ld8(&Es[(16 * vt + li) * DP + 32 * s + 8 * kq]), acw);
+          acw = mfma(wa[dt][s], ld8(&Es[(16 * vt + li) * DP + 32 * s + 8 * kq]), acw);
         dh[dt][vt] = dh[dt][vt] - acw;
       }
     // No barrier here: Hs, Ot and Og are last read before the barrier above,

@@ -17,25 +17,27 @@
 // commit). Chunks restart at each sequence start; the last chunk of a
 // sequence may be short and is zero-padded, which leaves every product exact.
 //
-// One workgroup (4 waves) handles one chunk of one key head: q and k are
+// One workgroup (8 waves) handles one chunk of one key head: q and k are
 // normalised once and K^K^T / Q~K^T are formed once on MFMA, then each value
 // head of the key head gets its gates, A, T and the products above. Only
 // e^x of x <= 0 (i >= j) is formed, so strong decays underflow to 0.
 //
-// Outputs, bf16 unless noted, in the layouts the scans read with one 16-byte
-// load per MFMA operand (a forward that saves for a backward writes both sets
-// in one pass). Per (value head, chunk) block:
-//            forward scan                    dh scan and gradient pass
-//   W        [64 tok][128 k]                 W^T   [128 k][64 tok]
-//   U        U^T [128 v][64 tok]             (not written)
-//   P        [64 i][64 j]                    P^T   [64 j][64 i]
-//   T        (not written)                   T [i][j] and T^T [j][i]
-//   gL       e^gamma_L (fp32)                same
-//   gE       e^gamma and e^(gamma_L - gamma) per token (fp32), same
-//   gB       (not written)                   gamma (base 2) and beta per token (fp32)
+// Outputs, bf16 unless noted, in the layouts the forward scan reads with one
+// 16-byte load per MFMA operand; the dh scan reads the same tiles and takes
+// the transposed operands it contracts from LDS with transposing reads. Only
+// what the backward alone needs is written in addition (when the forward
+// saves for it). Per (value head, chunk) block:
+//   W        [64 tok][128 k]
+//   U        U^T [128 v][64 tok]           (forward scan only)
+//   P        [64 i][64 j]                  (the lower 16 x 16 tiles)
+//   gL       e^gamma_L (fp32)
+//   gE       e^gamma and e^(gamma_L - gamma) per token (fp32)
+//   T        T [i][j] and T^T [j][i]      (backward only; the lower, resp.
+//                                          upper, 16 x 16 tiles)
+//   gB       gamma (base 2) and beta per token (fp32; backward only)
 // and per (key head, chunk) block, shared by the key head's value heads:
-//   Q~       [64 tok][128 k]                 Q~^T  [128 k][64 tok]
-//   K^       K^T [128 k][64 tok]             K^    [64 tok][128 k]
+//   Q~       [64 tok][128 k]
+//   K^       K^T [128 k][64 tok]
 // The scans apply the per-token decays that turn Q~ into Q_g and K^ into
 // K_bwd in fp32: Q_g h = diag(e^gamma) (Q~ h) and K_bwd^T D = K^T (diag(e^(gamma_L
 // - gamma)) D), and likewise in the backward.
@@ -108,17 +110,6 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t* __restr
 namespace {
 constexpr int KP = 136;  // LDS row pitch (bf16) of [64][128] tiles
 constexpr int FP = 68;   // LDS row pitch (fp32) of [64][64] tiles
-constexpr int XPP = 24;  // LDS row pitch (bf16) of a wave's 16 x 16 transpose tile
-
-// A 16 x 16 bf16 tile held as MFMA accumulator pieces (lane 16 kq + li: row li,
-// columns 4 kq .. 4 kq + 3) read back by columns: lane 16 kq + li (kq < 2)
-// gets column li, rows 8 kq .. 8 kq + 7. The wave's own LDS tile, written and
-// read by the wave alone (its LDS operations complete in order).
-__device__ __forceinline__ uint4 tile_transpose(uint16_t* xp, uint2 piece, int lane) {
-  const int li = lane & 15, kq = lane >> 4;
-  *reinterpret_cast<uint2*>(&xp[li * XPP + 4 * kq]) = piece;
-  return lds_col8(xp, XPP, 8 * (kq & 1), 0, lane);
-}
 
 // lower-including 16x16 tile t (0..9) of a 64x64 matrix -> (row block, col block)
 __device__ __forceinline__ void lower_tile(int t, int& ib, int& jb) {
@@ -134,8 +125,10 @@ constexpr int kRowThreads = kPrepThreads / 64;  // threads per token row, 2 x 16
                                                 // row, so a request covers whole lines)
 
 // Writes the forward scan's operands to fo and, with kB (a forward that saves
-// for a backward), the backward's to bo, so that the backward does not form
-// them again.
+// for a backward), what only the backward reads to bo (T, T^T, gamma and
+// beta), so that the backward does not form them again. The backward's dh
+// scan reads fo's W, P, Q~ and K^T themselves (transposed in LDS), so a
+// forward that saves points those into the saved buffer.
 template <bool kB>
 __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
     const ChunkInfo* __restrict__ table, int NC, int H, int HV, float scale,
@@ -155,7 +148,6 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
   // gates of the value head; gam is the cumulative log-decay in base 2
   __shared__ __align__(16) float gam[64], bet[64], fw[64];
   __shared__ float Xs[3 * 256];  // solve scratch
-  __shared__ __align__(16) uint16_t Xp[kPrepWaves][16 * XPP];  // per-wave 16 x 16 transpose tile
 
   // A value head's own inputs - its v rows (thread: row tid / 8, 2 x 8 columns)
   // and gates (wave 0) - through
@@ -267,23 +259,17 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
       fo.gE[blk * kGates + lane] = e;
       fo.gE[blk * kGates + kChunk + lane] = bw;
       if (kB) {
-        bo.gE[blk * kGates + lane] = e;
-        bo.gE[blk * kGates + kChunk + lane] = bw;
         bo.gB[blk * kGates + lane] = g2;  // the gradient pass reads these as they are
         bo.gB[blk * kGates + kChunk + lane] = bv;
       }
-      if (lane == 0) {
-        fo.gL[blk] = exp2_fast(gl2);
-        if (kB) bo.gL[blk] = exp2_fast(gl2);
-      }
+      if (lane == 0) fo.gL[blk] = exp2_fast(gl2);
     }
     *reinterpret_cast<uint4*>(&Vs[vr0 * KP + vsg0 * 8]) = vc0;
     *reinterpret_cast<uint4*>(&Vs[vr0 * KP + (vsg0 + kRowThreads) * 8]) = vc1;
     __syncthreads();
 
     // ---- 3. A (fp32, LDS: 10 lower tiles, 6 zero upper tiles) and P (bf16,
-    //      global: 16 tiles), 32 jobs over the 4 waves. A tile of P also goes
-    //      to the backward's P^T through the wave's LDS transpose tile.
+    //      global: the 10 lower tiles), 32 jobs over the waves.
     for (int job = wave; job < 32; job += kPrepWaves) {
       if (job < 10) {
         int ib, jb;
@@ -328,11 +314,6 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
         if (jb <= ib) {
           const uint2 pk = pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
           st8_nt(fo.P + blk * (64 * 64) + kcm(i, 16 * jb + 4 * kq, 64), pk);
-          if (kB) {  // P^T[j][i .. i + 7]: columns of the tile, 16-byte pieces from 32 lanes
-            const uint4 x = tile_transpose(Xp[wave], pk, lane);
-            if (kq < 2)
-              st16_nt(bo.P + blk * (64 * 64) + kcm(16 * jb + li, 16 * ib + 8 * kq, 64), x);
-          }
         }
       }
     }
@@ -366,8 +347,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
 
     // ---- 5. W = (T diag(beta e^gamma)) K^: the factor scales T's columns as
     //      T becomes an MFMA operand, K^ is read by columns from its row tile.
-    //      32 tiles of 16 x 16 over 4 waves, contraction over the chunk; a
-    //      tile also goes to the backward's W^T through the LDS transpose tile.
+    //      32 tiles of 16 x 16 over the waves, contraction over the chunk.
     for (int tt = wave; tt < 32; tt += kPrepWaves) {
       // C = K^T (T')^T: C[4kq+r][li] = W[t = 16 tb + li][k = 16 db + 4kq + r]
       const int db = tt >> 2, tb = tt & 3;
@@ -380,11 +360,6 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
       }
       const uint2 pk = pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
       st8_nt(fo.W + blk * 8192 + kcm(16 * tb + li, 16 * db + 4 * kq, 64), pk);
-      if (kB) {  // W^T[k][t .. t + 7]
-        const uint4 x = tile_transpose(Xp[wave], pk, lane);
-        if (kq < 2)
-          st16_nt(bo.W + blk * 8192 + kcm(16 * db + li, 16 * tb + 8 * kq, 128), x);
-      }
     }
 
     {
@@ -406,11 +381,10 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
     __syncthreads();  // gates, A, T and V are rewritten for the next value head
   }
 
-  // ---- Q~ and K^ of the key head (and their transposes for the backward),
-  //      after the value heads so that no load waits for these stores.
-  //      The transposed pieces (column chunks of 8 tokens) come from the row
-  //      tiles with transposing LDS reads: a wave covers one token group tg
-  //      and 64 consecutive features.
+  // ---- Q~ (rows) and K^T of the key head, after the value heads so that no
+  //      load waits for these stores. K^T's pieces (column chunks of 8
+  //      tokens) come from the row tile with transposing LDS reads: a wave
+  //      covers one token group tg and 64 consecutive features.
   {
     const int wave = tid >> 6, lane = tid & 63;
     const int li = lane & 15, kq = lane >> 4;
@@ -431,10 +405,6 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
     };
     rows_out(Qs, fo.Qn + kblk * 8192);   // Q~ [tok][k]
     cols_out(Ks, fo.Kn + kblk * 8192);   // K^T [k][tok]
-    if (kB) {
-      rows_out(Ks, bo.Kn + kblk * 8192);  // K^ [tok][k]
-      cols_out(Qs, bo.Qn + kblk * 8192);  // Q~^T [k][tok]
-    }
   }
 }
 

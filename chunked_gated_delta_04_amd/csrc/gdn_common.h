@@ -16,6 +16,7 @@ namespace gdn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32v4 __attribute__((ext_vector_type(4)));  // 16 raw bytes in registers
 
 constexpr int kHead = 128;   // K = V
 constexpr int kChunk = 64;   // tokens per chunk
@@ -195,6 +196,19 @@ __device__ __forceinline__ uint4 lds_col8(const uint16_t* tile, int pitch, int r
   const int j = lane & 15;
   const uint2 a = lds_tr16(tile + (r0 + (j >> 2)) * pitch + c0 + 4 * (j & 3));
   const uint2 b = lds_tr16(tile + (r0 + 4 + (j >> 2)) * pitch + c0 + 4 * (j & 3));
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// The same for a 16-column tile held as two column groups of 8 in the
+// chunk-major layout (row r of a group at 8 r, 16 bytes per row): ga holds
+// columns 0-7, gb columns 8-15. Lane i of a lane group receives column i of
+// rows r0 .. r0 + 7 (r0 per lane group).
+__device__ __forceinline__ uint4 lds_col8_cm(const uint16_t* ga, const uint16_t* gb, int r0,
+                                             int lane) {
+  const int j = lane & 15;
+  const uint16_t* p = ((j & 2) ? gb : ga) + (r0 + (j >> 2)) * 8 + 4 * (j & 1);
+  const uint2 a = lds_tr16(p);
+  const uint2 b = lds_tr16(p + 32);
   return make_uint4(a.x, a.y, b.x, b.y);
 }
 

@@ -14,11 +14,12 @@ namespace gdn {
 // head): kblk = (hv / G) * NC + c. Every tile is stored in the chunk-major
 // layout of kcm() with its contraction axis chunked.
 struct PrepOut {
-  uint16_t* W;   // value head; forward: W [tok][k]; backward: W^T [k][tok]
+  uint16_t* W;   // value head: W [tok][k]
   uint16_t* U;   // value head; forward only: U^T [v][tok]
-  uint16_t* Qn;  // key head; forward: Q~ [tok][k]; backward: Q~^T [k][tok]
-  uint16_t* P;   // value head; forward: P [i][j]; backward: P^T [j][i]
-  uint16_t* Kn;  // key head; forward: K^T [k][tok]; backward: K^ [tok][k]
+  uint16_t* Qn;  // key head: Q~ [tok][k]
+  uint16_t* P;   // value head: P [i][j] (its 16 x 16 tiles above the diagonal
+                 // are zero and are not stored)
+  uint16_t* Kn;  // key head: K^T [k][tok]
   float* gL;     // value head: e^gamma_L, 1 per block
   float* gE;     // value head: e^gamma (64), then e^(gamma_L - gamma) (64, zero past
                  // the chunk's end), 128 per block
@@ -38,8 +39,8 @@ struct BwdBufs {
 hipError_t launch_chunk_table(const int32_t* cu, int N, int T, int NC, ChunkInfo* table,
                               int32_t* seq_first, hipStream_t stream);
 
-// Which operand layouts the WY pass writes: the forward scan's only, or also
-// the backward's (dh scan and gradient pass) when the forward saves for it.
+// Whether the WY pass also writes what only the backward reads (T, T^T, the
+// cumulative decay and beta), when the forward saves for a backward.
 enum class PrepMode { kForward, kBoth };
 
 hipError_t launch_chunk_prep(PrepMode mode, const ChunkInfo* table, int NC, int H, int HV,
