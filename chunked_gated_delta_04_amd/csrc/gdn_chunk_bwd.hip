@@ -344,14 +344,14 @@ __global__ __launch_bounds__(256) void bwd_dh_scan_kernel(
     const int first = c_begin;
     Ops A, B;
     B.pf = 0;
-    load_ops(c_end - 1, A, max(c_end - 3, first));
+    load_ops(c_end - 1, A, max(c_end - 2, first));
     for (int c = c_end - 1;; c -= 2) {
       sink ^= B.pf;  // requested two sets ago
-      load_ops(max(c - 1, first), B, max(c - 3, first));
+      load_ops(max(c - 1, first), B, max(c - 2, first));
       step(c, A);
       if (c - 1 < first) break;
       sink ^= A.pf;
-      load_ops(max(c - 2, first), A, max(c - 4, first));
+      load_ops(max(c - 2, first), A, max(c - 3, first));
       step(c - 1, B);
       if (c - 2 < first) break;
     }

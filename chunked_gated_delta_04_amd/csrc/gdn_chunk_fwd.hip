@@ -211,8 +211,8 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     __syncthreads();
     // the next set's requests, issued by all waves together right after the
     // barrier (waves that issue them together share the lines they fetch),
-    // and the L2 warm-up of the chunk three steps ahead
-    load_ops(cn, nxt, min(cn + 2, c_end - 1));
+    // and the L2 warm-up of the chunk two steps ahead
+    load_ops(cn, nxt, min(cn + 1, c_end - 1));
     uint16_t* sv = saved + blk_saved(c, hv, HV);
     if constexpr (kSave) {
       // h = S^T as [v / 32][v % 32 / 8][k][v % 8]: chunk e = 64 q + lane holds
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     const int last = c_end - 1;
     Ops A, B;
     B.pf = 0;
-    load_ops(c_begin, A, min(c_begin + 2, last));
+    load_ops(c_begin, A, min(c_begin + 1, last));
     for (int c = c_begin;; c += 2) {
       step(c, A, min(c + 1, last), B);
       if (c + 1 > last) break;
