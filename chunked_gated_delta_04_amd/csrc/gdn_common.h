@@ -221,16 +221,35 @@ __device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, const f32x4& c) {
 // In-place inverse of I + A for a strictly lower-triangular 64 x 64 fp32 matrix A
 // in LDS (row pitch 68): on return T = (I + A)^-1, unit lower triangular, with
 // zeros above the diagonal blocks as on entry. Blocked in 16 x 16: each
-// diagonal block by forward substitution (one column per thread of wave 0),
-// then block rows i = 1..3 from T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj, block
-// j of row i on wave j with fp32 MFMA (the sum into the wave's scratch tile,
-// a barrier, then the product with T_ii). scratch: 768 floats. Must be called
-// by all 256 threads of the workgroup (it synchronises). Fixed summation order.
+// diagonal block by forward substitution (one column per lane of wave 3), then
+// the blocks below the diagonal from T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj,
+// column j on wave j (j = 0, 1, 2), top to bottom, with fp32 MFMA (the sum into
+// the wave's scratch tile, then the product with T_ii). A column uses only the
+// diagonal blocks and its own earlier blocks, so the columns need no barrier
+// between them; each wave reads the blocks of A it contracts into registers
+// before the one barrier (while wave 3 solves the diagonal), because the
+// blocks are overwritten in place by other columns. scratch: 768 floats. Must
+// be called by all threads of the workgroup (at least 4 waves; it
+// synchronises). Fixed summation order.
 __device__ __forceinline__ void invert_unit_lower_64(float* M, float* scratch, int tid) {
   constexpr int P = 68;
-  float x[16];
-  if (tid < 64) {
-    const int o16 = 16 * (tid >> 4), jc = tid & 15;
+  const int jb = tid >> 6, lane = tid & 63, li = lane & 15, kk = lane >> 4;
+  // a[i - 1][m][s]: A_im as the MFMA operand of k-step s (lane: row li, column 4 s + kk)
+  float a[3][3][4];
+  if (jb < 3) {
+#pragma unroll
+    for (int ib = 1; ib < 4; ++ib)
+#pragma unroll
+      for (int mb = 0; mb < 3; ++mb)
+        if (mb < ib && mb >= jb) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) a[ib - 1][mb][s] = M[(16 * ib + li) * P + 16 * mb + 4 * s + kk];
+        }
+  } else if (jb == 3) {
+    // diagonal blocks: lane = column jc of block o16 / 16 (this wave alone reads
+    // and then writes them; its LDS operations complete in order)
+    const int o16 = 16 * (lane >> 4), jc = lane & 15;
+    float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float acc = i == jc ? 1.f : 0.f;
@@ -238,39 +257,35 @@ __device__ __forceinline__ void invert_unit_lower_64(float* M, float* scratch, i
       for (int m = 0; m < i; ++m) acc -= M[(o16 + i) * P + o16 + m] * x[m];
       x[i] = acc;
     }
-  }
-  __syncthreads();
-  if (tid < 64) {
-    const int o16 = 16 * (tid >> 4), jc = tid & 15;
 #pragma unroll
     for (int i = 0; i < 16; ++i) M[(o16 + i) * P + o16 + jc] = x[i];
   }
   __syncthreads();
-  const int jb = tid >> 6, lane = tid & 63, li = lane & 15, kk = lane >> 4;
-  float* St = scratch + 256 * (jb < 3 ? jb : 0);
-  for (int ib = 1; ib < 4; ++ib) {
-    if (jb < ib) {  // S = sum_m A_(ib, m) T_(m, jb)
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int mb = jb; mb < ib; ++mb) {
+  if (jb < 3) {
+    float* St = scratch + 256 * jb;
+#pragma unroll
+    for (int ib = 1; ib < 4; ++ib) {
+      if (ib > jb) {  // S = sum_m A_(ib, m) T_(m, jb); T_(ib, jb) = -T_(ib, ib) S
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int mb = 0; mb < 3; ++mb)
+          if (mb < ib && mb >= jb) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              acc = mfma_f32_k4(a[ib - 1][mb][s], M[(16 * mb + 4 * s + kk) * P + 16 * jb + li], acc);
+          }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) St[(4 * kk + r) * 16 + li] = acc[r];
+        f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          acc = mfma_f32_k4(M[(16 * ib + li) * P + 16 * mb + 4 * s + kk],
-                            M[(16 * mb + 4 * s + kk) * P + 16 * jb + li], acc);
+          d = mfma_f32_k4(M[(16 * ib + li) * P + 16 * ib + 4 * s + kk], St[(4 * s + kk) * 16 + li], d);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) M[(16 * ib + 4 * kk + r) * P + 16 * jb + li] = -d[r];
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) St[(4 * kk + r) * 16 + li] = acc[r];
     }
-    __syncthreads();
-    if (jb < ib) {  // T_(ib, jb) = -T_(ib, ib) S
-      f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        d = mfma_f32_k4(M[(16 * ib + li) * P + 16 * ib + 4 * s + kk], St[(4 * s + kk) * 16 + li], d);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) M[(16 * ib + 4 * kk + r) * P + 16 * jb + li] = -d[r];
-    }
-    __syncthreads();
   }
+  __syncthreads();
 }
 
 // Saved-for-backward block of one (chunk, value head): the chunk-start state
