@@ -18,9 +18,10 @@
 // sequence may be short and is zero-padded, which leaves every product exact.
 //
 // One workgroup (8 waves) handles one chunk of one key head: q and k are
-// normalised once and K^K^T / Q~K^T are formed once on MFMA, then each value
-// head of the key head gets its gates, A, T and the products above. Only
-// e^x of x <= 0 (i >= j) is formed, so strong decays underflow to 0.
+// normalised once and K^K^T / Q~K^T are formed once on MFMA (held in
+// registers), then each value head of the key head gets its gates, A, T and
+// the products above. Only e^x of x <= 0 (i >= j) is formed, so strong decays
+// underflow to 0.
 //
 // Outputs, bf16 unless noted, in the layouts the forward scan reads with one
 // 16-byte load per MFMA operand; the dh scan reads the same tiles and takes
@@ -228,6 +229,38 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
   }
   __syncthreads();
 
+  // K^K^T and Q~K^T tiles of the key head, formed once for all its value heads:
+  // kk[n] belongs to job wave + n kPrepWaves of step 3 below (an A tile for
+  // jobs 0-9, a P tile at or below the diagonal for jobs 16-31, nothing else)
+  constexpr int kJobs = 32 / kPrepWaves;
+  f32x4 kk[kJobs];
+  {
+    const int wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int n = 0; n < kJobs; ++n) {
+      const int job = wave + kPrepWaves * n;
+      f32x4 acc = zero4();
+      if (job < 10) {
+        int ib, jb;
+        lower_tile(job, ib, jb);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          acc = mfma(ld8(&Ks[(16 * ib + li) * KP + 32 * s + 8 * kq]),
+                     ld8(&Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), acc);
+      } else if (job >= 16) {
+        const int pt = job - 16, ib = pt >> 2, jb = pt & 3;
+        if (jb <= ib) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            acc = mfma(ld8(&Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]),
+                       ld8(&Qs[(16 * ib + li) * KP + 32 * s + 8 * kq]), acc);
+        }
+      }
+      kk[n] = acc;
+    }
+  }
+
   for (int jg = 0; jg < G; ++jg) {
     // Re-derive the thread coordinates from an opaque copy each iteration, so
     // that the many LDS and global addresses built from them are formed where
@@ -269,16 +302,15 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
     __syncthreads();
 
     // ---- 3. A (fp32, LDS: 10 lower tiles, 6 zero upper tiles) and P (bf16,
-    //      global: the 10 lower tiles), 32 jobs over the waves.
-    for (int job = wave; job < 32; job += kPrepWaves) {
+    //      global: the 10 lower tiles), 32 jobs over the waves, from the key
+    //      head's tiles kk formed above.
+#pragma unroll
+    for (int n = 0; n < kJobs; ++n) {
+      const int job = wave + kPrepWaves * n;
       if (job < 10) {
         int ib, jb;
         lower_tile(job, ib, jb);
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          acc = mfma(ld8(&Ks[(16 * ib + li) * KP + 32 * s + 8 * kq]),
-                     ld8(&Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), acc);
+        const f32x4 acc = kk[n];
         const int j = 16 * jb + li;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -295,13 +327,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
       } else {
         const int pt = job - 16, ib = pt >> 2, jb = pt & 3;  // P tile (row block ib, col block jb)
         // C = K^ Q~^T tile: C[4kq+r][li] = P-row i = 16 ib + li, cols j = 16 jb + 4kq + r
-        f32x4 acc = zero4();
-        if (jb <= ib) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            acc = mfma(ld8(&Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]),
-                       ld8(&Qs[(16 * ib + li) * KP + 32 * s + 8 * kq]), acc);
-        }
+        const f32x4 acc = kk[n];
         const int i = 16 * ib + li;
         float pv[4];
 #pragma unroll
