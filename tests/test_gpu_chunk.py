@@ -108,6 +108,18 @@ def test_forward_device_only_boundaries_match_host_route_bitwise():
     assert torch.equal(o1, o2) and torch.equal(h1, h2)
 
 
+@pytest.mark.parametrize("H,HV", [(2, 4), (2, 6)])
+def test_forward_saving_for_the_backward_gives_the_same_bits(H, HV):
+    """A forward that saves for a backward writes the WY pass's tiles into the
+    saved buffer instead of the workspace (and adds T, T^T, gamma, beta); the
+    same arithmetic, so o and hT equal the forward without saving bit for bit."""
+    inp = small_inputs(H=H, HV=HV)
+    o1, h1, _ = run_fwd(inp, save=False)
+    o2, h2, saved = run_fwd(inp, save=True)
+    assert saved is not None
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
 def test_forward_strong_decay_is_finite():
     inp = small_inputs()
     inp["g"] = torch.full_like(inp["g"], -60.0)
