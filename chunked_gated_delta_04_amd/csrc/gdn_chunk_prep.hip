@@ -136,10 +136,14 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ g,
     const float* __restrict__ beta, PrepOut fo, PrepOut bo) {
-  const int c = blockIdx.x, h = blockIdx.y;
-  const ChunkInfo ci = table[c];
+  // Items (chunk c, key head h) = c H + h, in steps of the grid size; the chunk
+  // slots past the pack's chunks are the last ones, so a workgroup stops at
+  // its first empty item.
+  const int NI = NC * H;
+  int it = blockIdx.x;
+  if (it >= NI) return;
+  ChunkInfo ci = table[it / H];
   if (ci.seq < 0) return;
-  const int t0 = ci.t0, L = ci.len;
   const int tid = threadIdx.x;
 
   __shared__ __align__(16) uint16_t Ks[64 * KP];   // k^ rows (bf16)
@@ -151,15 +155,16 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
   __shared__ float Xs[3 * 256];  // solve scratch
 
   // A value head's own inputs - its v rows (thread: row tid / 8, 2 x 8 columns)
-  // and gates (wave 0) - through
-  // range-checked buffer loads: rows at or past the chunk's end read as zeros,
-  // and a zero range (live = false) moves no data. Requested one value head
-  // ahead, before the current head's stores: waiting for a load also waits
-  // for every store issued before it.
+  // and gates (wave 0) - and an item's q, k rows through range-checked buffer
+  // loads: rows at or past the chunk's end read as zeros, and a zero range
+  // (live = false) moves no data. Each value head's are requested one value
+  // head ahead, and the next item's q, k rows and first value head's inputs
+  // during the item's last value head, before that head's stores: waiting for
+  // a load also waits for every store issued before it.
   const int G = HV / H;
-  uint4 vx[2];
+  uint4 vx[2], kr[2], qr[2];
   float gq, bq;
-  auto request = [&](int hv_, bool live) {
+  auto request = [&](int t0, int L, int hv_, bool live) {
     const int n = live ? L : 0;
     const int vr0 = tid / kRowThreads, vsg0 = tid % kRowThreads, lane = tid & 63;
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
@@ -177,25 +182,28 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
     gq = load_f32(rg, goff);
     bq = load_f32(rb, goff);
   };
-
-  // ---- 1. load and L2-normalise q, k rows (thread: row tid / 8, 2 x 8 columns);
-  //      one division per row, then products with the reciprocal. The first
-  //      value head's requests follow the q, k rows, so the norms wait only
-  //      for those.
-  {
+  auto request_qk = [&](int t0, int L, int h, bool live) {
+    const int n = live ? L : 0;
     const int r = tid / kRowThreads, sg0 = tid % kRowThreads;
-    uint4 kr[2], qr[2];
-    float sk = 0.f, sq = 0.f;
     const __amdgpu_buffer_rsrc_t krng = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(k) + ((size_t)t0 * H + h) * kHead, 0, L * H * kHead * 2, kBufferWord3);
+        const_cast<uint16_t*>(k) + ((size_t)t0 * H + h) * kHead, 0, n * H * kHead * 2, kBufferWord3);
     const __amdgpu_buffer_rsrc_t qrng = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(q) + ((size_t)t0 * H + h) * kHead, 0, L * H * kHead * 2, kBufferWord3);
+        const_cast<uint16_t*>(q) + ((size_t)t0 * H + h) * kHead, 0, n * H * kHead * 2, kBufferWord3);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       kr[j] = load_b128(krng, (r * H * kHead + (sg0 + kRowThreads * j) * 8) * 2);
       qr[j] = load_b128(qrng, (r * H * kHead + (sg0 + kRowThreads * j) * 8) * 2);
     }
-    request(h * G, true);
+  };
+
+  // ---- 1. L2-normalise the item's q, k rows (thread: row tid / 8, 2 x 8
+  //      columns), requested before; one division per row, then products with
+  //      the reciprocal. Also waits for the item's first value head's inputs,
+  //      requested with them, so that no later wait of the item counts them.
+  auto norm_rows = [&]() {
+    const int r = tid / kRowThreads, sg0 = tid % kRowThreads;
+    float sk = 0.f, sq = 0.f;
+    asm volatile("" ::"v"(vx[0].x), "v"(vx[1].x), "v"(gq), "v"(bq));
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[j]);
@@ -226,211 +234,237 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
       *reinterpret_cast<uint4*>(&Ks[r * KP + (sg0 + kRowThreads * j) * 8]) = ko;
       *reinterpret_cast<uint4*>(&Qs[r * KP + (sg0 + kRowThreads * j) * 8]) = qo;
     }
-  }
-  __syncthreads();
+    __syncthreads();
+  };
 
-  // K^K^T and Q~K^T tiles of the key head, formed once for all its value heads:
-  // kk[n] belongs to job wave + n kPrepWaves of step 3 below (an A tile for
-  // jobs 0-9, a P tile at or below the diagonal for jobs 16-31, nothing else)
-  constexpr int kJobs = 32 / kPrepWaves;
-  f32x4 kk[kJobs];
   {
-    const int wave = tid >> 6, lane = tid & 63;
-    const int li = lane & 15, kq = lane >> 4;
+    const int h = it % H;
+    request_qk(ci.t0, ci.len, h, true);
+    request(ci.t0, ci.len, h * G, true);
+  }
+  norm_rows();
+
+  for (;;) {
+    const int c = it / H, h = it - c * H;
+    const int t0 = ci.t0, L = ci.len;
+    // the next item, whose rows the last value head requests
+    const int itn = it + (int)gridDim.x;
+    const ChunkInfo cin = itn < NI ? table[itn / H] : ChunkInfo{-1, 0, 0, 0};
+    const bool next = cin.seq >= 0;
+
+    // K^K^T and Q~K^T tiles of the key head, formed once for all its value heads:
+    // kk[n] belongs to job wave + n kPrepWaves of step 3 below (an A tile for
+    // jobs 0-9, a P tile at or below the diagonal for jobs 16-31, nothing else)
+    constexpr int kJobs = 32 / kPrepWaves;
+    f32x4 kk[kJobs];
+    {
+      const int wave = tid >> 6, lane = tid & 63;
+      const int li = lane & 15, kq = lane >> 4;
 #pragma unroll
-    for (int n = 0; n < kJobs; ++n) {
-      const int job = wave + kPrepWaves * n;
-      f32x4 acc = zero4();
-      if (job < 10) {
-        int ib, jb;
-        lower_tile(job, ib, jb);
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          acc = mfma(ld8(&Ks[(16 * ib + li) * KP + 32 * s + 8 * kq]),
-                     ld8(&Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), acc);
-      } else if (job >= 16) {
-        const int pt = job - 16, ib = pt >> 2, jb = pt & 3;
-        if (jb <= ib) {
+      for (int n = 0; n < kJobs; ++n) {
+        const int job = wave + kPrepWaves * n;
+        f32x4 acc = zero4();
+        if (job < 10) {
+          int ib, jb;
+          lower_tile(job, ib, jb);
 #pragma unroll
           for (int s = 0; s < 4; ++s)
-            acc = mfma(ld8(&Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]),
-                       ld8(&Qs[(16 * ib + li) * KP + 32 * s + 8 * kq]), acc);
+            acc = mfma(ld8(&Ks[(16 * ib + li) * KP + 32 * s + 8 * kq]),
+                       ld8(&Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]), acc);
+        } else if (job >= 16) {
+          const int pt = job - 16, ib = pt >> 2, jb = pt & 3;
+          if (jb <= ib) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              acc = mfma(ld8(&Ks[(16 * jb + li) * KP + 32 * s + 8 * kq]),
+                         ld8(&Qs[(16 * ib + li) * KP + 32 * s + 8 * kq]), acc);
+          }
         }
+        kk[n] = acc;
       }
-      kk[n] = acc;
     }
-  }
 
-  for (int jg = 0; jg < G; ++jg) {
-    // Re-derive the thread coordinates from an opaque copy each iteration, so
-    // that the many LDS and global addresses built from them are formed where
-    // they are used instead of being hoisted and kept live across the loop.
-    int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));
-    const int wave = tid >> 6, lane = tid & 63;
-    const int li = lane & 15, kq = lane >> 4;
-    const int hv = h * G + jg;
-    const size_t blk = (size_t)hv * NC + c;
+    for (int jg = 0; jg < G; ++jg) {
+      // Re-derive the thread coordinates from an opaque copy each iteration, so
+      // that the many LDS and global addresses built from them are formed where
+      // they are used instead of being hoisted and kept live across the loop.
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      const int wave = tid >> 6, lane = tid & 63;
+      const int li = lane & 15, kq = lane >> 4;
+      const int hv = h * G + jg;
+      const size_t blk = (size_t)hv * NC + c;
 
-    // ---- 2. gates: gamma = inclusive cumsum of g inside the chunk (kept in
-    //      base 2); the value rows go to LDS as they are. This head's v rows
-    //      and gates were requested before; the next head's are requested now.
-    const int vr0 = tid / kRowThreads, vsg0 = tid % kRowThreads;
-    const uint4 vc0 = vx[0], vc1 = vx[1];
-    float gv = gq;
-    const float bv = bq;
-    request(min(hv + 1, h * G + G - 1), jg + 1 < G);
-    if (wave == 0) {
-      gv = wave_prefix_sum(gv, lane);
-      const float g2 = gv * kLog2e;
-      const float gl2 = lane_value(g2, L - 1);
-      gam[lane] = g2;
-      bet[lane] = bv;
-      const float e = exp2_fast(g2);
-      fw[lane] = bv * e;
-      const float bw = lane < L ? exp2_fast(gl2 - g2) : 0.f;
-      fo.gE[blk * kGates + lane] = e;
-      fo.gE[blk * kGates + kChunk + lane] = bw;
-      if (kB) {
-        bo.gB[blk * kGates + lane] = g2;  // the gradient pass reads these as they are
-        bo.gB[blk * kGates + kChunk + lane] = bv;
-      }
-      if (lane == 0) fo.gL[blk] = exp2_fast(gl2);
-    }
-    *reinterpret_cast<uint4*>(&Vs[vr0 * KP + vsg0 * 8]) = vc0;
-    *reinterpret_cast<uint4*>(&Vs[vr0 * KP + (vsg0 + kRowThreads) * 8]) = vc1;
-    __syncthreads();
-
-    // ---- 3. A (fp32, LDS: 10 lower tiles, 6 zero upper tiles) and P (bf16,
-    //      global: the 10 lower tiles), 32 jobs over the waves, from the key
-    //      head's tiles kk formed above.
-#pragma unroll
-    for (int n = 0; n < kJobs; ++n) {
-      const int job = wave + kPrepWaves * n;
-      if (job < 10) {
-        int ib, jb;
-        lower_tile(job, ib, jb);
-        const f32x4 acc = kk[n];
-        const int j = 16 * jb + li;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * ib + 4 * kq + r;
-          Ts[i * FP + j] = i > j ? bet[i] * exp2_fast(gam[i] - gam[j]) * acc[r] : 0.f;
-        }
-      } else if (job < 16) {
-        // strictly upper 16 x 16 blocks: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
-        const int u = job - 10;
-        const int ib = u < 3 ? 0 : u < 5 ? 1 : 2;
-        const int jb = u < 3 ? u + 1 : u < 5 ? u - 1 : 3;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Ts[(16 * ib + 4 * kq + r) * FP + 16 * jb + li] = 0.f;
+      // ---- 2. gates: gamma = inclusive cumsum of g inside the chunk (kept in
+      //      base 2); the value rows go to LDS as they are. This head's v rows
+      //      and gates were requested before; the next head's are requested now.
+      const int vr0 = tid / kRowThreads, vsg0 = tid % kRowThreads;
+      const uint4 vc0 = vx[0], vc1 = vx[1];
+      float gv = gq;
+      const float bv = bq;
+      if (jg + 1 < G) {
+        request(t0, L, hv + 1, true);
       } else {
-        const int pt = job - 16, ib = pt >> 2, jb = pt & 3;  // P tile (row block ib, col block jb)
-        // C = K^ Q~^T tile: C[4kq+r][li] = P-row i = 16 ib + li, cols j = 16 jb + 4kq + r
-        const f32x4 acc = kk[n];
-        const int i = 16 * ib + li;
-        float pv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = 16 * jb + 4 * kq + r;
-          pv[r] = i >= j ? exp2_fast(gam[i] - gam[j]) * acc[r] : 0.f;
+        request_qk(cin.t0, cin.len, itn % H, next);
+        request(cin.t0, cin.len, (itn % H) * G, next);
+      }
+      if (wave == 0) {
+        gv = wave_prefix_sum(gv, lane);
+        const float g2 = gv * kLog2e;
+        const float gl2 = lane_value(g2, L - 1);
+        gam[lane] = g2;
+        bet[lane] = bv;
+        const float e = exp2_fast(g2);
+        fw[lane] = bv * e;
+        const float bw = lane < L ? exp2_fast(gl2 - g2) : 0.f;
+        fo.gE[blk * kGates + lane] = e;
+        fo.gE[blk * kGates + kChunk + lane] = bw;
+        if (kB) {
+          bo.gB[blk * kGates + lane] = g2;  // the gradient pass reads these as they are
+          bo.gB[blk * kGates + kChunk + lane] = bv;
         }
-        // (the tiles above the diagonal are zero and are not stored: their
-        // readers take zeros from past the end of a range-checked buffer)
-        if (jb <= ib) {
-          const uint2 pk = pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
-          st8_nt(fo.P + blk * (64 * 64) + kcm(i, 16 * jb + 4 * kq, 64), pk);
+        if (lane == 0) fo.gL[blk] = exp2_fast(gl2);
+      }
+      *reinterpret_cast<uint4*>(&Vs[vr0 * KP + vsg0 * 8]) = vc0;
+      *reinterpret_cast<uint4*>(&Vs[vr0 * KP + (vsg0 + kRowThreads) * 8]) = vc1;
+      __syncthreads();
+
+      // ---- 3. A (fp32, LDS: 10 lower tiles, 6 zero upper tiles) and P (bf16,
+      //      global: the 10 lower tiles), 32 jobs over the waves, from the key
+      //      head's tiles kk formed above.
+#pragma unroll
+      for (int n = 0; n < kJobs; ++n) {
+        const int job = wave + kPrepWaves * n;
+        if (job < 10) {
+          int ib, jb;
+          lower_tile(job, ib, jb);
+          const f32x4 acc = kk[n];
+          const int j = 16 * jb + li;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * ib + 4 * kq + r;
+            Ts[i * FP + j] = i > j ? bet[i] * exp2_fast(gam[i] - gam[j]) * acc[r] : 0.f;
+          }
+        } else if (job < 16) {
+          // strictly upper 16 x 16 blocks: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+          const int u = job - 10;
+          const int ib = u < 3 ? 0 : u < 5 ? 1 : 2;
+          const int jb = u < 3 ? u + 1 : u < 5 ? u - 1 : 3;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Ts[(16 * ib + 4 * kq + r) * FP + 16 * jb + li] = 0.f;
+        } else {
+          const int pt = job - 16, ib = pt >> 2, jb = pt & 3;  // P tile (row block ib, col block jb)
+          // C = K^ Q~^T tile: C[4kq+r][li] = P-row i = 16 ib + li, cols j = 16 jb + 4kq + r
+          const f32x4 acc = kk[n];
+          const int i = 16 * ib + li;
+          float pv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = 16 * jb + 4 * kq + r;
+            pv[r] = i >= j ? exp2_fast(gam[i] - gam[j]) * acc[r] : 0.f;
+          }
+          // (the tiles above the diagonal are zero and are not stored: their
+          // readers take zeros from past the end of a range-checked buffer)
+          if (jb <= ib) {
+            const uint2 pk = pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
+            st8_nt(fo.P + blk * (64 * 64) + kcm(i, 16 * jb + 4 * kq, 64), pk);
+          }
         }
       }
-    }
-    __syncthreads();
+      __syncthreads();
 
-    // ---- 4. T = (I + A)^-1 in place
-    invert_unit_lower_64(Ts, Xs, tid);
+      // ---- 4. T = (I + A)^-1 in place
+      invert_unit_lower_64(Ts, Xs, tid);
 
-    // T and T^T in bf16 for the backward's gradient pass: chunk (kc, r) of each
-    // holds row r, columns 8 kc .. 8 kc + 7 (the chunks of their zero 16 x 16
-    // tiles, above the diagonal of T and below that of T^T, are not stored)
-    if (kB) {
-      uint16_t* Tg = bo.T + blk * 8192;
+      // T and T^T in bf16 for the backward's gradient pass: chunk (kc, r) of each
+      // holds row r, columns 8 kc .. 8 kc + 7 (the chunks of their zero 16 x 16
+      // tiles, above the diagonal of T and below that of T^T, are not stored)
+      if (kB) {
+        uint16_t* Tg = bo.T + blk * 8192;
 #pragma unroll
-      for (int i = 0; i < 512 / kPrepThreads; ++i) {
-        const int e = tid + kPrepThreads * i;
-        const int kc = e >> 6, r = e & 63;
-        uint4 o4, t4;
-        uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
-        uint32_t* tw4 = reinterpret_cast<uint32_t*>(&t4);
+        for (int i = 0; i < 512 / kPrepThreads; ++i) {
+          const int e = tid + kPrepThreads * i;
+          const int kc = e >> 6, r = e & 63;
+          uint4 o4, t4;
+          uint32_t* ow = reinterpret_cast<uint32_t*>(&o4);
+          uint32_t* tw4 = reinterpret_cast<uint32_t*>(&t4);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int ja = 8 * kc + 2 * u;
-          ow[u] = pk2(Ts[r * FP + ja], Ts[r * FP + ja + 1]);
-          tw4[u] = pk2(Ts[ja * FP + r], Ts[(ja + 1) * FP + r]);
+          for (int u = 0; u < 4; ++u) {
+            const int ja = 8 * kc + 2 * u;
+            ow[u] = pk2(Ts[r * FP + ja], Ts[r * FP + ja + 1]);
+            tw4[u] = pk2(Ts[ja * FP + r], Ts[(ja + 1) * FP + r]);
+          }
+          if ((kc >> 1) <= (r >> 4)) st16_nt(Tg + kcm(r, 8 * kc, 64), o4);
+          if ((kc >> 1) >= (r >> 4)) st16_nt(Tg + 4096 + kcm(r, 8 * kc, 64), t4);
         }
-        if ((kc >> 1) <= (r >> 4)) st16_nt(Tg + kcm(r, 8 * kc, 64), o4);
-        if ((kc >> 1) >= (r >> 4)) st16_nt(Tg + 4096 + kcm(r, 8 * kc, 64), t4);
       }
-    }
 
-    // ---- 5. W = (T diag(beta e^gamma)) K^: the factor scales T's columns as
-    //      T becomes an MFMA operand, K^ is read by columns from its row tile.
-    //      32 tiles of 16 x 16 over the waves, contraction over the chunk.
-    for (int tt = wave; tt < 32; tt += kPrepWaves) {
-      // C = K^T (T')^T: C[4kq+r][li] = W[t = 16 tb + li][k = 16 db + 4kq + r]
-      const int db = tt >> 2, tb = tt & 3;
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const uint4 kc = lds_col8(Ks, KP, 32 * s + 8 * kq, 16 * db, lane);
-        acc = mfma(__builtin_bit_cast(bf16x8, kc),
-                   cvt8s(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq], &fw[32 * s + 8 * kq]), acc);
-      }
-      const uint2 pk = pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
-      st8_nt(fo.W + blk * 8192 + kcm(16 * tb + li, 16 * db + 4 * kq, 64), pk);
-    }
-
-    {
-      // ---- 6. U = (T diag(beta)) V, written as U^T [v][tok]
-      uint16_t* Ub = fo.U + blk * 8192;
-            for (int tt = wave; tt < 32; tt += kPrepWaves) {
-        // C = T' V: C[4kq+r][li] = U[t = 16 tb + 4kq + r][v = 16 vb + li] -> U^T[v][t..t+3]
-        const int tb = tt >> 3, vb = tt & 7;
+      // ---- 5. W = (T diag(beta e^gamma)) K^: the factor scales T's columns as
+      //      T becomes an MFMA operand, K^ is read by columns from its row tile.
+      //      32 tiles of 16 x 16 over the waves, contraction over the chunk.
+      for (int tt = wave; tt < 32; tt += kPrepWaves) {
+        // C = K^T (T')^T: C[4kq+r][li] = W[t = 16 tb + li][k = 16 db + 4kq + r]
+        const int db = tt >> 2, tb = tt & 3;
         f32x4 acc = zero4();
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const uint4 vc = lds_col8(Vs, KP, 32 * s + 8 * kq, 16 * vb, lane);
-          acc = mfma(cvt8s(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq], &bet[32 * s + 8 * kq]),
-                     __builtin_bit_cast(bf16x8, vc), acc);
+          const uint4 kc = lds_col8(Ks, KP, 32 * s + 8 * kq, 16 * db, lane);
+          acc = mfma(__builtin_bit_cast(bf16x8, kc),
+                     cvt8s(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq], &fw[32 * s + 8 * kq]), acc);
         }
-        st8_nt(Ub + kcm(16 * vb + li, 16 * tb + 4 * kq, 128), pack4_bf16(acc[0], acc[1], acc[2], acc[3]));
+        const uint2 pk = pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
+        st8_nt(fo.W + blk * 8192 + kcm(16 * tb + li, 16 * db + 4 * kq, 64), pk);
       }
-    }
-    __syncthreads();  // gates, A, T and V are rewritten for the next value head
-  }
 
-  // ---- Q~ (rows) and K^T of the key head, after the value heads so that no
-  //      load waits for these stores. K^T's pieces (column chunks of 8
-  //      tokens) come from the row tile with transposing LDS reads: a wave
-  //      covers one token group tg and 64 consecutive features.
-  {
-    const int wave = tid >> 6, lane = tid & 63;
-    const int li = lane & 15, kq = lane >> 4;
-    const size_t kblk = (size_t)h * NC + c;
-    auto rows_out = [&](const uint16_t* src, uint16_t* dst) {
-      for (int e = tid; e < 64 * 16; e += kPrepThreads) {
-        const int sg = e >> 6, t = e & 63;
-        st16_nt(dst + kcm(t, sg * 8, 64), *reinterpret_cast<const uint4*>(&src[t * KP + sg * 8]));
-      }
-    };
-    auto cols_out = [&](const uint16_t* src, uint16_t* dst) {
+      {
+        // ---- 6. U = (T diag(beta)) V, written as U^T [v][tok]
+        uint16_t* Ub = fo.U + blk * 8192;
+        for (int tt = wave; tt < 32; tt += kPrepWaves) {
+          // C = T' V: C[4kq+r][li] = U[t = 16 tb + 4kq + r][v = 16 vb + li] -> U^T[v][t..t+3]
+          const int tb = tt >> 3, vb = tt & 7;
+          f32x4 acc = zero4();
 #pragma unroll
-      for (int i = 0; i < 1024 / kPrepThreads; ++i) {
-        const int e0 = kPrepThreads * i + 64 * wave;  // wave-uniform
-        const int tg = e0 >> 7, d0 = (e0 & 127) + 16 * kq;
-        st16_nt(dst + kcm(d0 + li, 8 * tg, 128), lds_col8(src, KP, 8 * tg, d0, lane));
+          for (int s = 0; s < 2; ++s) {
+            const uint4 vc = lds_col8(Vs, KP, 32 * s + 8 * kq, 16 * vb, lane);
+            acc = mfma(cvt8s(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq], &bet[32 * s + 8 * kq]),
+                       __builtin_bit_cast(bf16x8, vc), acc);
+          }
+          st8_nt(Ub + kcm(16 * vb + li, 16 * tb + 4 * kq, 128), pack4_bf16(acc[0], acc[1], acc[2], acc[3]));
+        }
       }
-    };
-    rows_out(Qs, fo.Qn + kblk * 8192);   // Q~ [tok][k]
-    cols_out(Ks, fo.Kn + kblk * 8192);   // K^T [k][tok]
+      __syncthreads();  // gates, A, T and V are rewritten for the next value head
+    }
+
+    // ---- Q~ (rows) and K^T of the key head, after the value heads so that no
+    //      load waits for these stores. K^T's pieces (column chunks of 8
+    //      tokens) come from the row tile with transposing LDS reads: a wave
+    //      covers one token group tg and 64 consecutive features.
+    {
+      const int wave = tid >> 6, lane = tid & 63;
+      const int li = lane & 15, kq = lane >> 4;
+      const size_t kblk = (size_t)h * NC + c;
+      auto rows_out = [&](const uint16_t* src, uint16_t* dst) {
+        for (int e = tid; e < 64 * 16; e += kPrepThreads) {
+          const int sg = e >> 6, t = e & 63;
+          st16_nt(dst + kcm(t, sg * 8, 64), *reinterpret_cast<const uint4*>(&src[t * KP + sg * 8]));
+        }
+      };
+      auto cols_out = [&](const uint16_t* src, uint16_t* dst) {
+#pragma unroll
+        for (int i = 0; i < 1024 / kPrepThreads; ++i) {
+          const int e0 = kPrepThreads * i + 64 * wave;  // wave-uniform
+          const int tg = e0 >> 7, d0 = (e0 & 127) + 16 * kq;
+          st16_nt(dst + kcm(d0 + li, 8 * tg, 128), lds_col8(src, KP, 8 * tg, d0, lane));
+        }
+      };
+      rows_out(Qs, fo.Qn + kblk * 8192);   // Q~ [tok][k]
+      cols_out(Ks, fo.Kn + kblk * 8192);   // K^T [k][tok]
+    }
+    if (!next) break;
+    __syncthreads();  // the next item's rows overwrite Ks and Qs
+    it = itn;
+    ci = cin;
+    norm_rows();
   }
 }
 
@@ -445,7 +479,15 @@ hipError_t launch_chunk_prep(PrepMode mode, const ChunkInfo* table, int NC, int 
                              float scale, const uint16_t* q, const uint16_t* k,
                              const uint16_t* v, const float* g, const float* beta,
                              const PrepOut& fwd_out, const PrepOut& bwd_out, hipStream_t stream) {
-  const dim3 grid(NC, H);
+  // two workgroups per CU (their LDS allows no third), each looping over the
+  // items c H + h, c H + h + grid, ...
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const long items = (long)NC * H;
+  if (items <= 0) return hipSuccess;
+  const dim3 grid((unsigned)std::max(1L, std::min(items, 2L * cus)));
   switch (mode) {
     case PrepMode::kForward:
       hipLaunchKernelGGL((chunk_prep_kernel<false>), grid, dim3(kPrepThreads), 0, stream, table, NC, H, HV,
