@@ -89,15 +89,42 @@ STAGE_KERNELS = {"chunk_table": "chunk_table_kernel", "chunk_prep": "chunk_prep_
                  "bwd_dh_scan": "bwd_dh_scan_kernel", "bwd_chunk": "bwd_chunk_kernel"}
 
 
+def _code_tokens(text):
+    """C/HIP source with comments removed and whitespace runs collapsed (string
+    and character literals kept whole), so that editing a comment leaves the
+    hash below unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash():
-    """Hash of the HIP sources, to tie recorded counters to the code they measured."""
+    """Hash of the HIP sources' code (comments and layout ignored), to tie
+    recorded counters to the code they measured."""
     import glob
     import hashlib
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "chunked_gated_delta_04_amd", "csrc", "*"))):
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8", errors="replace") as fh:
+            h.update(_code_tokens(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -17,11 +17,12 @@
 // commit). Chunks restart at each sequence start; the last chunk of a
 // sequence may be short and is zero-padded, which leaves every product exact.
 //
-// One workgroup (8 waves) handles one chunk of one key head: q and k are
-// normalised once and K^K^T / Q~K^T are formed once on MFMA (held in
-// registers), then each value head of the key head gets its gates, A, T and
-// the products above. Only e^x of x <= 0 (i >= j) is formed, so strong decays
-// underflow to 0.
+// A workgroup (8 waves; two per CU, each looping over (chunk, key head)
+// items) handles one chunk of one key head at a time: q and k are normalised
+// once and K^K^T / Q~K^T are formed once on MFMA (held in registers), then
+// each value head of the key head gets its gates, A, T and the products
+// above. Only e^x of x <= 0 (i >= j) is formed, so strong decays underflow
+// to 0.
 //
 // Outputs, bf16 unless noted, in the layouts the forward scan reads with one
 // 16-byte load per MFMA operand; the dh scan reads the same tiles and takes

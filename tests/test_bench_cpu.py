@@ -81,3 +81,14 @@ def test_profile_sections_are_offered(section):
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"],
                        capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and section in r.stdout
+
+
+def test_source_hash_ignores_comments_but_not_code():
+    """A comment edit keeps recorded counters valid; a code edit voids them."""
+    base = "int f(int a) { return a + 1; } // one\n/* two */ const char* s = \"// x\";\n"
+    same = "int f(int a)   {\n  return a + 1;   }  // edited\nconst char* s = \"// x\"; /* new */\n"
+    code = base.replace("a + 1", "a + 2")
+    lit = base.replace("\"// x\"", "\"// y\"")
+    assert bench._code_tokens(base) == bench._code_tokens(same)
+    assert bench._code_tokens(base) != bench._code_tokens(code)
+    assert bench._code_tokens(base) != bench._code_tokens(lit)
