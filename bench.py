@@ -50,8 +50,8 @@ F_FWDBWD = 3 * F_FWD
 # per-kernel shares of the model (forward: WY pass vs scan; backward: its two kernels
 # split the 2 * F_FWD gradient work as the gradient contractions are assigned to them)
 KERNEL_FLOPS = {
-    "chunk_prep": F_KKT + F_TSOLVE + 3 * F_TRI,                 # K K^T, T, W, U, Q K^T
-    "fwd_scan": F_TRI + 3 * F_STATE,                            # attn D, W h, Q h, K^T D
+    "chunk_prep": F_KKT + F_TSOLVE + 2 * F_TRI,                 # K K^T, T, W, Q K^T
+    "fwd_scan": 2 * F_TRI + 3 * F_STATE,                        # U, attn D, W h, Q h, K^T D
     "bwd_dh_scan": F_TRI + 3 * F_STATE,                         # P^T dO, K dh, Q^T dO, W^T dD
     "bwd_chunk": 2 * F_FWD - (F_TRI + 3 * F_STATE),             # the remaining gradient work
 }
@@ -62,8 +62,8 @@ def method_bytes(T, N, H, HV, n_chunks):
     input read once, every output written once, and the per-chunk states h_c
     (bf16) written by the forward and read by the backward. Per kernel, the part
     of those the kernel's job needs - what it could not avoid moving whatever
-    the design: the WY pass reads q, k, v, g, beta; the forward scan reads h0
-    and writes o, hT, h_c; the dh scan reads q, k, g, beta and dO and writes
+    the design: the WY pass reads q, k, g, beta; the forward scan reads v and
+    h0 and writes o, hT, h_c; the dh scan reads q, k, g, beta and dO and writes
     dh0; the gradient pass reads q, k, v, g, beta, dO and h_c and writes dq, dk,
     dv, dg, dbeta. The step counts each tensor once per pass that must move it
     (the forward reads the inputs, the backward reads them again)."""
@@ -73,8 +73,8 @@ def method_bytes(T, N, H, HV, n_chunks):
     st = N * HV * D * D * 4              # h0, hT, dh0 (fp32 states)
     hc = n_chunks * HV * D * D * 2       # per-chunk start states, bf16
     per = {
-        "chunk_prep": 2 * qk + vv + 2 * gb,
-        "fwd_scan": st + vv + st + hc,
+        "chunk_prep": 2 * qk + 2 * gb,
+        "fwd_scan": vv + st + vv + st + hc,
         "bwd_dh_scan": 2 * qk + 2 * gb + vv + st,
         "bwd_chunk": 2 * qk + vv + 2 * gb + vv + hc + 2 * qk + vv + 2 * gb,
     }

@@ -28,7 +28,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
-  size_t table, seq_first, W, U, Qn, P, Kn, gL, gE, T, dh, dD, dDT, total;
+  size_t table, seq_first, W, T, Qn, P, Kn, gL, gE, dh, dD, dDT, total;
 };
 
 // Chunk slots: the bound T/64 + N (sum of ceil(L_n / 64) <= T/64 + N), with or
@@ -70,17 +70,17 @@ Layout make_layout(const gdn_problem* p, int64_t NC, bool bwd) {
   size_t off = 0;
   L.table = off;     off = align_up(off + sizeof(ChunkInfo) * (size_t)NC);
   L.seq_first = off; off = align_up(off + sizeof(int32_t) * (size_t)(p->N + 1));
-  L.W = L.U = L.Qn = L.P = L.Kn = L.gL = L.gE = off;
+  L.W = L.T = L.Qn = L.P = L.Kn = L.gL = L.gE = off;
   if (!bwd) {
     L.W = off;       off = align_up(off + 2 * kBlk64x128 * blocks);
-    L.U = off;       off = align_up(off + 2 * kBlk64x128 * blocks);
+    L.T = off;       off = align_up(off + 2 * 2 * kBlk64x64 * blocks);  // T (T^T's half unused)
     L.Qn = off;      off = align_up(off + 2 * kBlk64x128 * kblocks);
     L.P = off;       off = align_up(off + 2 * kBlk64x64 * blocks);
     L.Kn = off;      off = align_up(off + 2 * kBlk64x128 * kblocks);
     L.gL = off;      off = align_up(off + sizeof(float) * blocks);
     L.gE = off;      off = align_up(off + sizeof(float) * kGates * blocks);
   }
-  L.T = L.dh = L.dD = L.dDT = off;
+  L.dh = L.dD = L.dDT = off;
   if (bwd) {
     L.dh = off;      off = align_up(off + 2 * kState * blocks);
     L.dD = off;      off = align_up(off + 2 * kBlk64x128 * blocks);
@@ -93,13 +93,12 @@ Layout make_layout(const gdn_problem* p, int64_t NC, bool bwd) {
 PrepOut prep_views(char* ws, const Layout& L, const gdn_problem* p) {
   PrepOut o;
   o.W = reinterpret_cast<uint16_t*>(ws + L.W);
-  o.U = reinterpret_cast<uint16_t*>(ws + L.U);
+  o.T = reinterpret_cast<uint16_t*>(ws + L.T);
   o.Qn = reinterpret_cast<uint16_t*>(ws + L.Qn);
   o.P = reinterpret_cast<uint16_t*>(ws + L.P);
   o.Kn = reinterpret_cast<uint16_t*>(ws + L.Kn);
   o.gL = reinterpret_cast<float*>(ws + L.gL);
   o.gE = reinterpret_cast<float*>(ws + L.gE);
-  o.T = nullptr;
   o.gB = nullptr;
   o.G = p->HV / p->H;
   return o;
@@ -109,17 +108,17 @@ PrepOut prep_views(char* ws, const Layout& L, const gdn_problem* p) {
 // elements each); then the WY operands the forward scan reads and the
 // backward reads again: per (value head, chunk) W [tok][k] (64 x 128) and
 // P [i][j] (64 x 64), per (key head, chunk) Q~ [tok][k] and K^T [k][tok]
-// (64 x 128 each); then, for the backward only, per (value head, chunk) T and
-// T^T (2 x 64 x 64); then in fp32 per (value head, chunk) e^gamma_L, the
-// kGates gate factors, and the cumulative decay gamma (base 2) and beta
-// (kGates more).
+// (64 x 128 each); then per (value head, chunk) T and T^T (2 x 64 x 64, T
+// read by both, T^T by the backward only); then in fp32 per (value head,
+// chunk) e^gamma_L, the kGates gate factors (e^gamma, e^(gamma_L - gamma),
+// beta), and the cumulative decay gamma (base 2) and beta (kGatesB).
 // the gate factors start 16-byte aligned after the e^gamma_L values
 size_t gates_offset(size_t blocks) { return (blocks + 3) / 4 * 4; }
 size_t saved_bytes(const gdn_problem* p, int64_t NC) {
   const size_t blocks = (size_t)p->HV * (size_t)NC, kblocks = (size_t)p->H * (size_t)NC;
   return (blocks * ((size_t)kSavedBlock + kBlk64x128 + 3 * kBlk64x64) +
           kblocks * 2 * kBlk64x128) * 2 +
-         (gates_offset(blocks) + 2 * blocks * kGates) * sizeof(float);
+         (gates_offset(blocks) + blocks * (kGates + kGatesB)) * sizeof(float);
 }
 PrepOut saved_views(uint16_t* saved, const gdn_problem* p, int64_t NC) {
   const size_t blocks = (size_t)p->HV * (size_t)NC, kblocks = (size_t)p->H * (size_t)NC;
@@ -133,16 +132,16 @@ PrepOut saved_views(uint16_t* saved, const gdn_problem* p, int64_t NC) {
   o.gL = reinterpret_cast<float*>(b);
   o.gE = o.gL + gates_offset(blocks);
   o.gB = o.gE + blocks * kGates;
-  o.U = nullptr;
   o.G = p->HV / p->H;
   return o;
 }
 
-// The forward's WY pass views when it saves for a backward: the operands both
-// passes read (W, P, Q~, K^T and the gate factors) go to `saved`, U stays in
-// the workspace.
+// The forward's WY pass views when it saves for a backward: every operand the
+// forward scan reads (W, T, P, Q~, K^T and the gate factors) goes to `saved`,
+// which the backward reads again.
 PrepOut forward_views_saving(PrepOut f, const PrepOut& sv) {
   f.W = sv.W;
+  f.T = sv.T;
   f.P = sv.P;
   f.Qn = sv.Qn;
   f.Kn = sv.Kn;
@@ -314,11 +313,11 @@ static int chunk_fwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_
   if (NC > 0)
     GDN_TRY(clk.run([&] {
       return launch_chunk_prep(saved ? PrepMode::kBoth : PrepMode::kForward, table, (int)NC, p->H,
-                               p->HV, effective_scale(p), q, k, v, g, beta, prep, bprep, s);
+                               p->HV, effective_scale(p), q, k, g, beta, prep, bprep, s);
     }));
   GDN_TRY(clk.run([&] {
     return launch_fwd_scan(saved ? ScanMode::kOutSave : ScanMode::kOut, seq_first, p->N, p->HV,
-                           (int)NC, table, prep, sr, o, saved, s);
+                           (int)NC, table, prep, v, sr, o, saved, s);
   }));
   if (n_stages) *n_stages = clk.n;
   return GDN_OK;
@@ -438,13 +437,13 @@ GDN_API int gdn_chunk_transition(const gdn_problem* p, const uint16_t* q, const 
   if (launch_chunk_table(p->cu_seqlens, p->N, p->T, (int)NC, table, seq_first, s) != hipSuccess)
     return GDN_ERR_HIP;
   if (NC > 0 && launch_chunk_prep(PrepMode::kForward, table, (int)NC, p->H, p->HV,
-                                  effective_scale(p), q, k, v, g, beta, prep, PrepOut{}, s) !=
+                                  effective_scale(p), q, k, g, beta, prep, PrepOut{}, s) !=
                     hipSuccess)
     return GDN_ERR_HIP;
   StateRef sr{};
   sr.hT = s_end;
   sr.M = M;
-  if (launch_fwd_scan(ScanMode::kTransition, seq_first, p->N, p->HV, (int)NC, table, prep, sr,
+  if (launch_fwd_scan(ScanMode::kTransition, seq_first, p->N, p->HV, (int)NC, table, prep, v, sr,
                       nullptr, nullptr, s) != hipSuccess)
     return GDN_ERR_HIP;
   return GDN_OK;
@@ -495,20 +494,19 @@ static int chunk_bwd_impl(const gdn_problem* p, const uint16_t* q, const uint16_
   }));
   if (recompute) {
     // the forward's WY pass (saving) and a save-only scan rebuild `saved`
-    // after both workspace layouts; the forward's U occupies the workspace's
-    // start until the scan has read it, then the backward's scratch takes
-    // that place
+    // after both workspace layouts; a saving WY pass writes all its operands
+    // there, so the backward's scratch at the workspace's start is free
     uint16_t* rebuilt = reinterpret_cast<uint16_t*>(ws + recompute_saved_offset(p, NC));
     const PrepOut rv = saved_views(rebuilt, p, NC);
     const PrepOut fprep = forward_views_saving(prep_views(ws, make_layout(p, NC, false), p), rv);
     GDN_TRY(clk.run([&] {
-      return launch_chunk_prep(PrepMode::kBoth, table, (int)NC, p->H, p->HV, scale, q, k, v, g,
+      return launch_chunk_prep(PrepMode::kBoth, table, (int)NC, p->H, p->HV, scale, q, k, g,
                                beta, fprep, rv, s);
     }));
     StateRef sr{};
     sr.h0 = recompute_h0;
     GDN_TRY(clk.run([&] {
-      return launch_fwd_scan(ScanMode::kSave, seq_first, p->N, p->HV, (int)NC, table, fprep, sr,
+      return launch_fwd_scan(ScanMode::kSave, seq_first, p->N, p->HV, (int)NC, table, fprep, v, sr,
                              nullptr, rebuilt, s);
     }));
     saved = rebuilt;

@@ -658,8 +658,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       //      wait does not cover the operand requests below: gamma (base 2),
       //      beta, e^gamma and e^(gamma_L - gamma) of each token as the forward's
       //      WY pass formed them, four contiguous 256-byte rows
-      const float gam_t = gB[blk * kGates + lane];
-      const float bet_t = gB[blk * kGates + kChunk + lane];
+      const float gam_t = gB[blk * kGatesB + lane];
+      const float bet_t = gB[blk * kGatesB + kChunk + lane];
       const float eg_t = gE[blk * kGates + lane];
       const float ebw_t = gE[blk * kGates + kChunk + lane];
 

@@ -1,6 +1,8 @@
 // Forward state scan with the fused output of the chunked gated delta rule.
 //
 // Per chunk, with h = S^T the K x V start state (fp32, kept in registers):
+//   U  = T diag(beta) V              (no state needed: formed here from the
+//                                     WY pass's T and the raw value rows)
 //   D  = U - W h                     corrected values of the chunk
 //   O  = Q_g h + P D                 inter-chunk plus intra-chunk output
 //   h <- e^gamma_L h + K_bwd^T D     state at the next chunk's start
@@ -20,8 +22,9 @@
 // workgroups. Block b runs on XCD b % 8; the value blocks of one chain get
 // the same b % 8 so they share that XCD's L2 for the chunk operands they all
 // read. All operands come straight from global memory in MFMA fragment
-// layout (16 bytes per lane per operand); only S (bf16) and D pass through
-// LDS, where every wave needs all of them.
+// layout (16 bytes per lane per operand); only S (bf16), D and the block's
+// value rows (scaled by beta, contracted over the chunk's tokens, so read as
+// columns with transposing reads) pass through LDS.
 //
 // Transition mode (one GPU's share of a context-parallel forward): the end
 // state is affine in the start state, h_end = M_h h_0 + s, and the chunk map
@@ -39,13 +42,15 @@ namespace gdn {
 template <bool kSave, bool kOut, bool kTrans>
 __global__ __launch_bounds__(256) void fwd_scan_kernel(
     const int32_t* __restrict__ seq_first, int N, int HV, int NC,
-    const ChunkInfo* __restrict__ table, PrepOut prep, StateRef st,
+    const ChunkInfo* __restrict__ table, PrepOut prep, const uint16_t* __restrict__ v,
+    StateRef st,
     uint16_t* __restrict__ o, uint16_t* __restrict__ saved) {
   constexpr int VB = kScanVB;
   constexpr int NVB = kHead / VB;  // value blocks per head
   constexpr int VT = VB / 16;      // 16-wide value tiles per block
   constexpr int SP = 136;          // LDS pitch of S rows (bf16)
   constexpr int DP = 72;           // LDS pitch of D^T rows (bf16)
+  constexpr int VP = VB + 8;       // LDS pitch of the beta-scaled value rows (bf16)
 
   constexpr int NVBL = kTrans ? 2 * NVB : NVB;  // blocks per chain
   const int b = blockIdx.x;
@@ -65,6 +70,7 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
   __shared__ __align__(16) uint16_t Ss[VB * SP];  // S[v][k] of the chunk start (bf16)
   __shared__ __align__(16) uint16_t Ds[VB * DP];  // D^T[v][tok] (bf16)
   __shared__ __align__(16) uint16_t Es[VB * DP];  // (diag(e^(gamma_L - gamma)) D)^T (bf16)
+  __shared__ __align__(16) uint16_t Vs[kChunk * VP];  // diag(beta) V [tok][v - v0] (bf16)
 
   // start and end state of this chain (the paged form reads and writes one
   // pool slot in place: each thread reads its own elements before the scan
@@ -102,27 +108,40 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
       }
     }
 
+  // The chunks of one sequence are consecutive 64-token pieces, so a chunk's
+  // first token and length follow from the sequence's bounds without a table
+  // read on the chain's critical path.
+  const int c_begin = seq_first[seq], c_end = seq_first[seq + 1];
+  int bos = 0, eos = 0;
+  if (c_begin < c_end) {
+    const ChunkInfo first = table[c_begin], lastc = table[c_end - 1];
+    bos = first.t0;
+    eos = lastc.t0 + lastc.len;
+  }
+
   // Operands of one chunk in MFMA fragment layout. Two sets alternate: the
   // next chunk's set is requested before the current chunk computes. Every
   // chunk issues the same number of loads and stores, with no branch around
   // any of them, so the wait for a set counts exactly the memory operations
   // issued after it and never waits for a store to finish.
   struct Ops {
-    bf16x8 wa[4], qa[4], pa[2], ka[2][2];
-    uint2 u[VT];
+    uint4 vr;    // value row piece: token tid / 4, columns v0 + 8 (tid % 4) .. + 7
+    float bt;    // beta of that token
+    bf16x8 wa[4], qa[4], pa[2], ka[2][2], ta[2];
     float gl;
     float eg;    // e^gamma of token 16 wave + li (output rows)
     float4 ebw;  // e^(gamma_L - gamma) of tokens 16 wave + 4 kq .. + 3 (D rows)
     uint32_t pf;  // L2 warm-up word of a later chunk (see touch_line)
   };
   // This workgroup's share of a chunk's operand lines for the L2 warm-up: the
-  // value head's W, U^T, P and gate-factor lines (324) split over its value
-  // blocks, the key head's Q~ and K^T lines (256) over the workgroups of all its
-  // value heads. Lanes past the share all touch its first line (one request per
-  // wave instruction, the lanes' addresses being the same).
+  // value head's W lines (128), the stored lines of T and P (40 each), its gate
+  // factors (6) and value rows (128), split over its value blocks, and the key
+  // head's Q~ and K^T lines (256) over the workgroups of all its value heads.
+  // Lanes past the share all touch its first line (one request per wave
+  // instruction, the lanes' addresses being the same).
   const int vshare = (kTrans ? 2 * NVB : NVB);
   const int vpos = kTrans ? slot % NVBL : vb;
-  const int vlines = (324 + vshare - 1) / vshare;
+  const int vlines = (342 + vshare - 1) / vshare;
   const int kshares = NVBL * prep.G, kpos = (hv % prep.G) * NVBL + vpos;
   const int klines = (256 + kshares - 1) / kshares;
   auto warm_line = [&](int c) -> const void* {
@@ -130,12 +149,16 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     const size_t kblk = (size_t)(hv / prep.G) * NC + c;
     int i = tid < vlines + klines ? tid : 0;
     if (i < vlines) {
-      const int l = min(vpos * vlines + i, 323);
+      const int l = min(vpos * vlines + i, 341);
       if (l < 128) return prep.W + blk * 8192 + l * kLineElems16;
-      if (l < 256) return prep.U + blk * 8192 + (l - 128) * kLineElems16;
-      if (l < 320) return kOut ? (const void*)(prep.P + blk * 4096 + (l - 256) * kLineElems16)
+      if (l < 168) return prep.T + blk * 8192 + lower_tile_line(l - 128) * kLineElems16;
+      if (l < 208) return kOut ? (const void*)(prep.P + blk * 4096 + lower_tile_line(l - 168) * kLineElems16)
                                : (const void*)(prep.W + blk * 8192);
-      return prep.gE + blk * kGates + (l - 320) * kLineElems32;
+      if (l < 214) return prep.gE + blk * kGates + (l - 208) * kLineElems32;
+      // value rows: token (l - 214) / 2, half (l - 214) % 2 of its 256 bytes
+      const int t0 = bos + (c - c_begin) * kChunk, len = min(kChunk, eos - t0);
+      const int tok = (l - 214) >> 1;
+      return v + ((size_t)(t0 + (tok < len ? tok : 0)) * HV + hv) * kHead + 64 * ((l - 214) & 1);
     }
     const int l = min(kpos * klines + (i - vlines), 255);
     if (l < 128) return kOut ? (const void*)(prep.Qn + kblk * 8192 + l * kLineElems16)
@@ -148,10 +171,24 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     const size_t blk = (size_t)hv * NC + c;
     const size_t kblk = (size_t)(hv / prep.G) * NC + c;
     const uint16_t* Wb = prep.W + blk * 8192;
-    const uint16_t* Ub = prep.U + blk * 8192;
     const uint16_t* Qb = prep.Qn + kblk * 8192;  // Q~ [tok][k]
     const uint16_t* Pb = prep.P + blk * 4096;
     const uint16_t* Kb = prep.Kn + kblk * 8192;  // K^T [k][tok]
+    // The value row pieces and beta first: the step waits for them before its
+    // first barrier, for the rest only after it. Value rows at or past the
+    // chunk's end read as zeros, and so do all of them in a block of M's
+    // columns (U = 0 there).
+    {
+      const int t0 = bos + (c - c_begin) * kChunk;
+      const int n = mblk ? 0 : min(kChunk, eos - t0);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(v) + ((size_t)t0 * HV + hv) * kHead, 0, n * HV * kHead * 2,
+          kBufferWord3);
+      x.vr = load_b128(rv, ((tid >> 2) * HV * kHead + v0 + 8 * (tid & 3)) * 2);
+      // beta from the block's gate factors (64 consecutive floats), not from the
+      // input, whose betas of one value head are a line apart
+      x.bt = prep.gE[blk * kGates + 2 * kChunk + (tid >> 2)];
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       x.wa[s] = ld8(Wb + kcm(16 * wave + li, 32 * s + 8 * kq, 64));
@@ -172,9 +209,15 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
 #pragma unroll
       for (int s = 0; s < 2; ++s)
         x.ka[dt][s] = ld8(Kb + kcm(16 * (2 * wave + dt) + li, 32 * s + 8 * kq, 128));
+    {
+      // T [i][j]: the tiles above the diagonal are not stored and read as zeros
+      const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(prep.T + blk * 8192), 0, kChunk * kChunk * 2, kBufferWord3);
 #pragma unroll
-    for (int vt = 0; vt < VT; ++vt)
-      x.u[vt] = *reinterpret_cast<const uint2*>(Ub + kcm(v0 + 16 * vt + li, 16 * wave + 4 * kq, 128));
+      for (int s = 0; s < 2; ++s)
+        x.ta[s] = ld8_buf(rt, 2 * s + (kq >> 1) <= wave ? kcm(16 * wave + li, 32 * s + 8 * kq, 64) * 2
+                                                       : kChunk * kChunk * 2);
+    }
     x.gl = prep.gL[blk];
     const float* ge = prep.gE + blk * kGates;
     if constexpr (kOut) x.eg = ge[16 * wave + li];
@@ -182,23 +225,21 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     x.pf = touch_line(warm_line(pc));
   };
 
-  // The chunks of one sequence are consecutive 64-token pieces, so a chunk's
-  // first token and length follow from the sequence's bounds without a table
-  // read on the chain's critical path.
-  const int c_begin = seq_first[seq], c_end = seq_first[seq + 1];
-  int bos = 0, eos = 0;
-  if (c_begin < c_end) {
-    const ChunkInfo first = table[c_begin], lastc = table[c_end - 1];
-    bos = first.t0;
-    eos = lastc.t0 + lastc.len;
-  }
-
   auto step = [&](int c, const Ops& cur, int cn, Ops& nxt) {
     const int t0 = bos + (c - c_begin) * kChunk;
     const int len = min(kChunk, eos - t0);
     // the warm-up word nxt carries was requested two steps ago
     sink ^= nxt.pf;
-    // 1. chunk-start state -> LDS (bf16)
+    // 1. chunk-start state -> LDS (bf16), and the value rows scaled by beta
+    {
+      const uint32_t* vw = reinterpret_cast<const uint32_t*>(&cur.vr);
+      uint4 y;
+      uint32_t* yw = reinterpret_cast<uint32_t*>(&y);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        yw[e] = pk2(bf2f(vw[e] & 0xffffu) * cur.bt, bf2f(vw[e] >> 16) * cur.bt);
+      *reinterpret_cast<uint4*>(&Vs[(tid >> 2) * VP + 8 * (tid & 3)]) = y;
+    }
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -226,7 +267,9 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
       }
     }
 
-    // 2. D = U - W h; wave w owns tokens 16 w .. 16 w + 15. The state part of
+    // 2. D = U - W h with U = T (diag(beta) V); wave w owns tokens
+    //    16 w .. 16 w + 15 (T is lower triangular: tokens j > 16 w + 15
+    //    contribute nothing to U there). The state part of
     //    the output, (S Q~^T) diag(e^gamma), needs no D: it is formed here from
     //    the same S fragments, ahead of the barrier that D needs.
     f32x4 oq[VT];
@@ -248,10 +291,13 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
       a0 = mfma(cur.wa[2], sb[2], a0);
       a1 = mfma(cur.wa[3], sb[3], a1);
       const f32x4 acc = a0 + a1;
-      // acc[r] = (W h)[t = 16 w + 4 kq + r][v = 16 vt + li]
-      const uint2 u = mblk ? make_uint2(0u, 0u) : cur.u[vt];
-      const float d0 = bf2f(u.x & 0xffffu) - acc[0], d1 = bf2f(u.x >> 16) - acc[1];
-      const float d2 = bf2f(u.y & 0xffffu) - acc[2], d3 = bf2f(u.y >> 16) - acc[3];
+      // acc[r] = (W h)[t = 16 w + 4 kq + r][v = 16 vt + li], and u[r] = U there
+      f32x4 u = mfma(cur.ta[0], __builtin_bit_cast(bf16x8, lds_col8(Vs, VP, 8 * kq, 16 * vt, lane)),
+                     zero4());
+      if (wave >= 2)
+        u = mfma(cur.ta[1], __builtin_bit_cast(bf16x8, lds_col8(Vs, VP, 32 + 8 * kq, 16 * vt, lane)), u);
+      const float d0 = u[0] - acc[0], d1 = u[1] - acc[1];
+      const float d2 = u[2] - acc[2], d3 = u[3] - acc[3];
       const int ds = (16 * vt + li) * DP + 16 * wave + 4 * kq;
       *reinterpret_cast<uint2*>(&Ds[ds]) = pack4_bf16(d0, d1, d2, d3);
       *reinterpret_cast<uint2*>(&Es[ds]) = pack4_bf16(cur.ebw.x * d0, cur.ebw.y * d1,
@@ -315,9 +361,9 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
           acc = mfma(cur.ka[dt][s], ld8(&Es[(16 * vt + li) * DP + 32 * s + 8 * kq]), acc);
         h[dt][vt] = acc;
       }
-    // No barrier here: no wave reads Ss after the barrier above, and Ds, Es
-    // are rewritten only after the next chunk's first barrier, which every
-    // wave reaches after its reads of them.
+    // No barrier here: no wave reads Ss or Vs after the barrier above, and
+    // Ds, Es are rewritten only after the next chunk's first barrier, which
+    // every wave reaches after its reads of them.
   };
 
   if (c_begin < c_end) {
@@ -357,8 +403,9 @@ __global__ __launch_bounds__(256) void state_copy_kernel(const float* __restrict
 }
 
 hipError_t launch_fwd_scan(ScanMode mode, const int32_t* seq_first, int N, int HV, int NC,
-                           const ChunkInfo* table, const PrepOut& prep, const StateRef& st,
-                           uint16_t* o, uint16_t* saved, hipStream_t stream) {
+                           const ChunkInfo* table, const PrepOut& prep, const uint16_t* v,
+                           const StateRef& st, uint16_t* o, uint16_t* saved,
+                           hipStream_t stream) {
   const long chains = (long)N * HV;
   const long per_chain = (kHead / kScanVB) * (mode == ScanMode::kTransition ? 2 : 1);
   const long group = 8L * prep.G;  // chains per cycle over the XCDs (whole key heads)
@@ -366,19 +413,19 @@ hipError_t launch_fwd_scan(ScanMode mode, const int32_t* seq_first, int N, int H
   switch (mode) {
     case ScanMode::kOut:
       hipLaunchKernelGGL((fwd_scan_kernel<false, true, false>), grid, dim3(256), 0, stream,
-                         seq_first, N, HV, NC, table, prep, st, o, saved);
+                         seq_first, N, HV, NC, table, prep, v, st, o, saved);
       break;
     case ScanMode::kOutSave:
       hipLaunchKernelGGL((fwd_scan_kernel<true, true, false>), grid, dim3(256), 0, stream,
-                         seq_first, N, HV, NC, table, prep, st, o, saved);
+                         seq_first, N, HV, NC, table, prep, v, st, o, saved);
       break;
     case ScanMode::kSave:
       hipLaunchKernelGGL((fwd_scan_kernel<true, false, false>), grid, dim3(256), 0, stream,
-                         seq_first, N, HV, NC, table, prep, st, o, saved);
+                         seq_first, N, HV, NC, table, prep, v, st, o, saved);
       break;
     case ScanMode::kTransition:
       hipLaunchKernelGGL((fwd_scan_kernel<false, false, true>), grid, dim3(256), 0, stream,
-                         seq_first, N, HV, NC, table, prep, st, o, saved);
+                         seq_first, N, HV, NC, table, prep, v, st, o, saved);
       break;
   }
   return hipGetLastError();

@@ -9,7 +9,8 @@
 //   P_ij    = e^(gamma_i - gamma_j) q~_i . k^_j, i >= j
 //   Q_g     = diag(e^gamma) Q~,   K_bwd = diag(e^(gamma_L - gamma)) K^
 // The state-dependent part (D = U - W h, O = Q_g h + P D,
-// h' = e^gamma_L h + K_bwd^T D) runs in the scan kernels. This is the
+// h' = e^gamma_L h + K_bwd^T D) runs in the scan kernels, and so does U: the
+// forward scan forms it from T and the value rows it reads anyway. This is the
 // WY / UT-transform pass that the cake_gdn page (miles PR #3597, "What the
 // commits add") lists before its forward state scan, and the chunk
 // transition h' = (e^gamma_L I - K_bwd^T W) h + K_bwd^T U written on the
@@ -30,12 +31,11 @@
 // what the backward alone needs is written in addition (when the forward
 // saves for it). Per (value head, chunk) block:
 //   W        [64 tok][128 k]
-//   U        U^T [128 v][64 tok]           (forward scan only)
 //   P        [64 i][64 j]                  (the lower 16 x 16 tiles)
+//   T        T [i][j]                      (the lower 16 x 16 tiles), then
+//            T^T [j][i]                    (backward only; the upper tiles)
 //   gL       e^gamma_L (fp32)
-//   gE       e^gamma and e^(gamma_L - gamma) per token (fp32)
-//   T        T [i][j] and T^T [j][i]      (backward only; the lower, resp.
-//                                          upper, 16 x 16 tiles)
+//   gE       e^gamma, e^(gamma_L - gamma) and beta per token (fp32)
 //   gB       gamma (base 2) and beta per token (fp32; backward only)
 // and per (key head, chunk) block, shared by the key head's value heads:
 //   Q~       [64 tok][128 k]
@@ -127,16 +127,16 @@ constexpr int kRowThreads = kPrepThreads / 64;  // threads per token row, 2 x 16
                                                 // row, so a request covers whole lines)
 
 // Writes the forward scan's operands to fo and, with kB (a forward that saves
-// for a backward), what only the backward reads to bo (T, T^T, gamma and
-// beta), so that the backward does not form them again. The backward's dh
+// for a backward), what only the backward reads to bo (T^T, gamma and beta;
+// T itself goes to fo.T, which then points into bo's T blocks), so that the
+// backward does not form them again. The backward's dh
 // scan reads fo's W, P, Q~ and K^T themselves (transposed in LDS), so a
 // forward that saves points those into the saved buffer.
 template <bool kB>
 __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
     const ChunkInfo* __restrict__ table, int NC, int H, int HV, float scale,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const float* __restrict__ g,
-    const float* __restrict__ beta, PrepOut fo, PrepOut bo) {
+    const float* __restrict__ g, const float* __restrict__ beta, PrepOut fo, PrepOut bo) {
   // Items (chunk c, key head h) = c H + h, in steps of the grid size; the chunk
   // slots past the pack's chunks are the last ones, so a workgroup stops at
   // its first empty item.
@@ -150,29 +150,22 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
   __shared__ __align__(16) uint16_t Ks[64 * KP];   // k^ rows (bf16)
   __shared__ __align__(16) uint16_t Qs[64 * KP];   // q~ rows (bf16)
   __shared__ __align__(16) float Ts[64 * FP];      // A (strictly lower), inverted in place into T
-  __shared__ __align__(16) uint16_t Vs[64 * KP];   // v rows of the value head (bf16)
   // gates of the value head; gam is the cumulative log-decay in base 2
   __shared__ __align__(16) float gam[64], bet[64], fw[64];
   __shared__ float Xs[3 * 256];  // solve scratch
 
-  // A value head's own inputs - its v rows (thread: row tid / 8, 2 x 8 columns)
-  // and gates (wave 0) - and an item's q, k rows through range-checked buffer
-  // loads: rows at or past the chunk's end read as zeros, and a zero range
-  // (live = false) moves no data. Each value head's are requested one value
-  // head ahead, and the next item's q, k rows and first value head's inputs
-  // during the item's last value head, before that head's stores: waiting for
-  // a load also waits for every store issued before it.
+  // A value head's gates (wave 0) and an item's q, k rows through
+  // range-checked buffer loads: rows at or past the chunk's end read as zeros,
+  // and a zero range (live = false) moves no data. Each value head's gates are
+  // requested one value head ahead, and the next item's q, k rows and first
+  // value head's gates during the item's last value head, before that head's
+  // stores: waiting for a load also waits for every store issued before it.
   const int G = HV / H;
-  uint4 vx[2], kr[2], qr[2];
+  uint4 kr[2], qr[2];
   float gq, bq;
   auto request = [&](int t0, int L, int hv_, bool live) {
     const int n = live ? L : 0;
-    const int vr0 = tid / kRowThreads, vsg0 = tid % kRowThreads, lane = tid & 63;
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(v) + ((size_t)t0 * HV + hv_) * kHead, 0, n * HV * kHead * 2, kBufferWord3);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      vx[j] = load_b128(rv, (vr0 * HV * kHead + (vsg0 + kRowThreads * j) * 8) * 2);
+    const int lane = tid & 63;
     const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(g) + (size_t)t0 * HV + hv_, 0, n * HV * 4, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
@@ -204,7 +197,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
   auto norm_rows = [&]() {
     const int r = tid / kRowThreads, sg0 = tid % kRowThreads;
     float sk = 0.f, sq = 0.f;
-    asm volatile("" ::"v"(vx[0].x), "v"(vx[1].x), "v"(gq), "v"(bq));
+    asm volatile("" ::"v"(gq), "v"(bq));
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[j]);
@@ -297,10 +290,8 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
       const size_t blk = (size_t)hv * NC + c;
 
       // ---- 2. gates: gamma = inclusive cumsum of g inside the chunk (kept in
-      //      base 2); the value rows go to LDS as they are. This head's v rows
-      //      and gates were requested before; the next head's are requested now.
-      const int vr0 = tid / kRowThreads, vsg0 = tid % kRowThreads;
-      const uint4 vc0 = vx[0], vc1 = vx[1];
+      //      base 2). This head's gates were requested before; the next head's
+      //      are requested now.
       float gv = gq;
       const float bv = bq;
       if (jg + 1 < G) {
@@ -320,14 +311,13 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
         const float bw = lane < L ? exp2_fast(gl2 - g2) : 0.f;
         fo.gE[blk * kGates + lane] = e;
         fo.gE[blk * kGates + kChunk + lane] = bw;
+        fo.gE[blk * kGates + 2 * kChunk + lane] = bv;
         if (kB) {
-          bo.gB[blk * kGates + lane] = g2;  // the gradient pass reads these as they are
-          bo.gB[blk * kGates + kChunk + lane] = bv;
+          bo.gB[blk * kGatesB + lane] = g2;  // the gradient pass reads these as they are
+          bo.gB[blk * kGatesB + kChunk + lane] = bv;
         }
         if (lane == 0) fo.gL[blk] = exp2_fast(gl2);
       }
-      *reinterpret_cast<uint4*>(&Vs[vr0 * KP + vsg0 * 8]) = vc0;
-      *reinterpret_cast<uint4*>(&Vs[vr0 * KP + (vsg0 + kRowThreads) * 8]) = vc1;
       __syncthreads();
 
       // ---- 3. A (fp32, LDS: 10 lower tiles, 6 zero upper tiles) and P (bf16,
@@ -377,11 +367,11 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
       // ---- 4. T = (I + A)^-1 in place
       invert_unit_lower_64(Ts, Xs, tid);
 
-      // T and T^T in bf16 for the backward's gradient pass: chunk (kc, r) of each
-      // holds row r, columns 8 kc .. 8 kc + 7 (the chunks of their zero 16 x 16
-      // tiles, above the diagonal of T and below that of T^T, are not stored)
-      if (kB) {
-        uint16_t* Tg = bo.T + blk * 8192;
+      // T in bf16 for the forward scan (U = T diag(beta) V) and the backward's
+      // gradient pass, and T^T for the latter: chunk (kc, r) of each holds row
+      // r, columns 8 kc .. 8 kc + 7 (the chunks of their zero 16 x 16 tiles,
+      // above the diagonal of T and below that of T^T, are not stored)
+      {
 #pragma unroll
         for (int i = 0; i < 512 / kPrepThreads; ++i) {
           const int e = tid + kPrepThreads * i;
@@ -393,10 +383,10 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
           for (int u = 0; u < 4; ++u) {
             const int ja = 8 * kc + 2 * u;
             ow[u] = pk2(Ts[r * FP + ja], Ts[r * FP + ja + 1]);
-            tw4[u] = pk2(Ts[ja * FP + r], Ts[(ja + 1) * FP + r]);
+            if (kB) tw4[u] = pk2(Ts[ja * FP + r], Ts[(ja + 1) * FP + r]);
           }
-          if ((kc >> 1) <= (r >> 4)) st16_nt(Tg + kcm(r, 8 * kc, 64), o4);
-          if ((kc >> 1) >= (r >> 4)) st16_nt(Tg + 4096 + kcm(r, 8 * kc, 64), t4);
+          if ((kc >> 1) <= (r >> 4)) st16_nt(fo.T + blk * 8192 + kcm(r, 8 * kc, 64), o4);
+          if (kB && (kc >> 1) >= (r >> 4)) st16_nt(bo.T + blk * 8192 + 4096 + kcm(r, 8 * kc, 64), t4);
         }
       }
 
@@ -417,23 +407,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void chunk_prep_kernel(
         st8_nt(fo.W + blk * 8192 + kcm(16 * tb + li, 16 * db + 4 * kq, 64), pk);
       }
 
-      {
-        // ---- 6. U = (T diag(beta)) V, written as U^T [v][tok]
-        uint16_t* Ub = fo.U + blk * 8192;
-        for (int tt = wave; tt < 32; tt += kPrepWaves) {
-          // C = T' V: C[4kq+r][li] = U[t = 16 tb + 4kq + r][v = 16 vb + li] -> U^T[v][t..t+3]
-          const int tb = tt >> 3, vb = tt & 7;
-          f32x4 acc = zero4();
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const uint4 vc = lds_col8(Vs, KP, 32 * s + 8 * kq, 16 * vb, lane);
-            acc = mfma(cvt8s(&Ts[(16 * tb + li) * FP + 32 * s + 8 * kq], &bet[32 * s + 8 * kq]),
-                       __builtin_bit_cast(bf16x8, vc), acc);
-          }
-          st8_nt(Ub + kcm(16 * vb + li, 16 * tb + 4 * kq, 128), pack4_bf16(acc[0], acc[1], acc[2], acc[3]));
-        }
-      }
-      __syncthreads();  // gates, A, T and V are rewritten for the next value head
+      __syncthreads();  // gates, A and T are rewritten for the next value head
     }
 
     // ---- Q~ (rows) and K^T of the key head, after the value heads so that no
@@ -477,9 +451,9 @@ hipError_t launch_chunk_table(const int32_t* cu, int N, int T, int NC, ChunkInfo
 }
 
 hipError_t launch_chunk_prep(PrepMode mode, const ChunkInfo* table, int NC, int H, int HV,
-                             float scale, const uint16_t* q, const uint16_t* k,
-                             const uint16_t* v, const float* g, const float* beta,
-                             const PrepOut& fwd_out, const PrepOut& bwd_out, hipStream_t stream) {
+                             float scale, const uint16_t* q, const uint16_t* k, const float* g,
+                             const float* beta, const PrepOut& fwd_out, const PrepOut& bwd_out,
+                             hipStream_t stream) {
   // two workgroups per CU (their LDS allows no third), each looping over the
   // items c H + h, c H + h + grid, ...
   int dev = 0, cus = 0;
@@ -492,11 +466,11 @@ hipError_t launch_chunk_prep(PrepMode mode, const ChunkInfo* table, int NC, int 
   switch (mode) {
     case PrepMode::kForward:
       hipLaunchKernelGGL((chunk_prep_kernel<false>), grid, dim3(kPrepThreads), 0, stream, table, NC, H, HV,
-                         scale, q, k, v, g, beta, fwd_out, bwd_out);
+                         scale, q, k, g, beta, fwd_out, bwd_out);
       break;
     case PrepMode::kBoth:
       hipLaunchKernelGGL((chunk_prep_kernel<true>), grid, dim3(kPrepThreads), 0, stream, table, NC, H, HV,
-                         scale, q, k, v, g, beta, fwd_out, bwd_out);
+                         scale, q, k, g, beta, fwd_out, bwd_out);
       break;
   }
   return hipGetLastError();

@@ -22,7 +22,10 @@ constexpr int kHead = 128;   // K = V
 constexpr int kChunk = 64;   // tokens per chunk
 constexpr float kNormEps = 1e-6f;
 constexpr int kScanVB = 32;  // value columns per workgroup of the state scans
-constexpr int kGates = 2 * kChunk;  // per-token gate factors of a block: e^gamma, e^(gamma_L - gamma)
+// per-token gate factors of a block: e^gamma, e^(gamma_L - gamma), beta
+constexpr int kGates = 3 * kChunk;
+// per-token values of a block that only the backward reads: gamma (base 2), beta
+constexpr int kGatesB = 2 * kChunk;
 
 // Tile layout of every intermediate matrix that a kernel reads as MFMA
 // operands from global memory: an R x C tile (C the contraction axis) is
@@ -392,6 +395,24 @@ __device__ __forceinline__ float group_sum(float x) {
 // nothing) and the sink is consumed once at the end of the kernel.
 constexpr int kLineElems16 = 64;  // bf16 elements per 128-byte line
 constexpr int kLineElems32 = 32;  // fp32 elements per 128-byte line
+// Line l (0 .. 39) of the 40 128-byte lines that a 64 x 64 bf16 block holds
+// when only its 16 x 16 tiles at or below the diagonal are stored in the
+// chunk-major layout of kcm(): column chunk kc (1 KiB, 8 lines of 8 rows)
+// holds rows 16 (kc / 2) .. 63, i.e. its lines 2 (kc / 2) .. 7. Returns the
+// line's index in the block (0 .. 63).
+__device__ __forceinline__ int lower_tile_line(int l) {
+  int kc = 0;
+#pragma unroll
+  for (int x = 0; x < 7; ++x) {
+    const int n = 8 - 2 * (kc >> 1);
+    if (l >= n) {
+      l -= n;
+      ++kc;
+    }
+  }
+  return 8 * kc + 2 * (kc >> 1) + l;
+}
+
 __device__ __forceinline__ uint32_t touch_line(const void* p) {
   return *reinterpret_cast<const uint32_t*>(p);
 }

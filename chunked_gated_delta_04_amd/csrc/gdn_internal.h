@@ -15,17 +15,19 @@ namespace gdn {
 // layout of kcm() with its contraction axis chunked.
 struct PrepOut {
   uint16_t* W;   // value head: W [tok][k]
-  uint16_t* U;   // value head; forward only: U^T [v][tok]
   uint16_t* Qn;  // key head: Q~ [tok][k]
   uint16_t* P;   // value head: P [i][j] (its 16 x 16 tiles above the diagonal
                  // are zero and are not stored)
   uint16_t* Kn;  // key head: K^T [k][tok]
   float* gL;     // value head: e^gamma_L, 1 per block
-  float* gE;     // value head: e^gamma (64), then e^(gamma_L - gamma) (64, zero past
-                 // the chunk's end), 128 per block
-  uint16_t* T;   // value head, backward only: T [i][j] then T^T [j][i], 2 x 64 x 64
+  float* gE;     // value head: e^gamma (64), then e^(gamma_L - gamma) and beta (64
+                 // each, zero past the chunk's end), kGates = 192 per block
+  uint16_t* T;   // value head: T [i][j] (forward scan and backward; its 16 x 16 tiles
+                 // above the diagonal are zero and are not stored), then T^T [j][i]
+                 // (backward only), 2 x 64 x 64 per block
   float* gB;     // value head, backward only: the cumulative decay gamma in base 2
-                 // (64), then beta (64, zero past the chunk's end), 128 per block
+                 // (64), then beta (64, zero past the chunk's end), kGatesB = 128 per
+                 // block
   int G;         // value heads per key head
 };
 
@@ -39,14 +41,14 @@ struct BwdBufs {
 hipError_t launch_chunk_table(const int32_t* cu, int N, int T, int NC, ChunkInfo* table,
                               int32_t* seq_first, hipStream_t stream);
 
-// Whether the WY pass also writes what only the backward reads (T, T^T, the
+// Whether the WY pass also writes what only the backward reads (T^T, the
 // cumulative decay and beta), when the forward saves for a backward.
 enum class PrepMode { kForward, kBoth };
 
 hipError_t launch_chunk_prep(PrepMode mode, const ChunkInfo* table, int NC, int H, int HV,
-                             float scale, const uint16_t* q, const uint16_t* k,
-                             const uint16_t* v, const float* g, const float* beta,
-                             const PrepOut& fwd_out, const PrepOut& bwd_out, hipStream_t stream);
+                             float scale, const uint16_t* q, const uint16_t* k, const float* g,
+                             const float* beta, const PrepOut& fwd_out, const PrepOut& bwd_out,
+                             hipStream_t stream);
 
 // Where the forward scan takes each chain's start state and leaves its end
 // state. Direct: h0 / hT are [N, HV, V, K] (either NULL). Paged: h0 == hT is a
@@ -72,9 +74,11 @@ enum class ScanMode {
   kTransition,  // M and the zero-start end state, no o
 };
 
+// (v: the value rows the scan forms U = T diag(beta) V from)
 hipError_t launch_fwd_scan(ScanMode mode, const int32_t* seq_first, int N, int HV, int NC,
-                           const ChunkInfo* table, const PrepOut& prep, const StateRef& st,
-                           uint16_t* o, uint16_t* saved, hipStream_t stream);
+                           const ChunkInfo* table, const PrepOut& prep, const uint16_t* v,
+                           const StateRef& st, uint16_t* o, uint16_t* saved,
+                           hipStream_t stream);
 
 hipError_t launch_bwd_dh_scan(const int32_t* seq_first, int N, int HV, int NC,
                               const ChunkInfo* table, const PrepOut& prep, const uint16_t* dO,

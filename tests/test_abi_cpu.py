@@ -90,10 +90,11 @@ def test_chunk_counts_and_sizes(G):
     blocks = 4 * 4  # value heads x chunk slots
     kblocks = 2 * 4  # key heads x chunk slots
     # per value-head block: the bf16 start state and D, W, P, T, T^T in bf16,
-    # e^gamma_L, 128 per-token gate factors and 128 per-token gamma, beta in fp32
-    # (the factors start 16-byte aligned); per key-head block: Q~ and K^T in bf16
+    # e^gamma_L, 192 per-token gate factors (e^gamma, e^(gamma_L - gamma), beta)
+    # and 128 per-token gamma, beta in fp32 (the factors start 16-byte aligned);
+    # per key-head block: Q~ and K^T in bf16
     assert s == (blocks * ((128 * 128 + 64 * 128) + 64 * 128 + 3 * 64 * 64)
-                 + kblocks * 2 * 64 * 128) * 2 + ((blocks + 3) // 4 * 4 + 2 * blocks * 128) * 4
+                 + kblocks * 2 * 64 * 128) * 2 + ((blocks + 3) // 4 * 4 + blocks * (192 + 128)) * 4
     assert G.gdn_chunk_fwd_workspace_size(p) > 0
     assert G.gdn_chunk_bwd_workspace_size(p) > G.gdn_chunk_fwd_workspace_size(p) // 2
     assert G.gdn_chunk_fwd_workspace_size(p) == G.gdn_chunk_fwd_workspace_size(p)
