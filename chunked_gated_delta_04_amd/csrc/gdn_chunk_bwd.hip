@@ -585,21 +585,27 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     }
     lds_barrier();
 
-    // Gate gradients of value head hv_ (wave 0): fixed-order sums of the partial
-    // slots, then dg = reverse cumsum of dgamma inside the chunk. Run by wave 0
-    // at the top of the next value head (or after the last one): the slots and
-    // gamma are rewritten only after the next gate barrier, which wave 0 reaches
-    // after this, and the work overlaps the other waves' requests. t: the lane,
-    // from an opaque copy of the thread index (see the value-head loop), so that
+    // Gate gradients of value head hv_: fixed-order sums of the partial slots,
+    // then dg = reverse cumsum of dgamma inside the chunk (wave 0), and dbeta
+    // (wave 1), each wave storing one of the two. Run at the top of the next
+    // value head (or after the last one): the slots and gamma are rewritten only
+    // after the next gate barrier, which both waves reach after this, and the
+    // work overlaps the other waves' requests. Each store reaches 64 lines (a
+    // token's line holds every value head's value), and a wave's later loads
+    // wait for its stores, so the two go to different waves. t: the lane, from
+    // an opaque copy of the thread index (see the value-head loop), so that
     // none of the addresses below is hoisted out of the loop.
+    auto db_out = [&](int hv_, int t) {
+      const float dbt = (S.rowB[0][t] + S.rowB[1][t]) + (S.rowB2[0][t] + S.rowB2[1][t]) +
+                        (S.rowB3[0][t] + S.rowB3[1][t]);
+      if (t < L) dbeta[(size_t)(t0 + t) * HV + hv_] = dbt;
+    };
     auto dg_out = [&](int hv_, int t) {
       const int w0 = 4 * ((t >> 4) & 1);  // the waves whose column tiles hold t
       float dgm = (S.rowF[0][t] + S.rowF[1][t]) + (S.rowG[0][t] + S.rowG[1][t]) +
                   (S.rowE[0][t] + S.rowE[1][t]);
 #pragma unroll
       for (int w = 0; w < 4; ++w) dgm -= S.colF[w0 + w][t] + S.colE[w0 + w][t];
-      const float dbt = (S.rowB[0][t] + S.rowB[1][t]) + (S.rowB2[0][t] + S.rowB2[1][t]) +
-                        (S.rowB3[0][t] + S.rowB3[1][t]);
       float x = t < L ? dgm : 0.f;
       if (t == L - 1) {
         float glsum = 0.f, hdsum = 0.f;
@@ -611,10 +617,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         x += glsum + exp2_fast(S.gam[L - 1]) * hdsum;
       }
       x = wave_suffix_sum(x, t);
-      if (t < L) {
-        dg[(size_t)(t0 + t) * HV + hv_] = x;
-        dbeta[(size_t)(t0 + t) * HV + hv_] = dbt;
-      }
+      if (t < L) dg[(size_t)(t0 + t) * HV + hv_] = x;
     };
 
     // dq~, dk^ over the value heads: [j][r] = d[16 tw + 4 kq + r][16 (4 kh + j) + li]
@@ -712,6 +715,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         S.bet[lane] = bet_t;
         S.eg[lane] = eg_t;
         S.ebw[lane] = ebw_t;
+      } else if (wave == 1) {
+        if (jg > 0) db_out(hv - 1, lane);
       }
       lds_barrier();
 
@@ -1104,6 +1109,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
       int tid = threadIdx.x;
       asm volatile("" : "+v"(tid));
       if ((tid >> 6) == 0) dg_out(h * G + G - 1, tid & 63);
+      else if ((tid >> 6) == 1) db_out(h * G + G - 1, tid & 63);
     }
 
     // every wave is done with Hs, Gs, the P tiles and the dW / Y1^T region:
