@@ -86,7 +86,7 @@ def method_bytes(T, N, H, HV, n_chunks):
 # stage name (gdn_stage_name) -> kernel symbol as the profiler names it
 STAGE_KERNELS = {"chunk_table": "chunk_table_kernel", "chunk_prep": "chunk_prep_kernel<true>",
                  "fwd_scan": "fwd_scan_kernel<true, true, false>",
-                 "bwd_dh_scan": "bwd_dh_scan_kernel", "bwd_chunk": "bwd_chunk_kernel"}
+                 "bwd_dh_scan": "bwd_dh_scan_kernel", "bwd_chunk": "bwd_chunk_kernel<true>"}
 
 
 def _code_tokens(text):

@@ -408,7 +408,8 @@ struct BwdLds {
   float rowB[2][64];                        // dbeta of U
   float rowE[2][64], colE[8][64], rowB3[2][64];  // E = dA o A, dbeta of A
   float gl_part[8], hd_part[8];
-  float dot_q[2][64], dot_k[2][64];
+  float dot_q[2][64], dot_k[2][64];         // (dot_q also holds an even value head's
+                                            // dg, dbeta until its odd partner's)
 };
 
 // Column c0 + lane % 16 of a [64][KP] row tile: rows r0 .. r0 + 7 as an MFMA
@@ -432,6 +433,7 @@ __device__ __forceinline__ float dot8u(const uint4& a, const uint4& b) {  // bf1
 }
 }  // namespace
 
+template <bool kPair>
 __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     const ChunkInfo* __restrict__ table, int NC, int H, int HV, float scale,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -585,22 +587,36 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     }
     lds_barrier();
 
-    // Gate gradients of value head hv_: fixed-order sums of the partial slots,
-    // then dg = reverse cumsum of dgamma inside the chunk (wave 0), and dbeta
-    // (wave 1), each wave storing one of the two. Run at the top of the next
-    // value head (or after the last one): the slots and gamma are rewritten only
-    // after the next gate barrier, which both waves reach after this, and the
-    // work overlaps the other waves' requests. Each store reaches 64 lines (a
-    // token's line holds every value head's value), and a wave's later loads
-    // wait for its stores, so the two go to different waves. t: the lane, from
-    // an opaque copy of the thread index (see the value-head loop), so that
-    // none of the addresses below is hoisted out of the loop.
-    auto db_out = [&](int hv_, int t) {
+    // Gate gradients of value head hv_ (the item's jv-th): fixed-order sums of
+    // the partial slots, then dg = reverse cumsum of dgamma inside the chunk
+    // (wave 0), and dbeta (wave 1), each wave storing one of the two. Run at the
+    // top of the next value head (or after the last one): the slots and gamma
+    // are rewritten only after the next gate barrier, which both waves reach
+    // after this, and the work overlaps the other waves' requests. Each store
+    // reaches 64 lines (a token's line holds every value head's value) and a
+    // wave's later loads wait for its stores, so the two go to different waves,
+    // and with kPair (an even number of value heads per key head, dg and dbeta
+    // 8-byte aligned) an even head's values wait in LDS for its odd partner's,
+    // so that one store writes both. t: the lane, from an opaque
+    // copy of the thread index (see the value-head loop), so that none of the
+    // addresses below is hoisted out of the loop.
+    auto put = [&](float* dst, float* stash, int hv_, int jv, int t, float x) {
+      if (kPair && (jv & 1) == 0) {
+        stash[t] = x;
+      } else if (t < L) {
+        float* p = dst + (size_t)(t0 + t) * HV + hv_;
+        if (kPair)
+          *reinterpret_cast<float2*>(p - 1) = make_float2(stash[t], x);
+        else
+          *p = x;
+      }
+    };
+    auto db_out = [&](int hv_, int jv, int t) {
       const float dbt = (S.rowB[0][t] + S.rowB[1][t]) + (S.rowB2[0][t] + S.rowB2[1][t]) +
                         (S.rowB3[0][t] + S.rowB3[1][t]);
-      if (t < L) dbeta[(size_t)(t0 + t) * HV + hv_] = dbt;
+      put(dbeta, S.dot_q[1], hv_, jv, t, dbt);
     };
-    auto dg_out = [&](int hv_, int t) {
+    auto dg_out = [&](int hv_, int jv, int t) {
       const int w0 = 4 * ((t >> 4) & 1);  // the waves whose column tiles hold t
       float dgm = (S.rowF[0][t] + S.rowF[1][t]) + (S.rowG[0][t] + S.rowG[1][t]) +
                   (S.rowE[0][t] + S.rowE[1][t]);
@@ -617,7 +633,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
         x += glsum + exp2_fast(S.gam[L - 1]) * hdsum;
       }
       x = wave_suffix_sum(x, t);
-      if (t < L) dg[(size_t)(t0 + t) * HV + hv_] = x;
+      put(dg, S.dot_q[0], hv_, jv, t, x);
     };
 
     // dq~, dk^ over the value heads: [j][r] = d[16 tw + 4 kq + r][16 (4 kh + j) + li]
@@ -710,13 +726,13 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
 
       // ---- gates (wave 0, after the previous value head's gate gradients)
       if (wave == 0) {
-        if (jg > 0) dg_out(hv - 1, lane);
+        if (jg > 0) dg_out(hv - 1, jg - 1, lane);
         S.gam[lane] = gam_t;
         S.bet[lane] = bet_t;
         S.eg[lane] = eg_t;
         S.ebw[lane] = ebw_t;
       } else if (wave == 1) {
-        if (jg > 0) db_out(hv - 1, lane);
+        if (jg > 0) db_out(hv - 1, jg - 1, lane);
       }
       lds_barrier();
 
@@ -1108,8 +1124,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     {
       int tid = threadIdx.x;
       asm volatile("" : "+v"(tid));
-      if ((tid >> 6) == 0) dg_out(h * G + G - 1, tid & 63);
-      else if ((tid >> 6) == 1) db_out(h * G + G - 1, tid & 63);
+      if ((tid >> 6) == 0) dg_out(h * G + G - 1, G - 1, tid & 63);
+      else if ((tid >> 6) == 1) db_out(h * G + G - 1, G - 1, tid & 63);
     }
 
     // every wave is done with Hs, Gs, the P tiles and the dW / Y1^T region:
@@ -1232,8 +1248,15 @@ hipError_t launch_bwd_chunk(const ChunkInfo* table, int NC, int H, int HV, float
   const long items = (long)NC * H;
   if (items <= 0) return hipSuccess;
   const unsigned grid = (unsigned)std::max(1L, std::min(items, (long)cus));
-  hipLaunchKernelGGL(bwd_chunk_kernel, dim3(grid), dim3(512), 0, stream, table, NC, H, HV, scale,
-                     q, k, v, g, beta, saved, Tmat, gE, gB, bufs, dO, dq, dk, dv, dg, dbeta);
+  // dg and dbeta of two value heads of a key head in one 8-byte store
+  const bool pair = (HV / H) % 2 == 0 && (reinterpret_cast<uintptr_t>(dg) & 7) == 0 &&
+                    (reinterpret_cast<uintptr_t>(dbeta) & 7) == 0;
+  if (pair)
+    hipLaunchKernelGGL(bwd_chunk_kernel<true>, dim3(grid), dim3(512), 0, stream, table, NC, H, HV,
+                       scale, q, k, v, g, beta, saved, Tmat, gE, gB, bufs, dO, dq, dk, dv, dg, dbeta);
+  else
+    hipLaunchKernelGGL(bwd_chunk_kernel<false>, dim3(grid), dim3(512), 0, stream, table, NC, H, HV,
+                       scale, q, k, v, g, beta, saved, Tmat, gE, gB, bufs, dO, dq, dk, dv, dg, dbeta);
   return hipGetLastError();
 }
 

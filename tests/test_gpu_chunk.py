@@ -349,6 +349,37 @@ def test_backward_with_device_only_boundaries_matches_host_route_bitwise():
         assert torch.equal(g1[name], r1[name]), name
 
 
+def test_backward_gate_gradients_at_4_byte_aligned_outputs_give_the_same_bits():
+    """With an even number of value heads per key head and dg, dbeta 8-byte
+    aligned, the gradient pass writes two heads' gate gradients in one store;
+    outputs that are only 4-byte aligned take one store per head and must hold
+    the same bits."""
+    _say("bwd gate gradients at 4-byte aligned outputs")
+    inp = small_inputs(H=2, HV=4, with_do=True)
+    d = to_dev(inp)
+    host = inp["cu_seqlens"].to(torch.int32)
+    o, hT, saved = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                                 h0=d["h0"], cu_seqlens_host=host, save_for_backward=True)
+    ref = gdn.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], saved,
+                        d["do"], cu_seqlens_host=host)
+    T, HV = d["v"].shape[0], d["v"].shape[1]
+    N = host.numel() - 1
+    dev = d["q"].device
+    p = gdn.make_problem(N, T, 2, HV, d["cu_seqlens"], host, 0.0)
+    dg = torch.full((T * HV + 1,), float("nan"), dtype=torch.float32, device=dev)[1:].view(T, HV)
+    db = torch.full((T * HV + 1,), float("nan"), dtype=torch.float32, device=dev)[1:].view(T, HV)
+    assert dg.data_ptr() % 8 == 4 and db.data_ptr() % 8 == 4
+    out = dict(dq=torch.empty_like(d["q"]), dk=torch.empty_like(d["k"]),
+               dv=torch.empty_like(d["v"]), dg=dg, dbeta=db,
+               dh0=torch.empty(N, HV, 128, 128, dtype=torch.float32, device=dev))
+    ws = torch.empty(gdn.gdn_chunk_bwd_workspace_size(p), dtype=torch.uint8, device=dev)
+    gdn.gdn_chunk_bwd(p, d["q"], d["k"], d["v"], d["g"], d["beta"], saved, d["do"], None,
+                      out["dq"], out["dk"], out["dv"], out["dg"], out["dbeta"], out["dh0"], ws)
+    torch.cuda.synchronize()
+    for name in ref:
+        assert torch.equal(ref[name], out[name]), name
+
+
 def test_backward_repeats_bitwise_many_times_and_on_a_side_stream():
     inp = small_inputs(with_do=True)
     o, hT, g0 = run_fwd_bwd(inp)
