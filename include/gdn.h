@@ -131,9 +131,9 @@ size_t gdn_chunk_bwd_recompute_workspace_size(const gdn_problem* p);
  *             zero); after all those blocks come the chunk quantities the
  *             backward contracts with (W, P, T in bf16 per value head and
  *             chunk; the normalised q and k in bf16 per key head and chunk;
- *             e^gamma_L, the per-token decays e^gamma, e^(gamma_L - gamma),
- *             the cumulative decay gamma and beta in fp32 per value head and
- *             chunk), written by the same WY pass
+ *             e^gamma_L, the per-token factors e^gamma, e^(gamma_L - gamma)
+ *             and beta, and the cumulative decay gamma with beta again, in
+ *             fp32 per value head and chunk), written by the same WY pass
  *             that feeds the forward scan so that the backward does not form
  *             them again. All in tile orders internal to this library: only
  *             gdn_chunk_bwd of the same build reads them.
