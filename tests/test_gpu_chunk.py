@@ -183,6 +183,29 @@ def test_backward_with_all_zero_q_and_k_rows_matches_oracle():
                    (got * norm)[zero], (want * norm)[zero])
 
 
+def test_zero_beta_matches_oracle():
+    """beta = 0 writes nothing: U = T diag(beta) V and W vanish on those tokens,
+    so the corrected values D are zero there (a whole value head, a whole chunk
+    of every head, and single tokens), while dbeta still receives the
+    gradient of the write that did not happen."""
+    _say("fwd+bwd zero beta")
+    inp = small_inputs(with_do=True)
+    inp["beta"][:, 1] = 0
+    inp["beta"][64:128] = 0
+    for t in (0, 5, 63, 200, 450):
+        inp["beta"][t] = 0
+    o, hT, grads = run_fwd_bwd(inp)
+    o_ref, hT_ref = oracle_forward(inp)
+    assert_bar("o", f64(o), o_ref)
+    assert_bar("hT", f64(hT), hT_ref)
+    ref = oracle_backward(inp)
+    for name in ("dq", "dk", "dv", "dbeta", "dh0"):
+        assert_bar(f"zero beta {name}", f64(grads[name]), ref[name])
+    assert_dg_bar("zero beta dg", f64(grads["dg"]), ref["dg"])
+    # the head without writes: dv is zero (v never enters the state)
+    assert (grads["dv"][:, 1] == 0).all()
+
+
 # ------------------------------------------------------------------ edge cases
 def test_no_tokens_passes_the_state_through():
     H, HV, N = 2, 4, 3
